@@ -1,0 +1,183 @@
+"""CPU oracle for the KV-cache append + causal GQA attention step.
+
+TEST INFRASTRUCTURE ONLY.  Imported by ``tests/``, by ``__graft_entry__.smoke``
+and by the ``cpu_baseline`` leg of ``bench.py``; the product package never
+imports it and the GPU library never links it.
+
+The arithmetic lives in ``kvc_oracle.c`` (plain C, double precision); this
+module only builds that file with gcc and marshals numpy arrays through
+ctypes.  bfloat16 arrays travel as their raw ``uint16`` words.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "kvc_oracle.c")
+LIBRARY = os.path.join(HERE, "libkvc_oracle.so")
+
+F32, BF16 = 0, 1
+ROW_OK, ROW_BAD_LENGTH, ROW_OVERFLOW, ROW_NOT_PREFIX = 0, 1, 2, 3
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the oracle with gcc (IEEE double, no contraction, no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+           "-shared", "-fPIC", "-I", os.path.dirname(os.path.abspath(source)),
+           source, "-o", output + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(output + ".tmp", output)
+    return output
+
+
+def _ptr(a: np.ndarray | None) -> int | None:
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle takes float32 or bfloat16-as-uint16 arrays, got {a.dtype}")
+
+
+@dataclass
+class StepResult:
+    key_cache: np.ndarray
+    value_cache: np.ndarray
+    lengths: np.ndarray
+    attention: np.ndarray  # float64 [B, Hq, Q, M]
+    context: np.ndarray  # float64 [B, Hq, Q, Dv]
+    row_status: np.ndarray  # int32 [B]
+
+
+class Oracle:
+    """ctypes face of ``libkvc_oracle.so`` (or of any library built from a
+    variant of ``kvc_oracle.c``, which the mutation tests use)."""
+
+    def __init__(self, path: str = LIBRARY):
+        if not os.path.exists(path):
+            build(output=path)
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.kvc_oracle_append.restype = ctypes.c_int
+        lib.kvc_oracle_append.argtypes = [_i64] * 7 + [ctypes.c_int] + [_vp] * 11
+        lib.kvc_oracle_attend_row.restype = ctypes.c_int
+        lib.kvc_oracle_attend_row.argtypes = ([_i64] * 7 + [ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_double] + [_vp] * 3 + [_i64] * 5
+                                             + [_vp] * 2)
+        lib.kvc_oracle_step.restype = ctypes.c_int
+        lib.kvc_oracle_step.argtypes = ([_i64] * 7 + [ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_double] + [_vp] * 13)
+        self.lib = lib
+
+    # -- helpers -----------------------------------------------------------
+    @staticmethod
+    def _dims(query, new_key, new_value, key_cache, value_cache):
+        B, Hq, Q, D = query.shape
+        Hk, M = key_cache.shape[1], key_cache.shape[2]
+        Dv = value_cache.shape[3]
+        return B, Hq, Hk, Q, M, D, Dv
+
+    def step(self, query, new_key, new_value, key_cache, value_cache, lengths,
+             append_mask, scale: float | None = None) -> StepResult:
+        """The full step over numpy inputs; returns fresh output arrays."""
+        args = [np.ascontiguousarray(a) for a in (query, new_key, new_value, key_cache,
+                                                   value_cache)]
+        query, new_key, new_value, key_cache, value_cache = args
+        lengths = np.ascontiguousarray(lengths, dtype=np.int64)
+        append_mask = np.ascontiguousarray(append_mask, dtype=np.uint8)
+        dt = _dtype_code(query)
+        for a in args:
+            if _dtype_code(a) != dt:
+                raise TypeError("all float inputs must share one dtype")
+        B, Hq, Hk, Q, M, D, Dv = self._dims(*args)
+        kc_out = np.empty_like(key_cache)
+        vc_out = np.empty_like(value_cache)
+        len_out = np.empty(B, dtype=np.int64)
+        attn = np.empty((B, Hq, Q, M), dtype=np.float64)
+        ctx = np.empty((B, Hq, Q, Dv), dtype=np.float64)
+        status = np.empty(B, dtype=np.int32)
+        rc = self.lib.kvc_oracle_step(
+            B, Hq, Hk, Q, M, D, Dv, dt, 0 if scale is None else 1,
+            0.0 if scale is None else float(scale), _ptr(query), _ptr(new_key),
+            _ptr(new_value), _ptr(key_cache), _ptr(value_cache), _ptr(lengths),
+            _ptr(append_mask), _ptr(kc_out), _ptr(vc_out), _ptr(len_out), _ptr(attn),
+            _ptr(ctx), _ptr(status))
+        if rc != 0:
+            raise ValueError(f"oracle rejected the step (code {rc})")
+        return StepResult(kc_out, vc_out, len_out, attn, ctx, status)
+
+    def append(self, new_key, new_value, key_cache, value_cache, lengths, append_mask,
+               Hq: int | None = None):
+        """Append only: returns (key_cache_out, value_cache_out, lengths_out, n, status)."""
+        new_key, new_value, key_cache, value_cache = [
+            np.ascontiguousarray(a) for a in (new_key, new_value, key_cache, value_cache)]
+        lengths = np.ascontiguousarray(lengths, dtype=np.int64)
+        append_mask = np.ascontiguousarray(append_mask, dtype=np.uint8)
+        dt = _dtype_code(key_cache)
+        B, Hk, M, D = key_cache.shape
+        Dv = value_cache.shape[3]
+        Q = append_mask.shape[1]
+        Hq = Hk if Hq is None else Hq
+        kc_out = np.empty_like(key_cache)
+        vc_out = np.empty_like(value_cache)
+        len_out = np.empty(B, dtype=np.int64)
+        n = np.empty(B, dtype=np.int64)
+        status = np.empty(B, dtype=np.int32)
+        rc = self.lib.kvc_oracle_append(
+            B, Hq, Hk, Q, M, D, Dv, dt, _ptr(new_key), _ptr(new_value), _ptr(key_cache),
+            _ptr(value_cache), _ptr(lengths), _ptr(append_mask), _ptr(kc_out),
+            _ptr(vc_out), _ptr(len_out), _ptr(n), _ptr(status))
+        if rc != 0:
+            raise ValueError(f"oracle rejected the append (code {rc})")
+        return kc_out, vc_out, len_out, n, status
+
+    def attend_row(self, query, key_updated, value_updated, old_len: int, n: int, b: int,
+                   hq: int, t: int, scale: float | None = None):
+        """One (b, hq, t) row over an updated cache: returns (attention[M], context[Dv])."""
+        query = np.ascontiguousarray(query)
+        key_updated = np.ascontiguousarray(key_updated)
+        value_updated = np.ascontiguousarray(value_updated)
+        dt = _dtype_code(query)
+        B, Hq, Q, D = query.shape
+        Hk, M = key_updated.shape[1], key_updated.shape[2]
+        Dv = value_updated.shape[3]
+        attn = np.empty(M, dtype=np.float64)
+        ctx = np.empty(Dv, dtype=np.float64)
+        rc = self.lib.kvc_oracle_attend_row(
+            B, Hq, Hk, Q, M, D, Dv, dt, 0 if scale is None else 1,
+            0.0 if scale is None else float(scale), _ptr(query), _ptr(key_updated),
+            _ptr(value_updated), int(old_len), int(n), int(b), int(hq), int(t),
+            _ptr(attn), _ptr(ctx))
+        if rc != 0:
+            raise ValueError(f"oracle rejected the row (code {rc})")
+        return attn, ctx
+
+    def raw_step_code(self, B, Hq, Hk, Q, M, D, Dv, dtype=F32, has_scale=0, scale=0.0) -> int:
+        """Return code of a step call with NULL buffers (argument checks only)."""
+        return self.lib.kvc_oracle_step(B, Hq, Hk, Q, M, D, Dv, dtype, has_scale, scale,
+                                        *([None] * 13))
+
+
+_DEFAULT: Oracle | None = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``kvc_oracle.c`` (built on first use)."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        _DEFAULT = Oracle(LIBRARY)
+    return _DEFAULT
