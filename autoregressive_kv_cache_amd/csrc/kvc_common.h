@@ -1,0 +1,164 @@
+// kvc_common.h -- device-side types and helpers shared by the step's
+// kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+constexpr int kWave = 64;
+
+// bfloat16 storage word (the top 16 bits of a binary32).
+struct bf16 {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// binary32 -> bfloat16 with round-to-nearest-even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Element traits: storage type T, accumulation type Acc.  fp32 inputs
+// accumulate in fp64 (scores reach ~1e3 and the probabilities must hold to
+// 1e-5); bf16 inputs accumulate in fp32.
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+  using Acc = double;
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static double load(const float* p) { return static_cast<double>(*p); }
+  __device__ __forceinline__ static void store(float* p, double v) { *p = static_cast<float>(v); }
+  __device__ __forceinline__ static float zero() { return 0.0f; }
+};
+
+template <>
+struct Elem<bf16> {
+  using Acc = float;
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float load(const bf16* p) { return bf16_to_f32(p->bits); }
+  __device__ __forceinline__ static void store(bf16* p, float v) { p->bits = f32_to_bf16(v); }
+  __device__ __forceinline__ static bf16 zero() { return bf16{0}; }
+};
+
+__device__ __forceinline__ double acc_exp(double x) { return exp(x); }
+__device__ __forceinline__ float acc_exp(float x) { return __expf(x); }
+
+// Everything one step's kernels need; passed by value as the kernel argument.
+struct StepArgs {
+  int64_t B, Hq, Hk, Q, M, D, Dv;
+  int32_t G;          // Hq / Hk
+  int32_t R;          // packed rows per KV head = G * Q (row r = g * Q + t)
+  int32_t rows_per_tile;
+  int32_t row_tiles;
+  int64_t S;          // slots per split
+  int64_t nsplit;     // ceil(M / S)
+  double scale;       // resolved softmax scale
+  int32_t out_of_place;
+  const void* query;
+  const void* new_key;
+  const void* new_value;
+  const void* kc_in;  // cache read for slots < length (== kc_out in place)
+  const void* vc_in;
+  void* kc_out;       // cache written (copy + new rows, or new rows only)
+  void* vc_out;
+  const int64_t* lengths;
+  const uint8_t* mask;
+  void* attention;
+  void* context;
+  int64_t* lengths_out;
+  int32_t* row_status;
+  int64_t* ws_rowinfo;  // [B][4]: length, n, status, unused
+  double* ws_ml;        // [B*Hk][nsplit][R][2]: split max, split sum
+  float* ws_o;          // [B*Hk][nsplit][R][Dv]: split unnormalised context
+};
+
+struct RowInfo {
+  int64_t len;     // lengths[b] as given
+  int64_t n;       // appended rows (0 on a rejected row)
+  int32_t status;  // KVC_ROW_* code
+};
+
+// Row preparation for batch row b, run by one full wave (uniform result):
+// n = leading run of Trues in append_mask[b,:]; a length outside [0, M], a
+// True after a False, or length + n > M rejects the row (n = 0).  The order
+// of the checks fixes which code a row with several faults reports.
+__device__ inline RowInfo wave_row_info(const int64_t* lengths, const uint8_t* mask, int64_t Q,
+                                        int64_t M, int64_t b) {
+  const int lane = threadIdx.x & (kWave - 1);
+  RowInfo ri;
+  ri.len = lengths[b];
+  int64_t n = 0;
+  bool seen_false = false, not_prefix = false;
+  for (int64_t t0 = 0; t0 < Q; t0 += kWave) {
+    const int64_t t = t0 + lane;
+    const bool v = (t < Q) && (mask[b * Q + t] != 0);
+    const uint64_t ones = __ballot(v);
+    const int64_t left = Q - t0;
+    const uint64_t in_range = left >= kWave ? ~0ull : ((1ull << left) - 1ull);
+    const uint64_t falses = ~ones & in_range;
+    if (!seen_false) {
+      if (falses == 0) {
+        n += __popcll(in_range);
+      } else {
+        const int first_false = __ffsll(static_cast<unsigned long long>(falses)) - 1;
+        n += first_false;
+        seen_false = true;
+        const uint64_t above = first_false >= 63 ? 0ull : (ones >> (first_false + 1));
+        if (above != 0) not_prefix = true;
+      }
+    } else if (ones != 0) {
+      not_prefix = true;
+    }
+  }
+  if (ri.len < 0 || ri.len > M) {
+    ri.status = 1;
+    ri.n = 0;
+  } else if (not_prefix) {
+    ri.status = 3;
+    ri.n = 0;
+  } else if (ri.len + n > M) {
+    ri.status = 2;
+    ri.n = 0;
+  } else {
+    ri.status = 0;
+    ri.n = n;
+  }
+  return ri;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    T w = __shfl_xor(v, o);
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Number of splits of one batch row that hold at least one slot a valid
+// query can see (all slots < length + n), 0 when the row appends nothing.
+__device__ __forceinline__ int64_t active_splits(int64_t len, int64_t n, int64_t S) {
+  return n > 0 ? ceil_div(len + n, S) : 0;
+}
+
+}  // namespace kvc

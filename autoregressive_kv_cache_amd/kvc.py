@@ -1,0 +1,296 @@
+"""Python binding of the C ABI in ``include/kvc.h`` (ctypes; argument
+marshalling only -- every step of the computation runs in the HIP kernels of
+``libkvc.so``).  PyTorch supplies device memory and the current HIP stream.
+
+Low level (same names as the C entry points, tensors instead of pointers):
+``kvc_workspace_bytes``, ``kvc_plan_step``, ``kvc_step_out_of_place``,
+``kvc_step_inplace``, ``kvc_status_string``.
+
+Page-style face ("Autoregressive KV-cache append and causal attention",
+Function signature / Starter code): ``kv_cache_attention_step`` returns a
+dict with ``key_cache``, ``value_cache``, ``lengths``, ``attention`` and
+``context`` and leaves its inputs untouched; ``kv_cache_attention_step_``
+is the in-place twin (the caches are updated where they are).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libkvc.so")
+
+KVC_F32, KVC_BF16 = 0, 1
+KVC_OK = 0
+ERRORS = {-1: "KVC_ERR_NULL", -2: "KVC_ERR_SHAPE", -3: "KVC_ERR_DTYPE", -4: "KVC_ERR_SCALE",
+          -5: "KVC_ERR_WORKSPACE", -6: "KVC_ERR_ALIAS", -7: "KVC_ERR_HIP"}
+ROW_OK, ROW_BAD_LENGTH, ROW_OVERFLOW, ROW_NOT_PREFIX = 0, 1, 2, 3
+EXPORTED = ("kvc_workspace_bytes", "kvc_plan_step", "kvc_step_out_of_place",
+            "kvc_step_inplace", "kvc_status_string")
+
+
+class KvcDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("B", "Hq", "Hk", "Q", "M", "D", "Dv")]
+
+
+class KvcEvents(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_void_p), ("stop", ctypes.c_void_p)]
+
+
+class KvcPlan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("rows", ctypes.c_int32),
+                ("rows_per_tile", ctypes.c_int32), ("row_tiles", ctypes.c_int32),
+                ("split", ctypes.c_int64), ("nsplit", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class KvcError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {ERRORS.get(code, code)} ({kvc_status_string(code)})")
+        self.code = code
+
+
+_vp, _i64, _int, _dbl, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double,
+                              ctypes.c_size_t)
+_LIB = None
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load ``libkvc.so``; raises ImportError when it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m autoregressive_kv_cache_amd._build`")
+    lib = ctypes.CDLL(path)
+    lib.kvc_workspace_bytes.restype = _sz
+    lib.kvc_workspace_bytes.argtypes = [ctypes.POINTER(KvcDims), _int]
+    lib.kvc_plan_step.restype = _int
+    lib.kvc_plan_step.argtypes = [ctypes.POINTER(KvcDims), _int, ctypes.POINTER(KvcPlan)]
+    lib.kvc_step_out_of_place.restype = _int
+    lib.kvc_step_out_of_place.argtypes = ([ctypes.POINTER(KvcDims), _int, _int, _dbl]
+                                          + [_vp] * 13 + [_vp, _sz, _vp,
+                                                          ctypes.POINTER(KvcEvents)])
+    lib.kvc_step_inplace.restype = _int
+    lib.kvc_step_inplace.argtypes = ([ctypes.POINTER(KvcDims), _int, _int, _dbl]
+                                     + [_vp] * 11 + [_vp, _sz, _vp, ctypes.POINTER(KvcEvents)])
+    lib.kvc_status_string.restype = ctypes.c_char_p
+    lib.kvc_status_string.argtypes = [_int]
+    _LIB = lib
+    return lib
+
+
+def kvc_status_string(code: int) -> str:
+    return load().kvc_status_string(int(code)).decode()
+
+
+def dims_of(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor) -> KvcDims:
+    B, Hq, Q, D = query.shape
+    return KvcDims(B, Hq, key_cache.shape[1], Q, key_cache.shape[2], D, value_cache.shape[3])
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return KVC_F32
+    if dt == torch.bfloat16:
+        return KVC_BF16
+    raise TypeError(f"unsupported dtype {dt} (float32 or bfloat16)")
+
+
+def kvc_workspace_bytes(dims: KvcDims, dtype: int) -> int:
+    return int(load().kvc_workspace_bytes(ctypes.byref(dims), int(dtype)))
+
+
+def kvc_plan_step(dims: KvcDims, dtype: int) -> dict:
+    plan = KvcPlan()
+    rc = load().kvc_plan_step(ctypes.byref(dims), int(dtype), ctypes.byref(plan))
+    if rc != KVC_OK:
+        raise KvcError(rc, "kvc_plan_step")
+    return {f: getattr(plan, f) for f, _ in KvcPlan._fields_}
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the C ABI must be contiguous")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _events(events) -> ctypes.POINTER(KvcEvents) | None:
+    if events is None:
+        return None
+    start, stop = events
+    return ctypes.pointer(KvcEvents(int(start), int(stop)))
+
+
+def _scale_args(scale: float | None) -> tuple[int, float]:
+    return (0, 0.0) if scale is None else (1, float(scale))
+
+
+def workspace_for(dims: KvcDims, dtype: int, device) -> torch.Tensor:
+    return torch.empty(max(1, kvc_workspace_bytes(dims, dtype)), dtype=torch.uint8, device=device)
+
+
+def kvc_step_out_of_place(query, new_key, new_value, key_cache, value_cache, lengths, append_mask,
+                          key_cache_out, value_cache_out, lengths_out, attention, context,
+                          row_status=None, workspace=None, scale=None, stream=None,
+                          events=None) -> None:
+    """Enqueue the out-of-place step on ``stream`` (default: torch's current
+    stream).  All tensors are device tensors in the layouts of ``kvc.h``."""
+    lib = load()
+    dims = dims_of(query, key_cache, value_cache)
+    dt = dtype_code(key_cache.dtype)
+    if workspace is None:
+        workspace = workspace_for(dims, dt, key_cache.device)
+    hs, sc = _scale_args(scale)
+    rc = lib.kvc_step_out_of_place(
+        ctypes.byref(dims), dt, hs, sc, _ptr(query), _ptr(new_key), _ptr(new_value),
+        _ptr(key_cache), _ptr(value_cache), _ptr(lengths), _ptr(append_mask), _ptr(key_cache_out),
+        _ptr(value_cache_out), _ptr(lengths_out), _ptr(attention), _ptr(context), _ptr(row_status),
+        _ptr(workspace), workspace.numel(), _stream(stream, key_cache.device), _events(events))
+    if rc != KVC_OK:
+        raise KvcError(rc, "kvc_step_out_of_place")
+
+
+def kvc_step_inplace(query, new_key, new_value, key_cache, value_cache, lengths, append_mask,
+                     lengths_out, attention, context, row_status=None, workspace=None, scale=None,
+                     stream=None, events=None) -> None:
+    """Enqueue the in-place step on ``stream``; ``lengths_out`` may be
+    ``lengths`` itself."""
+    lib = load()
+    dims = dims_of(query, key_cache, value_cache)
+    dt = dtype_code(key_cache.dtype)
+    if workspace is None:
+        workspace = workspace_for(dims, dt, key_cache.device)
+    hs, sc = _scale_args(scale)
+    rc = lib.kvc_step_inplace(
+        ctypes.byref(dims), dt, hs, sc, _ptr(query), _ptr(new_key), _ptr(new_value),
+        _ptr(key_cache), _ptr(value_cache), _ptr(lengths), _ptr(append_mask), _ptr(lengths_out),
+        _ptr(attention), _ptr(context), _ptr(row_status), _ptr(workspace), workspace.numel(),
+        _stream(stream, key_cache.device), _events(events))
+    if rc != KVC_OK:
+        raise KvcError(rc, "kvc_step_inplace")
+
+
+# ---------------------------------------------------------------------------
+# page-style face
+# ---------------------------------------------------------------------------
+def _check_inputs(query, new_key, new_value, key_cache, value_cache, lengths, append_mask):
+    ts = (query, new_key, new_value, key_cache, value_cache)
+    dev = key_cache.device
+    if dev.type != "cuda":
+        raise ValueError("the KV-cache step runs on a GPU; inputs must be device tensors")
+    for t in ts + (lengths, append_mask):
+        if t.device != dev:
+            raise ValueError("all inputs must be on one device")
+    for t in ts:
+        if t.dtype != key_cache.dtype:
+            raise ValueError("query, new_key, new_value and the caches must share one dtype")
+        if t.dim() != 4:
+            raise ValueError("query/new_key/new_value/caches must be 4-D")
+    B, Hq, Q, D = query.shape
+    _, Hk, M, _ = key_cache.shape
+    Dv = value_cache.shape[3]
+    if (tuple(new_key.shape) != (B, Hk, Q, D) or tuple(new_value.shape) != (B, Hk, Q, Dv)
+            or tuple(key_cache.shape) != (B, Hk, M, D)
+            or tuple(value_cache.shape) != (B, Hk, M, Dv)):
+        raise ValueError("inconsistent shapes")
+    if tuple(lengths.shape) != (B,) or tuple(append_mask.shape) != (B, Q):
+        raise ValueError("lengths must be [B] and append_mask [B, Q]")
+    if Hq % Hk != 0:
+        raise ValueError("Hq must be a multiple of Hk")
+
+
+def _options_scale(options) -> float | None:
+    options = dict(options or {})
+    extra = set(options) - {"scale"}
+    if extra:
+        raise ValueError(f"unknown options {sorted(extra)}: scale is the only key")
+    scale = options.get("scale")
+    if scale is None:
+        return None
+    scale = float(scale)
+    if not (scale > 0.0 and math.isfinite(scale)):
+        raise ValueError("scale must be a positive finite number")
+    return scale
+
+
+def _prep(lengths, append_mask):
+    lengths = lengths.to(torch.int64).contiguous()
+    mask = append_mask.to(torch.bool).contiguous().view(torch.uint8)
+    return lengths, mask
+
+
+def _raise_rejected(row_status: torch.Tensor):
+    st = row_status.cpu()
+    bad = torch.nonzero(st).flatten().tolist()
+    if bad:
+        b = bad[0]
+        raise ValueError(f"batch row {b}: {kvc_status_string(int(st[b]))}")
+
+
+def kv_cache_attention_step(query, new_key, new_value, key_cache, value_cache, lengths,
+                            append_mask, options=None, validate=False) -> dict:
+    """The step, out of place; returns the page's dict.  With
+    ``validate=True`` a rejected row raises ValueError (this synchronises)."""
+    _check_inputs(query, new_key, new_value, key_cache, value_cache, lengths, append_mask)
+    scale = _options_scale(options)
+    q, nk, nv, kc, vc = (t.contiguous() for t in (query, new_key, new_value, key_cache,
+                                                   value_cache))
+    lens, mask = _prep(lengths, append_mask)
+    B, Hq, Q, _ = q.shape
+    M, Dv = kc.shape[2], vc.shape[3]
+    out = {
+        "key_cache": torch.empty_like(kc),
+        "value_cache": torch.empty_like(vc),
+        "lengths": torch.empty_like(lens),
+        "attention": torch.empty(B, Hq, Q, M, dtype=kc.dtype, device=kc.device),
+        "context": torch.empty(B, Hq, Q, Dv, dtype=kc.dtype, device=kc.device),
+    }
+    status = torch.empty(B, dtype=torch.int32, device=kc.device)
+    kvc_step_out_of_place(q, nk, nv, kc, vc, lens, mask, out["key_cache"], out["value_cache"],
+                          out["lengths"], out["attention"], out["context"], status, scale=scale)
+    if validate:
+        _raise_rejected(status)
+    if lengths.dtype != torch.int64:
+        out["lengths"] = out["lengths"].to(lengths.dtype)
+    return out
+
+
+def kv_cache_attention_step_(query, new_key, new_value, key_cache, value_cache, lengths,
+                             append_mask, options=None, validate=False) -> dict:
+    """In-place twin: the new rows are written into ``key_cache`` and
+    ``value_cache`` (which must be contiguous) and ``lengths`` is updated in
+    place when it is a contiguous int64 tensor."""
+    _check_inputs(query, new_key, new_value, key_cache, value_cache, lengths, append_mask)
+    if not (key_cache.is_contiguous() and value_cache.is_contiguous()):
+        raise ValueError("in-place caches must be contiguous")
+    scale = _options_scale(options)
+    q, nk, nv = (t.contiguous() for t in (query, new_key, new_value))
+    inplace_len = lengths.dtype == torch.int64 and lengths.is_contiguous()
+    lens, mask = _prep(lengths, append_mask)
+    B, Hq, Q, _ = q.shape
+    M, Dv = key_cache.shape[2], value_cache.shape[3]
+    attention = torch.empty(B, Hq, Q, M, dtype=key_cache.dtype, device=key_cache.device)
+    context = torch.empty(B, Hq, Q, Dv, dtype=key_cache.dtype, device=key_cache.device)
+    status = torch.empty(B, dtype=torch.int32, device=key_cache.device)
+    lens_out = lens if inplace_len else torch.empty_like(lens)
+    kvc_step_inplace(q, nk, nv, key_cache, value_cache, lens, mask, lens_out, attention, context,
+                     status, scale=scale)
+    if not inplace_len:
+        lengths.copy_(lens_out.to(lengths.dtype))
+    if validate:
+        _raise_rejected(status)
+    return {"key_cache": key_cache, "value_cache": value_cache, "lengths": lengths,
+            "attention": attention, "context": context}

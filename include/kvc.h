@@ -1,0 +1,160 @@
+/*
+ * kvc.h -- C ABI of the MI355X (gfx950) library for one autoregressive step
+ * of a fixed-capacity KV cache: append new key/value rows, then run causal,
+ * GQA-aware softmax attention of the step's queries over the updated cache.
+ *
+ * The operation is the one defined on the page "Autoregressive KV-cache
+ * append and causal attention" (biotorch problem kv_cache_attention_step),
+ * sections "Function signature", "Required behavior" and "Starter code":
+ *
+ *   - query head h reads KV head floor(h / (Hq / Hk));
+ *   - append_mask[b,:] is a prefix of n_b Trues; new_key/new_value row t is
+ *     written to cache slot lengths[b] + t for t < n_b, and the new length
+ *     is lengths[b] + n_b;
+ *   - valid query t (t < n_b) attends slots j <= lengths[b] + t (and
+ *     j < lengths[b] + n_b) -- the lower-right causal alignment fixed by
+ *     KempnerForge pull request 542 (Summary);
+ *   - scores are scale * dot(q, k), scale > 0, default 1/sqrt(D); the
+ *     softmax is taken after subtracting the row maximum;
+ *   - attention[B,Hq,Q,M] holds the probabilities (exactly 0 outside the
+ *     allowed slots and on invalid rows) and context[B,Hq,Q,Dv] =
+ *     attention x updated values (0 on invalid rows);
+ *   - every cache entry that is not written keeps its exact bits.
+ *
+ * Layout.  Every tensor is dense, row-major and contiguous in device memory
+ * (HBM), head-major as on the page (and as the continuous cache layout of
+ * ClikaRT's attention_over_cache):
+ *
+ *   query       [B, Hq, Q, D]        new_key     [B, Hk, Q, D]
+ *   new_value   [B, Hk, Q, Dv]       key_cache   [B, Hk, M, D]
+ *   value_cache [B, Hk, M, Dv]       lengths     [B]  int64
+ *   append_mask [B, Q] uint8 (0 = False, other = True)
+ *   attention   [B, Hq, Q, M]        context     [B, Hq, Q, Dv]
+ *   row_status  [B]  int32 (optional)
+ *
+ * Floating tensors all have the element type `dtype` (KVC_F32 or KVC_BF16);
+ * attention and context are written in that type too.  bf16 inputs are
+ * computed with fp32 accumulation; fp32 inputs accumulate scores and softmax
+ * statistics in fp64.
+ *
+ * Ownership.  The caller owns every buffer.  All tensor pointers are device
+ * pointers; `dims` and `events` point to host memory.  The library keeps no
+ * state between calls, allocates no memory, performs no host/device
+ * synchronisation, and enqueues all of its work on `stream` (a hipStream_t;
+ * NULL is the default stream).  A call returns once its kernels are
+ * enqueued; the outputs are ready when the stream reaches that point.
+ * Scratch memory is the caller's `workspace` (size: kvc_workspace_bytes);
+ * its contents need no initialisation and are garbage after the call.
+ * Calls that share a workspace must be ordered on one stream.
+ *
+ * Errors.  Argument errors are found on the host before anything is
+ * enqueued and returned as a negative KVC_ERR_* code; nothing is written.
+ * Rows that break the page's preconditions (length outside [0, M], a mask
+ * that is not a prefix, length + n > M) are outside the page's contract;
+ * this library treats such a row as a no-op -- its cache row is left (or
+ * copied) unchanged, lengths_out[b] = lengths[b], its attention and context
+ * are zero -- and reports the reason in row_status[b] (KVC_ROW_*).
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Problem sizes.  B, Hq, Hk, M, D, Dv >= 1; Q >= 0; Hq % Hk == 0. */
+typedef struct kvc_dims {
+  int64_t B, Hq, Hk, Q, M, D, Dv;
+} kvc_dims;
+
+/* Element type of every floating tensor. */
+typedef enum kvc_dtype { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+/* Return codes. */
+enum {
+  KVC_OK = 0,
+  KVC_ERR_NULL = -1,        /* a required pointer is NULL */
+  KVC_ERR_SHAPE = -2,       /* sizes out of range, Hq % Hk != 0, or too large */
+  KVC_ERR_DTYPE = -3,       /* dtype is not a kvc_dtype */
+  KVC_ERR_SCALE = -4,       /* has_scale and scale not finite or <= 0 */
+  KVC_ERR_WORKSPACE = -5,   /* workspace_bytes < kvc_workspace_bytes() */
+  KVC_ERR_ALIAS = -6,       /* an output overlaps an input or another output */
+  KVC_ERR_HIP = -7          /* a kernel launch failed (HIP error) */
+};
+
+/* Per-row status written to row_status[b]. */
+enum {
+  KVC_ROW_OK = 0,
+  KVC_ROW_BAD_LENGTH = 1,   /* lengths[b] < 0 or > M */
+  KVC_ROW_OVERFLOW = 2,     /* lengths[b] + n_b > M */
+  KVC_ROW_NOT_PREFIX = 3    /* append_mask[b,:] has a True after a False */
+};
+
+/* Optional timing hook: when a kvc_events is passed, `start` and `stop`
+ * (hipEvent_t handles created by the caller) are recorded on the stream
+ * immediately before and after the attention kernel of the step. */
+typedef struct kvc_events {
+  void *start;
+  void *stop;
+} kvc_events;
+
+/* Kernel plan the library picks for a shape (host-only, no HIP call). */
+typedef struct kvc_plan {
+  int32_t path;          /* 0 generic, 1 vector decode, 2 MFMA chunk */
+  int32_t rows;          /* packed query rows per KV head: (Hq/Hk) * Q */
+  int32_t rows_per_tile; /* packed rows handled by one workgroup */
+  int32_t row_tiles;     /* ceil(rows / rows_per_tile) */
+  int64_t split;         /* cache slots per split-K workgroup */
+  int64_t nsplit;        /* ceil(M / split) */
+  size_t workspace_bytes;
+} kvc_plan;
+
+/* Bytes of device workspace a step with these sizes needs (0 on bad
+ * arguments).  Depends only on dims and dtype. */
+size_t kvc_workspace_bytes(const kvc_dims *dims, int dtype);
+
+/* Fill *plan for these sizes; returns KVC_OK or an argument error. */
+int kvc_plan_step(const kvc_dims *dims, int dtype, kvc_plan *plan);
+
+/* The page's step, leaving every input untouched ("never modify inputs"):
+ * the whole cache is copied bit for bit into key_cache_out/value_cache_out
+ * with the new rows in place, lengths_out[b] = lengths[b] + n_b, and
+ * attention/context are written.  No output may overlap an input or another
+ * output (KVC_ERR_ALIAS).  row_status may be NULL.  With Q = 0 only the
+ * cache copy and lengths_out are produced (attention/context may be NULL). */
+int kvc_step_out_of_place(const kvc_dims *dims, int dtype, int has_scale,
+                          double scale, const void *query,
+                          const void *new_key, const void *new_value,
+                          const void *key_cache, const void *value_cache,
+                          const int64_t *lengths, const uint8_t *append_mask,
+                          void *key_cache_out, void *value_cache_out,
+                          int64_t *lengths_out, void *attention,
+                          void *context, int32_t *row_status, void *workspace,
+                          size_t workspace_bytes, void *stream,
+                          const kvc_events *events);
+
+/* The same step for production decode: the new rows are written into
+ * key_cache/value_cache in place (nothing else of the cache is touched).
+ * lengths_out may be the same buffer as lengths (then it is updated in
+ * place); any other overlap between outputs, inputs and caches is rejected.
+ * With lengths_out != lengths a repeated call repeats the same step. */
+int kvc_step_inplace(const kvc_dims *dims, int dtype, int has_scale,
+                     double scale, const void *query, const void *new_key,
+                     const void *new_value, void *key_cache, void *value_cache,
+                     const int64_t *lengths, const uint8_t *append_mask,
+                     int64_t *lengths_out, void *attention, void *context,
+                     int32_t *row_status, void *workspace,
+                     size_t workspace_bytes, void *stream,
+                     const kvc_events *events);
+
+/* Static description of a return or row-status code. */
+const char *kvc_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

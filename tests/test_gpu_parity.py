@@ -1,0 +1,228 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+seeded inputs, element by element; cache contents and lengths bit-exact,
+floats within the stated tolerances (tests/gpu_helpers.py)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from autoregressive_kv_cache_amd import kvc
+from autoregressive_kv_cache_amd.workloads import (WORKLOADS, Workload, draw_lengths_and_counts,
+                                                   host_arrays, make_inputs)
+from gpu_helpers import (bits, check_floats, check_row_sums, check_step, run_gpu, say, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kvc.load()  # fail loudly when the HIP library is missing
+    yield
+
+
+def full_check(wl: Workload, seed: int, mode: str, scale="default", **kw):
+    scale = wl.scale if scale == "default" else scale
+    say(f"[case] {wl.name} seed={seed} mode={mode} scale={scale} {kw}")
+    inp = make_inputs(wl, seed, "cpu", **kw)
+    h = host_arrays(inp)
+    ref = oracle.default().step(h["query"], h["new_key"], h["new_value"], h["key_cache"],
+                                h["value_cache"], h["lengths"], h["append_mask"], scale=scale)
+    dinp = {k: v.to(DEV) for k, v in inp.items()}
+    out = run_gpu(dinp, mode, scale=scale)
+    check_step(out, ref, wl.dtype, f"{wl.name}/{seed}/{mode}")
+    if mode == "oop":  # inputs untouched
+        for k, v in inp.items():
+            assert torch.equal(dinp[k].cpu(), v), f"input {k} modified"
+    return out, ref
+
+
+# -- the small workloads, several seeds, both entry points -------------------
+SMALL = ["tiny_mixed_f32", "chunk_gqa_bf16", "chunk_gqa_f32", "mha_stress_f32"]
+
+
+@pytest.mark.parametrize("mode", ["oop", "inplace"])
+@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_small_workloads(name, seed, mode):
+    full_check(WORKLOADS[name], seed, mode)
+
+
+@pytest.mark.parametrize("seed", range(3, 8))
+def test_tiny_more_seeds(seed):
+    full_check(WORKLOADS["tiny_mixed_f32"], seed, "oop")
+
+
+# -- reduced decode shapes: several splits, ragged tails, full oracle -------
+@pytest.mark.parametrize("mode", ["oop", "inplace"])
+@pytest.mark.parametrize("wl", [
+    WORKLOADS["decode_gqa_bf16"].with_(name="decode_small", B=4, M=1536, len_range=(200, 1535)),
+    WORKLOADS["long_decode_bf16"].with_(name="long_small", B=2, M=4099, len_range=(1000, 4098)),
+    WORKLOADS["decode_gqa_bf16"].with_(name="decode_f32_small", B=3, M=777, dtype="f32",
+                                       len_range=(0, 776)),
+    WORKLOADS["chunk_gqa_bf16"].with_(name="chunk_ragged", M=700, len_range=(100, 640)),
+], ids=lambda w: w.name)
+def test_reduced_decode_shapes(wl, mode):
+    full_check(wl, 0, mode)
+
+
+# -- full sizes --------------------------------------------------------------
+def test_decode_gqa_full_size_inplace_and_oop():
+    """Single-token GQA decode at its full size (B=32, Hq=32, Hk=8, M=8192,
+    D=Dv=128, bf16, 1e4 sentinel tail): full oracle comparison."""
+    wl = WORKLOADS["decode_gqa_bf16"]
+    for mode in ("inplace", "oop"):
+        full_check(wl, 0, mode)
+
+
+def test_long_decode_full_size_sampled():
+    """Long-context decode at its full size (B=4, Hq=64, Hk=8, M=131072):
+    caches bit-exact against the oracle's append, sampled rows against the
+    oracle one by one, row sums and zero tails on every row."""
+    wl = WORKLOADS["long_decode_bf16"]
+    for mode in ("inplace", "oop"):
+        say(f"[case] {wl.name} full size mode={mode}")
+        dinp = make_inputs(wl, 0, DEV)
+        h = host_arrays(dinp)
+        kc, vc, lens, n, status = oracle.default().append(
+            h["new_key"], h["new_value"], h["key_cache"], h["value_cache"], h["lengths"],
+            h["append_mask"], Hq=wl.Hq)
+        out = run_gpu(dinp, mode)
+        assert np.array_equal(host_arrays({"x": out["key_cache"]})["x"], kc)
+        assert np.array_equal(host_arrays({"x": out["value_cache"]})["x"], vc)
+        assert np.array_equal(out["lengths"].cpu().numpy(), lens)
+        assert np.array_equal(out["row_status"].cpu().numpy(), status)
+        att = to_f64(out["attention"])
+        ctx = to_f64(out["context"])
+        check_row_sums(att, h["lengths"], n, wl.dtype, wl.name)
+        rng = np.random.default_rng(1)
+        for b in range(wl.B):
+            for hq in list(rng.choice(wl.Hq, 3, replace=False)):
+                a_ref, c_ref = oracle.default().attend_row(h["query"], kc, vc, int(h["lengths"][b]),
+                                                           int(n[b]), b, int(hq), 0)
+                check_floats(att[b, hq, 0], a_ref, wl.dtype, f"row {b},{hq}", "attention")
+                check_floats(ctx[b, hq, 0], c_ref, wl.dtype, f"row {b},{hq}", "context")
+        del dinp, out
+        torch.cuda.empty_cache()
+
+
+# -- edge cases --------------------------------------------------------------
+def tiny(**kw) -> Workload:
+    base = dict(name="edge", B=3, Hq=4, Hk=2, Q=3, M=20, D=8, Dv=8, dtype="f32",
+                len_range=(0, 17), n_rule="uniform")
+    base.update(kw)
+    return Workload(**base)
+
+
+@pytest.mark.parametrize("mode", ["oop", "inplace"])
+@pytest.mark.parametrize("wl", [
+    tiny(name="q0", Q=0),
+    tiny(name="all_n0", n_rule="choice", n_choices=(0,)),
+    tiny(name="m1", M=1, Q=1, len_range=(0, 0), n_rule="all"),
+    tiny(name="mha1", B=1, Hq=1, Hk=1, Q=1, M=5, len_range=(0, 4), n_rule="all"),
+    tiny(name="odd_dims", D=3, Dv=5, M=37, len_range=(0, 30)),
+    tiny(name="odd_dims_bf16", D=7, Dv=3, M=300, len_range=(0, 290), dtype="bf16"),
+    tiny(name="fill_to_capacity", M=10, Q=3, len_range=(7, 7), n_rule="all"),
+    tiny(name="full_cache", M=10, Q=2, len_range=(10, 10), n_rule="all"),
+    tiny(name="many_rows", Hq=32, Hk=2, Q=3, M=300, len_range=(0, 290)),
+    tiny(name="wide_head", Hq=2, Hk=1, D=512, Dv=256, M=64, len_range=(0, 60), dtype="bf16"),
+], ids=lambda w: w.name)
+def test_edge_shapes(wl, mode):
+    full_check(wl, 0, mode)
+
+
+@pytest.mark.parametrize("mode", ["oop", "inplace"])
+def test_rejected_rows(mode):
+    """Rows outside the contract (bad length, non-prefix mask, overflow) are
+    no-ops with a status; other rows of the batch are unaffected."""
+    wl = tiny(name="rejected", B=5, Q=3, M=12)
+    lengths = np.array([3, -1, 13, 4, 11], np.int64)
+    n = np.array([2, 1, 0, 1, 2], np.int64)
+    inp = make_inputs(wl, 4, "cpu", lengths=lengths, n=n)
+    inp["append_mask"][3] = torch.tensor([True, False, True])  # not a prefix
+    h = host_arrays(inp)
+    ref = oracle.default().step(h["query"], h["new_key"], h["new_value"], h["key_cache"],
+                                h["value_cache"], h["lengths"], h["append_mask"])
+    assert list(ref.row_status) == [0, 1, 1, 3, 2]
+    out = run_gpu({k: v.to(DEV) for k, v in inp.items()}, mode)
+    check_step(out, ref, "f32", f"rejected/{mode}")
+
+
+def test_lengths_updated_in_place():
+    wl = tiny(name="alias")
+    inp = {k: v.to(DEV) for k, v in make_inputs(wl, 2, "cpu").items()}
+    h = host_arrays(inp)
+    ref = oracle.default().step(h["query"], h["new_key"], h["new_value"], h["key_cache"],
+                                h["value_cache"], h["lengths"], h["append_mask"])
+    out = run_gpu(inp, "inplace", lengths_alias=True)
+    assert out["lengths"].data_ptr() == inp["lengths"].data_ptr()
+    check_step(out, ref, "f32", "alias")
+
+
+def test_inplace_repeat_is_idempotent():
+    """With lengths_out != lengths, repeating the in-place step repeats the
+    same step (what the benchmark relies on)."""
+    wl = WORKLOADS["decode_gqa_bf16"].with_(B=4, M=2048, len_range=(100, 2047))
+    inp = {k: v.to(DEV) for k, v in make_inputs(wl, 3, "cpu").items()}
+    first = {k: v.clone() for k, v in run_gpu(inp, "inplace").items()}
+    second = run_gpu(inp, "inplace")
+    for k in ("key_cache", "value_cache", "lengths", "attention", "context"):
+        assert torch.equal(bits_t(first[k]), bits_t(second[k])), k
+
+
+def bits_t(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+@pytest.mark.parametrize("mode", ["oop", "inplace"])
+def test_tail_future_invariance_bitwise(mode):
+    """Cache tail beyond the new length, new rows t >= n and query rows
+    t >= n cannot change any output (bitwise)."""
+    wl = WORKLOADS["chunk_gqa_bf16"].with_(M=900, len_range=(100, 800))
+    inp = make_inputs(wl, 6, "cpu")
+    lengths, n = draw_lengths_and_counts(wl, 6)
+    pert = {k: v.clone() for k, v in inp.items()}
+    for b in range(wl.B):
+        L, nb = int(lengths[b]), int(n[b])
+        pert["key_cache"][b, :, L + nb:] = 77.0
+        pert["value_cache"][b, :, L + nb:] = -55.0
+        pert["key_cache"][b, :, L:L + nb] = 3.0
+        pert["new_key"][b, :, nb:] = 1e3
+        pert["new_value"][b, :, nb:] = -1e3
+        pert["query"][b, :, nb:] = 1e3
+    o1 = run_gpu({k: v.to(DEV) for k, v in inp.items()}, mode)
+    o2 = run_gpu({k: v.to(DEV) for k, v in pert.items()}, mode)
+    assert torch.equal(bits_t(o1["attention"]), bits_t(o2["attention"]))
+    assert torch.equal(bits_t(o1["context"]), bits_t(o2["context"]))
+
+
+def test_page_face_dict_and_inplace_twin():
+    wl = WORKLOADS["tiny_mixed_f32"]
+    inp = {k: v.to(DEV) for k, v in make_inputs(wl, 1, "cpu").items()}
+    h = host_arrays(inp)
+    ref = oracle.default().step(h["query"], h["new_key"], h["new_value"], h["key_cache"],
+                                h["value_cache"], h["lengths"], h["append_mask"], scale=0.5)
+    out = kvc.kv_cache_attention_step(inp["query"], inp["new_key"], inp["new_value"],
+                                      inp["key_cache"], inp["value_cache"], inp["lengths"],
+                                      inp["append_mask"], {"scale": 0.5})
+    assert set(out) == {"key_cache", "value_cache", "lengths", "attention", "context"}
+    check_floats(to_f64(out["attention"]), ref.attention, "f32", "face attention", "attention")
+    check_floats(to_f64(out["context"]), ref.context, "f32", "face context", "context")
+    assert np.array_equal(out["lengths"].cpu().numpy(), ref.lengths)
+    out2 = kvc.kv_cache_attention_step_(inp["query"], inp["new_key"], inp["new_value"],
+                                        inp["key_cache"], inp["value_cache"], inp["lengths"],
+                                        inp["append_mask"], {"scale": 0.5})
+    assert out2["key_cache"].data_ptr() == inp["key_cache"].data_ptr()
+    assert np.array_equal(bits(inp["key_cache"]), ref.key_cache.view(np.int32))
+    assert np.array_equal(inp["lengths"].cpu().numpy(), ref.lengths)
+    bad = inp["append_mask"].clone()
+    bad[0] = torch.tensor([False, True, False])
+    with pytest.raises(ValueError):
+        kvc.kv_cache_attention_step(inp["query"], inp["new_key"], inp["new_value"],
+                                    inp["key_cache"], inp["value_cache"], inp["lengths"], bad,
+                                    {}, validate=True)
