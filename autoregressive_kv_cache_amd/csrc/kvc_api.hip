@@ -10,7 +10,9 @@
 #include "../../include/kvc.h"
 #include "kvc_combine.h"
 #include "kvc_common.h"
+#include "kvc_decode.h"
 #include "kvc_generic.h"
+#include "kvc_prep.h"
 
 namespace {
 
@@ -29,9 +31,88 @@ bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Vector decode kernels compiled in: (dtype, D, Dv, packed rows).
+template <typename T, int D, int DV, int ROWS>
+void launch_decode(const StepArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.P / kvc::kDecodeWaves)), block(kvc::kDecodeThreads);
+  if (a.Q == 1)
+    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, false>), grid, block, 0, s, a);
+}
+
+struct DecodeEntry {
+  int dtype, D, Dv, rows, chunk;
+  void (*launch)(const StepArgs&, hipStream_t);
+};
+
+#define KVC_DECODE(T, CODE, D, DV, ROWS) \
+  {CODE, D, DV, ROWS, kvc::decode_chunk<T, D, DV>(), &launch_decode<T, D, DV, ROWS>}
+const DecodeEntry kDecodeTable[] = {
+    KVC_DECODE(kvc::bf16, KVC_BF16, 128, 128, 4), KVC_DECODE(kvc::bf16, KVC_BF16, 128, 128, 8),
+    KVC_DECODE(kvc::bf16, KVC_BF16, 64, 64, 4),   KVC_DECODE(kvc::bf16, KVC_BF16, 64, 64, 8),
+    KVC_DECODE(kvc::bf16, KVC_BF16, 256, 256, 4), KVC_DECODE(kvc::bf16, KVC_BF16, 256, 256, 8),
+    KVC_DECODE(float, KVC_F32, 128, 128, 4),      KVC_DECODE(float, KVC_F32, 128, 128, 8),
+    KVC_DECODE(float, KVC_F32, 64, 64, 4),        KVC_DECODE(float, KVC_F32, 64, 64, 8),
+    KVC_DECODE(float, KVC_F32, 64, 32, 4),        KVC_DECODE(float, KVC_F32, 64, 32, 8),
+};
+#undef KVC_DECODE
+
+// Stream path: MI355X has 256 compute units; a few resident attend
+// workgroups (of 4 waves, each wave one stream worker) per unit keep enough
+// loads in flight.
+constexpr int64_t kStreamWorkgroupsPerCU = 4;
+constexpr int64_t kComputeUnits = 256;
+// Slots per combine workgroup on the stream path (a multiple of every
+// decode chunk size).
+constexpr int64_t kStreamCombineSlots = 2048;
+
+const DecodeEntry* find_decode(const kvc_dims* d, int dtype, int64_t R) {
+  if (R > 8) return nullptr;
+  const int rows = R <= 4 ? 4 : 8;
+  for (const DecodeEntry& e : kDecodeTable)
+    if (e.dtype == dtype && e.D == d->D && e.Dv == d->Dv && e.rows == rows) return &e;
+  return nullptr;
+}
+
+struct Layout {
+  int64_t C, nchunk_max, nseg, CS;
+  size_t off_hdr, off_rowinfo, off_chunk, off_seg_ml, off_seg_o, bytes;
+};
+
+bool make_layout(const kvc_dims* d, int64_t R, int64_t C, bool stream,
+                 int64_t P, Layout* L) {
+  L->C = C;
+  L->nchunk_max = (d->M + C - 1) / C;
+  L->CS = stream ? kStreamCombineSlots : C;
+  int64_t groups, chunks, nseg, x;
+  if (!mul_ok(d->B, d->Hk, kMaxElems, &groups) || !mul_ok(groups, L->nchunk_max, kMaxElems, &chunks))
+    return false;
+  nseg = stream ? P + groups : chunks;
+  L->nseg = nseg;
+  size_t off = 0;
+  L->off_hdr = off;
+  off = align_up(off + 8 * sizeof(int64_t), 256);
+  L->off_rowinfo = off;
+  off = align_up(off + static_cast<size_t>(d->B) * 4 * sizeof(int64_t), 256);
+  L->off_chunk = off;
+  if (!mul_ok(chunks, R, kMaxElems, &x)) return false;
+  off = align_up(off + static_cast<size_t>(x) * 2 * sizeof(double), 256);
+  L->off_seg_ml = off;
+  if (!mul_ok(nseg, R, kMaxElems, &x)) return false;
+  off = align_up(off + static_cast<size_t>(x) * 2 * sizeof(double), 256);
+  L->off_seg_o = off;
+  if (!mul_ok(x, d->Dv, kMaxElems, &x)) return false;
+  off = align_up(off + static_cast<size_t>(x) * sizeof(float), 256);
+  L->bytes = off;
+  return true;
+}
+
 struct Plan {
   kvc_plan pub;
-  size_t off_rowinfo, off_ml, off_o;
+  const DecodeEntry* decode;  // null: generic path
+  Layout generic, stream;
+  int64_t P;
 };
 
 int check_dims(const kvc_dims* d, int dtype) {
@@ -60,28 +141,33 @@ int make_plan(const kvc_dims* d, int dtype, Plan* p) {
   std::memset(p, 0, sizeof *p);
   const int64_t R = (d->Hq / d->Hk) * d->Q;
   p->pub.rows = static_cast<int32_t>(R);
-  p->pub.path = 0;
-  p->pub.rows_per_tile = kvc::kGenericRowsPerTile;
-  p->pub.split = kvc::kGenericSplit;
-  p->pub.row_tiles = static_cast<int32_t>(R == 0 ? 1 : (R + p->pub.rows_per_tile - 1) / p->pub.rows_per_tile);
-  p->pub.nsplit = (d->M + p->pub.split - 1) / p->pub.split;
-
-  int64_t groups, wgs, parts, obytes;
-  if (!mul_ok(d->B, d->Hk, kMaxElems, &groups) ||
-      !mul_ok(groups, p->pub.row_tiles, kMaxElems, &wgs) ||
-      !mul_ok(wgs, p->pub.nsplit, kMaxWorkgroups, &wgs))
+  p->decode = find_decode(d, dtype, R);
+  p->P = kComputeUnits * kStreamWorkgroupsPerCU * kvc::kDecodeWaves;
+  const int64_t row_tiles = R == 0 ? 1 : (R + kvc::kGenericRowsPerTile - 1) / kvc::kGenericRowsPerTile;
+  if (!make_layout(d, R, kvc::kGenericChunk, false, 0, &p->generic)) return KVC_ERR_SHAPE;
+  int64_t wgs;
+  if (!mul_ok(d->B * d->Hk, row_tiles, kMaxElems, &wgs) ||
+      !mul_ok(wgs, p->generic.nchunk_max, kMaxWorkgroups, &wgs))
     return KVC_ERR_SHAPE;
-  if (!mul_ok(groups, p->pub.nsplit, kMaxElems, &parts) || !mul_ok(parts, R, kMaxElems, &parts) ||
-      !mul_ok(parts, d->Dv, kMaxElems, &obytes))
-    return KVC_ERR_SHAPE;
-  size_t off = 0;
-  p->off_rowinfo = off;
-  off = align_up(off + static_cast<size_t>(d->B) * 4 * sizeof(int64_t), 256);
-  p->off_ml = off;
-  off = align_up(off + static_cast<size_t>(parts) * 2 * sizeof(double), 256);
-  p->off_o = off;
-  off = align_up(off + static_cast<size_t>(obytes) * sizeof(float), 256);
-  p->pub.workspace_bytes = off;
+  size_t bytes = p->generic.bytes;
+  if (p->decode) {
+    if (!make_layout(d, R, p->decode->chunk, true, p->P, &p->stream)) return KVC_ERR_SHAPE;
+    int64_t cwgs;
+    if (!mul_ok(d->B * d->Hk, p->stream.nchunk_max, kMaxWorkgroups, &cwgs)) return KVC_ERR_SHAPE;
+    if (p->stream.bytes > bytes) bytes = p->stream.bytes;
+    p->pub.path = 1;
+    p->pub.rows_per_tile = p->decode->rows;
+    p->pub.row_tiles = 1;
+    p->pub.split = p->decode->chunk;
+    p->pub.nsplit = p->stream.nchunk_max;
+  } else {
+    p->pub.path = 0;
+    p->pub.rows_per_tile = kvc::kGenericRowsPerTile;
+    p->pub.row_tiles = static_cast<int32_t>(row_tiles);
+    p->pub.split = kvc::kGenericChunk;
+    p->pub.nsplit = p->generic.nchunk_max;
+  }
+  p->pub.workspace_bytes = bytes;
   return KVC_OK;
 }
 
@@ -106,18 +192,43 @@ bool overlap(Range a, Range b) {
   return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
 }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+void set_layout(StepArgs& a, const Layout& L, void* workspace) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.C = L.C;
+  a.nchunk_max = L.nchunk_max;
+  a.CS = L.CS;
+  a.ws_hdr = reinterpret_cast<int64_t*>(ws + L.off_hdr);
+  a.ws_rowinfo = reinterpret_cast<int64_t*>(ws + L.off_rowinfo);
+  a.ws_chunk_ml = reinterpret_cast<double*>(ws + L.off_chunk);
+  a.ws_seg_ml = reinterpret_cast<double*>(ws + L.off_seg_ml);
+  a.ws_seg_o = reinterpret_cast<float*>(ws + L.off_seg_o);
+}
+
 template <typename T>
-void launch_all(const Plan& p, StepArgs& a, hipStream_t stream, const kvc_events* ev) {
+void launch_generic(StepArgs& a, hipStream_t stream, const kvc_events* ev) {
   const int64_t groups = a.B * a.Hk;
-  const dim3 grid_attend(static_cast<unsigned>(groups * a.row_tiles * a.nsplit));
-  const dim3 grid_combine(static_cast<unsigned>(groups * a.nsplit));
   if (ev && ev->start) hipEventRecord(static_cast<hipEvent_t>(ev->start), stream);
-  hipLaunchKernelGGL(kvc::attend_generic_kernel<T>, grid_attend, dim3(kvc::kGenericThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL(kvc::attend_generic_kernel<T>,
+                     dim3(static_cast<unsigned>(groups * a.row_tiles * a.nchunk_max)),
+                     dim3(kvc::kGenericThreads), 0, stream, a);
   if (ev && ev->stop) hipEventRecord(static_cast<hipEvent_t>(ev->stop), stream);
-  hipLaunchKernelGGL(kvc::combine_kernel<T>, grid_combine, dim3(kvc::kCombineThreads), 0, stream,
-                     a);
-  (void)p;
+  hipLaunchKernelGGL(kvc::combine_kernel<T>,
+                     dim3(static_cast<unsigned>(groups * ((a.M + a.CS - 1) / a.CS))),
+                     dim3(kvc::kCombineThreads), 0, stream, a);
+}
+
+template <typename T>
+void launch_stream(StepArgs& a, const DecodeEntry& e, hipStream_t stream, const kvc_events* ev) {
+  const int64_t groups = a.B * a.Hk;
+  hipLaunchKernelGGL(kvc::prep_kernel, dim3(1), dim3(kvc::kPrepThreads), 0, stream, a);
+  if (ev && ev->start) hipEventRecord(static_cast<hipEvent_t>(ev->start), stream);
+  e.launch(a, stream);
+  if (ev && ev->stop) hipEventRecord(static_cast<hipEvent_t>(ev->stop), stream);
+  hipLaunchKernelGGL(kvc::combine_kernel<T>,
+                     dim3(static_cast<unsigned>(groups * ((a.M + a.CS - 1) / a.CS))),
+                     dim3(kvc::kCombineThreads), 0, stream, a);
 }
 
 int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const void* query,
@@ -182,24 +293,41 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
   a.R = p.pub.rows;
   a.rows_per_tile = p.pub.rows_per_tile;
   a.row_tiles = p.pub.row_tiles;
-  a.S = p.pub.split;
-  a.nsplit = p.pub.nsplit;
+  a.P = p.P;
   a.scale = sc;
   a.out_of_place = out_of_place ? 1 : 0;
   a.query = query; a.new_key = new_key; a.new_value = new_value;
   a.kc_in = kc_in; a.vc_in = vc_in; a.kc_out = kc_out; a.vc_out = vc_out;
   a.lengths = lengths; a.mask = mask; a.attention = attention; a.context = context;
   a.lengths_out = lengths_out; a.row_status = row_status;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  a.ws_rowinfo = reinterpret_cast<int64_t*>(ws + p.off_rowinfo);
-  a.ws_ml = reinterpret_cast<double*>(ws + p.off_ml);
-  a.ws_o = reinterpret_cast<float*>(ws + p.off_o);
 
+  // the vector path needs 16-byte aligned rows
+  const bool vec_ok = p.decode && aligned16(query) && aligned16(new_key) && aligned16(new_value) &&
+                      aligned16(kc_in) && aligned16(vc_in) && aligned16(kc_out) &&
+                      aligned16(vc_out);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == KVC_F32)
-    launch_all<float>(p, a, s, events);
-  else
-    launch_all<kvc::bf16>(p, a, s, events);
+  if (vec_ok) {
+    set_layout(a, p.stream, workspace);
+    a.seg_mode = 1;
+    a.combine_copies_tail = 1;
+    a.rows_per_tile = p.decode->rows;
+    a.row_tiles = 1;
+    if (dtype == KVC_F32)
+      launch_stream<float>(a, *p.decode, s, events);
+    else
+      launch_stream<kvc::bf16>(a, *p.decode, s, events);
+  } else {
+    set_layout(a, p.generic, workspace);
+    a.seg_mode = 0;
+    a.combine_copies_tail = 0;
+    a.rows_per_tile = kvc::kGenericRowsPerTile;
+    a.row_tiles = static_cast<int32_t>(a.R == 0 ? 1 : (a.R + kvc::kGenericRowsPerTile - 1) /
+                                                        kvc::kGenericRowsPerTile);
+    if (dtype == KVC_F32)
+      launch_generic<float>(a, s, events);
+    else
+      launch_generic<kvc::bf16>(a, s, events);
+  }
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 

@@ -54,14 +54,32 @@ __device__ __forceinline__ double acc_exp(double x) { return exp(x); }
 __device__ __forceinline__ float acc_exp(float x) { return __expf(x); }
 
 // Everything one step's kernels need; passed by value as the kernel argument.
+//
+// Work is cut into chunks of C cache slots per (batch row b, KV head h):
+// chunk c of group g = b * Hk + h covers slots [c*C, min((c+1)*C, len+n)).
+// For every chunk the attend kernel leaves, per packed query row r,
+//   chunk statistics  m_c = max_j s_j,  l_c = sum_j exp(s_j - m_c),
+//   exp(s_j - m_c) in the attention buffer,
+// and per segment (a run of chunks of one group processed by one workgroup)
+//   m_seg, l_seg and o_seg = sum_j exp(s_j - m_seg) v_j.
+// Segments are addressed in one of two ways:
+//   seg_mode 0 ("dense"): one segment per chunk, id = g * nchunk_max + c;
+//   seg_mode 1 ("stream"): worker w of P (a wave) owns the chunk range
+//     [floor(w*Nc/P), floor((w+1)*Nc/P)) of the flattened chunk list, and its
+//     segment of group g has id w + g (unique: along the chunk list g and w
+//     never decrease and one of them grows between distinct pairs).
 struct StepArgs {
   int64_t B, Hq, Hk, Q, M, D, Dv;
   int32_t G;          // Hq / Hk
   int32_t R;          // packed rows per KV head = G * Q (row r = g * Q + t)
   int32_t rows_per_tile;
   int32_t row_tiles;
-  int64_t S;          // slots per split
-  int64_t nsplit;     // ceil(M / S)
+  int64_t C;          // slots per chunk
+  int64_t nchunk_max; // ceil(M / C)
+  int64_t CS;         // slots per combine workgroup (a multiple of C)
+  int64_t P;          // stream workers (waves of the attend grid, stream mode)
+  int32_t seg_mode;   // 0 dense, 1 stream
+  int32_t combine_copies_tail;  // out of place: combine copies slots the attend kernel skips
   double scale;       // resolved softmax scale
   int32_t out_of_place;
   const void* query;
@@ -77,9 +95,11 @@ struct StepArgs {
   void* context;
   int64_t* lengths_out;
   int32_t* row_status;
-  int64_t* ws_rowinfo;  // [B][4]: length, n, status, unused
-  double* ws_ml;        // [B*Hk][nsplit][R][2]: split max, split sum
-  float* ws_o;          // [B*Hk][nsplit][R][Dv]: split unnormalised context
+  int64_t* ws_hdr;       // [8]: [0] total chunk count Nc (stream mode)
+  int64_t* ws_rowinfo;   // [B][4]: length, n, status, first chunk index (stream mode)
+  double* ws_chunk_ml;   // [B*Hk][nchunk_max][R][2]: m_c, l_c
+  double* ws_seg_ml;     // [nseg][R][2]: m_seg, l_seg
+  float* ws_seg_o;       // [nseg][R][Dv]: o_seg
 };
 
 struct RowInfo {
@@ -155,10 +175,36 @@ __device__ __forceinline__ T wave_sum(T v) {
 
 __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Number of splits of one batch row that hold at least one slot a valid
-// query can see (all slots < length + n), 0 when the row appends nothing.
-__device__ __forceinline__ int64_t active_splits(int64_t len, int64_t n, int64_t S) {
-  return n > 0 ? ceil_div(len + n, S) : 0;
+// Number of chunks of one batch row's KV head that hold a slot a valid
+// query can see (all slots < length + n); 0 when the row appends nothing.
+__device__ __forceinline__ int64_t row_chunks(int64_t len, int64_t n, int64_t C) {
+  return n > 0 ? ceil_div(len + n, C) : 0;
+}
+
+// Row preparation by one thread (same checks, same order as wave_row_info).
+__device__ inline RowInfo thread_row_info(const int64_t* lengths, const uint8_t* mask, int64_t Q,
+                                          int64_t M, int64_t b) {
+  RowInfo ri;
+  ri.len = lengths[b];
+  int64_t n = 0;
+  while (n < Q && mask[b * Q + n] != 0) n++;
+  bool not_prefix = false;
+  for (int64_t t = n; t < Q; t++)
+    if (mask[b * Q + t] != 0) not_prefix = true;
+  if (ri.len < 0 || ri.len > M) {
+    ri.status = 1;
+    ri.n = 0;
+  } else if (not_prefix) {
+    ri.status = 3;
+    ri.n = 0;
+  } else if (ri.len + n > M) {
+    ri.status = 2;
+    ri.n = 0;
+  } else {
+    ri.status = 0;
+    ri.n = n;
+  }
+  return ri;
 }
 
 }  // namespace kvc

@@ -1,31 +1,29 @@
-// kvc_generic.h -- split-K attention kernel for any head sizes (D, Dv) and
-// any packed row count.  It is the path for shapes the vector decode and
-// MFMA chunk kernels do not cover (odd head sizes, tiny problems); those
-// kernels follow the same split protocol and share the combine kernel.
+// kvc_generic.h -- attend kernel for any head sizes (D, Dv) and any packed
+// row count, in dense chunk mode (one workgroup per chunk and row tile).
+// It is the path for shapes the vector decode kernel does not cover (odd
+// head sizes, misaligned buffers, many packed rows); it leaves the same
+// chunk and segment results and shares the combine kernel.
 //
-// One workgroup handles one (batch row b, KV head h, row tile, split s):
-//   1. cache writes for its slot range (row tile 0 only): the whole range is
-//      copied when out of place, otherwise only the appended rows are
-//      written ("Autoregressive KV-cache append and causal attention",
+// One workgroup handles one (batch row b, KV head h, row tile, chunk c):
+//   1. cache writes for the chunk's slot range (row tile 0 only): the whole
+//      range is copied when out of place, otherwise only the appended rows
+//      are written ("Autoregressive KV-cache append and causal attention",
 //      Required behavior: new rows at slot length + t, every other entry
 //      kept bit for bit);
 //   2. scores scale * dot(q, k) of its packed query rows against the slots
 //      they may see (j <= length + t, the lower-right alignment of
 //      KempnerForge PR 542, Summary); new rows are read from new_key /
 //      new_value, so no workgroup depends on another's cache writes;
-//   3. split softmax statistics m_s = max s_j, l_s = sum exp(s_j - m_s)
-//      and the unnormalised context o_s = sum exp(s_j - m_s) v_j;
-//   4. when the batch row has a single active split the outputs are final
-//      (attention = p / l, context = o / l); otherwise exp(s_j - m_s) goes to
-//      the attention buffer and (m_s, l_s, o_s) to the workspace for the
-//      combine kernel.
+//   3. chunk statistics m_c = max s_j, l_c = sum exp(s_j - m_c), the
+//      unnormalised context o_c = sum exp(s_j - m_c) v_j, and exp(s_j - m_c)
+//      into the attention buffer; the chunk is its own segment.
 #pragma once
 
 #include "kvc_common.h"
 
 namespace kvc {
 
-constexpr int kGenericSplit = 256;     // slots per split
+constexpr int kGenericChunk = 256;     // slots per chunk
 constexpr int kGenericRowsPerTile = 8; // packed query rows per workgroup
 constexpr int kGenericThreads = 256;
 
@@ -81,16 +79,16 @@ __global__ __launch_bounds__(kGenericThreads) void attend_generic_kernel(StepArg
   using E = Elem<T>;
   using Acc = typename E::Acc;
   constexpr int RT = kGenericRowsPerTile;
-  constexpr int S = kGenericSplit;
-  __shared__ Acc sc[RT][S];
+  constexpr int C = kGenericChunk;
+  __shared__ Acc sc[RT][C];
   __shared__ Acc row_m[RT], row_l[RT];
   __shared__ RowInfo info_sh;
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int64_t wg = blockIdx.x;
-  const int64_t s = wg % a.nsplit;
-  const int64_t rest = wg / a.nsplit;
+  const int64_t c = wg % a.nchunk_max;
+  const int64_t rest = wg / a.nchunk_max;
   const int rt = static_cast<int>(rest % a.row_tiles);
   const int64_t grp = rest / a.row_tiles;
   const int64_t b = grp / a.Hk, kvh = grp % a.Hk;
@@ -101,14 +99,15 @@ __global__ __launch_bounds__(kGenericThreads) void attend_generic_kernel(StepArg
   }
   __syncthreads();
   const RowInfo ri = info_sh;
-  if (s == 0 && kvh == 0 && rt == 0 && tid == 0) {
+  if (c == 0 && kvh == 0 && rt == 0 && tid == 0) {
     a.ws_rowinfo[b * 4 + 0] = ri.len;
     a.ws_rowinfo[b * 4 + 1] = ri.n;
     a.ws_rowinfo[b * 4 + 2] = ri.status;
+    a.ws_rowinfo[b * 4 + 3] = 0;
   }
   const int64_t len = ri.len, n = ri.n, new_len = len + n;
-  const int64_t s0 = s * S;
-  const int64_t s1 = s0 + S < a.M ? s0 + S : a.M;
+  const int64_t s0 = c * C;
+  const int64_t s1 = s0 + C < a.M ? s0 + C : a.M;
 
   const T* q = static_cast<const T*>(a.query);
   const T* nk = static_cast<const T*>(a.new_key);
@@ -136,10 +135,9 @@ __global__ __launch_bounds__(kGenericThreads) void attend_generic_kernel(StepArg
 
   const int r0 = rt * RT;
   const int rcount = a.R - r0 < RT ? a.R - r0 : RT;
-  if (rcount <= 0) return;
-  const int64_t nsa = active_splits(len, n, S);
-  const int64_t act_end = (n > 0) ? (s1 < new_len ? s1 : new_len) : s0;
-  const int nact = act_end > s0 ? static_cast<int>(act_end - s0) : 0;
+  if (rcount <= 0 || c >= row_chunks(len, n, C)) return;
+  const int64_t act_end = s1 < new_len ? s1 : new_len;
+  const int nact = static_cast<int>(act_end - s0);
   const Acc scale = static_cast<Acc>(a.scale);
   const Acc neg_inf = -static_cast<Acc>(INFINITY);
 
@@ -161,69 +159,55 @@ __global__ __launch_bounds__(kGenericThreads) void attend_generic_kernel(StepArg
   }
   __syncthreads();
 
-  // 3. split statistics; p = exp(s - m_s) replaces the score in LDS
+  // 3. chunk statistics; p = exp(s - m_c) replaces the score in LDS
+  T* att = static_cast<T*>(a.attention);
   for (int r = wave; r < rcount; r += kGenericThreads / kWave) {
+    const int rg = r0 + r;
+    const int64_t g = rg / a.Q, t = rg % a.Q;
     Acc m = neg_inf;
     for (int i = lane; i < nact; i += kWave) m = sc[r][i] > m ? sc[r][i] : m;
     m = wave_max(m);
     Acc l = 0;
+    T* arow = att + ((b * a.Hq + kvh * a.G + g) * a.Q + t) * a.M + s0;
     for (int i = lane; i < nact; i += kWave) {
       const Acc p = (m == neg_inf || sc[r][i] == neg_inf) ? Acc(0) : acc_exp(sc[r][i] - m);
       sc[r][i] = p;
       l += p;
+      if (t < n) E::store(arow + i, p);
     }
     l = wave_sum(l);
     if (lane == 0) {
       row_m[r] = m;
       row_l[r] = l;
+      if (t < n) {
+        double* cm = a.ws_chunk_ml + ((grp * a.nchunk_max + c) * a.R + rg) * 2;
+        cm[0] = static_cast<double>(m);
+        cm[1] = static_cast<double>(l);
+      }
     }
   }
   __syncthreads();
 
-  const bool single = (nsa == 1);
-  T* att = static_cast<T*>(a.attention);
-  // attention rows of this tile over [s0, s1)
-  for (int r = 0; r < rcount; r++) {
-    const int rg = r0 + r;
-    const int64_t g = rg / a.Q, t = rg % a.Q;
-    T* arow = att + ((b * a.Hq + kvh * a.G + g) * a.Q + t) * a.M;
-    const Acc inv_l = (single && row_l[r] > 0) ? Acc(1) / row_l[r] : Acc(1);
-    for (int64_t j = s0 + tid; j < s1; j += kGenericThreads) {
-      const int i = static_cast<int>(j - s0);
-      const Acc p = i < nact ? sc[r][i] : Acc(0);
-      E::store(arow + j, single ? p * inv_l : p);
-    }
-  }
-
-  // context pieces: o[r][dv] = sum_j p_j v_j over this split
-  T* ctx = static_cast<T*>(a.context);
-  const bool write_ctx = (s == 0 && nsa <= 1);
-  const bool write_part = (!single && s < nsa);
+  // segment = this chunk: statistics and o_c = sum_j p_j v_j
+  const int64_t seg = grp * a.nchunk_max + c;
   for (int idx = tid; idx < rcount * a.Dv; idx += kGenericThreads) {
     const int r = static_cast<int>(idx / a.Dv);
     const int64_t dv = idx % a.Dv;
     const int rg = r0 + r;
-    const int64_t g = rg / a.Q, t = rg % a.Q;
+    const int64_t t = rg % a.Q;
+    if (t >= n) continue;
     Acc o = 0;
-    if (t < n) {
-      for (int i = 0; i < nact; i++) {
-        const int64_t j = s0 + i;
-        const T* vp = j < len ? v_head + j * a.Dv : nv_head + (j - len) * a.Dv;
-        o += sc[r][i] * E::load(vp + dv);
-      }
+    for (int i = 0; i < nact; i++) {
+      const int64_t j = s0 + i;
+      const T* vp = j < len ? v_head + j * a.Dv : nv_head + (j - len) * a.Dv;
+      o += sc[r][i] * E::load(vp + dv);
     }
-    if (write_ctx) {
-      const Acc val = (t < n && row_l[r] > 0) ? o / row_l[r] : Acc(0);
-      E::store(ctx + ((b * a.Hq + kvh * a.G + g) * a.Q + t) * a.Dv + dv, val);
-    }
-    if (write_part) a.ws_o[((grp * a.nsplit + s) * a.R + rg) * a.Dv + dv] = static_cast<float>(o);
+    a.ws_seg_o[(seg * a.R + rg) * a.Dv + dv] = static_cast<float>(o);
   }
-  if (write_part) {
-    for (int r = tid; r < rcount; r += kGenericThreads) {
-      double* ml = a.ws_ml + ((grp * a.nsplit + s) * a.R + r0 + r) * 2;
-      ml[0] = static_cast<double>(row_m[r]);
-      ml[1] = static_cast<double>(row_l[r]);
-    }
+  for (int r = tid; r < rcount; r += kGenericThreads) {
+    double* ml = a.ws_seg_ml + (seg * a.R + r0 + r) * 2;
+    ml[0] = static_cast<double>(row_m[r]);
+    ml[1] = static_cast<double>(row_l[r]);
   }
 }
 

@@ -26,10 +26,10 @@ def _gpu():
     yield
 
 
-def full_check(wl: Workload, seed: int, mode: str, scale="default", **kw):
+def full_check(wl: Workload, seed: int, mode: str, scale="default", gen_device="cpu", **kw):
     scale = wl.scale if scale == "default" else scale
     say(f"[case] {wl.name} seed={seed} mode={mode} scale={scale} {kw}")
-    inp = make_inputs(wl, seed, "cpu", **kw)
+    inp = {k: v.cpu() for k, v in make_inputs(wl, seed, gen_device, **kw).items()}
     h = host_arrays(inp)
     ref = oracle.default().step(h["query"], h["new_key"], h["new_value"], h["key_cache"],
                                 h["value_cache"], h["lengths"], h["append_mask"], scale=scale)
@@ -77,7 +77,7 @@ def test_decode_gqa_full_size_inplace_and_oop():
     D=Dv=128, bf16, 1e4 sentinel tail): full oracle comparison."""
     wl = WORKLOADS["decode_gqa_bf16"]
     for mode in ("inplace", "oop"):
-        full_check(wl, 0, mode)
+        full_check(wl, 0, mode, gen_device=DEV)
 
 
 def test_long_decode_full_size_sampled():
@@ -226,3 +226,39 @@ def test_page_face_dict_and_inplace_twin():
         kvc.kv_cache_attention_step(inp["query"], inp["new_key"], inp["new_value"],
                                     inp["key_cache"], inp["value_cache"], inp["lengths"], bad,
                                     {}, validate=True)
+
+
+def test_plan_paths():
+    """The decode-shaped workloads take the vector stream path; the chunk
+    workloads (160 packed rows) and odd head sizes take the generic one."""
+    expect = {"decode_gqa_bf16": 1, "long_decode_bf16": 1, "mha_stress_f32": 1,
+              "tiny_mixed_f32": 0}
+    for name, path in expect.items():
+        w = WORKLOADS[name]
+        d = kvc.KvcDims(w.B, w.Hq, w.Hk, w.Q, w.M, w.D, w.Dv)
+        assert kvc.kvc_plan_step(d, kvc.dtype_code(w.torch_dtype))["path"] == path, name
+
+
+def misaligned(t: torch.Tensor) -> torch.Tensor:
+    """A copy of t whose data starts 2 bytes past a 16-byte boundary."""
+    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    view = flat[1:1 + t.numel()].view(t.shape)
+    view.copy_(t)
+    assert view.data_ptr() % 16 != 0
+    return view
+
+
+@pytest.mark.parametrize("mode", ["oop", "inplace"])
+def test_misaligned_buffers_take_generic_path(mode):
+    """Buffers that are not 16-byte aligned cannot use the vector path; the
+    library falls back to the generic kernel with the same results."""
+    wl = WORKLOADS["decode_gqa_bf16"].with_(name="misaligned", B=3, M=600, len_range=(10, 599))
+    inp = make_inputs(wl, 9, "cpu")
+    h = host_arrays(inp)
+    ref = oracle.default().step(h["query"], h["new_key"], h["new_value"], h["key_cache"],
+                                h["value_cache"], h["lengths"], h["append_mask"])
+    dinp = {k: v.to(DEV) for k, v in inp.items()}
+    for k in ("query", "key_cache", "value_cache"):
+        dinp[k] = misaligned(dinp[k])
+    out = run_gpu(dinp, mode)
+    check_step(out, ref, wl.dtype, f"misaligned/{mode}")
