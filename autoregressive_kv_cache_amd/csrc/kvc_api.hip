@@ -32,13 +32,25 @@ bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Vector decode kernels compiled in: (dtype, D, Dv, packed rows).
+template <typename T, int D, int DV, int ROWS, bool Q1>
+void launch_decode_q(const StepArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.P / kvc::kDecodeWaves)), block(kvc::kDecodeThreads);
+  const int64_t* ri = a.ws_rowinfo;
+  const int32_t* wst = a.ws_wstart;
+  if (a.out_of_place)
+    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, true>), grid, block, 0, s,
+                       a, ri, wst);
+  else
+    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, false>), grid, block, 0, s,
+                       a, ri, wst);
+}
+
 template <typename T, int D, int DV, int ROWS>
 void launch_decode(const StepArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.P / kvc::kDecodeWaves)), block(kvc::kDecodeThreads);
   if (a.Q == 1)
-    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, true>), grid, block, 0, s, a);
+    launch_decode_q<T, D, DV, ROWS, true>(a, s);
   else
-    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, false>), grid, block, 0, s, a);
+    launch_decode_q<T, D, DV, ROWS, false>(a, s);
 }
 
 struct DecodeEntry {
@@ -47,21 +59,20 @@ struct DecodeEntry {
 };
 
 #define KVC_DECODE(T, CODE, D, DV, ROWS) \
-  {CODE, D, DV, ROWS, kvc::decode_chunk<T, D, DV>(), &launch_decode<T, D, DV, ROWS>}
+  {CODE, D, DV, ROWS, kvc::decode_chunk<T, D, DV, ROWS>(), &launch_decode<T, D, DV, ROWS>}
 const DecodeEntry kDecodeTable[] = {
     KVC_DECODE(kvc::bf16, KVC_BF16, 128, 128, 4), KVC_DECODE(kvc::bf16, KVC_BF16, 128, 128, 8),
     KVC_DECODE(kvc::bf16, KVC_BF16, 64, 64, 4),   KVC_DECODE(kvc::bf16, KVC_BF16, 64, 64, 8),
     KVC_DECODE(kvc::bf16, KVC_BF16, 256, 256, 4), KVC_DECODE(kvc::bf16, KVC_BF16, 256, 256, 8),
-    KVC_DECODE(float, KVC_F32, 128, 128, 4),      KVC_DECODE(float, KVC_F32, 128, 128, 8),
-    KVC_DECODE(float, KVC_F32, 64, 64, 4),        KVC_DECODE(float, KVC_F32, 64, 64, 8),
-    KVC_DECODE(float, KVC_F32, 64, 32, 4),        KVC_DECODE(float, KVC_F32, 64, 32, 8),
+    KVC_DECODE(float, KVC_F32, 128, 128, 4),      KVC_DECODE(float, KVC_F32, 64, 64, 4),
+    KVC_DECODE(float, KVC_F32, 64, 32, 4),
 };
 #undef KVC_DECODE
 
 // Stream path: MI355X has 256 compute units; a few resident attend
 // workgroups (of 4 waves, each wave one stream worker) per unit keep enough
 // loads in flight.
-constexpr int64_t kStreamWorkgroupsPerCU = 4;
+constexpr int64_t kStreamWorkgroupsPerCU = 2;
 constexpr int64_t kComputeUnits = 256;
 // Slots per combine workgroup on the stream path (a multiple of every
 // decode chunk size).
@@ -77,7 +88,7 @@ const DecodeEntry* find_decode(const kvc_dims* d, int dtype, int64_t R) {
 
 struct Layout {
   int64_t C, nchunk_max, nseg, CS;
-  size_t off_hdr, off_rowinfo, off_chunk, off_seg_ml, off_seg_o, bytes;
+  size_t off_hdr, off_rowinfo, off_chunk, off_seg_ml, off_seg_o, off_wstart, bytes;
 };
 
 bool make_layout(const kvc_dims* d, int64_t R, int64_t C, bool stream,
@@ -104,6 +115,8 @@ bool make_layout(const kvc_dims* d, int64_t R, int64_t C, bool stream,
   L->off_seg_o = off;
   if (!mul_ok(x, d->Dv, kMaxElems, &x)) return false;
   off = align_up(off + static_cast<size_t>(x) * sizeof(float), 256);
+  L->off_wstart = off;
+  off = align_up(off + static_cast<size_t>(stream ? P : 0) * 4 * sizeof(int32_t), 256);
   L->bytes = off;
   return true;
 }
@@ -204,6 +217,7 @@ void set_layout(StepArgs& a, const Layout& L, void* workspace) {
   a.ws_chunk_ml = reinterpret_cast<double*>(ws + L.off_chunk);
   a.ws_seg_ml = reinterpret_cast<double*>(ws + L.off_seg_ml);
   a.ws_seg_o = reinterpret_cast<float*>(ws + L.off_seg_o);
+  a.ws_wstart = reinterpret_cast<int32_t*>(ws + L.off_wstart);
 }
 
 template <typename T>
@@ -222,7 +236,8 @@ void launch_generic(StepArgs& a, hipStream_t stream, const kvc_events* ev) {
 template <typename T>
 void launch_stream(StepArgs& a, const DecodeEntry& e, hipStream_t stream, const kvc_events* ev) {
   const int64_t groups = a.B * a.Hk;
-  hipLaunchKernelGGL(kvc::prep_kernel, dim3(1), dim3(kvc::kPrepThreads), 0, stream, a);
+  hipLaunchKernelGGL(kvc::prep_kernel, dim3(static_cast<unsigned>(a.B + 1)),
+                     dim3(kvc::kPrepThreads), 0, stream, a);
   if (ev && ev->start) hipEventRecord(static_cast<hipEvent_t>(ev->start), stream);
   e.launch(a, stream);
   if (ev && ev->stop) hipEventRecord(static_cast<hipEvent_t>(ev->stop), stream);
@@ -295,6 +310,7 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
   a.row_tiles = p.pub.row_tiles;
   a.P = p.P;
   a.scale = sc;
+  a.elem_bytes = static_cast<int64_t>(e);
   a.out_of_place = out_of_place ? 1 : 0;
   a.query = query; a.new_key = new_key; a.new_value = new_value;
   a.kc_in = kc_in; a.vc_in = vc_in; a.kc_out = kc_out; a.vc_out = vc_out;

@@ -28,18 +28,23 @@ namespace kvc {
 
 constexpr int kCombineThreads = 256;
 
-// Segment ids of group g in stream mode: the workers w whose chunk range
-// [start(w), start(w+1)) meets the group's chunks [x0, x1].
-struct StreamSegs {
-  int64_t Nc, P, x0, x1, g;
-  __device__ int64_t start(int64_t w) const { return w * Nc / P; }
-  __device__ int64_t first_w() const { return ((x0 + 1) * P - 1) / Nc; }
-  __device__ int64_t last_w() const { return ((x1 + 1) * P - 1) / Nc; }
-  __device__ bool owns(int64_t w) const {
-    const int64_t s = start(w), e = start(w + 1);
-    return s < e && e > x0 && s <= x1;
-  }
+// The segments of one group: ids first + s for s in [0, count).  Stream
+// mode: the workers owning chunks [x0, x1] of the flattened list are
+// consecutive, segment id = worker + group.  Dense mode: one per chunk.
+struct SegRange {
+  int64_t first, count;
 };
+
+__device__ inline SegRange group_segments(const StepArgs& a, int64_t grp, int64_t b, int64_t kvh,
+                                          int64_t nc) {
+  if (nc <= 0) return {0, 0};
+  if (!a.seg_mode) return {grp * a.nchunk_max, nc};
+  const int64_t Nc = a.ws_hdr[0], Pe = a.ws_hdr[1];
+  const int64_t x0 = a.ws_rowinfo[b * 4 + 3] + kvh * nc, x1 = x0 + nc - 1;
+  // owner(x) = the worker w with floor(w*Nc/Pe) <= x < floor((w+1)*Nc/Pe)
+  const int64_t w0 = ((x0 + 1) * Pe - 1) / Nc, w1 = ((x1 + 1) * Pe - 1) / Nc;
+  return {w0 + grp, w1 - w0 + 1};
+}
 
 template <typename Acc>
 struct RowStats {
@@ -48,36 +53,78 @@ struct RowStats {
 
 // m and l of packed row r over the segments of its group (whole wave).
 template <typename Acc>
-__device__ RowStats<Acc> row_stats(const StepArgs& a, int64_t grp, int64_t nc, const StreamSegs& ss,
-                                   int r, int lane) {
+__device__ RowStats<Acc> row_stats(const StepArgs& a, const SegRange& sr, int r, int lane) {
   const Acc neg_inf = -static_cast<Acc>(INFINITY);
   Acc m = neg_inf;
-  const int64_t k0 = a.seg_mode ? ss.first_w() : 0;
-  const int64_t k1 = a.seg_mode ? ss.last_w() + 1 : nc;
-  for (int64_t k = k0 + lane; k < k1; k += kWave) {
-    if (a.seg_mode && !ss.owns(k)) continue;
-    const int64_t seg = a.seg_mode ? k + grp : grp * a.nchunk_max + k;
-    const Acc mk = static_cast<Acc>(a.ws_seg_ml[(seg * a.R + r) * 2]);
+  for (int64_t s = lane; s < sr.count; s += kWave) {
+    const Acc mk = static_cast<Acc>(a.ws_seg_ml[((sr.first + s) * a.R + r) * 2]);
     m = mk > m ? mk : m;
   }
   m = wave_max(m);
   Acc l = 0;
-  for (int64_t k = k0 + lane; k < k1; k += kWave) {
-    if (a.seg_mode && !ss.owns(k)) continue;
-    const int64_t seg = a.seg_mode ? k + grp : grp * a.nchunk_max + k;
-    const Acc mk = static_cast<Acc>(a.ws_seg_ml[(seg * a.R + r) * 2]);
-    if (mk != neg_inf) l += static_cast<Acc>(a.ws_seg_ml[(seg * a.R + r) * 2 + 1]) * acc_exp(mk - m);
+  for (int64_t s = lane; s < sr.count; s += kWave) {
+    const double* ml = a.ws_seg_ml + ((sr.first + s) * a.R + r) * 2;
+    const Acc mk = static_cast<Acc>(ml[0]);
+    if (mk != neg_inf) l += static_cast<Acc>(ml[1]) * acc_exp(mk - m);
   }
   l = wave_sum(l);
   return {m, l};
 }
 
+// Eight consecutive elements of T (16 bytes of bf16, 32 of fp32).
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<bf16> {
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void store(bf16* p) const { *reinterpret_cast<uint4*>(p) = v; }
+  __device__ __forceinline__ void scale_by(float f) {
+    uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const uint32_t lo = f32_to_bf16(__uint_as_float(w[k] << 16) * f);
+      const uint32_t hi = f32_to_bf16(__uint_as_float(w[k] & 0xffff0000u) * f);
+      w[k] = lo | (hi << 16);
+    }
+  }
+  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+};
+template <>
+struct Vec8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void store(float* p) const {
+    reinterpret_cast<float4*>(p)[0] = a;
+    reinterpret_cast<float4*>(p)[1] = b;
+  }
+  __device__ __forceinline__ void scale_by(double f) {
+    a.x = static_cast<float>(a.x * f); a.y = static_cast<float>(a.y * f);
+    a.z = static_cast<float>(a.z * f); a.w = static_cast<float>(a.w * f);
+    b.x = static_cast<float>(b.x * f); b.y = static_cast<float>(b.y * f);
+    b.z = static_cast<float>(b.z * f); b.w = static_cast<float>(b.w * f);
+  }
+  __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+};
+
+constexpr int kCombineRowBlock = 8;   // packed rows per pass
+constexpr int kCombineMaxChunks = 64; // chunks per combine range (CS / C)
+
 template <typename T>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
   using E = Elem<T>;
   using Acc = typename E::Acc;
+  constexpr int RB = kCombineRowBlock;
+  __shared__ Acc row_m[RB], row_inv_l[RB];
+  __shared__ Acc fac[RB][kCombineMaxChunks];
+  __shared__ Acc seg_w[kCombineThreads];
+  __shared__ Acc ctx_red[kCombineThreads];
+
   const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int64_t ncw = ceil_div(a.M, a.CS);
   const int64_t k = blockIdx.x % ncw;
   const int64_t grp = blockIdx.x / ncw;
@@ -93,6 +140,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
   }
   const int64_t e0 = k * a.CS;
   const int64_t e1 = e0 + a.CS < a.M ? e0 + a.CS : a.M;
+  const int nchunks = static_cast<int>(ceil_div(e1 - e0, a.C));  // chunks in this range
+  const int64_t c0 = e0 / a.C;                                   // first chunk index
 
   if (a.out_of_place && a.combine_copies_tail) {
     const int64_t cover = n > 0 ? len + n : 0;
@@ -109,56 +158,135 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
     }
   }
 
-  StreamSegs ss{0, a.P, 0, 0, grp};
-  if (a.seg_mode && nc > 0) {
-    ss.Nc = a.ws_hdr[0];
-    ss.x0 = a.ws_rowinfo[b * 4 + 3] + kvh * nc;
-    ss.x1 = ss.x0 + nc - 1;
-  }
+  const SegRange sr = group_segments(a, grp, b, kvh, nc);
   const Acc neg_inf = -static_cast<Acc>(INFINITY);
   T* att = static_cast<T*>(a.attention);
   T* ctx = static_cast<T*>(a.context);
   const double* chunk_ml = a.ws_chunk_ml + grp * a.nchunk_max * a.R * 2;
+  // 8-element vectors need 16-byte aligned rows and ranges
+  const bool vec = (reinterpret_cast<uintptr_t>(att) % 16 == 0) && (a.M % 8 == 0) &&
+                   (e0 % 8 == 0);
 
-  for (int r = wave; r < a.R; r += kCombineThreads / kWave) {
-    const int64_t g = r / a.Q, t = r % a.Q;
-    const int64_t row = (b * a.Hq + kvh * a.G + g) * a.Q + t;
-    const bool ctx_owner = (r % ncw) == k;
-    T* arow = att + row * a.M;
-    if (t >= n) {  // invalid row: zero attention and context
-      for (int64_t j = e0 + lane; j < e1; j += kWave) arow[j] = E::zero();
-      if (ctx_owner)
-        for (int64_t dv = lane; dv < a.Dv; dv += kWave) ctx[row * a.Dv + dv] = E::zero();
-      continue;
-    }
-    const int64_t lim = len + t + 1;  // slots [0, lim) are visible
-    const int64_t v1 = e1 < lim ? e1 : lim;
-    if (v1 > e0 || ctx_owner) {
-      const RowStats<Acc> st = row_stats<Acc>(a, grp, nc, ss, r, lane);
-      const Acc inv_l = Acc(1) / st.l;
-      for (int64_t j = e0 + lane; j < v1; j += kWave) {
-        const Acc mc = static_cast<Acc>(chunk_ml[((j / a.C) * a.R + r) * 2]);
-        const Acc f = mc == neg_inf ? Acc(0) : acc_exp(mc - st.m) * inv_l;
-        E::store(arow + j, E::load(arow + j) * f);
-      }
-      if (ctx_owner) {
-        const int64_t k0 = a.seg_mode ? ss.first_w() : 0;
-        const int64_t k1 = a.seg_mode ? ss.last_w() + 1 : nc;
-        for (int64_t dv = lane; dv < a.Dv; dv += kWave) {
-          Acc o = 0;
-          for (int64_t s = k0; s < k1; s++) {
-            if (a.seg_mode && !ss.owns(s)) continue;
-            const int64_t seg = a.seg_mode ? s + grp : grp * a.nchunk_max + s;
-            const Acc mk = static_cast<Acc>(a.ws_seg_ml[(seg * a.R + r) * 2]);
-            if (mk == neg_inf) continue;
-            o += static_cast<Acc>(a.ws_seg_o[(seg * a.R + r) * a.Dv + dv]) * acc_exp(mk - st.m);
-          }
-          E::store(ctx + row * a.Dv + dv, o * inv_l);
+  for (int rb = 0; rb < a.R; rb += RB) {
+    const int nrows = a.R - rb < RB ? static_cast<int>(a.R - rb) : RB;
+    // 1. row statistics (m, 1/l) of the block's valid rows
+    for (int i = wave; i < nrows; i += kCombineThreads / kWave) {
+      const int r = rb + i;
+      const int64_t t = r % a.Q;
+      const bool need = t < n && (len + t + 1 > e0 || (r % ncw) == k);
+      if (need) {
+        const RowStats<Acc> st = row_stats<Acc>(a, sr, r, lane);
+        if (lane == 0) {
+          row_m[i] = st.m;
+          row_inv_l[i] = Acc(1) / st.l;
         }
       }
     }
-    const int64_t z0 = v1 > e0 ? v1 : e0;
-    for (int64_t j = z0 + lane; j < e1; j += kWave) arow[j] = E::zero();
+    __syncthreads();
+    // 2. one factor exp(m_c - m) / l per (row, chunk) of the range
+    for (int idx = tid; idx < nrows * nchunks; idx += kCombineThreads) {
+      const int i = idx / nchunks, cc = idx % nchunks;
+      const int r = rb + i;
+      const int64_t t = r % a.Q;
+      const int64_t ch = c0 + cc;
+      Acc f = 0;
+      if (t < n && ch < nc && ch * a.C <= len + t) {
+        const Acc mc = static_cast<Acc>(chunk_ml[(ch * a.R + r) * 2]);
+        f = mc == neg_inf ? Acc(0) : acc_exp(mc - row_m[i]) * row_inv_l[i];
+      }
+      fac[i][cc] = f;
+    }
+    __syncthreads();
+    // 3. rescale visible slots, zero the rest
+    if (vec) {
+      for (int64_t base = e0 + tid * 8; base < e1; base += kCombineThreads * 8) {
+        const int cc = static_cast<int>((base - e0) / a.C);
+        Vec8<T> x[RB];
+#pragma unroll
+        for (int i = 0; i < RB; i++) {
+          if (i < nrows) {
+            const int r = rb + i;
+            const int64_t g = r / a.Q, t = r % a.Q;
+            const int64_t row = (b * a.Hq + kvh * a.G + g) * a.Q + t;
+            const int64_t lim = t < n ? len + t + 1 : 0;  // visible slots [0, lim)
+            if (base < lim) x[i].load(att + row * a.M + base); else x[i].zero();
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; i++) {
+          if (i < nrows) {
+            const int r = rb + i;
+            const int64_t g = r / a.Q, t = r % a.Q;
+            const int64_t row = (b * a.Hq + kvh * a.G + g) * a.Q + t;
+            const int64_t lim = t < n ? len + t + 1 : 0;
+            if (base < lim) {
+              x[i].scale_by(fac[i][cc]);
+              if (base + 8 > lim) {  // zero the invisible part of this vector
+                T* el = reinterpret_cast<T*>(&x[i]);
+                for (int q = static_cast<int>(lim - base); q < 8; q++) el[q] = E::zero();
+              }
+            }
+            x[i].store(att + row * a.M + base);
+          }
+        }
+      }
+    } else {
+      for (int i = 0; i < nrows; i++) {
+        const int r = rb + i;
+        const int64_t g = r / a.Q, t = r % a.Q;
+        const int64_t row = (b * a.Hq + kvh * a.G + g) * a.Q + t;
+        const int64_t lim = t < n ? len + t + 1 : 0;
+        T* arow = att + row * a.M;
+        for (int64_t j = e0 + tid; j < e1; j += kCombineThreads) {
+          if (j < lim)
+            E::store(arow + j, E::load(arow + j) * fac[i][(j - e0) / a.C]);
+          else
+            arow[j] = E::zero();
+        }
+      }
+    }
+    // 4. context of the rows this range owns: the whole workgroup reduces
+    //    one row at a time, segment weights exp(m_seg - m) / l staged in LDS
+    for (int i = 0; i < nrows; i++) {
+      const int r = rb + i;
+      if ((r % ncw) != k) continue;
+      const int64_t g = r / a.Q, t = r % a.Q;
+      const int64_t row = (b * a.Hq + kvh * a.G + g) * a.Q + t;
+      if (t >= n) {
+        for (int64_t dv = tid; dv < a.Dv; dv += kCombineThreads) ctx[row * a.Dv + dv] = E::zero();
+        continue;
+      }
+      // PARTS threads per dv (Dv < 256) each sum every PARTS-th segment
+      const int parts = a.Dv >= kCombineThreads ? 1 : kCombineThreads / static_cast<int>(a.Dv);
+      for (int64_t dv0 = 0; dv0 < a.Dv; dv0 += kCombineThreads) {
+        const int64_t dv = dv0 + tid % (parts == 1 ? kCombineThreads : a.Dv);
+        const int part = parts == 1 ? 0 : tid / static_cast<int>(a.Dv);
+        Acc o = 0;
+        for (int64_t s0 = 0; s0 < sr.count; s0 += kCombineThreads) {
+          const int64_t ns = sr.count - s0 < kCombineThreads ? sr.count - s0 : kCombineThreads;
+          __syncthreads();
+          if (tid < ns) {
+            const Acc mk = static_cast<Acc>(a.ws_seg_ml[((sr.first + s0 + tid) * a.R + r) * 2]);
+            seg_w[tid] = mk == neg_inf ? Acc(0) : acc_exp(mk - row_m[i]) * row_inv_l[i];
+          }
+          __syncthreads();
+          if (part < parts && dv < a.Dv) {
+            const float* op = a.ws_seg_o + ((sr.first + s0) * a.R + r) * a.Dv + dv;
+#pragma unroll 4
+            for (int64_t s = part; s < ns; s += parts) o += seg_w[s] * static_cast<Acc>(op[s * a.R * a.Dv]);
+          }
+        }
+        __syncthreads();
+        ctx_red[tid] = part < parts ? o : Acc(0);  // slot tid = part * Dv + dv (parts > 1)
+        __syncthreads();
+        if (tid < (parts == 1 ? kCombineThreads : a.Dv) && dv0 + tid < a.Dv) {
+          Acc sum = 0;
+          for (int p = 0; p < parts; p++) sum += ctx_red[p * (parts == 1 ? 0 : a.Dv) + tid];
+          E::store(ctx + row * a.Dv + dv0 + tid, sum);
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 

@@ -64,10 +64,12 @@ __device__ __forceinline__ float acc_exp(float x) { return __expf(x); }
 //   m_seg, l_seg and o_seg = sum_j exp(s_j - m_seg) v_j.
 // Segments are addressed in one of two ways:
 //   seg_mode 0 ("dense"): one segment per chunk, id = g * nchunk_max + c;
-//   seg_mode 1 ("stream"): worker w of P (a wave) owns the chunk range
-//     [floor(w*Nc/P), floor((w+1)*Nc/P)) of the flattened chunk list, and its
-//     segment of group g has id w + g (unique: along the chunk list g and w
-//     never decrease and one of them grows between distinct pairs).
+//   seg_mode 1 ("stream"): worker w of Pe = min(P, Nc) (a wave) owns the
+//     chunk range [floor(w*Nc/Pe), floor((w+1)*Nc/Pe)) of the flattened
+//     chunk list -- never empty, as Pe <= Nc -- and its segment of group g
+//     has id w + g (unique: along the chunk list g and w never decrease and
+//     one of them grows between distinct pairs).  The segments of a group
+//     are therefore the consecutive ids of the workers owning its chunks.
 struct StepArgs {
   int64_t B, Hq, Hk, Q, M, D, Dv;
   int32_t G;          // Hq / Hk
@@ -81,6 +83,7 @@ struct StepArgs {
   int32_t seg_mode;   // 0 dense, 1 stream
   int32_t combine_copies_tail;  // out of place: combine copies slots the attend kernel skips
   double scale;       // resolved softmax scale
+  int64_t elem_bytes; // 4 (fp32) or 2 (bf16)
   int32_t out_of_place;
   const void* query;
   const void* new_key;
@@ -95,11 +98,12 @@ struct StepArgs {
   void* context;
   int64_t* lengths_out;
   int32_t* row_status;
-  int64_t* ws_hdr;       // [8]: [0] total chunk count Nc (stream mode)
+  int64_t* ws_hdr;       // [8]: [0] total chunk count Nc, [1] busy workers Pe (stream mode)
   int64_t* ws_rowinfo;   // [B][4]: length, n, status, first chunk index (stream mode)
   double* ws_chunk_ml;   // [B*Hk][nchunk_max][R][2]: m_c, l_c
   double* ws_seg_ml;     // [nseg][R][2]: m_seg, l_seg
   float* ws_seg_o;       // [nseg][R][Dv]: o_seg
+  int32_t* ws_wstart;    // [P][4]: first (b, head, chunk) of each stream worker
 };
 
 struct RowInfo {

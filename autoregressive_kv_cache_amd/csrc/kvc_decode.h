@@ -6,23 +6,26 @@
 // Work split ("stream-K" over cache slots, per wave): the visible slots of
 // every (batch row, KV head) are cut into chunks of C slots; the flattened
 // chunk list (row-major over b, head, chunk) is divided into equal
-// contiguous ranges, one per wave of the grid, so ragged lengths cost no
-// imbalance and no wave waits for another (there is no workgroup barrier).
-// A wave keeps running softmax statistics across the chunks of one KV head
-// (a "segment") and writes one partial per segment; the combine kernel
-// merges them.
+// contiguous ranges, one per wave, so ragged lengths cost no imbalance and
+// no wave waits for another (there is no workgroup barrier).  A wave keeps
+// running softmax statistics across the chunks of one KV head (a
+// "segment") and writes one partial per segment; the combine kernel merges
+// them.
 //
 // Per chunk a wave
-//   - issues its 16-byte K loads (lane l reads dims [(l % LK)*VEC, +VEC) of
-//     slot l / LK of every 1 KB load, so each load instruction reads
-//     contiguous bytes), computes partial dot products for all packed rows
-//     and reduces them across the LK lanes of a slot with a butterfly
-//     reduce-scatter (each lane ends with whole dot products);
-//   - takes per-row chunk statistics m_c, l_c over its LDS score tile,
-//     writes exp(s - m_c) to the attention buffer and (m_c, l_c) to the
-//     workspace, and folds the chunk into its running segment statistics;
-//   - issues its V loads into the registers K used and accumulates the
-//     context partial o += p * v.
+//   - receives its K rows (16-byte loads issued one chunk ahead: lane l
+//     holds dims [(l % LK)*VEC, +VEC) of slot l / LK of every 1 KB load, so
+//     each load instruction reads contiguous bytes) and its V rows (issued
+//     before the chunk's K math), so loads stay in flight during compute;
+//   - computes partial dot products for every packed row and finishes them
+//     with a butterfly reduce-scatter across the LK lanes of a slot (DPP
+//     lane exchanges); lane (ks, kc) ends with the score of row kc % ROWS;
+//   - takes per-row chunk statistics m_c, l_c (DPP rotations inside each
+//     16-lane row, then lane reads across rows), writes exp(s - m_c) to the
+//     attention buffer and (m_c, l_c) to the workspace, and folds the chunk
+//     into its running segment statistics;
+//   - accumulates the context partial o += p * v (bf16: p rounded to bf16,
+//     two slots per v_dot2; fp32: fp32 FMAs).
 // The same loads feed the cache writes: out of place every visited slot is
 // stored to the output cache (the copy the page's contract requires), in
 // place only the appended rows are stored.
@@ -41,6 +44,97 @@ namespace kvc {
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeWaves = kDecodeThreads / kWave;
 
+// ---- lane exchange -----------------------------------------------------------
+// DPP controls (gfx9): quad permutations, 16-lane row mirror / half mirror
+// and row rotations.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i inside each 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i inside each 16
+constexpr int dpp_row_ror(int n) { return 0x120 + n; }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+  const int2 w = __builtin_bit_cast(int2, v);
+  int2 r;
+  r.x = __builtin_amdgcn_update_dpp(0, w.x, CTRL, 0xF, 0xF, false);
+  r.y = __builtin_amdgcn_update_dpp(0, w.y, CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, r);
+}
+__device__ __forceinline__ float lane_read(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+__device__ __forceinline__ double lane_read(double v, int lane) {
+  const int2 w = __builtin_bit_cast(int2, v);
+  int2 r;
+  r.x = __builtin_amdgcn_readlane(w.x, lane);
+  r.y = __builtin_amdgcn_readlane(w.y, lane);
+  return __builtin_bit_cast(double, r);
+}
+
+// Value held by the lane paired with this one at butterfly step W (an
+// involution that pairs the two W-halves of every 2W-lane group).
+template <int W, typename A>
+__device__ __forceinline__ A partner(A v) {
+  if constexpr (W == 1) return dpp<kDppXor1>(v);
+  else if constexpr (W == 2) return dpp<kDppXor2>(v);
+  else if constexpr (W == 4) return dpp<kDppHalfMirror>(v);
+  else if constexpr (W == 8) return dpp<kDppMirror>(v);
+  else return __shfl_xor(v, W);
+}
+
+// Butterfly reduce-scatter over the W lanes that share one slot: lane kc
+// (its index within those lanes) starts with N partial sums and ends with
+// the complete sums of entries [kc * N / W, (kc + 1) * N / W) in v[0 ..).
+template <int W, int LEN, typename A, int N>
+__device__ __forceinline__ void reduce_scatter(A (&v)[N], int kc) {
+  if constexpr (W >= 1 && LEN >= 2) {
+    const bool upper = (kc & W) != 0;
+#pragma unroll
+    for (int i = 0; i < LEN / 2; i++) {
+      const A lo = v[i], hi = v[i + LEN / 2];
+      const A send = upper ? lo : hi;
+      const A keep = upper ? hi : lo;
+      v[i] = keep + partner<W>(send);
+    }
+    reduce_scatter<W / 2, LEN / 2>(v, kc);
+  }
+}
+
+// Reduce (max or sum) over the lanes of each 16-lane row that are
+// congruent modulo S0 (rotations by S0, 2*S0, ..., 8).
+template <int S, bool MAX, typename A>
+__device__ __forceinline__ A rot_reduce(A v) {
+  if constexpr (S < 16) {
+    const A w = dpp<dpp_row_ror(S)>(v);
+    v = MAX ? (v > w ? v : w) : v + w;
+    return rot_reduce<2 * S, MAX>(v);
+  } else {
+    return v;
+  }
+}
+
+// Per-row results: lane r (r < ROWS) of every 16-lane row holds that row's
+// partial for packed row r after rot_reduce<ROWS>; combine the four rows.
+template <int ROWS, bool MAX, typename A>
+__device__ __forceinline__ void rows_finish(A v, A (&out)[ROWS]) {
+#pragma unroll
+  for (int r = 0; r < ROWS; r++) {
+    A x = lane_read(v, r);
+#pragma unroll
+    for (int k = 1; k < kWave / 16; k++) {
+      const A y = lane_read(v, 16 * k + r);
+      x = MAX ? (x > y ? x : y) : x + y;
+    }
+    out[r] = x;
+  }
+}
+
 // ---- element-type specific pieces ------------------------------------------
 template <typename T>
 struct DecodeMath;
@@ -49,28 +143,18 @@ template <>
 struct DecodeMath<bf16> {
   static constexpr int kVec = 8;  // elements per 16 bytes
   using Acc = float;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  __device__ __forceinline__ static float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+  }
   // sum_i q_i k_i over 8 bf16 pairs with fp32 accumulation (v_dot2 bf16)
   __device__ __forceinline__ static float dot(const uint4& q, const uint4& k) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    float acc = 0.0f;
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.x),
-                                          __builtin_bit_cast(bf16x2, k.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.y),
-                                          __builtin_bit_cast(bf16x2, k.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.z),
-                                          __builtin_bit_cast(bf16x2, k.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w),
-                                          __builtin_bit_cast(bf16x2, k.w), acc, false);
+    float acc = dot2(q.x, k.x, 0.0f);
+    acc = dot2(q.y, k.y, acc);
+    acc = dot2(q.z, k.z, acc);
+    acc = dot2(q.w, k.w, acc);
     return acc;
-  }
-  // o[i] += p * v_i for the 8 bf16 values of v
-  __device__ __forceinline__ static void axpy(float p, const uint4& v, float (&o)[kVec]) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      o[2 * i] += p * __uint_as_float(w[i] << 16);
-      o[2 * i + 1] += p * __uint_as_float(w[i] & 0xffff0000u);
-    }
   }
 };
 
@@ -85,31 +169,7 @@ struct DecodeMath<float> {
     acc += static_cast<double>(__uint_as_float(q.w)) * __uint_as_float(k.w);
     return acc;
   }
-  __device__ __forceinline__ static void axpy(float p, const uint4& v, float (&o)[kVec]) {
-    o[0] += p * __uint_as_float(v.x);
-    o[1] += p * __uint_as_float(v.y);
-    o[2] += p * __uint_as_float(v.z);
-    o[3] += p * __uint_as_float(v.w);
-  }
 };
-
-// Butterfly reduce-scatter over the W lanes that share one slot: lane kc
-// (its index within the W lanes) starts with N partial sums and ends with
-// the complete sums of entries [kc * N / W, (kc + 1) * N / W) in v[0 ..).
-template <int W, int LEN, typename A, int N>
-__device__ __forceinline__ void reduce_scatter(A (&v)[N], int kc) {
-  if constexpr (W >= 1 && LEN >= 2) {
-    const bool upper = (kc & W) != 0;
-#pragma unroll
-    for (int i = 0; i < LEN / 2; i++) {
-      const A lo = v[i], hi = v[i + LEN / 2];
-      const A send = upper ? lo : hi;
-      const A keep = upper ? hi : lo;
-      v[i] = keep + __shfl_xor(send, W);
-    }
-    reduce_scatter<W / 2, LEN / 2>(v, kc);
-  }
-}
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *static_cast<const uint4*>(p); }
 
@@ -121,9 +181,17 @@ __device__ __forceinline__ uint4 ld16(const void* p) { return *static_cast<const
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBufferDword3 = 0x00020000;  // gfx9: 32-bit data format, raw access
 
+// Every descriptor here is built from wave-uniform values; reading them
+// through readfirstlane keeps the descriptor in scalar registers (a
+// descriptor the compiler places in vector registers costs a loop per load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), kBufferDword3);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* q = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, static_cast<short>(0), static_cast<int>(n),
+                                           kBufferDword3);
 }
 __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
@@ -134,15 +202,19 @@ __device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off,
   __builtin_amdgcn_raw_buffer_store_b128(w, r, static_cast<int>(off), 0, 0);
 }
 
-// Chunk size for a (D, Dv) pair: one wave's chunk is at most 16 loads of
-// 16 bytes per lane for K and for V, and at most 64 slots (one per lane in
-// the statistics step).
-template <typename T, int D, int DV>
+// Chunk size: one wave's chunk is at most 64 slots and at most 16 loads of
+// 16 bytes per lane for K and for V (8 when 8 packed rows or fp32 scores
+// need the registers), since both tensors' loads are in flight at once.
+template <typename T, int D, int DV, int ROWS>
 constexpr int decode_chunk() {
   constexpr int E = sizeof(T);
   constexpr int spl_k = kWave / (D * E / 16), spl_v = kWave / (DV * E / 16);
   constexpr int spl = spl_k < spl_v ? spl_k : spl_v;
-  return 16 * spl < kWave ? 16 * spl : kWave;
+#ifndef KVC_DECODE_LOADS
+#define KVC_DECODE_LOADS 16
+#endif
+  constexpr int loads = (E == 4 || ROWS > 4) ? 8 : KVC_DECODE_LOADS;
+  return loads * spl < kWave ? loads * spl : kWave;
 }
 
 // Wave-local ordering of LDS accesses (all lanes of one wave).
@@ -151,67 +223,93 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// One chunk of one cache tensor (K or V, rows of ROWB bytes) for one wave:
-// loads slot jl = u * SPL + lane_slot into buf[u] (cached rows [0, n_old)
-// from the cache, appended rows [n_old, n_all) from the new rows), and
-// writes the visited rows to the output cache (all of them out of place,
-// the appended ones in place).
-template <int U, int SPL, int ROWB>
-__device__ __forceinline__ void chunk_rows(uint4 (&buf)[16], const uint8_t* cache_in,
-                                           uint8_t* cache_out, const uint8_t* new_rows,
-                                           uint32_t lane_off, int n_old, int n_all, bool oop) {
-  const __amdgpu_buffer_rsrc_t rc = make_rsrc(cache_in, static_cast<uint32_t>(n_old) * ROWB);
-#pragma unroll
-  for (int u = 0; u < U; u++) buf[u] = buf_ld16(rc, lane_off + u * SPL * ROWB);
-  const uint32_t shift = static_cast<uint32_t>(n_old) * ROWB;  // appended rows start here
-  if (n_old < n_all) {
-    const __amdgpu_buffer_rsrc_t rn =
-        make_rsrc(new_rows, static_cast<uint32_t>(n_all - n_old) * ROWB);
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-      const uint4 x = buf_ld16(rn, lane_off + u * SPL * ROWB - shift);
-      buf[u].x |= x.x;
-      buf[u].y |= x.y;
-      buf[u].z |= x.z;
-      buf[u].w |= x.w;
-    }
+// The rows of one tensor a chunk visits: cached rows [0, n_old) at
+// `cached` and, out of place, appended rows [n_old, n_all) at `appended`
+// (all counts in bytes).  A zero count makes every load return zeros.
+struct RowSrc {
+  const uint8_t* cached;
+  uint32_t cached_bytes;
+  const uint8_t* appended;
+  uint32_t appended_bytes;
+  uint32_t shift;  // bytes before the first appended row (n_old rows)
+};
+
+// The 16-byte load u of a chunk (slot u * rows-per-load + lane slot; one
+// load covers 1 KB): the descriptor is rebased every 4 loads so that the
+// lane offset plus an immediate below 4 KB addresses the whole group.
+template <bool OOP>
+__device__ __forceinline__ uint4 load_one(const RowSrc& s, int u, uint32_t lane_off) {
+  const uint32_t base = static_cast<uint32_t>(u / 4) * 4096u;
+  const uint32_t imm = static_cast<uint32_t>(u % 4) * 1024u;
+  const uint32_t left = s.cached_bytes > base ? s.cached_bytes - base : 0u;
+  uint4 v = buf_ld16(make_rsrc(s.cached + base, left), lane_off + imm);
+  if constexpr (OOP) {
+    // out-of-range (slots before the appended rows wrap to huge offsets,
+    // slots after them are past the count) lanes read zeros
+    const uint4 x = buf_ld16(make_rsrc(s.appended, s.appended_bytes),
+                             lane_off + base + imm - s.shift);
+    v.x |= x.x;
+    v.y |= x.y;
+    v.z |= x.z;
+    v.w |= x.w;
   }
-  if (oop) {
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(cache_out, static_cast<uint32_t>(n_all) * ROWB);
-#pragma unroll
-    for (int u = 0; u < U; u++) buf_st16(ro, lane_off + u * SPL * ROWB, buf[u]);
-  } else if (n_old < n_all) {
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(cache_out + shift,
-                                                static_cast<uint32_t>(n_all - n_old) * ROWB);
-#pragma unroll
-    for (int u = 0; u < U; u++) buf_st16(ro, lane_off + u * SPL * ROWB - shift, buf[u]);
-  }
+  return v;
 }
 
-template <typename T, int D, int DV, int ROWS, bool Q1>
-__global__ __launch_bounds__(kDecodeThreads) void attend_decode_kernel(StepArgs a) {
+// Out of place: the copy of cached rows to the output cache (load u of the
+// chunk, same addressing as load_one; the appended rows are already there).
+__device__ __forceinline__ void store_one(uint8_t* out, uint32_t cached_bytes, int u,
+                                          uint32_t lane_off, const uint4& v) {
+  const uint32_t base = static_cast<uint32_t>(u / 4) * 4096u;
+  const uint32_t imm = static_cast<uint32_t>(u % 4) * 1024u;
+  const uint32_t left = cached_bytes > base ? cached_bytes - base : 0u;
+  buf_st16(make_rsrc(out + base, left), lane_off + imm, v);
+}
+
+// Position of a wave in the flattened chunk list (all fields wave-uniform).
+struct ChunkPos {
+  int b, kvh, c;   // batch row, KV head, chunk within the head
+  int len, n, nc;  // the row's old length, appended rows, chunks per head
+};
+
+#ifndef KVC_DECODE_WAVES_PER_EU
+#define KVC_DECODE_WAVES_PER_EU 2
+#endif
+
+template <typename T, int D, int DV, int ROWS, bool Q1, bool OOP>
+__global__ __launch_bounds__(kDecodeThreads)
+__attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode_kernel(
+    StepArgs a, const int64_t* __restrict__ rowinfo, const int32_t* __restrict__ wstart) {
   using Mth = DecodeMath<T>;
   using Acc = typename Mth::Acc;
+  constexpr bool kBf16 = sizeof(T) == 2;
   constexpr int E = sizeof(T);
   constexpr int VEC = Mth::kVec;
   constexpr int LK = D * E / 16, SPLK = kWave / LK;   // lanes per K row, K rows per load
   constexpr int LV = DV * E / 16, SPLV = kWave / LV;  // same for V
-  constexpr int C = decode_chunk<T, D, DV>();         // slots per chunk (one wave)
+  constexpr int C = decode_chunk<T, D, DV, ROWS>();   // slots per chunk (one wave)
   constexpr int UK = C / SPLK, UV = C / SPLV;         // 16-byte loads per lane
-  constexpr int GU = LK / ROWS > 1 ? LK / ROWS : 1;   // loads per reduce-scatter group
-  constexpr int NV = GU * ROWS;                       // partial dots per group
-  constexpr int KPL = NV / LK;                        // finished dots per lane
+  constexpr int GU = LK / ROWS;                       // loads per reduce-scatter group
+  constexpr int NG = UK / GU;                         // reduce-scatter groups per chunk
   constexpr int KROW = D * E, VROW = DV * E;          // row bytes
   static_assert(D * E % 16 == 0 && DV * E % 16 == 0 && LK <= kWave && LV <= kWave, "head size");
+  static_assert(LK >= ROWS && LK % ROWS == 0 && ROWS < 16, "one finished dot product per lane");
   static_assert(UK >= 1 && UK <= 16 && UV >= 1 && UV <= 16 && UK % GU == 0, "chunk shape");
-  static_assert(NV % LK == 0 && KPL >= 1 && C <= kWave, "row shape");
+  static_assert(!kBf16 || (D == DV && UV % 2 == 0), "bf16 context pairs slots of equal layout");
+  static_assert(SPLK * KROW == 1024 && SPLV * VROW == 1024, "one load covers 1 KB");
+  // probabilities for the context step: bf16 pairs [slot pair][slot lane][row]
+  // (packed bf16x2), or fp32 [row][slot]
+  constexpr int PTILE = kBf16 ? (UV / 2) * SPLV * ROWS : ROWS * C;
+  __shared__ uint32_t ptile_all[kDecodeWaves][PTILE];
 
-  __shared__ Acc sc_all[kDecodeWaves][ROWS][C];
-
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  Acc (*sc)[C] = sc_all[wave];
+  const int tid = threadIdx.x, lane = tid % kWave;
+  // the wave index is uniform across the wave; saying so keeps everything
+  // derived from it (chunk range, rows, buffer descriptors) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  uint32_t* ptile = ptile_all[wave];
   const int ks = lane / LK, kc = lane % LK;
   const int vs = lane / LV, vc = lane % LV;
+  const int my_row = kc % ROWS;  // packed row whose scores this lane finishes
   const uint32_t k_off = static_cast<uint32_t>(ks * KROW + kc * 16);
   const uint32_t v_off = static_cast<uint32_t>(vs * VROW + vc * 16);
   const Acc neg_inf = -static_cast<Acc>(INFINITY);
@@ -221,43 +319,80 @@ __global__ __launch_bounds__(kDecodeThreads) void attend_decode_kernel(StepArgs 
   const int Hk = static_cast<int>(a.Hk);
   const int64_t M = a.M;
 
+  // rowinfo and the header are written by the prep kernel and only read
+  // here; hdr: [0] total chunks, [1] busy stream workers (<= Nc, <= waves)
   const int64_t Nc = a.ws_hdr[0];
-  const int64_t Pw = a.P;  // stream workers = waves of the grid
+  const int64_t Pw = a.ws_hdr[1];
   const int64_t w = blockIdx.x * static_cast<int64_t>(kDecodeWaves) + wave;
+  if (w >= Pw) return;
   const int64_t x_begin = w * Nc / Pw, x_end = (w + 1) * Nc / Pw;
-  if (x_begin >= x_end) return;
+  if (x_begin >= x_end) return;  // no chunks at all (Nc = 0)
 
-  // locate the first chunk: the last row whose first chunk index <= x_begin
-  int lo = 0, hi = static_cast<int>(a.B) - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) / 2;
-    if (a.ws_rowinfo[mid * 4 + 3] <= x_begin) lo = mid; else hi = mid - 1;
-  }
-  int b = lo;
-  int len = static_cast<int>(a.ws_rowinfo[b * 4 + 0]);
-  int n = static_cast<int>(a.ws_rowinfo[b * 4 + 1]);
-  int nc = static_cast<int>(row_chunks(len, n, C));
-  int kvh, c;
+  // first chunk of this worker (found by the prep kernel)
+  ChunkPos pos;
   {
-    const int rel = static_cast<int>(x_begin - a.ws_rowinfo[b * 4 + 3]);
-    kvh = rel / nc;
-    c = rel % nc;
+    const int4 st = *reinterpret_cast<const int4*>(wstart + w * 4);
+    pos.b = st.x;
+    pos.kvh = st.y;
+    pos.c = st.z;
+    pos.len = static_cast<int>(rowinfo[pos.b * 4 + 0]);
+    pos.n = static_cast<int>(rowinfo[pos.b * 4 + 1]);
+    pos.nc = static_cast<int>(row_chunks(pos.len, pos.n, C));
   }
 
-  const T* qbase = static_cast<const T*>(a.query);
+  const uint8_t* qbase = static_cast<const uint8_t*>(a.query);
   const uint8_t* kin = static_cast<const uint8_t*>(a.kc_in);
   const uint8_t* vin = static_cast<const uint8_t*>(a.vc_in);
   uint8_t* kout = static_cast<uint8_t*>(a.kc_out);
   uint8_t* vout = static_cast<uint8_t*>(a.vc_out);
-  const uint8_t* nkb = static_cast<const uint8_t*>(a.new_key);
-  const uint8_t* nvb = static_cast<const uint8_t*>(a.new_value);
   T* att = static_cast<T*>(a.attention);
-  const bool oop = a.out_of_place != 0;
+
+  auto grp_of = [&](const ChunkPos& p) { return static_cast<int64_t>(p.b) * Hk + p.kvh; };
+  auto n_all_of = [&](const ChunkPos& p) {
+    const int j0 = p.c * C, new_len = p.len + p.n;
+    return (j0 + C < new_len ? j0 + C : new_len) - j0;
+  };
+  auto n_old_of = [&](const ChunkPos& p, int n_all) {
+    const int d = p.len - p.c * C;
+    return d < 0 ? 0 : (d < n_all ? d : n_all);
+  };
+  // The rows a chunk visits.  The prep kernel has already written the
+  // appended rows into the output cache: in place every visited slot is read
+  // from the cache; out of place the cached slots come from the input cache
+  // and the appended ones from the output cache.  live = false (past the last
+  // chunk): zero rows, so every path through the loop issues the same loads.
+  auto src_of = [&](const ChunkPos& p, bool live, const uint8_t* cin, const uint8_t* cout,
+                    int rowb) {
+    RowSrc r{cin, 0u, cout, 0u, 0u};
+    if (live) {
+      const int64_t g = grp_of(p);
+      const int j0 = p.c * C, n_all = n_all_of(p), n_old = n_old_of(p, n_all);
+      const int cached_rows = OOP ? n_old : n_all;
+      r.cached = cin + (g * M + j0) * rowb;
+      r.cached_bytes = static_cast<uint32_t>(cached_rows) * rowb;
+      r.appended = cout + (g * M + j0 + n_old) * rowb;
+      r.appended_bytes = OOP ? static_cast<uint32_t>(n_all - n_old) * rowb : 0u;
+      r.shift = static_cast<uint32_t>(n_old) * rowb;
+    }
+    return r;
+  };
+  // q rows of a chunk's KV head (rows that are padding or not appended read
+  // zeros; live = false reads zeros everywhere)
+  auto load_q = [&](uint4 (&qv)[ROWS], const ChunkPos& p, bool live) {
+#pragma unroll
+    for (int r = 0; r < ROWS; r++) {
+      const int t = Q1 ? 0 : r % Q;
+      const int g = Q1 ? r : r / Q;
+      const bool valid = live && r < R && t < p.n;
+      const int64_t row = valid ? (static_cast<int64_t>(p.b) * a.Hq + p.kvh * a.G + g) * Q + t : 0;
+      qv[r] = buf_ld16(make_rsrc(qbase + row * KROW, valid ? KROW : 0u), kc * 16u);
+    }
+  };
 
   uint4 qf[ROWS];
+  uint4 kbuf[16], vbuf[16];
   float o_acc[ROWS][VEC];
   Acc seg_m[ROWS], seg_l[ROWS];
-  bool new_group = true;
 #pragma unroll
   for (int r = 0; r < ROWS; r++) {
     seg_m[r] = neg_inf;
@@ -265,118 +400,208 @@ __global__ __launch_bounds__(kDecodeThreads) void attend_decode_kernel(StepArgs 
 #pragma unroll
     for (int i = 0; i < VEC; i++) o_acc[r][i] = 0.0f;
   }
+  load_q(qf, pos, true);
+  {
+    const RowSrc sk = src_of(pos, true, kin, kout, KROW);
+    const RowSrc sv = src_of(pos, true, vin, vout, VROW);
+#pragma unroll
+    for (int u = 0; u < UK; u++) kbuf[u] = load_one<OOP>(sk, u, k_off);
+#pragma unroll
+    for (int u = 0; u < UV; u++) vbuf[u] = load_one<OOP>(sv, u, v_off);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
   for (int64_t x = x_begin; x < x_end; x++) {
-    const int64_t grp = static_cast<int64_t>(b) * Hk + kvh;
-    const int j0 = c * C;
-    const int new_len = len + n;
-    const int j1 = j0 + C < new_len ? j0 + C : new_len;  // chunk end
-    const int n_all = j1 - j0;                           // visited slots
-    const int n_old = len - j0 < 0 ? 0 : (len - j0 < n_all ? len - j0 : n_all);  // cached ones
-    if (new_group) {
-#pragma unroll
-      for (int r = 0; r < ROWS; r++) {
-        const int t = Q1 ? 0 : r % Q;
-        const int g = Q1 ? r : r / Q;
-        const bool valid = r < R && t < n;
-        const int64_t row = (static_cast<int64_t>(b) * a.Hq + kvh * a.G + g) * Q + t;
-        qf[r] = valid ? ld16(qbase + row * D + kc * VEC) : make_uint4(0, 0, 0, 0);
-      }
-      new_group = false;
-    }
+    const int64_t grp = grp_of(pos);
+    const int j0 = pos.c * C;
+    const int n_all = n_all_of(pos);         // visited slots of the chunk
+    const int n_old = n_old_of(pos, n_all);  // cached ones; [n_old, n_all) are appended
 
-    // ---- K rows of the chunk: loads, cache writes, scores ----
-    uint4 buf[16];
-    chunk_rows<UK, SPLK, KROW>(buf, kin + (grp * M + j0) * KROW, kout + (grp * M + j0) * KROW,
-                               nkb + (grp * a.Q + (j0 + n_old - len)) * KROW, k_off, n_old,
-                               n_all, oop);
-#pragma unroll
-    for (int g0 = 0; g0 < UK; g0 += GU) {
-      Acc part[NV];
-#pragma unroll
-      for (int gu = 0; gu < GU; gu++)
-#pragma unroll
-        for (int r = 0; r < ROWS; r++) part[gu * ROWS + r] = Mth::dot(qf[r], buf[g0 + gu]);
-      reduce_scatter<LK / 2, NV>(part, kc);
-#pragma unroll
-      for (int k = 0; k < KPL; k++) {
-        const int i = kc * KPL + k;
-        const int gu = i / ROWS, r = i % ROWS;
-        const int jl = (g0 + gu) * SPLK + ks;
-        // visible: an existing row r (< R) whose token t is appended
-        // (t < n) and slot j0 + jl <= len + t
-        const int t = Q1 ? 0 : r % Q;
-        const bool ok = r < R && t < n && jl < n_all && j0 + jl <= len + t;
-        sc[r][jl] = ok ? part[k] * scale : neg_inf;
+    // ---- the next chunk: its position and sources ----
+    ChunkPos nxt = pos;
+    bool group_ends = false;
+    nxt.c++;
+    if (nxt.c == nxt.nc) {
+      group_ends = true;
+      nxt.c = 0;
+      nxt.kvh++;
+      if (nxt.kvh == Hk) {
+        nxt.kvh = 0;
+        do {
+          nxt.b++;
+          if (nxt.b >= a.B) break;
+          nxt.len = static_cast<int>(rowinfo[nxt.b * 4 + 0]);
+          nxt.n = static_cast<int>(rowinfo[nxt.b * 4 + 1]);
+          nxt.nc = static_cast<int>(row_chunks(nxt.len, nxt.n, C));
+        } while (nxt.nc == 0);
       }
     }
-    wave_lds_sync();
+    const bool more = x + 1 < x_end;
+    const RowSrc nk = src_of(nxt, more, kin, kout, KROW);
+    const RowSrc nv = src_of(nxt, more, vin, vout, VROW);
 
-    // ---- chunk statistics, attention values, segment update ----
-    Acc alpha[ROWS];
+    // ---- K: scores; each group's registers reload the next chunk's K ----
+    Acc sc[NG];  // this lane's finished scores: packed row my_row, one per group
+    {
+      const int t = Q1 ? 0 : my_row % Q;
+      const bool row_ok = my_row < R && t < pos.n;
+#pragma unroll
+      for (int g = 0; g < NG; g++) {
+        if constexpr (OOP) {
+#pragma unroll
+          for (int gu = 0; gu < GU; gu++)
+            store_one(kout + (grp * M + j0) * KROW, static_cast<uint32_t>(n_old) * KROW,
+                      g * GU + gu, k_off, kbuf[g * GU + gu]);
+        }
+        Acc part[LK];
+#pragma unroll
+        for (int gu = 0; gu < GU; gu++)
+#pragma unroll
+          for (int r = 0; r < ROWS; r++) part[gu * ROWS + r] = Mth::dot(qf[r], kbuf[g * GU + gu]);
+#pragma unroll
+        for (int gu = 0; gu < GU; gu++) kbuf[g * GU + gu] = load_one<OOP>(nk, g * GU + gu, k_off);
+        __builtin_amdgcn_sched_barrier(0);
+        reduce_scatter<LK / 2, LK>(part, kc);
+        // visible: an existing row whose token t is appended (t < n) and
+        // slot j0 + jl <= len + t
+        const int jl = (g * GU + kc / ROWS) * SPLK + ks;
+        const bool ok = row_ok && jl < n_all && j0 + jl <= pos.len + t;
+        sc[g] = ok ? part[0] * scale : neg_inf;
+      }
+    }
+    // q is dead until the next chunk's scores: reload it for that chunk now
+    // (the same rows unless the KV head changes; they stay in the caches)
+    load_q(qf, nxt, more);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- chunk statistics per row, segment update ----
+    Acc m_c[ROWS], l_c[ROWS];
+    {
+      Acc mloc = sc[0];
+#pragma unroll
+      for (int g = 1; g < NG; g++) mloc = sc[g] > mloc ? sc[g] : mloc;
+      rows_finish<ROWS, true>(rot_reduce<ROWS, true>(mloc), m_c);
+    }
+    Acc my_m = m_c[0];
+#pragma unroll
+    for (int r = 1; r < ROWS; r++) my_m = my_row == r ? m_c[r] : my_m;
+    Acc p[NG];
+    {
+      Acc lloc = 0;
+#pragma unroll
+      for (int g = 0; g < NG; g++) {
+        p[g] = sc[g] == neg_inf ? Acc(0) : acc_exp(sc[g] - my_m);
+        lloc += p[g];
+      }
+      rows_finish<ROWS, false>(rot_reduce<ROWS, false>(lloc), l_c);
+    }
+    Acc alpha[ROWS], beta[ROWS];
 #pragma unroll
     for (int r = 0; r < ROWS; r++) {
-      const Acc s = lane < C ? sc[r][lane] : neg_inf;
-      const Acc m = wave_max(s);
-      const Acc p = s == neg_inf ? Acc(0) : acc_exp(s - m);
-      const Acc l = wave_sum(p);
-      const Acc m_new = m > seg_m[r] ? m : seg_m[r];
+      const Acc m_new = m_c[r] > seg_m[r] ? m_c[r] : seg_m[r];
       alpha[r] = seg_m[r] == neg_inf ? Acc(0) : acc_exp(seg_m[r] - m_new);
-      const Acc beta = m == neg_inf ? Acc(0) : acc_exp(m - m_new);
-      seg_l[r] = seg_l[r] * alpha[r] + l * beta;
+      beta[r] = m_c[r] == neg_inf ? Acc(0) : acc_exp(m_c[r] - m_new);
+      seg_l[r] = seg_l[r] * alpha[r] + l_c[r] * beta[r];
       seg_m[r] = m_new;
       const int t = Q1 ? 0 : r % Q;
-      if (r < R && t < n) {
-        const int g = Q1 ? r : r / Q;
-        const int64_t row = (static_cast<int64_t>(b) * a.Hq + kvh * a.G + g) * Q + t;
-        if (lane < n_all) Elem<T>::store(att + row * M + j0 + lane, p);
-        if (lane == 0) {
-          double* cm = a.ws_chunk_ml + ((grp * a.nchunk_max + c) * R + r) * 2;
-          cm[0] = static_cast<double>(m);
-          cm[1] = static_cast<double>(l);
+      if (r < R && t < pos.n && lane == 0) {
+        double* cm = a.ws_chunk_ml + ((grp * a.nchunk_max + pos.c) * R + r) * 2;
+        cm[0] = static_cast<double>(m_c[r]);
+        cm[1] = static_cast<double>(l_c[r]);
+      }
+    }
+    // attention values exp(s - m_c), context weights p * beta into the tile
+    {
+      const int t = Q1 ? 0 : my_row % Q;
+      const int g_q = Q1 ? my_row : my_row / Q;
+      const bool row_ok = my_row < R && t < pos.n;
+      const int64_t row = (static_cast<int64_t>(pos.b) * a.Hq + pos.kvh * a.G + g_q) * Q + t;
+      T* arow = att + row * M + j0;
+      Acc my_beta = beta[0];
+#pragma unroll
+      for (int r = 1; r < ROWS; r++) my_beta = my_row == r ? beta[r] : my_beta;
+#pragma unroll
+      for (int g = 0; g < NG; g++) {
+        const int u = g * GU + kc / ROWS;  // load index of this lane's slot
+        const int jl = u * SPLK + ks;
+        if (row_ok && jl < n_all) Elem<T>::store(arow + jl, p[g]);
+        if constexpr (kBf16) {
+          uint16_t* ph = reinterpret_cast<uint16_t*>(ptile);
+          ph[(((u / 2) * SPLV + ks) * ROWS + my_row) * 2 + (u & 1)] =
+              f32_to_bf16(static_cast<float>(p[g] * my_beta));
+        } else {
+          reinterpret_cast<float*>(ptile)[my_row * C + jl] = static_cast<float>(p[g] * my_beta);
         }
       }
-      if (lane < C) sc[r][lane] = p * beta;
     }
     wave_lds_sync();
 
-    // ---- V rows of the chunk (same registers), cache writes, context ----
-    chunk_rows<UV, SPLV, VROW>(buf, vin + (grp * M + j0) * VROW, vout + (grp * M + j0) * VROW,
-                               nvb + (grp * a.Q + (j0 + n_old - len)) * VROW, v_off, n_old,
-                               n_all, oop);
+    // ---- V: context partials; each pair's registers reload the next V ----
 #pragma unroll
     for (int r = 0; r < ROWS; r++) {
       const float al = static_cast<float>(alpha[r]);
 #pragma unroll
       for (int i = 0; i < VEC; i++) o_acc[r][i] *= al;
     }
+    if constexpr (kBf16) {
 #pragma unroll
-    for (int u = 0; u < UV; u++) {
-      const int jl = u * SPLV + vs;  // p is 0 for slots past the chunk end
+      for (int j = 0; j < UV / 2; j++) {
+        if constexpr (OOP) {
+          store_one(vout + (grp * M + j0) * VROW, static_cast<uint32_t>(n_old) * VROW, 2 * j,
+                    v_off, vbuf[2 * j]);
+          store_one(vout + (grp * M + j0) * VROW, static_cast<uint32_t>(n_old) * VROW, 2 * j + 1,
+                    v_off, vbuf[2 * j + 1]);
+        }
+        uint32_t pp[ROWS];
 #pragma unroll
-      for (int r = 0; r < ROWS; r++) Mth::axpy(static_cast<float>(sc[r][jl]), buf[u], o_acc[r]);
+        for (int r = 0; r < ROWS; r++) pp[r] = ptile[(j * SPLV + vs) * ROWS + r];
+        // (v[slot 2j][d], v[slot 2j+1][d]) for d = 2e (lo) and d = 2e + 1 (hi)
+        const uint32_t w0[4] = {vbuf[2 * j].x, vbuf[2 * j].y, vbuf[2 * j].z, vbuf[2 * j].w};
+        const uint32_t w1[4] = {vbuf[2 * j + 1].x, vbuf[2 * j + 1].y, vbuf[2 * j + 1].z,
+                                vbuf[2 * j + 1].w};
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          lo[e] = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
+          hi[e] = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
+        }
+        // the registers are free again: the next chunk's V goes into them
+        // (a load into a register still in use would need a copy per chunk)
+        vbuf[2 * j] = load_one<OOP>(nv, 2 * j, v_off);
+        vbuf[2 * j + 1] = load_one<OOP>(nv, 2 * j + 1, v_off);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+#pragma unroll
+          for (int r = 0; r < ROWS; r++) {
+            o_acc[r][2 * e] = Mth::dot2(pp[r], lo[e], o_acc[r][2 * e]);
+            o_acc[r][2 * e + 1] = Mth::dot2(pp[r], hi[e], o_acc[r][2 * e + 1]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < UV; u++) {
+        if constexpr (OOP)
+          store_one(vout + (grp * M + j0) * VROW, static_cast<uint32_t>(n_old) * VROW, u, v_off,
+                    vbuf[u]);
+        const int jl = u * SPLV + vs;
+#pragma unroll
+        for (int r = 0; r < ROWS; r++) {
+          const float pr = reinterpret_cast<const float*>(ptile)[r * C + jl];
+          o_acc[r][0] += pr * __uint_as_float(vbuf[u].x);
+          o_acc[r][1] += pr * __uint_as_float(vbuf[u].y);
+          o_acc[r][2] += pr * __uint_as_float(vbuf[u].z);
+          o_acc[r][3] += pr * __uint_as_float(vbuf[u].w);
+        }
+        vbuf[u] = load_one<OOP>(nv, u, v_off);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     wave_lds_sync();  // the next chunk overwrites the tile
 
-    // ---- advance; flush the segment when the KV head changes or at the end ----
-    const int64_t prev_grp = grp;
-    c++;
-    if (c == nc) {
-      c = 0;
-      kvh++;
-      new_group = true;
-      if (kvh == Hk) {
-        kvh = 0;
-        do {
-          b++;
-          if (b >= a.B) break;
-          len = static_cast<int>(a.ws_rowinfo[b * 4 + 0]);
-          n = static_cast<int>(a.ws_rowinfo[b * 4 + 1]);
-          nc = static_cast<int>(row_chunks(len, n, C));
-        } while (nc == 0);
-      }
-    }
-    if (new_group || x + 1 == x_end) {
+    // ---- flush the segment when the KV head changes or at the end ----
+    if (group_ends || !more) {
       // sum o over the lanes that hold the same dims
 #pragma unroll
       for (int off = LV; off < kWave; off <<= 1)
@@ -384,7 +609,7 @@ __global__ __launch_bounds__(kDecodeThreads) void attend_decode_kernel(StepArgs 
         for (int r = 0; r < ROWS; r++)
 #pragma unroll
           for (int i = 0; i < VEC; i++) o_acc[r][i] += __shfl_xor(o_acc[r][i], off);
-      const int64_t seg = w + prev_grp;
+      const int64_t seg = w + grp;
       if (vs == 0) {
 #pragma unroll
         for (int r = 0; r < ROWS; r++) {
@@ -413,6 +638,7 @@ __global__ __launch_bounds__(kDecodeThreads) void attend_decode_kernel(StepArgs 
         for (int i = 0; i < VEC; i++) o_acc[r][i] = 0.0f;
       }
     }
+    pos = nxt;
   }
 }
 

@@ -1,13 +1,21 @@
-// kvc_prep.h -- row preparation for the stream-mode attend kernel.
+// kvc_prep.h -- row preparation and the append for the stream path.
 //
-// One workgroup computes, for every batch row b, the row information of
+// Workgroups 0 .. B-1: workgroup b works out row b's information as
 // "Autoregressive KV-cache append and causal attention" (Required
-// behavior: n = count of the True prefix of append_mask[b,:], 0 <= length
-// <= M, length + n <= M; a broken row becomes a no-op with a status), the
-// number of C-slot chunks each of its KV heads needs, and the exclusive
-// prefix sum of Hk * chunks over b (the row's first index in the flattened
-// chunk list).  Its output is all the attend and combine kernels read about
-// lengths and masks, so lengths_out may alias lengths.
+// behavior) defines it -- n = count of the True prefix of append_mask[b,:],
+// 0 <= length <= M, length + n <= M; a broken row becomes a no-op with a
+// status -- and writes new_key/new_value row t to slot length + t of the
+// destination cache for every KV head (the append itself; nothing else of
+// the cache is touched here).
+//
+// Workgroup B: the same row information for all rows, the number of C-slot
+// chunks each KV head needs, the exclusive prefix sum of Hk * chunks over b
+// (each row's first index in the flattened chunk list), the number of busy
+// stream workers Pe = min(P, Nc), and each worker's first chunk.
+//
+// After this kernel the attend and combine kernels read row information
+// only from the workspace, so lengths_out may alias lengths, and the
+// in-place attend kernel finds the appended rows in the cache.
 #pragma once
 
 #include "kvc_common.h"
@@ -19,7 +27,36 @@ constexpr int kPrepThreads = 1024;
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(StepArgs a) {
   __shared__ int64_t wave_total[kPrepThreads / kWave];
   __shared__ int64_t carry_sh;
+  __shared__ RowInfo info_sh;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+
+  if (blockIdx.x < a.B) {
+    // ---- the append of batch row b ----
+    const int64_t b = blockIdx.x;
+    if (wave == 0) {
+      const RowInfo ri = wave_row_info(a.lengths, a.mask, a.Q, a.M, b);
+      if (lane == 0) info_sh = ri;
+    }
+    __syncthreads();
+    const RowInfo ri = info_sh;
+    if (ri.n <= 0) return;
+    const int64_t esz = a.elem_bytes;
+    for (int which = 0; which < 2; which++) {
+      const int64_t rowb = (which == 0 ? a.D : a.Dv) * esz;  // bytes per row (multiple of 16)
+      const int64_t n16 = rowb / 16;
+      const uint4* src = static_cast<const uint4*>(which == 0 ? a.new_key : a.new_value);
+      uint4* dst = static_cast<uint4*>(which == 0 ? a.kc_out : a.vc_out);
+      const int64_t total = a.Hk * ri.n * n16;
+      for (int64_t i = tid; i < total; i += kPrepThreads) {
+        const int64_t h = i / (ri.n * n16), rem = i % (ri.n * n16);
+        const int64_t t = rem / n16, k = rem % n16;
+        dst[((b * a.Hk + h) * a.M + ri.len + t) * n16 + k] = src[((b * a.Hk + h) * a.Q + t) * n16 + k];
+      }
+    }
+    return;
+  }
+
+  // ---- row information, chunk offsets and worker starts ----
   if (tid == 0) carry_sh = 0;
   __syncthreads();
   for (int64_t base = 0; base < a.B; base += kPrepThreads) {
@@ -52,7 +89,31 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(StepArgs a) {
     if (tid == kPrepThreads - 1) carry_sh = before + incl;
     __syncthreads();
   }
-  if (tid == 0) a.ws_hdr[0] = carry_sh;
+  const int64_t Nc = carry_sh;
+  // stream workers that get work: at most one per chunk, so that every one
+  // of them owns at least one chunk
+  const int64_t Pe = Nc < a.P ? (Nc > 0 ? Nc : 1) : a.P;
+  if (tid == 0) {
+    a.ws_hdr[0] = Nc;
+    a.ws_hdr[1] = Pe;
+  }
+  if (Nc == 0) return;
+  // first chunk of each worker: x = floor(w * Nc / Pe) -> (b, head, chunk)
+  for (int64_t wk = tid; wk < Pe; wk += kPrepThreads) {
+    const int64_t x = wk * Nc / Pe;
+    int64_t lo = 0, hi = a.B - 1;  // last row whose first chunk index <= x
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) / 2;
+      if (a.ws_rowinfo[mid * 4 + 3] <= x) lo = mid; else hi = mid - 1;
+    }
+    const int64_t nc = row_chunks(a.ws_rowinfo[lo * 4 + 0], a.ws_rowinfo[lo * 4 + 1], a.C);
+    const int64_t rel = x - a.ws_rowinfo[lo * 4 + 3];
+    int32_t* ws = a.ws_wstart + wk * 4;
+    ws[0] = static_cast<int32_t>(lo);
+    ws[1] = static_cast<int32_t>(rel / nc);
+    ws[2] = static_cast<int32_t>(rel % nc);
+    ws[3] = 0;
+  }
 }
 
 }  // namespace kvc

@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--workload", default="decode_gqa_bf16")
     p.add_argument("--mode", choices=["inplace", "oop"], default="inplace")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--copies", type=int, default=4,
+                   help="independent input sets the steps rotate over (each step reads data "
+                        "the previous steps did not, as the layers of a model would)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU oracle time budget for the baseline sample")
@@ -183,43 +186,56 @@ def main():
     torch.cuda.set_device(dev)
     wl = WORKLOADS[args.workload]
     lengths, n = draw_lengths_and_counts(wl, args.seed)
-    inp = make_inputs(wl, args.seed, dev, lengths=lengths, n=n)
-    q, nk, nv, kc, vc = (inp[k] for k in ("query", "new_key", "new_value", "key_cache",
-                                          "value_cache"))
-    lens = inp["lengths"]
-    mask = inp["append_mask"].contiguous().view(torch.uint8)
-    att = torch.empty(wl.B, wl.Hq, wl.Q, wl.M, dtype=kc.dtype, device=dev)
-    ctx = torch.empty(wl.B, wl.Hq, wl.Q, wl.Dv, dtype=kc.dtype, device=dev)
-    lens_out = torch.empty_like(lens)
-    status = torch.empty(wl.B, dtype=torch.int32, device=dev)
-    dims = kvc.dims_of(q, kc, vc)
-    dt = kvc.dtype_code(kc.dtype)
+    # `copies` independent input sets with the same lengths and masks (one
+    # per "layer"), so that a step never re-reads the previous step's K/V
+    # from the 256 MB last-level cache
+    sets = []
+    for k in range(max(1, args.copies)):
+        inp = make_inputs(wl, args.seed + 1000 * k, dev, lengths=lengths, n=n)
+        d = {key: inp[key] for key in ("query", "new_key", "new_value", "key_cache",
+                                        "value_cache", "lengths")}
+        d["mask"] = inp["append_mask"].contiguous().view(torch.uint8)
+        d["att"] = torch.empty(wl.B, wl.Hq, wl.Q, wl.M, dtype=inp["key_cache"].dtype, device=dev)
+        d["ctx"] = torch.empty(wl.B, wl.Hq, wl.Q, wl.Dv, dtype=inp["key_cache"].dtype, device=dev)
+        d["lens_out"] = torch.empty_like(inp["lengths"])
+        d["status"] = torch.empty(wl.B, dtype=torch.int32, device=dev)
+        if args.mode == "oop":
+            d["kc_out"] = torch.empty_like(inp["key_cache"])
+            d["vc_out"] = torch.empty_like(inp["value_cache"])
+        sets.append(d)
+        if k == 0:
+            first_inputs = inp
+    q0, kc0, vc0 = sets[0]["query"], sets[0]["key_cache"], sets[0]["value_cache"]
+    dims = kvc.dims_of(q0, kc0, vc0)
+    dt = kvc.dtype_code(kc0.dtype)
     plan = kvc.kvc_plan_step(dims, dt)
     ws = kvc.workspace_for(dims, dt, dev)
-    if args.mode == "oop":
-        kc_out, vc_out = torch.empty_like(kc), torch.empty_like(vc)
 
     ev = HipEvents()
     starts = [ev.create() for _ in range(args.steps)]
     stops = [ev.create() for _ in range(args.steps)]
 
-    def step(i=None):
+    def step(i=None, k=0):
+        d = sets[k % len(sets)]
         events = None if i is None else (starts[i], stops[i])
         if args.mode == "inplace":
-            kvc.kvc_step_inplace(q, nk, nv, kc, vc, lens, mask, lens_out, att, ctx, status,
-                                 workspace=ws, scale=wl.scale, events=events)
+            kvc.kvc_step_inplace(d["query"], d["new_key"], d["new_value"], d["key_cache"],
+                                 d["value_cache"], d["lengths"], d["mask"], d["lens_out"],
+                                 d["att"], d["ctx"], d["status"], workspace=ws, scale=wl.scale,
+                                 events=events)
         else:
-            kvc.kvc_step_out_of_place(q, nk, nv, kc, vc, lens, mask, kc_out, vc_out, lens_out,
-                                      att, ctx, status, workspace=ws, scale=wl.scale,
-                                      events=events)
+            kvc.kvc_step_out_of_place(d["query"], d["new_key"], d["new_value"], d["key_cache"],
+                                      d["value_cache"], d["lengths"], d["mask"], d["kc_out"],
+                                      d["vc_out"], d["lens_out"], d["att"], d["ctx"],
+                                      d["status"], workspace=ws, scale=wl.scale, events=events)
 
     ceiling = copy_ceiling_gbps(torch, dev)
-    for _ in range(args.warmup):
-        step()
+    for w in range(args.warmup):
+        step(None, w)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        step(i, i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kernel_ms = [ev.elapsed_ms(a, b) for a, b in zip(starts, stops)]
@@ -253,7 +269,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "entry": f"kvc_step_{'inplace' if args.mode == 'inplace' else 'out_of_place'}",
                    "B": wl.B, "Hq": wl.Hq, "Hk": wl.Hk, "Q": wl.Q, "M": wl.M, "D": wl.D,
-                   "Dv": wl.Dv, "seed": args.seed, "plan": plan},
+                   "Dv": wl.Dv, "seed": args.seed, "input_copies": len(sets), "plan": plan},
         "achieved_gbps": step_gbps,
         "pct_of_peak_hbm": 100.0 * step_gbps / PEAK_HBM_GBPS,
         "tokens_per_s": steps_per_s * wl.B * wl.Q,
@@ -265,7 +281,7 @@ def main():
                      "avg_launch_ms": k_ms},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, first_inputs, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
