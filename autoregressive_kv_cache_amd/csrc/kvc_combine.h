@@ -89,6 +89,14 @@ struct Vec8<bf16> {
     }
   }
   __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+  // keep elements [0, cnt), zero the others (no indexed access: the vector
+  // stays in registers)
+  __device__ __forceinline__ void keep_first(int cnt) {
+    v.x &= (cnt > 0 ? 0xffffu : 0u) | (cnt > 1 ? 0xffff0000u : 0u);
+    v.y &= (cnt > 2 ? 0xffffu : 0u) | (cnt > 3 ? 0xffff0000u : 0u);
+    v.z &= (cnt > 4 ? 0xffffu : 0u) | (cnt > 5 ? 0xffff0000u : 0u);
+    v.w &= (cnt > 6 ? 0xffffu : 0u) | (cnt > 7 ? 0xffff0000u : 0u);
+  }
 };
 template <>
 struct Vec8<float> {
@@ -108,6 +116,12 @@ struct Vec8<float> {
     b.z = static_cast<float>(b.z * f); b.w = static_cast<float>(b.w * f);
   }
   __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void keep_first(int cnt) {
+    a.x = cnt > 0 ? a.x : 0.f; a.y = cnt > 1 ? a.y : 0.f;
+    a.z = cnt > 2 ? a.z : 0.f; a.w = cnt > 3 ? a.w : 0.f;
+    b.x = cnt > 4 ? b.x : 0.f; b.y = cnt > 5 ? b.y : 0.f;
+    b.z = cnt > 6 ? b.z : 0.f; b.w = cnt > 7 ? b.w : 0.f;
+  }
 };
 
 constexpr int kCombineRowBlock = 8;   // packed rows per pass
@@ -221,10 +235,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
             const int64_t lim = t < n ? len + t + 1 : 0;
             if (base < lim) {
               x[i].scale_by(fac[i][cc]);
-              if (base + 8 > lim) {  // zero the invisible part of this vector
-                T* el = reinterpret_cast<T*>(&x[i]);
-                for (int q = static_cast<int>(lim - base); q < 8; q++) el[q] = E::zero();
-              }
+              // zero the invisible part of this vector
+              if (base + 8 > lim) x[i].keep_first(static_cast<int>(lim - base));
             }
             x[i].store(att + row * a.M + base);
           }
