@@ -159,14 +159,20 @@ int make_plan(const kvc_dims* d, int dtype, Plan* p) {
   const int64_t row_tiles = R == 0 ? 1 : (R + kvc::kGenericRowsPerTile - 1) / kvc::kGenericRowsPerTile;
   if (!make_layout(d, R, kvc::kGenericChunk, false, 0, &p->generic)) return KVC_ERR_SHAPE;
   int64_t wgs;
+  // combine grid: groups x (slot ranges + 1) x blocks of kCombineWaves rows
+  const int64_t row_blocks = R == 0 ? 1 : (R + kvc::kCombineWaves - 1) / kvc::kCombineWaves;
   if (!mul_ok(d->B * d->Hk, row_tiles, kMaxElems, &wgs) ||
-      !mul_ok(wgs, p->generic.nchunk_max, kMaxWorkgroups, &wgs))
+      !mul_ok(wgs, p->generic.nchunk_max, kMaxWorkgroups, &wgs) ||
+      !mul_ok(d->B * d->Hk, row_blocks, kMaxElems, &wgs) ||
+      !mul_ok(wgs, (d->M + p->generic.CS - 1) / p->generic.CS + 1, kMaxWorkgroups, &wgs))
     return KVC_ERR_SHAPE;
   size_t bytes = p->generic.bytes;
   if (p->decode) {
     if (!make_layout(d, R, p->decode->chunk, true, p->P, &p->stream)) return KVC_ERR_SHAPE;
     int64_t cwgs;
-    if (!mul_ok(d->B * d->Hk, p->stream.nchunk_max, kMaxWorkgroups, &cwgs)) return KVC_ERR_SHAPE;
+    if (!mul_ok(d->B * d->Hk, row_blocks, kMaxElems, &cwgs) ||
+        !mul_ok(cwgs, (d->M + p->stream.CS - 1) / p->stream.CS + 1, kMaxWorkgroups, &cwgs))
+      return KVC_ERR_SHAPE;
     if (p->stream.bytes > bytes) bytes = p->stream.bytes;
     p->pub.path = 1;
     p->pub.rows_per_tile = p->decode->rows;
@@ -221,6 +227,15 @@ void set_layout(StepArgs& a, const Layout& L, void* workspace) {
 }
 
 template <typename T>
+void launch_combine(const StepArgs& a, hipStream_t stream) {
+  const int64_t groups = a.B * a.Hk;
+  const int64_t nrb = a.R > 0 ? (a.R + kvc::kCombineWaves - 1) / kvc::kCombineWaves : 1;
+  hipLaunchKernelGGL(kvc::combine_kernel<T>,
+                     dim3(static_cast<unsigned>(groups * ((a.M + a.CS - 1) / a.CS + 1) * nrb)),
+                     dim3(kvc::kCombineThreads), 0, stream, a);
+}
+
+template <typename T>
 void launch_generic(StepArgs& a, hipStream_t stream, const kvc_events* ev) {
   const int64_t groups = a.B * a.Hk;
   if (ev && ev->start) hipEventRecord(static_cast<hipEvent_t>(ev->start), stream);
@@ -228,9 +243,7 @@ void launch_generic(StepArgs& a, hipStream_t stream, const kvc_events* ev) {
                      dim3(static_cast<unsigned>(groups * a.row_tiles * a.nchunk_max)),
                      dim3(kvc::kGenericThreads), 0, stream, a);
   if (ev && ev->stop) hipEventRecord(static_cast<hipEvent_t>(ev->stop), stream);
-  hipLaunchKernelGGL(kvc::combine_kernel<T>,
-                     dim3(static_cast<unsigned>(groups * ((a.M + a.CS - 1) / a.CS))),
-                     dim3(kvc::kCombineThreads), 0, stream, a);
+  launch_combine<T>(a, stream);
 }
 
 template <typename T>
@@ -241,9 +254,7 @@ void launch_stream(StepArgs& a, const DecodeEntry& e, hipStream_t stream, const 
   if (ev && ev->start) hipEventRecord(static_cast<hipEvent_t>(ev->start), stream);
   e.launch(a, stream);
   if (ev && ev->stop) hipEventRecord(static_cast<hipEvent_t>(ev->stop), stream);
-  hipLaunchKernelGGL(kvc::combine_kernel<T>,
-                     dim3(static_cast<unsigned>(groups * ((a.M + a.CS - 1) / a.CS))),
-                     dim3(kvc::kCombineThreads), 0, stream, a);
+  launch_combine<T>(a, stream);
 }
 
 int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const void* query,

@@ -26,7 +26,8 @@
 
 namespace kvc {
 
-constexpr int kCombineThreads = 256;
+constexpr int kCombineWaves = 4;
+constexpr int kCombineThreads = kCombineWaves * kWave;
 
 // The segments of one group: ids first + s for s in [0, count).  Stream
 // mode: the workers owning chunks [x0, x1] of the flattened list are
@@ -44,31 +45,6 @@ __device__ inline SegRange group_segments(const StepArgs& a, int64_t grp, int64_
   // owner(x) = the worker w with floor(w*Nc/Pe) <= x < floor((w+1)*Nc/Pe)
   const int64_t w0 = ((x0 + 1) * Pe - 1) / Nc, w1 = ((x1 + 1) * Pe - 1) / Nc;
   return {w0 + grp, w1 - w0 + 1};
-}
-
-template <typename Acc>
-struct RowStats {
-  Acc m, l;
-};
-
-// m and l of packed row r over the segments of its group (whole wave).
-template <typename Acc>
-__device__ RowStats<Acc> row_stats(const StepArgs& a, const SegRange& sr, int r, int lane) {
-  const Acc neg_inf = -static_cast<Acc>(INFINITY);
-  Acc m = neg_inf;
-  for (int64_t s = lane; s < sr.count; s += kWave) {
-    const Acc mk = static_cast<Acc>(a.ws_seg_ml[((sr.first + s) * a.R + r) * 2]);
-    m = mk > m ? mk : m;
-  }
-  m = wave_max(m);
-  Acc l = 0;
-  for (int64_t s = lane; s < sr.count; s += kWave) {
-    const double* ml = a.ws_seg_ml + ((sr.first + s) * a.R + r) * 2;
-    const Acc mk = static_cast<Acc>(ml[0]);
-    if (mk != neg_inf) l += static_cast<Acc>(ml[1]) * acc_exp(mk - m);
-  }
-  l = wave_sum(l);
-  return {m, l};
 }
 
 // Eight consecutive elements of T (16 bytes of bf16, 32 of fp32).
@@ -124,40 +100,43 @@ struct Vec8<float> {
   }
 };
 
-constexpr int kCombineRowBlock = 8;   // packed rows per pass
-constexpr int kCombineMaxChunks = 64; // chunks per combine range (CS / C)
+constexpr int kCombineVecPerLane = 4;  // 8-element vectors per lane and pass
 
+// Workgroup = kCombineWaves waves; wave w owns packed row rb * kCombineWaves + w
+// of its group.  Workgroups k < ceil(M / CS) rescale the slot range
+// [k * CS, (k + 1) * CS) of their rows; workgroup k = ceil(M / CS) merges
+// their contexts, in parallel with the rescaling.  Every wave works alone:
+// the attention vectors, the chunk statistics, the segment statistics and
+// (context role) the first segment partials it needs are all requested
+// before any of them is used.
 template <typename T>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
   using E = Elem<T>;
   using Acc = typename E::Acc;
-  constexpr int RB = kCombineRowBlock;
-  __shared__ Acc row_m[RB], row_inv_l[RB];
-  __shared__ Acc fac[RB][kCombineMaxChunks];
-  __shared__ Acc seg_w[kCombineThreads];
-  __shared__ Acc ctx_red[kCombineThreads];
+  constexpr int VPL = kCombineVecPerLane;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int64_t ncw = ceil_div(a.M, a.CS);
-  const int64_t k = blockIdx.x % ncw;
-  const int64_t grp = blockIdx.x / ncw;
+  const int64_t nrb = a.R > 0 ? ceil_div(a.R, kCombineWaves) : 1;
+  const int64_t rb = blockIdx.x % nrb;
+  const int64_t k = (blockIdx.x / nrb) % (ncw + 1);
+  const int64_t grp = blockIdx.x / nrb / (ncw + 1);
+  const bool ctx_role = k == ncw;
   const int64_t b = grp / a.Hk, kvh = grp % a.Hk;
   const int64_t len = a.ws_rowinfo[b * 4 + 0];
   const int64_t n = a.ws_rowinfo[b * 4 + 1];
   const int32_t status = static_cast<int32_t>(a.ws_rowinfo[b * 4 + 2]);
   const int64_t nc = row_chunks(len, n, a.C);
 
-  if (k == 0 && kvh == 0 && tid == 0) {
+  if (k == 0 && kvh == 0 && rb == 0 && tid == 0) {
     a.lengths_out[b] = len + n;
     if (a.row_status) a.row_status[b] = status;
   }
-  const int64_t e0 = k * a.CS;
+  const int64_t e0 = ctx_role ? a.M : k * a.CS;
   const int64_t e1 = e0 + a.CS < a.M ? e0 + a.CS : a.M;
-  const int nchunks = static_cast<int>(ceil_div(e1 - e0, a.C));  // chunks in this range
-  const int64_t c0 = e0 / a.C;                                   // first chunk index
 
-  if (a.out_of_place && a.combine_copies_tail) {
+  if (rb == 0 && a.out_of_place && a.combine_copies_tail) {
     const int64_t cover = n > 0 ? len + n : 0;
     const int64_t j0 = e0 > cover ? e0 : cover;
     if (j0 < e1) {
@@ -172,133 +151,163 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
     }
   }
 
-  const SegRange sr = group_segments(a, grp, b, kvh, nc);
+  const int64_t r = rb * kCombineWaves + wave;
+  if (r >= a.R) return;
+  const int64_t g = r / a.Q, t = r % a.Q;
+  const int64_t row = (b * a.Hq + kvh * a.G + g) * a.Q + t;
+  const int64_t lim = t < n ? len + t + 1 : 0;  // visible slots [0, lim)
+  const bool owns_ctx = ctx_role;
   const Acc neg_inf = -static_cast<Acc>(INFINITY);
-  T* att = static_cast<T*>(a.attention);
-  T* ctx = static_cast<T*>(a.context);
+  T* arow = static_cast<T*>(a.attention) + row * a.M;
+  T* ctx = static_cast<T*>(a.context) + row * a.Dv;
   const double* chunk_ml = a.ws_chunk_ml + grp * a.nchunk_max * a.R * 2;
+  const SegRange sr = group_segments(a, grp, b, kvh, nc);
   // 8-element vectors need 16-byte aligned rows and ranges
-  const bool vec = (reinterpret_cast<uintptr_t>(att) % 16 == 0) && (a.M % 8 == 0) &&
-                   (e0 % 8 == 0);
+  const bool vec = (reinterpret_cast<uintptr_t>(a.attention) % 16 == 0) && (a.M % 8 == 0) &&
+                   (e0 % 8 == 0) && (e1 % 8 == 0);
 
-  for (int rb = 0; rb < a.R; rb += RB) {
-    const int nrows = a.R - rb < RB ? static_cast<int>(a.R - rb) : RB;
-    // 1. row statistics (m, 1/l) of the block's valid rows
-    for (int i = wave; i < nrows; i += kCombineThreads / kWave) {
-      const int r = rb + i;
-      const int64_t t = r % a.Q;
-      const bool need = t < n && (len + t + 1 > e0 || (r % ncw) == k);
-      if (need) {
-        const RowStats<Acc> st = row_stats<Acc>(a, sr, r, lane);
-        if (lane == 0) {
-          row_m[i] = st.m;
-          row_inv_l[i] = Acc(1) / st.l;
-        }
-      }
-    }
-    __syncthreads();
-    // 2. one factor exp(m_c - m) / l per (row, chunk) of the range
-    for (int idx = tid; idx < nrows * nchunks; idx += kCombineThreads) {
-      const int i = idx / nchunks, cc = idx % nchunks;
-      const int r = rb + i;
-      const int64_t t = r % a.Q;
-      const int64_t ch = c0 + cc;
-      Acc f = 0;
-      if (t < n && ch < nc && ch * a.C <= len + t) {
-        const Acc mc = static_cast<Acc>(chunk_ml[(ch * a.R + r) * 2]);
-        f = mc == neg_inf ? Acc(0) : acc_exp(mc - row_m[i]) * row_inv_l[i];
-      }
-      fac[i][cc] = f;
-    }
-    __syncthreads();
-    // 3. rescale visible slots, zero the rest
-    if (vec) {
-      for (int64_t base = e0 + tid * 8; base < e1; base += kCombineThreads * 8) {
-        const int cc = static_cast<int>((base - e0) / a.C);
-        Vec8<T> x[RB];
+  // ---- first pass of the range: its loads go out before the statistics ----
+  const int64_t nvec = (e1 - e0) / 8;
+  Vec8<T> x[VPL];
+  double mc[VPL];
+  if (vec) {
 #pragma unroll
-        for (int i = 0; i < RB; i++) {
-          if (i < nrows) {
-            const int r = rb + i;
-            const int64_t g = r / a.Q, t = r % a.Q;
-            const int64_t row = (b * a.Hq + kvh * a.G + g) * a.Q + t;
-            const int64_t lim = t < n ? len + t + 1 : 0;  // visible slots [0, lim)
-            if (base < lim) x[i].load(att + row * a.M + base); else x[i].zero();
-          }
-        }
+    for (int v = 0; v < VPL; v++) {
+      const int64_t base = e0 + (v * kWave + lane) * 8;
+      x[v].zero();
+      mc[v] = -INFINITY;
+      if (v * kWave + lane < nvec && base < lim) {
+        x[v].load(arow + base);
+        mc[v] = chunk_ml[((base / a.C) * a.R + r) * 2];
+      }
+    }
+  }
+
+  // segment statistics of the first kWave segments (lane s holds segment s)
+  // and, for the wave that writes the row's context, the first batch of
+  // segment partials: all requested before anything waits on them
+  constexpr int SB = 16;
+  const bool do_ctx = owns_ctx && t < n && sr.count > 0;
+  double seg_m0 = -INFINITY, seg_l0 = 0;
+  if (t < n && lane < sr.count) {
+    const double* ml = a.ws_seg_ml + ((sr.first + lane) * a.R + r) * 2;
+    seg_m0 = ml[0];
+    seg_l0 = ml[1];
+  }
+  float cv[SB][2];
+  auto load_batch = [&](int64_t s1, int64_t dv0) {
 #pragma unroll
-        for (int i = 0; i < RB; i++) {
-          if (i < nrows) {
-            const int r = rb + i;
-            const int64_t g = r / a.Q, t = r % a.Q;
-            const int64_t row = (b * a.Hq + kvh * a.G + g) * a.Q + t;
-            const int64_t lim = t < n ? len + t + 1 : 0;
-            if (base < lim) {
-              x[i].scale_by(fac[i][cc]);
-              // zero the invisible part of this vector
-              if (base + 8 > lim) x[i].keep_first(static_cast<int>(lim - base));
-            }
-            x[i].store(att + row * a.M + base);
+    for (int s = 0; s < SB; s++) {
+      const float* op = a.ws_seg_o + ((sr.first + s1 + s) * a.R + r) * a.Dv;
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        const int64_t dv = dv0 + q * kWave + lane;
+        cv[s][q] = (s1 + s < sr.count && dv < a.Dv) ? op[dv] : 0.0f;
+      }
+    }
+  };
+  if (do_ctx) load_batch(0, 0);
+
+  // ---- m and 1/l of the row over its segments (online merge) ----
+  Acc m = neg_inf, l = 0;
+  if (t < n) {
+    auto merge = [&](Acc ms, Acc ls) {
+      if (ms != neg_inf) {
+        const Acc mn = ms > m ? ms : m;
+        l = (m == neg_inf ? Acc(0) : l * acc_exp(m - mn)) + ls * acc_exp(ms - mn);
+        m = mn;
+      }
+    };
+    merge(static_cast<Acc>(seg_m0), static_cast<Acc>(seg_l0));
+    for (int64_t s = kWave + lane; s < sr.count; s += kWave) {
+      const double* ml = a.ws_seg_ml + ((sr.first + s) * a.R + r) * 2;
+      merge(static_cast<Acc>(ml[0]), static_cast<Acc>(ml[1]));
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      const Acc mo = __shfl_xor(m, o), lo = __shfl_xor(l, o);
+      const Acc mn = mo > m ? mo : m;
+      if (mn != neg_inf)
+        l = (m == neg_inf ? Acc(0) : l * acc_exp(m - mn)) +
+            (mo == neg_inf ? Acc(0) : lo * acc_exp(mo - mn));
+      m = mn;
+    }
+  }
+  const Acc inv_l = l > 0 ? Acc(1) / l : Acc(0);
+  auto factor = [&](double m_c) -> Acc {
+    const Acc mcv = static_cast<Acc>(m_c);
+    return mcv == neg_inf ? Acc(0) : acc_exp(mcv - m) * inv_l;
+  };
+
+  // ---- rescale the visible slots, zero the rest ----
+  if (vec) {
+    for (int64_t v0 = 0; v0 < nvec; v0 += VPL * kWave) {
+      if (v0 > 0) {  // later passes (ranges longer than VPL * 512 slots)
+#pragma unroll
+        for (int v = 0; v < VPL; v++) {
+          const int64_t base = e0 + (v0 + v * kWave + lane) * 8;
+          x[v].zero();
+          mc[v] = -INFINITY;
+          if (v0 + v * kWave + lane < nvec && base < lim) {
+            x[v].load(arow + base);
+            mc[v] = chunk_ml[((base / a.C) * a.R + r) * 2];
           }
         }
       }
-    } else {
-      for (int i = 0; i < nrows; i++) {
-        const int r = rb + i;
-        const int64_t g = r / a.Q, t = r % a.Q;
-        const int64_t row = (b * a.Hq + kvh * a.G + g) * a.Q + t;
-        const int64_t lim = t < n ? len + t + 1 : 0;
-        T* arow = att + row * a.M;
-        for (int64_t j = e0 + tid; j < e1; j += kCombineThreads) {
-          if (j < lim)
-            E::store(arow + j, E::load(arow + j) * fac[i][(j - e0) / a.C]);
-          else
-            arow[j] = E::zero();
+#pragma unroll
+      for (int v = 0; v < VPL; v++) {
+        const int64_t base = e0 + (v0 + v * kWave + lane) * 8;
+        if (v0 + v * kWave + lane < nvec) {
+          if (base < lim) {
+            x[v].scale_by(factor(mc[v]));
+            if (base + 8 > lim) x[v].keep_first(static_cast<int>(lim - base));
+          }
+          x[v].store(arow + base);
         }
       }
     }
-    // 4. context of the rows this range owns: the whole workgroup reduces
-    //    one row at a time, segment weights exp(m_seg - m) / l staged in LDS
-    for (int i = 0; i < nrows; i++) {
-      const int r = rb + i;
-      if ((r % ncw) != k) continue;
-      const int64_t g = r / a.Q, t = r % a.Q;
-      const int64_t row = (b * a.Hq + kvh * a.G + g) * a.Q + t;
-      if (t >= n) {
-        for (int64_t dv = tid; dv < a.Dv; dv += kCombineThreads) ctx[row * a.Dv + dv] = E::zero();
-        continue;
+  } else {
+    for (int64_t j = e0 + lane; j < e1; j += kWave) {
+      if (j < lim)
+        E::store(arow + j, E::load(arow + j) * factor(chunk_ml[((j / a.C) * a.R + r) * 2]));
+      else
+        arow[j] = E::zero();
+    }
+  }
+
+  // ---- context of the rows this range owns ----
+  if (!owns_ctx) return;
+  if (!do_ctx) {
+    for (int64_t dv = lane; dv < a.Dv; dv += kWave) ctx[dv] = E::zero();
+    return;
+  }
+  // lanes own dims dv0 + q * 64 + lane, q < 2
+  for (int64_t dv0 = 0; dv0 < a.Dv; dv0 += 2 * kWave) {
+    Acc o[2] = {0, 0};
+    for (int64_t s0 = 0; s0 < sr.count; s0 += kWave) {
+      // weight of segment s0 + lane; broadcast one segment at a time
+      Acc w = 0;
+      if (s0 == 0) {
+        w = factor(seg_m0);
+      } else if (s0 + lane < sr.count) {
+        w = factor(a.ws_seg_ml[((sr.first + s0 + lane) * a.R + r) * 2]);
       }
-      // PARTS threads per dv (Dv < 256) each sum every PARTS-th segment
-      const int parts = a.Dv >= kCombineThreads ? 1 : kCombineThreads / static_cast<int>(a.Dv);
-      for (int64_t dv0 = 0; dv0 < a.Dv; dv0 += kCombineThreads) {
-        const int64_t dv = dv0 + tid % (parts == 1 ? kCombineThreads : a.Dv);
-        const int part = parts == 1 ? 0 : tid / static_cast<int>(a.Dv);
-        Acc o = 0;
-        for (int64_t s0 = 0; s0 < sr.count; s0 += kCombineThreads) {
-          const int64_t ns = sr.count - s0 < kCombineThreads ? sr.count - s0 : kCombineThreads;
-          __syncthreads();
-          if (tid < ns) {
-            const Acc mk = static_cast<Acc>(a.ws_seg_ml[((sr.first + s0 + tid) * a.R + r) * 2]);
-            seg_w[tid] = mk == neg_inf ? Acc(0) : acc_exp(mk - row_m[i]) * row_inv_l[i];
-          }
-          __syncthreads();
-          if (part < parts && dv < a.Dv) {
-            const float* op = a.ws_seg_o + ((sr.first + s0) * a.R + r) * a.Dv + dv;
-#pragma unroll 4
-            for (int64_t s = part; s < ns; s += parts) o += seg_w[s] * static_cast<Acc>(op[s * a.R * a.Dv]);
-          }
-        }
-        __syncthreads();
-        ctx_red[tid] = part < parts ? o : Acc(0);  // slot tid = part * Dv + dv (parts > 1)
-        __syncthreads();
-        if (tid < (parts == 1 ? kCombineThreads : a.Dv) && dv0 + tid < a.Dv) {
-          Acc sum = 0;
-          for (int p = 0; p < parts; p++) sum += ctx_red[p * (parts == 1 ? 0 : a.Dv) + tid];
-          E::store(ctx + row * a.Dv + dv0 + tid, sum);
+      const int64_t ns = sr.count - s0 < kWave ? sr.count - s0 : kWave;
+      for (int64_t s1 = 0; s1 < ns; s1 += SB) {
+        if (dv0 > 0 || s0 > 0 || s1 > 0) load_batch(s0 + s1, dv0);
+#pragma unroll
+        for (int s = 0; s < SB; s++) {
+          const Acc ws = __shfl(w, static_cast<int>(s1 + s));  // 0 past the last segment
+#pragma unroll
+          for (int q = 0; q < 2; q++) o[q] += ws * static_cast<Acc>(cv[s][q]);
         }
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const int64_t dv = dv0 + q * kWave + lane;
+      if (dv < a.Dv) E::store(ctx + dv, o[q]);
+    }
   }
 }
 
