@@ -85,26 +85,38 @@ def algorithmic_bytes(wl, lengths, n):
     Step: read the visible prefix of K and V (length + n rows per KV head,
     the n new rows read from new_key/new_value), write the n new rows into
     the cache, read q, write the full attention rows and the context, plus
-    lengths, mask, lengths_out and row_status.  The attention kernel's
-    share is the same without the context, lengths_out and row_status."""
+    lengths, mask, lengths_out and row_status.
+
+    Attention kernel: the K/V rows it visits (length + n per KV head, the
+    appended ones already in the cache), q, the exp(s - m_c) values of the
+    visible slots (length + t + 1 per valid row) and lengths and mask; the
+    append itself, the zero tails, the normalisation and the context belong
+    to the kernels around it."""
     e = 2 if wl.dtype == "bf16" else 4
     kv = sum(wl.Hk * (int(L) + 2 * int(k)) * (wl.D + wl.Dv) * e for L, k in zip(lengths, n))
+    kv_read = sum(wl.Hk * (int(L) + int(k)) * (wl.D + wl.Dv) * e for L, k in zip(lengths, n))
     q = wl.B * wl.Hq * wl.Q * wl.D * e
     att = wl.B * wl.Hq * wl.Q * wl.M * e
+    att_visible = sum(wl.Hq * (int(L) + t + 1) * e for L, k in zip(lengths, n) for t in range(int(k)))
     ctx = wl.B * wl.Hq * wl.Q * wl.Dv * e
     small_in = wl.B * (8 + wl.Q)
     small_out = wl.B * (8 + 4)
     step = kv + q + att + ctx + small_in + small_out
-    attend = kv + q + att + small_in
+    attend = kv_read + q + att_visible + small_in
     return step, attend, kv
 
 
-def oop_extra_bytes(wl, n):
-    """Out of place the whole cache is also copied: every slot that is not
-    appended is read and written once."""
+def oop_extra_bytes(wl, lengths, n):
+    """Out of place the whole cache is also returned: per KV head the M - len
+    - n slots past the new rows are read and written once and the len cached
+    rows are written once more (their read is already counted).  Returns the
+    step's extra bytes and the attention kernel's (it writes the rows it
+    visits; the rest is copied by the kernels around it)."""
     e = 2 if wl.dtype == "bf16" else 4
-    rows = wl.B * wl.Hk * wl.M - sum(wl.Hk * int(k) for k in n)
-    return 2 * rows * (wl.D + wl.Dv) * e
+    row = (wl.D + wl.Dv) * e
+    step = sum(wl.Hk * (2 * wl.M - int(L) - int(k)) * row for L, k in zip(lengths, n))
+    attend = sum(wl.Hk * int(L) * row for L in lengths)
+    return step, attend
 
 
 def kernel_source_digest() -> str:
@@ -244,9 +256,9 @@ def main():
 
     step_bytes, attend_bytes, kv_bytes = algorithmic_bytes(wl, lengths, n)
     if args.mode == "oop":
-        extra = oop_extra_bytes(wl, n)
-        step_bytes += extra
-        attend_bytes += extra
+        extra_step, extra_attend = oop_extra_bytes(wl, lengths, n)
+        step_bytes += extra_step
+        attend_bytes += extra_attend
     ms_per_step = elapsed / args.steps * 1e3
     steps_per_s = args.steps / elapsed
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
