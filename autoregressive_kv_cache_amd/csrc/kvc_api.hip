@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "../../include/kvc.h"
+#include "kvc_chunk.h"
 #include "kvc_combine.h"
 #include "kvc_common.h"
 #include "kvc_decode.h"
@@ -74,9 +75,34 @@ const DecodeEntry kDecodeTable[] = {
 // loads in flight.
 constexpr int64_t kStreamWorkgroupsPerCU = 2;
 constexpr int64_t kComputeUnits = 256;
-// Slots per combine workgroup on the stream path (a multiple of every
-// decode chunk size).
-constexpr int64_t kStreamCombineSlots = 2048;
+// Slots per combine workgroup (a multiple of every chunk size).
+constexpr int64_t kCombineSlots = 2048;
+
+// Matrix-core chunk path: bf16, more than 8 packed rows per KV head.
+struct ChunkEntry {
+  int64_t D, Dv;
+  void (*launch)(const StepArgs&, hipStream_t);
+};
+
+template <int D, int DV>
+void launch_chunk(const StepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((kvc::attend_chunk_kernel<D, DV>),
+                     dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk_max)),
+                     dim3(kvc::kChunkThreads), 0, s, a);
+}
+
+const ChunkEntry kChunkTable[] = {
+    {64, 64, &launch_chunk<64, 64>},
+    {128, 128, &launch_chunk<128, 128>},
+    {256, 256, &launch_chunk<256, 256>},
+};
+
+const ChunkEntry* find_chunk(const kvc_dims* d, int dtype, int64_t R) {
+  if (dtype != KVC_BF16 || R <= 8) return nullptr;
+  for (const ChunkEntry& e : kChunkTable)
+    if (e.D == d->D && e.Dv == d->Dv) return &e;
+  return nullptr;
+}
 
 const DecodeEntry* find_decode(const kvc_dims* d, int dtype, int64_t R) {
   if (R > 8) return nullptr;
@@ -95,7 +121,7 @@ bool make_layout(const kvc_dims* d, int64_t R, int64_t C, bool stream,
                  int64_t P, Layout* L) {
   L->C = C;
   L->nchunk_max = (d->M + C - 1) / C;
-  L->CS = stream ? kStreamCombineSlots : C;
+  L->CS = kCombineSlots;
   int64_t groups, chunks, nseg, x;
   if (!mul_ok(d->B, d->Hk, kMaxElems, &groups) || !mul_ok(groups, L->nchunk_max, kMaxElems, &chunks))
     return false;
@@ -123,8 +149,9 @@ bool make_layout(const kvc_dims* d, int64_t R, int64_t C, bool stream,
 
 struct Plan {
   kvc_plan pub;
-  const DecodeEntry* decode;  // null: generic path
-  Layout generic, stream;
+  const DecodeEntry* decode;  // vector decode path, or null
+  const ChunkEntry* chunk;    // matrix-core chunk path, or null
+  Layout generic, stream, dense;
   int64_t P;
 };
 
@@ -155,6 +182,7 @@ int make_plan(const kvc_dims* d, int dtype, Plan* p) {
   const int64_t R = (d->Hq / d->Hk) * d->Q;
   p->pub.rows = static_cast<int32_t>(R);
   p->decode = find_decode(d, dtype, R);
+  p->chunk = p->decode ? nullptr : find_chunk(d, dtype, R);
   p->P = kComputeUnits * kStreamWorkgroupsPerCU * kvc::kDecodeWaves;
   const int64_t row_tiles = R == 0 ? 1 : (R + kvc::kGenericRowsPerTile - 1) / kvc::kGenericRowsPerTile;
   if (!make_layout(d, R, kvc::kGenericChunk, false, 0, &p->generic)) return KVC_ERR_SHAPE;
@@ -179,6 +207,19 @@ int make_plan(const kvc_dims* d, int dtype, Plan* p) {
     p->pub.row_tiles = 1;
     p->pub.split = p->decode->chunk;
     p->pub.nsplit = p->stream.nchunk_max;
+  } else if (p->chunk) {
+    if (!make_layout(d, R, kvc::kChunkSlots, false, 0, &p->dense)) return KVC_ERR_SHAPE;
+    int64_t cwgs;
+    if (!mul_ok(d->B * d->Hk, p->dense.nchunk_max, kMaxWorkgroups, &cwgs) ||
+        !mul_ok(d->B * d->Hk, row_blocks, kMaxElems, &cwgs) ||
+        !mul_ok(cwgs, (d->M + p->dense.CS - 1) / p->dense.CS + 1, kMaxWorkgroups, &cwgs))
+      return KVC_ERR_SHAPE;
+    if (p->dense.bytes > bytes) bytes = p->dense.bytes;
+    p->pub.path = 2;
+    p->pub.rows_per_tile = static_cast<int32_t>(R);
+    p->pub.row_tiles = 1;
+    p->pub.split = kvc::kChunkSlots;
+    p->pub.nsplit = p->dense.nchunk_max;
   } else {
     p->pub.path = 0;
     p->pub.rows_per_tile = kvc::kGenericRowsPerTile;
@@ -244,6 +285,14 @@ void launch_generic(StepArgs& a, hipStream_t stream, const kvc_events* ev) {
                      dim3(kvc::kGenericThreads), 0, stream, a);
   if (ev && ev->stop) hipEventRecord(static_cast<hipEvent_t>(ev->stop), stream);
   launch_combine<T>(a, stream);
+}
+
+void launch_dense_chunk(StepArgs& a, const ChunkEntry& e, hipStream_t stream,
+                        const kvc_events* ev) {
+  if (ev && ev->start) hipEventRecord(static_cast<hipEvent_t>(ev->start), stream);
+  e.launch(a, stream);
+  if (ev && ev->stop) hipEventRecord(static_cast<hipEvent_t>(ev->stop), stream);
+  launch_combine<kvc::bf16>(a, stream);
 }
 
 template <typename T>
@@ -328,12 +377,21 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
   a.lengths = lengths; a.mask = mask; a.attention = attention; a.context = context;
   a.lengths_out = lengths_out; a.row_status = row_status;
 
-  // the vector path needs 16-byte aligned rows
-  const bool vec_ok = p.decode && aligned16(query) && aligned16(new_key) && aligned16(new_value) &&
-                      aligned16(kc_in) && aligned16(vc_in) && aligned16(kc_out) &&
-                      aligned16(vc_out);
+  // the vector and matrix paths need 16-byte aligned rows
+  const bool aligned = aligned16(query) && aligned16(new_key) && aligned16(new_value) &&
+                       aligned16(kc_in) && aligned16(vc_in) && aligned16(kc_out) &&
+                       aligned16(vc_out);
+  const bool vec_ok = p.decode && aligned;
+  const bool chunk_ok = p.chunk && aligned;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (vec_ok) {
+  if (chunk_ok) {
+    set_layout(a, p.dense, workspace);
+    a.seg_mode = 0;
+    a.combine_copies_tail = 0;
+    a.rows_per_tile = a.R;
+    a.row_tiles = 1;
+    launch_dense_chunk(a, *p.chunk, s, events);
+  } else if (vec_ok) {
     set_layout(a, p.stream, workspace);
     a.seg_mode = 1;
     a.combine_copies_tail = 1;

@@ -1,0 +1,256 @@
+// kvc_chunk.h -- attend kernel for many packed query rows per KV head
+// (multi-token appends: G * Q > 8), bf16, on the matrix cores.
+//
+// One workgroup handles one (batch row b, KV head h, chunk c of 64 slots)
+// for all R = G * Q packed query rows of that head (row r = g * Q + t reads
+// query head h * G + g, token t):
+//   1. cache writes for the chunk's slot range, as on the page
+//      "Autoregressive KV-cache append and causal attention" (Required
+//      behavior): new rows at slot length + t, out of place every other slot
+//      copied bit for bit;
+//   2. the chunk's K rows [64 x D] into LDS and its V rows transposed
+//      [Dv x 64] into LDS (the appended slots read from new_key/new_value,
+//      slots past length + n as zeros), shared by the four waves;
+//   3. per block of 16 packed rows (one wave): S = Q K^T with
+//      v_mfma_f32_16x16x32_bf16 (fp32 accumulation), scale, the causal mask
+//      j <= length + t (lower-right alignment, KempnerForge PR 542), the
+//      chunk statistics m_c = max s_j and l_c = sum exp(s_j - m_c), the
+//      values exp(s_j - m_c) into the attention buffer, and
+//      o_c = sum_j exp(s_j - m_c) v_j with a second matrix product.
+// Every chunk is its own segment (dense mode); the combine kernel merges
+// them exactly as it merges the other attend kernels' results.
+//
+// Operand layouts of v_mfma_f32_16x16x32_bf16 (wave64): lane l supplies
+// A[l % 16][8 * (l / 16) + e] and B[8 * (l / 16) + e][l % 16] for e < 8, and
+// receives D[4 * (l / 16) + i][l % 16] for i < 4.
+#pragma once
+
+#include "kvc_common.h"
+#include "kvc_generic.h"
+
+namespace kvc {
+
+constexpr int kChunkSlots = 64;      // slots per chunk (C)
+constexpr int kChunkThreads = 256;   // four waves
+constexpr int kChunkWaves = kChunkThreads / kWave;
+constexpr int kChunkBlockRows = 16;  // packed rows per matrix block
+
+typedef __bf16 mfma_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float mfma_f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ mfma_f32x4 mfma_16x16x32(const uint4& a, const uint4& b,
+                                                    mfma_f32x4 c) {
+  mfma_bf16x8 av, bv;
+  __builtin_memcpy(&av, &a, 16);
+  __builtin_memcpy(&bv, &b, 16);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint4 ld_global16(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ uint4 ld_lds16(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+template <int D, int DV>
+__global__ __launch_bounds__(kChunkThreads) void attend_chunk_kernel(StepArgs a) {
+  constexpr int C = kChunkSlots;
+  constexpr int KP = D + 8;   // K row pitch in LDS (elements; 16-byte multiple)
+  constexpr int VP = C + 8;   // V^T row pitch
+  constexpr int PP = C + 8;   // probability tile pitch
+  static_assert(D % 32 == 0 && DV % 16 == 0, "head sizes");
+  __shared__ __align__(16) uint16_t k_s[C * KP];
+  __shared__ __align__(16) uint16_t vt_s[DV * VP];
+  __shared__ __align__(16) uint16_t p_s[kChunkWaves][kChunkBlockRows * PP];
+  __shared__ RowInfo info_sh;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int64_t c = blockIdx.x % a.nchunk_max;
+  const int64_t grp = blockIdx.x / a.nchunk_max;
+  const int64_t b = grp / a.Hk, kvh = grp % a.Hk;
+
+  if (wave == 0) {
+    const RowInfo ri = wave_row_info(a.lengths, a.mask, a.Q, a.M, b);
+    if (lane == 0) info_sh = ri;
+  }
+  __syncthreads();
+  const RowInfo ri = info_sh;
+  if (c == 0 && kvh == 0 && tid == 0) {
+    a.ws_rowinfo[b * 4 + 0] = ri.len;
+    a.ws_rowinfo[b * 4 + 1] = ri.n;
+    a.ws_rowinfo[b * 4 + 2] = ri.status;
+    a.ws_rowinfo[b * 4 + 3] = 0;
+  }
+  const int64_t len = ri.len, n = ri.n, new_len = len + n;
+  const int64_t s0 = c * C;
+  const int64_t s1 = s0 + C < a.M ? s0 + C : a.M;
+
+  const int64_t head = b * a.Hk + kvh;
+  const uint16_t* k_head = static_cast<const uint16_t*>(a.kc_in) + head * a.M * D;
+  const uint16_t* v_head = static_cast<const uint16_t*>(a.vc_in) + head * a.M * DV;
+  const uint16_t* nk_head = static_cast<const uint16_t*>(a.new_key) + head * a.Q * D;
+  const uint16_t* nv_head = static_cast<const uint16_t*>(a.new_value) + head * a.Q * DV;
+
+  // 1. cache writes of the slot range [s0, s1)
+  write_cache_slots(static_cast<uint8_t*>(a.kc_out) + head * a.M * D * 2,
+                    reinterpret_cast<const uint8_t*>(k_head),
+                    reinterpret_cast<const uint8_t*>(nk_head), D * 2, s0, s1, len, n,
+                    a.out_of_place != 0, tid, kChunkThreads);
+  write_cache_slots(static_cast<uint8_t*>(a.vc_out) + head * a.M * DV * 2,
+                    reinterpret_cast<const uint8_t*>(v_head),
+                    reinterpret_cast<const uint8_t*>(nv_head), DV * 2, s0, s1, len, n,
+                    a.out_of_place != 0, tid, kChunkThreads);
+  if (a.R == 0 || c >= row_chunks(len, n, C)) return;
+  const int nact = static_cast<int>((s1 < new_len ? s1 : new_len) - s0);  // visited slots
+
+  // 2. K rows and transposed V rows of the chunk into LDS
+  for (int idx = tid; idx < C * (D / 8); idx += kChunkThreads) {
+    const int slot = idx / (D / 8), part = idx % (D / 8);
+    const int64_t j = s0 + slot;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (slot < nact) v = ld_global16((j < len ? k_head + j * D : nk_head + (j - len) * D) + part * 8);
+    *reinterpret_cast<uint4*>(k_s + slot * KP + part * 8) = v;
+  }
+  for (int idx = tid; idx < C * (DV / 8); idx += kChunkThreads) {
+    const int slot = idx % C, part = idx / C;
+    const int64_t j = s0 + slot;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (slot < nact)
+      v = ld_global16((j < len ? v_head + j * DV : nv_head + (j - len) * DV) + part * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      vt_s[(part * 8 + 2 * e) * VP + slot] = static_cast<uint16_t>(w[e] & 0xffffu);
+      vt_s[(part * 8 + 2 * e + 1) * VP + slot] = static_cast<uint16_t>(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+
+  // 3. blocks of 16 packed rows, one wave each
+  const float scale = static_cast<float>(a.scale);
+  const float neg_inf = -INFINITY;
+  const int li = lane % 16, lq = lane / 16;
+  const int64_t seg = grp * a.nchunk_max + c;
+  const uint16_t* qbase = static_cast<const uint16_t*>(a.query);
+  uint16_t* att = static_cast<uint16_t*>(a.attention);
+  uint16_t* ptile = p_s[wave];
+  const int nblk = (a.R + kChunkBlockRows - 1) / kChunkBlockRows;
+  for (int blk = wave; blk < nblk; blk += kChunkWaves) {
+    // query rows as A operands: lane holds row li, dims kk*32 + 8*lq + e
+    uint4 qa[D / 32];
+    {
+      const int r = blk * kChunkBlockRows + li;
+      const int64_t g = r / a.Q, t = r % a.Q;
+      const bool ok = r < a.R && t < n;
+      const uint16_t* qrow = qbase + ((b * a.Hq + kvh * a.G + g) * a.Q + t) * D;
+#pragma unroll
+      for (int kk = 0; kk < D / 32; kk++)
+        qa[kk] = ok ? ld_global16(qrow + kk * 32 + 8 * lq) : make_uint4(0, 0, 0, 0);
+    }
+    // scores: s[jt][i] = S[4*lq + i][jt*16 + li]
+    mfma_f32x4 s[C / 16];
+#pragma unroll
+    for (int jt = 0; jt < C / 16; jt++) {
+      s[jt] = mfma_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < D / 32; kk++)
+        s[jt] = mfma_16x16x32(qa[kk], ld_lds16(k_s + (jt * 16 + li) * KP + kk * 32 + 8 * lq),
+                              s[jt]);
+    }
+    // rows of this lane's outputs: packed rows blk*16 + 4*lq + i
+    int64_t t_of[4];
+    bool row_ok[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = blk * kChunkBlockRows + 4 * lq + i;
+      t_of[i] = r % a.Q;
+      row_ok[i] = r < a.R && t_of[i] < n;
+    }
+    float sv[C / 16][4];
+#pragma unroll
+    for (int jt = 0; jt < C / 16; jt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int jl = jt * 16 + li;
+        const bool ok = row_ok[i] && jl < nact && s0 + jl <= len + t_of[i];
+        sv[jt][i] = ok ? s[jt][i] * scale : neg_inf;
+      }
+    // chunk statistics per row: over the 4 column tiles, then the 16 lanes
+    // that share lq
+    float m[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      float x = sv[0][i];
+#pragma unroll
+      for (int jt = 1; jt < C / 16; jt++) x = sv[jt][i] > x ? sv[jt][i] : x;
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        const float y = __shfl_xor(x, o);
+        x = y > x ? y : x;
+      }
+      m[i] = x;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      float x = 0.f;
+#pragma unroll
+      for (int jt = 0; jt < C / 16; jt++) {
+        const float p = sv[jt][i] == neg_inf ? 0.f : __expf(sv[jt][i] - m[i]);
+        sv[jt][i] = p;
+        x += p;
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) x += __shfl_xor(x, o);
+      l[i] = x;
+    }
+    // exp(s - m_c) into the attention buffer (visible slots) and the
+    // probability tile (bf16) for the context product
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = blk * kChunkBlockRows + 4 * lq + i;
+      const int64_t g = r / a.Q;
+      uint16_t* arow = att + ((b * a.Hq + kvh * a.G + g) * a.Q + t_of[i]) * a.M + s0;
+#pragma unroll
+      for (int jt = 0; jt < C / 16; jt++) {
+        const int jl = jt * 16 + li;
+        const uint16_t pb = f32_to_bf16(sv[jt][i]);
+        if (row_ok[i] && jl < nact && s0 + jl <= len + t_of[i]) arow[jl] = pb;
+        ptile[(4 * lq + i) * PP + jl] = pb;
+      }
+      if (li == 0 && r < a.R) {
+        if (row_ok[i]) {
+          double* cm = a.ws_chunk_ml + ((grp * a.nchunk_max + c) * a.R + r) * 2;
+          cm[0] = static_cast<double>(m[i]);
+          cm[1] = static_cast<double>(l[i]);
+        }
+        double* sm = a.ws_seg_ml + (seg * a.R + r) * 2;
+        sm[0] = static_cast<double>(m[i]);
+        sm[1] = static_cast<double>(l[i]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // context partial o = P V: A = probabilities (row li, slots kk*32 + 8*lq + e)
+    uint4 pa[C / 32];
+#pragma unroll
+    for (int kk = 0; kk < C / 32; kk++) pa[kk] = ld_lds16(ptile + li * PP + kk * 32 + 8 * lq);
+#pragma unroll
+    for (int nt = 0; nt < DV / 16; nt++) {
+      mfma_f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < C / 32; kk++)
+        o = mfma_16x16x32(pa[kk], ld_lds16(vt_s + (nt * 16 + li) * VP + kk * 32 + 8 * lq), o);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int r = blk * kChunkBlockRows + 4 * lq + i;
+        if (r < a.R) a.ws_seg_o[(seg * a.R + r) * DV + nt * 16 + li] = o[i];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the next block overwrites the tile
+  }
+}
+
+}  // namespace kvc

@@ -229,14 +229,80 @@ def test_page_face_dict_and_inplace_twin():
 
 
 def test_plan_paths():
-    """The decode-shaped workloads take the vector stream path; the chunk
-    workloads (160 packed rows) and odd head sizes take the generic one."""
+    """The decode-shaped workloads take the vector stream path, the bf16
+    chunk workload (160 packed rows) the matrix-core chunk path, the rest
+    the generic one."""
     expect = {"decode_gqa_bf16": 1, "long_decode_bf16": 1, "mha_stress_f32": 1,
-              "tiny_mixed_f32": 0}
+              "chunk_gqa_bf16": 2, "chunk_gqa_f32": 0, "tiny_mixed_f32": 0}
     for name, path in expect.items():
         w = WORKLOADS[name]
         d = kvc.KvcDims(w.B, w.Hq, w.Hk, w.Q, w.M, w.D, w.Dv)
         assert kvc.kvc_plan_step(d, kvc.dtype_code(w.torch_dtype))["path"] == path, name
+
+
+# -- the matrix-core chunk path (bf16, more than 8 packed rows) --------------
+def chunk_wl(**kw) -> Workload:
+    base = dict(name="chunk", B=2, Hq=4, Hk=1, Q=5, M=200, D=64, Dv=64, dtype="bf16",
+                len_range=(0, 190), n_rule="uniform")
+    base.update(kw)
+    return Workload(**base)
+
+
+CHUNK_CASES = [
+    chunk_wl(name="rows20_ragged"),                                   # R = 20, not a multiple of 16
+    chunk_wl(name="rows16_d128", Hq=2, Q=8, D=128, Dv=128, M=300, len_range=(0, 290)),
+    chunk_wl(name="rows12_d256", Hq=1, Q=12, D=256, Dv=256, M=130, len_range=(0, 118)),
+    chunk_wl(name="fill_to_capacity", Hq=1, Q=16, M=128, len_range=(112, 112), n_rule="all"),
+    chunk_wl(name="prefill_len0", Hq=8, Hk=2, Q=40, M=96, len_range=(0, 0), n_rule="all"),
+    chunk_wl(name="many_heads", B=3, Hq=16, Hk=2, Q=3, M=257, len_range=(0, 250)),
+]
+
+
+@pytest.mark.parametrize("mode", ["oop", "inplace"])
+@pytest.mark.parametrize("wl", CHUNK_CASES, ids=lambda w: w.name)
+def test_chunk_path_shapes(wl, mode):
+    d = kvc.KvcDims(wl.B, wl.Hq, wl.Hk, wl.Q, wl.M, wl.D, wl.Dv)
+    assert kvc.kvc_plan_step(d, kvc.dtype_code(wl.torch_dtype))["path"] == 2
+    for seed in (0, 1):
+        full_check(wl, seed, mode)
+
+
+@pytest.mark.parametrize("mode", ["oop", "inplace"])
+def test_chunk_path_rejected_rows(mode):
+    """Outside-contract rows on the chunk path: no-ops with a status."""
+    wl = chunk_wl(name="chunk_rejected", B=5, Q=5, M=70)
+    lengths = np.array([3, -1, 71, 4, 68], np.int64)
+    n = np.array([5, 1, 0, 2, 5], np.int64)
+    inp = make_inputs(wl, 4, "cpu", lengths=lengths, n=n)
+    inp["append_mask"][3] = torch.tensor([True, False, True, False, False])  # not a prefix
+    h = host_arrays(inp)
+    ref = oracle.default().step(h["query"], h["new_key"], h["new_value"], h["key_cache"],
+                                h["value_cache"], h["lengths"], h["append_mask"])
+    assert list(ref.row_status) == [0, 1, 1, 3, 2]
+    out = run_gpu({k: v.to(DEV) for k, v in inp.items()}, mode)
+    check_step(out, ref, "bf16", f"chunk_rejected/{mode}")
+
+
+def test_chunk_sequence_40_32_24():
+    """Chunks of 40, 32 and 24 tokens appended in turn through the chunk path
+    equal the oracle after every step (in place, lengths carried over)."""
+    wl = chunk_wl(name="seq", B=2, Hq=8, Hk=2, Q=40, M=400, len_range=(50, 60), n_rule="all")
+    inp = make_inputs(wl, 11, "cpu")
+    h = host_arrays(inp)
+    kc, vc, lens = h["key_cache"], h["value_cache"], h["lengths"]
+    dk, dv = inp["key_cache"].to(DEV), inp["value_cache"].to(DEV)
+    dlen = inp["lengths"].to(DEV)
+    for step, cnt in enumerate((40, 32, 24)):
+        step_in = make_inputs(wl, 100 + step, "cpu", lengths=lens, n=np.full(wl.B, cnt))
+        hs = host_arrays(step_in)
+        ref = oracle.default().step(hs["query"], hs["new_key"], hs["new_value"], kc, vc, lens,
+                                    hs["append_mask"])
+        dinp = {k: v.to(DEV) for k, v in step_in.items()}
+        dinp["key_cache"], dinp["value_cache"], dinp["lengths"] = dk, dv, dlen
+        out = run_gpu(dinp, "inplace")
+        check_step(out, ref, "bf16", f"seq step {step}")
+        kc, vc, lens = ref.key_cache, ref.value_cache, ref.lengths
+        dk, dv, dlen = out["key_cache"], out["value_cache"], out["lengths"]
 
 
 def misaligned(t: torch.Tensor) -> torch.Tensor:
