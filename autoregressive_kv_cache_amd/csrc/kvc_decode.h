@@ -301,12 +301,18 @@ __attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode
   // (packed bf16x2), or fp32 [row][slot]
   constexpr int PTILE = kBf16 ? (UV / 2) * SPLV * ROWS : ROWS * C;
   __shared__ uint32_t ptile_all[kDecodeWaves][PTILE];
+  // exp(s - m_c) of the chunk, [row][slot], so that the attention rows leave
+  // in 16-byte pieces (whole 128-byte lines when the chunk is 128 bytes)
+  constexpr int AVEC = 16 / E;  // elements per 16 bytes
+  static_assert(C % AVEC == 0, "attention pieces");
+  __shared__ __align__(16) T atile_all[kDecodeWaves][ROWS * C];
 
   const int tid = threadIdx.x, lane = tid % kWave;
   // the wave index is uniform across the wave; saying so keeps everything
   // derived from it (chunk range, rows, buffer descriptors) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   uint32_t* ptile = ptile_all[wave];
+  T* atile = atile_all[wave];
   const int ks = lane / LK, kc = lane % LK;
   const int vs = lane / LV, vc = lane % LV;
   const int my_row = kc % ROWS;  // packed row whose scores this lane finishes
@@ -510,13 +516,8 @@ __attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode
         cm[1] = static_cast<double>(l_c[r]);
       }
     }
-    // attention values exp(s - m_c), context weights p * beta into the tile
+    // attention values exp(s - m_c) and context weights p * beta into the tiles
     {
-      const int t = Q1 ? 0 : my_row % Q;
-      const int g_q = Q1 ? my_row : my_row / Q;
-      const bool row_ok = my_row < R && t < pos.n;
-      const int64_t row = (static_cast<int64_t>(pos.b) * a.Hq + pos.kvh * a.G + g_q) * Q + t;
-      T* arow = att + row * M + j0;
       Acc my_beta = beta[0];
 #pragma unroll
       for (int r = 1; r < ROWS; r++) my_beta = my_row == r ? beta[r] : my_beta;
@@ -524,7 +525,7 @@ __attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode
       for (int g = 0; g < NG; g++) {
         const int u = g * GU + kc / ROWS;  // load index of this lane's slot
         const int jl = u * SPLK + ks;
-        if (row_ok && jl < n_all) Elem<T>::store(arow + jl, p[g]);
+        Elem<T>::store(atile + my_row * C + jl, p[g]);
         if constexpr (kBf16) {
           uint16_t* ph = reinterpret_cast<uint16_t*>(ptile);
           ph[(((u / 2) * SPLV + ks) * ROWS + my_row) * 2 + (u & 1)] =
@@ -535,6 +536,26 @@ __attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode
       }
     }
     wave_lds_sync();
+    // attention rows of the chunk: lane takes AVEC consecutive slots of one
+    // packed row (the head's R rows are contiguous: row r = g * Q + t)
+    {
+      const int64_t head0 = (static_cast<int64_t>(pos.b) * a.Hq + pos.kvh * a.G) * Q;
+      T* abase = att + head0 * M + j0;
+      const bool vec16 = (reinterpret_cast<uintptr_t>(abase) & 15u) == 0 && (M % AVEC) == 0;
+#pragma unroll
+      for (int gi = lane; gi < ROWS * C / AVEC; gi += kWave) {
+        const int r = gi / (C / AVEC), s0 = (gi % (C / AVEC)) * AVEC;
+        const int t = Q1 ? 0 : r % Q;
+        if (r < R && t < pos.n && s0 < n_all) {
+          T* dst = abase + static_cast<int64_t>(r) * M + s0;
+          if (vec16 && s0 + AVEC <= n_all) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(atile + r * C + s0);
+          } else {
+            for (int k = 0; k < AVEC && s0 + k < n_all; k++) dst[k] = atile[r * C + s0 + k];
+          }
+        }
+      }
+    }
 
     // ---- V: context partials; each pair's registers reload the next V ----
 #pragma unroll
