@@ -23,9 +23,12 @@
 namespace kvc {
 
 constexpr int kPrepThreads = 1024;
+constexpr int kPrepLdsRows = 2048;  // rows whose first-chunk index stays in LDS
 
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(StepArgs a) {
   __shared__ int64_t wave_total[kPrepThreads / kWave];
+  __shared__ int64_t first_sh[kPrepLdsRows];
+  __shared__ int32_t nc_sh[kPrepLdsRows];
   __shared__ int64_t carry_sh;
   __shared__ RowInfo info_sh;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -84,6 +87,10 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(StepArgs a) {
       row[1] = ri.n;
       row[2] = ri.status;
       row[3] = before + incl - chunks;
+      if (b < kPrepLdsRows) {
+        first_sh[b] = before + incl - chunks;
+        nc_sh[b] = static_cast<int32_t>(row_chunks(ri.len, ri.n, a.C));
+      }
     }
     __syncthreads();
     if (tid == kPrepThreads - 1) carry_sh = before + incl;
@@ -98,16 +105,20 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(StepArgs a) {
     a.ws_hdr[1] = Pe;
   }
   if (Nc == 0) return;
-  // first chunk of each worker: x = floor(w * Nc / Pe) -> (b, head, chunk)
+  // first chunk of each worker: x = floor(w * Nc / Pe) -> (b, head, chunk);
+  // the search reads the row starts from LDS when they all fit there
+  const bool in_lds = a.B <= kPrepLdsRows;
   for (int64_t wk = tid; wk < Pe; wk += kPrepThreads) {
     const int64_t x = wk * Nc / Pe;
     int64_t lo = 0, hi = a.B - 1;  // last row whose first chunk index <= x
     while (lo < hi) {
       const int64_t mid = (lo + hi + 1) / 2;
-      if (a.ws_rowinfo[mid * 4 + 3] <= x) lo = mid; else hi = mid - 1;
+      const int64_t first = in_lds ? first_sh[mid] : a.ws_rowinfo[mid * 4 + 3];
+      if (first <= x) lo = mid; else hi = mid - 1;
     }
-    const int64_t nc = row_chunks(a.ws_rowinfo[lo * 4 + 0], a.ws_rowinfo[lo * 4 + 1], a.C);
-    const int64_t rel = x - a.ws_rowinfo[lo * 4 + 3];
+    const int64_t nc = in_lds ? nc_sh[lo]
+                              : row_chunks(a.ws_rowinfo[lo * 4 + 0], a.ws_rowinfo[lo * 4 + 1], a.C);
+    const int64_t rel = x - (in_lds ? first_sh[lo] : a.ws_rowinfo[lo * 4 + 3]);
     int32_t* ws = a.ws_wstart + wk * 4;
     ws[0] = static_cast<int32_t>(lo);
     ws[1] = static_cast<int32_t>(rel / nc);
