@@ -223,46 +223,30 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// The rows of one tensor a chunk visits: cached rows [0, n_old) at
-// `cached` and, out of place, appended rows [n_old, n_all) at `appended`
-// (all counts in bytes).  A zero count makes every load return zeros.
+// The rows of one tensor a chunk visits: `bytes` bytes of rows at `rows`.
+// A zero count makes every load return zeros.
 struct RowSrc {
-  const uint8_t* cached;
-  uint32_t cached_bytes;
-  const uint8_t* appended;
-  uint32_t appended_bytes;
-  uint32_t shift;  // bytes before the first appended row (n_old rows)
+  const uint8_t* rows;
+  uint32_t bytes;
 };
 
 // The 16-byte load u of a chunk (slot u * rows-per-load + lane slot; one
 // load covers 1 KB): the descriptor is rebased every 4 loads so that the
 // lane offset plus an immediate below 4 KB addresses the whole group.
-template <bool OOP>
 __device__ __forceinline__ uint4 load_one(const RowSrc& s, int u, uint32_t lane_off) {
   const uint32_t base = static_cast<uint32_t>(u / 4) * 4096u;
   const uint32_t imm = static_cast<uint32_t>(u % 4) * 1024u;
-  const uint32_t left = s.cached_bytes > base ? s.cached_bytes - base : 0u;
-  uint4 v = buf_ld16(make_rsrc(s.cached + base, left), lane_off + imm);
-  if constexpr (OOP) {
-    // out-of-range (slots before the appended rows wrap to huge offsets,
-    // slots after them are past the count) lanes read zeros
-    const uint4 x = buf_ld16(make_rsrc(s.appended, s.appended_bytes),
-                             lane_off + base + imm - s.shift);
-    v.x |= x.x;
-    v.y |= x.y;
-    v.z |= x.z;
-    v.w |= x.w;
-  }
-  return v;
+  const uint32_t left = s.bytes > base ? s.bytes - base : 0u;
+  return buf_ld16(make_rsrc(s.rows + base, left), lane_off + imm);
 }
 
-// Out of place: the copy of cached rows to the output cache (load u of the
-// chunk, same addressing as load_one; the appended rows are already there).
-__device__ __forceinline__ void store_one(uint8_t* out, uint32_t cached_bytes, int u,
+// Out of place: the copy of the visited rows to the output cache (load u of
+// the chunk, same addressing as load_one; `bytes` = 0 stores nothing).
+__device__ __forceinline__ void store_one(uint8_t* out, uint32_t bytes, int u,
                                           uint32_t lane_off, const uint4& v) {
   const uint32_t base = static_cast<uint32_t>(u / 4) * 4096u;
   const uint32_t imm = static_cast<uint32_t>(u % 4) * 1024u;
-  const uint32_t left = cached_bytes > base ? cached_bytes - base : 0u;
+  const uint32_t left = bytes > base ? bytes - base : 0u;
   buf_st16(make_rsrc(out + base, left), lane_off + imm, v);
 }
 
@@ -362,23 +346,22 @@ __attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode
     const int d = p.len - p.c * C;
     return d < 0 ? 0 : (d < n_all ? d : n_all);
   };
-  // The rows a chunk visits.  The prep kernel has already written the
-  // appended rows into the output cache: in place every visited slot is read
-  // from the cache; out of place the cached slots come from the input cache
-  // and the appended ones from the output cache.  live = false (past the last
-  // chunk): zero rows, so every path through the loop issues the same loads.
+  // The rows a chunk visits.  In place the prep kernel has written the
+  // appended rows into the cache, so every visited slot is read from it.
+  // Out of place the prep kernel has written, into the output cache, the
+  // appended rows and the cached rows of every chunk that holds appended
+  // rows: such a chunk is read from the output cache, every other chunk
+  // from the input cache (and copied to the output by this kernel).
+  // live = false (past the last chunk): zero rows, so every path through
+  // the loop issues the same loads.
   auto src_of = [&](const ChunkPos& p, bool live, const uint8_t* cin, const uint8_t* cout,
                     int rowb) {
-    RowSrc r{cin, 0u, cout, 0u, 0u};
+    RowSrc r{cin, 0u};
     if (live) {
       const int64_t g = grp_of(p);
       const int j0 = p.c * C, n_all = n_all_of(p), n_old = n_old_of(p, n_all);
-      const int cached_rows = OOP ? n_old : n_all;
-      r.cached = cin + (g * M + j0) * rowb;
-      r.cached_bytes = static_cast<uint32_t>(cached_rows) * rowb;
-      r.appended = cout + (g * M + j0 + n_old) * rowb;
-      r.appended_bytes = OOP ? static_cast<uint32_t>(n_all - n_old) * rowb : 0u;
-      r.shift = static_cast<uint32_t>(n_old) * rowb;
+      r.rows = (OOP && n_old < n_all ? cout : cin) + (g * M + j0) * rowb;
+      r.bytes = static_cast<uint32_t>(n_all) * rowb;
     }
     return r;
   };
@@ -411,9 +394,9 @@ __attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode
     const RowSrc sk = src_of(pos, true, kin, kout, KROW);
     const RowSrc sv = src_of(pos, true, vin, vout, VROW);
 #pragma unroll
-    for (int u = 0; u < UK; u++) kbuf[u] = load_one<OOP>(sk, u, k_off);
+    for (int u = 0; u < UK; u++) kbuf[u] = load_one(sk, u, k_off);
 #pragma unroll
-    for (int u = 0; u < UV; u++) vbuf[u] = load_one<OOP>(sv, u, v_off);
+    for (int u = 0; u < UV; u++) vbuf[u] = load_one(sv, u, v_off);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -422,6 +405,9 @@ __attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode
     const int j0 = pos.c * C;
     const int n_all = n_all_of(pos);         // visited slots of the chunk
     const int n_old = n_old_of(pos, n_all);  // cached ones; [n_old, n_all) are appended
+    // out of place: rows this kernel copies to the output cache
+    const uint32_t kcopy = n_old == n_all ? static_cast<uint32_t>(n_all) * KROW : 0u;
+    const uint32_t vcopy = n_old == n_all ? static_cast<uint32_t>(n_all) * VROW : 0u;
 
     // ---- the next chunk: its position and sources ----
     ChunkPos nxt = pos;
@@ -456,7 +442,7 @@ __attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode
         if constexpr (OOP) {
 #pragma unroll
           for (int gu = 0; gu < GU; gu++)
-            store_one(kout + (grp * M + j0) * KROW, static_cast<uint32_t>(n_old) * KROW,
+            store_one(kout + (grp * M + j0) * KROW, kcopy,
                       g * GU + gu, k_off, kbuf[g * GU + gu]);
         }
         Acc part[LK];
@@ -465,7 +451,7 @@ __attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode
 #pragma unroll
           for (int r = 0; r < ROWS; r++) part[gu * ROWS + r] = Mth::dot(qf[r], kbuf[g * GU + gu]);
 #pragma unroll
-        for (int gu = 0; gu < GU; gu++) kbuf[g * GU + gu] = load_one<OOP>(nk, g * GU + gu, k_off);
+        for (int gu = 0; gu < GU; gu++) kbuf[g * GU + gu] = load_one(nk, g * GU + gu, k_off);
         __builtin_amdgcn_sched_barrier(0);
         reduce_scatter<LK / 2, LK>(part, kc);
         // visible: an existing row whose token t is appended (t < n) and
@@ -568,9 +554,9 @@ __attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode
 #pragma unroll
       for (int j = 0; j < UV / 2; j++) {
         if constexpr (OOP) {
-          store_one(vout + (grp * M + j0) * VROW, static_cast<uint32_t>(n_old) * VROW, 2 * j,
+          store_one(vout + (grp * M + j0) * VROW, vcopy, 2 * j,
                     v_off, vbuf[2 * j]);
-          store_one(vout + (grp * M + j0) * VROW, static_cast<uint32_t>(n_old) * VROW, 2 * j + 1,
+          store_one(vout + (grp * M + j0) * VROW, vcopy, 2 * j + 1,
                     v_off, vbuf[2 * j + 1]);
         }
         uint32_t pp[ROWS];
@@ -588,8 +574,8 @@ __attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode
         }
         // the registers are free again: the next chunk's V goes into them
         // (a load into a register still in use would need a copy per chunk)
-        vbuf[2 * j] = load_one<OOP>(nv, 2 * j, v_off);
-        vbuf[2 * j + 1] = load_one<OOP>(nv, 2 * j + 1, v_off);
+        vbuf[2 * j] = load_one(nv, 2 * j, v_off);
+        vbuf[2 * j + 1] = load_one(nv, 2 * j + 1, v_off);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int e = 0; e < 4; e++) {
@@ -604,7 +590,7 @@ __attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode
 #pragma unroll
       for (int u = 0; u < UV; u++) {
         if constexpr (OOP)
-          store_one(vout + (grp * M + j0) * VROW, static_cast<uint32_t>(n_old) * VROW, u, v_off,
+          store_one(vout + (grp * M + j0) * VROW, vcopy, u, v_off,
                     vbuf[u]);
         const int jl = u * SPLV + vs;
 #pragma unroll
@@ -615,7 +601,7 @@ __attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode
           o_acc[r][2] += pr * __uint_as_float(vbuf[u].z);
           o_acc[r][3] += pr * __uint_as_float(vbuf[u].w);
         }
-        vbuf[u] = load_one<OOP>(nv, u, v_off);
+        vbuf[u] = load_one(nv, u, v_off);
         __builtin_amdgcn_sched_barrier(0);
       }
     }

@@ -5,8 +5,9 @@
 // behavior) defines it -- n = count of the True prefix of append_mask[b,:],
 // 0 <= length <= M, length + n <= M; a broken row becomes a no-op with a
 // status -- and writes new_key/new_value row t to slot length + t of the
-// destination cache for every KV head (the append itself; nothing else of
-// the cache is touched here).
+// destination cache for every KV head (the append itself).  Out of place it
+// also copies the cached rows of the chunk the first new row falls in, so
+// that every chunk holding new rows is whole in the output cache.
 //
 // Workgroup B: the same row information for all rows, the number of C-slot
 // chunks each KV head needs, the exclusive prefix sum of Hk * chunks over b
@@ -54,6 +55,18 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(StepArgs a) {
         const int64_t h = i / (ri.n * n16), rem = i % (ri.n * n16);
         const int64_t t = rem / n16, k = rem % n16;
         dst[((b * a.Hk + h) * a.M + ri.len + t) * n16 + k] = src[((b * a.Hk + h) * a.Q + t) * n16 + k];
+      }
+      if (a.out_of_place) {
+        // the cached rows of the chunk that receives the first new row, so
+        // that the attend kernel finds that chunk whole in the output cache
+        const uint4* in = static_cast<const uint4*>(which == 0 ? a.kc_in : a.vc_in);
+        const int64_t r0 = (ri.len / a.C) * a.C, nr = ri.len - r0;
+        const int64_t ctotal = a.Hk * nr * n16;
+        for (int64_t i = tid; i < ctotal; i += kPrepThreads) {
+          const int64_t h = i / (nr * n16), rem = i % (nr * n16);
+          const int64_t idx = ((b * a.Hk + h) * a.M + r0) * n16 + rem;
+          dst[idx] = in[idx];
+        }
       }
     }
     return;
