@@ -55,12 +55,13 @@ void launch_decode(const StepArgs& a, hipStream_t s) {
 }
 
 struct DecodeEntry {
-  int dtype, D, Dv, rows, chunk;
+  int dtype, D, Dv, rows, chunk, wgs_per_cu;
   void (*launch)(const StepArgs&, hipStream_t);
 };
 
 #define KVC_DECODE(T, CODE, D, DV, ROWS) \
-  {CODE, D, DV, ROWS, kvc::decode_chunk<T, D, DV, ROWS>(), &launch_decode<T, D, DV, ROWS>}
+  {CODE, D, DV, ROWS, kvc::decode_chunk<T, D, DV, ROWS>(), kvc::decode_waves_per_simd<ROWS>(), \
+   &launch_decode<T, D, DV, ROWS>}
 const DecodeEntry kDecodeTable[] = {
     KVC_DECODE(kvc::bf16, KVC_BF16, 128, 128, 4), KVC_DECODE(kvc::bf16, KVC_BF16, 128, 128, 8),
     KVC_DECODE(kvc::bf16, KVC_BF16, 64, 64, 4),   KVC_DECODE(kvc::bf16, KVC_BF16, 64, 64, 8),
@@ -70,10 +71,10 @@ const DecodeEntry kDecodeTable[] = {
 };
 #undef KVC_DECODE
 
-// Stream path: MI355X has 256 compute units; a few resident attend
-// workgroups (of 4 waves, each wave one stream worker) per unit keep enough
+// Stream path: MI355X has 256 compute units; every unit holds as many
+// attend workgroups (of 4 waves, one per SIMD, each wave one stream worker)
+// as the kernel's registers allow, and each wave keeps a whole chunk of
 // loads in flight.
-constexpr int64_t kStreamWorkgroupsPerCU = 2;
 constexpr int64_t kComputeUnits = 256;
 // Slots per combine workgroup (a multiple of every chunk size).
 constexpr int64_t kCombineSlots = 2048;
@@ -183,7 +184,7 @@ int make_plan(const kvc_dims* d, int dtype, Plan* p) {
   p->pub.rows = static_cast<int32_t>(R);
   p->decode = find_decode(d, dtype, R);
   p->chunk = p->decode ? nullptr : find_chunk(d, dtype, R);
-  p->P = kComputeUnits * kStreamWorkgroupsPerCU * kvc::kDecodeWaves;
+  p->P = p->decode ? kComputeUnits * p->decode->wgs_per_cu * kvc::kDecodeWaves : 0;
   const int64_t row_tiles = R == 0 ? 1 : (R + kvc::kGenericRowsPerTile - 1) / kvc::kGenericRowsPerTile;
   if (!make_layout(d, R, kvc::kGenericChunk, false, 0, &p->generic)) return KVC_ERR_SHAPE;
   int64_t wgs;

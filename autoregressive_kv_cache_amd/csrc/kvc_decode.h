@@ -203,18 +203,23 @@ __device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off,
 }
 
 // Chunk size: one wave's chunk is at most 64 slots and at most 16 loads of
-// 16 bytes per lane for K and for V (8 when 8 packed rows or fp32 scores
-// need the registers), since both tensors' loads are in flight at once.
+// 16 bytes per lane for K and for V (8 when fp32 scores need the
+// registers), since both tensors' loads are in flight at once.
 template <typename T, int D, int DV, int ROWS>
 constexpr int decode_chunk() {
   constexpr int E = sizeof(T);
   constexpr int spl_k = kWave / (D * E / 16), spl_v = kWave / (DV * E / 16);
   constexpr int spl = spl_k < spl_v ? spl_k : spl_v;
-#ifndef KVC_DECODE_LOADS
-#define KVC_DECODE_LOADS 16
-#endif
-  constexpr int loads = (E == 4 || ROWS > 4) ? 8 : KVC_DECODE_LOADS;
+  constexpr int loads = E == 4 ? 8 : 16;
   return loads * spl < kWave ? loads * spl : kWave;
+}
+
+// Resident waves per SIMD the decode kernel is built for: 8 packed rows
+// (their context accumulators and query rows) need a SIMD's whole register
+// file; the grid then holds one workgroup per compute unit.
+template <int ROWS>
+constexpr int decode_waves_per_simd() {
+  return ROWS > 4 ? 1 : 2;
 }
 
 // Wave-local ordering of LDS accesses (all lanes of one wave).
@@ -256,13 +261,9 @@ struct ChunkPos {
   int len, n, nc;  // the row's old length, appended rows, chunks per head
 };
 
-#ifndef KVC_DECODE_WAVES_PER_EU
-#define KVC_DECODE_WAVES_PER_EU 2
-#endif
-
 template <typename T, int D, int DV, int ROWS, bool Q1, bool OOP>
 __global__ __launch_bounds__(kDecodeThreads)
-__attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU))) void attend_decode_kernel(
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_decode_kernel(
     StepArgs a, const int64_t* __restrict__ rowinfo, const int32_t* __restrict__ wstart) {
   using Mth = DecodeMath<T>;
   using Acc = typename Mth::Acc;
