@@ -38,12 +38,19 @@ void launch_decode_q(const StepArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.P / kvc::kDecodeWaves)), block(kvc::kDecodeThreads);
   const int64_t* ri = a.ws_rowinfo;
   const int32_t* wst = a.ws_wstart;
-  if (a.out_of_place)
-    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, true>), grid, block, 0, s,
-                       a, ri, wst);
+  const bool fused = a.B <= kvc::kDecodeFusedRows;
+  if (a.out_of_place && fused)
+    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, true, true>), grid, block, 0,
+                       s, a, ri, wst);
+  else if (a.out_of_place)
+    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, true, false>), grid, block, 0,
+                       s, a, ri, wst);
+  else if (fused)
+    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, false, true>), grid, block, 0,
+                       s, a, ri, wst);
   else
-    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, false>), grid, block, 0, s,
-                       a, ri, wst);
+    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, false, false>), grid, block,
+                       0, s, a, ri, wst);
 }
 
 template <typename T, int D, int DV, int ROWS>
@@ -121,7 +128,9 @@ struct Layout {
 bool make_layout(const kvc_dims* d, int64_t R, int64_t C, bool stream,
                  int64_t P, Layout* L) {
   L->C = C;
-  L->nchunk_max = (d->M + C - 1) / C;
+  // stream mode: the cached slots in chunks of C plus one chunk of the
+  // appended rows per head
+  L->nchunk_max = (d->M + C - 1) / C + (stream ? 1 : 0);
   L->CS = kCombineSlots;
   int64_t groups, chunks, nseg, x;
   if (!mul_ok(d->B, d->Hk, kMaxElems, &groups) || !mul_ok(groups, L->nchunk_max, kMaxElems, &chunks))
@@ -258,6 +267,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 void set_layout(StepArgs& a, const Layout& L, void* workspace) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   a.C = L.C;
+  a.C_log2 = 0;
+  while ((int64_t(1) << a.C_log2) < L.C) a.C_log2++;
   a.nchunk_max = L.nchunk_max;
   a.CS = L.CS;
   a.ws_hdr = reinterpret_cast<int64_t*>(ws + L.off_hdr);
@@ -299,8 +310,9 @@ void launch_dense_chunk(StepArgs& a, const ChunkEntry& e, hipStream_t stream,
 template <typename T>
 void launch_stream(StepArgs& a, const DecodeEntry& e, hipStream_t stream, const kvc_events* ev) {
   const int64_t groups = a.B * a.Hk;
-  hipLaunchKernelGGL(kvc::prep_kernel, dim3(static_cast<unsigned>(a.B + 1)),
-                     dim3(kvc::kPrepThreads), 0, stream, a);
+  // up to kDecodeFusedRows rows the attend kernel prepares the rows itself
+  if (a.B > kvc::kDecodeFusedRows)
+    hipLaunchKernelGGL(kvc::prep_kernel, dim3(1), dim3(kvc::kPrepThreads), 0, stream, a);
   if (ev && ev->start) hipEventRecord(static_cast<hipEvent_t>(ev->start), stream);
   e.launch(a, stream);
   if (ev && ev->stop) hipEventRecord(static_cast<hipEvent_t>(ev->stop), stream);

@@ -64,6 +64,17 @@ struct Vec8<bf16> {
       w[k] = lo | (hi << 16);
     }
   }
+  // elements [0, k) scaled by f_lo, the others by f_hi
+  __device__ __forceinline__ void scale_split(float f_lo, float f_hi, int k) {
+    uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const uint32_t lo = f32_to_bf16(__uint_as_float(w[e] << 16) * (2 * e < k ? f_lo : f_hi));
+      const uint32_t hi =
+          f32_to_bf16(__uint_as_float(w[e] & 0xffff0000u) * (2 * e + 1 < k ? f_lo : f_hi));
+      w[e] = lo | (hi << 16);
+    }
+  }
   __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
   // keep elements [0, cnt), zero the others (no indexed access: the vector
   // stays in registers)
@@ -90,6 +101,16 @@ struct Vec8<float> {
     a.z = static_cast<float>(a.z * f); a.w = static_cast<float>(a.w * f);
     b.x = static_cast<float>(b.x * f); b.y = static_cast<float>(b.y * f);
     b.z = static_cast<float>(b.z * f); b.w = static_cast<float>(b.w * f);
+  }
+  __device__ __forceinline__ void scale_split(double f_lo, double f_hi, int k) {
+    a.x = static_cast<float>(a.x * (k > 0 ? f_lo : f_hi));
+    a.y = static_cast<float>(a.y * (k > 1 ? f_lo : f_hi));
+    a.z = static_cast<float>(a.z * (k > 2 ? f_lo : f_hi));
+    a.w = static_cast<float>(a.w * (k > 3 ? f_lo : f_hi));
+    b.x = static_cast<float>(b.x * (k > 4 ? f_lo : f_hi));
+    b.y = static_cast<float>(b.y * (k > 5 ? f_lo : f_hi));
+    b.z = static_cast<float>(b.z * (k > 6 ? f_lo : f_hi));
+    b.w = static_cast<float>(b.w * (k > 7 ? f_lo : f_hi));
   }
   __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
   __device__ __forceinline__ void keep_first(int cnt) {
@@ -127,7 +148,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
   const int64_t len = a.ws_rowinfo[b * 4 + 0];
   const int64_t n = a.ws_rowinfo[b * 4 + 1];
   const int32_t status = static_cast<int32_t>(a.ws_rowinfo[b * 4 + 2]);
-  const int64_t nc = row_chunks(len, n, a.C);
+  const int64_t nc = a.seg_mode ? stream_chunks(len, n, a.C) : row_chunks(len, n, a.C);
+  // chunk holding slot j (stream mode: the appended rows are a chunk of
+  // their own, so an 8-slot vector may straddle two chunks at slot len)
+  const int64_t len_chunks = (len + a.C - 1) >> a.C_log2;  // cached chunks (stream mode)
+  auto chunk_of = [&](int64_t j) {
+    return a.seg_mode && j >= len ? len_chunks : j >> a.C_log2;
+  };
 
   if (k == 0 && kvh == 0 && rb == 0 && tid == 0) {
     a.lengths_out[b] = len + n;
@@ -136,6 +163,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
   const int64_t e0 = ctx_role ? a.M : k * a.CS;
   const int64_t e1 = e0 + a.CS < a.M ? e0 + a.CS : a.M;
 
+  if (ctx_role && rb == 0 && a.seg_mode && !a.out_of_place && n > 0) {
+    // in place, stream path: the appended rows go to their cache slots
+    // (the attend kernel read them from new_key / new_value)
+    const int64_t kb = a.D * E::kBytes, vb = a.Dv * E::kBytes;
+    copy_bytes(static_cast<uint8_t*>(a.kc_out) + (grp * a.M + len) * kb,
+               static_cast<const uint8_t*>(a.new_key) + grp * a.Q * kb, n * kb, tid,
+               kCombineThreads);
+    copy_bytes(static_cast<uint8_t*>(a.vc_out) + (grp * a.M + len) * vb,
+               static_cast<const uint8_t*>(a.new_value) + grp * a.Q * vb, n * vb, tid,
+               kCombineThreads);
+  }
   if (rb == 0 && a.out_of_place && a.combine_copies_tail) {
     const int64_t cover = n > 0 ? len + n : 0;
     const int64_t j0 = e0 > cover ? e0 : cover;
@@ -169,18 +207,22 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
   // ---- first pass of the range: its loads go out before the statistics ----
   const int64_t nvec = (e1 - e0) / 8;
   Vec8<T> x[VPL];
-  double mc[VPL];
+  Acc mc[VPL], mc_hi[VPL];
+  int split[VPL];  // elements of the vector in the chunk of its first slot
+  auto load_vec = [&](int v, int64_t vi) {
+    const int64_t base = e0 + vi * 8;
+    const bool live = vi < nvec && base < lim;
+    // the vector's last slot may lie in the next chunk (stream mode, at len)
+    const int64_t last = base + 7 < lim ? base + 7 : lim - 1;
+    x[v].zero();
+    if (live) x[v].load(arow + base);
+    mc[v] = live ? static_cast<Acc>(chunk_ml[(chunk_of(base) * a.R + r) * 2]) : neg_inf;
+    mc_hi[v] = live ? static_cast<Acc>(chunk_ml[(chunk_of(last) * a.R + r) * 2]) : neg_inf;
+    split[v] = a.seg_mode && base < len && base + 8 > len ? static_cast<int>(len - base) : 8;
+  };
   if (vec) {
 #pragma unroll
-    for (int v = 0; v < VPL; v++) {
-      const int64_t base = e0 + (v * kWave + lane) * 8;
-      x[v].zero();
-      mc[v] = -INFINITY;
-      if (v * kWave + lane < nvec && base < lim) {
-        x[v].load(arow + base);
-        mc[v] = chunk_ml[((base / a.C) * a.R + r) * 2];
-      }
-    }
+    for (int v = 0; v < VPL; v++) load_vec(v, v * kWave + lane);
   }
 
   // segment statistics of the first kWave segments (lane s holds segment s)
@@ -234,32 +276,21 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
     }
   }
   const Acc inv_l = l > 0 ? Acc(1) / l : Acc(0);
-  auto factor = [&](double m_c) -> Acc {
-    const Acc mcv = static_cast<Acc>(m_c);
-    return mcv == neg_inf ? Acc(0) : acc_exp(mcv - m) * inv_l;
-  };
+  auto factor = [&](Acc m_c) -> Acc { return m_c == neg_inf ? Acc(0) : acc_exp(m_c - m) * inv_l; };
 
   // ---- rescale the visible slots, zero the rest ----
   if (vec) {
     for (int64_t v0 = 0; v0 < nvec; v0 += VPL * kWave) {
       if (v0 > 0) {  // later passes (ranges longer than VPL * 512 slots)
 #pragma unroll
-        for (int v = 0; v < VPL; v++) {
-          const int64_t base = e0 + (v0 + v * kWave + lane) * 8;
-          x[v].zero();
-          mc[v] = -INFINITY;
-          if (v0 + v * kWave + lane < nvec && base < lim) {
-            x[v].load(arow + base);
-            mc[v] = chunk_ml[((base / a.C) * a.R + r) * 2];
-          }
-        }
+        for (int v = 0; v < VPL; v++) load_vec(v, v0 + v * kWave + lane);
       }
 #pragma unroll
       for (int v = 0; v < VPL; v++) {
         const int64_t base = e0 + (v0 + v * kWave + lane) * 8;
         if (v0 + v * kWave + lane < nvec) {
           if (base < lim) {
-            x[v].scale_by(factor(mc[v]));
+            x[v].scale_split(factor(mc[v]), factor(mc_hi[v]), split[v]);
             if (base + 8 > lim) x[v].keep_first(static_cast<int>(lim - base));
           }
           x[v].store(arow + base);
@@ -269,7 +300,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
   } else {
     for (int64_t j = e0 + lane; j < e1; j += kWave) {
       if (j < lim)
-        E::store(arow + j, E::load(arow + j) * factor(chunk_ml[((j / a.C) * a.R + r) * 2]));
+        E::store(arow + j, E::load(arow + j) *
+                               factor(static_cast<Acc>(chunk_ml[(chunk_of(j) * a.R + r) * 2])));
       else
         arow[j] = E::zero();
     }
@@ -288,9 +320,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
       // weight of segment s0 + lane; broadcast one segment at a time
       Acc w = 0;
       if (s0 == 0) {
-        w = factor(seg_m0);
+        w = factor(static_cast<Acc>(seg_m0));
       } else if (s0 + lane < sr.count) {
-        w = factor(a.ws_seg_ml[((sr.first + s0 + lane) * a.R + r) * 2]);
+        w = factor(static_cast<Acc>(a.ws_seg_ml[((sr.first + s0 + lane) * a.R + r) * 2]));
       }
       const int64_t ns = sr.count - s0 < kWave ? sr.count - s0 : kWave;
       for (int64_t s1 = 0; s1 < ns; s1 += SB) {

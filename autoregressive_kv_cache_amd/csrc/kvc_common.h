@@ -55,8 +55,10 @@ __device__ __forceinline__ float acc_exp(float x) { return __expf(x); }
 
 // Everything one step's kernels need; passed by value as the kernel argument.
 //
-// Work is cut into chunks of C cache slots per (batch row b, KV head h):
-// chunk c of group g = b * Hk + h covers slots [c*C, min((c+1)*C, len+n)).
+// Work is cut into chunks of C cache slots per (batch row b, KV head h).
+// Dense mode: chunk c of group g = b * Hk + h covers slots
+// [c*C, min((c+1)*C, len+n)).  Stream mode: see stream_chunks (the cached
+// slots in chunks of C, then one chunk of the appended rows).
 // For every chunk the attend kernel leaves, per packed query row r,
 //   chunk statistics  m_c = max_j s_j,  l_c = sum_j exp(s_j - m_c),
 //   exp(s_j - m_c) in the attention buffer,
@@ -76,7 +78,8 @@ struct StepArgs {
   int32_t R;          // packed rows per KV head = G * Q (row r = g * Q + t)
   int32_t rows_per_tile;
   int32_t row_tiles;
-  int64_t C;          // slots per chunk
+  int64_t C;          // slots per chunk (a power of two)
+  int32_t C_log2;     // log2(C)
   int64_t nchunk_max; // ceil(M / C)
   int64_t CS;         // slots per combine workgroup (a multiple of C)
   int64_t P;          // stream workers (waves of the attend grid, stream mode)
@@ -183,6 +186,19 @@ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 // query can see (all slots < length + n); 0 when the row appends nothing.
 __device__ __forceinline__ int64_t row_chunks(int64_t len, int64_t n, int64_t C) {
   return n > 0 ? ceil_div(len + n, C) : 0;
+}
+
+// Stream path: the chunks of one batch row's KV head are the cached slots
+// [0, length) cut into ceil(length / C) chunks (the last one partial) and
+// one more chunk with the n appended rows (slots [length, length + n), read
+// from new_key / new_value); 0 chunks when the row appends nothing.  Slot
+// j < length lies in chunk j / C, an appended slot in chunk
+// ceil(length / C).
+__device__ __forceinline__ int64_t stream_chunks(int64_t len, int64_t n, int64_t C) {
+  return n > 0 ? ceil_div(len, C) + 1 : 0;
+}
+__device__ __forceinline__ int64_t stream_chunk_of(int64_t j, int64_t len, int64_t C) {
+  return j < len ? j / C : ceil_div(len, C);
 }
 
 // Row preparation by one thread (same checks, same order as wave_row_info).

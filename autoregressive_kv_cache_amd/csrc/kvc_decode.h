@@ -26,9 +26,14 @@
 //     into its running segment statistics;
 //   - accumulates the context partial o += p * v (bf16: p rounded to bf16,
 //     two slots per v_dot2; fp32: fp32 FMAs).
-// The same loads feed the cache writes: out of place every visited slot is
-// stored to the output cache (the copy the page's contract requires), in
-// place only the appended rows are stored.
+// The chunks of a (batch row, KV head) are its cached slots in chunks of C
+// and one last chunk with the appended rows, read from new_key/new_value
+// (stream_chunks).  Out of place the same loads feed the cache copy the
+// page's contract requires (every visited slot is stored to the output
+// cache); in place the appended rows are stored by the combine kernel,
+// which runs after this one.  So no kernel has to run before this one: for
+// batches of up to kDecodeFusedRows rows each workgroup also works out the
+// row information itself (FUSED).
 //
 // The step follows "Autoregressive KV-cache append and causal attention",
 // Required behavior: KV head floor(h / (Hq/Hk)) per query head, slot
@@ -255,13 +260,17 @@ __device__ __forceinline__ void store_one(uint8_t* out, uint32_t bytes, int u,
   buf_st16(make_rsrc(out + base, left), lane_off + imm, v);
 }
 
+// Batches of up to this many rows are prepared by the decode kernel itself
+// (a row table in LDS); larger ones by the prep kernel.
+constexpr int kDecodeFusedRows = 1024;
+
 // Position of a wave in the flattened chunk list (all fields wave-uniform).
 struct ChunkPos {
   int b, kvh, c;   // batch row, KV head, chunk within the head
   int len, n, nc;  // the row's old length, appended rows, chunks per head
 };
 
-template <typename T, int D, int DV, int ROWS, bool Q1, bool OOP>
+template <typename T, int D, int DV, int ROWS, bool Q1, bool OOP, bool FUSED>
 __global__ __launch_bounds__(kDecodeThreads)
 __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_decode_kernel(
     StepArgs a, const int64_t* __restrict__ rowinfo, const int32_t* __restrict__ wstart) {
@@ -282,6 +291,8 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
   static_assert(UK >= 1 && UK <= 16 && UV >= 1 && UV <= 16 && UK % GU == 0, "chunk shape");
   static_assert(!kBf16 || (D == DV && UV % 2 == 0), "bf16 context pairs slots of equal layout");
   static_assert(SPLK * KROW == 1024 && SPLV * VROW == 1024, "one load covers 1 KB");
+  static_assert((C & (C - 1)) == 0, "chunk sizes are powers of two (the combine shifts by log2 C)");
+
   // probabilities for the context step: bf16 pairs [slot pair][slot lane][row]
   // (packed bf16x2), or fp32 [row][slot]
   constexpr int PTILE = kBf16 ? (UV / 2) * SPLV * ROWS : ROWS * C;
@@ -291,6 +302,11 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
   constexpr int AVEC = 16 / E;  // elements per 16 bytes
   static_assert(C % AVEC == 0, "attention pieces");
   __shared__ __align__(16) T atile_all[kDecodeWaves][ROWS * C];
+  // FUSED: every batch row's old length, appended count and first chunk
+  constexpr int RT = FUSED ? kDecodeFusedRows : 1;
+  __shared__ int32_t rt_len[RT], rt_n[RT];
+  __shared__ int64_t rt_first[RT];
+  __shared__ int64_t rt_total;
 
   const int tid = threadIdx.x, lane = tid % kWave;
   // the wave index is uniform across the wave; saying so keeps everything
@@ -310,26 +326,83 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
   const int Hk = static_cast<int>(a.Hk);
   const int64_t M = a.M;
 
-  // rowinfo and the header are written by the prep kernel and only read
-  // here; hdr: [0] total chunks, [1] busy stream workers (<= Nc, <= waves)
-  const int64_t Nc = a.ws_hdr[0];
-  const int64_t Pw = a.ws_hdr[1];
+  // Row information.  FUSED: the workgroup builds the table of every batch
+  // row (the prep kernel's checks, each row's first chunk in the flattened
+  // list) in LDS, and workgroup 0 publishes it for the combine kernel;
+  // otherwise the prep kernel has written it and every worker's start.
+  // hdr: [0] total chunks Nc, [1] busy stream workers Pe = min(P, Nc).
+  auto row_len = [&](int b) { return FUSED ? rt_len[b] : static_cast<int>(rowinfo[b * 4 + 0]); };
+  auto row_n = [&](int b) { return FUSED ? rt_n[b] : static_cast<int>(rowinfo[b * 4 + 1]); };
+  int64_t Nc, Pw;
+  if constexpr (FUSED) {
+    for (int b = tid; b < a.B; b += kDecodeThreads) {
+      const RowInfo ri = thread_row_info(a.lengths, a.mask, a.Q, a.M, b);
+      rt_len[b] = static_cast<int32_t>(ri.len);
+      rt_n[b] = static_cast<int32_t>(ri.n);
+      if (blockIdx.x == 0) {
+        a.ws_rowinfo[b * 4 + 0] = ri.len;
+        a.ws_rowinfo[b * 4 + 1] = ri.n;
+        a.ws_rowinfo[b * 4 + 2] = ri.status;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {  // exclusive prefix of Hk * chunks over the rows
+      int64_t carry = 0;
+      for (int base = 0; base < a.B; base += kWave) {
+        const int b = base + lane;
+        const int64_t ch = b < a.B ? Hk * stream_chunks(rt_len[b], rt_n[b], C) : 0;
+        int64_t incl = ch;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int64_t up = __shfl_up(incl, o);
+          if (lane >= o) incl += up;
+        }
+        if (b < a.B) rt_first[b] = carry + incl - ch;
+        carry += __shfl(incl, kWave - 1);
+      }
+      if (lane == 0) rt_total = carry;
+    }
+    __syncthreads();
+    Nc = rt_total;
+    Pw = Nc < a.P ? (Nc > 0 ? Nc : 1) : a.P;
+    if (blockIdx.x == 0) {
+      for (int b = tid; b < a.B; b += kDecodeThreads) a.ws_rowinfo[b * 4 + 3] = rt_first[b];
+      if (tid == 0) {
+        a.ws_hdr[0] = Nc;
+        a.ws_hdr[1] = Pw;
+      }
+    }
+  } else {
+    Nc = a.ws_hdr[0];
+    Pw = a.ws_hdr[1];
+  }
   const int64_t w = blockIdx.x * static_cast<int64_t>(kDecodeWaves) + wave;
   if (w >= Pw) return;
   const int64_t x_begin = w * Nc / Pw, x_end = (w + 1) * Nc / Pw;
   if (x_begin >= x_end) return;  // no chunks at all (Nc = 0)
 
-  // first chunk of this worker (found by the prep kernel)
+  // first chunk of this worker
   ChunkPos pos;
-  {
+  if constexpr (FUSED) {
+    int lo = 0, hi = static_cast<int>(a.B) - 1;  // last row whose first chunk <= x_begin
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (rt_first[mid] <= x_begin) lo = mid; else hi = mid - 1;
+    }
+    const int nc = static_cast<int>(stream_chunks(rt_len[lo], rt_n[lo], C));
+    const int64_t rel = x_begin - rt_first[lo];
+    pos.b = lo;
+    pos.kvh = static_cast<int>(rel / nc);
+    pos.c = static_cast<int>(rel % nc);
+  } else {
     const int4 st = *reinterpret_cast<const int4*>(wstart + w * 4);
     pos.b = st.x;
     pos.kvh = st.y;
     pos.c = st.z;
-    pos.len = static_cast<int>(rowinfo[pos.b * 4 + 0]);
-    pos.n = static_cast<int>(rowinfo[pos.b * 4 + 1]);
-    pos.nc = static_cast<int>(row_chunks(pos.len, pos.n, C));
   }
+  pos.len = row_len(pos.b);
+  pos.n = row_n(pos.b);
+  pos.nc = static_cast<int>(stream_chunks(pos.len, pos.n, C));
 
   const uint8_t* qbase = static_cast<const uint8_t*>(a.query);
   const uint8_t* kin = static_cast<const uint8_t*>(a.kc_in);
@@ -339,30 +412,24 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
   T* att = static_cast<T*>(a.attention);
 
   auto grp_of = [&](const ChunkPos& p) { return static_cast<int64_t>(p.b) * Hk + p.kvh; };
+  // the last chunk of a head holds its appended rows, the others cached ones
+  auto is_new_of = [&](const ChunkPos& p) { return p.c == p.nc - 1; };
+  auto j0_of = [&](const ChunkPos& p) { return is_new_of(p) ? p.len : p.c * C; };
   auto n_all_of = [&](const ChunkPos& p) {
-    const int j0 = p.c * C, new_len = p.len + p.n;
-    return (j0 + C < new_len ? j0 + C : new_len) - j0;
+    return is_new_of(p) ? p.n : (p.c * C + C < p.len ? C : p.len - p.c * C);
   };
-  auto n_old_of = [&](const ChunkPos& p, int n_all) {
-    const int d = p.len - p.c * C;
-    return d < 0 ? 0 : (d < n_all ? d : n_all);
-  };
-  // The rows a chunk visits.  In place the prep kernel has written the
-  // appended rows into the cache, so every visited slot is read from it.
-  // Out of place the prep kernel has written, into the output cache, the
-  // appended rows and the cached rows of every chunk that holds appended
-  // rows: such a chunk is read from the output cache, every other chunk
-  // from the input cache (and copied to the output by this kernel).
+  // The rows a chunk visits: cached rows from the input cache, appended rows
+  // from new_key / new_value (row t of the head's new rows is slot len + t).
   // live = false (past the last chunk): zero rows, so every path through
   // the loop issues the same loads.
-  auto src_of = [&](const ChunkPos& p, bool live, const uint8_t* cin, const uint8_t* cout,
+  auto src_of = [&](const ChunkPos& p, bool live, const uint8_t* cin, const void* fresh,
                     int rowb) {
     RowSrc r{cin, 0u};
     if (live) {
       const int64_t g = grp_of(p);
-      const int j0 = p.c * C, n_all = n_all_of(p), n_old = n_old_of(p, n_all);
-      r.rows = (OOP && n_old < n_all ? cout : cin) + (g * M + j0) * rowb;
-      r.bytes = static_cast<uint32_t>(n_all) * rowb;
+      r.rows = is_new_of(p) ? static_cast<const uint8_t*>(fresh) + g * Q * rowb
+                            : cin + (g * M + p.c * C) * rowb;
+      r.bytes = static_cast<uint32_t>(n_all_of(p)) * rowb;
     }
     return r;
   };
@@ -392,8 +459,8 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
   }
   load_q(qf, pos, true);
   {
-    const RowSrc sk = src_of(pos, true, kin, kout, KROW);
-    const RowSrc sv = src_of(pos, true, vin, vout, VROW);
+    const RowSrc sk = src_of(pos, true, kin, a.new_key, KROW);
+    const RowSrc sv = src_of(pos, true, vin, a.new_value, VROW);
 #pragma unroll
     for (int u = 0; u < UK; u++) kbuf[u] = load_one(sk, u, k_off);
 #pragma unroll
@@ -403,12 +470,14 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
 
   for (int64_t x = x_begin; x < x_end; x++) {
     const int64_t grp = grp_of(pos);
-    const int j0 = pos.c * C;
-    const int n_all = n_all_of(pos);         // visited slots of the chunk
-    const int n_old = n_old_of(pos, n_all);  // cached ones; [n_old, n_all) are appended
-    // out of place: rows this kernel copies to the output cache
-    const uint32_t kcopy = n_old == n_all ? static_cast<uint32_t>(n_all) * KROW : 0u;
-    const uint32_t vcopy = n_old == n_all ? static_cast<uint32_t>(n_all) * VROW : 0u;
+    const int j0 = j0_of(pos);         // first slot of the chunk
+    const int n_all = n_all_of(pos);   // visited slots
+    // out of place: every visited row goes to the output cache at slots
+    // j0.. (next to the math below, before each register is reloaded); in
+    // place this kernel writes no cache row (the combine kernel stores the
+    // appended rows)
+    const uint32_t kcopy = static_cast<uint32_t>(n_all) * KROW;
+    const uint32_t vcopy = static_cast<uint32_t>(n_all) * VROW;
 
     // ---- the next chunk: its position and sources ----
     ChunkPos nxt = pos;
@@ -423,15 +492,15 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
         do {
           nxt.b++;
           if (nxt.b >= a.B) break;
-          nxt.len = static_cast<int>(rowinfo[nxt.b * 4 + 0]);
-          nxt.n = static_cast<int>(rowinfo[nxt.b * 4 + 1]);
-          nxt.nc = static_cast<int>(row_chunks(nxt.len, nxt.n, C));
+          nxt.len = row_len(nxt.b);
+          nxt.n = row_n(nxt.b);
+          nxt.nc = static_cast<int>(stream_chunks(nxt.len, nxt.n, C));
         } while (nxt.nc == 0);
       }
     }
     const bool more = x + 1 < x_end;
-    const RowSrc nk = src_of(nxt, more, kin, kout, KROW);
-    const RowSrc nv = src_of(nxt, more, vin, vout, VROW);
+    const RowSrc nk = src_of(nxt, more, kin, a.new_key, KROW);
+    const RowSrc nv = src_of(nxt, more, vin, a.new_value, VROW);
 
     // ---- K: scores; each group's registers reload the next chunk's K ----
     Acc sc[NG];  // this lane's finished scores: packed row my_row, one per group

@@ -1,22 +1,17 @@
-// kvc_prep.h -- row preparation and the append for the stream path.
+// kvc_prep.h -- row preparation for the stream path on large batches.
 //
-// Workgroups 0 .. B-1: workgroup b works out row b's information as
-// "Autoregressive KV-cache append and causal attention" (Required
-// behavior) defines it -- n = count of the True prefix of append_mask[b,:],
-// 0 <= length <= M, length + n <= M; a broken row becomes a no-op with a
-// status -- and writes new_key/new_value row t to slot length + t of the
-// destination cache for every KV head (the append itself).  Out of place it
-// also copies the cached rows of the chunk the first new row falls in, so
-// that every chunk holding new rows is whole in the output cache.
-//
-// Workgroup B: the same row information for all rows, the number of C-slot
-// chunks each KV head needs, the exclusive prefix sum of Hk * chunks over b
-// (each row's first index in the flattened chunk list), the number of busy
-// stream workers Pe = min(P, Nc), and each worker's first chunk.
+// One workgroup works out every batch row's information as "Autoregressive
+// KV-cache append and causal attention" (Required behavior) defines it --
+// n = count of the True prefix of append_mask[b,:], 0 <= length <= M,
+// length + n <= M; a broken row becomes a no-op with a status -- the number
+// of stream chunks each KV head needs (stream_chunks), the exclusive prefix
+// sum of Hk * chunks over b (each row's first index in the flattened chunk
+// list), the number of busy stream workers Pe = min(P, Nc), and each
+// worker's first chunk.  (Batches of up to kDecodeFusedRows rows skip this
+// kernel: the attend kernel builds the same table in LDS.)
 //
 // After this kernel the attend and combine kernels read row information
-// only from the workspace, so lengths_out may alias lengths, and the
-// in-place attend kernel finds the appended rows in the cache.
+// only from the workspace, so lengths_out may alias lengths.
 #pragma once
 
 #include "kvc_common.h"
@@ -31,46 +26,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(StepArgs a) {
   __shared__ int64_t first_sh[kPrepLdsRows];
   __shared__ int32_t nc_sh[kPrepLdsRows];
   __shared__ int64_t carry_sh;
-  __shared__ RowInfo info_sh;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-
-  if (blockIdx.x < a.B) {
-    // ---- the append of batch row b ----
-    const int64_t b = blockIdx.x;
-    if (wave == 0) {
-      const RowInfo ri = wave_row_info(a.lengths, a.mask, a.Q, a.M, b);
-      if (lane == 0) info_sh = ri;
-    }
-    __syncthreads();
-    const RowInfo ri = info_sh;
-    if (ri.n <= 0) return;
-    const int64_t esz = a.elem_bytes;
-    for (int which = 0; which < 2; which++) {
-      const int64_t rowb = (which == 0 ? a.D : a.Dv) * esz;  // bytes per row (multiple of 16)
-      const int64_t n16 = rowb / 16;
-      const uint4* src = static_cast<const uint4*>(which == 0 ? a.new_key : a.new_value);
-      uint4* dst = static_cast<uint4*>(which == 0 ? a.kc_out : a.vc_out);
-      const int64_t total = a.Hk * ri.n * n16;
-      for (int64_t i = tid; i < total; i += kPrepThreads) {
-        const int64_t h = i / (ri.n * n16), rem = i % (ri.n * n16);
-        const int64_t t = rem / n16, k = rem % n16;
-        dst[((b * a.Hk + h) * a.M + ri.len + t) * n16 + k] = src[((b * a.Hk + h) * a.Q + t) * n16 + k];
-      }
-      if (a.out_of_place) {
-        // the cached rows of the chunk that receives the first new row, so
-        // that the attend kernel finds that chunk whole in the output cache
-        const uint4* in = static_cast<const uint4*>(which == 0 ? a.kc_in : a.vc_in);
-        const int64_t r0 = (ri.len / a.C) * a.C, nr = ri.len - r0;
-        const int64_t ctotal = a.Hk * nr * n16;
-        for (int64_t i = tid; i < ctotal; i += kPrepThreads) {
-          const int64_t h = i / (nr * n16), rem = i % (nr * n16);
-          const int64_t idx = ((b * a.Hk + h) * a.M + r0) * n16 + rem;
-          dst[idx] = in[idx];
-        }
-      }
-    }
-    return;
-  }
 
   // ---- row information, chunk offsets and worker starts ----
   if (tid == 0) carry_sh = 0;
@@ -81,7 +37,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(StepArgs a) {
     int64_t chunks = 0;
     if (b < a.B) {
       ri = thread_row_info(a.lengths, a.mask, a.Q, a.M, b);
-      chunks = a.Hk * row_chunks(ri.len, ri.n, a.C);
+      chunks = a.Hk * stream_chunks(ri.len, ri.n, a.C);
     }
     // inclusive scan inside the wave
     int64_t incl = chunks;
@@ -102,7 +58,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(StepArgs a) {
       row[3] = before + incl - chunks;
       if (b < kPrepLdsRows) {
         first_sh[b] = before + incl - chunks;
-        nc_sh[b] = static_cast<int32_t>(row_chunks(ri.len, ri.n, a.C));
+        nc_sh[b] = static_cast<int32_t>(stream_chunks(ri.len, ri.n, a.C));
       }
     }
     __syncthreads();
@@ -130,7 +86,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(StepArgs a) {
       if (first <= x) lo = mid; else hi = mid - 1;
     }
     const int64_t nc = in_lds ? nc_sh[lo]
-                              : row_chunks(a.ws_rowinfo[lo * 4 + 0], a.ws_rowinfo[lo * 4 + 1], a.C);
+                              : stream_chunks(a.ws_rowinfo[lo * 4 + 0], a.ws_rowinfo[lo * 4 + 1], a.C);
     const int64_t rel = x - (in_lds ? first_sh[lo] : a.ws_rowinfo[lo * 4 + 3]);
     int32_t* ws = a.ws_wstart + wk * 4;
     ws[0] = static_cast<int32_t>(lo);

@@ -66,6 +66,14 @@ def test_tiny_more_seeds(seed):
     WORKLOADS["decode_gqa_bf16"].with_(name="decode_f32_small", B=3, M=777, dtype="f32",
                                        len_range=(0, 776)),
     WORKLOADS["chunk_gqa_bf16"].with_(name="chunk_ragged", M=700, len_range=(100, 640)),
+    # stream path with two tokens per step: empty caches, rows that append
+    # nothing, caches filled to capacity
+    Workload(name="decode_q2_edges", B=8, Hq=4, Hk=2, Q=2, M=200, D=64, Dv=64, dtype="bf16",
+             len_range=(0, 198), n_rule="uniform", force_len0_row=0, force_n0_row=1),
+    # more batch rows than the attend kernel prepares by itself (the
+    # preparation kernel runs first)
+    Workload(name="decode_b1030", B=1030, Hq=2, Hk=1, Q=1, M=96, D=64, Dv=64, dtype="bf16",
+             len_range=(0, 95), n_rule="all"),
 ], ids=lambda w: w.name)
 def test_reduced_decode_shapes(wl, mode):
     full_check(wl, 0, mode)
