@@ -88,6 +88,7 @@ constexpr int64_t kCombineSlots = 2048;
 
 // Matrix-core chunk path: bf16, more than 8 packed rows per KV head.
 struct ChunkEntry {
+  int dtype;
   int64_t D, Dv;
   void (*launch)(const StepArgs&, hipStream_t);
 };
@@ -99,16 +100,26 @@ void launch_chunk(const StepArgs& a, hipStream_t s) {
                      dim3(kvc::kChunkThreads), 0, s, a);
 }
 
+template <int D, int DV>
+void launch_chunk_f32(const StepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((kvc::attend_chunk_f32_kernel<D, DV>),
+                     dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk_max)),
+                     dim3(kvc::kChunkThreads), 0, s, a);
+}
+
+// bf16 on the bf16 matrix cores, fp32 on the fp64 ones
 const ChunkEntry kChunkTable[] = {
-    {64, 64, &launch_chunk<64, 64>},
-    {128, 128, &launch_chunk<128, 128>},
-    {256, 256, &launch_chunk<256, 256>},
+    {KVC_BF16, 64, 64, &launch_chunk<64, 64>},
+    {KVC_BF16, 128, 128, &launch_chunk<128, 128>},
+    {KVC_BF16, 256, 256, &launch_chunk<256, 256>},
+    {KVC_F32, 64, 64, &launch_chunk_f32<64, 64>},
+    {KVC_F32, 128, 128, &launch_chunk_f32<128, 128>},
 };
 
 const ChunkEntry* find_chunk(const kvc_dims* d, int dtype, int64_t R) {
-  if (dtype != KVC_BF16 || R <= 8) return nullptr;
+  if (R <= 8) return nullptr;
   for (const ChunkEntry& e : kChunkTable)
-    if (e.D == d->D && e.Dv == d->Dv) return &e;
+    if (e.dtype == dtype && e.D == d->D && e.Dv == d->Dv) return &e;
   return nullptr;
 }
 
@@ -304,7 +315,10 @@ void launch_dense_chunk(StepArgs& a, const ChunkEntry& e, hipStream_t stream,
   if (ev && ev->start) hipEventRecord(static_cast<hipEvent_t>(ev->start), stream);
   e.launch(a, stream);
   if (ev && ev->stop) hipEventRecord(static_cast<hipEvent_t>(ev->stop), stream);
-  launch_combine<kvc::bf16>(a, stream);
+  if (e.dtype == KVC_F32)
+    launch_combine<float>(a, stream);
+  else
+    launch_combine<kvc::bf16>(a, stream);
 }
 
 template <typename T>

@@ -254,3 +254,183 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_kernel(StepArgs a)
 }
 
 }  // namespace kvc
+
+namespace kvc {
+
+// ---- fp32 inputs: the same chunk kernel on the fp64 matrix cores ----------
+//
+// fp32 scores reach ~1e3 and the probabilities must hold to 1e-5, so the
+// products run in fp64 (v_mfma_f64_16x16x4_f64, inputs widened exactly).
+// Operand layouts (wave64): lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16], one element each, and receives D[4 i + l / 16][l % 16]
+// for i < 4.  K and V stay row-major fp32 in LDS (both operands read one
+// element per lane), the probabilities go through a per-wave fp64 tile.
+typedef double mfma_f64x4 __attribute__((ext_vector_type(4)));
+
+template <int D, int DV>
+__global__ __launch_bounds__(kChunkThreads) void attend_chunk_f32_kernel(StepArgs a) {
+  constexpr int C = kChunkSlots;
+  constexpr int KP = D + 1;    // row pitches (odd: the 16 lanes of a column
+  constexpr int VP = DV + 1;   // read 16 different rows without conflicts)
+  constexpr int PP = C + 1;
+  static_assert(D % 4 == 0 && DV % 16 == 0, "head sizes");
+  __shared__ float k_s[C * KP];
+  __shared__ float v_s[C * VP];
+  __shared__ double p_s[kChunkWaves][kChunkBlockRows * PP];
+  __shared__ RowInfo info_sh;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int64_t c = blockIdx.x % a.nchunk_max;
+  const int64_t grp = blockIdx.x / a.nchunk_max;
+  const int64_t b = grp / a.Hk, kvh = grp % a.Hk;
+
+  if (wave == 0) {
+    const RowInfo ri = wave_row_info(a.lengths, a.mask, a.Q, a.M, b);
+    if (lane == 0) info_sh = ri;
+  }
+  __syncthreads();
+  const RowInfo ri = info_sh;
+  if (c == 0 && kvh == 0 && tid == 0) {
+    a.ws_rowinfo[b * 4 + 0] = ri.len;
+    a.ws_rowinfo[b * 4 + 1] = ri.n;
+    a.ws_rowinfo[b * 4 + 2] = ri.status;
+    a.ws_rowinfo[b * 4 + 3] = 0;
+  }
+  const int64_t len = ri.len, n = ri.n, new_len = len + n;
+  const int64_t s0 = c * C;
+  const int64_t s1 = s0 + C < a.M ? s0 + C : a.M;
+
+  const int64_t head = b * a.Hk + kvh;
+  const float* k_head = static_cast<const float*>(a.kc_in) + head * a.M * D;
+  const float* v_head = static_cast<const float*>(a.vc_in) + head * a.M * DV;
+  const float* nk_head = static_cast<const float*>(a.new_key) + head * a.Q * D;
+  const float* nv_head = static_cast<const float*>(a.new_value) + head * a.Q * DV;
+
+  // 1. cache writes of the slot range [s0, s1)
+  write_cache_slots(static_cast<uint8_t*>(a.kc_out) + head * a.M * D * 4,
+                    reinterpret_cast<const uint8_t*>(k_head),
+                    reinterpret_cast<const uint8_t*>(nk_head), D * 4, s0, s1, len, n,
+                    a.out_of_place != 0, tid, kChunkThreads);
+  write_cache_slots(static_cast<uint8_t*>(a.vc_out) + head * a.M * DV * 4,
+                    reinterpret_cast<const uint8_t*>(v_head),
+                    reinterpret_cast<const uint8_t*>(nv_head), DV * 4, s0, s1, len, n,
+                    a.out_of_place != 0, tid, kChunkThreads);
+  if (a.R == 0 || c >= row_chunks(len, n, C)) return;
+  const int nact = static_cast<int>((s1 < new_len ? s1 : new_len) - s0);
+
+  // 2. K and V rows of the chunk into LDS (slots >= nact as zeros)
+  for (int idx = tid; idx < C * D; idx += kChunkThreads) {
+    const int slot = idx / D, d = idx % D;
+    const int64_t j = s0 + slot;
+    float x = 0.f;
+    if (slot < nact) x = j < len ? k_head[j * D + d] : nk_head[(j - len) * D + d];
+    k_s[slot * KP + d] = x;
+  }
+  for (int idx = tid; idx < C * DV; idx += kChunkThreads) {
+    const int slot = idx / DV, d = idx % DV;
+    const int64_t j = s0 + slot;
+    float x = 0.f;
+    if (slot < nact) x = j < len ? v_head[j * DV + d] : nv_head[(j - len) * DV + d];
+    v_s[slot * VP + d] = x;
+  }
+  __syncthreads();
+
+  // 3. blocks of 16 packed rows, one wave each
+  const double scale = a.scale;
+  const double neg_inf = -INFINITY;
+  const int li = lane % 16, lq = lane / 16;
+  const int64_t seg = grp * a.nchunk_max + c;
+  const float* qbase = static_cast<const float*>(a.query);
+  float* att = static_cast<float*>(a.attention);
+  double* ptile = p_s[wave];
+  const int nblk = (a.R + kChunkBlockRows - 1) / kChunkBlockRows;
+  for (int blk = wave; blk < nblk; blk += kChunkWaves) {
+    // query row li as A operand: element 4 kk + lq
+    double qa[D / 4];
+    {
+      const int r = blk * kChunkBlockRows + li;
+      const int64_t g = r / a.Q, t = r % a.Q;
+      const bool ok = r < a.R && t < n;
+      const float* qrow = qbase + ((b * a.Hq + kvh * a.G + g) * a.Q + t) * D;
+#pragma unroll
+      for (int kk = 0; kk < D / 4; kk++) qa[kk] = ok ? static_cast<double>(qrow[4 * kk + lq]) : 0.0;
+    }
+    // scores: s[jt][i] = S[4 i + lq][16 jt + li]
+    mfma_f64x4 s[C / 16];
+#pragma unroll
+    for (int jt = 0; jt < C / 16; jt++) {
+      s[jt] = mfma_f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int kk = 0; kk < D / 4; kk++)
+        s[jt] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+            qa[kk], static_cast<double>(k_s[(jt * 16 + li) * KP + 4 * kk + lq]), s[jt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = blk * kChunkBlockRows + 4 * i + lq;
+      const int64_t g = r / a.Q, t = r % a.Q;
+      const bool row_ok = r < a.R && t < n;
+      double sv[C / 16];
+      double mx = neg_inf;
+#pragma unroll
+      for (int jt = 0; jt < C / 16; jt++) {
+        const int jl = jt * 16 + li;
+        const bool ok = row_ok && jl < nact && s0 + jl <= len + t;
+        sv[jt] = ok ? s[jt][i] * scale : neg_inf;
+        mx = sv[jt] > mx ? sv[jt] : mx;
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        const double y = __shfl_xor(mx, o);
+        mx = y > mx ? y : mx;
+      }
+      double sum = 0.0;
+#pragma unroll
+      for (int jt = 0; jt < C / 16; jt++) {
+        sv[jt] = sv[jt] == neg_inf ? 0.0 : exp(sv[jt] - mx);
+        sum += sv[jt];
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+      float* arow = att + ((b * a.Hq + kvh * a.G + g) * a.Q + t) * a.M + s0;
+#pragma unroll
+      for (int jt = 0; jt < C / 16; jt++) {
+        const int jl = jt * 16 + li;
+        if (row_ok && jl < nact && s0 + jl <= len + t) arow[jl] = static_cast<float>(sv[jt]);
+        ptile[(4 * i + lq) * PP + jl] = sv[jt];
+      }
+      if (li == 0 && r < a.R) {
+        if (row_ok) {
+          double* cm = a.ws_chunk_ml + ((grp * a.nchunk_max + c) * a.R + r) * 2;
+          cm[0] = mx;
+          cm[1] = sum;
+        }
+        double* sm = a.ws_seg_ml + (seg * a.R + r) * 2;
+        sm[0] = mx;
+        sm[1] = sum;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // context partial o = P V
+#pragma unroll
+    for (int nt = 0; nt < DV / 16; nt++) {
+      mfma_f64x4 o = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int kk = 0; kk < C / 4; kk++)
+        o = __builtin_amdgcn_mfma_f64_16x16x4f64(
+            ptile[li * PP + 4 * kk + lq],
+            static_cast<double>(v_s[(4 * kk + lq) * VP + nt * 16 + li]), o, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int r = blk * kChunkBlockRows + 4 * i + lq;
+        if (r < a.R) a.ws_seg_o[(seg * a.R + r) * DV + nt * 16 + li] = static_cast<float>(o[i]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the next block overwrites the tile
+  }
+}
+
+}  // namespace kvc

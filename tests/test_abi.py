@@ -61,15 +61,16 @@ def test_workspace_and_plan(lib):
 
 def test_plan_dispatch_rule(lib):
     """Host-only path choice: <= 8 packed rows with a tabled head size -> the
-    vector decode kernel (1); bf16 with > 8 packed rows and D = Dv in
-    {64, 128, 256} -> the matrix-core chunk kernel (2); the rest -> the
-    generic kernel (0).  The workspace covers every path of the shape."""
+    vector decode kernel (1); > 8 packed rows with D = Dv in {64, 128, 256}
+    (bf16) or {64, 128} (fp32) -> the matrix-core chunk kernel (2); the rest
+    -> the generic kernel (0).  The workspace covers every path of the shape."""
     cases = [
         (dims(B=32, Hq=32, Hk=8, Q=1, M=8192, D=128, Dv=128), kvc.KVC_BF16, 1),
         (dims(B=4, Hq=64, Hk=8, Q=1, M=131072, D=128, Dv=128), kvc.KVC_BF16, 1),
         (dims(B=8, Hq=16, Hk=16, Q=4, M=1024, D=64, Dv=32), kvc.KVC_F32, 1),
         (dims(B=2, Hq=8, Hk=2, Q=40, M=4096, D=64, Dv=64), kvc.KVC_BF16, 2),
-        (dims(B=2, Hq=8, Hk=2, Q=40, M=4096, D=64, Dv=64), kvc.KVC_F32, 0),
+        (dims(B=2, Hq=8, Hk=2, Q=40, M=4096, D=64, Dv=64), kvc.KVC_F32, 2),
+        (dims(B=2, Hq=8, Hk=2, Q=40, M=4096, D=256, Dv=256), kvc.KVC_F32, 0),
         (dims(B=2, Hq=4, Hk=1, Q=3, M=100, D=128, Dv=128), kvc.KVC_BF16, 2),   # R = 12
         (dims(B=2, Hq=4, Hk=1, Q=3, M=100, D=96, Dv=96), kvc.KVC_BF16, 0),     # no table entry
         (dims(B=2, Hq=4, Hk=2, Q=3, M=16, D=8, Dv=8), kvc.KVC_F32, 0),

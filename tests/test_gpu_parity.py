@@ -237,18 +237,18 @@ def test_page_face_dict_and_inplace_twin():
 
 
 def test_plan_paths():
-    """The decode-shaped workloads take the vector stream path, the bf16
-    chunk workload (160 packed rows) the matrix-core chunk path, the rest
-    the generic one."""
+    """The decode-shaped workloads take the vector stream path, the chunk
+    workloads (160 packed rows) the matrix-core chunk path, the rest the
+    generic one."""
     expect = {"decode_gqa_bf16": 1, "long_decode_bf16": 1, "mha_stress_f32": 1,
-              "chunk_gqa_bf16": 2, "chunk_gqa_f32": 0, "tiny_mixed_f32": 0}
+              "chunk_gqa_bf16": 2, "chunk_gqa_f32": 2, "tiny_mixed_f32": 0}
     for name, path in expect.items():
         w = WORKLOADS[name]
         d = kvc.KvcDims(w.B, w.Hq, w.Hk, w.Q, w.M, w.D, w.Dv)
         assert kvc.kvc_plan_step(d, kvc.dtype_code(w.torch_dtype))["path"] == path, name
 
 
-# -- the matrix-core chunk path (bf16, more than 8 packed rows) --------------
+# -- the matrix-core chunk path (more than 8 packed rows) --------------------
 def chunk_wl(**kw) -> Workload:
     base = dict(name="chunk", B=2, Hq=4, Hk=1, Q=5, M=200, D=64, Dv=64, dtype="bf16",
                 len_range=(0, 190), n_rule="uniform")
@@ -264,6 +264,19 @@ CHUNK_CASES = [
     chunk_wl(name="prefill_len0", Hq=8, Hk=2, Q=40, M=96, len_range=(0, 0), n_rule="all"),
     chunk_wl(name="many_heads", B=3, Hq=16, Hk=2, Q=3, M=257, len_range=(0, 250)),
 ]
+# fp32 inputs take the fp64 matrix-core variant (D = Dv in {64, 128});
+# the stress scale (std 8, scale 4) pushes the scores into the hundreds
+CHUNK_CASES += [
+    chunk_wl(name="rows20_ragged_f32", dtype="f32"),
+    chunk_wl(name="rows16_d128_f32", dtype="f32", Hq=2, Q=8, D=128, Dv=128, M=300,
+             len_range=(0, 290)),
+    chunk_wl(name="fill_to_capacity_f32", dtype="f32", Hq=1, Q=16, M=128,
+             len_range=(112, 112), n_rule="all"),
+    chunk_wl(name="prefill_len0_f32", dtype="f32", Hq=8, Hk=2, Q=40, M=96,
+             len_range=(0, 0), n_rule="all"),
+    chunk_wl(name="stress_f32", dtype="f32", B=3, Hq=16, Hk=2, Q=3, M=257,
+             len_range=(0, 250), std=8.0, scale=4.0),
+]
 
 
 @pytest.mark.parametrize("mode", ["oop", "inplace"])
@@ -275,10 +288,11 @@ def test_chunk_path_shapes(wl, mode):
         full_check(wl, seed, mode)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("mode", ["oop", "inplace"])
-def test_chunk_path_rejected_rows(mode):
+def test_chunk_path_rejected_rows(mode, dtype):
     """Outside-contract rows on the chunk path: no-ops with a status."""
-    wl = chunk_wl(name="chunk_rejected", B=5, Q=5, M=70)
+    wl = chunk_wl(name="chunk_rejected", B=5, Q=5, M=70, dtype=dtype)
     lengths = np.array([3, -1, 71, 4, 68], np.int64)
     n = np.array([5, 1, 0, 2, 5], np.int64)
     inp = make_inputs(wl, 4, "cpu", lengths=lengths, n=n)
@@ -288,7 +302,7 @@ def test_chunk_path_rejected_rows(mode):
                                 h["value_cache"], h["lengths"], h["append_mask"])
     assert list(ref.row_status) == [0, 1, 1, 3, 2]
     out = run_gpu({k: v.to(DEV) for k, v in inp.items()}, mode)
-    check_step(out, ref, "bf16", f"chunk_rejected/{mode}")
+    check_step(out, ref, dtype, f"chunk_rejected/{mode}/{dtype}")
 
 
 def test_chunk_sequence_40_32_24():
