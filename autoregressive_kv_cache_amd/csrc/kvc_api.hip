@@ -86,7 +86,7 @@ constexpr int64_t kComputeUnits = 256;
 // Slots per combine workgroup (a multiple of every chunk size).
 constexpr int64_t kCombineSlots = 2048;
 
-// Matrix-core chunk path: bf16, more than 8 packed rows per KV head.
+// Matrix-core chunk path: more than 8 packed rows per KV head.
 struct ChunkEntry {
   int dtype;
   int64_t D, Dv;
