@@ -39,18 +39,24 @@ void launch_decode_q(const StepArgs& a, hipStream_t s) {
   const int64_t* ri = a.ws_rowinfo;
   const int32_t* wst = a.ws_wstart;
   const bool fused = a.B <= kvc::kDecodeFusedRows;
-  if (a.out_of_place && fused)
-    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, true, true>), grid, block, 0,
-                       s, a, ri, wst);
+  if (a.paged && fused)
+    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, false, true, true>), grid,
+                       block, 0, s, a, ri, wst);
+  else if (a.paged)
+    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, false, false, true>), grid,
+                       block, 0, s, a, ri, wst);
+  else if (a.out_of_place && fused)
+    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, true, true, false>), grid,
+                       block, 0, s, a, ri, wst);
   else if (a.out_of_place)
-    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, true, false>), grid, block, 0,
-                       s, a, ri, wst);
+    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, true, false, false>), grid,
+                       block, 0, s, a, ri, wst);
   else if (fused)
-    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, false, true>), grid, block, 0,
-                       s, a, ri, wst);
+    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, false, true, false>), grid,
+                       block, 0, s, a, ri, wst);
   else
-    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, false, false>), grid, block,
-                       0, s, a, ri, wst);
+    hipLaunchKernelGGL((kvc::attend_decode_kernel<T, D, DV, ROWS, Q1, false, false, false>), grid,
+                       block, 0, s, a, ri, wst);
 }
 
 template <typename T, int D, int DV, int ROWS>
@@ -333,18 +339,38 @@ void launch_stream(StepArgs& a, const DecodeEntry& e, hipStream_t stream, const 
   launch_combine<T>(a, stream);
 }
 
+// The paged layout: block pools [num_blocks][Hk][block_size][D or Dv] and a
+// [B][M / block_size] int32 block table.
+struct PagedPool {
+  int64_t num_blocks, block_size;
+  const int32_t* table;
+};
+
 int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const void* query,
              const void* new_key, const void* new_value, const void* kc_in, const void* vc_in,
              void* kc_out, void* vc_out, bool out_of_place, const int64_t* lengths,
              const uint8_t* mask, int64_t* lengths_out, void* attention, void* context,
              int32_t* row_status, void* workspace, size_t workspace_bytes, void* stream,
-             const kvc_events* events) {
+             const kvc_events* events, const PagedPool* pg = nullptr) {
   Plan p;
   int rc = make_plan(d, dtype, &p);
   if (rc != KVC_OK) return rc;
   double sc;
   rc = check_scale(has_scale, scale, d->D, &sc);
   if (rc != KVC_OK) return rc;
+
+  if (pg) {
+    if (!pg->table) return KVC_ERR_NULL;
+    const int64_t bs = pg->block_size;
+    if (pg->num_blocks < 1 || bs < 1 || (bs & (bs - 1)) != 0 || d->M % bs != 0)
+      return KVC_ERR_SHAPE;
+    int64_t x;
+    if (!mul_ok(pg->num_blocks, d->Hk, kMaxElems, &x) || !mul_ok(x, bs, kMaxElems, &x) ||
+        !mul_ok(x, d->D > d->Dv ? d->D : d->Dv, kMaxElems, &x))
+      return KVC_ERR_SHAPE;
+    // the stream decode path only, with every chunk inside one block
+    if (!p.decode || bs < p.decode->chunk) return KVC_ERR_UNSUPPORTED;
+  }
 
   if (!kc_in || !vc_in || !kc_out || !vc_out || !lengths || !lengths_out) return KVC_ERR_NULL;
   if (d->Q > 0 && (!query || !new_key || !new_value || !mask || !attention || !context))
@@ -354,15 +380,19 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
 
   const size_t e = dtype == KVC_F32 ? 4 : 2;
   const size_t B = d->B, Hq = d->Hq, Hk = d->Hk, Q = d->Q, M = d->M, D = d->D, Dv = d->Dv;
+  // cache extent: B rows of M slots, or the block pools
+  const size_t slots = pg ? static_cast<size_t>(pg->num_blocks * pg->block_size) : B * M;
   const Range r_q{query, B * Hq * Q * D * e}, r_nk{new_key, B * Hk * Q * D * e},
-      r_nv{new_value, B * Hk * Q * Dv * e}, r_kin{kc_in, B * Hk * M * D * e},
-      r_vin{vc_in, B * Hk * M * Dv * e}, r_len{lengths, B * 8}, r_mask{mask, B * Q},
-      r_kout{kc_out, B * Hk * M * D * e}, r_vout{vc_out, B * Hk * M * Dv * e},
+      r_nv{new_value, B * Hk * Q * Dv * e}, r_kin{kc_in, Hk * slots * D * e},
+      r_vin{vc_in, Hk * slots * Dv * e}, r_len{lengths, B * 8}, r_mask{mask, B * Q},
+      r_kout{kc_out, Hk * slots * D * e}, r_vout{vc_out, Hk * slots * Dv * e},
       r_lout{lengths_out, B * 8}, r_att{attention, B * Hq * Q * M * e},
       r_ctx{context, B * Hq * Q * Dv * e}, r_st{row_status, row_status ? B * 4 : 0},
       r_ws{workspace, p.pub.workspace_bytes};
+  const Range r_tab{pg ? pg->table : nullptr, pg ? B * (M / pg->block_size) * 4 : 0};
   const bool len_in_place = !out_of_place && lengths_out == lengths;
-  const Range inputs[] = {r_q, r_nk, r_nv, r_mask, len_in_place ? Range{nullptr, 0} : r_len};
+  const Range inputs[] = {r_q, r_nk, r_nv, r_mask, r_tab,
+                          len_in_place ? Range{nullptr, 0} : r_len};
   const Range caches_in[] = {r_kin, r_vin};
   const Range outs[] = {r_kout, r_vout, len_in_place ? Range{nullptr, 0} : r_lout,
                         r_att, r_ctx, r_st, r_ws};
@@ -377,7 +407,7 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
       if (overlap(outp[i], outp[j])) return KVC_ERR_ALIAS;
   }
   if (len_in_place) {  // lengths itself must still not overlap other buffers
-    const Range others[] = {r_q, r_nk, r_nv, r_mask, r_kin, r_vin, r_att, r_ctx, r_st, r_ws};
+    const Range others[] = {r_q, r_nk, r_nv, r_mask, r_tab, r_kin, r_vin, r_att, r_ctx, r_st, r_ws};
     for (const Range& o : others)
       if (overlap(r_len, o)) return KVC_ERR_ALIAS;
   }
@@ -409,6 +439,14 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
                        aligned16(kc_in) && aligned16(vc_in) && aligned16(kc_out) &&
                        aligned16(vc_out);
   const bool vec_ok = p.decode && aligned;
+  if (pg) {
+    if (!vec_ok) return KVC_ERR_UNSUPPORTED;
+    a.paged = 1;
+    a.num_blocks = pg->num_blocks;
+    a.max_blocks = d->M / pg->block_size;
+    a.block_table = pg->table;
+    while ((int64_t(1) << a.block_log2) < pg->block_size) a.block_log2++;
+  }
   const bool chunk_ok = p.chunk && aligned;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (chunk_ok) {
@@ -484,6 +522,19 @@ int kvc_step_inplace(const kvc_dims* dims, int dtype, int has_scale, double scal
                   attention, context, row_status, workspace, workspace_bytes, stream, events);
 }
 
+int kvc_step_paged(const kvc_dims* dims, int dtype, int has_scale, double scale,
+                   const void* query, const void* new_key, const void* new_value, void* key_pool,
+                   void* value_pool, int64_t num_blocks, int64_t block_size,
+                   const int32_t* block_table, const int64_t* lengths, const uint8_t* append_mask,
+                   int64_t* lengths_out, void* attention, void* context, int32_t* row_status,
+                   void* workspace, size_t workspace_bytes, void* stream,
+                   const kvc_events* events) {
+  const PagedPool pg{num_blocks, block_size, block_table};
+  return run_step(dims, dtype, has_scale, scale, query, new_key, new_value, key_pool, value_pool,
+                  key_pool, value_pool, false, lengths, append_mask, lengths_out, attention,
+                  context, row_status, workspace, workspace_bytes, stream, events, &pg);
+}
+
 const char* kvc_status_string(int code) {
   switch (code) {
     case KVC_OK: return "ok";
@@ -494,6 +545,8 @@ const char* kvc_status_string(int code) {
     case KVC_ERR_WORKSPACE: return "workspace too small";
     case KVC_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case KVC_ERR_HIP: return "a HIP launch failed";
+    case KVC_ERR_UNSUPPORTED: return "the paged cache needs the stream decode path and blocks of "
+                                     ">= 64 slots";
     case KVC_ROW_BAD_LENGTH: return "row rejected: length outside [0, M]";
     case KVC_ROW_OVERFLOW: return "row rejected: length + n exceeds M";
     case KVC_ROW_NOT_PREFIX: return "row rejected: append mask is not a prefix";

@@ -167,12 +167,22 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
     // in place, stream path: the appended rows go to their cache slots
     // (the attend kernel read them from new_key / new_value)
     const int64_t kb = a.D * E::kBytes, vb = a.Dv * E::kBytes;
-    copy_bytes(static_cast<uint8_t*>(a.kc_out) + (grp * a.M + len) * kb,
-               static_cast<const uint8_t*>(a.new_key) + grp * a.Q * kb, n * kb, tid,
-               kCombineThreads);
-    copy_bytes(static_cast<uint8_t*>(a.vc_out) + (grp * a.M + len) * vb,
-               static_cast<const uint8_t*>(a.new_value) + grp * a.Q * vb, n * vb, tid,
-               kCombineThreads);
+    const uint8_t* nk = static_cast<const uint8_t*>(a.new_key) + grp * a.Q * kb;
+    const uint8_t* nv = static_cast<const uint8_t*>(a.new_value) + grp * a.Q * vb;
+    if (!a.paged) {
+      copy_bytes(static_cast<uint8_t*>(a.kc_out) + (grp * a.M + len) * kb, nk, n * kb, tid,
+                 kCombineThreads);
+      copy_bytes(static_cast<uint8_t*>(a.vc_out) + (grp * a.M + len) * vb, nv, n * vb, tid,
+                 kCombineThreads);
+    } else {
+      // one row at a time: consecutive slots may lie in different blocks
+      for (int64_t t = 0; t < n; t++) {
+        uint8_t* kd = const_cast<uint8_t*>(slot_row(a, a.kc_out, b, kvh, len + t, kb));
+        uint8_t* vd = const_cast<uint8_t*>(slot_row(a, a.vc_out, b, kvh, len + t, vb));
+        if (kd) copy_bytes(kd, nk + t * kb, kb, tid, kCombineThreads);
+        if (vd) copy_bytes(vd, nv + t * vb, vb, tid, kCombineThreads);
+      }
+    }
   }
   if (rb == 0 && a.out_of_place && a.combine_copies_tail) {
     const int64_t cover = n > 0 ? len + n : 0;

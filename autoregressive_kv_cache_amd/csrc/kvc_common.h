@@ -107,7 +107,29 @@ struct StepArgs {
   double* ws_seg_ml;     // [nseg][R][2]: m_seg, l_seg
   float* ws_seg_o;       // [nseg][R][Dv]: o_seg
   int32_t* ws_wstart;    // [P][4]: first (b, head, chunk) of each stream worker
+  // paged cache (stream path, in place): kc_in/kc_out and vc_in/vc_out are
+  // the block pools [num_blocks][Hk][block][D or Dv]; slot j of batch row b
+  // is row j % block of block block_table[b * max_blocks + j / block]
+  int32_t paged;
+  int32_t block_log2;
+  int64_t num_blocks;
+  int64_t max_blocks;
+  const int32_t* block_table;
 };
+
+// Base of cache slot j of (batch row b, KV head h), rows of row_bytes bytes:
+// the dense [B][Hk][M] layout, or the paged block pool (nullptr when the
+// table entry is outside [0, num_blocks): such rows are neither read nor
+// written).
+__device__ inline const uint8_t* slot_row(const StepArgs& a, const void* cache, int64_t b,
+                                          int64_t h, int64_t j, int64_t row_bytes) {
+  const uint8_t* base = static_cast<const uint8_t*>(cache);
+  if (!a.paged) return base + ((b * a.Hk + h) * a.M + j) * row_bytes;
+  const int64_t blk = a.block_table[b * a.max_blocks + (j >> a.block_log2)];
+  if (blk < 0 || blk >= a.num_blocks) return nullptr;
+  const int64_t bs = int64_t(1) << a.block_log2;
+  return base + ((blk * a.Hk + h) * bs + (j & (bs - 1))) * row_bytes;
+}
 
 struct RowInfo {
   int64_t len;     // lengths[b] as given

@@ -270,7 +270,7 @@ struct ChunkPos {
   int len, n, nc;  // the row's old length, appended rows, chunks per head
 };
 
-template <typename T, int D, int DV, int ROWS, bool Q1, bool OOP, bool FUSED>
+template <typename T, int D, int DV, int ROWS, bool Q1, bool OOP, bool FUSED, bool PAGED>
 __global__ __launch_bounds__(kDecodeThreads)
 __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_decode_kernel(
     StepArgs a, const int64_t* __restrict__ rowinfo, const int32_t* __restrict__ wstart) {
@@ -292,6 +292,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
   static_assert(!kBf16 || (D == DV && UV % 2 == 0), "bf16 context pairs slots of equal layout");
   static_assert(SPLK * KROW == 1024 && SPLV * VROW == 1024, "one load covers 1 KB");
   static_assert((C & (C - 1)) == 0, "chunk sizes are powers of two (the combine shifts by log2 C)");
+  static_assert(!(PAGED && OOP), "the paged cache is updated in place");
 
   // probabilities for the context step: bf16 pairs [slot pair][slot lane][row]
   // (packed bf16x2), or fp32 [row][slot]
@@ -422,14 +423,24 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
   // from new_key / new_value (row t of the head's new rows is slot len + t).
   // live = false (past the last chunk): zero rows, so every path through
   // the loop issues the same loads.
+  // Paged: a chunk lies inside one block (blocks hold a power of two >= C
+  // slots), so its rows are contiguous too; an entry outside the pool reads
+  // as zero rows.
   auto src_of = [&](const ChunkPos& p, bool live, const uint8_t* cin, const void* fresh,
                     int rowb) {
     RowSrc r{cin, 0u};
     if (live) {
       const int64_t g = grp_of(p);
-      r.rows = is_new_of(p) ? static_cast<const uint8_t*>(fresh) + g * Q * rowb
-                            : cin + (g * M + p.c * C) * rowb;
       r.bytes = static_cast<uint32_t>(n_all_of(p)) * rowb;
+      if (is_new_of(p)) {
+        r.rows = static_cast<const uint8_t*>(fresh) + g * Q * rowb;
+      } else if constexpr (PAGED) {
+        const uint8_t* row0 = slot_row(a, cin, p.b, p.kvh, static_cast<int64_t>(p.c) * C, rowb);
+        r.rows = row0 ? row0 : cin;
+        r.bytes = row0 ? r.bytes : 0u;
+      } else {
+        r.rows = cin + (g * M + p.c * C) * rowb;
+      }
     }
     return r;
   };

@@ -4,7 +4,7 @@ marshalling only -- every step of the computation runs in the HIP kernels of
 
 Low level (same names as the C entry points, tensors instead of pointers):
 ``kvc_workspace_bytes``, ``kvc_plan_step``, ``kvc_step_out_of_place``,
-``kvc_step_inplace``, ``kvc_status_string``.
+``kvc_step_inplace``, ``kvc_step_paged``, ``kvc_status_string``.
 
 Page-style face ("Autoregressive KV-cache append and causal attention",
 Function signature / Starter code): ``kv_cache_attention_step`` returns a
@@ -26,10 +26,11 @@ LIBRARY = os.path.join(HERE, "libkvc.so")
 KVC_F32, KVC_BF16 = 0, 1
 KVC_OK = 0
 ERRORS = {-1: "KVC_ERR_NULL", -2: "KVC_ERR_SHAPE", -3: "KVC_ERR_DTYPE", -4: "KVC_ERR_SCALE",
-          -5: "KVC_ERR_WORKSPACE", -6: "KVC_ERR_ALIAS", -7: "KVC_ERR_HIP"}
+          -5: "KVC_ERR_WORKSPACE", -6: "KVC_ERR_ALIAS", -7: "KVC_ERR_HIP",
+          -8: "KVC_ERR_UNSUPPORTED"}
 ROW_OK, ROW_BAD_LENGTH, ROW_OVERFLOW, ROW_NOT_PREFIX = 0, 1, 2, 3
 EXPORTED = ("kvc_workspace_bytes", "kvc_plan_step", "kvc_step_out_of_place",
-            "kvc_step_inplace", "kvc_status_string")
+            "kvc_step_inplace", "kvc_step_paged", "kvc_status_string")
 
 
 class KvcDims(ctypes.Structure):
@@ -78,6 +79,10 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kvc_step_inplace.restype = _int
     lib.kvc_step_inplace.argtypes = ([ctypes.POINTER(KvcDims), _int, _int, _dbl]
                                      + [_vp] * 11 + [_vp, _sz, _vp, ctypes.POINTER(KvcEvents)])
+    lib.kvc_step_paged.restype = _int
+    lib.kvc_step_paged.argtypes = ([ctypes.POINTER(KvcDims), _int, _int, _dbl] + [_vp] * 5
+                                   + [_i64, _i64] + [_vp] * 8 + [_sz, _vp,
+                                                                 ctypes.POINTER(KvcEvents)])
     lib.kvc_status_string.restype = ctypes.c_char_p
     lib.kvc_status_string.argtypes = [_int]
     _LIB = lib
@@ -181,6 +186,30 @@ def kvc_step_inplace(query, new_key, new_value, key_cache, value_cache, lengths,
         _stream(stream, key_cache.device), _events(events))
     if rc != KVC_OK:
         raise KvcError(rc, "kvc_step_inplace")
+
+
+def kvc_step_paged(query, new_key, new_value, key_pool, value_pool, block_table, lengths,
+                   append_mask, lengths_out, attention, context, row_status=None,
+                   workspace=None, scale=None, stream=None, events=None) -> None:
+    """Enqueue the in-place step over a paged cache on ``stream``: pools
+    ``[num_blocks, Hk, block_size, D|Dv]``, ``block_table`` int32
+    ``[B, max_blocks]``; each row's capacity is ``max_blocks * block_size``."""
+    lib = load()
+    B, Hq, Q, D = query.shape
+    num_blocks, Hk, block_size, _ = key_pool.shape
+    dims = KvcDims(B, Hq, Hk, Q, block_table.shape[1] * block_size, D, value_pool.shape[3])
+    dt = dtype_code(key_pool.dtype)
+    if workspace is None:
+        workspace = workspace_for(dims, dt, key_pool.device)
+    hs, sc = _scale_args(scale)
+    rc = lib.kvc_step_paged(
+        ctypes.byref(dims), dt, hs, sc, _ptr(query), _ptr(new_key), _ptr(new_value),
+        _ptr(key_pool), _ptr(value_pool), int(num_blocks), int(block_size), _ptr(block_table),
+        _ptr(lengths), _ptr(append_mask), _ptr(lengths_out), _ptr(attention), _ptr(context),
+        _ptr(row_status), _ptr(workspace), workspace.numel(), _stream(stream, key_pool.device),
+        _events(events))
+    if rc != KVC_OK:
+        raise KvcError(rc, "kvc_step_paged")
 
 
 # ---------------------------------------------------------------------------

@@ -165,3 +165,29 @@ def host_arrays(inputs: dict[str, torch.Tensor]) -> dict[str, np.ndarray]:
 def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
     """Widen raw bfloat16 words to float64 (exact)."""
     return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def paged_layout(key_cache: torch.Tensor, value_cache: torch.Tensor, block_size: int,
+                 seed: int, spare_blocks: int = 3, fill: float = 7.0
+                 ) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """The same caches in the block-pool layout: pools [num_blocks, Hk,
+    block_size, D|Dv] and an int32 table [B, M / block_size] that sends row b's
+    i-th block to a seeded random pool block.  ``spare_blocks`` extra pool
+    blocks belong to no row and hold ``fill`` (so a stray write shows)."""
+    B, Hk, M, D = key_cache.shape
+    Dv = value_cache.shape[3]
+    if M % block_size:
+        raise ValueError("block_size must divide M")
+    mb = M // block_size
+    nb = B * mb + spare_blocks
+    perm = np.random.default_rng(seed).permutation(nb)[:B * mb]
+    idx = torch.from_numpy(perm.astype(np.int64)).to(key_cache.device)
+    kp = torch.full((nb, Hk, block_size, D), fill, dtype=key_cache.dtype, device=key_cache.device)
+    vp = torch.full((nb, Hk, block_size, Dv), fill, dtype=value_cache.dtype,
+                    device=value_cache.device)
+    kp[idx] = key_cache.reshape(B, Hk, mb, block_size, D).permute(0, 2, 1, 3, 4).reshape(
+        B * mb, Hk, block_size, D)
+    vp[idx] = value_cache.reshape(B, Hk, mb, block_size, Dv).permute(0, 2, 1, 3, 4).reshape(
+        B * mb, Hk, block_size, Dv)
+    table = torch.from_numpy(perm.reshape(B, mb).astype(np.int32)).to(key_cache.device)
+    return kp.contiguous(), vp.contiguous(), table.contiguous()

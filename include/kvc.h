@@ -82,7 +82,8 @@ enum {
   KVC_ERR_SCALE = -4,       /* has_scale and scale not finite or <= 0 */
   KVC_ERR_WORKSPACE = -5,   /* workspace_bytes < kvc_workspace_bytes() */
   KVC_ERR_ALIAS = -6,       /* an output overlaps an input or another output */
-  KVC_ERR_HIP = -7          /* a kernel launch failed (HIP error) */
+  KVC_ERR_HIP = -7,         /* a kernel launch failed (HIP error) */
+  KVC_ERR_UNSUPPORTED = -8  /* kvc_step_paged: a shape or block size it does not take */
 };
 
 /* Per-row status written to row_status[b]. */
@@ -149,6 +150,44 @@ int kvc_step_inplace(const kvc_dims *dims, int dtype, int has_scale,
                      int32_t *row_status, void *workspace,
                      size_t workspace_bytes, void *stream,
                      const kvc_events *events);
+
+/* The same in-place step over a paged cache -- the block-pool layout that
+ * ClikaRT's attention_over_cache names beside the continuous one (a pool
+ * [num_blocks, H_kv, block_size, D] with a rank-2 [B, max_blocks] block
+ * table):
+ *
+ *   key_pool    [num_blocks, Hk, block_size, D]
+ *   value_pool  [num_blocks, Hk, block_size, Dv]
+ *   block_table [B, M / block_size] int32
+ *
+ * Slot j of batch row b -- key_cache[b, h, j, :] of the dense layout -- is
+ * key_pool[block_table[b, j / block_size], h, j % block_size, :] (the same
+ * for values).  dims->M is each row's capacity and a multiple of
+ * block_size; everything else (lengths, mask, query, new rows, attention,
+ * context, row_status, workspace) is as for kvc_step_inplace, and the
+ * results equal kvc_step_inplace's on the dense cache the table describes.
+ *
+ * Scope: shapes the plan sends to the vector decode path (path 1: at most 8
+ * packed query rows and a tabled (D, Dv)), 16-byte aligned buffers, and a
+ * block_size that is a power of two of at least 64 slots; anything else
+ * returns KVC_ERR_UNSUPPORTED (or KVC_ERR_SHAPE for a block_size that does
+ * not divide M).  Table entries are device data: an entry outside
+ * [0, num_blocks) for a slot below lengths[b] + n_b is outside the contract
+ * -- those slots read as zero rows and are never written, so no access
+ * leaves the pools -- and the row's results are then unspecified.  Rows may
+ * share blocks for slots below their lengths (a shared prefix); a block that
+ * receives appended rows must not be used by another row of the same step.
+ * The pools, the table and every other input must not overlap the outputs
+ * (KVC_ERR_ALIAS); lengths_out may be lengths. */
+int kvc_step_paged(const kvc_dims *dims, int dtype, int has_scale,
+                   double scale, const void *query, const void *new_key,
+                   const void *new_value, void *key_pool, void *value_pool,
+                   int64_t num_blocks, int64_t block_size,
+                   const int32_t *block_table, const int64_t *lengths,
+                   const uint8_t *append_mask, int64_t *lengths_out,
+                   void *attention, void *context, int32_t *row_status,
+                   void *workspace, size_t workspace_bytes, void *stream,
+                   const kvc_events *events);
 
 /* Static description of a return or row-status code. */
 const char *kvc_status_string(int code);

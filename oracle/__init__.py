@@ -172,6 +172,57 @@ class Oracle:
                                         *([None] * 13))
 
 
+@dataclass
+class PagedStepResult:
+    key_pool: np.ndarray
+    value_pool: np.ndarray
+    lengths: np.ndarray
+    attention: np.ndarray  # float64 [B, Hq, Q, M]
+    context: np.ndarray  # float64 [B, Hq, Q, Dv]
+    row_status: np.ndarray  # int32 [B]
+
+
+def paged_to_dense(pool: np.ndarray, block_table: np.ndarray) -> np.ndarray:
+    """The dense cache [B, H, M, D] a block pool [num_blocks, H, block_size, D]
+    and a table [B, max_blocks] describe: slot j of row b is row j % block_size
+    of block block_table[b, j // block_size] (the block-pool layout of ClikaRT's
+    attention_over_cache).  Entries outside the pool (allowed only for slots a
+    step never reads) gather block 0."""
+    nb, H, bs, D = pool.shape
+    B, max_blocks = block_table.shape
+    j = np.arange(max_blocks * bs)
+    blk = np.clip(block_table[:, j // bs], 0, nb - 1)  # [B, M]
+    dense = pool[blk, :, (j % bs)[None, :], :]  # [B, M, H, D]
+    return np.ascontiguousarray(dense.transpose(0, 2, 1, 3))
+
+
+def _oracle_step_paged(oracle: "Oracle", query, new_key, new_value, key_pool, value_pool,
+                       block_table, lengths, append_mask, scale=None) -> PagedStepResult:
+    """The step over a paged cache, read as the step over the dense cache the
+    table describes: gather that cache, run the dense step, and write back
+    exactly the slots the step wrote (slot length + t of each accepted row);
+    every other pool row keeps its bits."""
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    lengths = np.ascontiguousarray(lengths, dtype=np.int64)
+    nb, Hk, bs, _ = key_pool.shape
+    kc = paged_to_dense(key_pool, block_table)
+    vc = paged_to_dense(value_pool, block_table)
+    res = oracle.step(query, new_key, new_value, kc, vc, lengths, append_mask, scale=scale)
+    kp, vp = key_pool.copy(), value_pool.copy()
+    for b in range(block_table.shape[0]):
+        if res.row_status[b] != 0:
+            continue
+        for j in range(int(lengths[b]), int(res.lengths[b])):
+            blk = int(block_table[b, j // bs])
+            if not 0 <= blk < nb:
+                raise ValueError(f"row {b}: slot {j} maps to block {blk} outside the pool")
+            kp[blk, :, j % bs] = res.key_cache[b, :, j]
+            vp[blk, :, j % bs] = res.value_cache[b, :, j]
+    return PagedStepResult(kp, vp, res.lengths, res.attention, res.context, res.row_status)
+
+
+Oracle.step_paged = _oracle_step_paged
+
 _DEFAULT: Oracle | None = None
 
 

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, 1, 2, 3]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, 1, 2, 3]:
         s = kvc.kvc_status_string(code)
         assert s and s != "unknown code"
     assert kvc.kvc_status_string(12345) == "unknown code"
@@ -161,3 +161,44 @@ def test_page_face_rejects_cpu_and_options():
     with pytest.raises(ValueError):
         kvc._options_scale({"scale": -1.0})
     assert kvc._options_scale({}) is None and kvc._options_scale({"scale": 2}) == 2.0
+
+
+def test_host_checks_paged(lib):
+    """kvc_step_paged: block size, scope and aliasing are checked on the host
+    (every call here fails one of those checks; none reaches a launch)."""
+    def run(d, block_size=64, num_blocks=64, ptrs=None, ws=1 << 30, dtype=kvc.KVC_BF16):
+        e = 2 if dtype == kvc.KVC_BF16 else 4
+        B, Hq, Hk, Q, M, D, Dv = d.B, d.Hq, d.Hk, d.Q, d.M, d.D, d.Dv
+        mb = max(1, M // block_size)
+        sizes = [B * Hq * Q * D * e, B * Hk * Q * D * e, B * Hk * Q * Dv * e,
+                 num_blocks * Hk * block_size * D * e, num_blocks * Hk * block_size * Dv * e,
+                 B * mb * 4, B * 8, B * Q, B * 8, B * Hq * Q * M * e, B * Hq * Q * Dv * e, B * 4]
+        if ptrs is None:
+            ptrs, off = [], FAKE
+            for sz in sizes:
+                ptrs.append(off)
+                off += (sz + 4095) // 4096 * 4096 + 4096
+        q, nk, nv, kp, vp, tab, ln, mk, lo, at, cx, st = ptrs
+        return lib.kvc_step_paged(ctypes.byref(d), dtype, 0, 0.0, q, nk, nv, kp, vp, num_blocks,
+                                  block_size, tab, ln, mk, lo, at, cx, st, FAKE * 4, ws, None,
+                                  None), ptrs
+
+    d = dims(B=4, Hq=8, Hk=2, Q=1, M=1024, D=128, Dv=128)  # 4 packed rows: the decode path
+    assert run(d, block_size=48)[0] == -2       # not a power of two
+    assert run(d, block_size=2048)[0] == -2     # does not divide M
+    assert run(d, block_size=32)[0] == -8       # smaller than a decode chunk
+    assert run(d, num_blocks=0)[0] == -2
+    assert run(dims(B=4, Hq=8, Hk=2, Q=4, M=1024, D=128, Dv=128))[0] == -8  # 16 rows: chunk path
+    assert run(dims(B=4, Hq=8, Hk=2, Q=1, M=1024, D=96, Dv=96))[0] == -8   # no decode kernel
+    _, ptrs = run(d, ws=16)
+    assert run(d, ws=16)[0] == -5
+    bad = list(ptrs)
+    bad[5] = None  # no block table
+    assert run(d, ptrs=bad)[0] == -1
+    for out_i, in_i in [(9, 5), (9, 3), (10, 4), (11, 5)]:
+        bad = list(ptrs)
+        bad[out_i] = bad[in_i]  # attention on the table / pool, row_status on the table
+        assert run(d, ptrs=bad)[0] == -6, (out_i, in_i)
+    bad = list(ptrs)
+    bad[4] = bad[3]  # both pools on one buffer
+    assert run(d, ptrs=bad)[0] == -6

@@ -10,7 +10,7 @@ import torch
 import oracle
 from autoregressive_kv_cache_amd import kvc
 from autoregressive_kv_cache_amd.workloads import (WORKLOADS, Workload, draw_lengths_and_counts,
-                                                   host_arrays, make_inputs)
+                                                   host_arrays, make_inputs, paged_layout)
 from gpu_helpers import (bits, check_floats, check_row_sums, check_step, run_gpu, say, to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -350,3 +350,143 @@ def test_misaligned_buffers_take_generic_path(mode):
         dinp[k] = misaligned(dinp[k])
     out = run_gpu(dinp, mode)
     check_step(out, ref, wl.dtype, f"misaligned/{mode}")
+
+
+# -- the paged cache (kvc_step_paged: block pools + block table) ------------
+def run_paged(inp: dict, kp, vp, table, scale=None):
+    """kvc_step_paged on device copies; returns the updated pools and outputs."""
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    kp, vp, table = kp.to(DEV), vp.to(DEV), table.to(DEV)
+    B, Hq, Q, _ = d["query"].shape
+    M = table.shape[1] * kp.shape[2]
+    att = torch.full((B, Hq, Q, M), 3.0, dtype=kp.dtype, device=DEV)  # stale values must go
+    ctx = torch.full((B, Hq, Q, vp.shape[3]), 3.0, dtype=kp.dtype, device=DEV)
+    lens_out = torch.empty_like(d["lengths"])
+    status = torch.empty(B, dtype=torch.int32, device=DEV)
+    mask = d["append_mask"].contiguous().view(torch.uint8)
+    kvc.kvc_step_paged(d["query"], d["new_key"], d["new_value"], kp, vp, table, d["lengths"], mask,
+                       lens_out, att, ctx, status, scale=scale)
+    torch.cuda.synchronize()
+    return {"key_cache": kp.cpu(), "value_cache": vp.cpu(), "lengths": lens_out.cpu(),
+            "attention": att.cpu(), "context": ctx.cpu(), "row_status": status.cpu()}
+
+
+def paged_ref(inp: dict, kp, vp, table, scale=None):
+    h = host_arrays(dict(inp, key_pool=kp, value_pool=vp))
+    r = oracle.default().step_paged(h["query"], h["new_key"], h["new_value"], h["key_pool"],
+                                    h["value_pool"], table.numpy(), h["lengths"],
+                                    h["append_mask"], scale=scale)
+    # check_step reads the pools where it reads the caches
+    return oracle.StepResult(r.key_pool, r.value_pool, r.lengths, r.attention, r.context,
+                             r.row_status)
+
+
+PAGED_CASES = [
+    # (workload, block size): 4 packed rows (bf16 D = 128), 8 packed rows
+    # (Q = 2, appends that cross a block edge), fp32 with D != Dv, bf16 D = 64
+    (WORKLOADS["decode_gqa_bf16"].with_(name="paged_d128", B=5, M=1024,
+                                        len_range=(0, 1023)), 64),
+    (WORKLOADS["decode_gqa_bf16"].with_(name="paged_d128_b256", B=3, M=1024,
+                                        len_range=(1, 1023)), 256),
+    (chunk_wl(name="paged_rows8", B=4, Hq=4, Hk=1, Q=2, M=512, D=128, Dv=128,
+              len_range=(60, 70), n_rule="all"), 64),
+    (WORKLOADS["mha_stress_f32"].with_(name="paged_f32", B=4, M=512, len_range=(0, 508)), 128),
+    (chunk_wl(name="paged_d64", B=3, Hq=8, Hk=2, Q=1, M=640, len_range=(0, 639), n_rule="all"),
+     128),
+]
+
+
+@pytest.mark.parametrize("wl,bs", PAGED_CASES, ids=lambda x: getattr(x, "name", str(x)))
+def test_paged_against_oracle(wl, bs):
+    for seed in (0, 1):
+        say(f"[case] paged {wl.name} bs={bs} seed={seed}")
+        inp = make_inputs(wl, seed, "cpu")
+        kp, vp, table = paged_layout(inp["key_cache"], inp["value_cache"], bs, seed)
+        inp = {k: v for k, v in inp.items() if k not in ("key_cache", "value_cache")}
+        ref = paged_ref(inp, kp, vp, table, scale=wl.scale)
+        out = run_paged(inp, kp, vp, table, scale=wl.scale)
+        check_step(out, ref, wl.dtype, f"paged {wl.name}/{seed}")
+
+
+def test_paged_identity_table_matches_dense_bitwise():
+    """A table that lays the pool out like the dense cache gives bit-identical
+    outputs to kvc_step_inplace on that dense cache (same kernels, same order)."""
+    wl = WORKLOADS["decode_gqa_bf16"].with_(name="paged_ident", B=3, M=512, len_range=(0, 511))
+    inp = make_inputs(wl, 5, "cpu")
+    B, Hk, M, D = inp["key_cache"].shape
+    bs = 64
+    mb = M // bs
+    kp = inp["key_cache"].reshape(B, Hk, mb, bs, D).permute(0, 2, 1, 3, 4).reshape(
+        B * mb, Hk, bs, D).contiguous()
+    vp = inp["value_cache"].reshape(B, Hk, mb, bs, D).permute(0, 2, 1, 3, 4).reshape(
+        B * mb, Hk, bs, D).contiguous()
+    table = torch.arange(B * mb, dtype=torch.int32).reshape(B, mb)
+    dense = run_gpu({k: v.to(DEV) for k, v in inp.items()}, "inplace")
+    rest = {k: v for k, v in inp.items() if k not in ("key_cache", "value_cache")}
+    paged = run_paged(rest, kp, vp, table)
+    assert torch.equal(bits_t(paged["attention"]), bits_t(dense["attention"].cpu()))
+    assert torch.equal(bits_t(paged["context"]), bits_t(dense["context"].cpu()))
+    back = paged["key_cache"].reshape(B, mb, Hk, bs, D).permute(0, 2, 1, 3, 4).reshape(B, Hk, M, D)
+    assert torch.equal(bits_t(back), bits_t(dense["key_cache"].cpu()))
+
+
+def bits_t(t: torch.Tensor) -> torch.Tensor:
+    return t.contiguous().view(torch.int16 if t.element_size() == 2 else torch.int32)
+
+
+def test_paged_shared_prefix_and_spare_blocks():
+    """Rows 0 and 1 map the same first block (a prefix below both lengths);
+    spare pool blocks and the shared block keep their bits."""
+    wl = WORKLOADS["decode_gqa_bf16"].with_(name="paged_shared", B=3, M=512, len_range=(70, 500))
+    inp = make_inputs(wl, 7, "cpu")
+    kp, vp, table = paged_layout(inp["key_cache"], inp["value_cache"], 64, 7, spare_blocks=4)
+    shared = int(table[0, 0])
+    table[1, 0] = shared
+    inp = {k: v for k, v in inp.items() if k not in ("key_cache", "value_cache")}
+    ref = paged_ref(inp, kp, vp, table)
+    out = run_paged(inp, kp, vp, table)
+    check_step(out, ref, "bf16", "paged shared prefix")
+    assert torch.equal(bits_t(out["key_cache"][shared]), bits_t(kp[shared]))
+
+
+def test_paged_bad_entries_stay_inside_the_pool():
+    """Table entries outside the pool: past a row's length + n they are never
+    touched (results exact); inside a row's visible range they read as zero
+    rows and are never written, and every other row is still exact."""
+    wl = WORKLOADS["decode_gqa_bf16"].with_(name="paged_bad", B=4, M=512, len_range=(10, 300))
+    inp = make_inputs(wl, 9, "cpu")
+    kp, vp, table = paged_layout(inp["key_cache"], inp["value_cache"], 64, 9, spare_blocks=2)
+    lens = inp["lengths"].numpy()
+    nb = kp.shape[0]
+    for b in range(4):  # unused blocks of every row: out of range both ways
+        first_unused = (int(lens[b]) + 1 + 63) // 64
+        table[b, first_unused:] = torch.tensor([-5, nb, 1 << 30, -1, nb + 7, 12345, -99, nb])[
+            :table.shape[1] - first_unused]
+    rest = {k: v for k, v in inp.items() if k not in ("key_cache", "value_cache")}
+    ref = paged_ref(rest, kp, vp, table)
+    out = run_paged(rest, kp, vp, table)
+    check_step(out, ref, "bf16", "paged unused bad entries")
+    # now a bad entry inside the visible prefix of the longest row (its first
+    # block, not the one its new row goes to): the other rows stay exact
+    bb = int(np.argmax(lens))
+    assert lens[bb] >= 64
+    bad = table.clone()
+    bad[bb, 0] = nb + 3
+    out2 = run_paged(rest, kp, vp, bad)
+    for b in [x for x in range(4) if x != bb]:
+        np.testing.assert_array_equal(to_f64(out2["attention"][b]), to_f64(out["attention"][b]))
+        np.testing.assert_array_equal(to_f64(out2["context"][b]), to_f64(out["context"][b]))
+    assert torch.equal(bits_t(out2["key_cache"]), bits_t(out["key_cache"]))
+    assert torch.equal(bits_t(out2["value_cache"]), bits_t(out["value_cache"]))
+
+
+def test_paged_unsupported_shapes_are_refused():
+    """Blocks smaller than a decode chunk, and shapes outside the decode path,
+    come back as KVC_ERR_UNSUPPORTED before anything runs."""
+    wl = WORKLOADS["decode_gqa_bf16"].with_(name="paged_refuse", B=2, M=256, len_range=(0, 200))
+    inp = make_inputs(wl, 1, "cpu")
+    kp, vp, table = paged_layout(inp["key_cache"], inp["value_cache"], 32, 1)
+    rest = {k: v for k, v in inp.items() if k not in ("key_cache", "value_cache")}
+    with pytest.raises(kvc.KvcError) as e:
+        run_paged(rest, kp, vp, table)
+    assert e.value.code == -8
