@@ -425,15 +425,51 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
   // the loop issues the same loads.
   // Paged: a chunk lies inside one block (blocks hold a power of two >= C
   // slots), so its rows are contiguous too; an entry outside the pool reads
-  // as zero rows.
-  auto src_of = [&](const ChunkPos& p, bool live, const uint8_t* cin, const void* fresh,
-                    int rowb) {
+  // as zero rows.  FUSED: the wave keeps the blocks of its next 64 chunks
+  // in LDS (entry i: chunk blk_base + i, read once per 64 chunks, so no
+  // chunk waits on the table); otherwise each chunk reads its table entry.
+  __shared__ int32_t blk_all[(PAGED && FUSED) ? kDecodeWaves : 1][kWave];
+  int64_t blk_base = x_begin;
+  auto fill_blocks = [&](int64_t x0) {
+    blk_base = x0;
+    if constexpr (PAGED && FUSED) {
+      int32_t blk_lane = -1;
+      const int64_t xl = x0 + lane;
+      if (xl < x_end) {
+        int lo = 0, hi = static_cast<int>(a.B) - 1;  // the row holding chunk xl
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) / 2;
+          if (rt_first[mid] <= xl) lo = mid; else hi = mid - 1;
+        }
+        const int nc = static_cast<int>(stream_chunks(rt_len[lo], rt_n[lo], C));
+        const int rel = static_cast<int>(xl - rt_first[lo]);
+        const int c = rel % nc;
+        if (c != nc - 1)  // cached rows (the last chunk holds the appended ones)
+          blk_lane = a.block_table[static_cast<int64_t>(lo) * a.max_blocks +
+                                   ((static_cast<int64_t>(c) * C) >> a.block_log2)];
+      }
+      blk_all[wave][lane] = blk_lane;
+      wave_lds_sync();
+    }
+  };
+  if constexpr (PAGED && FUSED) fill_blocks(x_begin);
+  auto src_of = [&](const ChunkPos& p, int64_t xp, bool live, const uint8_t* cin,
+                    const void* fresh, int rowb) {
     RowSrc r{cin, 0u};
     if (live) {
       const int64_t g = grp_of(p);
       r.bytes = static_cast<uint32_t>(n_all_of(p)) * rowb;
       if (is_new_of(p)) {
         r.rows = static_cast<const uint8_t*>(fresh) + g * Q * rowb;
+      } else if constexpr (PAGED && FUSED) {
+        const int64_t blk =
+            __builtin_amdgcn_readfirstlane(blk_all[wave][static_cast<int>(xp - blk_base)]);
+        const int64_t bs = int64_t(1) << a.block_log2;
+        const bool ok = blk >= 0 && blk < a.num_blocks;
+        r.rows = cin + ((blk * Hk + p.kvh) * bs + ((static_cast<int64_t>(p.c) * C) & (bs - 1))) *
+                           rowb;
+        r.rows = ok ? r.rows : cin;
+        r.bytes = ok ? r.bytes : 0u;
       } else if constexpr (PAGED) {
         const uint8_t* row0 = slot_row(a, cin, p.b, p.kvh, static_cast<int64_t>(p.c) * C, rowb);
         r.rows = row0 ? row0 : cin;
@@ -470,8 +506,8 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
   }
   load_q(qf, pos, true);
   {
-    const RowSrc sk = src_of(pos, true, kin, a.new_key, KROW);
-    const RowSrc sv = src_of(pos, true, vin, a.new_value, VROW);
+    const RowSrc sk = src_of(pos, x_begin, true, kin, a.new_key, KROW);
+    const RowSrc sv = src_of(pos, x_begin, true, vin, a.new_value, VROW);
 #pragma unroll
     for (int u = 0; u < UK; u++) kbuf[u] = load_one(sk, u, k_off);
 #pragma unroll
@@ -510,8 +546,11 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
       }
     }
     const bool more = x + 1 < x_end;
-    const RowSrc nk = src_of(nxt, more, kin, a.new_key, KROW);
-    const RowSrc nv = src_of(nxt, more, vin, a.new_value, VROW);
+    if constexpr (PAGED && FUSED) {
+      if (more && x + 1 - blk_base == kWave) fill_blocks(x + 1);
+    }
+    const RowSrc nk = src_of(nxt, x + 1, more, kin, a.new_key, KROW);
+    const RowSrc nv = src_of(nxt, x + 1, more, vin, a.new_value, VROW);
 
     // ---- K: scores; each group's registers reload the next chunk's K ----
     Acc sc[NG];  // this lane's finished scores: packed row my_row, one per group

@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode steps/s + achieved HBM GB/s (% of MI355X peak), GQA Hq32/Hk8 D128 M8192"
 PEAK_HBM_GBPS = 8000.0
 DOMINANT_KERNEL = "attend"
+ENTRY = {"inplace": "kvc_step_inplace", "oop": "kvc_step_out_of_place", "paged": "kvc_step_paged"}
 
 
 def parse():
@@ -41,7 +42,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode_gqa_bf16")
-    p.add_argument("--mode", choices=["inplace", "oop"], default="inplace")
+    p.add_argument("--mode", choices=["inplace", "oop", "paged"], default="inplace")
+    p.add_argument("--block-size", type=int, default=64,
+                   help="paged mode: slots per cache block (the pools are block-permuted)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--copies", type=int, default=4,
                    help="independent input sets the steps rotate over (each step reads data "
@@ -192,7 +195,7 @@ def main():
     import torch
     from autoregressive_kv_cache_amd import kvc
     from autoregressive_kv_cache_amd.workloads import (WORKLOADS, draw_lengths_and_counts,
-                                                       make_inputs)
+                                                       make_inputs, paged_layout)
     kvc.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -214,6 +217,11 @@ def main():
         if args.mode == "oop":
             d["kc_out"] = torch.empty_like(inp["key_cache"])
             d["vc_out"] = torch.empty_like(inp["value_cache"])
+        if args.mode == "paged":
+            d["kp"], d["vp"], d["table"] = paged_layout(inp["key_cache"], inp["value_cache"],
+                                                        args.block_size, args.seed + k)
+            if k > 0:  # only the first set's dense caches are kept (for the plan)
+                del d["key_cache"], d["value_cache"], inp
         sets.append(d)
         if k == 0:
             first_inputs = inp
@@ -230,7 +238,11 @@ def main():
     def step(i=None, k=0):
         d = sets[k % len(sets)]
         events = None if i is None else (starts[i], stops[i])
-        if args.mode == "inplace":
+        if args.mode == "paged":
+            kvc.kvc_step_paged(d["query"], d["new_key"], d["new_value"], d["kp"], d["vp"],
+                               d["table"], d["lengths"], d["mask"], d["lens_out"], d["att"],
+                               d["ctx"], d["status"], workspace=ws, scale=wl.scale, events=events)
+        elif args.mode == "inplace":
             kvc.kvc_step_inplace(d["query"], d["new_key"], d["new_value"], d["key_cache"],
                                  d["value_cache"], d["lengths"], d["mask"], d["lens_out"],
                                  d["att"], d["ctx"], d["status"], workspace=ws, scale=wl.scale,
@@ -279,7 +291,7 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "entry": f"kvc_step_{'inplace' if args.mode == 'inplace' else 'out_of_place'}",
+        "config": {"workload": wl.name, "entry": ENTRY[args.mode],
                    "B": wl.B, "Hq": wl.Hq, "Hk": wl.Hk, "Q": wl.Q, "M": wl.M, "D": wl.D,
                    "Dv": wl.Dv, "seed": args.seed, "input_copies": len(sets), "plan": plan},
         "achieved_gbps": step_gbps,
@@ -292,6 +304,8 @@ def main():
                      "traffic": traffic, "bytes_per_launch": attend_bytes,
                      "avg_launch_ms": k_ms},
     }
+    if args.mode == "paged":
+        result["config"]["block_size"] = args.block_size
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, first_inputs, args.cpu_seconds)
     print(json.dumps(result), flush=True)
