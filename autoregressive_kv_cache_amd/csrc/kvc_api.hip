@@ -102,14 +102,16 @@ struct ChunkEntry {
 template <int D, int DV>
 void launch_chunk(const StepArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((kvc::attend_chunk_kernel<D, DV>),
-                     dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk_max)),
+                     dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk_max *
+                                                kvc::chunk_row_groups(a.R))),
                      dim3(kvc::kChunkThreads), 0, s, a);
 }
 
 template <int D, int DV>
 void launch_chunk_f32(const StepArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((kvc::attend_chunk_f32_kernel<D, DV>),
-                     dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk_max)),
+                     dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk_max *
+                                                kvc::chunk_row_groups(a.R))),
                      dim3(kvc::kChunkThreads), 0, s, a);
 }
 
@@ -237,7 +239,8 @@ int make_plan(const kvc_dims* d, int dtype, Plan* p) {
   } else if (p->chunk) {
     if (!make_layout(d, R, kvc::kChunkSlots, false, 0, &p->dense)) return KVC_ERR_SHAPE;
     int64_t cwgs;
-    if (!mul_ok(d->B * d->Hk, p->dense.nchunk_max, kMaxWorkgroups, &cwgs) ||
+    if (!mul_ok(d->B * d->Hk, p->dense.nchunk_max * kvc::chunk_row_groups(R), kMaxWorkgroups,
+                &cwgs) ||
         !mul_ok(d->B * d->Hk, row_blocks, kMaxElems, &cwgs) ||
         !mul_ok(cwgs, (d->M + p->dense.CS - 1) / p->dense.CS + 1, kMaxWorkgroups, &cwgs))
       return KVC_ERR_SHAPE;

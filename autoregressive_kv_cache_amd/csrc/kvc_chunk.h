@@ -2,9 +2,9 @@
 // (multi-token appends: G * Q > 8), bf16, on the matrix cores.
 //
 // One workgroup handles one (batch row b, KV head h, chunk c of 64 slots)
-// for all R = G * Q packed query rows of that head (row r = g * Q + t reads
-// query head h * G + g, token t):
-//   1. cache writes for the chunk's slot range, as on the page
+// and one group of up to 64 packed query rows of that head (row r = g * Q +
+// t reads query head h * G + g, token t; chunk_row_groups groups per chunk):
+//   1. (first group only) cache writes for the chunk's slot range, as on the page
 //      "Autoregressive KV-cache append and causal attention" (Required
 //      behavior): new rows at slot length + t, out of place every other slot
 //      copied bit for bit;
@@ -34,6 +34,15 @@ constexpr int kChunkSlots = 64;      // slots per chunk (C)
 constexpr int kChunkThreads = 256;   // four waves
 constexpr int kChunkWaves = kChunkThreads / kWave;
 constexpr int kChunkBlockRows = 16;  // packed rows per matrix block
+
+// Workgroups per (b, KV head, chunk): each takes kChunkWaves blocks of 16
+// packed rows (one per wave), so many packed rows spread over more compute
+// units instead of queueing on one.
+__host__ __device__ inline int chunk_row_groups(int64_t R) {
+  const int64_t nblk = (R + kChunkBlockRows - 1) / kChunkBlockRows;
+  const int64_t g = (nblk + kChunkWaves - 1) / kChunkWaves;
+  return static_cast<int>(g > 0 ? g : 1);
+}
 
 typedef __bf16 mfma_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float mfma_f32x4 __attribute__((ext_vector_type(4)));
@@ -67,8 +76,10 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_kernel(StepArgs a)
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
-  const int64_t c = blockIdx.x % a.nchunk_max;
-  const int64_t grp = blockIdx.x / a.nchunk_max;
+  const int RG = chunk_row_groups(a.R);
+  const int rg = static_cast<int>(blockIdx.x % RG);
+  const int64_t c = (blockIdx.x / RG) % a.nchunk_max;
+  const int64_t grp = blockIdx.x / RG / a.nchunk_max;
   const int64_t b = grp / a.Hk, kvh = grp % a.Hk;
 
   if (wave == 0) {
@@ -77,7 +88,7 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_kernel(StepArgs a)
   }
   __syncthreads();
   const RowInfo ri = info_sh;
-  if (c == 0 && kvh == 0 && tid == 0) {
+  if (c == 0 && kvh == 0 && rg == 0 && tid == 0) {
     a.ws_rowinfo[b * 4 + 0] = ri.len;
     a.ws_rowinfo[b * 4 + 1] = ri.n;
     a.ws_rowinfo[b * 4 + 2] = ri.status;
@@ -94,14 +105,16 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_kernel(StepArgs a)
   const uint16_t* nv_head = static_cast<const uint16_t*>(a.new_value) + head * a.Q * DV;
 
   // 1. cache writes of the slot range [s0, s1)
-  write_cache_slots(static_cast<uint8_t*>(a.kc_out) + head * a.M * D * 2,
-                    reinterpret_cast<const uint8_t*>(k_head),
-                    reinterpret_cast<const uint8_t*>(nk_head), D * 2, s0, s1, len, n,
-                    a.out_of_place != 0, tid, kChunkThreads);
-  write_cache_slots(static_cast<uint8_t*>(a.vc_out) + head * a.M * DV * 2,
-                    reinterpret_cast<const uint8_t*>(v_head),
-                    reinterpret_cast<const uint8_t*>(nv_head), DV * 2, s0, s1, len, n,
-                    a.out_of_place != 0, tid, kChunkThreads);
+  if (rg == 0) {  // the chunk's cache writes, once
+    write_cache_slots(static_cast<uint8_t*>(a.kc_out) + head * a.M * D * 2,
+                      reinterpret_cast<const uint8_t*>(k_head),
+                      reinterpret_cast<const uint8_t*>(nk_head), D * 2, s0, s1, len, n,
+                      a.out_of_place != 0, tid, kChunkThreads);
+    write_cache_slots(static_cast<uint8_t*>(a.vc_out) + head * a.M * DV * 2,
+                      reinterpret_cast<const uint8_t*>(v_head),
+                      reinterpret_cast<const uint8_t*>(nv_head), DV * 2, s0, s1, len, n,
+                      a.out_of_place != 0, tid, kChunkThreads);
+  }
   if (a.R == 0 || c >= row_chunks(len, n, C)) return;
   const int nact = static_cast<int>((s1 < new_len ? s1 : new_len) - s0);  // visited slots
 
@@ -137,7 +150,8 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_kernel(StepArgs a)
   uint16_t* att = static_cast<uint16_t*>(a.attention);
   uint16_t* ptile = p_s[wave];
   const int nblk = (a.R + kChunkBlockRows - 1) / kChunkBlockRows;
-  for (int blk = wave; blk < nblk; blk += kChunkWaves) {
+  const int blk_end = (rg + 1) * kChunkWaves < nblk ? (rg + 1) * kChunkWaves : nblk;
+  for (int blk = rg * kChunkWaves + wave; blk < blk_end; blk += kChunkWaves) {
     // query rows as A operands: lane holds row li, dims kk*32 + 8*lq + e
     uint4 qa[D / 32];
     {
@@ -281,8 +295,10 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_f32_kernel(StepArg
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
-  const int64_t c = blockIdx.x % a.nchunk_max;
-  const int64_t grp = blockIdx.x / a.nchunk_max;
+  const int RG = chunk_row_groups(a.R);
+  const int rg = static_cast<int>(blockIdx.x % RG);
+  const int64_t c = (blockIdx.x / RG) % a.nchunk_max;
+  const int64_t grp = blockIdx.x / RG / a.nchunk_max;
   const int64_t b = grp / a.Hk, kvh = grp % a.Hk;
 
   if (wave == 0) {
@@ -291,7 +307,7 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_f32_kernel(StepArg
   }
   __syncthreads();
   const RowInfo ri = info_sh;
-  if (c == 0 && kvh == 0 && tid == 0) {
+  if (c == 0 && kvh == 0 && rg == 0 && tid == 0) {
     a.ws_rowinfo[b * 4 + 0] = ri.len;
     a.ws_rowinfo[b * 4 + 1] = ri.n;
     a.ws_rowinfo[b * 4 + 2] = ri.status;
@@ -308,14 +324,16 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_f32_kernel(StepArg
   const float* nv_head = static_cast<const float*>(a.new_value) + head * a.Q * DV;
 
   // 1. cache writes of the slot range [s0, s1)
-  write_cache_slots(static_cast<uint8_t*>(a.kc_out) + head * a.M * D * 4,
-                    reinterpret_cast<const uint8_t*>(k_head),
-                    reinterpret_cast<const uint8_t*>(nk_head), D * 4, s0, s1, len, n,
-                    a.out_of_place != 0, tid, kChunkThreads);
-  write_cache_slots(static_cast<uint8_t*>(a.vc_out) + head * a.M * DV * 4,
-                    reinterpret_cast<const uint8_t*>(v_head),
-                    reinterpret_cast<const uint8_t*>(nv_head), DV * 4, s0, s1, len, n,
-                    a.out_of_place != 0, tid, kChunkThreads);
+  if (rg == 0) {  // the chunk's cache writes, once
+    write_cache_slots(static_cast<uint8_t*>(a.kc_out) + head * a.M * D * 4,
+                      reinterpret_cast<const uint8_t*>(k_head),
+                      reinterpret_cast<const uint8_t*>(nk_head), D * 4, s0, s1, len, n,
+                      a.out_of_place != 0, tid, kChunkThreads);
+    write_cache_slots(static_cast<uint8_t*>(a.vc_out) + head * a.M * DV * 4,
+                      reinterpret_cast<const uint8_t*>(v_head),
+                      reinterpret_cast<const uint8_t*>(nv_head), DV * 4, s0, s1, len, n,
+                      a.out_of_place != 0, tid, kChunkThreads);
+  }
   if (a.R == 0 || c >= row_chunks(len, n, C)) return;
   const int nact = static_cast<int>((s1 < new_len ? s1 : new_len) - s0);
 
@@ -345,7 +363,8 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_f32_kernel(StepArg
   float* att = static_cast<float*>(a.attention);
   double* ptile = p_s[wave];
   const int nblk = (a.R + kChunkBlockRows - 1) / kChunkBlockRows;
-  for (int blk = wave; blk < nblk; blk += kChunkWaves) {
+  const int blk_end = (rg + 1) * kChunkWaves < nblk ? (rg + 1) * kChunkWaves : nblk;
+  for (int blk = rg * kChunkWaves + wave; blk < blk_end; blk += kChunkWaves) {
     // query row li as A operand: element 4 kk + lq
     double qa[D / 4];
     {
