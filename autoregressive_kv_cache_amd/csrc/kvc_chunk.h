@@ -337,20 +337,26 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_f32_kernel(StepArg
   if (a.R == 0 || c >= row_chunks(len, n, C)) return;
   const int nact = static_cast<int>((s1 < new_len ? s1 : new_len) - s0);
 
-  // 2. K and V rows of the chunk into LDS (slots >= nact as zeros)
-  for (int idx = tid; idx < C * D; idx += kChunkThreads) {
-    const int slot = idx / D, d = idx % D;
+  // 2. K and V rows of the chunk into LDS (slots >= nact as zeros), read in
+  // 16-byte pieces
+  for (int idx = tid; idx < C * (D / 4); idx += kChunkThreads) {
+    const int slot = idx / (D / 4), d = (idx % (D / 4)) * 4;
     const int64_t j = s0 + slot;
-    float x = 0.f;
-    if (slot < nact) x = j < len ? k_head[j * D + d] : nk_head[(j - len) * D + d];
-    k_s[slot * KP + d] = x;
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (slot < nact)
+      x = *reinterpret_cast<const float4*>(j < len ? k_head + j * D + d : nk_head + (j - len) * D + d);
+    float* dst = k_s + slot * KP + d;
+    dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
   }
-  for (int idx = tid; idx < C * DV; idx += kChunkThreads) {
-    const int slot = idx / DV, d = idx % DV;
+  for (int idx = tid; idx < C * (DV / 4); idx += kChunkThreads) {
+    const int slot = idx / (DV / 4), d = (idx % (DV / 4)) * 4;
     const int64_t j = s0 + slot;
-    float x = 0.f;
-    if (slot < nact) x = j < len ? v_head[j * DV + d] : nv_head[(j - len) * DV + d];
-    v_s[slot * VP + d] = x;
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (slot < nact)
+      x = *reinterpret_cast<const float4*>(j < len ? v_head + j * DV + d
+                                                   : nv_head + (j - len) * DV + d);
+    float* dst = v_s + slot * VP + d;
+    dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
   }
   __syncthreads();
 
@@ -407,7 +413,9 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_f32_kernel(StepArg
       double sum = 0.0;
 #pragma unroll
       for (int jt = 0; jt < C / 16; jt++) {
-        sv[jt] = sv[jt] == neg_inf ? 0.0 : exp(sv[jt] - mx);
+        // s - m is exact in fp64; its exponential in fp32 is within ~1e-6
+        // relative for every term that is not negligible (s - m > -88)
+        sv[jt] = sv[jt] == neg_inf ? 0.0 : static_cast<double>(expf(static_cast<float>(sv[jt] - mx)));
         sum += sv[jt];
       }
 #pragma unroll
