@@ -490,3 +490,63 @@ def test_paged_unsupported_shapes_are_refused():
     with pytest.raises(kvc.KvcError) as e:
         run_paged(rest, kp, vp, table)
     assert e.value.code == -8
+
+
+# -- capture in a HIP graph (serving loops replay a captured step) ----------
+@pytest.mark.parametrize("wl_name,paged", [("decode_gqa_bf16", False), ("chunk_gqa_bf16", False),
+                                           ("decode_gqa_bf16", True)])
+def test_graph_replays_match_eager(wl_name, paged):
+    """The step enqueues only kernels on the caller's stream (no allocation,
+    no memset, no synchronisation), so it can be captured in a HIP graph.
+    Several replays, with eager work and synchronisations between them, each
+    give the eager result bit for bit (in place, lengths_out != lengths, so
+    every replay is the same step)."""
+    wl = WORKLOADS[wl_name].with_(name="graph", B=4, M=1024, len_range=(0, 1000))
+    inp = {k: v.to(DEV) for k, v in make_inputs(wl, 3, "cpu").items()}
+    B, Hq, Q, _ = inp["query"].shape
+    M, Dv = inp["key_cache"].shape[2], inp["value_cache"].shape[3]
+    mask = inp["append_mask"].contiguous().view(torch.uint8)
+    if paged:
+        kp, vp, table = paged_layout(inp["key_cache"], inp["value_cache"], 64, 3)
+        dims = kvc.KvcDims(B, Hq, kp.shape[1], Q, M, inp["query"].shape[3], Dv)
+    else:
+        dims = kvc.dims_of(inp["query"], inp["key_cache"], inp["value_cache"])
+    ws = kvc.workspace_for(dims, kvc.dtype_code(wl.torch_dtype), DEV)
+    att = torch.empty(B, Hq, Q, M, dtype=wl.torch_dtype, device=DEV)
+    ctx = torch.empty(B, Hq, Q, Dv, dtype=wl.torch_dtype, device=DEV)
+    lens_out = torch.empty_like(inp["lengths"])
+    status = torch.empty(B, dtype=torch.int32, device=DEV)
+
+    def step(stream=None):
+        if paged:
+            kvc.kvc_step_paged(inp["query"], inp["new_key"], inp["new_value"], kp, vp, table,
+                               inp["lengths"], mask, lens_out, att, ctx, status, workspace=ws,
+                               stream=stream)
+        else:
+            kvc.kvc_step_inplace(inp["query"], inp["new_key"], inp["new_value"],
+                                 inp["key_cache"], inp["value_cache"], inp["lengths"], mask,
+                                 lens_out, att, ctx, status, workspace=ws, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (att, ctx, lens_out, status)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step(stream=s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in (att, ctx):
+            t.fill_(float("nan"))
+        lens_out.fill_(-1)
+        status.fill_(-9)
+        scratch = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, exp in zip((att, ctx, lens_out, status), want):
+            assert torch.equal(got.view(torch.int16) if got.element_size() == 2 else got,
+                               exp.view(torch.int16) if exp.element_size() == 2 else exp), \
+                f"replay {rep} differs ({wl_name}, paged={paged})"
+        del scratch
