@@ -22,7 +22,7 @@ SOURCE = os.path.join(HERE, "kvc_oracle.c")
 LIBRARY = os.path.join(HERE, "libkvc_oracle.so")
 
 F32, BF16 = 0, 1
-ROW_OK, ROW_BAD_LENGTH, ROW_OVERFLOW, ROW_NOT_PREFIX = 0, 1, 2, 3
+ROW_OK, ROW_BAD_LENGTH, ROW_OVERFLOW, ROW_NOT_PREFIX, ROW_BAD_QUERIES = 0, 1, 2, 3, 4
 
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -78,6 +78,9 @@ class Oracle:
         lib.kvc_oracle_attend_row.argtypes = ([_i64] * 7 + [ctypes.c_int, ctypes.c_int,
                                               ctypes.c_double] + [_vp] * 3 + [_i64] * 5
                                              + [_vp] * 2)
+        lib.kvc_oracle_reattend.restype = ctypes.c_int
+        lib.kvc_oracle_reattend.argtypes = ([_i64] * 7 + [ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_double, _i64] + [_vp] * 8)
         lib.kvc_oracle_step.restype = ctypes.c_int
         lib.kvc_oracle_step.argtypes = ([_i64] * 7 + [ctypes.c_int, ctypes.c_int,
                                         ctypes.c_double] + [_vp] * 13)
@@ -222,6 +225,36 @@ def _oracle_step_paged(oracle: "Oracle", query, new_key, new_value, key_pool, va
 
 
 Oracle.step_paged = _oracle_step_paged
+
+
+def _oracle_reattend(oracle: "Oracle", q, cu_seqlens_q, key, value, seqlens_k, Q: int,
+                     sink=None, scale=None):
+    """Read-only re-attention over the logical caches key [B, Hk, M, D] /
+    value [B, Hk, M, Dv] (sequence b's cache; paged or row-mapped caches are
+    gathered into this form first).  Returns (out [Tq, Hq, Dv] float64,
+    status [B] int32)."""
+    q = np.ascontiguousarray(q)
+    key = np.ascontiguousarray(key)
+    value = np.ascontiguousarray(value)
+    cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int64)
+    lk = np.ascontiguousarray(seqlens_k, dtype=np.int64)
+    dt = _dtype_code(q)
+    Tq, Hq, D = q.shape
+    B, Hk, M, _ = key.shape
+    Dv = value.shape[3]
+    sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float64)
+    out = np.empty((Tq, Hq, Dv), dtype=np.float64)
+    status = np.empty(B, dtype=np.int32)
+    rc = oracle.lib.kvc_oracle_reattend(
+        B, Hq, Hk, int(Q), M, D, Dv, dt, 0 if scale is None else 1,
+        0.0 if scale is None else float(scale), Tq, _ptr(q), _ptr(cu), _ptr(key), _ptr(value),
+        _ptr(lk), _ptr(sk), _ptr(out), _ptr(status))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the re-attention (code {rc})")
+    return out, status
+
+
+Oracle.reattend = _oracle_reattend
 
 _DEFAULT: Oracle | None = None
 

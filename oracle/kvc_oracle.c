@@ -232,3 +232,68 @@ int kvc_oracle_step(int64_t B, int64_t Hq, int64_t Hk, int64_t Q, int64_t M,
   free(n);
   return rc;
 }
+
+/* Read-only re-attention ("ClikaRT::ops::attention_over_cache", function
+ * description): the cache is never written; sequence b's S_b queries are
+ * the last S_b positions of its L_b cached ones (the query position follows
+ * from the total cached length), so query t attends the prefix
+ * j <= L_b - S_b + t -- the same lower-right alignment as the step.  The
+ * per-head sink is one more logit in the softmax denominator that carries
+ * no value row.  Reading taken here: the sink is compared with the scaled
+ * scores as it is (it is not multiplied by the scale). */
+int kvc_oracle_reattend(int64_t B, int64_t Hq, int64_t Hk, int64_t Q,
+                        int64_t M, int64_t D, int64_t Dv, int dtype,
+                        int has_scale, double scale, int64_t Tq,
+                        const void *q, const int64_t *cu_q, const void *key,
+                        const void *value, const int64_t *seqlens_k,
+                        const double *sink, double *out, int32_t *status) {
+  int rc = check_dims(B, Hq, Hk, Q, M, D, Dv, dtype);
+  if (rc != KVC_ORACLE_OK) return rc;
+  double sc;
+  rc = resolve_scale(has_scale, scale, D, &sc);
+  if (rc != KVC_ORACLE_OK) return rc;
+  if (!q || !cu_q || !key || !value || !seqlens_k || !out || !status || Tq < 0)
+    return KVC_ORACLE_ENULL;
+  const int64_t G = Hq / Hk;
+  int64_t i, b, t, h, j, d;
+  for (i = 0; i < Tq * Hq * Dv; i++) out[i] = 0.0;
+  for (b = 0; b < B; b++) {
+    const int64_t L = seqlens_k[b], S = cu_q[b + 1] - cu_q[b];
+    if (L < 0 || L > M) {
+      status[b] = KVC_ORACLE_ROW_BAD_LENGTH;
+      continue;
+    }
+    if (S < 0 || S > Q || S > L || cu_q[b] < 0 || cu_q[b + 1] > Tq) {
+      status[b] = KVC_ORACLE_ROW_BAD_QUERIES;
+      continue;
+    }
+    status[b] = KVC_ORACLE_ROW_OK;
+    for (t = 0; t < S; t++) {
+      const int64_t qrow = cu_q[b] + t, pos = L - S + t;
+      for (h = 0; h < Hq; h++) {
+        const int64_t kh = h / G;
+        double *s = (double *)malloc((size_t)(pos + 1) * sizeof(double));
+        double m = -INFINITY, z = 0.0;
+        for (j = 0; j <= pos; j++) {
+          double acc = 0.0;
+          for (d = 0; d < D; d++)
+            acc += load_elem(q, (qrow * Hq + h) * D + d, dtype) *
+                   load_elem(key, ((b * Hk + kh) * M + j) * D + d, dtype);
+          s[j] = sc * acc;
+          if (s[j] > m) m = s[j];
+        }
+        if (sink && sink[h] > m) m = sink[h];
+        for (j = 0; j <= pos; j++) z += exp(s[j] - m);
+        if (sink) z += exp(sink[h] - m);
+        double *o = out + (qrow * Hq + h) * Dv;
+        for (j = 0; j <= pos; j++) {
+          const double p = exp(s[j] - m) / z;
+          for (d = 0; d < Dv; d++)
+            o[d] += p * load_elem(value, ((b * Hk + kh) * M + j) * Dv + d, dtype);
+        }
+        free(s);
+      }
+    }
+  }
+  return KVC_ORACLE_OK;
+}

@@ -42,6 +42,7 @@ extern "C" {
 #define KVC_ORACLE_ROW_BAD_LENGTH 1
 #define KVC_ORACLE_ROW_OVERFLOW 2
 #define KVC_ORACLE_ROW_NOT_PREFIX 3
+#define KVC_ORACLE_ROW_BAD_QUERIES 4
 
 /* Append only: copies both caches bit for bit into *_out, writes the True
  * prefix of new rows at slots length+t, and returns lengths_out, the number
@@ -76,6 +77,24 @@ int kvc_oracle_step(int64_t B, int64_t Hq, int64_t Hk, int64_t Q, int64_t M,
                     const uint8_t *append_mask, void *key_cache_out,
                     void *value_cache_out, int64_t *lengths_out,
                     double *attention, double *context, int32_t *row_status);
+
+/* Read-only re-attention over an already-appended cache ("ClikaRT::ops::
+ * attention_over_cache", function description): packed varlen queries
+ * q [Tq, Hq, D], sequence b owning rows cu_q[b] .. cu_q[b+1]-1 (S_b of
+ * them), over the logical cache key [B, Hk, M, D] / value [B, Hk, M, Dv]
+ * of which seqlens_k[b] = L_b slots are filled.  Query t of sequence b sits
+ * at position L_b - S_b + t and attends slots j <= L_b - S_b + t.  sink
+ * (double [Hq], or NULL) is a virtual logit per query head added to the
+ * softmax denominator.  out [Tq, Hq, Dv] double; status[b]:
+ * KVC_ORACLE_ROW_BAD_LENGTH (L_b outside [0, M]) or
+ * KVC_ORACLE_ROW_BAD_QUERIES (S_b < 0, S_b > Q or S_b > L_b), whose rows
+ * are zero. */
+int kvc_oracle_reattend(int64_t B, int64_t Hq, int64_t Hk, int64_t Q,
+                        int64_t M, int64_t D, int64_t Dv, int dtype,
+                        int has_scale, double scale, int64_t Tq,
+                        const void *q, const int64_t *cu_q, const void *key,
+                        const void *value, const int64_t *seqlens_k,
+                        const double *sink, double *out, int32_t *status);
 
 #ifdef __cplusplus
 }
