@@ -14,6 +14,7 @@
 #include "kvc_decode.h"
 #include "kvc_generic.h"
 #include "kvc_prep.h"
+#include "kvc_reattend.h"
 
 namespace {
 
@@ -346,15 +347,33 @@ void launch_stream(StepArgs& a, const DecodeEntry& e, hipStream_t stream, const 
 // [B][M / block_size] int32 block table.
 struct PagedPool {
   int64_t num_blocks, block_size;
-  const int32_t* table;
+  const int32_t* table;  // [B][M / block_size], or none with identity (block b)
+  bool identity;
 };
+
+void set_paged(StepArgs& a, const kvc_dims* d, const PagedPool& pg) {
+  a.paged = 1;
+  a.num_blocks = pg.num_blocks;
+  a.max_blocks = d->M / pg.block_size;
+  a.block_table = pg.table;
+  a.block_rows = pg.block_size;
+  a.block_log2 = 0;
+  if (pg.block_size == d->M) {  // one block per row (any M)
+    a.block_log2 = 62;
+    a.block_mask = -1;
+  } else {
+    while ((int64_t(1) << a.block_log2) < pg.block_size) a.block_log2++;
+    a.block_mask = pg.block_size - 1;
+  }
+}
 
 int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const void* query,
              const void* new_key, const void* new_value, const void* kc_in, const void* vc_in,
              void* kc_out, void* vc_out, bool out_of_place, const int64_t* lengths,
              const uint8_t* mask, int64_t* lengths_out, void* attention, void* context,
              int32_t* row_status, void* workspace, size_t workspace_bytes, void* stream,
-             const kvc_events* events, const PagedPool* pg = nullptr) {
+             const kvc_events* events, const PagedPool* pg = nullptr, bool read_only = false,
+             const float* sinks = nullptr) {
   Plan p;
   int rc = make_plan(d, dtype, &p);
   if (rc != KVC_OK) return rc;
@@ -363,16 +382,17 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
   if (rc != KVC_OK) return rc;
 
   if (pg) {
-    if (!pg->table) return KVC_ERR_NULL;
+    if (!pg->table && !pg->identity) return KVC_ERR_NULL;
     const int64_t bs = pg->block_size;
-    if (pg->num_blocks < 1 || bs < 1 || (bs & (bs - 1)) != 0 || d->M % bs != 0)
+    const bool single = bs == d->M;  // one block per row: a continuous cache, rows by table
+    if (pg->num_blocks < 1 || bs < 1 || (!single && ((bs & (bs - 1)) != 0 || d->M % bs != 0)))
       return KVC_ERR_SHAPE;
     int64_t x;
     if (!mul_ok(pg->num_blocks, d->Hk, kMaxElems, &x) || !mul_ok(x, bs, kMaxElems, &x) ||
         !mul_ok(x, d->D > d->Dv ? d->D : d->Dv, kMaxElems, &x))
       return KVC_ERR_SHAPE;
     // the stream decode path only, with every chunk inside one block
-    if (!p.decode || bs < p.decode->chunk) return KVC_ERR_UNSUPPORTED;
+    if (!p.decode || (!single && bs < p.decode->chunk)) return KVC_ERR_UNSUPPORTED;
   }
 
   if (!kc_in || !vc_in || !kc_out || !vc_out || !lengths || !lengths_out) return KVC_ERR_NULL;
@@ -392,7 +412,7 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
       r_lout{lengths_out, B * 8}, r_att{attention, B * Hq * Q * M * e},
       r_ctx{context, B * Hq * Q * Dv * e}, r_st{row_status, row_status ? B * 4 : 0},
       r_ws{workspace, p.pub.workspace_bytes};
-  const Range r_tab{pg ? pg->table : nullptr, pg ? B * (M / pg->block_size) * 4 : 0};
+  const Range r_tab{pg ? pg->table : nullptr, pg && pg->table ? B * (M / pg->block_size) * 4 : 0};
   const bool len_in_place = !out_of_place && lengths_out == lengths;
   const Range inputs[] = {r_q, r_nk, r_nv, r_mask, r_tab,
                           len_in_place ? Range{nullptr, 0} : r_len};
@@ -444,12 +464,10 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
   const bool vec_ok = p.decode && aligned;
   if (pg) {
     if (!vec_ok) return KVC_ERR_UNSUPPORTED;
-    a.paged = 1;
-    a.num_blocks = pg->num_blocks;
-    a.max_blocks = d->M / pg->block_size;
-    a.block_table = pg->table;
-    while ((int64_t(1) << a.block_log2) < pg->block_size) a.block_log2++;
+    set_paged(a, d, *pg);
   }
+  a.read_only = read_only ? 1 : 0;
+  a.sinks = sinks;
   const bool chunk_ok = p.chunk && aligned;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (chunk_ok) {
@@ -484,9 +502,158 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 
+// Workspace of a re-attention: the equivalent step's own workspace, then its
+// inputs (old lengths, mask, query rows, the appended-row copies) and
+// outputs (lengths, status, attention, context).
+struct ReattLayout {
+  size_t step, len0, lens_out, rstat, status, mask, qs, nk, nv, att, ctx, bytes;
+};
+
+bool reatt_layout(const kvc_dims* d, int dtype, ReattLayout* L) {
+  Plan p;
+  if (make_plan(d, dtype, &p) != KVC_OK) return false;
+  const size_t e = dtype == KVC_F32 ? 4 : 2;
+  const size_t B = d->B, Hq = d->Hq, Hk = d->Hk, Q = d->Q, M = d->M, D = d->D, Dv = d->Dv;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  L->step = p.pub.workspace_bytes;
+  take(L->step);
+  L->len0 = take(B * 8);
+  L->lens_out = take(B * 8);
+  L->rstat = take(B * 4);
+  L->status = take(B * 4);
+  L->mask = take(B * Q);
+  L->qs = take(B * Hq * Q * D * e);
+  L->nk = take(B * Hk * Q * D * e);
+  L->nv = take(B * Hk * Q * Dv * e);
+  L->att = take(B * Hq * Q * M * e);
+  L->ctx = take(B * Hq * Q * Dv * e);
+  L->bytes = off;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t kvc_attend_workspace_bytes(const kvc_dims* dims, int dtype) {
+  ReattLayout L;
+  return dims && reatt_layout(dims, dtype, &L) ? L.bytes : 0;
+}
+
+int kvc_attend_over_cache(const kvc_dims* dims, int dtype, int has_scale, double scale,
+                          const void* q, int64_t total_q, const int64_t* cu_seqlens_q,
+                          const void* key_cache, const void* value_cache, int64_t num_blocks,
+                          int64_t block_size, const int32_t* block_table, const int32_t* slot_ids,
+                          const int64_t* seqlens_k, const float* head_sink, void* out,
+                          int32_t* row_status, void* workspace, size_t workspace_bytes,
+                          void* stream, const kvc_events* events) {
+  if (!dims) return KVC_ERR_NULL;
+  const kvc_dims* d = dims;
+  int rc = check_dims(d, dtype);
+  if (rc != KVC_OK) return rc;
+  double sc;
+  rc = check_scale(has_scale, scale, d->D, &sc);
+  if (rc != KVC_OK) return rc;
+  ReattLayout L;
+  if (!reatt_layout(d, dtype, &L)) return KVC_ERR_SHAPE;
+  if (total_q < 0 || num_blocks < 1) return KVC_ERR_SHAPE;
+  if (!cu_seqlens_q || !key_cache || !value_cache || !seqlens_k || !workspace) return KVC_ERR_NULL;
+  if (total_q > 0 && (!q || !out)) return KVC_ERR_NULL;
+  if (workspace_bytes < L.bytes) return KVC_ERR_WORKSPACE;
+  int64_t x;
+  if (!mul_ok(total_q, d->Hq, kMaxElems, &x) || !mul_ok(x, d->D > d->Dv ? d->D : d->Dv, kMaxElems, &x))
+    return KVC_ERR_SHAPE;
+
+  // the cache: a block pool with a table, a continuous cache whose rows
+  // slot_ids picks (one block of M rows per sequence), or the continuous
+  // cache read row b for sequence b
+  PagedPool pg{num_blocks, block_size, nullptr, false};
+  const PagedPool* pgp = nullptr;
+  if (block_table) {
+    if (slot_ids) return KVC_ERR_SHAPE;  // one layout at a time
+    pg.table = block_table;
+    pgp = &pg;
+  } else {
+    if (block_size != d->M && block_size != 0) return KVC_ERR_SHAPE;
+    pg.block_size = d->M;
+    if (slot_ids) {
+      pg.table = slot_ids;
+      pgp = &pg;
+    } else if (num_blocks < d->B) {
+      return KVC_ERR_SHAPE;
+    }
+  }
+  if (pgp) {  // the checks the step makes on the mapped cache, before anything is enqueued
+    Plan p;
+    make_plan(d, dtype, &p);
+    const int64_t bs = pg.block_size;
+    const bool single = bs == d->M;
+    if (!single && ((bs & (bs - 1)) != 0 || d->M % bs != 0)) return KVC_ERR_SHAPE;
+    if (!p.decode || (!single && bs < p.decode->chunk) || !aligned16(key_cache) ||
+        !aligned16(value_cache))
+      return KVC_ERR_UNSUPPORTED;
+  }
+  const size_t e = dtype == KVC_F32 ? 4 : 2;
+  const size_t B = d->B, Hq = d->Hq, Hk = d->Hk, Tq = total_q, D = d->D, Dv = d->Dv;
+  const size_t rows = static_cast<size_t>(num_blocks) * static_cast<size_t>(pg.block_size);
+  const size_t tab = block_table ? B * static_cast<size_t>(d->M / pg.block_size) * 4
+                                 : (slot_ids ? B * 4 : 0);
+  const Range r_q{q, Tq * Hq * D * e}, r_cu{cu_seqlens_q, (B + 1) * 8},
+      r_kc{key_cache, rows * Hk * D * e}, r_vc{value_cache, rows * Hk * Dv * e},
+      r_tab{block_table ? static_cast<const void*>(block_table) : slot_ids, tab},
+      r_lk{seqlens_k, B * 8}, r_sink{head_sink, head_sink ? Hq * 4 : 0},
+      r_out{out, Tq * Hq * Dv * e}, r_st{row_status, row_status ? B * 4 : 0},
+      r_ws{workspace, L.bytes};
+  const Range ins[] = {r_q, r_cu, r_kc, r_vc, r_tab, r_lk, r_sink};
+  const Range outs[] = {r_out, r_st, r_ws};
+  for (int i = 0; i < 3; i++) {
+    for (const Range& in : ins)
+      if (overlap(outs[i], in)) return KVC_ERR_ALIAS;
+    for (int j = i + 1; j < 3; j++)
+      if (overlap(outs[i], outs[j])) return KVC_ERR_ALIAS;
+  }
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  StepArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.B = d->B; a.Hq = d->Hq; a.Hk = d->Hk; a.Q = d->Q; a.M = d->M; a.D = d->D; a.Dv = d->Dv;
+  a.G = static_cast<int32_t>(d->Hq / d->Hk);
+  a.elem_bytes = static_cast<int64_t>(e);
+  a.kc_in = key_cache;
+  a.vc_in = value_cache;
+  if (pgp) set_paged(a, d, *pgp);
+  kvc::ReattArgs r;
+  r.Tq = total_q;
+  r.q = static_cast<const uint8_t*>(q);
+  r.cu_q = cu_seqlens_q;
+  r.seqlens_k = seqlens_k;
+  r.out = static_cast<uint8_t*>(out);
+  r.row_status = row_status;
+  r.len0 = reinterpret_cast<int64_t*>(ws + L.len0);
+  r.mask = ws + L.mask;
+  r.qs = ws + L.qs;
+  r.nk = ws + L.nk;
+  r.nv = ws + L.nv;
+  r.rstat = reinterpret_cast<int32_t*>(ws + L.rstat);
+  r.ctx = ws + L.ctx;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(kvc::reattend_prep_kernel, dim3(static_cast<unsigned>(d->B)),
+                     dim3(kvc::kReattThreads), 0, s, a, r);
+  rc = run_step(d, dtype, has_scale, scale, r.qs, r.nk, r.nv, key_cache, value_cache,
+                const_cast<void*>(key_cache), const_cast<void*>(value_cache), false, r.len0,
+                r.mask, reinterpret_cast<int64_t*>(ws + L.lens_out), ws + L.att, ws + L.ctx,
+                reinterpret_cast<int32_t*>(ws + L.status), workspace, L.step, stream, events,
+                pgp, true, head_sink);
+  if (rc != KVC_OK) return rc;
+  hipLaunchKernelGGL(kvc::reattend_scatter_kernel, dim3(static_cast<unsigned>(d->B)),
+                     dim3(kvc::kReattThreads), 0, s, a, r);
+  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
 
 size_t kvc_workspace_bytes(const kvc_dims* dims, int dtype) {
   Plan p;
@@ -532,7 +699,7 @@ int kvc_step_paged(const kvc_dims* dims, int dtype, int has_scale, double scale,
                    int64_t* lengths_out, void* attention, void* context, int32_t* row_status,
                    void* workspace, size_t workspace_bytes, void* stream,
                    const kvc_events* events) {
-  const PagedPool pg{num_blocks, block_size, block_table};
+  const PagedPool pg{num_blocks, block_size, block_table, false};
   return run_step(dims, dtype, has_scale, scale, query, new_key, new_value, key_pool, value_pool,
                   key_pool, value_pool, false, lengths, append_mask, lengths_out, attention,
                   context, row_status, workspace, workspace_bytes, stream, events, &pg);
@@ -553,6 +720,8 @@ const char* kvc_status_string(int code) {
     case KVC_ROW_BAD_LENGTH: return "row rejected: length outside [0, M]";
     case KVC_ROW_OVERFLOW: return "row rejected: length + n exceeds M";
     case KVC_ROW_NOT_PREFIX: return "row rejected: append mask is not a prefix";
+    case KVC_ROW_BAD_QUERIES: return "sequence rejected: query range outside the packed queries, "
+                                     "longer than Q or than the cached length";
     default: return "unknown code";
   }
 }

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_kernel(StepArgs a)
   const uint16_t* nv_head = static_cast<const uint16_t*>(a.new_value) + head * a.Q * DV;
 
   // 1. cache writes of the slot range [s0, s1)
-  if (rg == 0) {  // the chunk's cache writes, once
+  if (rg == 0 && !a.read_only) {  // the chunk's cache writes, once
     write_cache_slots(static_cast<uint8_t*>(a.kc_out) + head * a.M * D * 2,
                       reinterpret_cast<const uint8_t*>(k_head),
                       reinterpret_cast<const uint8_t*>(nk_head), D * 2, s0, s1, len, n,
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_f32_kernel(StepArg
   const float* nv_head = static_cast<const float*>(a.new_value) + head * a.Q * DV;
 
   // 1. cache writes of the slot range [s0, s1)
-  if (rg == 0) {  // the chunk's cache writes, once
+  if (rg == 0 && !a.read_only) {  // the chunk's cache writes, once
     write_cache_slots(static_cast<uint8_t*>(a.kc_out) + head * a.M * D * 4,
                       reinterpret_cast<const uint8_t*>(k_head),
                       reinterpret_cast<const uint8_t*>(nk_head), D * 4, s0, s1, len, n,

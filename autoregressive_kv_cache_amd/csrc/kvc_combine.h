@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
   const int64_t e0 = ctx_role ? a.M : k * a.CS;
   const int64_t e1 = e0 + a.CS < a.M ? e0 + a.CS : a.M;
 
-  if (ctx_role && rb == 0 && a.seg_mode && !a.out_of_place && n > 0) {
+  if (ctx_role && rb == 0 && a.seg_mode && !a.out_of_place && !a.read_only && n > 0) {
     // in place, stream path: the appended rows go to their cache slots
     // (the attend kernel read them from new_key / new_value)
     const int64_t kb = a.D * E::kBytes, vb = a.Dv * E::kBytes;
@@ -292,6 +292,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
             (mo == neg_inf ? Acc(0) : lo * acc_exp(mo - mn));
       m = mn;
     }
+  }
+  if (t < n && a.sinks) {  // the head's sink: one more logit, no value row
+    const Acc sk = static_cast<Acc>(a.sinks[kvh * a.G + g]);
+    const Acc mn = sk > m ? sk : m;
+    l = (m == neg_inf ? Acc(0) : l * acc_exp(m - mn)) + acc_exp(sk - mn);
+    m = mn;
   }
   const Acc inv_l = l > 0 ? Acc(1) / l : Acc(0);
   auto factor = [&](Acc m_c) -> Acc { return m_c == neg_inf ? Acc(0) : acc_exp(m_c - m) * inv_l; };

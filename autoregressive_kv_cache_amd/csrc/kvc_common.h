@@ -107,15 +107,28 @@ struct StepArgs {
   double* ws_seg_ml;     // [nseg][R][2]: m_seg, l_seg
   float* ws_seg_o;       // [nseg][R][Dv]: o_seg
   int32_t* ws_wstart;    // [P][4]: first (b, head, chunk) of each stream worker
-  // paged cache (stream path, in place): kc_in/kc_out and vc_in/vc_out are
-  // the block pools [num_blocks][Hk][block][D or Dv]; slot j of batch row b
-  // is row j % block of block block_table[b * max_blocks + j / block]
+  // paged cache (stream path): kc_in/kc_out and vc_in/vc_out are the block
+  // pools [num_blocks][Hk][block_rows][D or Dv]; slot j of batch row b is
+  // row j & block_mask of block block_table[b * max_blocks + (j >> block_log2)]
+  // (a power-of-two block, or one block of M rows per batch row: log2 62,
+  // mask all ones); no table = block b
   int32_t paged;
   int32_t block_log2;
+  int64_t block_rows;
+  int64_t block_mask;
   int64_t num_blocks;
   int64_t max_blocks;
   const int32_t* block_table;
+  // read-only re-attention: no cache slot is written, and the combine adds
+  // sinks[query head] (if given) as one more logit to each softmax
+  int32_t read_only;
+  const float* sinks;
 };
+
+// Block holding slot j of batch row b (paged cache).
+__device__ inline int64_t block_of(const StepArgs& a, int64_t b, int64_t j) {
+  return a.block_table ? a.block_table[b * a.max_blocks + (j >> a.block_log2)] : b;
+}
 
 // Base of cache slot j of (batch row b, KV head h), rows of row_bytes bytes:
 // the dense [B][Hk][M] layout, or the paged block pool (nullptr when the
@@ -125,10 +138,9 @@ __device__ inline const uint8_t* slot_row(const StepArgs& a, const void* cache, 
                                           int64_t h, int64_t j, int64_t row_bytes) {
   const uint8_t* base = static_cast<const uint8_t*>(cache);
   if (!a.paged) return base + ((b * a.Hk + h) * a.M + j) * row_bytes;
-  const int64_t blk = a.block_table[b * a.max_blocks + (j >> a.block_log2)];
+  const int64_t blk = block_of(a, b, j);
   if (blk < 0 || blk >= a.num_blocks) return nullptr;
-  const int64_t bs = int64_t(1) << a.block_log2;
-  return base + ((blk * a.Hk + h) * bs + (j & (bs - 1))) * row_bytes;
+  return base + ((blk * a.Hk + h) * a.block_rows + (j & a.block_mask)) * row_bytes;
 }
 
 struct RowInfo {

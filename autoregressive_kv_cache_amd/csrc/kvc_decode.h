@@ -445,8 +445,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
         const int rel = static_cast<int>(xl - rt_first[lo]);
         const int c = rel % nc;
         if (c != nc - 1)  // cached rows (the last chunk holds the appended ones)
-          blk_lane = a.block_table[static_cast<int64_t>(lo) * a.max_blocks +
-                                   ((static_cast<int64_t>(c) * C) >> a.block_log2)];
+          blk_lane = static_cast<int32_t>(block_of(a, lo, static_cast<int64_t>(c) * C));
       }
       blk_all[wave][lane] = blk_lane;
       wave_lds_sync();
@@ -464,9 +463,9 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
       } else if constexpr (PAGED && FUSED) {
         const int64_t blk =
             __builtin_amdgcn_readfirstlane(blk_all[wave][static_cast<int>(xp - blk_base)]);
-        const int64_t bs = int64_t(1) << a.block_log2;
         const bool ok = blk >= 0 && blk < a.num_blocks;
-        r.rows = cin + ((blk * Hk + p.kvh) * bs + ((static_cast<int64_t>(p.c) * C) & (bs - 1))) *
+        r.rows = cin + ((blk * Hk + p.kvh) * a.block_rows +
+                        ((static_cast<int64_t>(p.c) * C) & a.block_mask)) *
                            rowb;
         r.rows = ok ? r.rows : cin;
         r.bytes = ok ? r.bytes : 0u;

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kGenericThreads) void attend_generic_kernel(StepArg
   const T* nv_head = nv + head * a.Q * a.Dv;
 
   // 1. cache writes
-  if (rt == 0) {
+  if (rt == 0 && !a.read_only) {
     const int64_t kb = a.D * E::kBytes, vb = a.Dv * E::kBytes;
     write_cache_slots(static_cast<uint8_t*>(a.kc_out) + head * a.M * kb,
                       reinterpret_cast<const uint8_t*>(k_head),

@@ -4,7 +4,8 @@ marshalling only -- every step of the computation runs in the HIP kernels of
 
 Low level (same names as the C entry points, tensors instead of pointers):
 ``kvc_workspace_bytes``, ``kvc_plan_step``, ``kvc_step_out_of_place``,
-``kvc_step_inplace``, ``kvc_step_paged``, ``kvc_status_string``.
+``kvc_step_inplace``, ``kvc_step_paged``, ``kvc_attend_workspace_bytes``,
+``kvc_attend_over_cache``, ``kvc_status_string``.
 
 Page-style face ("Autoregressive KV-cache append and causal attention",
 Function signature / Starter code): ``kv_cache_attention_step`` returns a
@@ -28,9 +29,10 @@ KVC_OK = 0
 ERRORS = {-1: "KVC_ERR_NULL", -2: "KVC_ERR_SHAPE", -3: "KVC_ERR_DTYPE", -4: "KVC_ERR_SCALE",
           -5: "KVC_ERR_WORKSPACE", -6: "KVC_ERR_ALIAS", -7: "KVC_ERR_HIP",
           -8: "KVC_ERR_UNSUPPORTED"}
-ROW_OK, ROW_BAD_LENGTH, ROW_OVERFLOW, ROW_NOT_PREFIX = 0, 1, 2, 3
+ROW_OK, ROW_BAD_LENGTH, ROW_OVERFLOW, ROW_NOT_PREFIX, ROW_BAD_QUERIES = 0, 1, 2, 3, 4
 EXPORTED = ("kvc_workspace_bytes", "kvc_plan_step", "kvc_step_out_of_place",
-            "kvc_step_inplace", "kvc_step_paged", "kvc_status_string")
+            "kvc_step_inplace", "kvc_step_paged", "kvc_attend_workspace_bytes",
+            "kvc_attend_over_cache", "kvc_status_string")
 
 
 class KvcDims(ctypes.Structure):
@@ -83,6 +85,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kvc_step_paged.argtypes = ([ctypes.POINTER(KvcDims), _int, _int, _dbl] + [_vp] * 5
                                    + [_i64, _i64] + [_vp] * 8 + [_sz, _vp,
                                                                  ctypes.POINTER(KvcEvents)])
+    lib.kvc_attend_workspace_bytes.restype = _sz
+    lib.kvc_attend_workspace_bytes.argtypes = [ctypes.POINTER(KvcDims), _int]
+    lib.kvc_attend_over_cache.restype = _int
+    lib.kvc_attend_over_cache.argtypes = ([ctypes.POINTER(KvcDims), _int, _int, _dbl, _vp, _i64,
+                                           _vp, _vp, _vp, _i64, _i64] + [_vp] * 7
+                                          + [_sz, _vp, ctypes.POINTER(KvcEvents)])
     lib.kvc_status_string.restype = ctypes.c_char_p
     lib.kvc_status_string.argtypes = [_int]
     _LIB = lib
@@ -210,6 +218,39 @@ def kvc_step_paged(query, new_key, new_value, key_pool, value_pool, block_table,
         _events(events))
     if rc != KVC_OK:
         raise KvcError(rc, "kvc_step_paged")
+
+
+def kvc_attend_workspace_bytes(dims: KvcDims, dtype: int) -> int:
+    return int(load().kvc_attend_workspace_bytes(ctypes.byref(dims), int(dtype)))
+
+
+def kvc_attend_over_cache(q, cu_seqlens_q, key_cache, value_cache, seqlens_k, out, Q: int,
+                          M: int | None = None, block_table=None, slot_ids=None, head_sink=None,
+                          row_status=None, workspace=None, scale=None, stream=None,
+                          events=None) -> None:
+    """Enqueue the read-only re-attention on ``stream``.  ``key_cache`` is a
+    block pool ``[num_blocks, Hk, block_size, D]`` when ``block_table`` is
+    given, else a continuous cache ``[rows, Hk, M, D]`` read through
+    ``slot_ids`` (or row b); ``Q`` is the most query tokens of a sequence."""
+    lib = load()
+    Tq, Hq, D = q.shape
+    num_blocks, Hk, bs, _ = key_cache.shape
+    B = seqlens_k.shape[0]
+    if M is None:
+        M = block_table.shape[1] * bs if block_table is not None else bs
+    dims = KvcDims(B, Hq, Hk, int(Q), int(M), D, value_cache.shape[3])
+    dt = dtype_code(key_cache.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(1, kvc_attend_workspace_bytes(dims, dt)), dtype=torch.uint8,
+                                device=key_cache.device)
+    hs, sc = _scale_args(scale)
+    rc = lib.kvc_attend_over_cache(
+        ctypes.byref(dims), dt, hs, sc, _ptr(q), int(Tq), _ptr(cu_seqlens_q), _ptr(key_cache),
+        _ptr(value_cache), int(num_blocks), int(bs), _ptr(block_table), _ptr(slot_ids),
+        _ptr(seqlens_k), _ptr(head_sink), _ptr(out), _ptr(row_status), _ptr(workspace),
+        workspace.numel(), _stream(stream, key_cache.device), _events(events))
+    if rc != KVC_OK:
+        raise KvcError(rc, "kvc_attend_over_cache")
 
 
 # ---------------------------------------------------------------------------

@@ -91,7 +91,10 @@ enum {
   KVC_ROW_OK = 0,
   KVC_ROW_BAD_LENGTH = 1,   /* lengths[b] < 0 or > M */
   KVC_ROW_OVERFLOW = 2,     /* lengths[b] + n_b > M */
-  KVC_ROW_NOT_PREFIX = 3    /* append_mask[b,:] has a True after a False */
+  KVC_ROW_NOT_PREFIX = 3,   /* append_mask[b,:] has a True after a False */
+  KVC_ROW_BAD_QUERIES = 4   /* kvc_attend_over_cache: a sequence's query range is
+                               not inside [0, total_q], or holds more than
+                               dims->Q tokens or more tokens than are cached */
 };
 
 /* Optional timing hook: when a kvc_events is passed, `start` and `stop`
@@ -169,9 +172,10 @@ int kvc_step_inplace(const kvc_dims *dims, int dtype, int has_scale,
  *
  * Scope: shapes the plan sends to the vector decode path (path 1: at most 8
  * packed query rows and a tabled (D, Dv)), 16-byte aligned buffers, and a
- * block_size that is a power of two of at least 64 slots; anything else
- * returns KVC_ERR_UNSUPPORTED (or KVC_ERR_SHAPE for a block_size that does
- * not divide M).  Table entries are device data: an entry outside
+ * block_size that is a power of two of at least 64 slots, or M itself (one
+ * block per row: a continuous cache whose rows the table picks); anything
+ * else returns KVC_ERR_UNSUPPORTED (or KVC_ERR_SHAPE for a block_size that
+ * does not divide M).  Table entries are device data: an entry outside
  * [0, num_blocks) for a slot below lengths[b] + n_b is outside the contract
  * -- those slots read as zero rows and are never written, so no access
  * leaves the pools -- and the row's results are then unspecified.  Rows may
@@ -188,6 +192,52 @@ int kvc_step_paged(const kvc_dims *dims, int dtype, int has_scale,
                    void *attention, void *context, int32_t *row_status,
                    void *workspace, size_t workspace_bytes, void *stream,
                    const kvc_events *events);
+
+/* Read-only re-attention over a cache another call already appended
+ * ("ClikaRT::ops::attention_over_cache", function description): no cache
+ * entry is written.
+ *
+ *   q            [total_q, Hq, D]   packed varlen queries; sequence b owns
+ *                                   rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *   cu_seqlens_q [B + 1] int64      (S_b = cu_seqlens_q[b+1] - cu_seqlens_q[b])
+ *   seqlens_k    [B] int64          each sequence's total cached length L_b
+ *   head_sink    [Hq] float32       optional per-head sink logit
+ *   out          [total_q, Hq, Dv]  written for every query row
+ *
+ * The cache is one of three layouts:
+ *   - paged: block_table [B, M / block_size] int32 (slot_ids NULL), pools
+ *     [num_blocks, Hk, block_size, D|Dv] as for kvc_step_paged;
+ *   - continuous with slot_ids [B] int32 (block_table NULL): key_cache
+ *     [num_blocks, Hk, M, D], sequence b reading row slot_ids[b];
+ *   - continuous without either: sequence b reads row b (num_blocks >= B).
+ * block_size is M (or 0) for the continuous layouts.
+ *
+ * dims: B sequences, Hq, Hk, Q = the most query tokens any sequence has,
+ * M = capacity per sequence, D, Dv.  Query t of sequence b sits at position
+ * L_b - S_b + t and attends slots j <= L_b - S_b + t (the lower-right
+ * alignment of the step); scores are scale * dot(q, k) (default 1/sqrt(D)),
+ * and the softmax denominator gains exp(head_sink[h] - m) when a sink is
+ * given (the sink is a logit on the scores' scale and carries no value).
+ * A sequence with L_b outside [0, M] (KVC_ROW_BAD_LENGTH) or a bad query
+ * range (KVC_ROW_BAD_QUERIES) gets zero output rows where its range is
+ * addressable, and its code in row_status (optional).
+ *
+ * Scope: the paged and slot_ids layouts take the shapes of the vector decode
+ * path ((Hq/Hk) * Q <= 8, tabled head sizes; else KVC_ERR_UNSUPPORTED); the
+ * continuous layout read by row takes every shape of kvc_step_inplace.
+ * workspace: kvc_attend_workspace_bytes(dims, dtype) bytes.  Outputs and the
+ * workspace must not overlap any input (KVC_ERR_ALIAS). */
+size_t kvc_attend_workspace_bytes(const kvc_dims *dims, int dtype);
+int kvc_attend_over_cache(const kvc_dims *dims, int dtype, int has_scale,
+                          double scale, const void *q, int64_t total_q,
+                          const int64_t *cu_seqlens_q, const void *key_cache,
+                          const void *value_cache, int64_t num_blocks,
+                          int64_t block_size, const int32_t *block_table,
+                          const int32_t *slot_ids, const int64_t *seqlens_k,
+                          const float *head_sink, void *out,
+                          int32_t *row_status, void *workspace,
+                          size_t workspace_bytes, void *stream,
+                          const kvc_events *events);
 
 /* Static description of a return or row-status code. */
 const char *kvc_status_string(int code);

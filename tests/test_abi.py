@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, 1, 2, 3]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, 1, 2, 3, 4]:
         s = kvc.kvc_status_string(code)
         assert s and s != "unknown code"
     assert kvc.kvc_status_string(12345) == "unknown code"
@@ -202,3 +202,45 @@ def test_host_checks_paged(lib):
     bad = list(ptrs)
     bad[4] = bad[3]  # both pools on one buffer
     assert run(d, ptrs=bad)[0] == -6
+
+
+def test_host_checks_attend_over_cache(lib):
+    """kvc_attend_over_cache: layout, scope, workspace and aliasing are checked
+    on the host before anything is enqueued (every call here fails one)."""
+    def run(d, Tq=4, num_blocks=8, block_size=None, table=False, slots=False, ptrs=None,
+            ws=1 << 34, sink=True):
+        e = 2
+        B, Hq, Hk, Q, M, D, Dv = d.B, d.Hq, d.Hk, d.Q, d.M, d.D, d.Dv
+        bs = M if block_size is None else block_size
+        sizes = [Tq * Hq * D * e, (B + 1) * 8, num_blocks * Hk * bs * D * e,
+                 num_blocks * Hk * bs * Dv * e, B * max(1, M // bs) * 4, B * 4, B * 8, Hq * 4,
+                 Tq * Hq * Dv * e, B * 4]
+        if ptrs is None:
+            ptrs, off = [], FAKE
+            for sz in sizes:
+                ptrs.append(off)
+                off += (sz + 4095) // 4096 * 4096 + 4096
+        qp, cu, kc, vc, tb, sl, lk, sk, out, st = ptrs
+        return lib.kvc_attend_over_cache(ctypes.byref(d), kvc.KVC_BF16, 0, 0.0, qp, Tq, cu, kc, vc,
+                                         num_blocks, bs, tb if table else None,
+                                         sl if slots else None, lk, sk if sink else None, out, st,
+                                         FAKE * 4, ws, None, None), ptrs
+
+    d = dims(B=4, Hq=8, Hk=2, Q=1, M=1024, D=128, Dv=128)
+    assert kvc.kvc_attend_workspace_bytes(d, kvc.KVC_BF16) > kvc.kvc_workspace_bytes(d, 1)
+    assert run(d, table=True, slots=True, block_size=64)[0] == -2   # two layouts at once
+    assert run(d, block_size=64)[0] == -2                           # continuous: block = M
+    assert run(d, num_blocks=3)[0] == -2                            # row b needs B rows
+    assert run(d, Tq=-1)[0] == -2
+    assert run(d, table=True, block_size=48)[0] == -2
+    assert run(d, table=True, block_size=32)[0] == -8               # smaller than a chunk
+    assert run(dims(B=4, Hq=8, Hk=2, Q=4, M=1024, D=128, Dv=128), slots=True)[0] == -8
+    assert run(d, ws=16)[0] == -5
+    _, ptrs = run(d, ws=16)
+    bad = list(ptrs)
+    bad[1] = None
+    assert run(d, ptrs=bad)[0] == -1
+    for out_i, in_i in [(8, 0), (8, 2), (9, 6), (8, 7)]:
+        bad = list(ptrs)
+        bad[out_i] = bad[in_i]
+        assert run(d, ptrs=bad)[0] == -6, (out_i, in_i)

@@ -550,3 +550,116 @@ def test_graph_replays_match_eager(wl_name, paged):
                                exp.view(torch.int16) if exp.element_size() == 2 else exp), \
                 f"replay {rep} differs ({wl_name}, paged={paged})"
         del scratch
+
+
+# -- read-only re-attention (kvc_attend_over_cache) --------------------------
+def reatt_case(dtype: str, B: int, Hq: int, Hk: int, Qmax: int, M: int, D: int, Dv: int,
+               seed: int, rows: int | None = None, std: float = 1.0):
+    """Packed queries, a continuous cache of ``rows`` rows, per-sequence query
+    counts S_b in [0, Qmax] and cached lengths L_b in [S_b, M] (seeded)."""
+    rng = np.random.default_rng(seed)
+    S = rng.integers(0, Qmax + 1, B)
+    S[0] = Qmax
+    L = np.array([rng.integers(s, M + 1) for s in S], np.int64)
+    L[-1] = M  # a full row
+    cu = np.concatenate([[0], np.cumsum(S)]).astype(np.int64)
+    g = torch.Generator().manual_seed(seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    rows = B if rows is None else rows
+    q = (torch.randn(int(cu[-1]), Hq, D, generator=g) * std).to(tdt)
+    kc = (torch.randn(rows, Hk, M, D, generator=g) * std).to(tdt)
+    vc = (torch.randn(rows, Hk, M, Dv, generator=g) * std).to(tdt)
+    return q, torch.from_numpy(cu), kc, vc, torch.from_numpy(L), S
+
+
+def run_reatt(q, cu, kc, vc, L, Q, M=None, table=None, slots=None, sink=None, scale=None):
+    d = {k: (None if v is None else v.to(DEV)) for k, v in dict(
+        q=q, cu=cu, kc=kc, vc=vc, L=L, table=table, slots=slots, sink=sink).items()}
+    out = torch.full((q.shape[0], q.shape[1], vc.shape[3]), float("nan"), dtype=kc.dtype,
+                     device=DEV)
+    status = torch.full((L.shape[0],), -9, dtype=torch.int32, device=DEV)
+    before = (bits_t(d["kc"]).clone(), bits_t(d["vc"]).clone())
+    kvc.kvc_attend_over_cache(d["q"], d["cu"], d["kc"], d["vc"], d["L"], out, Q, M=M,
+                              block_table=d["table"], slot_ids=d["slots"], head_sink=d["sink"],
+                              row_status=status, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(bits_t(d["kc"]), before[0]) and torch.equal(bits_t(d["vc"]), before[1]), \
+        "the cache was written"
+    return out.cpu(), status.cpu()
+
+
+def reatt_ref(q, cu, kc_logical, vc_logical, L, Q, sink=None, scale=None):
+    h = host_arrays({"q": q, "k": kc_logical, "v": vc_logical})
+    return oracle.default().reattend(h["q"], cu.numpy(), h["k"], h["v"], L.numpy(), Q,
+                                     sink=None if sink is None else sink.numpy().astype(np.float64),
+                                     scale=scale)
+
+
+REATT_CASES = [
+    # dtype, B, Hq, Hk, Qmax, M, D, Dv (decode-shaped: (Hq/Hk) * Qmax <= 8)
+    ("bf16", 6, 16, 4, 2, 700, 128, 128),
+    ("bf16", 5, 8, 2, 1, 1024, 64, 64),
+    ("f32", 4, 8, 8, 4, 300, 64, 32),
+]
+
+
+@pytest.mark.parametrize("case", REATT_CASES, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("layout", ["rows", "slot_ids", "paged"])
+def test_reattend_against_oracle(case, layout):
+    dtype, B, Hq, Hk, Qmax, M, D, Dv = case
+    for seed in (0, 1):
+        say(f"[case] reattend {case} {layout} seed={seed}")
+        rows = B + 3 if layout == "slot_ids" else B
+        q, cu, kc, vc, L, S = reatt_case(dtype, B, Hq, Hk, Qmax, M, D, Dv, seed, rows=rows,
+                                         std=4.0 if dtype == "f32" else 1.0)
+        sink = torch.from_numpy(np.random.default_rng(seed + 9).standard_normal(Hq) * 3
+                                ).float() if seed == 1 else None
+        scale = 0.25 if dtype == "f32" else None
+        if layout == "rows":
+            out, st = run_reatt(q, cu, kc, vc, L, Qmax, sink=sink, scale=scale)
+            ref, rst = reatt_ref(q, cu, kc, vc, L, Qmax, sink, scale)
+        elif layout == "slot_ids":
+            slots = torch.from_numpy(np.random.default_rng(seed).permutation(rows)[:B]
+                                     .astype(np.int32))
+            out, st = run_reatt(q, cu, kc, vc, L, Qmax, slots=slots, sink=sink, scale=scale)
+            ref, rst = reatt_ref(q, cu, kc[slots.long()], vc[slots.long()], L, Qmax, sink, scale)
+        else:
+            Mp = (M + 63) // 64 * 64
+            kpad = torch.zeros(B, Hk, Mp, D, dtype=kc.dtype)
+            vpad = torch.zeros(B, Hk, Mp, Dv, dtype=vc.dtype)
+            kpad[:, :, :M], vpad[:, :, :M] = kc, vc
+            kp, vp, table = paged_layout(kpad, vpad, 64, seed)
+            out, st = run_reatt(q, cu, kp, vp, L, Qmax, M=Mp, table=table, sink=sink,
+                                scale=scale)
+            ref, rst = reatt_ref(q, cu, kpad, vpad, L, Qmax, sink, scale)
+        assert list(st.numpy()) == list(rst), (st, rst)
+        check_floats(to_f64(out), ref, dtype, f"reattend {layout} {case}/{seed}", "context")
+
+
+def test_reattend_chunk_path_with_sink():
+    """A prefill-sized re-attention (40 queries x 4 heads per KV head) takes
+    the matrix-core chunk kernel, with the sink added in the combine."""
+    q, cu, kc, vc, L, S = reatt_case("bf16", 3, 8, 2, 40, 400, 64, 64, 4)
+    sink = torch.linspace(-2, 2, 8)
+    d = kvc.KvcDims(3, 8, 2, 40, 400, 64, 64)
+    assert kvc.kvc_plan_step(d, kvc.KVC_BF16)["path"] == 2
+    out, st = run_reatt(q, cu, kc, vc, L, 40, sink=sink)
+    ref, rst = reatt_ref(q, cu, kc, vc, L, 40, sink)
+    assert list(st.numpy()) == list(rst)
+    check_floats(to_f64(out), ref, "bf16", "reattend chunk path", "context")
+
+
+def test_reattend_rejected_sequences():
+    """L > M, more queries than cached positions, more than Q queries: zero
+    rows and their codes; the other sequences exact."""
+    q, cu, kc, vc, L, S = reatt_case("bf16", 4, 8, 2, 2, 256, 128, 128, 5)
+    cu = torch.tensor([0, 1, 3, 4, 7], dtype=torch.int64)  # S = 1, 2, 1, 3 (> Q = 2)
+    q = torch.randn(7, 8, 128).to(torch.bfloat16)
+    L = torch.tensor([300, 1, 50, 100], dtype=torch.int64)   # L > M; S > L
+    out, st = run_reatt(q, cu, kc, vc, L, 2)
+    ref, rst = reatt_ref(q, cu, kc, vc, L, 2)
+    assert list(st.numpy()) == [kvc.ROW_BAD_LENGTH, kvc.ROW_BAD_QUERIES, kvc.ROW_OK,
+                                kvc.ROW_BAD_QUERIES] == list(rst)
+    got = to_f64(out)
+    assert not got[[0, 1, 2, 4, 5, 6]].any()
+    check_floats(got, ref, "bf16", "reattend rejected", "context")
