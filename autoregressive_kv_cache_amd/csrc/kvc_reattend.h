@@ -36,6 +36,31 @@ struct ReattArgs {
   const uint8_t* ctx;  // [B][Hq][Q][Dv]
 };
 
+// Copy `rows` rows of `rb` bytes, row i from src(i) to dst(i) (null src:
+// zeros), all rows at once: 16-byte pieces over the whole workgroup when
+// every address and the row size allow it, else 2-byte ones.
+template <typename Src, typename Dst>
+__device__ inline void copy_rows(int64_t rows, int64_t rb, Src src, Dst dst, bool aligned16) {
+  const int tid = threadIdx.x;
+  if (aligned16 && rb % 16 == 0) {
+    const int64_t parts = rb / 16;
+    for (int64_t i = tid; i < rows * parts; i += kReattThreads) {
+      const int64_t row = i / parts, part = i % parts;
+      const uint8_t* sp = src(row);
+      const uint4 v = sp ? reinterpret_cast<const uint4*>(sp)[part] : make_uint4(0, 0, 0, 0);
+      reinterpret_cast<uint4*>(dst(row))[part] = v;
+    }
+  } else {
+    const int64_t parts = rb / 2;
+    for (int64_t i = tid; i < rows * parts; i += kReattThreads) {
+      const int64_t row = i / parts, part = i % parts;
+      const uint8_t* sp = src(row);
+      const uint16_t v = sp ? reinterpret_cast<const uint16_t*>(sp)[part] : uint16_t(0);
+      reinterpret_cast<uint16_t*>(dst(row))[part] = v;
+    }
+  }
+}
+
 // Row checks of sequence b: a cached length outside [0, M] (bad length), or
 // a query range that is not inside [0, Tq], holds more than Q tokens or more
 // tokens than are cached (bad queries).
@@ -62,28 +87,22 @@ __global__ __launch_bounds__(kReattThreads) void reattend_prep_kernel(StepArgs a
   }
   for (int64_t t = tid; t < a.Q; t += kReattThreads) r.mask[b * a.Q + t] = t < S ? 1 : 0;
   const int64_t e = a.elem_bytes, qb = a.D * e, kb = a.D * e, vb = a.Dv * e;
-  for (int64_t i = 0; i < S * a.Hq; i++) {
-    const int64_t t = i / a.Hq, hq = i % a.Hq;
-    copy_bytes(r.qs + ((b * a.Hq + hq) * a.Q + t) * qb, r.q + ((c0 + t) * a.Hq + hq) * qb, qb,
-               tid, kReattThreads);
-  }
-  for (int64_t i = 0; i < S * a.Hk; i++) {
-    const int64_t t = i / a.Hk, h = i % a.Hk, j = L - S + t;
-    uint8_t* kd = r.nk + ((b * a.Hk + h) * a.Q + t) * kb;
-    uint8_t* vd = r.nv + ((b * a.Hk + h) * a.Q + t) * vb;
-    const uint8_t* ks = slot_row(a, a.kc_in, b, h, j, kb);
-    const uint8_t* vs = slot_row(a, a.vc_in, b, h, j, vb);
-    if (ks) {
-      copy_bytes(kd, ks, kb, tid, kReattThreads);
-    } else {
-      for (int64_t x = tid; x < kb; x += kReattThreads) kd[x] = 0;
-    }
-    if (vs) {
-      copy_bytes(vd, vs, vb, tid, kReattThreads);
-    } else {
-      for (int64_t x = tid; x < vb; x += kReattThreads) vd[x] = 0;
-    }
-  }
+  const bool al = ((reinterpret_cast<uintptr_t>(r.q) | reinterpret_cast<uintptr_t>(a.kc_in) |
+                    reinterpret_cast<uintptr_t>(a.vc_in) | reinterpret_cast<uintptr_t>(r.qs) |
+                    reinterpret_cast<uintptr_t>(r.nk) | reinterpret_cast<uintptr_t>(r.nv)) & 15u) == 0;
+  // query row (t, hq) -> step query (b, hq, t)
+  copy_rows(
+      S * a.Hq, qb, [&](int64_t i) { return r.q + ((c0 + i / a.Hq) * a.Hq + i % a.Hq) * qb; },
+      [&](int64_t i) { return r.qs + ((b * a.Hq + i % a.Hq) * a.Q + i / a.Hq) * qb; }, al);
+  // cache row L - S + t of head h -> the step's appended row (b, h, t)
+  copy_rows(
+      S * a.Hk, kb,
+      [&](int64_t i) { return slot_row(a, a.kc_in, b, i % a.Hk, L - S + i / a.Hk, kb); },
+      [&](int64_t i) { return r.nk + ((b * a.Hk + i % a.Hk) * a.Q + i / a.Hk) * kb; }, al);
+  copy_rows(
+      S * a.Hk, vb,
+      [&](int64_t i) { return slot_row(a, a.vc_in, b, i % a.Hk, L - S + i / a.Hk, vb); },
+      [&](int64_t i) { return r.nv + ((b * a.Hk + i % a.Hk) * a.Q + i / a.Hk) * vb; }, al);
 }
 
 // One workgroup per sequence: its context rows to the packed output (zeros
@@ -97,15 +116,15 @@ __global__ __launch_bounds__(kReattThreads) void reattend_scatter_kernel(StepArg
   const int64_t c0 = r.cu_q[b], c1 = r.cu_q[b + 1], S = c1 - c0;
   if (c0 < 0 || c1 > r.Tq || S <= 0) return;
   const int64_t vb = a.Dv * a.elem_bytes;
-  for (int64_t i = 0; i < S * a.Hq; i++) {
-    const int64_t t = i / a.Hq, hq = i % a.Hq;
-    uint8_t* dst = r.out + ((c0 + t) * a.Hq + hq) * vb;
-    if (st == kRowOk) {
-      copy_bytes(dst, r.ctx + ((b * a.Hq + hq) * a.Q + t) * vb, vb, tid, kReattThreads);
-    } else {
-      for (int64_t x = tid; x < vb; x += kReattThreads) dst[x] = 0;
-    }
-  }
+  const bool al = ((reinterpret_cast<uintptr_t>(r.out) | reinterpret_cast<uintptr_t>(r.ctx)) &
+                   15u) == 0;
+  const bool ok = st == kRowOk;
+  copy_rows(
+      S * a.Hq, vb,
+      [&](int64_t i) -> const uint8_t* {
+        return ok ? r.ctx + ((b * a.Hq + i % a.Hq) * a.Q + i / a.Hq) * vb : nullptr;
+      },
+      [&](int64_t i) { return r.out + ((c0 + i / a.Hq) * a.Hq + i % a.Hq) * vb; }, al);
 }
 
 }  // namespace kvc

@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 METRIC = "decode steps/s + achieved HBM GB/s (% of MI355X peak), GQA Hq32/Hk8 D128 M8192"
 PEAK_HBM_GBPS = 8000.0
 DOMINANT_KERNEL = "attend"
-ENTRY = {"inplace": "kvc_step_inplace", "oop": "kvc_step_out_of_place", "paged": "kvc_step_paged"}
+ENTRY = {"inplace": "kvc_step_inplace", "oop": "kvc_step_out_of_place", "paged": "kvc_step_paged",
+         "reattend": "kvc_attend_over_cache"}
 
 
 def parse():
@@ -42,7 +43,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode_gqa_bf16")
-    p.add_argument("--mode", choices=["inplace", "oop", "paged"], default="inplace")
+    p.add_argument("--mode", choices=["inplace", "oop", "paged", "reattend"], default="inplace")
     p.add_argument("--block-size", type=int, default=64,
                    help="paged mode: slots per cache block (the pools are block-permuted)")
     p.add_argument("--seed", type=int, default=0)
@@ -111,6 +112,20 @@ def algorithmic_bytes(wl, lengths, n):
     step = kv + q + att + ctx + small_in + small_out
     attend = kv_read + q + att_visible + small_in
     return step, attend, kv
+
+
+def reattend_bytes(wl, lengths, n):
+    """Read-only re-attention of the last n_b of length_b + n_b cached
+    positions: read the visible K/V prefix and q, write the packed output,
+    plus the small per-sequence inputs.  Returns (whole call, attention
+    kernel share: the K/V rows and q)."""
+    e = 2 if wl.dtype == "bf16" else 4
+    kv = sum(wl.Hk * (int(L) + int(k)) * (wl.D + wl.Dv) * e for L, k in zip(lengths, n))
+    tq = int(sum(int(k) for k in n))
+    q = tq * wl.Hq * wl.D * e
+    out = tq * wl.Hq * wl.Dv * e
+    small = wl.B * (8 + 8 + 4)
+    return kv + q + out + small, kv + q
 
 
 def oop_extra_bytes(wl, lengths, n):
@@ -196,6 +211,7 @@ def main():
               "(sharding across GPUs is a design note, not an implementation)", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     from autoregressive_kv_cache_amd import kvc
     from autoregressive_kv_cache_amd.workloads import (WORKLOADS, draw_lengths_and_counts,
@@ -221,6 +237,15 @@ def main():
         if args.mode == "oop":
             d["kc_out"] = torch.empty_like(inp["key_cache"])
             d["vc_out"] = torch.empty_like(inp["value_cache"])
+        if args.mode == "reattend":
+            # the cache already holds length + n rows; re-attend the last n
+            cnt = torch.from_numpy(np.asarray(n, dtype=np.int64))
+            d["cu"] = torch.cat([torch.zeros(1, dtype=torch.int64), cnt.cumsum(0)]).to(dev)
+            d["lk"] = (inp["lengths"].cpu() + cnt).to(dev)
+            rows = [inp["query"][b, :, :int(n[b])].transpose(0, 1) for b in range(wl.B)]
+            d["qp"] = torch.cat(rows).contiguous()
+            d["out"] = torch.empty(d["qp"].shape[0], wl.Hq, wl.Dv, dtype=inp["key_cache"].dtype,
+                                   device=dev)
         if args.mode == "paged":
             d["kp"], d["vp"], d["table"] = paged_layout(inp["key_cache"], inp["value_cache"],
                                                         args.block_size, args.seed + k)
@@ -233,7 +258,10 @@ def main():
     dims = kvc.dims_of(q0, kc0, vc0)
     dt = kvc.dtype_code(kc0.dtype)
     plan = kvc.kvc_plan_step(dims, dt)
-    ws = kvc.workspace_for(dims, dt, dev)
+    if args.mode == "reattend":
+        ws = torch.empty(kvc.kvc_attend_workspace_bytes(dims, dt), dtype=torch.uint8, device=dev)
+    else:
+        ws = kvc.workspace_for(dims, dt, dev)
 
     ev = HipEvents()
     starts = [ev.create() for _ in range(args.steps)]
@@ -242,7 +270,11 @@ def main():
     def step(i=None, k=0):
         d = sets[k % len(sets)]
         events = None if i is None or i % args.event_every else (starts[i], stops[i])
-        if args.mode == "paged":
+        if args.mode == "reattend":
+            kvc.kvc_attend_over_cache(d["qp"], d["cu"], d["key_cache"], d["value_cache"], d["lk"],
+                                      d["out"], wl.Q, row_status=d["status"], workspace=ws,
+                                      scale=wl.scale, events=events)
+        elif args.mode == "paged":
             kvc.kvc_step_paged(d["query"], d["new_key"], d["new_value"], d["kp"], d["vp"],
                                d["table"], d["lengths"], d["mask"], d["lens_out"], d["att"],
                                d["ctx"], d["status"], workspace=ws, scale=wl.scale, events=events)
@@ -276,6 +308,8 @@ def main():
         extra_step, extra_attend = oop_extra_bytes(wl, lengths, n)
         step_bytes += extra_step
         attend_bytes += extra_attend
+    if args.mode == "reattend":
+        step_bytes, attend_bytes = reattend_bytes(wl, lengths, n)
     ms_per_step = elapsed / args.steps * 1e3
     steps_per_s = args.steps / elapsed
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
