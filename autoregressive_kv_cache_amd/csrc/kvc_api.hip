@@ -391,8 +391,9 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
     if (!mul_ok(pg->num_blocks, d->Hk, kMaxElems, &x) || !mul_ok(x, bs, kMaxElems, &x) ||
         !mul_ok(x, d->D > d->Dv ? d->D : d->Dv, kMaxElems, &x))
       return KVC_ERR_SHAPE;
-    // the stream decode path only, with every chunk inside one block
-    if (!p.decode || (!single && bs < p.decode->chunk)) return KVC_ERR_UNSUPPORTED;
+    // the stream decode or matrix-core chunk path, every chunk inside one block
+    const int64_t chunk = p.decode ? p.decode->chunk : (p.chunk ? kvc::kChunkSlots : 0);
+    if (!chunk || (!single && bs < chunk)) return KVC_ERR_UNSUPPORTED;
   }
 
   if (!kc_in || !vc_in || !kc_out || !vc_out || !lengths || !lengths_out) return KVC_ERR_NULL;
@@ -463,7 +464,7 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
                        aligned16(vc_out);
   const bool vec_ok = p.decode && aligned;
   if (pg) {
-    if (!vec_ok) return KVC_ERR_UNSUPPORTED;
+    if (!aligned) return KVC_ERR_UNSUPPORTED;
     set_paged(a, d, *pg);
   }
   a.read_only = read_only ? 1 : 0;
@@ -594,8 +595,8 @@ int kvc_attend_over_cache(const kvc_dims* dims, int dtype, int has_scale, double
     const int64_t bs = pg.block_size;
     const bool single = bs == d->M;
     if (!single && ((bs & (bs - 1)) != 0 || d->M % bs != 0)) return KVC_ERR_SHAPE;
-    if (!p.decode || (!single && bs < p.decode->chunk) || !aligned16(key_cache) ||
-        !aligned16(value_cache))
+    const int64_t chunk = p.decode ? p.decode->chunk : (p.chunk ? kvc::kChunkSlots : 0);
+    if (!chunk || (!single && bs < chunk) || !aligned16(key_cache) || !aligned16(value_cache))
       return KVC_ERR_UNSUPPORTED;
   }
   const size_t e = dtype == KVC_F32 ? 4 : 2;

@@ -99,21 +99,34 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_kernel(StepArgs a)
   const int64_t s1 = s0 + C < a.M ? s0 + C : a.M;
 
   const int64_t head = b * a.Hk + kvh;
+  // slot j of the head at k_head + j * D: the dense cache, or (paged) the
+  // chunk's block, which holds all of its slots; null = outside the pool
   const uint16_t* k_head = static_cast<const uint16_t*>(a.kc_in) + head * a.M * D;
   const uint16_t* v_head = static_cast<const uint16_t*>(a.vc_in) + head * a.M * DV;
+  if (a.paged) {
+    const auto* kp = reinterpret_cast<const uint16_t*>(slot_row(a, a.kc_in, b, kvh, s0, D * 2));
+    const auto* vp = reinterpret_cast<const uint16_t*>(slot_row(a, a.vc_in, b, kvh, s0, DV * 2));
+    k_head = kp ? kp - s0 * D : nullptr;
+    v_head = vp ? vp - s0 * DV : nullptr;
+  }
   const uint16_t* nk_head = static_cast<const uint16_t*>(a.new_key) + head * a.Q * D;
   const uint16_t* nv_head = static_cast<const uint16_t*>(a.new_value) + head * a.Q * DV;
 
   // 1. cache writes of the slot range [s0, s1)
   if (rg == 0 && !a.read_only) {  // the chunk's cache writes, once
-    write_cache_slots(static_cast<uint8_t*>(a.kc_out) + head * a.M * D * 2,
-                      reinterpret_cast<const uint8_t*>(k_head),
-                      reinterpret_cast<const uint8_t*>(nk_head), D * 2, s0, s1, len, n,
-                      a.out_of_place != 0, tid, kChunkThreads);
-    write_cache_slots(static_cast<uint8_t*>(a.vc_out) + head * a.M * DV * 2,
-                      reinterpret_cast<const uint8_t*>(v_head),
-                      reinterpret_cast<const uint8_t*>(nv_head), DV * 2, s0, s1, len, n,
-                      a.out_of_place != 0, tid, kChunkThreads);
+    // (paged: in place, into the chunk's block, which is the one read)
+    uint8_t* kd = a.paged ? const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(k_head))
+                          : static_cast<uint8_t*>(a.kc_out) + head * a.M * D * 2;
+    uint8_t* vd = a.paged ? const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(v_head))
+                          : static_cast<uint8_t*>(a.vc_out) + head * a.M * DV * 2;
+    if (kd)
+      write_cache_slots(kd, reinterpret_cast<const uint8_t*>(k_head),
+                        reinterpret_cast<const uint8_t*>(nk_head), D * 2, s0, s1, len, n,
+                        a.out_of_place != 0, tid, kChunkThreads);
+    if (vd)
+      write_cache_slots(vd, reinterpret_cast<const uint8_t*>(v_head),
+                        reinterpret_cast<const uint8_t*>(nv_head), DV * 2, s0, s1, len, n,
+                        a.out_of_place != 0, tid, kChunkThreads);
   }
   if (a.R == 0 || c >= row_chunks(len, n, C)) return;
   const int nact = static_cast<int>((s1 < new_len ? s1 : new_len) - s0);  // visited slots
@@ -123,14 +136,15 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_kernel(StepArgs a)
     const int slot = idx / (D / 8), part = idx % (D / 8);
     const int64_t j = s0 + slot;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (slot < nact) v = ld_global16((j < len ? k_head + j * D : nk_head + (j - len) * D) + part * 8);
+    if (slot < nact && (j >= len || k_head))
+      v = ld_global16((j < len ? k_head + j * D : nk_head + (j - len) * D) + part * 8);
     *reinterpret_cast<uint4*>(k_s + slot * KP + part * 8) = v;
   }
   for (int idx = tid; idx < C * (DV / 8); idx += kChunkThreads) {
     const int slot = idx % C, part = idx / C;
     const int64_t j = s0 + slot;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (slot < nact)
+    if (slot < nact && (j >= len || v_head))
       v = ld_global16((j < len ? v_head + j * DV : nv_head + (j - len) * DV) + part * 8);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -318,21 +332,34 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_f32_kernel(StepArg
   const int64_t s1 = s0 + C < a.M ? s0 + C : a.M;
 
   const int64_t head = b * a.Hk + kvh;
+  // slot j of the head at k_head + j * D: the dense cache, or (paged) the
+  // chunk's block, which holds all of its slots; null = outside the pool
   const float* k_head = static_cast<const float*>(a.kc_in) + head * a.M * D;
   const float* v_head = static_cast<const float*>(a.vc_in) + head * a.M * DV;
+  if (a.paged) {
+    const auto* kp = reinterpret_cast<const float*>(slot_row(a, a.kc_in, b, kvh, s0, D * 4));
+    const auto* vp = reinterpret_cast<const float*>(slot_row(a, a.vc_in, b, kvh, s0, DV * 4));
+    k_head = kp ? kp - s0 * D : nullptr;
+    v_head = vp ? vp - s0 * DV : nullptr;
+  }
   const float* nk_head = static_cast<const float*>(a.new_key) + head * a.Q * D;
   const float* nv_head = static_cast<const float*>(a.new_value) + head * a.Q * DV;
 
   // 1. cache writes of the slot range [s0, s1)
   if (rg == 0 && !a.read_only) {  // the chunk's cache writes, once
-    write_cache_slots(static_cast<uint8_t*>(a.kc_out) + head * a.M * D * 4,
-                      reinterpret_cast<const uint8_t*>(k_head),
-                      reinterpret_cast<const uint8_t*>(nk_head), D * 4, s0, s1, len, n,
-                      a.out_of_place != 0, tid, kChunkThreads);
-    write_cache_slots(static_cast<uint8_t*>(a.vc_out) + head * a.M * DV * 4,
-                      reinterpret_cast<const uint8_t*>(v_head),
-                      reinterpret_cast<const uint8_t*>(nv_head), DV * 4, s0, s1, len, n,
-                      a.out_of_place != 0, tid, kChunkThreads);
+    // (paged: in place, into the chunk's block, which is the one read)
+    uint8_t* kd = a.paged ? const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(k_head))
+                          : static_cast<uint8_t*>(a.kc_out) + head * a.M * D * 4;
+    uint8_t* vd = a.paged ? const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(v_head))
+                          : static_cast<uint8_t*>(a.vc_out) + head * a.M * DV * 4;
+    if (kd)
+      write_cache_slots(kd, reinterpret_cast<const uint8_t*>(k_head),
+                        reinterpret_cast<const uint8_t*>(nk_head), D * 4, s0, s1, len, n,
+                        a.out_of_place != 0, tid, kChunkThreads);
+    if (vd)
+      write_cache_slots(vd, reinterpret_cast<const uint8_t*>(v_head),
+                        reinterpret_cast<const uint8_t*>(nv_head), DV * 4, s0, s1, len, n,
+                        a.out_of_place != 0, tid, kChunkThreads);
   }
   if (a.R == 0 || c >= row_chunks(len, n, C)) return;
   const int nact = static_cast<int>((s1 < new_len ? s1 : new_len) - s0);
@@ -343,7 +370,7 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_f32_kernel(StepArg
     const int slot = idx / (D / 4), d = (idx % (D / 4)) * 4;
     const int64_t j = s0 + slot;
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (slot < nact)
+    if (slot < nact && (j >= len || k_head))
       x = *reinterpret_cast<const float4*>(j < len ? k_head + j * D + d : nk_head + (j - len) * D + d);
     float* dst = k_s + slot * KP + d;
     dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
@@ -352,7 +379,7 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_f32_kernel(StepArg
     const int slot = idx / (DV / 4), d = (idx % (DV / 4)) * 4;
     const int64_t j = s0 + slot;
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (slot < nact)
+    if (slot < nact && (j >= len || v_head))
       x = *reinterpret_cast<const float4*>(j < len ? v_head + j * DV + d
                                                    : nv_head + (j - len) * DV + d);
     float* dst = v_s + slot * VP + d;

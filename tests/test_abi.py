@@ -188,7 +188,8 @@ def test_host_checks_paged(lib):
     assert run(d, block_size=2048)[0] == -2     # does not divide M
     assert run(d, block_size=32)[0] == -8       # smaller than a decode chunk
     assert run(d, num_blocks=0)[0] == -2
-    assert run(dims(B=4, Hq=8, Hk=2, Q=4, M=1024, D=128, Dv=128))[0] == -8  # 16 rows: chunk path
+    assert run(dims(B=4, Hq=8, Hk=2, Q=4, M=1024, D=128, Dv=128),
+               block_size=32)[0] == -8                  # chunk path, blocks below 64 slots
     assert run(dims(B=4, Hq=8, Hk=2, Q=1, M=1024, D=96, Dv=96))[0] == -8   # no decode kernel
     _, ptrs = run(d, ws=16)
     assert run(d, ws=16)[0] == -5
@@ -234,7 +235,7 @@ def test_host_checks_attend_over_cache(lib):
     assert run(d, Tq=-1)[0] == -2
     assert run(d, table=True, block_size=48)[0] == -2
     assert run(d, table=True, block_size=32)[0] == -8               # smaller than a chunk
-    assert run(dims(B=4, Hq=8, Hk=2, Q=4, M=1024, D=128, Dv=128), slots=True)[0] == -8
+    assert run(dims(B=4, Hq=8, Hk=2, Q=4, M=1024, D=96, Dv=96), slots=True)[0] == -8  # generic
     assert run(d, ws=16)[0] == -5
     _, ptrs = run(d, ws=16)
     bad = list(ptrs)

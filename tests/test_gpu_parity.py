@@ -393,6 +393,12 @@ PAGED_CASES = [
     (WORKLOADS["mha_stress_f32"].with_(name="paged_f32", B=4, M=512, len_range=(0, 508)), 128),
     (chunk_wl(name="paged_d64", B=3, Hq=8, Hk=2, Q=1, M=640, len_range=(0, 639), n_rule="all"),
      128),
+    # more than 8 packed rows: the matrix-core chunk kernels over the pool
+    (chunk_wl(name="paged_chunk_bf16", B=2, Hq=8, Hk=2, Q=40, M=512, len_range=(0, 470)), 64),
+    (chunk_wl(name="paged_chunk_d128", B=3, Hq=4, Hk=1, Q=5, M=512, D=128, Dv=128,
+              len_range=(0, 500)), 128),
+    (chunk_wl(name="paged_chunk_f32", dtype="f32", B=2, Hq=8, Hk=2, Q=20, M=256,
+              len_range=(0, 230), std=8.0, scale=4.0), 64),
 ]
 
 
