@@ -265,3 +265,78 @@ def default() -> Oracle:
     if _DEFAULT is None:
         _DEFAULT = Oracle(LIBRARY)
     return _DEFAULT
+
+
+@dataclass
+class StepGrads:
+    query: np.ndarray        # [B, Hq, Q, D]
+    new_key: np.ndarray      # [B, Hk, Q, D]
+    new_value: np.ndarray    # [B, Hk, Q, Dv]
+    key_cache: np.ndarray    # [B, Hk, M, D]
+    value_cache: np.ndarray  # [B, Hk, M, Dv]
+
+
+def step_backward(query, new_key, new_value, key_cache, value_cache, lengths, append_mask,
+                  d_attention=None, d_context=None, d_key_cache_out=None,
+                  d_value_cache_out=None, scale=None) -> StepGrads:
+    """Gradients of the step (all in float64, from the definition) given the
+    gradients of its outputs: attention, context and the two returned caches
+    (each may be None = zero).  The step: the updated caches K', V' are the
+    inputs with slots length + t (t < n) replaced by the new rows; valid
+    query t (t < n) has scores s_j = scale q.K'_j on j <= length + t,
+    P = softmax(s), attention = P, context = P V'.  Backward, per valid row:
+    dP_j = dA_j + dO . V'_j, dS_j = P_j (dP_j - sum_k P_k dP_k),
+    dq = scale sum_j dS_j K'_j, dK'_j += scale dS_j q, dV'_j += P_j dO;
+    then dK' splits into the cache slots that were kept and the new rows
+    that were written (an overwritten cache slot gets no gradient).  Rows
+    outside the contract are no-ops: only the returned caches pass their
+    gradients through."""
+    f = lambda a: None if a is None else np.asarray(a, dtype=np.float64)
+    q, nk, nv, kc, vc = (np.asarray(a, dtype=np.float64)
+                         for a in (query, new_key, new_value, key_cache, value_cache))
+    B, Hq, Q, D = q.shape
+    Hk, M, Dv = kc.shape[1], kc.shape[2], vc.shape[3]
+    G = Hq // Hk
+    sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    dA, dO = f(d_attention), f(d_context)
+    dKo, dVo = f(d_key_cache_out), f(d_value_cache_out)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    mask = np.asarray(append_mask).astype(bool)
+    gq = np.zeros_like(q)
+    gnk, gnv = np.zeros_like(nk), np.zeros_like(nv)
+    dKp = np.zeros_like(kc) if dKo is None else dKo.copy()  # gradient of K' (updated cache)
+    dVp = np.zeros_like(vc) if dVo is None else dVo.copy()
+    for b in range(B):
+        L = int(lengths[b])
+        n = 0
+        while n < Q and mask[b, n]:
+            n += 1
+        ok = 0 <= L <= M and not mask[b, n:].any() and L + n <= M
+        if not ok:
+            continue  # the step leaves this row alone
+        Kp, Vp = kc[b].copy(), vc[b].copy()
+        Kp[:, L:L + n] = nk[b, :, :n]
+        Vp[:, L:L + n] = nv[b, :, :n]
+        for h in range(Hq):
+            kh = h // G
+            for t in range(n):
+                vis = L + t + 1
+                s = sc * (Kp[kh, :vis] @ q[b, h, t])
+                p = np.exp(s - s.max())
+                p /= p.sum()
+                dP = np.zeros(vis)
+                if dA is not None:
+                    dP += dA[b, h, t, :vis]
+                if dO is not None:
+                    dP += Vp[kh, :vis] @ dO[b, h, t]
+                dS = p * (dP - p @ dP)
+                gq[b, h, t] = sc * (dS @ Kp[kh, :vis])
+                dKp[b, kh, :vis] += sc * np.outer(dS, q[b, h, t])
+                if dO is not None:
+                    dVp[b, kh, :vis] += np.outer(p, dO[b, h, t])
+        # K' = cache with slots L .. L+n-1 replaced
+        gnk[b, :, :n] = dKp[b, :, L:L + n]
+        gnv[b, :, :n] = dVp[b, :, L:L + n]
+        dKp[b, :, L:L + n] = 0.0
+        dVp[b, :, L:L + n] = 0.0
+    return StepGrads(gq, gnk, gnv, dKp, dVp)
