@@ -5,7 +5,8 @@ marshalling only -- every step of the computation runs in the HIP kernels of
 Low level (same names as the C entry points, tensors instead of pointers):
 ``kvc_workspace_bytes``, ``kvc_plan_step``, ``kvc_step_out_of_place``,
 ``kvc_step_inplace``, ``kvc_step_paged``, ``kvc_attend_workspace_bytes``,
-``kvc_attend_over_cache``, ``kvc_status_string``.
+``kvc_attend_over_cache``, ``kvc_backward_workspace_bytes``, ``kvc_step_backward``,
+``kvc_status_string``.
 
 Page-style face ("Autoregressive KV-cache append and causal attention",
 Function signature / Starter code): ``kv_cache_attention_step`` returns a
@@ -32,7 +33,8 @@ ERRORS = {-1: "KVC_ERR_NULL", -2: "KVC_ERR_SHAPE", -3: "KVC_ERR_DTYPE", -4: "KVC
 ROW_OK, ROW_BAD_LENGTH, ROW_OVERFLOW, ROW_NOT_PREFIX, ROW_BAD_QUERIES = 0, 1, 2, 3, 4
 EXPORTED = ("kvc_workspace_bytes", "kvc_plan_step", "kvc_step_out_of_place",
             "kvc_step_inplace", "kvc_step_paged", "kvc_attend_workspace_bytes",
-            "kvc_attend_over_cache", "kvc_status_string")
+            "kvc_attend_over_cache", "kvc_backward_workspace_bytes", "kvc_step_backward",
+            "kvc_status_string")
 
 
 class KvcDims(ctypes.Structure):
@@ -91,6 +93,11 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kvc_attend_over_cache.argtypes = ([ctypes.POINTER(KvcDims), _int, _int, _dbl, _vp, _i64,
                                            _vp, _vp, _vp, _i64, _i64] + [_vp] * 7
                                           + [_sz, _vp, ctypes.POINTER(KvcEvents)])
+    lib.kvc_backward_workspace_bytes.restype = _sz
+    lib.kvc_backward_workspace_bytes.argtypes = [ctypes.POINTER(KvcDims), _int]
+    lib.kvc_step_backward.restype = _int
+    lib.kvc_step_backward.argtypes = ([ctypes.POINTER(KvcDims), _int, _int, _dbl] + [_vp] * 17
+                                      + [_sz, _vp])
     lib.kvc_status_string.restype = ctypes.c_char_p
     lib.kvc_status_string.argtypes = [_int]
     _LIB = lib
@@ -251,6 +258,29 @@ def kvc_attend_over_cache(q, cu_seqlens_q, key_cache, value_cache, seqlens_k, ou
         workspace.numel(), _stream(stream, key_cache.device), _events(events))
     if rc != KVC_OK:
         raise KvcError(rc, "kvc_attend_over_cache")
+
+
+def kvc_step_backward(query, new_key, new_value, key_cache, value_cache, lengths, append_mask,
+                      d_attention, d_context, d_key_cache_out, d_value_cache_out, g_query,
+                      g_new_key, g_new_value, g_key_cache, g_value_cache, workspace=None,
+                      scale=None, stream=None) -> None:
+    """Enqueue the backward of the step (fp32) on ``stream``; the ``d_*``
+    gradients of the outputs may be None."""
+    lib = load()
+    dims = dims_of(query, key_cache, value_cache)
+    if workspace is None:
+        workspace = torch.empty(max(1, int(lib.kvc_backward_workspace_bytes(
+            ctypes.byref(dims), KVC_F32))), dtype=torch.uint8, device=key_cache.device)
+    hs, sc = _scale_args(scale)
+    rc = lib.kvc_step_backward(
+        ctypes.byref(dims), dtype_code(key_cache.dtype), hs, sc, _ptr(query), _ptr(new_key),
+        _ptr(new_value), _ptr(key_cache), _ptr(value_cache), _ptr(lengths), _ptr(append_mask),
+        _ptr(d_attention), _ptr(d_context),
+        _ptr(d_key_cache_out), _ptr(d_value_cache_out), _ptr(g_query), _ptr(g_new_key),
+        _ptr(g_new_value), _ptr(g_key_cache), _ptr(g_value_cache), _ptr(workspace),
+        workspace.numel(), _stream(stream, key_cache.device))
+    if rc != KVC_OK:
+        raise KvcError(rc, "kvc_step_backward")
 
 
 # ---------------------------------------------------------------------------

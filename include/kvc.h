@@ -239,6 +239,44 @@ int kvc_attend_over_cache(const kvc_dims *dims, int dtype, int has_scale,
                           size_t workspace_bytes, void *stream,
                           const kvc_events *events);
 
+/* Backward of the step (fp32 inputs; head sizes (D, Dv) in {(64, 64),
+ * (128, 128), (64, 32)}, else KVC_ERR_UNSUPPORTED): the gradients of the
+ * step's inputs given those of its outputs.  The page grades gradients as
+ * well as values ("Autoregressive KV-cache append and causal attention",
+ * the workspace note).
+ *
+ * Inputs: the step's own inputs (query, new_key, new_value, lengths,
+ * append_mask as given to the step; key_cache / value_cache either the
+ * caches before the step or after an in-place step -- only slots below
+ * lengths[b] are read from them) and the gradients of its outputs
+ * d_attention [B,Hq,Q,M], d_context [B,Hq,Q,Dv], d_key_cache_out
+ * [B,Hk,M,D], d_value_cache_out [B,Hk,M,Dv] (each may be NULL = zero).
+ * The attention is recomputed from the scores with fp64 row statistics,
+ * so the forward's outputs are not needed.
+ * Outputs (all written): g_query [B,Hq,Q,D], g_new_key [B,Hk,Q,D],
+ * g_new_value [B,Hk,Q,Dv], g_key_cache [B,Hk,M,D], g_value_cache
+ * [B,Hk,M,Dv].  With K', V' the updated caches and P the attention of a
+ * valid row (t < n_b): dP_j = dA_j + dO.V'_j on j <= lengths[b] + t,
+ * dS_j = P_j (dP_j - sum_k P_k dP_k), g_query = scale sum_j dS_j K'_j,
+ * dK'_j gains scale dS_j q and dV'_j gains P_j dO; dK' plus the returned
+ * cache's gradient goes to g_key_cache at kept slots and to g_new_key at
+ * the appended slots (whose old cache entries get 0).  Tokens t >= n_b and
+ * rows outside the contract get zero query and new-row gradients; their
+ * cache passes its gradient through.
+ * workspace: kvc_backward_workspace_bytes(dims, dtype) bytes.  No output
+ * may overlap an input or another output (KVC_ERR_ALIAS). */
+size_t kvc_backward_workspace_bytes(const kvc_dims *dims, int dtype);
+int kvc_step_backward(const kvc_dims *dims, int dtype, int has_scale,
+                      double scale, const void *query, const void *new_key,
+                      const void *new_value, const void *key_cache,
+                      const void *value_cache, const int64_t *lengths,
+                      const uint8_t *append_mask, const void *d_attention,
+                      const void *d_context, const void *d_key_cache_out,
+                      const void *d_value_cache_out, void *g_query,
+                      void *g_new_key, void *g_new_value, void *g_key_cache,
+                      void *g_value_cache, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
 /* Static description of a return or row-status code. */
 const char *kvc_status_string(int code);
 

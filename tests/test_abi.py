@@ -245,3 +245,15 @@ def test_host_checks_attend_over_cache(lib):
         bad = list(ptrs)
         bad[out_i] = bad[in_i]
         assert run(d, ptrs=bad)[0] == -6, (out_i, in_i)
+
+
+def test_binding_argument_counts_match_the_header(lib):
+    """Every ctypes declaration of the binding has as many arguments as the
+    C prototype in include/kvc.h (a short list would let ctypes pass the
+    trailing ones, such as the stream handle, with the wrong width)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    protos = dict(re.findall(r"\b(kvc_[a-z_]+)\s*\(([^;{]*?)\)\s*;", text))
+    assert set(protos) == set(kvc.EXPORTED)
+    for name, params in protos.items():
+        count = 0 if params.strip() in ("", "void") else params.count(",") + 1
+        assert len(getattr(lib, name).argtypes) == count, (name, count)

@@ -669,3 +669,56 @@ def test_reattend_rejected_sequences():
     got = to_f64(out)
     assert not got[[0, 1, 2, 4, 5, 6]].any()
     check_floats(got, ref, "bf16", "reattend rejected", "context")
+
+
+# -- backward of the step (kvc_step_backward, fp32) ---------------------------
+BWD_TOL = 1e-4  # |d| <= 1e-4 (1 + |ref|): fp32 sums of <= M terms against the double oracle
+
+BWD_CASES = [
+    WORKLOADS["decode_gqa_bf16"].with_(name="bwd_decode", dtype="f32", B=3, M=300,
+                                       len_range=(0, 299), tail_sentinel=None),
+    chunk_wl(name="bwd_chunk", dtype="f32", B=3, Hq=8, Hk=2, Q=5, M=200, len_range=(0, 190)),
+    WORKLOADS["mha_stress_f32"].with_(name="bwd_stress", B=3, M=160, len_range=(0, 150)),
+]
+
+
+@pytest.mark.parametrize("wl", BWD_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("upstream", ["all", "context_only"])
+def test_backward_against_oracle(wl, upstream):
+    for seed in (0, 1):
+        say(f"[case] backward {wl.name} {upstream} seed={seed}")
+        inp = make_inputs(wl, seed, "cpu")
+        if seed == 1:  # a rejected row and a row that appends nothing
+            inp["lengths"][0] = wl.M + 5
+            inp["append_mask"][1] = False
+        dinp = {k: v.to(DEV) for k, v in inp.items()}
+        g = torch.Generator().manual_seed(100 + seed)
+        B, Hq, Q, D = inp["query"].shape
+        Hk, M, Dv = inp["key_cache"].shape[1], inp["key_cache"].shape[2], inp["value_cache"].shape[3]
+        ups = {"d_attention": torch.randn(B, Hq, Q, M, generator=g),
+               "d_context": torch.randn(B, Hq, Q, Dv, generator=g),
+               "d_key_cache_out": torch.randn(B, Hk, M, D, generator=g),
+               "d_value_cache_out": torch.randn(B, Hk, M, Dv, generator=g)}
+        if upstream == "context_only":
+            ups = {k: (v if k == "d_context" else None) for k, v in ups.items()}
+        outs = {k: torch.full_like(dinp[src], float("nan")) for k, src in
+                (("g_query", "query"), ("g_new_key", "new_key"), ("g_new_value", "new_value"),
+                 ("g_key_cache", "key_cache"), ("g_value_cache", "value_cache"))}
+        mask = dinp["append_mask"].contiguous().view(torch.uint8)
+        kvc.kvc_step_backward(dinp["query"], dinp["new_key"], dinp["new_value"],
+                              dinp["key_cache"], dinp["value_cache"], dinp["lengths"], mask,
+                              *[None if v is None else v.to(DEV) for v in ups.values()],
+                              **outs, scale=wl.scale)
+        torch.cuda.synchronize()
+        h = host_arrays(inp)
+        ref = oracle.step_backward(h["query"], h["new_key"], h["new_value"], h["key_cache"],
+                                   h["value_cache"], h["lengths"], h["append_mask"],
+                                   **{k: None if v is None else v.numpy() for k, v in ups.items()},
+                                   scale=wl.scale)
+        for name, want in (("g_query", ref.query), ("g_new_key", ref.new_key),
+                           ("g_new_value", ref.new_value), ("g_key_cache", ref.key_cache),
+                           ("g_value_cache", ref.value_cache)):
+            got = outs[name].cpu().numpy().astype(np.float64)
+            assert np.all(np.isfinite(got)), f"{wl.name}/{seed}: {name} not finite"
+            err = np.abs(got - want) - BWD_TOL * (1 + np.abs(want))
+            assert err.max() <= 0, f"{wl.name}/{upstream}/{seed}: {name} off by {err.max():.3e}"
