@@ -34,7 +34,7 @@ METRIC = "decode steps/s + achieved HBM GB/s (% of MI355X peak), GQA Hq32/Hk8 D1
 PEAK_HBM_GBPS = 8000.0
 DOMINANT_KERNEL = "attend"
 ENTRY = {"inplace": "kvc_step_inplace", "oop": "kvc_step_out_of_place", "paged": "kvc_step_paged",
-         "reattend": "kvc_attend_over_cache"}
+         "reattend": "kvc_attend_over_cache", "backward": "kvc_step_backward"}
 
 
 def parse():
@@ -43,7 +43,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode_gqa_bf16")
-    p.add_argument("--mode", choices=["inplace", "oop", "paged", "reattend"], default="inplace")
+    p.add_argument("--mode", choices=["inplace", "oop", "paged", "reattend", "backward"],
+                   default="inplace")
     p.add_argument("--block-size", type=int, default=64,
                    help="paged mode: slots per cache block (the pools are block-permuted)")
     p.add_argument("--seed", type=int, default=0)
@@ -82,6 +83,11 @@ class HipEvents:
         assert self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
                                             ctypes.c_void_p(b)) == 0
         return float(ms.value)
+
+    def record(self, e: int, stream: int = 0):
+        """Record event e on the current (default) stream."""
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        assert self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) == 0
 
     def destroy(self, e: int):
         self.hip.hipEventDestroy(ctypes.c_void_p(e))
@@ -126,6 +132,23 @@ def reattend_bytes(wl, lengths, n):
     out = tq * wl.Hq * wl.Dv * e
     small = wl.B * (8 + 8 + 4)
     return kv + q + out + small, kv + q
+
+
+def backward_bytes(wl, lengths, n):
+    """Backward of the step: read q, the visible K'/V' rows, the gradients of
+    the attention (visible entries), the context and the returned caches;
+    write the gradients of q, the new rows and the whole caches.  Returns
+    (whole call, the slot-gradient kernel's share: visible K'/V' rows, the
+    caches' gradients read and written, q and the context gradient)."""
+    e = 4
+    vis = sum(wl.Hk * (int(L) + int(k)) * (wl.D + wl.Dv) * e for L, k in zip(lengths, n))
+    full = wl.B * wl.Hk * wl.M * (wl.D + wl.Dv) * e
+    q = wl.B * wl.Hq * wl.Q * wl.D * e
+    dctx = wl.B * wl.Hq * wl.Q * wl.Dv * e
+    datt = sum(wl.Hq * (int(L) + t + 1) * e for L, k in zip(lengths, n) for t in range(int(k)))
+    new = wl.B * wl.Hk * wl.Q * (wl.D + wl.Dv) * e
+    step = vis + 2 * full + 2 * q + dctx + datt + new
+    return step, vis + 2 * full + q + dctx + new
 
 
 def oop_extra_bytes(wl, lengths, n):
@@ -237,6 +260,18 @@ def main():
         if args.mode == "oop":
             d["kc_out"] = torch.empty_like(inp["key_cache"])
             d["vc_out"] = torch.empty_like(inp["value_cache"])
+        if args.mode == "backward":
+            if wl.dtype != "f32":
+                raise SystemExit("--mode backward takes an fp32 workload")
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(7 + k)
+            for name, like in (("d_attention", "att"), ("d_context", "ctx")):
+                d[name] = torch.randn(d[like].shape, generator=gen, device=dev)
+            d["d_kc"] = torch.randn(inp["key_cache"].shape, generator=gen, device=dev)
+            d["d_vc"] = torch.randn(inp["value_cache"].shape, generator=gen, device=dev)
+            for name, like in (("g_q", "query"), ("g_nk", "new_key"), ("g_nv", "new_value"),
+                               ("g_kc", "key_cache"), ("g_vc", "value_cache")):
+                d[name] = torch.empty_like(inp[like])
         if args.mode == "reattend":
             # the cache already holds length + n rows; re-attend the last n
             cnt = torch.from_numpy(np.asarray(n, dtype=np.int64))
@@ -260,6 +295,9 @@ def main():
     plan = kvc.kvc_plan_step(dims, dt)
     if args.mode == "reattend":
         ws = torch.empty(kvc.kvc_attend_workspace_bytes(dims, dt), dtype=torch.uint8, device=dev)
+    elif args.mode == "backward":
+        ws = torch.empty(int(kvc.load().kvc_backward_workspace_bytes(ctypes.byref(dims), dt)),
+                         dtype=torch.uint8, device=dev)
     else:
         ws = kvc.workspace_for(dims, dt, dev)
 
@@ -270,7 +308,16 @@ def main():
     def step(i=None, k=0):
         d = sets[k % len(sets)]
         events = None if i is None or i % args.event_every else (starts[i], stops[i])
-        if args.mode == "reattend":
+        if args.mode == "backward":
+            if events:
+                ev.record(events[0])
+            kvc.kvc_step_backward(d["query"], d["new_key"], d["new_value"], d["key_cache"],
+                                  d["value_cache"], d["lengths"], d["mask"], d["d_attention"],
+                                  d["d_context"], d["d_kc"], d["d_vc"], d["g_q"], d["g_nk"],
+                                  d["g_nv"], d["g_kc"], d["g_vc"], workspace=ws, scale=wl.scale)
+            if events:
+                ev.record(events[1])
+        elif args.mode == "reattend":
             kvc.kvc_attend_over_cache(d["qp"], d["cu"], d["key_cache"], d["value_cache"], d["lk"],
                                       d["out"], wl.Q, row_status=d["status"], workspace=ws,
                                       scale=wl.scale, events=events)
@@ -310,6 +357,8 @@ def main():
         attend_bytes += extra_attend
     if args.mode == "reattend":
         step_bytes, attend_bytes = reattend_bytes(wl, lengths, n)
+    if args.mode == "backward":
+        step_bytes, attend_bytes = backward_bytes(wl, lengths, n)
     ms_per_step = elapsed / args.steps * 1e3
     steps_per_s = args.steps / elapsed
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -338,7 +387,9 @@ def main():
         "tokens_per_s": steps_per_s * wl.B * wl.Q,
         "step_algorithmic_bytes": step_bytes,
         "copy_ceiling_gbps": ceiling,
-        "roofline": {"bound": "hbm", "kernel": DOMINANT_KERNEL, "achieved": k_gbps,
+        "roofline": {"bound": "hbm",
+                     "kernel": "backward (all three kernels)" if args.mode == "backward"
+                     else DOMINANT_KERNEL, "achieved": k_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": k_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic, "bytes_per_launch": attend_bytes,
                      "avg_launch_ms": k_ms},
