@@ -541,8 +541,15 @@ bool reatt_layout(const kvc_dims* d, int dtype, ReattLayout* L) {
 // Backward: fp32, head sizes with a chunk kernel below.
 struct BwdEntry {
   int64_t D, Dv;
-  void (*launch)(const kvc::BwdArgs&, hipStream_t);
+  void (*stats)(const kvc::BwdArgs&, hipStream_t);
+  void (*chunk)(const kvc::BwdArgs&, hipStream_t);
 };
+template <int D, int DV>
+void launch_bwd_stats(const kvc::BwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((kvc::bwd_stats_kernel<D, DV>),
+                     dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk)), dim3(kvc::kBwdThreads), 0,
+                     s, a);
+}
 template <int D, int DV>
 void launch_bwd_chunk(const kvc::BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((kvc::bwd_chunk_kernel<D, DV>),
@@ -550,9 +557,9 @@ void launch_bwd_chunk(const kvc::BwdArgs& a, hipStream_t s) {
                      s, a);
 }
 const BwdEntry kBwdTable[] = {
-    {64, 64, &launch_bwd_chunk<64, 64>},
-    {128, 128, &launch_bwd_chunk<128, 128>},
-    {64, 32, &launch_bwd_chunk<64, 32>},
+    {64, 64, &launch_bwd_stats<64, 64>, &launch_bwd_chunk<64, 64>},
+    {128, 128, &launch_bwd_stats<128, 128>, &launch_bwd_chunk<128, 128>},
+    {64, 32, &launch_bwd_stats<64, 32>, &launch_bwd_chunk<64, 32>},
 };
 const BwdEntry* find_bwd(const kvc_dims* d) {
   for (const BwdEntry& e : kBwdTable)
@@ -564,7 +571,8 @@ size_t bwd_workspace(const kvc_dims* d) {
   const size_t B = d->B, Hq = d->Hq, Hk = d->Hk, Q = d->Q, D = d->D;
   const size_t R = (d->Hq / d->Hk) * d->Q;
   const size_t nchunk = (d->M + kvc::kBwdSlots - 1) / kvc::kBwdSlots;
-  return align_up(B * Hq * Q * 4 * 8, 256) + align_up(B * Hk * nchunk * R * D * 8, 256);
+  return align_up(B * Hq * Q * 4 * 8, 256) + align_up(B * Hk * nchunk * R * 4 * 8, 256) +
+         align_up(B * Hk * nchunk * R * D * 8, 256);
 }
 
 }  // namespace
@@ -640,15 +648,19 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
   a.g_kc = static_cast<float*>(g_key_cache);
   a.g_vc = static_cast<float*>(g_value_cache);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const size_t nchunk = static_cast<size_t>(a.nchunk), R = static_cast<size_t>(a.R);
   a.ws_row = reinterpret_cast<double*>(ws);
-  a.ws_dq = reinterpret_cast<double*>(ws + align_up(B * Hq * Q * 4 * 8, 256));
+  a.ws_part = reinterpret_cast<double*>(ws + align_up(B * Hq * Q * 4 * 8, 256));
+  a.ws_dq = reinterpret_cast<double*>(ws + align_up(B * Hq * Q * 4 * 8, 256) +
+                                      align_up(B * Hk * nchunk * R * 4 * 8, 256));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t rows = d->B * d->Hq * d->Q;
   const unsigned row_blocks = static_cast<unsigned>((rows + 3) / 4);
-  if (rows > 0)
-    hipLaunchKernelGGL(kvc::bwd_rows_kernel, dim3(static_cast<unsigned>(rows)),
-                       dim3(kvc::kBwdThreads), 0, s, a);
-  e->launch(a, s);
+  if (rows > 0) {
+    e->stats(a, s);
+    hipLaunchKernelGGL(kvc::bwd_rows_kernel, dim3(row_blocks), dim3(kvc::kBwdThreads), 0, s, a);
+  }
+  e->chunk(a, s);
   if (rows > 0)
     hipLaunchKernelGGL(kvc::bwd_dq_kernel, dim3(row_blocks), dim3(kvc::kBwdThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;

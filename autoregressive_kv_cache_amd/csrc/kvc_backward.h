@@ -19,11 +19,13 @@
 // dP and that sum are formed in fp64, and the query gradient is summed in
 // fp64.  The forward's fp32 attention and context are not needed.
 //
-// Kernels: bwd_rows (one workgroup per packed row: m, l and
-// sum_k P_k dP_k), bwd_chunk (one workgroup per (b, KV head, 64-slot
-// chunk): dS for the chunk's slots and all packed rows, the slot
-// gradients, and per-chunk dq partials), bwd_dq (one wave per packed row:
-// the partials summed).
+// Kernels: bwd_stats (one workgroup per (b, KV head, 64-slot chunk): each
+// packed row's max, sum and sum of P dP over the chunk's slots, K' and V'
+// staged once for all rows of the head), bwd_rows (one wave per packed
+// row: the chunk statistics merged as the forward merges its segments),
+// bwd_chunk (same grid as bwd_stats: dS for the chunk's slots and all
+// packed rows, the slot gradients, and per-chunk dq partials), bwd_dq (one
+// wave per packed row: the partials summed).
 #pragma once
 
 #include "kvc_common.h"
@@ -55,7 +57,8 @@ struct BwdArgs {
   float* g_new_value;
   float* g_kc;
   float* g_vc;
-  double* ws_row;          // [B][Hq][Q][4]: m, l, sum_k P_k dP_k
+  double* ws_row;          // [B][Hq][Q][4]: m, l, sum_k P_k dP_k / l
+  double* ws_part;         // [B*Hk][nchunk][R][4]: m_c, l_c, sum over the chunk of e^(s-m_c) dP
   double* ws_dq;           // [B*Hk][nchunk][R][D]
 };
 
@@ -70,27 +73,21 @@ __device__ inline void bwd_row_info(const BwdArgs& a, int64_t b, int64_t* len, i
   *n = ok ? k : 0;
 }
 
-// Block-wide reductions over the kBwdThreads threads of a workgroup.
-__device__ inline double bwd_block_max(double x, double* red) {
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const double y = __shfl_xor(x, o);
-    x = y > x ? y : x;
+// fp64 dot product of two fp32 vectors of length N (a multiple of 4), as
+// four independent partial sums so that consecutive FMAs do not wait on
+// each other.
+template <int N>
+__device__ __forceinline__ double dot_f64(const float* x, const float* y) {
+  static_assert(N % 4 == 0, "length");
+  double s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+#pragma unroll 4
+  for (int d = 0; d < N; d += 4) {
+    s0 += static_cast<double>(x[d]) * y[d];
+    s1 += static_cast<double>(x[d + 1]) * y[d + 1];
+    s2 += static_cast<double>(x[d + 2]) * y[d + 2];
+    s3 += static_cast<double>(x[d + 3]) * y[d + 3];
   }
-  __syncthreads();
-  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = x;
-  __syncthreads();
-  double r = red[0];
-  for (int w = 1; w < kBwdThreads / kWave; w++) r = red[w] > r ? red[w] : r;
-  return r;
-}
-__device__ inline double bwd_block_sum(double x, double* red) {
-  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  __syncthreads();
-  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = x;
-  __syncthreads();
-  double r = 0;
-  for (int w = 0; w < kBwdThreads / kWave; w++) r += red[w];
-  return r;
+  return (s0 + s1) + (s2 + s3);
 }
 
 // Slot j of the updated caches: kept rows from the cache, appended rows
@@ -103,53 +100,124 @@ __device__ inline const float* bwd_value_row(const BwdArgs& a, int64_t grp, int6
   return j < len ? a.vc + (grp * a.M + j) * a.Dv : a.new_value + (grp * a.Q + (j - len)) * a.Dv;
 }
 
-// One workgroup per packed row (b, hq, t): the row's score max m and sum l
-// over its visible slots, and sum_j P_j dP_j, all in fp64 (0s for rows that
-// are not valid).
-__global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(BwdArgs a) {
-  __shared__ double red[kBwdThreads / kWave];
-  const int64_t row = blockIdx.x;
-  const int64_t t = row % a.Q, hq = (row / a.Q) % a.Hq, b = row / (a.Hq * a.Q);
-  const int64_t grp = b * a.Hk + hq / a.G;
+// One workgroup per (b, KV head, chunk of kBwdSlots slots): for every valid
+// packed row, over the chunk's slots it sees, m_c = max s_j, l_c =
+// sum e^(s_j - m_c) and sum e^(s_j - m_c) dP_j, in fp64 (one wave per row,
+// one lane per slot).
+template <int D, int DV>
+__global__ __launch_bounds__(kBwdThreads) void bwd_stats_kernel(BwdArgs a) {
+  constexpr int C = kBwdSlots, RT = kBwdRowTile, W = kBwdThreads / kWave;
+  static_assert(C == kWave, "one lane per slot");
+  __shared__ float k_s[C][D + 1];
+  __shared__ float v_s[C][DV + 1];
+  __shared__ float q_s[RT][D + 1];
+  __shared__ float o_s[RT][DV + 1];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int64_t c = blockIdx.x % a.nchunk;
+  const int64_t grp = blockIdx.x / a.nchunk;
+  const int64_t b = grp / a.Hk, kvh = grp % a.Hk;
   int64_t len, n;
   bwd_row_info(a, b, &len, &n);
-  double* out = a.ws_row + row * 4;
-  if (t >= n) {
-    if (threadIdx.x == 0) out[0] = out[1] = out[2] = out[3] = 0.0;
-    return;
+  const int64_t s0 = c * C;
+  const int64_t nvis = n > 0 ? len + n : 0;
+  if (s0 >= nvis) return;  // no row sees this chunk
+  for (int idx = tid; idx < C * D; idx += kBwdThreads) {
+    const int sl = idx / D, d = idx % D;
+    const int64_t j = s0 + sl;
+    k_s[sl][d] = j < nvis ? bwd_key_row(a, grp, len, j)[d] : 0.f;
   }
-  const float* q = a.query + row * a.D;
-  const float* dO = a.d_ctx ? a.d_ctx + row * a.Dv : nullptr;
-  const double sc = a.scale;
-  auto score = [&](int64_t j) {
-    const float* k = bwd_key_row(a, grp, len, j);
-    double acc = 0;
-    for (int64_t d = 0; d < a.D; d++) acc += static_cast<double>(q[d]) * k[d];
-    return sc * acc;
-  };
-  double m = -INFINITY;
-  for (int64_t j = threadIdx.x; j <= len + t; j += kBwdThreads) {
-    const double s = score(j);
-    m = s > m ? s : m;
+  for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
+    const int sl = idx / DV, d = idx % DV;
+    const int64_t j = s0 + sl;
+    v_s[sl][d] = j < nvis ? bwd_value_row(a, grp, len, j)[d] : 0.f;
   }
-  m = bwd_block_max(m, red);
-  double l = 0, pd = 0;
-  for (int64_t j = threadIdx.x; j <= len + t; j += kBwdThreads) {
-    const double p = exp(score(j) - m);
-    double dp = a.d_att ? static_cast<double>(a.d_att[row * a.M + j]) : 0.0;
-    if (dO) {
-      const float* v = bwd_value_row(a, grp, len, j);
-      for (int64_t d = 0; d < a.Dv; d++) dp += static_cast<double>(dO[d]) * v[d];
+  const int64_t j = s0 + lane;
+  for (int r0 = 0; r0 < a.R; r0 += RT) {
+    __syncthreads();
+    for (int idx = tid; idx < RT * D; idx += kBwdThreads) {
+      const int rr = idx / D, d = idx % D, r = r0 + rr;
+      const int64_t g = r / a.Q, t = r % a.Q;
+      q_s[rr][d] = (r < a.R && t < n)
+                       ? a.query[((b * a.Hq + kvh * a.G + g) * a.Q + t) * D + d] : 0.f;
     }
-    l += p;
-    pd += p * dp;
+    for (int idx = tid; idx < RT * DV; idx += kBwdThreads) {
+      const int rr = idx / DV, d = idx % DV, r = r0 + rr;
+      const int64_t g = r / a.Q, t = r % a.Q;
+      o_s[rr][d] = (a.d_ctx && r < a.R && t < n)
+                       ? a.d_ctx[((b * a.Hq + kvh * a.G + g) * a.Q + t) * DV + d] : 0.f;
+    }
+    __syncthreads();
+    for (int rr = wave; rr < RT; rr += W) {
+      const int r = r0 + rr;
+      if (r >= a.R) break;
+      const int64_t g = r / a.Q, t = r % a.Q;
+      if (t >= n) continue;
+      const int64_t row = (b * a.Hq + kvh * a.G + g) * a.Q + t;
+      const bool vis = j <= len + t;
+      double sc = 0, dp = 0;
+      if (vis) {
+        sc = static_cast<double>(a.scale) * dot_f64<D>(q_s[rr], k_s[lane]);
+        dp = (a.d_att ? static_cast<double>(a.d_att[row * a.M + j]) : 0.0) +
+             dot_f64<DV>(o_s[rr], v_s[lane]);
+      }
+      double m = vis ? sc : -INFINITY;
+      for (int o = kWave / 2; o > 0; o >>= 1) {
+        const double y = __shfl_xor(m, o);
+        m = y > m ? y : m;
+      }
+      const double e = vis ? exp(sc - m) : 0.0;
+      double l = e, pd = e * dp;
+      for (int o = kWave / 2; o > 0; o >>= 1) {
+        l += __shfl_xor(l, o);
+        pd += __shfl_xor(pd, o);
+      }
+      if (lane == 0) {
+        double* out = a.ws_part + ((grp * a.nchunk + c) * a.R + r) * 4;
+        out[0] = m;
+        out[1] = l;
+        out[2] = pd;
+        out[3] = 0.0;
+      }
+    }
   }
-  l = bwd_block_sum(l, red);
-  pd = bwd_block_sum(pd, red);
-  if (threadIdx.x == 0) {
-    out[0] = m;
-    out[1] = l;
-    out[2] = pd / l;
+}
+
+// One wave per packed row: its chunk statistics merged (m = max m_c,
+// l = sum l_c e^(m_c - m), the same for the P dP sums), then divided by l.
+__global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(BwdArgs a) {
+  const int64_t row = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (row >= a.B * a.Hq * a.Q) return;
+  const int64_t t = row % a.Q, hq = (row / a.Q) % a.Hq, b = row / (a.Hq * a.Q);
+  int64_t len, n;
+  bwd_row_info(a, b, &len, &n);
+  const int64_t kvh = hq / a.G, g = hq % a.G, r = g * a.Q + t, grp = b * a.Hk + kvh;
+  const int64_t nc = t < n ? (len + t) / kBwdSlots + 1 : 0;
+  double m = -INFINITY, l = 0, pd = 0;
+  for (int64_t c = lane; c < nc; c += kWave) {
+    const double* p = a.ws_part + ((grp * a.nchunk + c) * a.R + r) * 4;
+    const double mn = p[0] > m ? p[0] : m;
+    const double fo = m == -INFINITY ? 0.0 : exp(m - mn), fn = exp(p[0] - mn);
+    l = l * fo + p[1] * fn;
+    pd = pd * fo + p[2] * fn;
+    m = mn;
+  }
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const double mo = __shfl_xor(m, o), lo = __shfl_xor(l, o), po = __shfl_xor(pd, o);
+    const double mn = mo > m ? mo : m;
+    if (mn != -INFINITY) {
+      const double fa = m == -INFINITY ? 0.0 : exp(m - mn);
+      const double fb = mo == -INFINITY ? 0.0 : exp(mo - mn);
+      l = l * fa + lo * fb;
+      pd = pd * fa + po * fb;
+    }
+    m = mn;
+  }
+  if (lane == 0) {
+    double* out = a.ws_row + row * 4;
+    out[0] = nc > 0 ? m : 0.0;
+    out[1] = nc > 0 ? l : 0.0;
+    out[2] = nc > 0 ? pd / l : 0.0;
     out[3] = 0.0;
   }
 }
@@ -228,11 +296,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
       if (r < a.R && t < n && j <= len + t) {
         const int64_t row = (b * a.Hq + kvh * a.G + g) * a.Q + t;
         const double* st = a.ws_row + row * 4;
-        double sc = 0;
-        for (int d = 0; d < D; d++) sc += static_cast<double>(q_s[rr][d]) * k_s[s][d];
+        const double sc = dot_f64<D>(q_s[rr], k_s[s]);
         p = exp(static_cast<double>(a.scale) * sc - st[0]) / st[1];
-        double dp = a.d_att ? static_cast<double>(a.d_att[row * a.M + j]) : 0.0;
-        for (int d = 0; d < DV; d++) dp += static_cast<double>(o_s[rr][d]) * v_s[s][d];
+        const double dp = (a.d_att ? static_cast<double>(a.d_att[row * a.M + j]) : 0.0) +
+                          dot_f64<DV>(o_s[rr], v_s[s]);
         ds = static_cast<double>(a.scale) * p * (dp - st[2]);
       }
       ds_s[rr][s] = ds;
@@ -264,9 +331,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     for (int idx = tid; idx < RT * D; idx += kBwdThreads) {
       const int rr = idx / D, d = idx % D, r = r0 + rr;
       if (r >= a.R) continue;
-      double acc = 0;
-      for (int s = 0; s < C; s++) acc += ds_s[rr][s] * k_s[s][d];
-      a.ws_dq[((grp * a.nchunk + c) * a.R + r) * D + d] = acc;
+      double acc0 = 0, acc1 = 0;
+      for (int s = 0; s < C; s += 2) {
+        acc0 += ds_s[rr][s] * k_s[s][d];
+        acc1 += ds_s[rr][s + 1] * k_s[s + 1][d];
+      }
+      a.ws_dq[((grp * a.nchunk + c) * a.R + r) * D + d] = acc0 + acc1;
     }
   }
 
