@@ -1,0 +1,145 @@
+// kvc_backward_api.hip -- host side of the backward entry points of
+// include/kvc.h (kvc_backward_workspace_bytes, kvc_step_backward): checks,
+// workspace layout and the four launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/kvc.h"
+#include "kvc_backward.h"
+#include "kvc_host.h"
+
+namespace {
+
+using namespace kvc_host;
+
+// Backward: fp32, head sizes with a chunk kernel below.
+struct BwdEntry {
+  int64_t D, Dv;
+  void (*stats)(const kvc::BwdArgs&, hipStream_t);
+  void (*chunk)(const kvc::BwdArgs&, hipStream_t);
+};
+template <int D, int DV>
+void launch_bwd_stats(const kvc::BwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((kvc::bwd_stats_kernel<D, DV>),
+                     dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk)), dim3(kvc::kBwdThreads), 0,
+                     s, a);
+}
+template <int D, int DV>
+void launch_bwd_chunk(const kvc::BwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((kvc::bwd_chunk_kernel<D, DV>),
+                     dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk)), dim3(kvc::kBwdThreads), 0,
+                     s, a);
+}
+const BwdEntry kBwdTable[] = {
+    {64, 64, &launch_bwd_stats<64, 64>, &launch_bwd_chunk<64, 64>},
+    {128, 128, &launch_bwd_stats<128, 128>, &launch_bwd_chunk<128, 128>},
+    {64, 32, &launch_bwd_stats<64, 32>, &launch_bwd_chunk<64, 32>},
+};
+const BwdEntry* find_bwd(const kvc_dims* d) {
+  for (const BwdEntry& e : kBwdTable)
+    if (e.D == d->D && e.Dv == d->Dv) return &e;
+  return nullptr;
+}
+
+size_t bwd_workspace(const kvc_dims* d) {
+  const size_t B = d->B, Hq = d->Hq, Hk = d->Hk, Q = d->Q, D = d->D;
+  const size_t R = (d->Hq / d->Hk) * d->Q;
+  const size_t nchunk = (d->M + kvc::kBwdSlots - 1) / kvc::kBwdSlots;
+  return align_up(B * Hq * Q * 4 * 8, 256) + align_up(B * Hk * nchunk * R * 4 * 8, 256) +
+         align_up(B * Hk * nchunk * R * D * 8, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvc_backward_workspace_bytes(const kvc_dims* dims, int dtype) {
+  if (!dims || check_dims(dims, dtype) != KVC_OK || dtype != KVC_F32) return 0;
+  return bwd_workspace(dims);
+}
+
+int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double scale,
+                      const void* query, const void* new_key, const void* new_value,
+                      const void* key_cache, const void* value_cache, const int64_t* lengths,
+                      const uint8_t* append_mask, const void* d_attention, const void* d_context,
+                      const void* d_key_cache_out, const void* d_value_cache_out,
+                      void* g_query, void* g_new_key, void* g_new_value, void* g_key_cache,
+                      void* g_value_cache, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!dims) return KVC_ERR_NULL;
+  const kvc_dims* d = dims;
+  int rc = check_dims(d, dtype);
+  if (rc != KVC_OK) return rc;
+  if (dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
+  const BwdEntry* e = find_bwd(d);
+  if (!e) return KVC_ERR_UNSUPPORTED;
+  double sc;
+  rc = check_scale(has_scale, scale, d->D, &sc);
+  if (rc != KVC_OK) return rc;
+  if (!key_cache || !value_cache || !lengths || !g_key_cache || !g_value_cache || !workspace)
+    return KVC_ERR_NULL;
+  if (d->Q > 0 && (!query || !new_key || !new_value || !append_mask || !g_query || !g_new_key ||
+                   !g_new_value))
+    return KVC_ERR_NULL;
+  if (workspace_bytes < bwd_workspace(d)) return KVC_ERR_WORKSPACE;
+  const size_t B = d->B, Hq = d->Hq, Hk = d->Hk, Q = d->Q, M = d->M, D = d->D, Dv = d->Dv;
+  const Range ins[] = {{query, B * Hq * Q * D * 4}, {new_key, B * Hk * Q * D * 4},
+                       {new_value, B * Hk * Q * Dv * 4}, {key_cache, B * Hk * M * D * 4},
+                       {value_cache, B * Hk * M * Dv * 4}, {lengths, B * 8},
+                       {append_mask, B * Q}, {d_attention, B * Hq * Q * M * 4},
+                       {d_context, B * Hq * Q * Dv * 4}, {d_key_cache_out, B * Hk * M * D * 4},
+                       {d_value_cache_out, B * Hk * M * Dv * 4}};
+  const Range outs[] = {{g_query, B * Hq * Q * D * 4}, {g_new_key, B * Hk * Q * D * 4},
+                        {g_new_value, B * Hk * Q * Dv * 4}, {g_key_cache, B * Hk * M * D * 4},
+                        {g_value_cache, B * Hk * M * Dv * 4}, {workspace, bwd_workspace(d)}};
+  for (int i = 0; i < 6; i++) {
+    for (const Range& in : ins)
+      if (overlap(outs[i], in)) return KVC_ERR_ALIAS;
+    for (int j = i + 1; j < 6; j++)
+      if (overlap(outs[i], outs[j])) return KVC_ERR_ALIAS;
+  }
+  kvc::BwdArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.B = d->B; a.Hq = d->Hq; a.Hk = d->Hk; a.Q = d->Q; a.M = d->M; a.D = d->D; a.Dv = d->Dv;
+  a.G = static_cast<int32_t>(d->Hq / d->Hk);
+  a.R = static_cast<int32_t>(a.G * d->Q);
+  a.nchunk = (d->M + kvc::kBwdSlots - 1) / kvc::kBwdSlots;
+  a.scale = static_cast<float>(sc);
+  a.query = static_cast<const float*>(query);
+  a.new_key = static_cast<const float*>(new_key);
+  a.new_value = static_cast<const float*>(new_value);
+  a.kc = static_cast<const float*>(key_cache);
+  a.vc = static_cast<const float*>(value_cache);
+  a.lengths = lengths;
+  a.mask = append_mask;
+  a.d_att = static_cast<const float*>(d_attention);
+  a.d_ctx = static_cast<const float*>(d_context);
+  a.d_kc_out = static_cast<const float*>(d_key_cache_out);
+  a.d_vc_out = static_cast<const float*>(d_value_cache_out);
+  a.g_query = static_cast<float*>(g_query);
+  a.g_new_key = static_cast<float*>(g_new_key);
+  a.g_new_value = static_cast<float*>(g_new_value);
+  a.g_kc = static_cast<float*>(g_key_cache);
+  a.g_vc = static_cast<float*>(g_value_cache);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const size_t nchunk = static_cast<size_t>(a.nchunk), R = static_cast<size_t>(a.R);
+  a.ws_row = reinterpret_cast<double*>(ws);
+  a.ws_part = reinterpret_cast<double*>(ws + align_up(B * Hq * Q * 4 * 8, 256));
+  a.ws_dq = reinterpret_cast<double*>(ws + align_up(B * Hq * Q * 4 * 8, 256) +
+                                      align_up(B * Hk * nchunk * R * 4 * 8, 256));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t rows = d->B * d->Hq * d->Q;
+  const unsigned row_blocks = static_cast<unsigned>((rows + 3) / 4);
+  if (rows > 0) {
+    e->stats(a, s);
+    hipLaunchKernelGGL(kvc::bwd_rows_kernel, dim3(row_blocks), dim3(kvc::kBwdThreads), 0, s, a);
+  }
+  e->chunk(a, s);
+  if (rows > 0)
+    hipLaunchKernelGGL(kvc::bwd_dq_kernel, dim3(row_blocks), dim3(kvc::kBwdThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
+}  // extern "C"

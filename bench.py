@@ -164,10 +164,16 @@ def oop_extra_bytes(wl, lengths, n):
     return step, attend
 
 
+# Sources the attend kernel is compiled from and launched by (the stream
+# decode kernel, its row preparation, the host plan and launch code): a change
+# to any of them makes a committed counter summary stale.
+ATTEND_SOURCES = ("kvc_api.hip", "kvc_common.h", "kvc_decode.h", "kvc_host.h", "kvc_prep.h")
+
+
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "autoregressive_kv_cache_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ATTEND_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
