@@ -217,26 +217,21 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
   // ---- first pass of the range: its loads go out before the statistics ----
   const int64_t nvec = (e1 - e0) / 8;
   Vec8<T> x[VPL];
-  double mcd[VPL], mcd_hi[VPL];  // chunk maxima as loaded (converted when used)
-  bool live[VPL];
+  Acc mc[VPL], mc_hi[VPL];
   int split[VPL];  // elements of the vector in the chunk of its first slot
-  // No value loaded here is used before all of them are requested: the
-  // statistics of dead vectors come from chunk 0 (always a valid address)
-  // and are discarded, so no load waits behind a branch.
+  // The chunk maxima are converted as they are loaded: keeping them as
+  // loaded (fp64) to defer that wait costs 8 more registers per lane, which
+  // drops the bf16 kernel from 5 to 4 waves per SIMD and is slower.
   auto load_vec = [&](int v, int64_t vi) {
     const int64_t base = e0 + vi * 8;
-    live[v] = vi < nvec && base < lim;
+    const bool live = vi < nvec && base < lim;
     // the vector's last slot may lie in the next chunk (stream mode, at len)
     const int64_t last = base + 7 < lim ? base + 7 : lim - 1;
-    const int64_t c_lo = live[v] ? chunk_of(base) : 0, c_hi = live[v] ? chunk_of(last) : 0;
     x[v].zero();
-    if (live[v]) x[v].load(arow + base);
-    mcd[v] = chunk_ml[(c_lo * a.R + r) * 2];
-    mcd_hi[v] = chunk_ml[(c_hi * a.R + r) * 2];
+    if (live) x[v].load(arow + base);
+    mc[v] = live ? static_cast<Acc>(chunk_ml[(chunk_of(base) * a.R + r) * 2]) : neg_inf;
+    mc_hi[v] = live ? static_cast<Acc>(chunk_ml[(chunk_of(last) * a.R + r) * 2]) : neg_inf;
     split[v] = a.seg_mode && base < len && base + 8 > len ? static_cast<int>(len - base) : 8;
-  };
-  auto mc_of = [&](int v, bool hi) {
-    return live[v] ? static_cast<Acc>(hi ? mcd_hi[v] : mcd[v]) : neg_inf;
   };
   if (vec) {
 #pragma unroll
@@ -314,7 +309,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
         const int64_t base = e0 + (v0 + v * kWave + lane) * 8;
         if (v0 + v * kWave + lane < nvec) {
           if (base < lim) {
-            x[v].scale_split(factor(mc_of(v, false)), factor(mc_of(v, true)), split[v]);
+            x[v].scale_split(factor(mc[v]), factor(mc_hi[v]), split[v]);
             if (base + 8 > lim) x[v].keep_first(static_cast<int>(lim - base));
           }
           x[v].store(arow + base);
