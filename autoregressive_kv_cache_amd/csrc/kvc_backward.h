@@ -25,7 +25,9 @@
 // row: the chunk statistics merged as the forward merges its segments),
 // bwd_chunk (same grid as bwd_stats: dS for the chunk's slots and all
 // packed rows, the slot gradients, and per-chunk dq partials), bwd_dq (one
-// wave per packed row: the partials summed).
+// wave per packed row: the partials summed).  The products of the two
+// chunk kernels (scores, dO . V', dK', dV', dq) run on the fp64 matrix
+// cores; the slot gradients are summed in fp64 before the fp32 store.
 #pragma once
 
 #include "kvc_common.h"
@@ -35,11 +37,22 @@ namespace kvc {
 constexpr int kBwdThreads = 256;
 constexpr int kBwdSlots = 64;   // slots per chunk workgroup
 constexpr int kBwdRowTile = 16; // packed rows staged in LDS at a time
+constexpr int kBwdMaxRowGroups = 16;
+
+// bwd_chunk: workgroups per chunk, each over a share of the 16-column tiles
+// of dK', dV' and dq (the scores are recomputed by each).  One: splitting
+// the columns over four workgroups was slower (the scores, the attention
+// gradient loads and the staging are repeated by each).
+template <int D, int DV>
+constexpr int bwd_col_groups() {
+  return 1;
+}
 
 struct BwdArgs {
   int64_t B, Hq, Hk, Q, M, D, Dv;
   int32_t G, R;
   int64_t nchunk;  // ceil(M / kBwdSlots)
+  int32_t row_groups;  // bwd_stats: workgroups per chunk, each over every row_groups-th row tile
   float scale;
   const float* query;      // [B][Hq][Q][D]
   const float* new_key;    // [B][Hk][Q][D]
@@ -62,32 +75,36 @@ struct BwdArgs {
   double* ws_dq;           // [B*Hk][nchunk][R][D]
 };
 
-// Row information of batch row b for one thread (prefix count n, status).
+// Row information of batch row b: its length and prefix count n (0 for a
+// row outside the contract).  Called by whole waves: lane t reads mask
+// entry t of each 64-entry piece and the wave's ballot gives the prefix,
+// so no load waits on another.
 __device__ inline void bwd_row_info(const BwdArgs& a, int64_t b, int64_t* len, int64_t* n) {
+  const int lane = threadIdx.x % kWave;
   const int64_t L = a.lengths[b];
   int64_t k = 0;
-  while (k < a.Q && a.mask[b * a.Q + k]) k++;
-  bool ok = L >= 0 && L <= a.M && L + k <= a.M;
-  for (int64_t t = k; t < a.Q; t++) ok = ok && !a.mask[b * a.Q + t];
+  bool open = true, ok = true;  // open: every entry so far is set
+  for (int64_t base = 0; base < a.Q; base += kWave) {
+    const int64_t t = base + lane;
+    const uint64_t set = __ballot(t < a.Q && a.mask[b * a.Q + t] != 0);
+    const int64_t cnt = a.Q - base < kWave ? a.Q - base : kWave;
+    if (open) {
+      const uint64_t all = cnt == kWave ? ~0ull : (1ull << cnt) - 1;
+      if (set == all) {
+        k += cnt;
+      } else {  // entries [0, lead) set, entry lead clear: nothing above may be set
+        const int lead = __builtin_ctzll(~set);
+        k += lead;
+        open = false;
+        ok = (set >> lead) == 0;
+      }
+    } else {
+      ok = ok && set == 0;
+    }
+  }
+  ok = ok && L >= 0 && L <= a.M && L + k <= a.M;
   *len = L;
   *n = ok ? k : 0;
-}
-
-// fp64 dot product of two fp32 vectors of length N (a multiple of 4), as
-// four independent partial sums so that consecutive FMAs do not wait on
-// each other.
-template <int N>
-__device__ __forceinline__ double dot_f64(const float* x, const float* y) {
-  static_assert(N % 4 == 0, "length");
-  double s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-#pragma unroll 4
-  for (int d = 0; d < N; d += 4) {
-    s0 += static_cast<double>(x[d]) * y[d];
-    s1 += static_cast<double>(x[d + 1]) * y[d + 1];
-    s2 += static_cast<double>(x[d + 2]) * y[d + 2];
-    s3 += static_cast<double>(x[d + 3]) * y[d + 3];
-  }
-  return (s0 + s1) + (s2 + s3);
 }
 
 // Slot j of the updated caches: kept rows from the cache, appended rows
@@ -100,78 +117,216 @@ __device__ inline const float* bwd_value_row(const BwdArgs& a, int64_t grp, int6
   return j < len ? a.vc + (grp * a.M + j) * a.Dv : a.new_value + (grp * a.Q + (j - len)) * a.Dv;
 }
 
-// One workgroup per (b, KV head, chunk of kBwdSlots slots): for every valid
-// packed row, over the chunk's slots it sees, m_c = max s_j, l_c =
-// sum e^(s_j - m_c) and sum e^(s_j - m_c) dP_j, in fp64 (one wave per row,
-// one lane per slot).
+// The chunk kernels run their products on the fp64 matrix cores
+// (v_mfma_f64_16x16x4_f64, fp32 inputs widened exactly).  Operand layout
+// (wave64): lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and
+// holds D[4 i + l / 16][l % 16] for i < 4.  A workgroup holds the K', V'
+// rows of its chunk; the packed rows go through in tiles of 16, and wave w
+// owns the chunk's slots [16 w, 16 w + 16).
+typedef double bwd_f64x4 __attribute__((ext_vector_type(4)));
+
+// LDS row pitches (in elements): the operand reads run down a column
+// (16 rows x 4 columns, or 4 rows x 16 columns per instruction); these
+// pitches keep such reads on distinct banks.
+template <int N>
+constexpr int bwd_pitch() {
+  return N + 4;
+}
+
+// K', V' rows of the chunk starting at slot s0 (zeros past nvis).
+template <int D, int DV>
+__device__ inline void bwd_stage_kv(const BwdArgs& a, int64_t grp, int64_t len, int64_t nvis,
+                                    int64_t s0, float* k_s, float* v_s) {
+  constexpr int C = kBwdSlots, KP = bwd_pitch<D>(), VP = bwd_pitch<DV>();
+  for (int idx = threadIdx.x; idx < C * D; idx += kBwdThreads) {
+    const int sl = idx / D, d = idx % D;
+    const int64_t j = s0 + sl;
+    k_s[sl * KP + d] = j < nvis ? bwd_key_row(a, grp, len, j)[d] : 0.f;
+  }
+  for (int idx = threadIdx.x; idx < C * DV; idx += kBwdThreads) {
+    const int sl = idx / DV, d = idx % DV;
+    const int64_t j = s0 + sl;
+    v_s[sl * VP + d] = j < nvis ? bwd_value_row(a, grp, len, j)[d] : 0.f;
+  }
+}
+
+// The inputs of one tile of 16 packed rows, held in registers from their
+// loads until the tile before has finished with LDS (so the loads of tile
+// r + 1 are in flight while tile r computes): q and dO (zeros for rows that
+// are not valid), this lane's four attention-gradient entries (rows
+// 4 i + l / 16 of the tile, its slot j; 0 where not visible), and for
+// threads below 16 the row's m, l and sum P dP (bwd_chunk).
+template <int D, int DV>
+struct BwdTileRegs {
+  static constexpr int NQ = (kBwdRowTile * D + kBwdThreads - 1) / kBwdThreads;
+  static constexpr int NO = (kBwdRowTile * DV + kBwdThreads - 1) / kBwdThreads;
+  float q[NQ], o[NO];
+  float da[4];
+  double st[3];
+};
+
+template <int D, int DV>
+__device__ inline void bwd_fetch_tile(const BwdArgs& a, int64_t b, int64_t kvh, int64_t len,
+                                      int64_t n, int r0, int64_t j, bool stats,
+                                      BwdTileRegs<D, DV>& x) {
+  using X = BwdTileRegs<D, DV>;
+  constexpr int RT = kBwdRowTile;
+  const int tid = threadIdx.x, lq = (tid % kWave) / 16;
+#pragma unroll
+  for (int i = 0; i < X::NQ; i++) {
+    const int idx = tid + i * kBwdThreads;
+    const int rr = idx / D, d = idx % D, r = r0 + rr;
+    const int64_t g = r / a.Q, t = r % a.Q;
+    x.q[i] = (idx < RT * D && r < a.R && t < n)
+                 ? a.query[((b * a.Hq + kvh * a.G + g) * a.Q + t) * D + d] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < X::NO; i++) {
+    const int idx = tid + i * kBwdThreads;
+    const int rr = idx / DV, d = idx % DV, r = r0 + rr;
+    const int64_t g = r / a.Q, t = r % a.Q;
+    x.o[i] = (a.d_ctx && idx < RT * DV && r < a.R && t < n)
+                 ? a.d_ctx[((b * a.Hq + kvh * a.G + g) * a.Q + t) * DV + d] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int r = r0 + 4 * i + lq;
+    const int64_t g = r / a.Q, t = r % a.Q;
+    const bool vis = a.d_att && r < a.R && t < n && j <= len + t;
+    x.da[i] = vis ? a.d_att[((b * a.Hq + kvh * a.G + g) * a.Q + t) * a.M + j] : 0.f;
+  }
+  if (stats && tid < RT) {
+    const int r = r0 + tid;
+    const int64_t g = r / a.Q, t = r % a.Q;
+    const bool ok = r < a.R && t < n;
+    const double* st = a.ws_row + ((b * a.Hq + kvh * a.G + g) * a.Q + t) * 4;
+    x.st[0] = ok ? st[0] : 0.0;
+    x.st[1] = ok ? st[1] : 1.0;
+    x.st[2] = ok ? st[2] : 0.0;
+  }
+}
+
+// q and dO of the tile into LDS (row pitch bwd_pitch).
+template <int D, int DV>
+__device__ inline void bwd_commit_tile(const BwdTileRegs<D, DV>& x, float* q_s, float* o_s) {
+  using X = BwdTileRegs<D, DV>;
+  constexpr int RT = kBwdRowTile, KP = bwd_pitch<D>(), VP = bwd_pitch<DV>();
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < X::NQ; i++) {
+    const int idx = tid + i * kBwdThreads;
+    if (idx < RT * D) q_s[(idx / D) * KP + idx % D] = x.q[i];
+  }
+#pragma unroll
+  for (int i = 0; i < X::NO; i++) {
+    const int idx = tid + i * kBwdThreads;
+    if (idx < RT * DV) o_s[(idx / DV) * VP + idx % DV] = x.o[i];
+  }
+}
+
+// S = q . K'_j and dO . V'_j for the 16 staged rows and this wave's 16
+// slots: s[i], dov[i] belong to row 4 i + l / 16 and slot 16 w + l % 16.
+template <int D, int DV>
+__device__ inline void bwd_scores(const float* q_s, const float* o_s, const float* k_s,
+                                  const float* v_s, int w, int li, int lq, bwd_f64x4& s,
+                                  bwd_f64x4& dov) {
+  constexpr int KP = bwd_pitch<D>(), VP = bwd_pitch<DV>();
+  s = bwd_f64x4{0.0, 0.0, 0.0, 0.0};
+  dov = bwd_f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int kk = 0; kk < D / 4; kk++)
+    s = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(q_s[li * KP + 4 * kk + lq]),
+                                             static_cast<double>(k_s[(16 * w + li) * KP + 4 * kk + lq]),
+                                             s, 0, 0, 0);
+#pragma unroll
+  for (int kk = 0; kk < DV / 4; kk++)
+    dov = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(o_s[li * VP + 4 * kk + lq]),
+                                               static_cast<double>(v_s[(16 * w + li) * VP + 4 * kk + lq]),
+                                               dov, 0, 0, 0);
+}
+
+// One workgroup per (b, KV head, chunk of kBwdSlots slots, row group): for
+// every valid packed row of its row tiles, over the chunk's slots it sees, m_c = max s_j, l_c =
+// sum e^(s_j - m_c) and sum e^(s_j - m_c) dP_j, in fp64 (each wave over its
+// 16 slots, then the four merged).
 template <int D, int DV>
 __global__ __launch_bounds__(kBwdThreads) void bwd_stats_kernel(BwdArgs a) {
   constexpr int C = kBwdSlots, RT = kBwdRowTile, W = kBwdThreads / kWave;
-  static_assert(C == kWave, "one lane per slot");
-  __shared__ float k_s[C][D + 1];
-  __shared__ float v_s[C][DV + 1];
-  __shared__ float q_s[RT][D + 1];
-  __shared__ float o_s[RT][DV + 1];
+  constexpr int KP = bwd_pitch<D>(), VP = bwd_pitch<DV>();
+  static_assert(C == 16 * W && RT == 16 && D % 16 == 0 && DV % 16 == 0, "tile shape");
+  __shared__ float k_s[C * KP];
+  __shared__ float v_s[C * VP];
+  __shared__ float q_s[RT * KP];
+  __shared__ float o_s[RT * VP];
+  __shared__ double part_s[W][RT][3];
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int64_t c = blockIdx.x % a.nchunk;
-  const int64_t grp = blockIdx.x / a.nchunk;
+  const int li = lane % 16, lq = lane / 16;
+  const int rg = static_cast<int>(blockIdx.x % a.row_groups);
+  const int64_t c = (blockIdx.x / a.row_groups) % a.nchunk;
+  const int64_t grp = blockIdx.x / a.row_groups / a.nchunk;
   const int64_t b = grp / a.Hk, kvh = grp % a.Hk;
   int64_t len, n;
   bwd_row_info(a, b, &len, &n);
   const int64_t s0 = c * C;
   const int64_t nvis = n > 0 ? len + n : 0;
-  if (s0 >= nvis) return;  // no row sees this chunk
-  for (int idx = tid; idx < C * D; idx += kBwdThreads) {
-    const int sl = idx / D, d = idx % D;
-    const int64_t j = s0 + sl;
-    k_s[sl][d] = j < nvis ? bwd_key_row(a, grp, len, j)[d] : 0.f;
-  }
-  for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
-    const int sl = idx / DV, d = idx % DV;
-    const int64_t j = s0 + sl;
-    v_s[sl][d] = j < nvis ? bwd_value_row(a, grp, len, j)[d] : 0.f;
-  }
-  const int64_t j = s0 + lane;
-  for (int r0 = 0; r0 < a.R; r0 += RT) {
+  if (s0 >= nvis || rg * RT >= a.R) return;  // no row of this workgroup sees the chunk
+  const double scale = a.scale;
+  const int64_t j = s0 + 16 * wave + li;  // this lane's slot
+  const int step = a.row_groups * RT;
+  BwdTileRegs<D, DV> nx;  // the next tile's inputs, loading while this one computes
+  bwd_fetch_tile<D, DV>(a, b, kvh, len, n, rg * RT, j, false, nx);
+  bwd_stage_kv<D, DV>(a, grp, len, nvis, s0, k_s, v_s);
+  for (int r0 = rg * RT; r0 < a.R; r0 += step) {
+    __syncthreads();  // the previous tile is no longer read
+    bwd_commit_tile<D, DV>(nx, q_s, o_s);
+    float da[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) da[i] = nx.da[i];
     __syncthreads();
-    for (int idx = tid; idx < RT * D; idx += kBwdThreads) {
-      const int rr = idx / D, d = idx % D, r = r0 + rr;
-      const int64_t g = r / a.Q, t = r % a.Q;
-      q_s[rr][d] = (r < a.R && t < n)
-                       ? a.query[((b * a.Hq + kvh * a.G + g) * a.Q + t) * D + d] : 0.f;
-    }
-    for (int idx = tid; idx < RT * DV; idx += kBwdThreads) {
-      const int rr = idx / DV, d = idx % DV, r = r0 + rr;
-      const int64_t g = r / a.Q, t = r % a.Q;
-      o_s[rr][d] = (a.d_ctx && r < a.R && t < n)
-                       ? a.d_ctx[((b * a.Hq + kvh * a.G + g) * a.Q + t) * DV + d] : 0.f;
-    }
-    __syncthreads();
-    for (int rr = wave; rr < RT; rr += W) {
-      const int r = r0 + rr;
-      if (r >= a.R) break;
-      const int64_t g = r / a.Q, t = r % a.Q;
-      if (t >= n) continue;
-      const int64_t row = (b * a.Hq + kvh * a.G + g) * a.Q + t;
-      const bool vis = j <= len + t;
-      double sc = 0, dp = 0;
-      if (vis) {
-        sc = static_cast<double>(a.scale) * dot_f64<D>(q_s[rr], k_s[lane]);
-        dp = (a.d_att ? static_cast<double>(a.d_att[row * a.M + j]) : 0.0) +
-             dot_f64<DV>(o_s[rr], v_s[lane]);
-      }
+    if (r0 + step < a.R) bwd_fetch_tile<D, DV>(a, b, kvh, len, n, r0 + step, j, false, nx);
+    bwd_f64x4 s, dov;
+    bwd_scores<D, DV>(q_s, o_s, k_s, v_s, wave, li, lq, s, dov);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = r0 + 4 * i + lq;
+      const int64_t t = r % a.Q;
+      const bool vis = r < a.R && t < n && j <= len + t;
+      const double sc = scale * s[i];
+      const double dp = vis ? dov[i] + static_cast<double>(da[i]) : 0.0;
       double m = vis ? sc : -INFINITY;
-      for (int o = kWave / 2; o > 0; o >>= 1) {
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
         const double y = __shfl_xor(m, o);
         m = y > m ? y : m;
       }
       const double e = vis ? exp(sc - m) : 0.0;
       double l = e, pd = e * dp;
-      for (int o = kWave / 2; o > 0; o >>= 1) {
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
         l += __shfl_xor(l, o);
         pd += __shfl_xor(pd, o);
       }
-      if (lane == 0) {
+      if (li == 0) {
+        part_s[wave][4 * i + lq][0] = m;
+        part_s[wave][4 * i + lq][1] = l;
+        part_s[wave][4 * i + lq][2] = pd;
+      }
+    }
+    __syncthreads();
+    if (tid < RT) {  // the four strips of each row merged
+      const int r = r0 + tid;
+      const int64_t t = r % a.Q;
+      if (r < a.R && t < n) {
+        double m = -INFINITY, l = 0, pd = 0;
+#pragma unroll
+        for (int w = 0; w < W; w++) m = part_s[w][tid][0] > m ? part_s[w][tid][0] : m;
+#pragma unroll
+        for (int w = 0; w < W; w++) {
+          const double mw = part_s[w][tid][0];
+          const double f = mw == -INFINITY ? 0.0 : exp(mw - m);
+          l += part_s[w][tid][1] * f;
+          pd += part_s[w][tid][2] * f;
+        }
         double* out = a.ws_part + ((grp * a.nchunk + c) * a.R + r) * 4;
         out[0] = m;
         out[1] = l;
@@ -222,121 +377,112 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(BwdArgs a) {
   }
 }
 
-// One workgroup per (b, KV head, chunk of kBwdSlots slots).
+// One workgroup per (b, KV head, chunk of kBwdSlots slots, column group):
+// dS for the chunk's slots and every packed row, and for the group's
+// columns the slot gradients of the chunk and the chunk's share of every
+// row's dq.
 template <int D, int DV>
 __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
-  constexpr int C = kBwdSlots, RT = kBwdRowTile;
-  __shared__ float k_s[C][D + 1];
-  __shared__ float v_s[C][DV + 1];
-  __shared__ float q_s[RT][D + 1];
-  __shared__ float o_s[RT][DV + 1];   // dO rows
-  __shared__ double ds_s[RT][C + 1];  // scale * dS
-  __shared__ float p_s[RT][C + 1];    // P (0 where not visible)
-  const int tid = threadIdx.x;
-  const int64_t c = blockIdx.x % a.nchunk;
-  const int64_t grp = blockIdx.x / a.nchunk;
+  constexpr int C = kBwdSlots, RT = kBwdRowTile, W = kBwdThreads / kWave;
+  constexpr int KP = bwd_pitch<D>(), VP = bwd_pitch<DV>(), SP = C + 1;
+  constexpr int CG = bwd_col_groups<D, DV>();
+  constexpr int DT = D / 16 / CG, VT = DV / 16 / CG;  // this workgroup's 16-column tiles
+  static_assert(C == 16 * W && RT == 16 && D % (16 * CG) == 0 && DV % (16 * CG) == 0, "tile shape");
+  __shared__ float k_s[C * KP];
+  __shared__ float v_s[C * VP];
+  __shared__ float q_s[RT * KP];
+  __shared__ float o_s[RT * VP];
+  __shared__ double ds_s[RT * SP];  // scale * dS (0 where not visible)
+  __shared__ double p_s[RT * SP];   // P (0 where not visible)
+  __shared__ double st_s[RT][3];    // the rows' m, l and sum_k P_k dP_k
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int li = lane % 16, lq = lane / 16;
+  const int cg = static_cast<int>(blockIdx.x % CG);
+  const int64_t c = (blockIdx.x / CG) % a.nchunk;
+  const int64_t grp = blockIdx.x / CG / a.nchunk;
   const int64_t b = grp / a.Hk, kvh = grp % a.Hk;
   int64_t len, n;
   bwd_row_info(a, b, &len, &n);
   const int64_t s0 = c * C;
+  const int dc0 = cg * DT * 16, vc0 = cg * VT * 16;  // first dK'/dq and dV' column
   // slots with any attention gradient (none on a row that appends nothing
   // or is rejected; then only the pass-through below remains)
   const int64_t nvis = n > 0 ? len + n : 0;
-
-  // K', V' rows of the chunk (zeros past the visible slots)
-  for (int idx = tid; idx < C * D; idx += kBwdThreads) {
-    const int s = idx / D, d = idx % D;
-    const int64_t j = s0 + s;
-    float x = 0.f;
-    if (j < nvis)
-      x = j < len ? a.kc[((grp * a.M) + j) * D + d] : a.new_key[(grp * a.Q + (j - len)) * D + d];
-    k_s[s][d] = x;
-  }
-  for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
-    const int s = idx / DV, d = idx % DV;
-    const int64_t j = s0 + s;
-    float x = 0.f;
-    if (j < nvis)
-      x = j < len ? a.vc[((grp * a.M) + j) * DV + d]
-                  : a.new_value[(grp * a.Q + (j - len)) * DV + d];
-    v_s[s][d] = x;
-  }
-
-  // slot gradients: thread owns (slot, dim) pairs of dK' and dV'
-  constexpr int KPT = (C * D + kBwdThreads - 1) / kBwdThreads;
-  constexpr int VPT = (C * DV + kBwdThreads - 1) / kBwdThreads;
-  float gk[KPT], gv[VPT];
-#pragma unroll
-  for (int i = 0; i < KPT; i++) gk[i] = 0.f;
-#pragma unroll
-  for (int i = 0; i < VPT; i++) gv[i] = 0.f;
-
   const bool any = s0 < nvis;  // nvis <= M
+  const int64_t j = s0 + 16 * wave + li;  // this lane's slot in the score tile
+  BwdTileRegs<D, DV> nx;  // the next tile's inputs, loading while this one computes
+  if (any) {
+    bwd_fetch_tile<D, DV>(a, b, kvh, len, n, 0, j, true, nx);
+    bwd_stage_kv<D, DV>(a, grp, len, nvis, s0, k_s, v_s);
+  }
+
+  // dK', dV' of this wave's 16 slots: gk[dt][i] = dK'[slot 16 w + 4 i + lq][dc0 + 16 dt + li]
+  bwd_f64x4 gk[DT], gv[VT];
+#pragma unroll
+  for (int dt = 0; dt < DT; dt++) gk[dt] = bwd_f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int vt = 0; vt < VT; vt++) gv[vt] = bwd_f64x4{0.0, 0.0, 0.0, 0.0};
+
+  const double scale = a.scale;
   for (int r0 = 0; any && r0 < a.R; r0 += RT) {
-    __syncthreads();  // the previous tile's LDS is no longer read
-    for (int idx = tid; idx < RT * D; idx += kBwdThreads) {
-      const int rr = idx / D, d = idx % D, r = r0 + rr;
-      const int64_t g = r / a.Q, t = r % a.Q;
-      q_s[rr][d] = (r < a.R && t < n)
-                       ? a.query[((b * a.Hq + kvh * a.G + g) * a.Q + t) * D + d] : 0.f;
+    __syncthreads();  // the previous tile is no longer read
+    bwd_commit_tile<D, DV>(nx, q_s, o_s);
+    if (tid < RT) {
+      st_s[tid][0] = nx.st[0];
+      st_s[tid][1] = nx.st[1];
+      st_s[tid][2] = nx.st[2];
     }
-    for (int idx = tid; idx < RT * DV; idx += kBwdThreads) {
-      const int rr = idx / DV, d = idx % DV, r = r0 + rr;
-      const int64_t g = r / a.Q, t = r % a.Q;
-      o_s[rr][d] = (a.d_ctx && r < a.R && t < n)
-                       ? a.d_ctx[((b * a.Hq + kvh * a.G + g) * a.Q + t) * DV + d] : 0.f;
-    }
-    __syncthreads();
-    // dS for (row, slot), in fp64: P from the score and the row's m, l;
-    // dP = dA + dO . V'_j
-    for (int idx = tid; idx < RT * C; idx += kBwdThreads) {
-      const int rr = idx / C, s = idx % C, r = r0 + rr;
-      const int64_t g = r / a.Q, t = r % a.Q, j = s0 + s;
-      double ds = 0, p = 0;
-      if (r < a.R && t < n && j <= len + t) {
-        const int64_t row = (b * a.Hq + kvh * a.G + g) * a.Q + t;
-        const double* st = a.ws_row + row * 4;
-        const double sc = dot_f64<D>(q_s[rr], k_s[s]);
-        p = exp(static_cast<double>(a.scale) * sc - st[0]) / st[1];
-        const double dp = (a.d_att ? static_cast<double>(a.d_att[row * a.M + j]) : 0.0) +
-                          dot_f64<DV>(o_s[rr], v_s[s]);
-        ds = static_cast<double>(a.scale) * p * (dp - st[2]);
-      }
-      ds_s[rr][s] = ds;
-      p_s[rr][s] = static_cast<float>(p);
-    }
-    __syncthreads();
-    // dK'_j += sum_r ds q_r, dV'_j += sum_r p dO_r
+    float da[4];
 #pragma unroll
-    for (int i = 0; i < KPT; i++) {
-      const int idx = tid + i * kBwdThreads;
-      if (idx < C * D) {
-        const int s = idx / D, d = idx % D;
-        float acc = gk[i];
-        for (int rr = 0; rr < RT; rr++) acc += static_cast<float>(ds_s[rr][s]) * q_s[rr][d];
-        gk[i] = acc;
-      }
-    }
+    for (int i = 0; i < 4; i++) da[i] = nx.da[i];
+    __syncthreads();
+    if (r0 + RT < a.R) bwd_fetch_tile<D, DV>(a, b, kvh, len, n, r0 + RT, j, true, nx);
+    // P from the score and the row's m, l; dS = P (dP - sum_k P_k dP_k)
+    bwd_f64x4 s, dov;
+    bwd_scores<D, DV>(q_s, o_s, k_s, v_s, wave, li, lq, s, dov);
 #pragma unroll
-    for (int i = 0; i < VPT; i++) {
-      const int idx = tid + i * kBwdThreads;
-      if (idx < C * DV) {
-        const int s = idx / DV, d = idx % DV;
-        float acc = gv[i];
-        for (int rr = 0; rr < RT; rr++) acc += p_s[rr][s] * o_s[rr][d];
-        gv[i] = acc;
+    for (int i = 0; i < 4; i++) {
+      const int rr = 4 * i + lq, r = r0 + rr;
+      const int64_t t = r % a.Q;
+      const bool vis = r < a.R && t < n && j <= len + t;
+      double p = 0.0, ds = 0.0;
+      if (vis) {
+        const double dp = dov[i] + static_cast<double>(da[i]);
+        p = exp(scale * s[i] - st_s[rr][0]) / st_s[rr][1];
+        ds = scale * p * (dp - st_s[rr][2]);
       }
+      ds_s[rr * SP + 16 * wave + li] = ds;
+      p_s[rr * SP + 16 * wave + li] = p;
     }
-    // dq partial of this chunk: sum_j ds_j K'_j
-    for (int idx = tid; idx < RT * D; idx += kBwdThreads) {
-      const int rr = idx / D, d = idx % D, r = r0 + rr;
-      if (r >= a.R) continue;
-      double acc0 = 0, acc1 = 0;
-      for (int s = 0; s < C; s += 2) {
-        acc0 += ds_s[rr][s] * k_s[s][d];
-        acc1 += ds_s[rr][s + 1] * k_s[s + 1][d];
+    __syncthreads();  // dq below reads every wave's slots
+    // dK'_j += sum_r scale dS q_r and dV'_j += sum_r P dO_r over the tile's rows
+#pragma unroll
+    for (int kk = 0; kk < RT / 4; kk++) {
+      const double dsa = ds_s[(4 * kk + lq) * SP + 16 * wave + li];
+      const double pa = p_s[(4 * kk + lq) * SP + 16 * wave + li];
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++)
+        gk[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+            dsa, static_cast<double>(q_s[(4 * kk + lq) * KP + dc0 + 16 * dt + li]), gk[dt], 0, 0, 0);
+#pragma unroll
+      for (int vt = 0; vt < VT; vt++)
+        gv[vt] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+            pa, static_cast<double>(o_s[(4 * kk + lq) * VP + vc0 + 16 * vt + li]), gv[vt], 0, 0, 0);
+    }
+    // the chunk's share of dq = sum_j scale dS_j K'_j over this workgroup's
+    // columns: wave w takes its 16-column tiles w, w + W, ...
+    for (int dt = wave; dt < DT; dt += W) {
+      bwd_f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int kk = 0; kk < C / 4; kk++)
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(
+            ds_s[li * SP + 4 * kk + lq],
+            static_cast<double>(k_s[(4 * kk + lq) * KP + dc0 + 16 * dt + li]), acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int r = r0 + 4 * i + lq;
+        if (r < a.R) a.ws_dq[((grp * a.nchunk + c) * a.R + r) * D + dc0 + 16 * dt + li] = acc[i];
       }
-      a.ws_dq[((grp * a.nchunk + c) * a.R + r) * D + d] = acc0 + acc1;
     }
   }
 
@@ -344,43 +490,37 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
   // -> the appended rows' gradient (the cache entry gets 0), the rest ->
   // the pass-through alone
 #pragma unroll
-  for (int i = 0; i < KPT; i++) {
-    const int idx = tid + i * kBwdThreads;
-    if (idx < C * D) {
-      const int s = idx / D, d = idx % D;
-      const int64_t j = s0 + s;
-      if (j < a.M) {
-        const int64_t at = (grp * a.M + j) * D + d;
-        const float total = gk[i] + (a.d_kc_out ? a.d_kc_out[at] : 0.f);
-        if (j >= len && j < len + n) {
-          a.g_new_key[(grp * a.Q + (j - len)) * D + d] = total;
-          a.g_kc[at] = 0.f;
-        } else {
-          a.g_kc[at] = total;
-        }
+  for (int i = 0; i < 4; i++) {
+    const int64_t js = s0 + 16 * wave + 4 * i + lq;
+    if (js >= a.M) continue;
+    const bool appended = js >= len && js < len + n;
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) {
+      const int d = dc0 + 16 * dt + li;
+      const int64_t at = (grp * a.M + js) * D + d;
+      const float total = static_cast<float>(gk[dt][i]) + (a.d_kc_out ? a.d_kc_out[at] : 0.f);
+      if (appended) {
+        a.g_new_key[(grp * a.Q + (js - len)) * D + d] = total;
+        a.g_kc[at] = 0.f;
+      } else {
+        a.g_kc[at] = total;
       }
     }
-  }
 #pragma unroll
-  for (int i = 0; i < VPT; i++) {
-    const int idx = tid + i * kBwdThreads;
-    if (idx < C * DV) {
-      const int s = idx / DV, d = idx % DV;
-      const int64_t j = s0 + s;
-      if (j < a.M) {
-        const int64_t at = (grp * a.M + j) * DV + d;
-        const float total = gv[i] + (a.d_vc_out ? a.d_vc_out[at] : 0.f);
-        if (j >= len && j < len + n) {
-          a.g_new_value[(grp * a.Q + (j - len)) * DV + d] = total;
-          a.g_vc[at] = 0.f;
-        } else {
-          a.g_vc[at] = total;
-        }
+    for (int vt = 0; vt < VT; vt++) {
+      const int d = vc0 + 16 * vt + li;
+      const int64_t at = (grp * a.M + js) * DV + d;
+      const float total = static_cast<float>(gv[vt][i]) + (a.d_vc_out ? a.d_vc_out[at] : 0.f);
+      if (appended) {
+        a.g_new_value[(grp * a.Q + (js - len)) * DV + d] = total;
+        a.g_vc[at] = 0.f;
+      } else {
+        a.g_vc[at] = total;
       }
     }
   }
   // appended rows that do not exist (t >= n, rejected rows): zero gradient
-  if (c == 0) {
+  if (c == 0 && cg == 0) {
     for (int64_t idx = tid; idx < (a.Q - n) * D; idx += kBwdThreads)
       a.g_new_key[(grp * a.Q + n + idx / D) * D + idx % D] = 0.f;
     for (int64_t idx = tid; idx < (a.Q - n) * DV; idx += kBwdThreads)

@@ -14,6 +14,8 @@ namespace {
 
 using namespace kvc_host;
 
+constexpr int64_t kMaxBwdWorkgroups = int64_t(1) << 30;
+
 // Backward: fp32, head sizes with a chunk kernel below.
 struct BwdEntry {
   int64_t D, Dv;
@@ -23,14 +25,14 @@ struct BwdEntry {
 template <int D, int DV>
 void launch_bwd_stats(const kvc::BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((kvc::bwd_stats_kernel<D, DV>),
-                     dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk)), dim3(kvc::kBwdThreads), 0,
-                     s, a);
+                     dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk * a.row_groups)),
+                     dim3(kvc::kBwdThreads), 0, s, a);
 }
 template <int D, int DV>
 void launch_bwd_chunk(const kvc::BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((kvc::bwd_chunk_kernel<D, DV>),
-                     dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk)), dim3(kvc::kBwdThreads), 0,
-                     s, a);
+                     dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk * kvc::bwd_col_groups<D, DV>())),
+                     dim3(kvc::kBwdThreads), 0, s, a);
 }
 const BwdEntry kBwdTable[] = {
     {64, 64, &launch_bwd_stats<64, 64>, &launch_bwd_chunk<64, 64>},
@@ -106,6 +108,16 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
   a.G = static_cast<int32_t>(d->Hq / d->Hk);
   a.R = static_cast<int32_t>(a.G * d->Q);
   a.nchunk = (d->M + kvc::kBwdSlots - 1) / kvc::kBwdSlots;
+  {
+    const int64_t tiles = (a.R + kvc::kBwdRowTile - 1) / kvc::kBwdRowTile;
+    a.row_groups = static_cast<int32_t>(tiles < 1 ? 1 : tiles < kvc::kBwdMaxRowGroups ? tiles : kvc::kBwdMaxRowGroups);
+  }
+  {  // the chunk grids (chunks x row or column groups) must fit one launch
+    int64_t x;
+    if (!mul_ok(d->B * d->Hk, a.nchunk, kMaxElems, &x) ||
+        !mul_ok(x, a.row_groups > 4 ? a.row_groups : 4, kMaxBwdWorkgroups, &x))
+      return KVC_ERR_SHAPE;
+  }
   a.scale = static_cast<float>(sc);
   a.query = static_cast<const float*>(query);
   a.new_key = static_cast<const float*>(new_key);
