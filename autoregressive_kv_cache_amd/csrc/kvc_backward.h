@@ -36,7 +36,10 @@ namespace kvc {
 
 constexpr int kBwdThreads = 256;
 constexpr int kBwdSlots = 64;   // slots per chunk workgroup
-constexpr int kBwdRowTile = 16; // packed rows staged in LDS at a time
+constexpr int kBwdRowTile = 16;   // packed rows per tile in bwd_stats
+// bwd_chunk takes 32 packed rows per tile (two 16-row blocks, independent
+// product chains, half the barriers) when a head has more than 16, else 16
+constexpr int kBwdChunkRowsWide = 32;
 constexpr int kBwdMaxRowGroups = 16;
 
 // bwd_chunk: workgroups per chunk, each over a share of the 16-column tiles
@@ -156,21 +159,20 @@ __device__ inline void bwd_stage_kv(const BwdArgs& a, int64_t grp, int64_t len, 
 // are not valid), this lane's four attention-gradient entries (rows
 // 4 i + l / 16 of the tile, its slot j; 0 where not visible), and for
 // threads below 16 the row's m, l and sum P dP (bwd_chunk).
-template <int D, int DV>
+template <int D, int DV, int RT>
 struct BwdTileRegs {
-  static constexpr int NQ = (kBwdRowTile * D + kBwdThreads - 1) / kBwdThreads;
-  static constexpr int NO = (kBwdRowTile * DV + kBwdThreads - 1) / kBwdThreads;
+  static constexpr int NQ = (RT * D + kBwdThreads - 1) / kBwdThreads;
+  static constexpr int NO = (RT * DV + kBwdThreads - 1) / kBwdThreads;
   float q[NQ], o[NO];
-  float da[4];
+  float da[RT / 4];  // [16-row block][i]
   double st[3];
 };
 
-template <int D, int DV>
+template <int D, int DV, int RT>
 __device__ inline void bwd_fetch_tile(const BwdArgs& a, int64_t b, int64_t kvh, int64_t len,
                                       int64_t n, int r0, int64_t j, bool stats,
-                                      BwdTileRegs<D, DV>& x) {
-  using X = BwdTileRegs<D, DV>;
-  constexpr int RT = kBwdRowTile;
+                                      BwdTileRegs<D, DV, RT>& x) {
+  using X = BwdTileRegs<D, DV, RT>;
   const int tid = threadIdx.x, lq = (tid % kWave) / 16;
 #pragma unroll
   for (int i = 0; i < X::NQ; i++) {
@@ -189,11 +191,11 @@ __device__ inline void bwd_fetch_tile(const BwdArgs& a, int64_t b, int64_t kvh, 
                  ? a.d_ctx[((b * a.Hq + kvh * a.G + g) * a.Q + t) * DV + d] : 0.f;
   }
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int r = r0 + 4 * i + lq;
+  for (int k = 0; k < RT / 4; k++) {
+    const int r = r0 + 16 * (k / 4) + 4 * (k % 4) + lq;
     const int64_t g = r / a.Q, t = r % a.Q;
     const bool vis = a.d_att && r < a.R && t < n && j <= len + t;
-    x.da[i] = vis ? a.d_att[((b * a.Hq + kvh * a.G + g) * a.Q + t) * a.M + j] : 0.f;
+    x.da[k] = vis ? a.d_att[((b * a.Hq + kvh * a.G + g) * a.Q + t) * a.M + j] : 0.f;
   }
   if (stats && tid < RT) {
     const int r = r0 + tid;
@@ -207,10 +209,10 @@ __device__ inline void bwd_fetch_tile(const BwdArgs& a, int64_t b, int64_t kvh, 
 }
 
 // q and dO of the tile into LDS (row pitch bwd_pitch).
-template <int D, int DV>
-__device__ inline void bwd_commit_tile(const BwdTileRegs<D, DV>& x, float* q_s, float* o_s) {
-  using X = BwdTileRegs<D, DV>;
-  constexpr int RT = kBwdRowTile, KP = bwd_pitch<D>(), VP = bwd_pitch<DV>();
+template <int D, int DV, int RT>
+__device__ inline void bwd_commit_tile(const BwdTileRegs<D, DV, RT>& x, float* q_s, float* o_s) {
+  using X = BwdTileRegs<D, DV, RT>;
+  constexpr int KP = bwd_pitch<D>(), VP = bwd_pitch<DV>();
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < X::NQ; i++) {
@@ -273,17 +275,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_stats_kernel(BwdArgs a) {
   const double scale = a.scale;
   const int64_t j = s0 + 16 * wave + li;  // this lane's slot
   const int step = a.row_groups * RT;
-  BwdTileRegs<D, DV> nx;  // the next tile's inputs, loading while this one computes
-  bwd_fetch_tile<D, DV>(a, b, kvh, len, n, rg * RT, j, false, nx);
+  BwdTileRegs<D, DV, RT> nx;  // the next tile's inputs, loading while this one computes
+  bwd_fetch_tile<D, DV, RT>(a, b, kvh, len, n, rg * RT, j, false, nx);
   bwd_stage_kv<D, DV>(a, grp, len, nvis, s0, k_s, v_s);
   for (int r0 = rg * RT; r0 < a.R; r0 += step) {
     __syncthreads();  // the previous tile is no longer read
-    bwd_commit_tile<D, DV>(nx, q_s, o_s);
+    bwd_commit_tile<D, DV, RT>(nx, q_s, o_s);
     float da[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) da[i] = nx.da[i];
     __syncthreads();
-    if (r0 + step < a.R) bwd_fetch_tile<D, DV>(a, b, kvh, len, n, r0 + step, j, false, nx);
+    if (r0 + step < a.R) bwd_fetch_tile<D, DV, RT>(a, b, kvh, len, n, r0 + step, j, false, nx);
     bwd_f64x4 s, dov;
     bwd_scores<D, DV>(q_s, o_s, k_s, v_s, wave, li, lq, s, dov);
 #pragma unroll
@@ -381,13 +383,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(BwdArgs a) {
 // dS for the chunk's slots and every packed row, and for the group's
 // columns the slot gradients of the chunk and the chunk's share of every
 // row's dq.
-template <int D, int DV>
+template <int D, int DV, int RT>
 __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
-  constexpr int C = kBwdSlots, RT = kBwdRowTile, W = kBwdThreads / kWave;
+  constexpr int C = kBwdSlots, NB = RT / 16, W = kBwdThreads / kWave;
   constexpr int KP = bwd_pitch<D>(), VP = bwd_pitch<DV>(), SP = C + 1;
   constexpr int CG = bwd_col_groups<D, DV>();
   constexpr int DT = D / 16 / CG, VT = DV / 16 / CG;  // this workgroup's 16-column tiles
-  static_assert(C == 16 * W && RT == 16 && D % (16 * CG) == 0 && DV % (16 * CG) == 0, "tile shape");
+  static_assert(C == 16 * W && RT % 16 == 0 && D % (16 * CG) == 0 && DV % (16 * CG) == 0, "tile shape");
   __shared__ float k_s[C * KP];
   __shared__ float v_s[C * VP];
   __shared__ float q_s[RT * KP];
@@ -410,9 +412,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
   const int64_t nvis = n > 0 ? len + n : 0;
   const bool any = s0 < nvis;  // nvis <= M
   const int64_t j = s0 + 16 * wave + li;  // this lane's slot in the score tile
-  BwdTileRegs<D, DV> nx;  // the next tile's inputs, loading while this one computes
+  BwdTileRegs<D, DV, RT> nx;  // the next tile's inputs, loading while this one computes
   if (any) {
-    bwd_fetch_tile<D, DV>(a, b, kvh, len, n, 0, j, true, nx);
+    bwd_fetch_tile<D, DV, RT>(a, b, kvh, len, n, 0, j, true, nx);
     bwd_stage_kv<D, DV>(a, grp, len, nvis, s0, k_s, v_s);
   }
 
@@ -426,33 +428,40 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
   const double scale = a.scale;
   for (int r0 = 0; any && r0 < a.R; r0 += RT) {
     __syncthreads();  // the previous tile is no longer read
-    bwd_commit_tile<D, DV>(nx, q_s, o_s);
+    bwd_commit_tile<D, DV, RT>(nx, q_s, o_s);
     if (tid < RT) {
       st_s[tid][0] = nx.st[0];
       st_s[tid][1] = nx.st[1];
       st_s[tid][2] = nx.st[2];
     }
-    float da[4];
+    float da[RT / 4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) da[i] = nx.da[i];
+    for (int k = 0; k < RT / 4; k++) da[k] = nx.da[k];
     __syncthreads();
-    if (r0 + RT < a.R) bwd_fetch_tile<D, DV>(a, b, kvh, len, n, r0 + RT, j, true, nx);
-    // P from the score and the row's m, l; dS = P (dP - sum_k P_k dP_k)
-    bwd_f64x4 s, dov;
-    bwd_scores<D, DV>(q_s, o_s, k_s, v_s, wave, li, lq, s, dov);
+    if (r0 + RT < a.R) bwd_fetch_tile<D, DV, RT>(a, b, kvh, len, n, r0 + RT, j, true, nx);
+    // P from the score and the row's m, l; dS = P (dP - sum_k P_k dP_k);
+    // the 16-row blocks' products are independent chains
+    bwd_f64x4 s[NB], dov[NB];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int rr = 4 * i + lq, r = r0 + rr;
-      const int64_t t = r % a.Q;
-      const bool vis = r < a.R && t < n && j <= len + t;
-      double p = 0.0, ds = 0.0;
-      if (vis) {
-        const double dp = dov[i] + static_cast<double>(da[i]);
-        p = exp(scale * s[i] - st_s[rr][0]) / st_s[rr][1];
-        ds = scale * p * (dp - st_s[rr][2]);
+    for (int nb = 0; nb < NB; nb++)
+      bwd_scores<D, DV>(q_s + nb * 16 * KP, o_s + nb * 16 * VP, k_s, v_s, wave, li, lq, s[nb],
+                        dov[nb]);
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int rr = 16 * nb + 4 * i + lq, r = r0 + rr;
+        const int64_t t = r % a.Q;
+        const bool vis = r < a.R && t < n && j <= len + t;
+        double p = 0.0, ds = 0.0;
+        if (vis) {
+          const double dp = dov[nb][i] + static_cast<double>(da[4 * nb + i]);
+          p = exp(scale * s[nb][i] - st_s[rr][0]) / st_s[rr][1];
+          ds = scale * p * (dp - st_s[rr][2]);
+        }
+        ds_s[rr * SP + 16 * wave + li] = ds;
+        p_s[rr * SP + 16 * wave + li] = p;
       }
-      ds_s[rr * SP + 16 * wave + li] = ds;
-      p_s[rr * SP + 16 * wave + li] = p;
     }
     __syncthreads();  // dq below reads every wave's slots
     // dK'_j += sum_r scale dS q_r and dV'_j += sum_r P dO_r over the tile's rows
@@ -472,16 +481,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     // the chunk's share of dq = sum_j scale dS_j K'_j over this workgroup's
     // columns: wave w takes its 16-column tiles w, w + W, ...
     for (int dt = wave; dt < DT; dt += W) {
-      bwd_f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+      bwd_f64x4 acc[NB];
 #pragma unroll
-      for (int kk = 0; kk < C / 4; kk++)
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(
-            ds_s[li * SP + 4 * kk + lq],
-            static_cast<double>(k_s[(4 * kk + lq) * KP + dc0 + 16 * dt + li]), acc, 0, 0, 0);
+      for (int nb = 0; nb < NB; nb++) acc[nb] = bwd_f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int r = r0 + 4 * i + lq;
-        if (r < a.R) a.ws_dq[((grp * a.nchunk + c) * a.R + r) * D + dc0 + 16 * dt + li] = acc[i];
+      for (int kk = 0; kk < C / 4; kk++) {
+        const double kb = static_cast<double>(k_s[(4 * kk + lq) * KP + dc0 + 16 * dt + li]);
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+          acc[nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(ds_s[(16 * nb + li) * SP + 4 * kk + lq],
+                                                         kb, acc[nb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int r = r0 + 16 * nb + 4 * i + lq;
+          if (r < a.R)
+            a.ws_dq[((grp * a.nchunk + c) * a.R + r) * D + dc0 + 16 * dt + li] = acc[nb][i];
+        }
       }
     }
   }

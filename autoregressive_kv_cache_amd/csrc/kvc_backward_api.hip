@@ -30,9 +30,13 @@ void launch_bwd_stats(const kvc::BwdArgs& a, hipStream_t s) {
 }
 template <int D, int DV>
 void launch_bwd_chunk(const kvc::BwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((kvc::bwd_chunk_kernel<D, DV>),
-                     dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk * kvc::bwd_col_groups<D, DV>())),
-                     dim3(kvc::kBwdThreads), 0, s, a);
+  const dim3 grid(static_cast<unsigned>(a.B * a.Hk * a.nchunk * kvc::bwd_col_groups<D, DV>()));
+  if (a.R > kvc::kBwdRowTile)
+    hipLaunchKernelGGL((kvc::bwd_chunk_kernel<D, DV, kvc::kBwdChunkRowsWide>), grid,
+                       dim3(kvc::kBwdThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((kvc::bwd_chunk_kernel<D, DV, kvc::kBwdRowTile>), grid,
+                       dim3(kvc::kBwdThreads), 0, s, a);
 }
 const BwdEntry kBwdTable[] = {
     {64, 64, &launch_bwd_stats<64, 64>, &launch_bwd_chunk<64, 64>},
