@@ -136,20 +136,37 @@ constexpr int bwd_pitch() {
   return N + 4;
 }
 
-// K', V' rows of the chunk starting at slot s0 (zeros past nvis).
+// K', V' rows of the chunk starting at slot s0 (zeros past nvis).  Every
+// load is issued before the first LDS store, so the loads overlap.
 template <int D, int DV>
 __device__ inline void bwd_stage_kv(const BwdArgs& a, int64_t grp, int64_t len, int64_t nvis,
                                     int64_t s0, float* k_s, float* v_s) {
   constexpr int C = kBwdSlots, KP = bwd_pitch<D>(), VP = bwd_pitch<DV>();
-  for (int idx = threadIdx.x; idx < C * D; idx += kBwdThreads) {
-    const int sl = idx / D, d = idx % D;
+  constexpr int NK = C * D / kBwdThreads, NV = C * DV / kBwdThreads;
+  static_assert(C * D % kBwdThreads == 0 && C * DV % kBwdThreads == 0, "staging shape");
+  const int tid = threadIdx.x;
+  float kx[NK], vx[NV];
+#pragma unroll
+  for (int i = 0; i < NK; i++) {
+    const int idx = tid + i * kBwdThreads, sl = idx / D, d = idx % D;
     const int64_t j = s0 + sl;
-    k_s[sl * KP + d] = j < nvis ? bwd_key_row(a, grp, len, j)[d] : 0.f;
+    kx[i] = j < nvis ? bwd_key_row(a, grp, len, j)[d] : 0.f;
   }
-  for (int idx = threadIdx.x; idx < C * DV; idx += kBwdThreads) {
-    const int sl = idx / DV, d = idx % DV;
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int idx = tid + i * kBwdThreads, sl = idx / DV, d = idx % DV;
     const int64_t j = s0 + sl;
-    v_s[sl * VP + d] = j < nvis ? bwd_value_row(a, grp, len, j)[d] : 0.f;
+    vx[i] = j < nvis ? bwd_value_row(a, grp, len, j)[d] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < NK; i++) {
+    const int idx = tid + i * kBwdThreads;
+    k_s[(idx / D) * KP + idx % D] = kx[i];
+  }
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int idx = tid + i * kBwdThreads;
+    v_s[(idx / DV) * VP + idx % DV] = vx[i];
   }
 }
 
@@ -178,7 +195,7 @@ __device__ inline void bwd_fetch_tile(const BwdArgs& a, int64_t b, int64_t kvh, 
   for (int i = 0; i < X::NQ; i++) {
     const int idx = tid + i * kBwdThreads;
     const int rr = idx / D, d = idx % D, r = r0 + rr;
-    const int64_t g = r / a.Q, t = r % a.Q;
+    const int g = r / static_cast<int>(a.Q), t = r % static_cast<int>(a.Q);
     x.q[i] = (idx < RT * D && r < a.R && t < n)
                  ? a.query[((b * a.Hq + kvh * a.G + g) * a.Q + t) * D + d] : 0.f;
   }
@@ -186,20 +203,20 @@ __device__ inline void bwd_fetch_tile(const BwdArgs& a, int64_t b, int64_t kvh, 
   for (int i = 0; i < X::NO; i++) {
     const int idx = tid + i * kBwdThreads;
     const int rr = idx / DV, d = idx % DV, r = r0 + rr;
-    const int64_t g = r / a.Q, t = r % a.Q;
+    const int g = r / static_cast<int>(a.Q), t = r % static_cast<int>(a.Q);
     x.o[i] = (a.d_ctx && idx < RT * DV && r < a.R && t < n)
                  ? a.d_ctx[((b * a.Hq + kvh * a.G + g) * a.Q + t) * DV + d] : 0.f;
   }
 #pragma unroll
   for (int k = 0; k < RT / 4; k++) {
     const int r = r0 + 16 * (k / 4) + 4 * (k % 4) + lq;
-    const int64_t g = r / a.Q, t = r % a.Q;
+    const int g = r / static_cast<int>(a.Q), t = r % static_cast<int>(a.Q);
     const bool vis = a.d_att && r < a.R && t < n && j <= len + t;
     x.da[k] = vis ? a.d_att[((b * a.Hq + kvh * a.G + g) * a.Q + t) * a.M + j] : 0.f;
   }
   if (stats && tid < RT) {
     const int r = r0 + tid;
-    const int64_t g = r / a.Q, t = r % a.Q;
+    const int g = r / static_cast<int>(a.Q), t = r % static_cast<int>(a.Q);
     const bool ok = r < a.R && t < n;
     const double* st = a.ws_row + ((b * a.Hq + kvh * a.G + g) * a.Q + t) * 4;
     x.st[0] = ok ? st[0] : 0.0;
@@ -291,7 +308,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_stats_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int r = r0 + 4 * i + lq;
-      const int64_t t = r % a.Q;
+      const int t = r % static_cast<int>(a.Q);
       const bool vis = r < a.R && t < n && j <= len + t;
       const double sc = scale * s[i];
       const double dp = vis ? dov[i] + static_cast<double>(da[i]) : 0.0;
@@ -317,7 +334,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_stats_kernel(BwdArgs a) {
     __syncthreads();
     if (tid < RT) {  // the four strips of each row merged
       const int r = r0 + tid;
-      const int64_t t = r % a.Q;
+      const int t = r % static_cast<int>(a.Q);
       if (r < a.R && t < n) {
         double m = -INFINITY, l = 0, pd = 0;
 #pragma unroll
@@ -451,7 +468,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int rr = 16 * nb + 4 * i + lq, r = r0 + rr;
-        const int64_t t = r % a.Q;
+        const int t = r % static_cast<int>(a.Q);
         const bool vis = r < a.R && t < n && j <= len + t;
         double p = 0.0, ds = 0.0;
         if (vis) {
@@ -506,7 +523,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
 
   // slot gradients out: kept slots -> the cache gradient, overwritten ones
   // -> the appended rows' gradient (the cache entry gets 0), the rest ->
-  // the pass-through alone
+  // the pass-through alone.  The pass-through values are all loaded before
+  // the first store: the host refuses overlapping buffers, but the compiler
+  // cannot know that and would otherwise wait for each load in turn.
+  float pk[4][DT], pv[4][VT];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int64_t js = s0 + 16 * wave + 4 * i + lq;
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+      pk[i][dt] = (a.d_kc_out && js < a.M) ? a.d_kc_out[(grp * a.M + js) * D + dc0 + 16 * dt + li]
+                                           : 0.f;
+#pragma unroll
+    for (int vt = 0; vt < VT; vt++)
+      pv[i][vt] = (a.d_vc_out && js < a.M)
+                      ? a.d_vc_out[(grp * a.M + js) * DV + vc0 + 16 * vt + li] : 0.f;
+  }
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int64_t js = s0 + 16 * wave + 4 * i + lq;
@@ -516,7 +548,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     for (int dt = 0; dt < DT; dt++) {
       const int d = dc0 + 16 * dt + li;
       const int64_t at = (grp * a.M + js) * D + d;
-      const float total = static_cast<float>(gk[dt][i]) + (a.d_kc_out ? a.d_kc_out[at] : 0.f);
+      const float total = static_cast<float>(gk[dt][i]) + pk[i][dt];
       if (appended) {
         a.g_new_key[(grp * a.Q + (js - len)) * D + d] = total;
         a.g_kc[at] = 0.f;
@@ -528,7 +560,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     for (int vt = 0; vt < VT; vt++) {
       const int d = vc0 + 16 * vt + li;
       const int64_t at = (grp * a.M + js) * DV + d;
-      const float total = static_cast<float>(gv[vt][i]) + (a.d_vc_out ? a.d_vc_out[at] : 0.f);
+      const float total = static_cast<float>(gv[vt][i]) + pv[i][vt];
       if (appended) {
         a.g_new_value[(grp * a.Q + (js - len)) * DV + d] = total;
         a.g_vc[at] = 0.f;
