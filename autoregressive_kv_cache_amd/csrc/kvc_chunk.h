@@ -131,22 +131,37 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_kernel(StepArgs a)
   if (a.R == 0 || c >= row_chunks(len, n, C)) return;
   const int nact = static_cast<int>((s1 < new_len ? s1 : new_len) - s0);  // visited slots
 
-  // 2. K rows and transposed V rows of the chunk into LDS
-  for (int idx = tid; idx < C * (D / 8); idx += kChunkThreads) {
-    const int slot = idx / (D / 8), part = idx % (D / 8);
+  // 2. K rows and transposed V rows of the chunk into LDS.  Every 16-byte
+  // load is issued before the first LDS store, so the loads overlap.
+  constexpr int NK = C * (D / 8) / kChunkThreads, NV = C * (DV / 8) / kChunkThreads;
+  static_assert(NK * kChunkThreads == C * (D / 8) && NV * kChunkThreads == C * (DV / 8),
+                "staging shape");
+  uint4 kx[NK], vx[NV];
+#pragma unroll
+  for (int i = 0; i < NK; i++) {
+    const int idx = tid + i * kChunkThreads, slot = idx / (D / 8), part = idx % (D / 8);
     const int64_t j = s0 + slot;
-    uint4 v = make_uint4(0, 0, 0, 0);
+    kx[i] = make_uint4(0, 0, 0, 0);
     if (slot < nact && (j >= len || k_head))
-      v = ld_global16((j < len ? k_head + j * D : nk_head + (j - len) * D) + part * 8);
-    *reinterpret_cast<uint4*>(k_s + slot * KP + part * 8) = v;
+      kx[i] = ld_global16((j < len ? k_head + j * D : nk_head + (j - len) * D) + part * 8);
   }
-  for (int idx = tid; idx < C * (DV / 8); idx += kChunkThreads) {
-    const int slot = idx % C, part = idx / C;
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int idx = tid + i * kChunkThreads, slot = idx % C, part = idx / C;
     const int64_t j = s0 + slot;
-    uint4 v = make_uint4(0, 0, 0, 0);
+    vx[i] = make_uint4(0, 0, 0, 0);
     if (slot < nact && (j >= len || v_head))
-      v = ld_global16((j < len ? v_head + j * DV : nv_head + (j - len) * DV) + part * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      vx[i] = ld_global16((j < len ? v_head + j * DV : nv_head + (j - len) * DV) + part * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < NK; i++) {
+    const int idx = tid + i * kChunkThreads, slot = idx / (D / 8), part = idx % (D / 8);
+    *reinterpret_cast<uint4*>(k_s + slot * KP + part * 8) = kx[i];
+  }
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int idx = tid + i * kChunkThreads, slot = idx % C, part = idx / C;
+    const uint32_t w[4] = {vx[i].x, vx[i].y, vx[i].z, vx[i].w};
 #pragma unroll
     for (int e = 0; e < 4; e++) {
       vt_s[(part * 8 + 2 * e) * VP + slot] = static_cast<uint16_t>(w[e] & 0xffffu);
@@ -365,25 +380,40 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_f32_kernel(StepArg
   const int nact = static_cast<int>((s1 < new_len ? s1 : new_len) - s0);
 
   // 2. K and V rows of the chunk into LDS (slots >= nact as zeros), read in
-  // 16-byte pieces
-  for (int idx = tid; idx < C * (D / 4); idx += kChunkThreads) {
-    const int slot = idx / (D / 4), d = (idx % (D / 4)) * 4;
+  // 16-byte pieces, every load issued before the first LDS store
+  constexpr int NK = C * (D / 4) / kChunkThreads, NV = C * (DV / 4) / kChunkThreads;
+  static_assert(NK * kChunkThreads == C * (D / 4) && NV * kChunkThreads == C * (DV / 4),
+                "staging shape");
+  float4 kx[NK], vx[NV];
+#pragma unroll
+  for (int i = 0; i < NK; i++) {
+    const int idx = tid + i * kChunkThreads, slot = idx / (D / 4), d = (idx % (D / 4)) * 4;
     const int64_t j = s0 + slot;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    kx[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (slot < nact && (j >= len || k_head))
-      x = *reinterpret_cast<const float4*>(j < len ? k_head + j * D + d : nk_head + (j - len) * D + d);
-    float* dst = k_s + slot * KP + d;
-    dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
+      kx[i] = *reinterpret_cast<const float4*>(j < len ? k_head + j * D + d
+                                                       : nk_head + (j - len) * D + d);
   }
-  for (int idx = tid; idx < C * (DV / 4); idx += kChunkThreads) {
-    const int slot = idx / (DV / 4), d = (idx % (DV / 4)) * 4;
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int idx = tid + i * kChunkThreads, slot = idx / (DV / 4), d = (idx % (DV / 4)) * 4;
     const int64_t j = s0 + slot;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    vx[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (slot < nact && (j >= len || v_head))
-      x = *reinterpret_cast<const float4*>(j < len ? v_head + j * DV + d
-                                                   : nv_head + (j - len) * DV + d);
-    float* dst = v_s + slot * VP + d;
-    dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
+      vx[i] = *reinterpret_cast<const float4*>(j < len ? v_head + j * DV + d
+                                                       : nv_head + (j - len) * DV + d);
+  }
+#pragma unroll
+  for (int i = 0; i < NK; i++) {
+    const int idx = tid + i * kChunkThreads;
+    float* dst = k_s + (idx / (D / 4)) * KP + (idx % (D / 4)) * 4;
+    dst[0] = kx[i].x; dst[1] = kx[i].y; dst[2] = kx[i].z; dst[3] = kx[i].w;
+  }
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int idx = tid + i * kChunkThreads;
+    float* dst = v_s + (idx / (DV / 4)) * VP + (idx % (DV / 4)) * 4;
+    dst[0] = vx[i].x; dst[1] = vx[i].y; dst[2] = vx[i].z; dst[3] = vx[i].w;
   }
   __syncthreads();
 

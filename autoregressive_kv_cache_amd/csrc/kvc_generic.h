@@ -28,16 +28,30 @@ constexpr int kGenericRowsPerTile = 8; // packed query rows per workgroup
 constexpr int kGenericThreads = 256;
 
 // Copy nbytes from src to dst with the widest unit both addresses allow.
+// The 16-byte path takes four pieces per thread per round, loaded before
+// any of them is stored: the compiler cannot tell that src and dst do not
+// overlap, and would otherwise wait for each load before its store.
 __device__ inline void copy_bytes(uint8_t* dst, const uint8_t* src, int64_t nbytes, int tid,
                                   int nthr) {
   if (nbytes <= 0) return;
   const uintptr_t al = reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src) |
                        static_cast<uintptr_t>(nbytes);
   if ((al & 15u) == 0) {
-    const int64_t n = nbytes / 16;
+    const int64_t n = nbytes / 16, step = nthr;
     uint4* d = reinterpret_cast<uint4*>(dst);
     const uint4* s = reinterpret_cast<const uint4*>(src);
-    for (int64_t i = tid; i < n; i += nthr) d[i] = s[i];
+    for (int64_t i = tid; i < n; i += 4 * step) {
+      // past the end: the last piece again, not stored
+      const int64_t k1 = i + step, k2 = i + 2 * step, k3 = i + 3 * step;
+      const uint4 v0 = s[i];
+      const uint4 v1 = s[k1 < n ? k1 : n - 1];
+      const uint4 v2 = s[k2 < n ? k2 : n - 1];
+      const uint4 v3 = s[k3 < n ? k3 : n - 1];
+      d[i] = v0;
+      if (k1 < n) d[k1] = v1;
+      if (k2 < n) d[k2] = v2;
+      if (k3 < n) d[k3] = v3;
+    }
   } else {
     const int64_t n = nbytes / 2;
     uint16_t* d = reinterpret_cast<uint16_t*>(dst);
