@@ -679,6 +679,12 @@ BWD_CASES = [
                                        len_range=(0, 299), tail_sentinel=None),
     chunk_wl(name="bwd_chunk", dtype="f32", B=3, Hq=8, Hk=2, Q=5, M=200, len_range=(0, 190)),
     WORKLOADS["mha_stress_f32"].with_(name="bwd_stress", B=3, M=160, len_range=(0, 150)),
+    # R = 320 packed rows: ten 32-row tiles per chunk, and statistics row
+    # groups that take a second tile
+    chunk_wl(name="bwd_rows320", dtype="f32", B=2, Hq=16, Hk=2, Q=40, M=160, len_range=(0, 100)),
+    # the two backward workloads of bench.py at their full sizes
+    WORKLOADS["chunk_gqa_f32"].with_(name="bwd_chunk_gqa_full"),
+    WORKLOADS["mha_stress_f32"].with_(name="bwd_stress_full"),
 ]
 
 
