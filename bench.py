@@ -369,6 +369,10 @@ def main():
     steps_per_s = args.steps / elapsed
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     k_ms = sum(kernel_ms) / len(kernel_ms)
+    k_sorted = sorted(kernel_ms)
+
+    def pct(q):  # nearest-rank percentile of the sampled launch durations
+        return k_sorted[min(len(k_sorted) - 1, max(0, int(round(q * (len(k_sorted) - 1)))))]
     k_gbps = attend_bytes / (k_ms * 1e-3) / 1e9
     digest = kernel_source_digest()
     traffic = committed_traffic(wl.name, args.mode, digest)
@@ -394,11 +398,14 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "copy_ceiling_gbps": ceiling,
         "roofline": {"bound": "hbm",
-                     "kernel": "backward (all three kernels)" if args.mode == "backward"
+                     "kernel": "backward (all four kernels)" if args.mode == "backward"
                      else DOMINANT_KERNEL, "achieved": k_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": k_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic, "bytes_per_launch": attend_bytes,
-                     "avg_launch_ms": k_ms},
+                     "avg_launch_ms": k_ms, "launches_sampled": len(kernel_ms),
+                     "p10_launch_ms": pct(0.1), "median_launch_ms": pct(0.5),
+                     "p90_launch_ms": pct(0.9),
+                     "frac_of_copy_ceiling": k_gbps / ceiling},
     }
     if args.mode == "paged":
         result["config"]["block_size"] = args.block_size
