@@ -36,12 +36,14 @@ struct SegRange {
   int64_t first, count;
 };
 
-__device__ inline SegRange group_segments(const StepArgs& a, int64_t grp, int64_t b, int64_t kvh,
-                                          int64_t nc) {
+// first_chunk: the row's first chunk in the flattened list (row record
+// entry 3); Nc, Pe: header entries 0 and 1 (all loaded by the caller with
+// the row record, so that no load waits on another).
+__device__ inline SegRange group_segments(const StepArgs& a, int64_t grp, int64_t kvh, int64_t nc,
+                                          int64_t first_chunk, int64_t Nc, int64_t Pe) {
   if (nc <= 0) return {0, 0};
   if (!a.seg_mode) return {grp * a.nchunk_max, nc};
-  const int64_t Nc = a.ws_hdr[0], Pe = a.ws_hdr[1];
-  const int64_t x0 = a.ws_rowinfo[b * 4 + 3] + kvh * nc, x1 = x0 + nc - 1;
+  const int64_t x0 = first_chunk + kvh * nc, x1 = x0 + nc - 1;
   // owner(x) = the worker w with floor(w*Nc/Pe) <= x < floor((w+1)*Nc/Pe)
   const int64_t w0 = ((x0 + 1) * Pe - 1) / Nc, w1 = ((x1 + 1) * Pe - 1) / Nc;
   return {w0 + grp, w1 - w0 + 1};
@@ -145,9 +147,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
   const int64_t grp = blockIdx.x / nrb / (ncw + 1);
   const bool ctx_role = k == ncw;
   const int64_t b = grp / a.Hk, kvh = grp % a.Hk;
+  // the row record and the stream header in one round of loads
   const int64_t len = a.ws_rowinfo[b * 4 + 0];
   const int64_t n = a.ws_rowinfo[b * 4 + 1];
   const int32_t status = static_cast<int32_t>(a.ws_rowinfo[b * 4 + 2]);
+  const int64_t first_chunk = a.ws_rowinfo[b * 4 + 3];
+  const int64_t hdr_nc = a.ws_hdr[0], hdr_pe = a.ws_hdr[1];
   const int64_t nc = a.seg_mode ? stream_chunks(len, n, a.C) : row_chunks(len, n, a.C);
   // chunk holding slot j (stream mode: the appended rows are a chunk of
   // their own, so an 8-slot vector may straddle two chunks at slot len)
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
   T* arow = static_cast<T*>(a.attention) + row * a.M;
   T* ctx = static_cast<T*>(a.context) + row * a.Dv;
   const double* chunk_ml = a.ws_chunk_ml + grp * a.nchunk_max * a.R * 2;
-  const SegRange sr = group_segments(a, grp, b, kvh, nc);
+  const SegRange sr = group_segments(a, grp, kvh, nc, first_chunk, hdr_nc, hdr_pe);
   // 8-element vectors need 16-byte aligned rows and ranges
   const bool vec = (reinterpret_cast<uintptr_t>(a.attention) % 16 == 0) && (a.M % 8 == 0) &&
                    (e0 % 8 == 0) && (e1 % 8 == 0);
