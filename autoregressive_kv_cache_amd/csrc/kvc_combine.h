@@ -52,11 +52,22 @@ __device__ inline SegRange group_segments(const StepArgs& a, int64_t grp, int64_
 // Eight consecutive elements of T (16 bytes of bf16, 32 of fp32).
 template <typename T>
 struct Vec8;
+// The combine reads each exponential once and writes each attention entry
+// once: both go through non-temporal accesses, which do not keep the lines
+// in the caches (the next step's K/V rows then find them emptier).
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
 template <>
 struct Vec8<bf16> {
   uint4 v;
-  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void store(bf16* p) const { *reinterpret_cast<uint4*>(p) = v; }
+  __device__ __forceinline__ void load(const bf16* p) {
+    const nt_u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+    v = make_uint4(w.x, w.y, w.z, w.w);
+  }
+  __device__ __forceinline__ void store(bf16* p) const {
+    const nt_u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<nt_u32x4*>(p));
+  }
   __device__ __forceinline__ void scale_by(float f) {
     uint32_t* w = reinterpret_cast<uint32_t*>(&v);
 #pragma unroll
@@ -91,12 +102,15 @@ template <>
 struct Vec8<float> {
   float4 a, b;
   __device__ __forceinline__ void load(const float* p) {
-    a = reinterpret_cast<const float4*>(p)[0];
-    b = reinterpret_cast<const float4*>(p)[1];
+    const nt_f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p));
+    const nt_f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p) + 1);
+    a = make_float4(x.x, x.y, x.z, x.w);
+    b = make_float4(y.x, y.y, y.z, y.w);
   }
   __device__ __forceinline__ void store(float* p) const {
-    reinterpret_cast<float4*>(p)[0] = a;
-    reinterpret_cast<float4*>(p)[1] = b;
+    const nt_f32x4 x = {a.x, a.y, a.z, a.w}, y = {b.x, b.y, b.z, b.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<nt_f32x4*>(p));
+    __builtin_nontemporal_store(y, reinterpret_cast<nt_f32x4*>(p) + 1);
   }
   __device__ __forceinline__ void scale_by(double f) {
     a.x = static_cast<float>(a.x * f); a.y = static_cast<float>(a.y * f);

@@ -198,13 +198,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(q, static_cast<short>(0), static_cast<int>(n),
                                            kBufferDword3);
 }
+// Cache policy operand of a buffer load: 0 (default) or kNonTemporal (the
+// nt bit), for data read once, which then does not allocate in the caches
+// as if it were going to be read again.
+constexpr int kNonTemporal = 2;
+template <int POLICY = 0>
 __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, POLICY);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// Non-temporal store (the copy into the output cache, not read again by the step).
 __device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4& v) {
   const u32x4 w = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(w, r, static_cast<int>(off), 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, static_cast<int>(off), 0, kNonTemporal);
 }
 
 // Chunk size: one wave's chunk is at most 64 slots and at most 16 loads of
@@ -243,11 +249,14 @@ struct RowSrc {
 // The 16-byte load u of a chunk (slot u * rows-per-load + lane slot; one
 // load covers 1 KB): the descriptor is rebased every 4 loads so that the
 // lane offset plus an immediate below 4 KB addresses the whole group.
+// Every K/V row is read once per step, so the loads are non-temporal
+// (with the default policy the kernel takes ~16 % longer at 32 sequences
+// of up to 8192 slots: the caches fill with rows nobody reads again).
 __device__ __forceinline__ uint4 load_one(const RowSrc& s, int u, uint32_t lane_off) {
   const uint32_t base = static_cast<uint32_t>(u / 4) * 4096u;
   const uint32_t imm = static_cast<uint32_t>(u % 4) * 1024u;
   const uint32_t left = s.bytes > base ? s.bytes - base : 0u;
-  return buf_ld16(make_rsrc(s.rows + base, left), lane_off + imm);
+  return buf_ld16<kNonTemporal>(make_rsrc(s.rows + base, left), lane_off + imm);
 }
 
 // Out of place: the copy of the visited rows to the output cache (load u of

@@ -30,7 +30,10 @@ constexpr int kGenericThreads = 256;
 // Copy nbytes from src to dst with the widest unit both addresses allow.
 // The 16-byte path takes four pieces per thread per round, loaded before
 // any of them is stored: the compiler cannot tell that src and dst do not
-// overlap, and would otherwise wait for each load before its store.
+// overlap, and would otherwise wait for each load before its store.  The
+// copied bytes are not used again by the step, so the accesses are
+// non-temporal.
+typedef unsigned int cu32x4 __attribute__((ext_vector_type(4)));
 __device__ inline void copy_bytes(uint8_t* dst, const uint8_t* src, int64_t nbytes, int tid,
                                   int nthr) {
   if (nbytes <= 0) return;
@@ -43,14 +46,16 @@ __device__ inline void copy_bytes(uint8_t* dst, const uint8_t* src, int64_t nbyt
     for (int64_t i = tid; i < n; i += 4 * step) {
       // past the end: the last piece again, not stored
       const int64_t k1 = i + step, k2 = i + 2 * step, k3 = i + 3 * step;
-      const uint4 v0 = s[i];
-      const uint4 v1 = s[k1 < n ? k1 : n - 1];
-      const uint4 v2 = s[k2 < n ? k2 : n - 1];
-      const uint4 v3 = s[k3 < n ? k3 : n - 1];
-      d[i] = v0;
-      if (k1 < n) d[k1] = v1;
-      if (k2 < n) d[k2] = v2;
-      if (k3 < n) d[k3] = v3;
+      const cu32x4* sv = reinterpret_cast<const cu32x4*>(s);
+      cu32x4* dv = reinterpret_cast<cu32x4*>(d);
+      const cu32x4 v0 = __builtin_nontemporal_load(sv + i);
+      const cu32x4 v1 = __builtin_nontemporal_load(sv + (k1 < n ? k1 : n - 1));
+      const cu32x4 v2 = __builtin_nontemporal_load(sv + (k2 < n ? k2 : n - 1));
+      const cu32x4 v3 = __builtin_nontemporal_load(sv + (k3 < n ? k3 : n - 1));
+      __builtin_nontemporal_store(v0, dv + i);
+      if (k1 < n) __builtin_nontemporal_store(v1, dv + k1);
+      if (k2 < n) __builtin_nontemporal_store(v2, dv + k2);
+      if (k3 < n) __builtin_nontemporal_store(v3, dv + k3);
     }
   } else {
     const int64_t n = nbytes / 2;
