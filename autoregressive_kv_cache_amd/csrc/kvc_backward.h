@@ -1,6 +1,8 @@
-// kvc_backward.h -- backward of the step for fp32 inputs: the gradients of
-// the query, the appended rows and the cache given those of the outputs
-// (attention, context, and the returned caches).  The page "Autoregressive
+// kvc_backward.h -- backward of the step for fp32 or bf16 tensors (the math
+// runs in fp32 and fp64 either way; each gradient is rounded once to the
+// tensors' type): the gradients of the query, the appended rows and the
+// cache given those of the outputs (attention, context, and the returned
+// caches).  The page "Autoregressive
 // KV-cache append and causal attention" grades gradients too (its workspace
 // note); the forward is the one of Required behavior, so with K', V' the
 // updated caches, P the attention rows and O the context of a valid row:
@@ -57,22 +59,23 @@ struct BwdArgs {
   int64_t nchunk;  // ceil(M / kBwdSlots)
   int32_t row_groups;  // bwd_stats: workgroups per chunk, each over every row_groups-th row tile
   float scale;
-  const float* query;      // [B][Hq][Q][D]
-  const float* new_key;    // [B][Hk][Q][D]
-  const float* new_value;  // [B][Hk][Q][Dv]
-  const float* kc;         // [B][Hk][M][D]: slots < length (the updated cache or the old one)
-  const float* vc;
+  // tensors of the element type T the kernels are built for (float or bf16)
+  const void* query;       // [B][Hq][Q][D]
+  const void* new_key;     // [B][Hk][Q][D]
+  const void* new_value;   // [B][Hk][Q][Dv]
+  const void* kc;          // [B][Hk][M][D]: slots < length (the updated cache or the old one)
+  const void* vc;
   const int64_t* lengths;  // the step's input lengths
   const uint8_t* mask;
-  const float* d_att;      // gradients of the outputs (null = zero)
-  const float* d_ctx;
-  const float* d_kc_out;   // [B][Hk][M][D]
-  const float* d_vc_out;
-  float* g_query;          // gradients of the inputs
-  float* g_new_key;
-  float* g_new_value;
-  float* g_kc;
-  float* g_vc;
+  const void* d_att;       // gradients of the outputs (null = zero)
+  const void* d_ctx;
+  const void* d_kc_out;    // [B][Hk][M][D]
+  const void* d_vc_out;
+  void* g_query;           // gradients of the inputs
+  void* g_new_key;
+  void* g_new_value;
+  void* g_kc;
+  void* g_vc;
   double* ws_row;          // [B][Hq][Q][4]: m, l, sum_k P_k dP_k / l
   double* ws_part;         // [B*Hk][nchunk][R][4]: m_c, l_c, sum over the chunk of e^(s-m_c) dP
   double* ws_dq;           // [B*Hk][nchunk][R][D]
@@ -110,14 +113,53 @@ __device__ inline void bwd_row_info(const BwdArgs& a, int64_t b, int64_t* len, i
   *n = ok ? k : 0;
 }
 
-// Slot j of the updated caches: kept rows from the cache, appended rows
-// (j >= len) from new_key / new_value.
-__device__ inline const float* bwd_key_row(const BwdArgs& a, int64_t grp, int64_t len, int64_t j) {
-  return j < len ? a.kc + (grp * a.M + j) * a.D : a.new_key + (grp * a.Q + (j - len)) * a.D;
+// Element access: values are widened exactly to fp32 as they are loaded,
+// and each gradient is rounded once to the element type as it is stored.
+template <typename T>
+__device__ __forceinline__ float bwd_ld(const void* p, int64_t i) {
+  if constexpr (sizeof(T) == 2)
+    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  else
+    return static_cast<const float*>(p)[i];
 }
-__device__ inline const float* bwd_value_row(const BwdArgs& a, int64_t grp, int64_t len,
-                                             int64_t j) {
-  return j < len ? a.vc + (grp * a.M + j) * a.Dv : a.new_value + (grp * a.Q + (j - len)) * a.Dv;
+// Element i of p where ok, else 0.
+//   fp32: masked-off lanes issue no load (the load sits in a branch whose
+//   value is used after it, so the loads of a batch all go out first).
+//   bf16: the same form would widen inside the branch and wait for each
+//   load in turn; instead every lane loads, a masked-off one element i_safe
+//   of the same tensor (a valid element next to what the other lanes
+//   read), and a select zeroes it.
+template <typename T>
+__device__ __forceinline__ float bwd_ld_or0(bool ok, const void* p, int64_t i, int64_t i_safe) {
+  if constexpr (sizeof(T) == 2) {
+    const float v = bwd_ld<T>(p, ok ? i : i_safe);
+    return ok ? v : 0.f;
+  } else {
+    float v = 0.f;
+    if (ok) v = static_cast<const float*>(p)[i];
+    return v;
+  }
+}
+template <typename T>
+__device__ __forceinline__ void bwd_st(void* p, int64_t i, float v) {
+  if constexpr (sizeof(T) == 2)
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+  else
+    static_cast<float*>(p)[i] = v;
+}
+
+// Slot j of the updated caches (element offset of its first value, and the
+// tensor): kept rows from the cache, appended rows (j >= len) from
+// new_key / new_value.
+__device__ inline const void* bwd_key_src(const BwdArgs& a, int64_t grp, int64_t len, int64_t j,
+                                          int64_t* off) {
+  *off = j < len ? (grp * a.M + j) * a.D : (grp * a.Q + (j - len)) * a.D;
+  return j < len ? a.kc : a.new_key;
+}
+__device__ inline const void* bwd_value_src(const BwdArgs& a, int64_t grp, int64_t len,
+                                            int64_t j, int64_t* off) {
+  *off = j < len ? (grp * a.M + j) * a.Dv : (grp * a.Q + (j - len)) * a.Dv;
+  return j < len ? a.vc : a.new_value;
 }
 
 // The chunk kernels run their products on the fp64 matrix cores
@@ -138,7 +180,7 @@ constexpr int bwd_pitch() {
 
 // K', V' rows of the chunk starting at slot s0 (zeros past nvis).  Every
 // load is issued before the first LDS store, so the loads overlap.
-template <int D, int DV>
+template <typename T, int D, int DV>
 __device__ inline void bwd_stage_kv(const BwdArgs& a, int64_t grp, int64_t len, int64_t nvis,
                                     int64_t s0, float* k_s, float* v_s) {
   constexpr int C = kBwdSlots, KP = bwd_pitch<D>(), VP = bwd_pitch<DV>();
@@ -150,13 +192,17 @@ __device__ inline void bwd_stage_kv(const BwdArgs& a, int64_t grp, int64_t len, 
   for (int i = 0; i < NK; i++) {
     const int idx = tid + i * kBwdThreads, sl = idx / D, d = idx % D;
     const int64_t j = s0 + sl;
-    kx[i] = j < nvis ? bwd_key_row(a, grp, len, j)[d] : 0.f;
+    int64_t off = 0;  // bf16: slots past nvis read the last visible slot's row (nvis > s0 here)
+    const void* src = bwd_key_src(a, grp, len, (sizeof(T) == 4 || j < nvis) ? j : nvis - 1, &off);
+    kx[i] = bwd_ld_or0<T>(j < nvis, src, off + d, off + d);
   }
 #pragma unroll
   for (int i = 0; i < NV; i++) {
     const int idx = tid + i * kBwdThreads, sl = idx / DV, d = idx % DV;
     const int64_t j = s0 + sl;
-    vx[i] = j < nvis ? bwd_value_row(a, grp, len, j)[d] : 0.f;
+    int64_t off = 0;
+    const void* src = bwd_value_src(a, grp, len, (sizeof(T) == 4 || j < nvis) ? j : nvis - 1, &off);
+    vx[i] = bwd_ld_or0<T>(j < nvis, src, off + d, off + d);
   }
 #pragma unroll
   for (int i = 0; i < NK; i++) {
@@ -185,40 +231,79 @@ struct BwdTileRegs {
   double st[3];
 };
 
-template <int D, int DV, int RT>
+template <typename T, int D, int DV, int RT>
 __device__ inline void bwd_fetch_tile(const BwdArgs& a, int64_t b, int64_t kvh, int64_t len,
                                       int64_t n, int r0, int64_t j, bool stats,
                                       BwdTileRegs<D, DV, RT>& x) {
   using X = BwdTileRegs<D, DV, RT>;
   const int tid = threadIdx.x, lq = (tid % kWave) / 16;
+  const int Q = static_cast<int>(a.Q);
+  // the head's packed row r as a (b, query head, token) row; rows past R
+  // (tile padding) read the head's last row instead
+  auto qrow = [&](int r) {
+    const int rc = r < a.R ? r : a.R - 1;
+    return (b * a.Hq + kvh * a.G + rc / Q) * a.Q + rc % Q;
+  };
+  if constexpr (sizeof(T) == 4) {  // masked-off lanes load nothing (see bwd_ld_or0)
+#pragma unroll
+    for (int i = 0; i < X::NQ; i++) {
+      const int idx = tid + i * kBwdThreads;
+      const int rr = idx / D, d = idx % D, r = r0 + rr;
+      const int g = r / Q, t = r % Q;
+      x.q[i] = (idx < RT * D && r < a.R && t < n)
+                   ? bwd_ld<T>(a.query, ((b * a.Hq + kvh * a.G + g) * a.Q + t) * D + d) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < X::NO; i++) {
+      const int idx = tid + i * kBwdThreads;
+      const int rr = idx / DV, d = idx % DV, r = r0 + rr;
+      const int g = r / Q, t = r % Q;
+      x.o[i] = (a.d_ctx && idx < RT * DV && r < a.R && t < n)
+                   ? bwd_ld<T>(a.d_ctx, ((b * a.Hq + kvh * a.G + g) * a.Q + t) * DV + d) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < RT / 4; k++) {
+      const int r = r0 + 16 * (k / 4) + 4 * (k % 4) + lq;
+      const int g = r / Q, t = r % Q;
+      const bool vis = a.d_att && r < a.R && t < n && j <= len + t;
+      x.da[k] = vis ? bwd_ld<T>(a.d_att, ((b * a.Hq + kvh * a.G + g) * a.Q + t) * a.M + j) : 0.f;
+    }
+  } else {
 #pragma unroll
   for (int i = 0; i < X::NQ; i++) {
     const int idx = tid + i * kBwdThreads;
     const int rr = idx / D, d = idx % D, r = r0 + rr;
-    const int g = r / static_cast<int>(a.Q), t = r % static_cast<int>(a.Q);
-    x.q[i] = (idx < RT * D && r < a.R && t < n)
-                 ? a.query[((b * a.Hq + kvh * a.G + g) * a.Q + t) * D + d] : 0.f;
+    const bool ok = idx < RT * D && r < a.R && r % Q < n;
+    x.q[i] = bwd_ld_or0<T>(ok, a.query, qrow(r) * D + d, qrow(r) * D + d);
   }
 #pragma unroll
-  for (int i = 0; i < X::NO; i++) {
-    const int idx = tid + i * kBwdThreads;
-    const int rr = idx / DV, d = idx % DV, r = r0 + rr;
-    const int g = r / static_cast<int>(a.Q), t = r % static_cast<int>(a.Q);
-    x.o[i] = (a.d_ctx && idx < RT * DV && r < a.R && t < n)
-                 ? a.d_ctx[((b * a.Hq + kvh * a.G + g) * a.Q + t) * DV + d] : 0.f;
+  for (int i = 0; i < X::NO; i++) x.o[i] = 0.f;
+  if (a.d_ctx) {
+#pragma unroll
+    for (int i = 0; i < X::NO; i++) {
+      const int idx = tid + i * kBwdThreads;
+      const int rr = idx / DV, d = idx % DV, r = r0 + rr;
+      const bool ok = idx < RT * DV && r < a.R && r % Q < n;
+      x.o[i] = bwd_ld_or0<T>(ok, a.d_ctx, qrow(r) * DV + d, qrow(r) * DV + d);
+    }
   }
 #pragma unroll
-  for (int k = 0; k < RT / 4; k++) {
-    const int r = r0 + 16 * (k / 4) + 4 * (k % 4) + lq;
-    const int g = r / static_cast<int>(a.Q), t = r % static_cast<int>(a.Q);
-    const bool vis = a.d_att && r < a.R && t < n && j <= len + t;
-    x.da[k] = vis ? a.d_att[((b * a.Hq + kvh * a.G + g) * a.Q + t) * a.M + j] : 0.f;
+  for (int k = 0; k < RT / 4; k++) x.da[k] = 0.f;
+  if (a.d_att) {
+    const int64_t jc = j < a.M ? j : a.M - 1;
+#pragma unroll
+    for (int k = 0; k < RT / 4; k++) {
+      const int r = r0 + 16 * (k / 4) + 4 * (k % 4) + lq;
+      const int t = r % Q;
+      const bool vis = r < a.R && t < n && j <= len + t;
+      x.da[k] = bwd_ld_or0<T>(vis, a.d_att, qrow(r) * a.M + j, qrow(r) * a.M + jc);
+    }
+  }
   }
   if (stats && tid < RT) {
     const int r = r0 + tid;
-    const int g = r / static_cast<int>(a.Q), t = r % static_cast<int>(a.Q);
-    const bool ok = r < a.R && t < n;
-    const double* st = a.ws_row + ((b * a.Hq + kvh * a.G + g) * a.Q + t) * 4;
+    const bool ok = r < a.R && r % Q < n;
+    const double* st = a.ws_row + qrow(r) * 4;
     x.st[0] = ok ? st[0] : 0.0;
     x.st[1] = ok ? st[1] : 1.0;
     x.st[2] = ok ? st[2] : 0.0;
@@ -268,7 +353,7 @@ __device__ inline void bwd_scores(const float* q_s, const float* o_s, const floa
 // every valid packed row of its row tiles, over the chunk's slots it sees, m_c = max s_j, l_c =
 // sum e^(s_j - m_c) and sum e^(s_j - m_c) dP_j, in fp64 (each wave over its
 // 16 slots, then the four merged).
-template <int D, int DV>
+template <typename T, int D, int DV>
 __global__ __launch_bounds__(kBwdThreads) void bwd_stats_kernel(BwdArgs a) {
   constexpr int C = kBwdSlots, RT = kBwdRowTile, W = kBwdThreads / kWave;
   constexpr int KP = bwd_pitch<D>(), VP = bwd_pitch<DV>();
@@ -293,8 +378,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_stats_kernel(BwdArgs a) {
   const int64_t j = s0 + 16 * wave + li;  // this lane's slot
   const int step = a.row_groups * RT;
   BwdTileRegs<D, DV, RT> nx;  // the next tile's inputs, loading while this one computes
-  bwd_fetch_tile<D, DV, RT>(a, b, kvh, len, n, rg * RT, j, false, nx);
-  bwd_stage_kv<D, DV>(a, grp, len, nvis, s0, k_s, v_s);
+  bwd_fetch_tile<T, D, DV, RT>(a, b, kvh, len, n, rg * RT, j, false, nx);
+  bwd_stage_kv<T, D, DV>(a, grp, len, nvis, s0, k_s, v_s);
   for (int r0 = rg * RT; r0 < a.R; r0 += step) {
     __syncthreads();  // the previous tile is no longer read
     bwd_commit_tile<D, DV, RT>(nx, q_s, o_s);
@@ -302,7 +387,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_stats_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; i++) da[i] = nx.da[i];
     __syncthreads();
-    if (r0 + step < a.R) bwd_fetch_tile<D, DV, RT>(a, b, kvh, len, n, r0 + step, j, false, nx);
+    if (r0 + step < a.R) bwd_fetch_tile<T, D, DV, RT>(a, b, kvh, len, n, r0 + step, j, false, nx);
     bwd_f64x4 s, dov;
     bwd_scores<D, DV>(q_s, o_s, k_s, v_s, wave, li, lq, s, dov);
 #pragma unroll
@@ -400,7 +485,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(BwdArgs a) {
 // dS for the chunk's slots and every packed row, and for the group's
 // columns the slot gradients of the chunk and the chunk's share of every
 // row's dq.
-template <int D, int DV, int RT>
+template <typename T, int D, int DV, int RT>
 __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
   constexpr int C = kBwdSlots, NB = RT / 16, W = kBwdThreads / kWave;
   constexpr int KP = bwd_pitch<D>(), VP = bwd_pitch<DV>(), SP = C + 1;
@@ -431,8 +516,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
   const int64_t j = s0 + 16 * wave + li;  // this lane's slot in the score tile
   BwdTileRegs<D, DV, RT> nx;  // the next tile's inputs, loading while this one computes
   if (any) {
-    bwd_fetch_tile<D, DV, RT>(a, b, kvh, len, n, 0, j, true, nx);
-    bwd_stage_kv<D, DV>(a, grp, len, nvis, s0, k_s, v_s);
+    bwd_fetch_tile<T, D, DV, RT>(a, b, kvh, len, n, 0, j, true, nx);
+    bwd_stage_kv<T, D, DV>(a, grp, len, nvis, s0, k_s, v_s);
   }
 
   // dK', dV' of this wave's 16 slots: gk[dt][i] = dK'[slot 16 w + 4 i + lq][dc0 + 16 dt + li]
@@ -455,7 +540,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int k = 0; k < RT / 4; k++) da[k] = nx.da[k];
     __syncthreads();
-    if (r0 + RT < a.R) bwd_fetch_tile<D, DV, RT>(a, b, kvh, len, n, r0 + RT, j, true, nx);
+    if (r0 + RT < a.R) bwd_fetch_tile<T, D, DV, RT>(a, b, kvh, len, n, r0 + RT, j, true, nx);
     // P from the score and the row's m, l; dS = P (dP - sum_k P_k dP_k);
     // the 16-row blocks' products are independent chains
     bwd_f64x4 s[NB], dov[NB];
@@ -527,17 +612,48 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
   // the first store: the host refuses overlapping buffers, but the compiler
   // cannot know that and would otherwise wait for each load in turn.
   float pk[4][DT], pv[4][VT];
+  if constexpr (sizeof(T) == 4) {  // masked-off lanes load nothing (see bwd_ld_or0)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t js = s0 + 16 * wave + 4 * i + lq;
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++)
+        pk[i][dt] = (a.d_kc_out && js < a.M)
+                        ? bwd_ld<T>(a.d_kc_out, (grp * a.M + js) * D + dc0 + 16 * dt + li) : 0.f;
+#pragma unroll
+      for (int vt = 0; vt < VT; vt++)
+        pv[i][vt] = (a.d_vc_out && js < a.M)
+                        ? bwd_ld<T>(a.d_vc_out, (grp * a.M + js) * DV + vc0 + 16 * vt + li) : 0.f;
+    }
+  } else {
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const int64_t js = s0 + 16 * wave + 4 * i + lq;
 #pragma unroll
-    for (int dt = 0; dt < DT; dt++)
-      pk[i][dt] = (a.d_kc_out && js < a.M) ? a.d_kc_out[(grp * a.M + js) * D + dc0 + 16 * dt + li]
-                                           : 0.f;
+    for (int dt = 0; dt < DT; dt++) pk[i][dt] = 0.f;
 #pragma unroll
-    for (int vt = 0; vt < VT; vt++)
-      pv[i][vt] = (a.d_vc_out && js < a.M)
-                      ? a.d_vc_out[(grp * a.M + js) * DV + vc0 + 16 * vt + li] : 0.f;
+    for (int vt = 0; vt < VT; vt++) pv[i][vt] = 0.f;
+  }
+  if (a.d_kc_out) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t js = s0 + 16 * wave + 4 * i + lq, jc = js < a.M ? js : a.M - 1;
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++)
+        pk[i][dt] = bwd_ld_or0<T>(js < a.M, a.d_kc_out, (grp * a.M + js) * D + dc0 + 16 * dt + li,
+                                  (grp * a.M + jc) * D + dc0 + 16 * dt + li);
+    }
+  }
+  if (a.d_vc_out) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t js = s0 + 16 * wave + 4 * i + lq, jc = js < a.M ? js : a.M - 1;
+#pragma unroll
+      for (int vt = 0; vt < VT; vt++)
+        pv[i][vt] = bwd_ld_or0<T>(js < a.M, a.d_vc_out,
+                                  (grp * a.M + js) * DV + vc0 + 16 * vt + li,
+                                  (grp * a.M + jc) * DV + vc0 + 16 * vt + li);
+    }
+  }
   }
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -550,10 +666,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
       const int64_t at = (grp * a.M + js) * D + d;
       const float total = static_cast<float>(gk[dt][i]) + pk[i][dt];
       if (appended) {
-        a.g_new_key[(grp * a.Q + (js - len)) * D + d] = total;
-        a.g_kc[at] = 0.f;
+        bwd_st<T>(a.g_new_key, (grp * a.Q + (js - len)) * D + d, total);
+        bwd_st<T>(a.g_kc, at, 0.f);
       } else {
-        a.g_kc[at] = total;
+        bwd_st<T>(a.g_kc, at, total);
       }
     }
 #pragma unroll
@@ -562,24 +678,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
       const int64_t at = (grp * a.M + js) * DV + d;
       const float total = static_cast<float>(gv[vt][i]) + pv[i][vt];
       if (appended) {
-        a.g_new_value[(grp * a.Q + (js - len)) * DV + d] = total;
-        a.g_vc[at] = 0.f;
+        bwd_st<T>(a.g_new_value, (grp * a.Q + (js - len)) * DV + d, total);
+        bwd_st<T>(a.g_vc, at, 0.f);
       } else {
-        a.g_vc[at] = total;
+        bwd_st<T>(a.g_vc, at, total);
       }
     }
   }
   // appended rows that do not exist (t >= n, rejected rows): zero gradient
   if (c == 0 && cg == 0) {
     for (int64_t idx = tid; idx < (a.Q - n) * D; idx += kBwdThreads)
-      a.g_new_key[(grp * a.Q + n + idx / D) * D + idx % D] = 0.f;
+      bwd_st<T>(a.g_new_key, (grp * a.Q + n + idx / D) * D + idx % D, 0.f);
     for (int64_t idx = tid; idx < (a.Q - n) * DV; idx += kBwdThreads)
-      a.g_new_value[(grp * a.Q + n + idx / DV) * DV + idx % DV] = 0.f;
+      bwd_st<T>(a.g_new_value, (grp * a.Q + n + idx / DV) * DV + idx % DV, 0.f);
   }
 }
 
 // dq_r = sum over the chunks its row can see of the partials (0 for rows
 // that are not valid).
+template <typename T>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a) {
   const int64_t row = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -592,7 +709,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a) {
   for (int64_t d = lane; d < a.D; d += kWave) {
     double acc = 0;
     for (int64_t c = 0; c < nc; c++) acc += a.ws_dq[((grp * a.nchunk + c) * a.R + r) * a.D + d];
-    a.g_query[row * a.D + d] = static_cast<float>(acc);
+    bwd_st<T>(a.g_query, row * a.D + d, static_cast<float>(acc));
   }
 }
 

@@ -16,36 +16,47 @@ using namespace kvc_host;
 
 constexpr int64_t kMaxBwdWorkgroups = int64_t(1) << 30;
 
-// Backward: fp32, head sizes with a chunk kernel below.
+// Backward: fp32 or bf16 tensors, head sizes with a chunk kernel below.
 struct BwdEntry {
+  int dtype;
   int64_t D, Dv;
   void (*stats)(const kvc::BwdArgs&, hipStream_t);
   void (*chunk)(const kvc::BwdArgs&, hipStream_t);
+  void (*dq)(const kvc::BwdArgs&, hipStream_t);
 };
-template <int D, int DV>
+template <typename T, int D, int DV>
 void launch_bwd_stats(const kvc::BwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((kvc::bwd_stats_kernel<D, DV>),
+  hipLaunchKernelGGL((kvc::bwd_stats_kernel<T, D, DV>),
                      dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk * a.row_groups)),
                      dim3(kvc::kBwdThreads), 0, s, a);
 }
-template <int D, int DV>
+template <typename T, int D, int DV>
 void launch_bwd_chunk(const kvc::BwdArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.B * a.Hk * a.nchunk * kvc::bwd_col_groups<D, DV>()));
   if (a.R > kvc::kBwdRowTile)
-    hipLaunchKernelGGL((kvc::bwd_chunk_kernel<D, DV, kvc::kBwdChunkRowsWide>), grid,
+    hipLaunchKernelGGL((kvc::bwd_chunk_kernel<T, D, DV, kvc::kBwdChunkRowsWide>), grid,
                        dim3(kvc::kBwdThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((kvc::bwd_chunk_kernel<D, DV, kvc::kBwdRowTile>), grid,
+    hipLaunchKernelGGL((kvc::bwd_chunk_kernel<T, D, DV, kvc::kBwdRowTile>), grid,
                        dim3(kvc::kBwdThreads), 0, s, a);
 }
+template <typename T>
+void launch_bwd_dq(const kvc::BwdArgs& a, hipStream_t s) {
+  const int64_t rows = a.B * a.Hq * a.Q;
+  hipLaunchKernelGGL((kvc::bwd_dq_kernel<T>), dim3(static_cast<unsigned>((rows + 3) / 4)),
+                     dim3(kvc::kBwdThreads), 0, s, a);
+}
+#define KVC_BWD(T, CODE, D, DV)                                                            \
+  {CODE, D, DV, &launch_bwd_stats<T, D, DV>, &launch_bwd_chunk<T, D, DV>, &launch_bwd_dq<T>}
 const BwdEntry kBwdTable[] = {
-    {64, 64, &launch_bwd_stats<64, 64>, &launch_bwd_chunk<64, 64>},
-    {128, 128, &launch_bwd_stats<128, 128>, &launch_bwd_chunk<128, 128>},
-    {64, 32, &launch_bwd_stats<64, 32>, &launch_bwd_chunk<64, 32>},
+    KVC_BWD(float, KVC_F32, 64, 64),       KVC_BWD(float, KVC_F32, 128, 128),
+    KVC_BWD(float, KVC_F32, 64, 32),       KVC_BWD(kvc::bf16, KVC_BF16, 64, 64),
+    KVC_BWD(kvc::bf16, KVC_BF16, 128, 128), KVC_BWD(kvc::bf16, KVC_BF16, 64, 32),
 };
-const BwdEntry* find_bwd(const kvc_dims* d) {
+#undef KVC_BWD
+const BwdEntry* find_bwd(const kvc_dims* d, int dtype) {
   for (const BwdEntry& e : kBwdTable)
-    if (e.D == d->D && e.Dv == d->Dv) return &e;
+    if (e.dtype == dtype && e.D == d->D && e.Dv == d->Dv) return &e;
   return nullptr;
 }
 
@@ -62,7 +73,7 @@ size_t bwd_workspace(const kvc_dims* d) {
 extern "C" {
 
 size_t kvc_backward_workspace_bytes(const kvc_dims* dims, int dtype) {
-  if (!dims || check_dims(dims, dtype) != KVC_OK || dtype != KVC_F32) return 0;
+  if (!dims || check_dims(dims, dtype) != KVC_OK) return 0;
   return bwd_workspace(dims);
 }
 
@@ -78,8 +89,7 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
   const kvc_dims* d = dims;
   int rc = check_dims(d, dtype);
   if (rc != KVC_OK) return rc;
-  if (dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
-  const BwdEntry* e = find_bwd(d);
+  const BwdEntry* e = find_bwd(d, dtype);
   if (!e) return KVC_ERR_UNSUPPORTED;
   double sc;
   rc = check_scale(has_scale, scale, d->D, &sc);
@@ -91,15 +101,16 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
     return KVC_ERR_NULL;
   if (workspace_bytes < bwd_workspace(d)) return KVC_ERR_WORKSPACE;
   const size_t B = d->B, Hq = d->Hq, Hk = d->Hk, Q = d->Q, M = d->M, D = d->D, Dv = d->Dv;
-  const Range ins[] = {{query, B * Hq * Q * D * 4}, {new_key, B * Hk * Q * D * 4},
-                       {new_value, B * Hk * Q * Dv * 4}, {key_cache, B * Hk * M * D * 4},
-                       {value_cache, B * Hk * M * Dv * 4}, {lengths, B * 8},
-                       {append_mask, B * Q}, {d_attention, B * Hq * Q * M * 4},
-                       {d_context, B * Hq * Q * Dv * 4}, {d_key_cache_out, B * Hk * M * D * 4},
-                       {d_value_cache_out, B * Hk * M * Dv * 4}};
-  const Range outs[] = {{g_query, B * Hq * Q * D * 4}, {g_new_key, B * Hk * Q * D * 4},
-                        {g_new_value, B * Hk * Q * Dv * 4}, {g_key_cache, B * Hk * M * D * 4},
-                        {g_value_cache, B * Hk * M * Dv * 4}, {workspace, bwd_workspace(d)}};
+  const size_t e4 = dtype == KVC_BF16 ? 2 : 4;  // element bytes
+  const Range ins[] = {{query, B * Hq * Q * D * e4}, {new_key, B * Hk * Q * D * e4},
+                       {new_value, B * Hk * Q * Dv * e4}, {key_cache, B * Hk * M * D * e4},
+                       {value_cache, B * Hk * M * Dv * e4}, {lengths, B * 8},
+                       {append_mask, B * Q}, {d_attention, B * Hq * Q * M * e4},
+                       {d_context, B * Hq * Q * Dv * e4}, {d_key_cache_out, B * Hk * M * D * e4},
+                       {d_value_cache_out, B * Hk * M * Dv * e4}};
+  const Range outs[] = {{g_query, B * Hq * Q * D * e4}, {g_new_key, B * Hk * Q * D * e4},
+                        {g_new_value, B * Hk * Q * Dv * e4}, {g_key_cache, B * Hk * M * D * e4},
+                        {g_value_cache, B * Hk * M * Dv * e4}, {workspace, bwd_workspace(d)}};
   for (int i = 0; i < 6; i++) {
     for (const Range& in : ins)
       if (overlap(outs[i], in)) return KVC_ERR_ALIAS;
@@ -123,22 +134,22 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
       return KVC_ERR_SHAPE;
   }
   a.scale = static_cast<float>(sc);
-  a.query = static_cast<const float*>(query);
-  a.new_key = static_cast<const float*>(new_key);
-  a.new_value = static_cast<const float*>(new_value);
-  a.kc = static_cast<const float*>(key_cache);
-  a.vc = static_cast<const float*>(value_cache);
+  a.query = query;
+  a.new_key = new_key;
+  a.new_value = new_value;
+  a.kc = key_cache;
+  a.vc = value_cache;
   a.lengths = lengths;
   a.mask = append_mask;
-  a.d_att = static_cast<const float*>(d_attention);
-  a.d_ctx = static_cast<const float*>(d_context);
-  a.d_kc_out = static_cast<const float*>(d_key_cache_out);
-  a.d_vc_out = static_cast<const float*>(d_value_cache_out);
-  a.g_query = static_cast<float*>(g_query);
-  a.g_new_key = static_cast<float*>(g_new_key);
-  a.g_new_value = static_cast<float*>(g_new_value);
-  a.g_kc = static_cast<float*>(g_key_cache);
-  a.g_vc = static_cast<float*>(g_value_cache);
+  a.d_att = d_attention;
+  a.d_ctx = d_context;
+  a.d_kc_out = d_key_cache_out;
+  a.d_vc_out = d_value_cache_out;
+  a.g_query = g_query;
+  a.g_new_key = g_new_key;
+  a.g_new_value = g_new_value;
+  a.g_kc = g_key_cache;
+  a.g_vc = g_value_cache;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const size_t nchunk = static_cast<size_t>(a.nchunk), R = static_cast<size_t>(a.R);
   a.ws_row = reinterpret_cast<double*>(ws);
@@ -153,8 +164,7 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
     hipLaunchKernelGGL(kvc::bwd_rows_kernel, dim3(row_blocks), dim3(kvc::kBwdThreads), 0, s, a);
   }
   e->chunk(a, s);
-  if (rows > 0)
-    hipLaunchKernelGGL(kvc::bwd_dq_kernel, dim3(row_blocks), dim3(kvc::kBwdThreads), 0, s, a);
+  if (rows > 0) e->dq(a, s);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 

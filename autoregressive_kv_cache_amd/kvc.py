@@ -264,13 +264,14 @@ def kvc_step_backward(query, new_key, new_value, key_cache, value_cache, lengths
                       d_attention, d_context, d_key_cache_out, d_value_cache_out, g_query,
                       g_new_key, g_new_value, g_key_cache, g_value_cache, workspace=None,
                       scale=None, stream=None) -> None:
-    """Enqueue the backward of the step (fp32) on ``stream``; the ``d_*``
-    gradients of the outputs may be None."""
+    """Enqueue the backward of the step (fp32 or bf16 tensors, all of one
+    dtype) on ``stream``; the ``d_*`` gradients of the outputs may be None."""
     lib = load()
     dims = dims_of(query, key_cache, value_cache)
     if workspace is None:
         workspace = torch.empty(max(1, int(lib.kvc_backward_workspace_bytes(
-            ctypes.byref(dims), KVC_F32))), dtype=torch.uint8, device=key_cache.device)
+            ctypes.byref(dims), dtype_code(key_cache.dtype)))), dtype=torch.uint8,
+            device=key_cache.device)
     hs, sc = _scale_args(scale)
     rc = lib.kvc_step_backward(
         ctypes.byref(dims), dtype_code(key_cache.dtype), hs, sc, _ptr(query), _ptr(new_key),

@@ -140,7 +140,7 @@ def backward_bytes(wl, lengths, n):
     write the gradients of q, the new rows and the whole caches.  Returns
     (whole call, the slot-gradient kernel's share: visible K'/V' rows, the
     caches' gradients read and written, q and the context gradient)."""
-    e = 4
+    e = 2 if wl.dtype == "bf16" else 4
     vis = sum(wl.Hk * (int(L) + int(k)) * (wl.D + wl.Dv) * e for L, k in zip(lengths, n))
     full = wl.B * wl.Hk * wl.M * (wl.D + wl.Dv) * e
     q = wl.B * wl.Hq * wl.Q * wl.D * e
@@ -267,14 +267,13 @@ def main():
             d["kc_out"] = torch.empty_like(inp["key_cache"])
             d["vc_out"] = torch.empty_like(inp["value_cache"])
         if args.mode == "backward":
-            if wl.dtype != "f32":
-                raise SystemExit("--mode backward takes an fp32 workload")
             gen = torch.Generator(device=dev)
             gen.manual_seed(7 + k)
+            fdt = inp["key_cache"].dtype
             for name, like in (("d_attention", "att"), ("d_context", "ctx")):
-                d[name] = torch.randn(d[like].shape, generator=gen, device=dev)
-            d["d_kc"] = torch.randn(inp["key_cache"].shape, generator=gen, device=dev)
-            d["d_vc"] = torch.randn(inp["value_cache"].shape, generator=gen, device=dev)
+                d[name] = torch.randn(d[like].shape, generator=gen, device=dev).to(fdt)
+            d["d_kc"] = torch.randn(inp["key_cache"].shape, generator=gen, device=dev).to(fdt)
+            d["d_vc"] = torch.randn(inp["value_cache"].shape, generator=gen, device=dev).to(fdt)
             for name, like in (("g_q", "query"), ("g_nk", "new_key"), ("g_nv", "new_value"),
                                ("g_kc", "key_cache"), ("g_vc", "value_cache")):
                 d[name] = torch.empty_like(inp[like])

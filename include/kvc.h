@@ -239,9 +239,11 @@ int kvc_attend_over_cache(const kvc_dims *dims, int dtype, int has_scale,
                           size_t workspace_bytes, void *stream,
                           const kvc_events *events);
 
-/* Backward of the step (fp32 inputs; head sizes (D, Dv) in {(64, 64),
+/* Backward of the step (fp32 or bf16: every tensor argument of the dtype,
+ * gradients in and out included; head sizes (D, Dv) in {(64, 64),
  * (128, 128), (64, 32)}, else KVC_ERR_UNSUPPORTED): the gradients of the
- * step's inputs given those of its outputs.  The page grades gradients as
+ * step's inputs given those of its outputs.  The math runs in fp32 and
+ * fp64 either way; each gradient is rounded once to the dtype.  The page grades gradients as
  * well as values ("Autoregressive KV-cache append and causal attention",
  * the workspace note).
  *

@@ -672,7 +672,8 @@ def test_reattend_rejected_sequences():
 
 
 # -- backward of the step (kvc_step_backward, fp32) ---------------------------
-BWD_TOL = 1e-4  # |d| <= 1e-4 (1 + |ref|): fp32 sums of <= M terms against the double oracle
+BWD_TOL = {"f32": 1e-4,   # |d| <= 1e-4 (1 + |ref|): fp32 sums of <= M terms against the double oracle
+           "bf16": 4e-3}  # plus one rounding to bf16 (relative <= 2^-9) of every gradient
 
 BWD_CASES = [
     WORKLOADS["decode_gqa_bf16"].with_(name="bwd_decode", dtype="f32", B=3, M=300,
@@ -690,9 +691,12 @@ BWD_CASES = [
 
 @pytest.mark.parametrize("wl", BWD_CASES, ids=lambda w: w.name)
 @pytest.mark.parametrize("upstream", ["all", "context_only"])
-def test_backward_against_oracle(wl, upstream):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_against_oracle(wl, upstream, dtype):
+    wl = wl.with_(dtype=dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     for seed in (0, 1):
-        say(f"[case] backward {wl.name} {upstream} seed={seed}")
+        say(f"[case] backward {wl.name} {dtype} {upstream} seed={seed}")
         inp = make_inputs(wl, seed, "cpu")
         if seed == 1:  # a rejected row and a row that appends nothing
             inp["lengths"][0] = wl.M + 5
@@ -701,10 +705,10 @@ def test_backward_against_oracle(wl, upstream):
         g = torch.Generator().manual_seed(100 + seed)
         B, Hq, Q, D = inp["query"].shape
         Hk, M, Dv = inp["key_cache"].shape[1], inp["key_cache"].shape[2], inp["value_cache"].shape[3]
-        ups = {"d_attention": torch.randn(B, Hq, Q, M, generator=g),
-               "d_context": torch.randn(B, Hq, Q, Dv, generator=g),
-               "d_key_cache_out": torch.randn(B, Hk, M, D, generator=g),
-               "d_value_cache_out": torch.randn(B, Hk, M, Dv, generator=g)}
+        ups = {"d_attention": torch.randn(B, Hq, Q, M, generator=g).to(tdt),
+               "d_context": torch.randn(B, Hq, Q, Dv, generator=g).to(tdt),
+               "d_key_cache_out": torch.randn(B, Hk, M, D, generator=g).to(tdt),
+               "d_value_cache_out": torch.randn(B, Hk, M, Dv, generator=g).to(tdt)}
         if upstream == "context_only":
             ups = {k: (v if k == "d_context" else None) for k, v in ups.items()}
         outs = {k: torch.full_like(dinp[src], float("nan")) for k, src in
@@ -717,14 +721,16 @@ def test_backward_against_oracle(wl, upstream):
                               **outs, scale=wl.scale)
         torch.cuda.synchronize()
         h = host_arrays(inp)
-        ref = oracle.step_backward(h["query"], h["new_key"], h["new_value"], h["key_cache"],
-                                   h["value_cache"], h["lengths"], h["append_mask"],
-                                   **{k: None if v is None else v.numpy() for k, v in ups.items()},
+        ref = oracle.step_backward(*(to_f64(inp[k]) for k in ("query", "new_key", "new_value",
+                                                              "key_cache", "value_cache")),
+                                   h["lengths"], h["append_mask"],
+                                   **{k: None if v is None else to_f64(v) for k, v in ups.items()},
                                    scale=wl.scale)
         for name, want in (("g_query", ref.query), ("g_new_key", ref.new_key),
                            ("g_new_value", ref.new_value), ("g_key_cache", ref.key_cache),
                            ("g_value_cache", ref.value_cache)):
-            got = outs[name].cpu().numpy().astype(np.float64)
+            got = to_f64(outs[name])
             assert np.all(np.isfinite(got)), f"{wl.name}/{seed}: {name} not finite"
-            err = np.abs(got - want) - BWD_TOL * (1 + np.abs(want))
-            assert err.max() <= 0, f"{wl.name}/{upstream}/{seed}: {name} off by {err.max():.3e}"
+            err = np.abs(got - want) - BWD_TOL[dtype] * (1 + np.abs(want))
+            assert err.max() <= 0, \
+                f"{wl.name}/{dtype}/{upstream}/{seed}: {name} off by {err.max():.3e}"
