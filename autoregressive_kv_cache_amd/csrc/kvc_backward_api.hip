@@ -127,10 +127,12 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
     const int64_t tiles = (a.R + kvc::kBwdRowTile - 1) / kvc::kBwdRowTile;
     a.row_groups = static_cast<int32_t>(tiles < 1 ? 1 : tiles < kvc::kBwdMaxRowGroups ? tiles : kvc::kBwdMaxRowGroups);
   }
-  {  // the chunk grids (chunks x row or column groups) must fit one launch
+  {  // every grid must fit one launch: the chunk grids (chunks x row or
+     // column groups) and the per-row grids (4 packed rows per workgroup)
     int64_t x;
     if (!mul_ok(d->B * d->Hk, a.nchunk, kMaxElems, &x) ||
-        !mul_ok(x, a.row_groups > 4 ? a.row_groups : 4, kMaxBwdWorkgroups, &x))
+        !mul_ok(x, a.row_groups > 4 ? a.row_groups : 4, kMaxBwdWorkgroups, &x) ||
+        !mul_ok(d->B * d->Hq, d->Q, kMaxElems, &x) || (x + 3) / 4 > kMaxBwdWorkgroups)
       return KVC_ERR_SHAPE;
   }
   a.scale = static_cast<float>(sc);
