@@ -45,3 +45,36 @@ def test_decode_bytes_are_kv_dominated():
     assert 0.95 < kv / step < 1.0
     assert attend < step
     assert np.isclose(attend / step, 1.0, atol=0.03)
+
+
+def test_backward_bytes_scale_with_the_element_size():
+    """The backward reads and writes whole elements of the tensors' dtype:
+    the same shape in bf16 moves exactly half the bytes of fp32."""
+    f32 = WORKLOADS["chunk_gqa_f32"]
+    bf = f32.with_(dtype="bf16")
+    lengths, n = draw_lengths_and_counts(f32, 0)
+    lengths = [int(x) for x in lengths]
+    n = [int(x) for x in n]
+    step32, kern32 = bench.backward_bytes(f32, lengths, n)
+    step16, kern16 = bench.backward_bytes(bf, lengths, n)
+    assert step32 == 2 * step16 and kern32 == 2 * kern16
+
+
+def test_committed_traffic_is_gated_by_the_source_digest():
+    """The HBM traffic figure is reported only for the kernel source it was
+    measured on: the committed summary's digest returns its byte count, any
+    other digest returns None."""
+    import re
+    path = bench.os.path.join(bench.ROOT, "profiles", "attend_decode_gqa_bf16_inplace_traffic.md")
+    text = open(path).read()
+    sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text).group(1)
+    nbytes = float(re.search(r"traffic_bytes_per_dispatch:\s*([0-9.eE+]+)", text).group(1))
+    assert bench.committed_traffic("decode_gqa_bf16", "inplace", sha) == nbytes
+    other = ("0" if sha[0] != "0" else "1") + sha[1:]
+    assert bench.committed_traffic("decode_gqa_bf16", "inplace", other) is None
+    assert bench.committed_traffic("decode_gqa_bf16", "paged", sha) is None
+    # the measured traffic is within a few per cent of the algorithmic bytes
+    wl = WORKLOADS["decode_gqa_bf16"]
+    lengths, n = draw_lengths_and_counts(wl, 0)
+    _, attend, _ = bench.algorithmic_bytes(wl, [int(x) for x in lengths], [int(x) for x in n])
+    assert 1.0 <= nbytes / attend < 1.05
