@@ -2,9 +2,9 @@
 // runs in fp32 and fp64 either way; each gradient is rounded once to the
 // tensors' type): the gradients of the query, the appended rows and the
 // cache given those of the outputs (attention, context, and the returned
-// caches).  The page "Autoregressive
-// KV-cache append and causal attention" grades gradients too (its workspace
-// note); the forward is the one of Required behavior, so with K', V' the
+// caches).  The page "Autoregressive KV-cache append and causal attention"
+// grades gradients too (its workspace note); the forward is the one of
+// Required behavior, so with K', V' the
 // updated caches, P the attention rows and O the context of a valid row:
 //   dP_j = dA_j + dO . V'_j,   dS_j = P_j (dP_j - sum_k P_k dP_k),
 //   dq   = scale sum_j dS_j K'_j,
@@ -21,15 +21,16 @@
 // dP and that sum are formed in fp64, and the query gradient is summed in
 // fp64.  The forward's fp32 attention and context are not needed.
 //
-// Kernels: bwd_stats (one workgroup per (b, KV head, 64-slot chunk): each
-// packed row's max, sum and sum of P dP over the chunk's slots, K' and V'
-// staged once for all rows of the head), bwd_rows (one wave per packed
+// Kernels: bwd_stats (one workgroup per (b, KV head, 64-slot chunk, row
+// group): each packed row's max, sum and sum of P dP over the chunk's
+// slots, K' and V' staged once for the group's rows), bwd_rows (one wave per packed
 // row: the chunk statistics merged as the forward merges its segments),
-// bwd_chunk (same grid as bwd_stats: dS for the chunk's slots and all
-// packed rows, the slot gradients, and per-chunk dq partials), bwd_dq (one
-// wave per packed row: the partials summed).  The products of the two
-// chunk kernels (scores, dO . V', dK', dV', dq) run on the fp64 matrix
-// cores; the slot gradients are summed in fp64 before the fp32 store.
+// bwd_chunk (one workgroup per (b, KV head, 64-slot chunk): dS for the
+// chunk's slots and all packed rows, the slot gradients, and per-chunk dq
+// partials), bwd_dq (one wave per packed row: the partials summed).  The
+// products of the two chunk kernels (scores, dO . V', dK', dV', dq) run on
+// the fp64 matrix cores; the slot gradients are summed in fp64 and rounded
+// once when stored.
 #pragma once
 
 #include "kvc_common.h"
