@@ -78,6 +78,12 @@ WORKLOADS: dict[str, Workload] = {
     "long_decode_bf16": Workload(
         "long_decode_bf16", B=4, Hq=64, Hk=8, Q=1, M=131072, D=128, Dv=128,
         dtype="bf16", len_range=(65536, 131071), n_rule="all"),
+    # One GPU's share of long_decode_bf16 when its slot axis is split over 8
+    # GPUs (each holding a contiguous 16384-slot range of every sequence):
+    # the same heads, an eighth of the capacity and of the lengths.
+    "long_decode_share8_bf16": Workload(
+        "long_decode_share8_bf16", B=4, Hq=64, Hk=8, Q=1, M=16384, D=128, Dv=128,
+        dtype="bf16", len_range=(8192, 16383), n_rule="all"),
 }
 
 

@@ -88,6 +88,15 @@ def test_decode_gqa_full_size_inplace_and_oop():
         full_check(wl, 0, mode, gen_device=DEV)
 
 
+def test_long_decode_share_full_check():
+    """One GPU's share of the slot-sharded long decode (M = 16384 of 131072,
+    64 query heads over 8 KV heads): every output against the oracle, in
+    place and out of place."""
+    wl = WORKLOADS["long_decode_share8_bf16"]
+    for mode in ("inplace", "oop"):
+        full_check(wl, 0, mode, gen_device=DEV)
+
+
 def test_long_decode_full_size_sampled():
     """Long-context decode at its full size (B=4, Hq=64, Hk=8, M=131072):
     caches bit-exact against the oracle's append, sampled rows against the
