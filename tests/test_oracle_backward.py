@@ -80,3 +80,33 @@ def test_structure(orc):
     # see only the pass-through
     assert not g.query[0, :, 2].any() and not g.new_key[0, :, 2].any()
     np.testing.assert_array_equal(g.key_cache[0, :, 5:], ups["d_key_cache_out"][0, :, 5:])
+
+
+def test_closed_forms():
+    """Two cases with a closed form.  One visible slot (length 0, one token):
+    P = 1, so dS = P (dP - P dP) = 0; the query gets nothing, the appended
+    key only the returned cache's gradient, and the appended value the sum
+    of dO over its query heads plus that gradient.  All visible keys equal:
+    P is uniform and sum_j dS_j = 0, so dq = scale sum_j dS_j K_j = 0 while
+    the keys still get scale dS_j q."""
+    rng = np.random.default_rng(11)
+    B, Hq, Hk, Q, M, D, Dv = 2, 4, 2, 1, 5, 3, 2
+    G = Hq // Hk
+    inp, lengths, mask, ups = make(rng, B, Hq, Hk, Q, M, D, Dv, [0, 0], [1, 1])
+    g = oracle.step_backward(**inp, lengths=lengths, append_mask=mask, **ups)
+    assert np.abs(g.query).max() < 1e-12
+    np.testing.assert_allclose(g.new_key[:, :, 0], ups["d_key_cache_out"][:, :, 0], atol=1e-12)
+    want_v = ups["d_context"][:, :, 0].reshape(B, Hk, G, Dv).sum(axis=2) \
+        + ups["d_value_cache_out"][:, :, 0]
+    np.testing.assert_allclose(g.new_value[:, :, 0], want_v, rtol=1e-12, atol=1e-12)
+    assert not g.key_cache[:, :, 0].any() and not g.value_cache[:, :, 0].any()
+
+    # equal keys: rows of length 3 plus one appended row, every visible key the same
+    inp, lengths, mask, ups = make(rng, B, Hq, Hk, Q, M, D, Dv, [3, 2], [1, 1])
+    k = grid(rng, (D,))
+    inp["key_cache"][:] = k
+    inp["new_key"][:] = k
+    g = oracle.step_backward(**inp, lengths=lengths, append_mask=mask, **ups)
+    assert np.abs(g.query).max() < 1e-12
+    # ... while dS itself is not zero: the keys do get a gradient beyond the pass-through
+    assert np.abs(g.key_cache[:, :, :2] - ups["d_key_cache_out"][:, :, :2]).max() > 1e-3
