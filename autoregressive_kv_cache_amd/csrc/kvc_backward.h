@@ -568,8 +568,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     }
     __syncthreads();  // dq below reads every wave's slots
     // dK'_j += sum_r scale dS q_r and dV'_j += sum_r P dO_r over the tile's rows
+    // (groups of 4 rows; groups past the head's last packed row are padding)
 #pragma unroll
     for (int kk = 0; kk < RT / 4; kk++) {
+      if (r0 + 4 * kk >= a.R) break;
       const double dsa = ds_s[(4 * kk + lq) * SP + 16 * wave + li];
       const double pa = p_s[(4 * kk + lq) * SP + 16 * wave + li];
 #pragma unroll
