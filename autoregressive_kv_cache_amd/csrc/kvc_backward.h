@@ -311,11 +311,10 @@ __device__ inline void bwd_fetch_tile(const BwdArgs& a, int64_t b, int64_t kvh, 
   }
 }
 
-// q and dO of the tile into LDS (row pitch bwd_pitch).
-template <int D, int DV, int RT>
+// q and dO of the tile into LDS (row pitches KP and VP elements).
+template <int D, int DV, int RT, int KP = bwd_pitch<D>(), int VP = bwd_pitch<DV>()>
 __device__ inline void bwd_commit_tile(const BwdTileRegs<D, DV, RT>& x, float* q_s, float* o_s) {
   using X = BwdTileRegs<D, DV, RT>;
-  constexpr int KP = bwd_pitch<D>(), VP = bwd_pitch<DV>();
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < X::NQ; i++) {
@@ -350,6 +349,43 @@ __device__ inline void bwd_scores(const float* q_s, const float* o_s, const floa
                                                dov, 0, 0, 0);
 }
 
+// N consecutive elements of row `off` of a T tensor, widened to fp32, in
+// 16-byte loads (the row and the tensor are 16-byte aligned; the host
+// checks); ok = false gives zeros (the loads then read the same row, which
+// the caller chooses valid).
+template <typename T, int N>
+__device__ __forceinline__ void bwd_row_slice(const void* src, int64_t off, bool ok, float (&x)[N]) {
+  if constexpr (sizeof(T) == 2) {
+    static_assert(N % 8 == 0, "slice");
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + off);
+    uint4 w[N / 8];
+#pragma unroll
+    for (int u = 0; u < N / 8; u++) w[u] = p[u];
+#pragma unroll
+    for (int u = 0; u < N / 8; u++) {
+      const uint32_t h[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        x[8 * u + 2 * e] = ok ? __uint_as_float(h[e] << 16) : 0.f;
+        x[8 * u + 2 * e + 1] = ok ? __uint_as_float(h[e] & 0xffff0000u) : 0.f;
+      }
+    }
+  } else {
+    static_assert(N % 4 == 0, "slice");
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + off);
+    float4 w[N / 4];
+#pragma unroll
+    for (int u = 0; u < N / 4; u++) w[u] = p[u];
+#pragma unroll
+    for (int u = 0; u < N / 4; u++) {
+      x[4 * u] = ok ? w[u].x : 0.f;
+      x[4 * u + 1] = ok ? w[u].y : 0.f;
+      x[4 * u + 2] = ok ? w[u].z : 0.f;
+      x[4 * u + 3] = ok ? w[u].w : 0.f;
+    }
+  }
+}
+
 // One workgroup per (b, KV head, chunk of kBwdSlots slots, row group): for
 // every valid packed row of its row tiles, over the chunk's slots it sees, m_c = max s_j, l_c =
 // sum e^(s_j - m_c) and sum e^(s_j - m_c) dP_j, in fp64 (each wave over its
@@ -357,12 +393,15 @@ __device__ inline void bwd_scores(const float* q_s, const float* o_s, const floa
 template <typename T, int D, int DV>
 __global__ __launch_bounds__(kBwdThreads) void bwd_stats_kernel(BwdArgs a) {
   constexpr int C = kBwdSlots, RT = kBwdRowTile, W = kBwdThreads / kWave;
-  constexpr int KP = bwd_pitch<D>(), VP = bwd_pitch<DV>();
-  static_assert(C == 16 * W && RT == 16 && D % 16 == 0 && DV % 16 == 0, "tile shape");
-  __shared__ float k_s[C * KP];
-  __shared__ float v_s[C * VP];
-  __shared__ float q_s[RT * KP];
-  __shared__ float o_s[RT * VP];
+  // The products run over the head dimension in the order where lane group
+  // l / 16 takes the contiguous quarter [lq D/4, (lq + 1) D/4): so each
+  // lane's K' (and V') operands are one contiguous slice of its slot's row,
+  // loaded straight into registers, and only the q and dO tiles go through
+  // LDS (odd pitches: the A-operand reads hit distinct banks).
+  constexpr int KQ = D / 4, VQ = DV / 4, QP = D + 1, OP = DV + 1;
+  static_assert(C == 16 * W && RT == 16 && D % 32 == 0 && DV % 32 == 0, "tile shape");
+  __shared__ float q_s[RT * QP];
+  __shared__ float o_s[RT * OP];
   __shared__ double part_s[W][RT][3];
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int li = lane % 16, lq = lane / 16;
@@ -380,17 +419,34 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_stats_kernel(BwdArgs a) {
   const int step = a.row_groups * RT;
   BwdTileRegs<D, DV, RT> nx;  // the next tile's inputs, loading while this one computes
   bwd_fetch_tile<T, D, DV, RT>(a, b, kvh, len, n, rg * RT, j, false, nx);
-  bwd_stage_kv<T, D, DV>(a, grp, len, nvis, s0, k_s, v_s);
+  // this lane's K' and V' operand slices (slots past nvis: zeros, read from
+  // the last visible slot's row, nvis > s0 here)
+  float kx[KQ], vx[VQ];
+  {
+    const int64_t jr = j < nvis ? j : nvis - 1;
+    int64_t koff = 0, voff = 0;
+    const void* ksrc = bwd_key_src(a, grp, len, jr, &koff);
+    const void* vsrc = bwd_value_src(a, grp, len, jr, &voff);
+    bwd_row_slice<T, KQ>(ksrc, koff + lq * KQ, j < nvis, kx);
+    bwd_row_slice<T, VQ>(vsrc, voff + lq * VQ, j < nvis, vx);
+  }
   for (int r0 = rg * RT; r0 < a.R; r0 += step) {
     __syncthreads();  // the previous tile is no longer read
-    bwd_commit_tile<D, DV, RT>(nx, q_s, o_s);
+    bwd_commit_tile<D, DV, RT, QP, OP>(nx, q_s, o_s);
     float da[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) da[i] = nx.da[i];
     __syncthreads();
     if (r0 + step < a.R) bwd_fetch_tile<T, D, DV, RT>(a, b, kvh, len, n, r0 + step, j, false, nx);
-    bwd_f64x4 s, dov;
-    bwd_scores<D, DV>(q_s, o_s, k_s, v_s, wave, li, lq, s, dov);
+    bwd_f64x4 s = {0.0, 0.0, 0.0, 0.0}, dov = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int kk = 0; kk < KQ; kk++)
+      s = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(q_s[li * QP + lq * KQ + kk]),
+                                               static_cast<double>(kx[kk]), s, 0, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < VQ; kk++)
+      dov = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(o_s[li * OP + lq * VQ + kk]),
+                                                 static_cast<double>(vx[kk]), dov, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int r = r0 + 4 * i + lq;

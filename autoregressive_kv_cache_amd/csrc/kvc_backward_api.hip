@@ -99,6 +99,12 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
   if (d->Q > 0 && (!query || !new_key || !new_value || !append_mask || !g_query || !g_new_key ||
                    !g_new_value))
     return KVC_ERR_NULL;
+  {  // the K'/V' row slices are read in 16-byte pieces
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    if (!al16(key_cache) || !al16(value_cache) ||
+        (d->Q > 0 && (!al16(new_key) || !al16(new_value))))
+      return KVC_ERR_UNSUPPORTED;
+  }
   if (workspace_bytes < bwd_workspace(d)) return KVC_ERR_WORKSPACE;
   const size_t B = d->B, Hq = d->Hq, Hk = d->Hk, Q = d->Q, M = d->M, D = d->D, Dv = d->Dv;
   const size_t e4 = dtype == KVC_BF16 ? 2 : 4;  // element bytes
