@@ -423,6 +423,22 @@ def test_paged_against_oracle(wl, bs):
         check_step(out, ref, wl.dtype, f"paged {wl.name}/{seed}")
 
 
+def test_paged_full_size_bench_configuration():
+    """The paged step at the full decode size in the configuration bench.py
+    times (B=32, Hq=32, Hk=8, M=8192, 64-slot blocks permuted over the pool):
+    every output against the oracle."""
+    wl = WORKLOADS["decode_gqa_bf16"]
+    say(f"[case] paged {wl.name} full size bs=64")
+    inp = make_inputs(wl, 0, "cpu")
+    kp, vp, table = paged_layout(inp["key_cache"], inp["value_cache"], 64, 0)
+    inp = {k: v for k, v in inp.items() if k not in ("key_cache", "value_cache")}
+    ref = paged_ref(inp, kp, vp, table, scale=wl.scale)
+    out = run_paged(inp, kp, vp, table, scale=wl.scale)
+    check_step(out, ref, wl.dtype, f"paged {wl.name} full size")
+    del inp, kp, vp, out
+    torch.cuda.empty_cache()
+
+
 def test_paged_identity_table_matches_dense_bitwise():
     """A table that lays the pool out like the dense cache gives bit-identical
     outputs to kvc_step_inplace on that dense cache (same kernels, same order)."""
@@ -608,6 +624,20 @@ def reatt_ref(q, cu, kc_logical, vc_logical, L, Q, sink=None, scale=None):
     return oracle.default().reattend(h["q"], cu.numpy(), h["k"], h["v"], L.numpy(), Q,
                                      sink=None if sink is None else sink.numpy().astype(np.float64),
                                      scale=scale)
+
+
+def test_reattend_full_size_decode_shape():
+    """Re-attention at the full decode size (32 sequences, 32 query heads
+    over 8 KV heads, 8192 cached slots, up to one query each): the packed
+    output against the oracle."""
+    say("[case] reattend full decode size")
+    q, cu, kc, vc, L, S = reatt_case("bf16", 32, 32, 8, 1, 8192, 128, 128, 3)
+    out, st = run_reatt(q, cu, kc, vc, L, 1)
+    ref, rst = reatt_ref(q, cu, kc, vc, L, 1)
+    assert list(st.numpy()) == list(rst)
+    check_floats(to_f64(out), ref, "bf16", "reattend full size", "context")
+    del q, kc, vc
+    torch.cuda.empty_cache()
 
 
 REATT_CASES = [
