@@ -391,7 +391,8 @@ __device__ __forceinline__ void bwd_row_slice(const void* src, int64_t off, bool
 // sum e^(s_j - m_c) and sum e^(s_j - m_c) dP_j, in fp64 (each wave over its
 // 16 slots, then the four merged).
 template <typename T, int D, int DV>
-__global__ __launch_bounds__(kBwdThreads) void bwd_stats_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void
+bwd_stats_kernel(BwdArgs a) {
   constexpr int C = kBwdSlots, RT = kBwdRowTile, W = kBwdThreads / kWave;
   // The products run over the head dimension in the order where lane group
   // l / 16 takes the contiguous quarter [lq D/4, (lq + 1) D/4): so each
@@ -538,6 +539,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(BwdArgs a) {
   }
 }
 
+// Whether bwd_chunk_kernel loads the pass-through gradients before its
+// products: for the shapes that hold one wave per SIMD whatever the order
+// and keep the extra registers without spilling (the 16-row tile at
+// D + Dv >= 128, the 32-row tile at D + Dv = 128).
+template <int D, int DV, int RT>
+constexpr bool bwd_early_pass() {
+  return D + DV >= 128 && RT * (D + DV) <= 4096;
+}
+
 // One workgroup per (b, KV head, chunk of kBwdSlots slots, column group):
 // dS for the chunk's slots and every packed row, and for the group's
 // columns the slot gradients of the chunk and the chunk's share of every
@@ -584,6 +594,59 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
   for (int vt = 0; vt < VT; vt++) gv[vt] = bwd_f64x4{0.0, 0.0, 0.0, 0.0};
 
+  // The pass-through gradients of the chunk's slots, all loaded before the
+  // first store: the host refuses overlapping buffers, but the compiler
+  // cannot know that and would otherwise wait for each load in turn.  Where
+  // the kernel runs at one wave per SIMD anyway and the registers are there
+  // (bwd_early_pass), they are loaded before the products, which then hide
+  // their latency.
+  float pk[4][DT], pv[4][VT];
+  auto load_pass = [&]() {
+  if constexpr (sizeof(T) == 4) {  // masked-off lanes load nothing (see bwd_ld_or0)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t js = s0 + 16 * wave + 4 * i + lq;
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++)
+        pk[i][dt] = (a.d_kc_out && js < a.M)
+                        ? bwd_ld<T>(a.d_kc_out, (grp * a.M + js) * D + dc0 + 16 * dt + li) : 0.f;
+#pragma unroll
+      for (int vt = 0; vt < VT; vt++)
+        pv[i][vt] = (a.d_vc_out && js < a.M)
+                        ? bwd_ld<T>(a.d_vc_out, (grp * a.M + js) * DV + vc0 + 16 * vt + li) : 0.f;
+    }
+  } else {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) pk[i][dt] = 0.f;
+#pragma unroll
+    for (int vt = 0; vt < VT; vt++) pv[i][vt] = 0.f;
+  }
+  if (a.d_kc_out) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t js = s0 + 16 * wave + 4 * i + lq, jc = js < a.M ? js : a.M - 1;
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++)
+        pk[i][dt] = bwd_ld_or0<T>(js < a.M, a.d_kc_out, (grp * a.M + js) * D + dc0 + 16 * dt + li,
+                                  (grp * a.M + jc) * D + dc0 + 16 * dt + li);
+    }
+  }
+  if (a.d_vc_out) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t js = s0 + 16 * wave + 4 * i + lq, jc = js < a.M ? js : a.M - 1;
+#pragma unroll
+      for (int vt = 0; vt < VT; vt++)
+        pv[i][vt] = bwd_ld_or0<T>(js < a.M, a.d_vc_out,
+                                  (grp * a.M + js) * DV + vc0 + 16 * vt + li,
+                                  (grp * a.M + jc) * DV + vc0 + 16 * vt + li);
+    }
+  }
+  }
+  };
+  if constexpr (bwd_early_pass<D, DV, RT>()) load_pass();
   const double scale = a.scale;
   for (int r0 = 0; any && r0 < a.R; r0 += RT) {
     __syncthreads();  // the previous tile is no longer read
@@ -665,55 +728,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     }
   }
 
+  if constexpr (!bwd_early_pass<D, DV, RT>()) load_pass();
   // slot gradients out: kept slots -> the cache gradient, overwritten ones
   // -> the appended rows' gradient (the cache entry gets 0), the rest ->
-  // the pass-through alone.  The pass-through values are all loaded before
-  // the first store: the host refuses overlapping buffers, but the compiler
-  // cannot know that and would otherwise wait for each load in turn.
-  float pk[4][DT], pv[4][VT];
-  if constexpr (sizeof(T) == 4) {  // masked-off lanes load nothing (see bwd_ld_or0)
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int64_t js = s0 + 16 * wave + 4 * i + lq;
-#pragma unroll
-      for (int dt = 0; dt < DT; dt++)
-        pk[i][dt] = (a.d_kc_out && js < a.M)
-                        ? bwd_ld<T>(a.d_kc_out, (grp * a.M + js) * D + dc0 + 16 * dt + li) : 0.f;
-#pragma unroll
-      for (int vt = 0; vt < VT; vt++)
-        pv[i][vt] = (a.d_vc_out && js < a.M)
-                        ? bwd_ld<T>(a.d_vc_out, (grp * a.M + js) * DV + vc0 + 16 * vt + li) : 0.f;
-    }
-  } else {
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-#pragma unroll
-    for (int dt = 0; dt < DT; dt++) pk[i][dt] = 0.f;
-#pragma unroll
-    for (int vt = 0; vt < VT; vt++) pv[i][vt] = 0.f;
-  }
-  if (a.d_kc_out) {
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int64_t js = s0 + 16 * wave + 4 * i + lq, jc = js < a.M ? js : a.M - 1;
-#pragma unroll
-      for (int dt = 0; dt < DT; dt++)
-        pk[i][dt] = bwd_ld_or0<T>(js < a.M, a.d_kc_out, (grp * a.M + js) * D + dc0 + 16 * dt + li,
-                                  (grp * a.M + jc) * D + dc0 + 16 * dt + li);
-    }
-  }
-  if (a.d_vc_out) {
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int64_t js = s0 + 16 * wave + 4 * i + lq, jc = js < a.M ? js : a.M - 1;
-#pragma unroll
-      for (int vt = 0; vt < VT; vt++)
-        pv[i][vt] = bwd_ld_or0<T>(js < a.M, a.d_vc_out,
-                                  (grp * a.M + js) * DV + vc0 + 16 * vt + li,
-                                  (grp * a.M + jc) * DV + vc0 + 16 * vt + li);
-    }
-  }
-  }
+  // the pass-through alone.
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int64_t js = s0 + 16 * wave + 4 * i + lq;
