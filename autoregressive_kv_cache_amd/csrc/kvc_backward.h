@@ -389,7 +389,8 @@ __device__ __forceinline__ void bwd_row_slice(const void* src, int64_t off, bool
 // One workgroup per (b, KV head, chunk of kBwdSlots slots, row group): for
 // every valid packed row of its row tiles, over the chunk's slots it sees, m_c = max s_j, l_c =
 // sum e^(s_j - m_c) and sum e^(s_j - m_c) dP_j, in fp64 (each wave over its
-// 16 slots, then the four merged).
+// 16 slots, then the four merged).  Held to two waves per SIMD: at D = 128
+// the compiler otherwise takes 262 registers and runs one.
 template <typename T, int D, int DV>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 bwd_stats_kernel(BwdArgs a) {
@@ -539,15 +540,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(BwdArgs a) {
   }
 }
 
-// Whether bwd_chunk_kernel loads the pass-through gradients before its
-// products: for the shapes that hold one wave per SIMD whatever the order
-// and keep the extra registers without spilling (the 16-row tile at
-// D + Dv >= 128, the 32-row tile at D + Dv = 128).
-template <int D, int DV, int RT>
-constexpr bool bwd_early_pass() {
-  return D + DV >= 128 && RT * (D + DV) <= 4096;
-}
-
 // One workgroup per (b, KV head, chunk of kBwdSlots slots, column group):
 // dS for the chunk's slots and every packed row, and for the group's
 // columns the slot gradients of the chunk and the chunk's share of every
@@ -594,59 +586,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
   for (int vt = 0; vt < VT; vt++) gv[vt] = bwd_f64x4{0.0, 0.0, 0.0, 0.0};
 
-  // The pass-through gradients of the chunk's slots, all loaded before the
-  // first store: the host refuses overlapping buffers, but the compiler
-  // cannot know that and would otherwise wait for each load in turn.  Where
-  // the kernel runs at one wave per SIMD anyway and the registers are there
-  // (bwd_early_pass), they are loaded before the products, which then hide
-  // their latency.
-  float pk[4][DT], pv[4][VT];
-  auto load_pass = [&]() {
-  if constexpr (sizeof(T) == 4) {  // masked-off lanes load nothing (see bwd_ld_or0)
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int64_t js = s0 + 16 * wave + 4 * i + lq;
-#pragma unroll
-      for (int dt = 0; dt < DT; dt++)
-        pk[i][dt] = (a.d_kc_out && js < a.M)
-                        ? bwd_ld<T>(a.d_kc_out, (grp * a.M + js) * D + dc0 + 16 * dt + li) : 0.f;
-#pragma unroll
-      for (int vt = 0; vt < VT; vt++)
-        pv[i][vt] = (a.d_vc_out && js < a.M)
-                        ? bwd_ld<T>(a.d_vc_out, (grp * a.M + js) * DV + vc0 + 16 * vt + li) : 0.f;
-    }
-  } else {
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-#pragma unroll
-    for (int dt = 0; dt < DT; dt++) pk[i][dt] = 0.f;
-#pragma unroll
-    for (int vt = 0; vt < VT; vt++) pv[i][vt] = 0.f;
-  }
-  if (a.d_kc_out) {
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int64_t js = s0 + 16 * wave + 4 * i + lq, jc = js < a.M ? js : a.M - 1;
-#pragma unroll
-      for (int dt = 0; dt < DT; dt++)
-        pk[i][dt] = bwd_ld_or0<T>(js < a.M, a.d_kc_out, (grp * a.M + js) * D + dc0 + 16 * dt + li,
-                                  (grp * a.M + jc) * D + dc0 + 16 * dt + li);
-    }
-  }
-  if (a.d_vc_out) {
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int64_t js = s0 + 16 * wave + 4 * i + lq, jc = js < a.M ? js : a.M - 1;
-#pragma unroll
-      for (int vt = 0; vt < VT; vt++)
-        pv[i][vt] = bwd_ld_or0<T>(js < a.M, a.d_vc_out,
-                                  (grp * a.M + js) * DV + vc0 + 16 * vt + li,
-                                  (grp * a.M + jc) * DV + vc0 + 16 * vt + li);
-    }
-  }
-  }
-  };
-  if constexpr (bwd_early_pass<D, DV, RT>()) load_pass();
   const double scale = a.scale;
   for (int r0 = 0; any && r0 < a.R; r0 += RT) {
     __syncthreads();  // the previous tile is no longer read
@@ -728,10 +667,55 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     }
   }
 
-  if constexpr (!bwd_early_pass<D, DV, RT>()) load_pass();
   // slot gradients out: kept slots -> the cache gradient, overwritten ones
   // -> the appended rows' gradient (the cache entry gets 0), the rest ->
-  // the pass-through alone.
+  // the pass-through alone.  The pass-through values are all loaded before
+  // the first store: the host refuses overlapping buffers, but the compiler
+  // cannot know that and would otherwise wait for each load in turn.
+  float pk[4][DT], pv[4][VT];
+  if constexpr (sizeof(T) == 4) {  // masked-off lanes load nothing (see bwd_ld_or0)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t js = s0 + 16 * wave + 4 * i + lq;
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++)
+        pk[i][dt] = (a.d_kc_out && js < a.M)
+                        ? bwd_ld<T>(a.d_kc_out, (grp * a.M + js) * D + dc0 + 16 * dt + li) : 0.f;
+#pragma unroll
+      for (int vt = 0; vt < VT; vt++)
+        pv[i][vt] = (a.d_vc_out && js < a.M)
+                        ? bwd_ld<T>(a.d_vc_out, (grp * a.M + js) * DV + vc0 + 16 * vt + li) : 0.f;
+    }
+  } else {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) pk[i][dt] = 0.f;
+#pragma unroll
+    for (int vt = 0; vt < VT; vt++) pv[i][vt] = 0.f;
+  }
+  if (a.d_kc_out) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t js = s0 + 16 * wave + 4 * i + lq, jc = js < a.M ? js : a.M - 1;
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++)
+        pk[i][dt] = bwd_ld_or0<T>(js < a.M, a.d_kc_out, (grp * a.M + js) * D + dc0 + 16 * dt + li,
+                                  (grp * a.M + jc) * D + dc0 + 16 * dt + li);
+    }
+  }
+  if (a.d_vc_out) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t js = s0 + 16 * wave + 4 * i + lq, jc = js < a.M ? js : a.M - 1;
+#pragma unroll
+      for (int vt = 0; vt < VT; vt++)
+        pv[i][vt] = bwd_ld_or0<T>(js < a.M, a.d_vc_out,
+                                  (grp * a.M + js) * DV + vc0 + 16 * vt + li,
+                                  (grp * a.M + jc) * DV + vc0 + 16 * vt + li);
+    }
+  }
+  }
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int64_t js = s0 + 16 * wave + 4 * i + lq;
@@ -772,21 +756,38 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
 }
 
 // dq_r = sum over the chunks its row can see of the partials (0 for rows
-// that are not valid).
+// that are not valid).  One workgroup per row: thread (cl, d) sums column d
+// over the chunks cl, cl + CL, ... (CL = kBwdThreads / D column lanes, four
+// independent sums so that several loads are in flight), then the CL sums
+// are merged in LDS.  D divides kBwdThreads (the host admits D in {64, 128}).
 template <typename T>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a) {
-  const int64_t row = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  if (row >= a.B * a.Hq * a.Q) return;
+  __shared__ double part_s[kBwdThreads];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int D = static_cast<int>(a.D), CL = kBwdThreads / D, cl = tid / D, d = tid % D;
   const int64_t t = row % a.Q, hq = (row / a.Q) % a.Hq, b = row / (a.Hq * a.Q);
   int64_t len, n;
   bwd_row_info(a, b, &len, &n);
   const int64_t kvh = hq / a.G, g = hq % a.G, r = g * a.Q + t, grp = b * a.Hk + kvh;
   const int64_t nc = t < n ? (len + t) / kBwdSlots + 1 : 0;  // chunks holding slots <= len + t
-  for (int64_t d = lane; d < a.D; d += kWave) {
+  const int64_t cs = static_cast<int64_t>(a.R) * D;          // one chunk's stride
+  const double* p = a.ws_dq + (grp * a.nchunk * a.R + r) * D + d;
+  double s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+  int64_t c = cl;
+  for (; c + 3 * CL < nc; c += 4 * CL) {
+    s0 += p[c * cs];
+    s1 += p[(c + CL) * cs];
+    s2 += p[(c + 2 * CL) * cs];
+    s3 += p[(c + 3 * CL) * cs];
+  }
+  for (; c < nc; c += CL) s0 += p[c * cs];
+  part_s[tid] = (s0 + s1) + (s2 + s3);
+  __syncthreads();
+  if (tid < D) {
     double acc = 0;
-    for (int64_t c = 0; c < nc; c++) acc += a.ws_dq[((grp * a.nchunk + c) * a.R + r) * a.D + d];
-    bwd_st<T>(a.g_query, row * a.D + d, static_cast<float>(acc));
+    for (int k = 0; k < CL; k++) acc += part_s[k * D + tid];
+    bwd_st<T>(a.g_query, row * D + tid, static_cast<float>(acc));
   }
 }
 

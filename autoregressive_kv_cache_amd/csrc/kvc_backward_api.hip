@@ -43,7 +43,7 @@ void launch_bwd_chunk(const kvc::BwdArgs& a, hipStream_t s) {
 template <typename T>
 void launch_bwd_dq(const kvc::BwdArgs& a, hipStream_t s) {
   const int64_t rows = a.B * a.Hq * a.Q;
-  hipLaunchKernelGGL((kvc::bwd_dq_kernel<T>), dim3(static_cast<unsigned>((rows + 3) / 4)),
+  hipLaunchKernelGGL((kvc::bwd_dq_kernel<T>), dim3(static_cast<unsigned>(rows)),
                      dim3(kvc::kBwdThreads), 0, s, a);
 }
 #define KVC_BWD(T, CODE, D, DV)                                                            \
@@ -134,11 +134,11 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
     a.row_groups = static_cast<int32_t>(tiles < 1 ? 1 : tiles < kvc::kBwdMaxRowGroups ? tiles : kvc::kBwdMaxRowGroups);
   }
   {  // every grid must fit one launch: the chunk grids (chunks x row or
-     // column groups) and the per-row grids (4 packed rows per workgroup)
+     // column groups) and the per-row grids (one row per workgroup for dq)
     int64_t x;
     if (!mul_ok(d->B * d->Hk, a.nchunk, kMaxElems, &x) ||
         !mul_ok(x, a.row_groups > 4 ? a.row_groups : 4, kMaxBwdWorkgroups, &x) ||
-        !mul_ok(d->B * d->Hq, d->Q, kMaxElems, &x) || (x + 3) / 4 > kMaxBwdWorkgroups)
+        !mul_ok(d->B * d->Hq, d->Q, kMaxElems, &x) || x > kMaxBwdWorkgroups)
       return KVC_ERR_SHAPE;
   }
   a.scale = static_cast<float>(sc);
