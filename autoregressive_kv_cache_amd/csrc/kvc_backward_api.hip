@@ -26,6 +26,7 @@ struct BwdEntry {
 };
 template <typename T, int D, int DV>
 void launch_bwd_stats(const kvc::BwdArgs& a, hipStream_t s) {
+  static_assert(kvc::kBwdThreads % D == 0, "bwd_dq spreads a row's D columns over the workgroup");
   hipLaunchKernelGGL((kvc::bwd_stats_kernel<T, D, DV>),
                      dim3(static_cast<unsigned>(a.B * a.Hk * a.nchunk * a.row_groups)),
                      dim3(kvc::kBwdThreads), 0, s, a);
