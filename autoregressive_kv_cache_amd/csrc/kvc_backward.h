@@ -540,6 +540,68 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(BwdArgs a) {
   }
 }
 
+// Piece p (16 bytes, slot p / (N / EP), elements from (p % (N / EP)) EP on)
+// of a chunk's slot rows of the pass-through gradient src [B, Hk, M, N]:
+// zeros for a NULL src and past M.  Every lane loads (slots past M read the
+// last slot's row) and a select zeroes, so no load waits inside a branch.
+template <typename T, int N>
+__device__ __forceinline__ uint4 bwd_pass_piece(const BwdArgs& a, const void* src, int64_t grp,
+                                                int64_t s0, int p) {
+  constexpr int EP = 16 / static_cast<int>(sizeof(T)), PR = N / EP;
+  if (!src) return uint4{0u, 0u, 0u, 0u};
+  const int64_t js = s0 + p / PR, jc = js < a.M ? js : a.M - 1;
+  const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const T*>(src) +
+                                                  (grp * a.M + jc) * N + (p % PR) * EP);
+  return js < a.M ? x : uint4{0u, 0u, 0u, 0u};
+}
+
+// Piece p of the chunk's slot gradients: the pass-through x plus the
+// products' part from the LDS tile (pitch TP floats), rounded once to T.
+// Kept slots -> g_cache; appended ones (len <= j < len + n) -> their row of
+// g_new, with zeros in g_cache; nothing past M.
+template <typename T, int N, int TP>
+__device__ __forceinline__ void bwd_piece_out(const BwdArgs& a, int64_t grp, int64_t len,
+                                              int64_t n, int64_t s0, int p, const uint4& x,
+                                              const float* tile, void* g_cache, void* g_new) {
+  constexpr int EP = 16 / static_cast<int>(sizeof(T)), PR = N / EP;
+  const int sl = p / PR, col = (p % PR) * EP;
+  const int64_t js = s0 + sl;
+  if (js >= a.M) return;
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  float v[EP];
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {  // little-endian: element 2k in the low half
+      v[2 * k] = __uint_as_float(w[k] << 16);
+      v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; k++) v[k] = __uint_as_float(w[k]);
+  }
+  const float* t = tile + sl * TP + col;
+#pragma unroll
+  for (int e = 0; e < EP; e++) v[e] = t[e] + v[e];
+  uint32_t y[4];
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int k = 0; k < 4; k++)
+      y[k] = static_cast<uint32_t>(f32_to_bf16(v[2 * k])) |
+             (static_cast<uint32_t>(f32_to_bf16(v[2 * k + 1])) << 16);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; k++) y[k] = __float_as_uint(v[k]);
+  }
+  const uint4 out{y[0], y[1], y[2], y[3]};
+  uint4* at = reinterpret_cast<uint4*>(static_cast<T*>(g_cache) + (grp * a.M + js) * N + col);
+  if (js >= len && js < len + n) {
+    *reinterpret_cast<uint4*>(static_cast<T*>(g_new) + (grp * a.Q + (js - len)) * N + col) = out;
+    *at = uint4{0u, 0u, 0u, 0u};
+  } else {
+    *at = out;
+  }
+}
+
 // One workgroup per (b, KV head, chunk of kBwdSlots slots, column group):
 // dS for the chunk's slots and every packed row, and for the group's
 // columns the slot gradients of the chunk and the chunk's share of every
@@ -667,85 +729,42 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     }
   }
 
-  // slot gradients out: kept slots -> the cache gradient, overwritten ones
-  // -> the appended rows' gradient (the cache entry gets 0), the rest ->
-  // the pass-through alone.  The pass-through values are all loaded before
-  // the first store: the host refuses overlapping buffers, but the compiler
-  // cannot know that and would otherwise wait for each load in turn.
-  float pk[4][DT], pv[4][VT];
-  if constexpr (sizeof(T) == 4) {  // masked-off lanes load nothing (see bwd_ld_or0)
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int64_t js = s0 + 16 * wave + 4 * i + lq;
-#pragma unroll
-      for (int dt = 0; dt < DT; dt++)
-        pk[i][dt] = (a.d_kc_out && js < a.M)
-                        ? bwd_ld<T>(a.d_kc_out, (grp * a.M + js) * D + dc0 + 16 * dt + li) : 0.f;
-#pragma unroll
-      for (int vt = 0; vt < VT; vt++)
-        pv[i][vt] = (a.d_vc_out && js < a.M)
-                        ? bwd_ld<T>(a.d_vc_out, (grp * a.M + js) * DV + vc0 + 16 * vt + li) : 0.f;
-    }
-  } else {
+  // Slot gradients out, in 16-byte pieces of slot rows: each wave's dK'/dV'
+  // strip goes through LDS (the K'/V' tiles are no longer read), so that a
+  // thread adds the pass-through to whole pieces and stores them with one
+  // instruction each.  All pass-through pieces are loaded before the first
+  // store: the host refuses overlapping buffers, but the compiler cannot
+  // know that and would otherwise wait for each load in turn.
+  static_assert(CG == 1, "the pieces span whole slot rows");
+  constexpr int EP = 16 / static_cast<int>(sizeof(T));  // elements per piece
+  constexpr int NPK = C * (D / EP) / kBwdThreads, NPV = C * (DV / EP) / kBwdThreads;
+  static_assert(D % EP == 0 && DV % EP == 0 && C * (D / EP) % kBwdThreads == 0 &&
+                    C * (DV / EP) % kBwdThreads == 0, "piece shape");
+  __syncthreads();  // every wave is past its last read of k_s / v_s
 #pragma unroll
   for (int i = 0; i < 4; i++) {
+    const int sl = 16 * wave + 4 * i + lq;
 #pragma unroll
-    for (int dt = 0; dt < DT; dt++) pk[i][dt] = 0.f;
+    for (int dt = 0; dt < DT; dt++) k_s[sl * KP + 16 * dt + li] = static_cast<float>(gk[dt][i]);
 #pragma unroll
-    for (int vt = 0; vt < VT; vt++) pv[i][vt] = 0.f;
+    for (int vt = 0; vt < VT; vt++) v_s[sl * VP + 16 * vt + li] = static_cast<float>(gv[vt][i]);
   }
-  if (a.d_kc_out) {
+  uint4 xk[NPK], xv[NPV];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int64_t js = s0 + 16 * wave + 4 * i + lq, jc = js < a.M ? js : a.M - 1;
+  for (int u = 0; u < NPK; u++)
+    xk[u] = bwd_pass_piece<T, D>(a, a.d_kc_out, grp, s0, tid + u * kBwdThreads);
 #pragma unroll
-      for (int dt = 0; dt < DT; dt++)
-        pk[i][dt] = bwd_ld_or0<T>(js < a.M, a.d_kc_out, (grp * a.M + js) * D + dc0 + 16 * dt + li,
-                                  (grp * a.M + jc) * D + dc0 + 16 * dt + li);
-    }
-  }
-  if (a.d_vc_out) {
+  for (int u = 0; u < NPV; u++)
+    xv[u] = bwd_pass_piece<T, DV>(a, a.d_vc_out, grp, s0, tid + u * kBwdThreads);
+  __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int64_t js = s0 + 16 * wave + 4 * i + lq, jc = js < a.M ? js : a.M - 1;
+  for (int u = 0; u < NPK; u++)
+    bwd_piece_out<T, D, KP>(a, grp, len, n, s0, tid + u * kBwdThreads, xk[u], k_s, a.g_kc,
+                            a.g_new_key);
 #pragma unroll
-      for (int vt = 0; vt < VT; vt++)
-        pv[i][vt] = bwd_ld_or0<T>(js < a.M, a.d_vc_out,
-                                  (grp * a.M + js) * DV + vc0 + 16 * vt + li,
-                                  (grp * a.M + jc) * DV + vc0 + 16 * vt + li);
-    }
-  }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int64_t js = s0 + 16 * wave + 4 * i + lq;
-    if (js >= a.M) continue;
-    const bool appended = js >= len && js < len + n;
-#pragma unroll
-    for (int dt = 0; dt < DT; dt++) {
-      const int d = dc0 + 16 * dt + li;
-      const int64_t at = (grp * a.M + js) * D + d;
-      const float total = static_cast<float>(gk[dt][i]) + pk[i][dt];
-      if (appended) {
-        bwd_st<T>(a.g_new_key, (grp * a.Q + (js - len)) * D + d, total);
-        bwd_st<T>(a.g_kc, at, 0.f);
-      } else {
-        bwd_st<T>(a.g_kc, at, total);
-      }
-    }
-#pragma unroll
-    for (int vt = 0; vt < VT; vt++) {
-      const int d = vc0 + 16 * vt + li;
-      const int64_t at = (grp * a.M + js) * DV + d;
-      const float total = static_cast<float>(gv[vt][i]) + pv[i][vt];
-      if (appended) {
-        bwd_st<T>(a.g_new_value, (grp * a.Q + (js - len)) * DV + d, total);
-        bwd_st<T>(a.g_vc, at, 0.f);
-      } else {
-        bwd_st<T>(a.g_vc, at, total);
-      }
-    }
-  }
+  for (int u = 0; u < NPV; u++)
+    bwd_piece_out<T, DV, VP>(a, grp, len, n, s0, tid + u * kBwdThreads, xv[u], v_s, a.g_vc,
+                             a.g_new_value);
   // appended rows that do not exist (t >= n, rejected rows): zero gradient
   if (c == 0 && cg == 0) {
     for (int64_t idx = tid; idx < (a.Q - n) * D; idx += kBwdThreads)
