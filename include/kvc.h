@@ -83,7 +83,7 @@ enum {
   KVC_ERR_WORKSPACE = -5,   /* workspace_bytes < kvc_workspace_bytes() */
   KVC_ERR_ALIAS = -6,       /* an output overlaps an input or another output */
   KVC_ERR_HIP = -7,         /* a kernel launch failed (HIP error) */
-  KVC_ERR_UNSUPPORTED = -8  /* kvc_step_paged: a shape or block size it does not take */
+  KVC_ERR_UNSUPPORTED = -8  /* a shape, block size or buffer alignment the entry point does not take */
 };
 
 /* Per-row status written to row_status[b]. */

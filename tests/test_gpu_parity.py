@@ -773,3 +773,33 @@ def test_backward_against_oracle(wl, upstream, dtype):
             err = np.abs(got - want) - BWD_TOL[dtype] * (1 + np.abs(want))
             assert err.max() <= 0, \
                 f"{wl.name}/{dtype}/{upstream}/{seed}: {name} off by {err.max():.3e}"
+
+
+@pytest.mark.parametrize("which", ["d_key_cache_out", "g_value_cache", "g_new_key"])
+def test_backward_refuses_misaligned_gradient_buffers(which):
+    """The slot gradients move in 16-byte pieces: a gradient buffer, in or
+    out, that is not 16-byte aligned is refused (KVC_ERR_UNSUPPORTED) before
+    anything runs, and the outputs stay as they were."""
+    wl = BWD_CASES[0]
+    say(f"[case] backward misaligned {which}")
+    dinp = {k: v.to(DEV) for k, v in make_inputs(wl, 0, "cpu").items()}
+    B, Hq, Q, D = dinp["query"].shape
+    Hk, M = dinp["key_cache"].shape[1], dinp["key_cache"].shape[2]
+    ups = {"d_attention": None, "d_context": None,
+           "d_key_cache_out": torch.zeros(B, Hk, M, D, dtype=dinp["query"].dtype, device=DEV),
+           "d_value_cache_out": None}
+    outs = {k: torch.full_like(dinp[src], float("nan")) for k, src in
+            (("g_query", "query"), ("g_new_key", "new_key"), ("g_new_value", "new_value"),
+             ("g_key_cache", "key_cache"), ("g_value_cache", "value_cache"))}
+    if which in ups:
+        ups[which] = misaligned(ups[which])
+    else:
+        outs[which] = misaligned(outs[which])
+    mask = dinp["append_mask"].contiguous().view(torch.uint8)
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kvc_step_backward(dinp["query"], dinp["new_key"], dinp["new_value"],
+                              dinp["key_cache"], dinp["value_cache"], dinp["lengths"], mask,
+                              *ups.values(), **outs, scale=wl.scale)
+    assert e.value.code == -8
+    torch.cuda.synchronize()
+    assert all(torch.isnan(v).all() for v in outs.values())
