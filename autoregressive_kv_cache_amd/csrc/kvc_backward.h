@@ -179,41 +179,86 @@ constexpr int bwd_pitch() {
   return N + 4;
 }
 
-// K', V' rows of the chunk starting at slot s0 (zeros past nvis).  Every
-// load is issued before the first LDS store, so the loads overlap.
+// N consecutive elements of row `off` of a T tensor, widened to fp32, in
+// 16-byte loads (the row and the tensor are 16-byte aligned; the host
+// checks); ok = false gives zeros (the loads then read the same row, which
+// the caller chooses valid).
+template <typename T, int N>
+__device__ __forceinline__ void bwd_row_slice(const void* src, int64_t off, bool ok, float (&x)[N]) {
+  if constexpr (sizeof(T) == 2) {
+    static_assert(N % 8 == 0, "slice");
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + off);
+    uint4 w[N / 8];
+#pragma unroll
+    for (int u = 0; u < N / 8; u++) w[u] = p[u];
+#pragma unroll
+    for (int u = 0; u < N / 8; u++) {
+      const uint32_t h[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        x[8 * u + 2 * e] = ok ? __uint_as_float(h[e] << 16) : 0.f;
+        x[8 * u + 2 * e + 1] = ok ? __uint_as_float(h[e] & 0xffff0000u) : 0.f;
+      }
+    }
+  } else {
+    static_assert(N % 4 == 0, "slice");
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + off);
+    float4 w[N / 4];
+#pragma unroll
+    for (int u = 0; u < N / 4; u++) w[u] = p[u];
+#pragma unroll
+    for (int u = 0; u < N / 4; u++) {
+      x[4 * u] = ok ? w[u].x : 0.f;
+      x[4 * u + 1] = ok ? w[u].y : 0.f;
+      x[4 * u + 2] = ok ? w[u].z : 0.f;
+      x[4 * u + 3] = ok ? w[u].w : 0.f;
+    }
+  }
+}
+
+// K', V' rows of the chunk starting at slot s0 (zeros past nvis), in 16-byte
+// pieces of slot rows.  Every load is issued before the first LDS store, so
+// the loads overlap; slots past nvis read the last visible slot's row (nvis >
+// s0 here) and a select zeroes them.
 template <typename T, int D, int DV>
 __device__ inline void bwd_stage_kv(const BwdArgs& a, int64_t grp, int64_t len, int64_t nvis,
                                     int64_t s0, float* k_s, float* v_s) {
   constexpr int C = kBwdSlots, KP = bwd_pitch<D>(), VP = bwd_pitch<DV>();
-  constexpr int NK = C * D / kBwdThreads, NV = C * DV / kBwdThreads;
-  static_assert(C * D % kBwdThreads == 0 && C * DV % kBwdThreads == 0, "staging shape");
+  constexpr int EP = 16 / static_cast<int>(sizeof(T));  // elements per piece
+  constexpr int NPK = C * (D / EP) / kBwdThreads, NPV = C * (DV / EP) / kBwdThreads;
+  static_assert(D % EP == 0 && DV % EP == 0 && C * (D / EP) % kBwdThreads == 0 &&
+                    C * (DV / EP) % kBwdThreads == 0, "staging shape");
   const int tid = threadIdx.x;
-  float kx[NK], vx[NV];
+  float kx[NPK][EP], vx[NPV][EP];
 #pragma unroll
-  for (int i = 0; i < NK; i++) {
-    const int idx = tid + i * kBwdThreads, sl = idx / D, d = idx % D;
-    const int64_t j = s0 + sl;
-    int64_t off = 0;  // bf16: slots past nvis read the last visible slot's row (nvis > s0 here)
-    const void* src = bwd_key_src(a, grp, len, (sizeof(T) == 4 || j < nvis) ? j : nvis - 1, &off);
-    kx[i] = bwd_ld_or0<T>(j < nvis, src, off + d, off + d);
-  }
-#pragma unroll
-  for (int i = 0; i < NV; i++) {
-    const int idx = tid + i * kBwdThreads, sl = idx / DV, d = idx % DV;
+  for (int u = 0; u < NPK; u++) {
+    const int p = tid + u * kBwdThreads, sl = p / (D / EP), col = (p % (D / EP)) * EP;
     const int64_t j = s0 + sl;
     int64_t off = 0;
-    const void* src = bwd_value_src(a, grp, len, (sizeof(T) == 4 || j < nvis) ? j : nvis - 1, &off);
-    vx[i] = bwd_ld_or0<T>(j < nvis, src, off + d, off + d);
+    const void* src = bwd_key_src(a, grp, len, j < nvis ? j : nvis - 1, &off);
+    bwd_row_slice<T, EP>(src, off + col, j < nvis, kx[u]);
   }
 #pragma unroll
-  for (int i = 0; i < NK; i++) {
-    const int idx = tid + i * kBwdThreads;
-    k_s[(idx / D) * KP + idx % D] = kx[i];
+  for (int u = 0; u < NPV; u++) {
+    const int p = tid + u * kBwdThreads, sl = p / (DV / EP), col = (p % (DV / EP)) * EP;
+    const int64_t j = s0 + sl;
+    int64_t off = 0;
+    const void* src = bwd_value_src(a, grp, len, j < nvis ? j : nvis - 1, &off);
+    bwd_row_slice<T, EP>(src, off + col, j < nvis, vx[u]);
   }
 #pragma unroll
-  for (int i = 0; i < NV; i++) {
-    const int idx = tid + i * kBwdThreads;
-    v_s[(idx / DV) * VP + idx % DV] = vx[i];
+  for (int u = 0; u < NPK; u++) {
+    const int p = tid + u * kBwdThreads;
+    float* dst = k_s + (p / (D / EP)) * KP + (p % (D / EP)) * EP;
+#pragma unroll
+    for (int e = 0; e < EP; e++) dst[e] = kx[u][e];
+  }
+#pragma unroll
+  for (int u = 0; u < NPV; u++) {
+    const int p = tid + u * kBwdThreads;
+    float* dst = v_s + (p / (DV / EP)) * VP + (p % (DV / EP)) * EP;
+#pragma unroll
+    for (int e = 0; e < EP; e++) dst[e] = vx[u][e];
   }
 }
 
@@ -349,42 +394,6 @@ __device__ inline void bwd_scores(const float* q_s, const float* o_s, const floa
                                                dov, 0, 0, 0);
 }
 
-// N consecutive elements of row `off` of a T tensor, widened to fp32, in
-// 16-byte loads (the row and the tensor are 16-byte aligned; the host
-// checks); ok = false gives zeros (the loads then read the same row, which
-// the caller chooses valid).
-template <typename T, int N>
-__device__ __forceinline__ void bwd_row_slice(const void* src, int64_t off, bool ok, float (&x)[N]) {
-  if constexpr (sizeof(T) == 2) {
-    static_assert(N % 8 == 0, "slice");
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + off);
-    uint4 w[N / 8];
-#pragma unroll
-    for (int u = 0; u < N / 8; u++) w[u] = p[u];
-#pragma unroll
-    for (int u = 0; u < N / 8; u++) {
-      const uint32_t h[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        x[8 * u + 2 * e] = ok ? __uint_as_float(h[e] << 16) : 0.f;
-        x[8 * u + 2 * e + 1] = ok ? __uint_as_float(h[e] & 0xffff0000u) : 0.f;
-      }
-    }
-  } else {
-    static_assert(N % 4 == 0, "slice");
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + off);
-    float4 w[N / 4];
-#pragma unroll
-    for (int u = 0; u < N / 4; u++) w[u] = p[u];
-#pragma unroll
-    for (int u = 0; u < N / 4; u++) {
-      x[4 * u] = ok ? w[u].x : 0.f;
-      x[4 * u + 1] = ok ? w[u].y : 0.f;
-      x[4 * u + 2] = ok ? w[u].z : 0.f;
-      x[4 * u + 3] = ok ? w[u].w : 0.f;
-    }
-  }
-}
 
 // One workgroup per (b, KV head, chunk of kBwdSlots slots, row group): for
 // every valid packed row of its row tiles, over the chunk's slots it sees, m_c = max s_j, l_c =
