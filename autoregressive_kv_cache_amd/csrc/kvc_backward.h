@@ -264,15 +264,20 @@ __device__ inline void bwd_stage_kv(const BwdArgs& a, int64_t grp, int64_t len, 
 
 // The inputs of one tile of 16 packed rows, held in registers from their
 // loads until the tile before has finished with LDS (so the loads of tile
-// r + 1 are in flight while tile r computes): q and dO (zeros for rows that
-// are not valid), this lane's four attention-gradient entries (rows
-// 4 i + l / 16 of the tile, its slot j; 0 where not visible), and for
-// threads below 16 the row's m, l and sum P dP (bwd_chunk).
-template <int D, int DV, int RT>
+// r + 1 are in flight while tile r computes): q and dO as raw 16-byte pieces
+// of their rows (zeros for rows that are not valid; widened only when the
+// tile is committed to LDS, so no load is waited for earlier), this lane's
+// four attention-gradient entries (rows 4 i + l / 16 of the tile, its slot
+// j; 0 where not visible), and for threads below 16 the row's m, l and
+// sum P dP (bwd_chunk).
+template <typename T, int D, int DV, int RT>
 struct BwdTileRegs {
-  static constexpr int NQ = (RT * D + kBwdThreads - 1) / kBwdThreads;
-  static constexpr int NO = (RT * DV + kBwdThreads - 1) / kBwdThreads;
-  float q[NQ], o[NO];
+  static constexpr int EP = 16 / static_cast<int>(sizeof(T));  // elements per piece
+  static constexpr int PQ = RT * D / EP, PO = RT * DV / EP;     // pieces per tile
+  static constexpr int NQ = (PQ + kBwdThreads - 1) / kBwdThreads;
+  static constexpr int NO = (PO + kBwdThreads - 1) / kBwdThreads;
+  static_assert(D % EP == 0 && DV % EP == 0, "row pieces");
+  uint4 q[NQ], o[NO];
   float da[RT / 4];  // [16-row block][i]
   double st[3];
 };
@@ -280,8 +285,9 @@ struct BwdTileRegs {
 template <typename T, int D, int DV, int RT>
 __device__ inline void bwd_fetch_tile(const BwdArgs& a, int64_t b, int64_t kvh, int64_t len,
                                       int64_t n, int r0, int64_t j, bool stats,
-                                      BwdTileRegs<D, DV, RT>& x) {
-  using X = BwdTileRegs<D, DV, RT>;
+                                      BwdTileRegs<T, D, DV, RT>& x) {
+  using X = BwdTileRegs<T, D, DV, RT>;
+  constexpr int EP = X::EP;
   const int tid = threadIdx.x, lq = (tid % kWave) / 16;
   const int Q = static_cast<int>(a.Q);
   // the head's packed row r as a (b, query head, token) row; rows past R
@@ -290,23 +296,24 @@ __device__ inline void bwd_fetch_tile(const BwdArgs& a, int64_t b, int64_t kvh, 
     const int rc = r < a.R ? r : a.R - 1;
     return (b * a.Hq + kvh * a.G + rc / Q) * a.Q + rc % Q;
   };
+  // q and dO pieces: a piece of a row that is not valid is not loaded
+#pragma unroll
+  for (int u = 0; u < X::NQ; u++) {
+    const int p = tid + u * kBwdThreads, r = r0 + p / (D / EP);
+    x.q[u] = uint4{0u, 0u, 0u, 0u};
+    if (p < X::PQ && r < a.R && r % Q < n)
+      x.q[u] = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.query) + qrow(r) * D +
+                                               (p % (D / EP)) * EP);
+  }
+#pragma unroll
+  for (int u = 0; u < X::NO; u++) {
+    const int p = tid + u * kBwdThreads, r = r0 + p / (DV / EP);
+    x.o[u] = uint4{0u, 0u, 0u, 0u};
+    if (a.d_ctx && p < X::PO && r < a.R && r % Q < n)
+      x.o[u] = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.d_ctx) + qrow(r) * DV +
+                                               (p % (DV / EP)) * EP);
+  }
   if constexpr (sizeof(T) == 4) {  // masked-off lanes load nothing (see bwd_ld_or0)
-#pragma unroll
-    for (int i = 0; i < X::NQ; i++) {
-      const int idx = tid + i * kBwdThreads;
-      const int rr = idx / D, d = idx % D, r = r0 + rr;
-      const int g = r / Q, t = r % Q;
-      x.q[i] = (idx < RT * D && r < a.R && t < n)
-                   ? bwd_ld<T>(a.query, ((b * a.Hq + kvh * a.G + g) * a.Q + t) * D + d) : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < X::NO; i++) {
-      const int idx = tid + i * kBwdThreads;
-      const int rr = idx / DV, d = idx % DV, r = r0 + rr;
-      const int g = r / Q, t = r % Q;
-      x.o[i] = (a.d_ctx && idx < RT * DV && r < a.R && t < n)
-                   ? bwd_ld<T>(a.d_ctx, ((b * a.Hq + kvh * a.G + g) * a.Q + t) * DV + d) : 0.f;
-    }
 #pragma unroll
     for (int k = 0; k < RT / 4; k++) {
       const int r = r0 + 16 * (k / 4) + 4 * (k % 4) + lq;
@@ -315,24 +322,6 @@ __device__ inline void bwd_fetch_tile(const BwdArgs& a, int64_t b, int64_t kvh, 
       x.da[k] = vis ? bwd_ld<T>(a.d_att, ((b * a.Hq + kvh * a.G + g) * a.Q + t) * a.M + j) : 0.f;
     }
   } else {
-#pragma unroll
-  for (int i = 0; i < X::NQ; i++) {
-    const int idx = tid + i * kBwdThreads;
-    const int rr = idx / D, d = idx % D, r = r0 + rr;
-    const bool ok = idx < RT * D && r < a.R && r % Q < n;
-    x.q[i] = bwd_ld_or0<T>(ok, a.query, qrow(r) * D + d, qrow(r) * D + d);
-  }
-#pragma unroll
-  for (int i = 0; i < X::NO; i++) x.o[i] = 0.f;
-  if (a.d_ctx) {
-#pragma unroll
-    for (int i = 0; i < X::NO; i++) {
-      const int idx = tid + i * kBwdThreads;
-      const int rr = idx / DV, d = idx % DV, r = r0 + rr;
-      const bool ok = idx < RT * DV && r < a.R && r % Q < n;
-      x.o[i] = bwd_ld_or0<T>(ok, a.d_ctx, qrow(r) * DV + d, qrow(r) * DV + d);
-    }
-  }
 #pragma unroll
   for (int k = 0; k < RT / 4; k++) x.da[k] = 0.f;
   if (a.d_att) {
@@ -356,20 +345,50 @@ __device__ inline void bwd_fetch_tile(const BwdArgs& a, int64_t b, int64_t kvh, 
   }
 }
 
+// 16-byte piece w of a T row, widened to fp32.
+template <typename T>
+__device__ __forceinline__ void bwd_widen(const uint4& w, float (&v)[16 / sizeof(T)]) {
+  const uint32_t h[4] = {w.x, w.y, w.z, w.w};
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {  // little-endian: element 2k in the low half
+      v[2 * k] = __uint_as_float(h[k] << 16);
+      v[2 * k + 1] = __uint_as_float(h[k] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; k++) v[k] = __uint_as_float(h[k]);
+  }
+}
+
 // q and dO of the tile into LDS (row pitches KP and VP elements).
-template <int D, int DV, int RT, int KP = bwd_pitch<D>(), int VP = bwd_pitch<DV>()>
-__device__ inline void bwd_commit_tile(const BwdTileRegs<D, DV, RT>& x, float* q_s, float* o_s) {
-  using X = BwdTileRegs<D, DV, RT>;
+template <typename T, int D, int DV, int RT, int KP = bwd_pitch<D>(), int VP = bwd_pitch<DV>()>
+__device__ inline void bwd_commit_tile(const BwdTileRegs<T, D, DV, RT>& x, float* q_s,
+                                       float* o_s) {
+  using X = BwdTileRegs<T, D, DV, RT>;
+  constexpr int EP = X::EP;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < X::NQ; i++) {
-    const int idx = tid + i * kBwdThreads;
-    if (idx < RT * D) q_s[(idx / D) * KP + idx % D] = x.q[i];
+  for (int u = 0; u < X::NQ; u++) {
+    const int p = tid + u * kBwdThreads;
+    if (p < X::PQ) {
+      float v[EP];
+      bwd_widen<T>(x.q[u], v);
+      float* dst = q_s + (p / (D / EP)) * KP + (p % (D / EP)) * EP;
+#pragma unroll
+      for (int e = 0; e < EP; e++) dst[e] = v[e];
+    }
   }
 #pragma unroll
-  for (int i = 0; i < X::NO; i++) {
-    const int idx = tid + i * kBwdThreads;
-    if (idx < RT * DV) o_s[(idx / DV) * VP + idx % DV] = x.o[i];
+  for (int u = 0; u < X::NO; u++) {
+    const int p = tid + u * kBwdThreads;
+    if (p < X::PO) {
+      float v[EP];
+      bwd_widen<T>(x.o[u], v);
+      float* dst = o_s + (p / (DV / EP)) * VP + (p % (DV / EP)) * EP;
+#pragma unroll
+      for (int e = 0; e < EP; e++) dst[e] = v[e];
+    }
   }
 }
 
@@ -428,7 +447,7 @@ bwd_stats_kernel(BwdArgs a) {
   const double scale = a.scale;
   const int64_t j = s0 + 16 * wave + li;  // this lane's slot
   const int step = a.row_groups * RT;
-  BwdTileRegs<D, DV, RT> nx;  // the next tile's inputs, loading while this one computes
+  BwdTileRegs<T, D, DV, RT> nx;  // the next tile's inputs, loading while this one computes
   bwd_fetch_tile<T, D, DV, RT>(a, b, kvh, len, n, rg * RT, j, false, nx);
   // this lane's K' and V' operand slices (slots past nvis: zeros, read from
   // the last visible slot's row, nvis > s0 here)
@@ -443,7 +462,7 @@ bwd_stats_kernel(BwdArgs a) {
   }
   for (int r0 = rg * RT; r0 < a.R; r0 += step) {
     __syncthreads();  // the previous tile is no longer read
-    bwd_commit_tile<D, DV, RT, QP, OP>(nx, q_s, o_s);
+    bwd_commit_tile<T, D, DV, RT, QP, OP>(nx, q_s, o_s);
     float da[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) da[i] = nx.da[i];
@@ -644,7 +663,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
   const int64_t nvis = n > 0 ? len + n : 0;
   const bool any = s0 < nvis;  // nvis <= M
   const int64_t j = s0 + 16 * wave + li;  // this lane's slot in the score tile
-  BwdTileRegs<D, DV, RT> nx;  // the next tile's inputs, loading while this one computes
+  BwdTileRegs<T, D, DV, RT> nx;  // the next tile's inputs, loading while this one computes
   if (any) {
     bwd_fetch_tile<T, D, DV, RT>(a, b, kvh, len, n, 0, j, true, nx);
     bwd_stage_kv<T, D, DV>(a, grp, len, nvis, s0, k_s, v_s);
@@ -660,7 +679,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
   const double scale = a.scale;
   for (int r0 = 0; any && r0 < a.R; r0 += RT) {
     __syncthreads();  // the previous tile is no longer read
-    bwd_commit_tile<D, DV, RT>(nx, q_s, o_s);
+    bwd_commit_tile<T, D, DV, RT>(nx, q_s, o_s);
     if (tid < RT) {
       st_s[tid][0] = nx.st[0];
       st_s[tid][1] = nx.st[1];

@@ -100,12 +100,12 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
   if (d->Q > 0 && (!query || !new_key || !new_value || !append_mask || !g_query || !g_new_key ||
                    !g_new_value))
     return KVC_ERR_NULL;
-  {  // the K'/V' row slices and the slot gradients move in 16-byte pieces
+  {  // the K'/V', q and dO rows and the slot gradients move in 16-byte pieces
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
     if (!al16(key_cache) || !al16(value_cache) || !al16(d_key_cache_out) ||
         !al16(d_value_cache_out) || !al16(g_key_cache) || !al16(g_value_cache) ||
-        (d->Q > 0 && (!al16(new_key) || !al16(new_value) || !al16(g_new_key) ||
-                      !al16(g_new_value))))
+        (d->Q > 0 && (!al16(query) || !al16(new_key) || !al16(new_value) ||
+                      !al16(d_context) || !al16(g_new_key) || !al16(g_new_value))))
       return KVC_ERR_UNSUPPORTED;
   }
   if (workspace_bytes < bwd_workspace(d)) return KVC_ERR_WORKSPACE;

@@ -241,9 +241,10 @@ int kvc_attend_over_cache(const kvc_dims *dims, int dtype, int has_scale,
 
 /* Backward of the step (fp32 or bf16: every tensor argument of the dtype,
  * gradients in and out included; head sizes (D, Dv) in {(64, 64),
- * (128, 128), (64, 32)}; key_cache, value_cache, new_key, new_value,
- * d_key_cache_out, d_value_cache_out and the five gradient outputs
- * 16-byte aligned; else KVC_ERR_UNSUPPORTED): the gradients of the
+ * (128, 128), (64, 32)}; query, key_cache, value_cache, new_key,
+ * new_value, d_context, d_key_cache_out, d_value_cache_out and the five
+ * gradient outputs 16-byte aligned; else KVC_ERR_UNSUPPORTED): the
+ * gradients of the
  * step's inputs given those of its outputs.  The math runs in fp32 and
  * fp64 either way; each gradient is rounded once to the dtype.  The page grades gradients as
  * well as values ("Autoregressive KV-cache append and causal attention",

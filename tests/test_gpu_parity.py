@@ -775,7 +775,7 @@ def test_backward_against_oracle(wl, upstream, dtype):
                 f"{wl.name}/{dtype}/{upstream}/{seed}: {name} off by {err.max():.3e}"
 
 
-@pytest.mark.parametrize("which", ["d_key_cache_out", "g_value_cache", "g_new_key"])
+@pytest.mark.parametrize("which", ["query", "d_key_cache_out", "g_value_cache", "g_new_key"])
 def test_backward_refuses_misaligned_gradient_buffers(which):
     """The slot gradients move in 16-byte pieces: a gradient buffer, in or
     out, that is not 16-byte aligned is refused (KVC_ERR_UNSUPPORTED) before
@@ -791,7 +791,9 @@ def test_backward_refuses_misaligned_gradient_buffers(which):
     outs = {k: torch.full_like(dinp[src], float("nan")) for k, src in
             (("g_query", "query"), ("g_new_key", "new_key"), ("g_new_value", "new_value"),
              ("g_key_cache", "key_cache"), ("g_value_cache", "value_cache"))}
-    if which in ups:
+    if which == "query":
+        dinp["query"] = misaligned(dinp["query"])
+    elif which in ups:
         ups[which] = misaligned(ups[which])
     else:
         outs[which] = misaligned(outs[which])
