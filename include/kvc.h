@@ -244,11 +244,10 @@ int kvc_attend_over_cache(const kvc_dims *dims, int dtype, int has_scale,
  * (128, 128), (64, 32)}; query, key_cache, value_cache, new_key,
  * new_value, d_context, d_key_cache_out, d_value_cache_out and the five
  * gradient outputs 16-byte aligned; else KVC_ERR_UNSUPPORTED): the
- * gradients of the
- * step's inputs given those of its outputs.  The math runs in fp32 and
- * fp64 either way; each gradient is rounded once to the dtype.  The page grades gradients as
- * well as values ("Autoregressive KV-cache append and causal attention",
- * the workspace note).
+ * gradients of the step's inputs given those of its outputs.  The math
+ * runs in fp32 and fp64 either way; each gradient is rounded once to the
+ * dtype.  The page grades gradients as well as values ("Autoregressive
+ * KV-cache append and causal attention", the workspace note).
  *
  * Inputs: the step's own inputs (query, new_key, new_value, lengths,
  * append_mask as given to the step; key_cache / value_cache either the
