@@ -328,6 +328,9 @@ __device__ inline void bwd_fetch_tile(const BwdArgs& a, int64_t b, int64_t kvh, 
     const int64_t jc = j < a.M ? j : a.M - 1;
 #pragma unroll
     for (int k = 0; k < RT / 4; k++) {
+      // rows grow with k: from the first group of four that is all tile
+      // padding on, nothing is visible (the entries stay 0)
+      if (r0 + 16 * (k / 4) + 4 * (k % 4) >= a.R) break;
       const int r = r0 + 16 * (k / 4) + 4 * (k % 4) + lq;
       const int t = r % Q;
       const bool vis = r < a.R && t < n && j <= len + t;
