@@ -482,6 +482,9 @@ bwd_stats_kernel(BwdArgs a) {
                                                  static_cast<double>(vx[kk]), dov, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
+      // rows grow with i: groups of four that are all tile padding are not
+      // reduced (the merge below reads rows below R only)
+      if (r0 + 4 * i >= a.R) break;
       const int r = r0 + 4 * i + lq;
       const int t = r % static_cast<int>(a.Q);
       const bool vis = r < a.R && t < n && j <= len + t;
