@@ -805,3 +805,44 @@ def test_backward_refuses_misaligned_gradient_buffers(which):
     assert e.value.code == -8
     torch.cuda.synchronize()
     assert all(torch.isnan(v).all() for v in outs.values())
+
+
+def test_backward_full_decode_bench_configuration():
+    """The backward at the full decode size bench.py --mode backward times
+    (bf16, 32 sequences, 32 query heads over 8 KV heads, 8192 slots, upstream
+    gradients for all four outputs): every gradient element against the
+    oracle (about half a minute of oracle time)."""
+    wl = WORKLOADS["decode_gqa_bf16"]
+    say(f"[case] backward {wl.name} full size")
+    inp = make_inputs(wl, 0, "cpu")
+    dinp = {k: v.to(DEV) for k, v in inp.items()}
+    g = torch.Generator().manual_seed(100)
+    B, Hq, Q, D = inp["query"].shape
+    Hk, M, Dv = inp["key_cache"].shape[1], inp["key_cache"].shape[2], inp["value_cache"].shape[3]
+    tdt = torch.bfloat16
+    ups = {"d_attention": torch.randn(B, Hq, Q, M, generator=g).to(tdt),
+           "d_context": torch.randn(B, Hq, Q, Dv, generator=g).to(tdt),
+           "d_key_cache_out": torch.randn(B, Hk, M, D, generator=g).to(tdt),
+           "d_value_cache_out": torch.randn(B, Hk, M, Dv, generator=g).to(tdt)}
+    outs = {k: torch.full_like(dinp[src], float("nan")) for k, src in
+            (("g_query", "query"), ("g_new_key", "new_key"), ("g_new_value", "new_value"),
+             ("g_key_cache", "key_cache"), ("g_value_cache", "value_cache"))}
+    mask = dinp["append_mask"].contiguous().view(torch.uint8)
+    kvc.kvc_step_backward(dinp["query"], dinp["new_key"], dinp["new_value"],
+                          dinp["key_cache"], dinp["value_cache"], dinp["lengths"], mask,
+                          *[v.to(DEV) for v in ups.values()], **outs, scale=wl.scale)
+    torch.cuda.synchronize()
+    got = {k: to_f64(v) for k, v in outs.items()}
+    del dinp, outs
+    torch.cuda.empty_cache()
+    h = host_arrays(inp)
+    ref = oracle.step_backward(*(to_f64(inp[k]) for k in ("query", "new_key", "new_value",
+                                                          "key_cache", "value_cache")),
+                               h["lengths"], h["append_mask"],
+                               **{k: to_f64(v) for k, v in ups.items()}, scale=wl.scale)
+    for name, want in (("g_query", ref.query), ("g_new_key", ref.new_key),
+                       ("g_new_value", ref.new_value), ("g_key_cache", ref.key_cache),
+                       ("g_value_cache", ref.value_cache)):
+        assert np.all(np.isfinite(got[name])), f"full decode backward: {name} not finite"
+        err = np.abs(got[name] - want) - BWD_TOL["bf16"] * (1 + np.abs(want))
+        assert err.max() <= 0, f"full decode backward: {name} off by {err.max():.3e}"
