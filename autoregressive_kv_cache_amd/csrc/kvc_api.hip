@@ -16,6 +16,8 @@
 #include "kvc_host.h"
 #include "kvc_prep.h"
 #include "kvc_reattend.h"
+#include "kvc_combine_stream.h"
+#include "kvc_stream.h"
 
 namespace {
 
@@ -60,22 +62,62 @@ void launch_decode(const StepArgs& a, hipStream_t s) {
     launch_decode_q<T, D, DV, ROWS, false>(a, s);
 }
 
+// bf16 caches: the stream kernel of kvc_stream.h.
+template <int D, int DV, int ROWS, bool Q1>
+void launch_stream_q(const StepArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.P / kvc::kDecodeWaves)), block(kvc::kDecodeThreads);
+  const int64_t* ri = a.ws_rowinfo;
+  const int32_t* wst = a.ws_wstart;
+  const bool fused = a.B <= kvc::kDecodeFusedRows;
+  if (a.paged && fused)
+    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, false, true, true>), grid,
+                       block, 0, s, a, ri, wst);
+  else if (a.paged)
+    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, false, false, true>), grid,
+                       block, 0, s, a, ri, wst);
+  else if (a.out_of_place && fused)
+    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, true, true, false>), grid,
+                       block, 0, s, a, ri, wst);
+  else if (a.out_of_place)
+    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, true, false, false>), grid,
+                       block, 0, s, a, ri, wst);
+  else if (fused)
+    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, false, true, false>), grid,
+                       block, 0, s, a, ri, wst);
+  else
+    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, false, false, false>), grid,
+                       block, 0, s, a, ri, wst);
+}
+
+template <typename T, int D, int DV, int ROWS>
+void launch_decode_bf16(const StepArgs& a, hipStream_t s) {
+  if (a.Q == 1)
+    launch_stream_q<D, DV, ROWS, true>(a, s);
+  else
+    launch_stream_q<D, DV, ROWS, false>(a, s);
+}
+
 struct DecodeEntry {
   int dtype, D, Dv, rows, chunk, wgs_per_cu;
   void (*launch)(const StepArgs&, hipStream_t);
+  bool stream;  // attend_stream_kernel (its own workspace layout and combine)
 };
 
 #define KVC_DECODE(T, CODE, D, DV, ROWS) \
   {CODE, D, DV, ROWS, kvc::decode_chunk<T, D, DV, ROWS>(), kvc::decode_waves_per_simd<ROWS>(), \
-   &launch_decode<T, D, DV, ROWS>}
+   &launch_decode<T, D, DV, ROWS>, false}
+// the two kernels of a bf16 entry share chunk size and occupancy
+#define KVC_STREAM(D, DV, ROWS) \
+  {KVC_BF16, D, DV, ROWS, kvc::kStreamChunk, kvc::stream_waves_per_simd<ROWS>(), \
+   &launch_decode_bf16<kvc::bf16, D, DV, ROWS>, true}
 const DecodeEntry kDecodeTable[] = {
-    KVC_DECODE(kvc::bf16, KVC_BF16, 128, 128, 4), KVC_DECODE(kvc::bf16, KVC_BF16, 128, 128, 8),
-    KVC_DECODE(kvc::bf16, KVC_BF16, 64, 64, 4),   KVC_DECODE(kvc::bf16, KVC_BF16, 64, 64, 8),
+    KVC_STREAM(128, 128, 4), KVC_STREAM(128, 128, 8), KVC_STREAM(64, 64, 4), KVC_STREAM(64, 64, 8),
     KVC_DECODE(kvc::bf16, KVC_BF16, 256, 256, 4), KVC_DECODE(kvc::bf16, KVC_BF16, 256, 256, 8),
     KVC_DECODE(float, KVC_F32, 128, 128, 4),      KVC_DECODE(float, KVC_F32, 64, 64, 4),
     KVC_DECODE(float, KVC_F32, 64, 32, 4),
 };
 #undef KVC_DECODE
+#undef KVC_STREAM
 
 // Stream path: MI355X has 256 compute units; every unit holds as many
 // attend workgroups (of 4 waves, one per SIMD, each wave one stream worker)
@@ -134,11 +176,15 @@ const DecodeEntry* find_decode(const kvc_dims* d, int dtype, int64_t R) {
 
 struct Layout {
   int64_t C, nchunk_max, nseg, CS;
-  size_t off_hdr, off_rowinfo, off_chunk, off_seg_ml, off_seg_o, off_wstart, bytes;
+  size_t off_hdr, off_rowinfo, off_chunk, off_seg_ml, off_seg_o, off_wstart, off_pexp, off_cref,
+      off_seg2, bytes;
 };
 
+// stream2: the arrays of attend_stream_kernel (exp values and references
+// per chunk, segment statistics in float) instead of the per-chunk double
+// statistics of the other attend kernels.
 bool make_layout(const kvc_dims* d, int64_t R, int64_t C, bool stream,
-                 int64_t P, Layout* L) {
+                 int64_t P, Layout* L, bool stream2 = false) {
   L->C = C;
   // stream mode: the cached slots in chunks of C plus one chunk of the
   // appended rows per head
@@ -156,7 +202,7 @@ bool make_layout(const kvc_dims* d, int64_t R, int64_t C, bool stream,
   off = align_up(off + static_cast<size_t>(d->B) * 4 * sizeof(int64_t), 256);
   L->off_chunk = off;
   if (!mul_ok(chunks, R, kMaxElems, &x)) return false;
-  off = align_up(off + static_cast<size_t>(x) * 2 * sizeof(double), 256);
+  if (!stream2) off = align_up(off + static_cast<size_t>(x) * 2 * sizeof(double), 256);
   L->off_seg_ml = off;
   if (!mul_ok(nseg, R, kMaxElems, &x)) return false;
   off = align_up(off + static_cast<size_t>(x) * 2 * sizeof(double), 256);
@@ -165,6 +211,18 @@ bool make_layout(const kvc_dims* d, int64_t R, int64_t C, bool stream,
   off = align_up(off + static_cast<size_t>(x) * sizeof(float), 256);
   L->off_wstart = off;
   off = align_up(off + static_cast<size_t>(stream ? P : 0) * 4 * sizeof(int32_t), 256);
+  L->off_pexp = L->off_cref = L->off_seg2 = off;
+  if (stream2) {
+    int64_t xr;  // chunks x rows
+    if (!mul_ok(chunks, R, kMaxElems, &xr) || !mul_ok(xr, C, kMaxElems, &x)) return false;
+    L->off_pexp = off;
+    off = align_up(off + static_cast<size_t>(x) * sizeof(uint16_t), 256);
+    L->off_cref = off;
+    off = align_up(off + static_cast<size_t>(xr) * sizeof(float), 256);
+    if (!mul_ok(nseg, R, kMaxElems, &x)) return false;
+    L->off_seg2 = off;
+    off = align_up(off + static_cast<size_t>(x) * 2 * sizeof(float), 256);
+  }
   L->bytes = off;
   return true;
 }
@@ -198,7 +256,8 @@ int make_plan(const kvc_dims* d, int dtype, Plan* p) {
     return KVC_ERR_SHAPE;
   size_t bytes = p->generic.bytes;
   if (p->decode) {
-    if (!make_layout(d, R, p->decode->chunk, true, p->P, &p->stream)) return KVC_ERR_SHAPE;
+    if (!make_layout(d, R, p->decode->chunk, true, p->P, &p->stream, p->decode->stream))
+      return KVC_ERR_SHAPE;
     int64_t cwgs;
     if (!mul_ok(d->B * d->Hk, row_blocks, kMaxElems, &cwgs) ||
         !mul_ok(cwgs, (d->M + p->stream.CS - 1) / p->stream.CS + 1, kMaxWorkgroups, &cwgs))
@@ -249,6 +308,9 @@ void set_layout(StepArgs& a, const Layout& L, void* workspace) {
   a.ws_seg_ml = reinterpret_cast<double*>(ws + L.off_seg_ml);
   a.ws_seg_o = reinterpret_cast<float*>(ws + L.off_seg_o);
   a.ws_wstart = reinterpret_cast<int32_t*>(ws + L.off_wstart);
+  a.ws_pexp = reinterpret_cast<uint16_t*>(ws + L.off_pexp);
+  a.ws_cref = reinterpret_cast<float*>(ws + L.off_cref);
+  a.ws_seg2 = reinterpret_cast<float*>(ws + L.off_seg2);
 }
 
 template <typename T>
@@ -291,7 +353,15 @@ void launch_stream(StepArgs& a, const DecodeEntry& e, hipStream_t stream, const 
   if (ev && ev->start) hipEventRecord(static_cast<hipEvent_t>(ev->start), stream);
   e.launch(a, stream);
   if (ev && ev->stop) hipEventRecord(static_cast<hipEvent_t>(ev->stop), stream);
-  launch_combine<T>(a, stream);
+  if (e.stream) {
+    const int64_t groups = a.B * a.Hk;
+    const int64_t nrb = a.R > 0 ? (a.R + kvc::kCombineWaves - 1) / kvc::kCombineWaves : 1;
+    hipLaunchKernelGGL(kvc::combine_stream_kernel,
+                       dim3(static_cast<unsigned>(groups * ((a.M + a.CS - 1) / a.CS + 1) * nrb)),
+                       dim3(kvc::kCombineThreads), 0, stream, a);
+  } else {
+    launch_combine<T>(a, stream);
+  }
 }
 
 // The paged layout: block pools [num_blocks][Hk][block_size][D or Dv] and a
@@ -431,7 +501,7 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
     launch_dense_chunk(a, *p.chunk, s, events);
   } else if (vec_ok) {
     set_layout(a, p.stream, workspace);
-    a.seg_mode = 1;
+    a.seg_mode = p.decode->stream ? 2 : 1;
     a.combine_copies_tail = 1;
     a.rows_per_tile = p.decode->rows;
     a.row_tiles = 1;

@@ -83,7 +83,7 @@ struct StepArgs {
   int64_t nchunk_max; // ceil(M / C)
   int64_t CS;         // slots per combine workgroup (a multiple of C)
   int64_t P;          // stream workers (waves of the attend grid, stream mode)
-  int32_t seg_mode;   // 0 dense, 1 stream
+  int32_t seg_mode;   // 0 dense, 1 stream, 2 stream with the bf16 stream kernel's workspace
   int32_t combine_copies_tail;  // out of place: combine copies slots the attend kernel skips
   double scale;       // resolved softmax scale
   int64_t elem_bytes; // 4 (fp32) or 2 (bf16)
@@ -107,6 +107,10 @@ struct StepArgs {
   double* ws_seg_ml;     // [nseg][R][2]: m_seg, l_seg
   float* ws_seg_o;       // [nseg][R][Dv]: o_seg
   int32_t* ws_wstart;    // [P][4]: first (b, head, chunk) of each stream worker
+  // bf16 stream kernel (kvc_stream.h), indexed by the flattened chunk x:
+  uint16_t* ws_pexp;     // [Nc][R][C]: exp2(s - m_ref) of the chunk's slots (bf16)
+  float* ws_cref;        // [Nc][R]: the reference m_ref (log2 units) of each chunk
+  float* ws_seg2;        // [nseg][R][2]: m (log2 units) and l of each segment
   // paged cache (stream path): kc_in/kc_out and vc_in/vc_out are the block
   // pools [num_blocks][Hk][block_rows][D or Dv]; slot j of batch row b is
   // row j & block_mask of block block_table[b * max_blocks + (j >> block_log2)]
