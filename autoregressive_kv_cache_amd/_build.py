@@ -24,7 +24,8 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
-SOURCES = [os.path.join(CSRC, "kvc_api.hip"), os.path.join(CSRC, "kvc_backward_api.hip")]
+SOURCES = [os.path.join(CSRC, "kvc_api.hip"), os.path.join(CSRC, "kvc_backward_api.hip"),
+           os.path.join(CSRC, "kvc_measure.hip")]
 
 
 def build(output: str = LIBRARY, extra: list[str] | None = None, verbose: bool = False) -> str:

@@ -119,11 +119,21 @@ const DecodeEntry kDecodeTable[] = {
 #undef KVC_DECODE
 #undef KVC_STREAM
 
-// Stream path: MI355X has 256 compute units; every unit holds as many
-// attend workgroups (of 4 waves, one per SIMD, each wave one stream worker)
-// as the kernel's registers allow, and each wave keeps a whole chunk of
-// loads in flight.
-constexpr int64_t kComputeUnits = 256;
+// Stream path: every compute unit of the current device holds as many attend
+// workgroups (of 4 waves, one per SIMD, each wave one stream worker) as the
+// kernel's registers allow, and each wave keeps a whole chunk of loads in
+// flight.  The count comes from the device (256 on MI355X); without a device
+// (a host-only caller) the MI355X count is assumed.
+int64_t compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n < 1) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return n;
+}
 // Slots per combine workgroup (a multiple of every chunk size).
 constexpr int64_t kCombineSlots = 2048;
 
@@ -243,7 +253,7 @@ int make_plan(const kvc_dims* d, int dtype, Plan* p) {
   p->pub.rows = static_cast<int32_t>(R);
   p->decode = find_decode(d, dtype, R);
   p->chunk = p->decode ? nullptr : find_chunk(d, dtype, R);
-  p->P = p->decode ? kComputeUnits * p->decode->wgs_per_cu * kvc::kDecodeWaves : 0;
+  p->P = p->decode ? compute_units() * p->decode->wgs_per_cu * kvc::kDecodeWaves : 0;
   const int64_t row_tiles = R == 0 ? 1 : (R + kvc::kGenericRowsPerTile - 1) / kvc::kGenericRowsPerTile;
   if (!make_layout(d, R, kvc::kGenericChunk, false, 0, &p->generic)) return KVC_ERR_SHAPE;
   int64_t wgs;
@@ -463,6 +473,8 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
     if (overlap(r_kin, r_vin)) return KVC_ERR_ALIAS;
   }
 
+  // an error left by earlier, unrelated work must not be reported as ours
+  (void)hipGetLastError();
   StepArgs a;
   std::memset(&a, 0, sizeof a);
   a.B = d->B; a.Hq = d->Hq; a.Hk = d->Hk; a.Q = d->Q; a.M = d->M; a.D = d->D; a.Dv = d->Dv;
@@ -641,6 +653,7 @@ int kvc_attend_over_cache(const kvc_dims* dims, int dtype, int has_scale, double
   }
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  (void)hipGetLastError();  // an earlier error is not ours
   StepArgs a;
   std::memset(&a, 0, sizeof a);
   a.B = d->B; a.Hq = d->Hq; a.Hk = d->Hk; a.Q = d->Q; a.M = d->M; a.D = d->D; a.Dv = d->Dv;

@@ -45,15 +45,6 @@ constexpr int kBwdRowTile = 16;   // packed rows per tile in bwd_stats
 constexpr int kBwdChunkRowsWide = 32;
 constexpr int kBwdMaxRowGroups = 16;
 
-// bwd_chunk: workgroups per chunk, each over a share of the 16-column tiles
-// of dK', dV' and dq (the scores are recomputed by each).  One: splitting
-// the columns over four workgroups was slower (the scores, the attention
-// gradient loads and the staging are repeated by each).
-template <int D, int DV>
-constexpr int bwd_col_groups() {
-  return 1;
-}
-
 struct BwdArgs {
   int64_t B, Hq, Hk, Q, M, D, Dv;
   int32_t G, R;
@@ -644,9 +635,8 @@ template <typename T, int D, int DV, int RT>
 __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
   constexpr int C = kBwdSlots, NB = RT / 16, W = kBwdThreads / kWave;
   constexpr int KP = bwd_pitch<D>(), VP = bwd_pitch<DV>(), SP = C + 1;
-  constexpr int CG = bwd_col_groups<D, DV>();
-  constexpr int DT = D / 16 / CG, VT = DV / 16 / CG;  // this workgroup's 16-column tiles
-  static_assert(C == 16 * W && RT % 16 == 0 && D % (16 * CG) == 0 && DV % (16 * CG) == 0, "tile shape");
+  constexpr int DT = D / 16, VT = DV / 16;  // 16-column tiles of dK'/dq and dV'
+  static_assert(C == 16 * W && RT % 16 == 0 && D % 16 == 0 && DV % 16 == 0, "tile shape");
   __shared__ float k_s[C * KP];
   __shared__ float v_s[C * VP];
   __shared__ float q_s[RT * KP];
@@ -656,14 +646,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ double st_s[RT][3];    // the rows' m, l and sum_k P_k dP_k
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int li = lane % 16, lq = lane / 16;
-  const int cg = static_cast<int>(blockIdx.x % CG);
-  const int64_t c = (blockIdx.x / CG) % a.nchunk;
-  const int64_t grp = blockIdx.x / CG / a.nchunk;
+  const int64_t c = blockIdx.x % a.nchunk;
+  const int64_t grp = blockIdx.x / a.nchunk;
   const int64_t b = grp / a.Hk, kvh = grp % a.Hk;
   int64_t len, n;
   bwd_row_info(a, b, &len, &n);
   const int64_t s0 = c * C;
-  const int dc0 = cg * DT * 16, vc0 = cg * VT * 16;  // first dK'/dq and dV' column
+  constexpr int dc0 = 0, vc0 = 0;  // first dK'/dq and dV' column
   // slots with any attention gradient (none on a row that appends nothing
   // or is rejected; then only the pass-through below remains)
   const int64_t nvis = n > 0 ? len + n : 0;
@@ -769,7 +758,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
   // instruction each.  All pass-through pieces are loaded before the first
   // store: the host refuses overlapping buffers, but the compiler cannot
   // know that and would otherwise wait for each load in turn.
-  static_assert(CG == 1, "the pieces span whole slot rows");
   constexpr int EP = 16 / static_cast<int>(sizeof(T));  // elements per piece
   constexpr int NPK = C * (D / EP) / kBwdThreads, NPV = C * (DV / EP) / kBwdThreads;
   static_assert(D % EP == 0 && DV % EP == 0 && C * (D / EP) % kBwdThreads == 0 &&
@@ -800,7 +788,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     bwd_piece_out<T, DV, VP>(a, grp, len, n, s0, tid + u * kBwdThreads, xv[u], v_s, a.g_vc,
                              a.g_new_value);
   // appended rows that do not exist (t >= n, rejected rows): zero gradient
-  if (c == 0 && cg == 0) {
+  if (c == 0) {
     for (int64_t idx = tid; idx < (a.Q - n) * D; idx += kBwdThreads)
       bwd_st<T>(a.g_new_key, (grp * a.Q + n + idx / D) * D + idx % D, 0.f);
     for (int64_t idx = tid; idx < (a.Q - n) * DV; idx += kBwdThreads)

@@ -33,7 +33,7 @@ void launch_bwd_stats(const kvc::BwdArgs& a, hipStream_t s) {
 }
 template <typename T, int D, int DV>
 void launch_bwd_chunk(const kvc::BwdArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.B * a.Hk * a.nchunk * kvc::bwd_col_groups<D, DV>()));
+  const dim3 grid(static_cast<unsigned>(a.B * a.Hk * a.nchunk));
   if (a.R > kvc::kBwdRowTile)
     hipLaunchKernelGGL((kvc::bwd_chunk_kernel<T, D, DV, kvc::kBwdChunkRowsWide>), grid,
                        dim3(kvc::kBwdThreads), 0, s, a);
@@ -126,6 +126,7 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
     for (int j = i + 1; j < 6; j++)
       if (overlap(outs[i], outs[j])) return KVC_ERR_ALIAS;
   }
+  (void)hipGetLastError();  // an earlier error is not ours
   kvc::BwdArgs a;
   std::memset(&a, 0, sizeof a);
   a.B = d->B; a.Hq = d->Hq; a.Hk = d->Hk; a.Q = d->Q; a.M = d->M; a.D = d->D; a.Dv = d->Dv;

@@ -34,7 +34,8 @@ ROW_OK, ROW_BAD_LENGTH, ROW_OVERFLOW, ROW_NOT_PREFIX, ROW_BAD_QUERIES = 0, 1, 2,
 EXPORTED = ("kvc_workspace_bytes", "kvc_plan_step", "kvc_step_out_of_place",
             "kvc_step_inplace", "kvc_step_paged", "kvc_attend_workspace_bytes",
             "kvc_attend_over_cache", "kvc_backward_workspace_bytes", "kvc_step_backward",
-            "kvc_status_string")
+            "kvc_status_string",
+            "kvc_read_ceiling_sink_bytes", "kvc_read_ceiling")
 
 
 class KvcDims(ctypes.Structure):
@@ -100,12 +101,25 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
                                       + [_sz, _vp])
     lib.kvc_status_string.restype = ctypes.c_char_p
     lib.kvc_status_string.argtypes = [_int]
+    lib.kvc_read_ceiling_sink_bytes.restype = _sz
+    lib.kvc_read_ceiling_sink_bytes.argtypes = [_int]
+    lib.kvc_read_ceiling.restype = _int
+    lib.kvc_read_ceiling.argtypes = [_vp, _sz, _int, _vp, _sz, _vp]
     _LIB = lib
     return lib
 
 
 def kvc_status_string(code: int) -> str:
     return load().kvc_status_string(int(code)).decode()
+
+
+def kvc_read_ceiling(buffer: torch.Tensor, workgroups: int, sink: torch.Tensor, stream=None):
+    """Enqueue the streaming-read measurement over `buffer` (see kvc.h)."""
+    rc = load().kvc_read_ceiling(_ptr(buffer), buffer.numel() * buffer.element_size(),
+                                 int(workgroups), _ptr(sink), sink.numel() * sink.element_size(),
+                                 _stream(stream, buffer.device))
+    if rc != KVC_OK:
+        raise KvcError(rc, "kvc_read_ceiling")
 
 
 def dims_of(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor) -> KvcDims:

@@ -101,23 +101,50 @@ def algorithmic_bytes(wl, lengths, n):
     the cache, read q, write the full attention rows and the context, plus
     lengths, mask, lengths_out and row_status.
 
-    Attention kernel: the K/V rows it visits (length + n per KV head, the
-    appended ones already in the cache), q, the exp(s - m_c) values of the
-    visible slots (length + t + 1 per valid row) and lengths and mask; the
-    append itself, the zero tails, the normalisation and the context belong
-    to the kernels around it."""
+    Attention kernel: the K/V rows it visits (length + n per KV head), q,
+    and lengths and mask.  What it writes for the combine kernel (exp values,
+    their references, segment partials) is intermediate traffic, not
+    algorithmic (see intermediate_bytes); the append itself, the attention
+    rows, the normalisation and the context belong to the combine."""
     e = 2 if wl.dtype == "bf16" else 4
     kv = sum(wl.Hk * (int(L) + 2 * int(k)) * (wl.D + wl.Dv) * e for L, k in zip(lengths, n))
     kv_read = sum(wl.Hk * (int(L) + int(k)) * (wl.D + wl.Dv) * e for L, k in zip(lengths, n))
     q = wl.B * wl.Hq * wl.Q * wl.D * e
     att = wl.B * wl.Hq * wl.Q * wl.M * e
-    att_visible = sum(wl.Hq * (int(L) + t + 1) * e for L, k in zip(lengths, n) for t in range(int(k)))
     ctx = wl.B * wl.Hq * wl.Q * wl.Dv * e
     small_in = wl.B * (8 + wl.Q)
     small_out = wl.B * (8 + 4)
     step = kv + q + att + ctx + small_in + small_out
-    attend = kv_read + q + att_visible + small_in
+    attend = kv_read + q + small_in
     return step, attend, kv
+
+
+def intermediate_bytes(wl, lengths, n, P: int, C: int = 64, seg_partials: bool = True):
+    """Bytes the stream attend kernel writes for the combine kernel (bf16
+    decode path): per chunk of the flattened list, R rows of C exp values
+    (2 B) and R references (4 B); per segment (a worker's run of one KV
+    head), R rows of Dv fp32 context partials and (m, l) as two floats.
+    Workers own equal contiguous ranges of the chunk list, as the kernel
+    splits it."""
+    R = wl.Hq // wl.Hk * wl.Q
+    heads = []  # flattened chunk list: one entry per chunk, its (b, head)
+    for b, (L, k) in enumerate(zip(lengths, n)):
+        if int(k) == 0:
+            continue
+        nc = -(-int(L) // C) + 1
+        for h in range(wl.Hk):
+            heads.extend([(b, h)] * nc)
+    Nc = len(heads)
+    if Nc == 0:
+        return 0
+    Pe = min(P, Nc)
+    segs = 0
+    for w in range(Pe):
+        x0, x1 = w * Nc // Pe, (w + 1) * Nc // Pe
+        segs += len(set(heads[x0:x1]))
+    per_chunk = R * C * 2 + R * 4
+    per_seg = R * (wl.Dv * 4 + 8) if seg_partials else 0
+    return Nc * per_chunk + segs * per_seg
 
 
 def reattend_bytes(wl, lengths, n):
@@ -165,9 +192,10 @@ def oop_extra_bytes(wl, lengths, n):
 
 
 # Sources the attend kernel is compiled from and launched by (the stream
-# decode kernel, its row preparation, the host plan and launch code): a change
+# decode kernels, their row preparation, the host plan and launch code): a change
 # to any of them makes a committed counter summary stale.
-ATTEND_SOURCES = ("kvc_api.hip", "kvc_common.h", "kvc_decode.h", "kvc_host.h", "kvc_prep.h")
+ATTEND_SOURCES = ("kvc_api.hip", "kvc_common.h", "kvc_decode.h", "kvc_host.h", "kvc_prep.h",
+                  "kvc_stream.h")
 
 
 def kernel_source_digest() -> str:
@@ -213,24 +241,60 @@ def copy_ceiling_gbps(torch, dev, nbytes=2 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def read_ceiling_gbps(torch, kvc, dev, nbytes=2 << 30, reps=10):
+    """Streaming read of a 2 GiB buffer with the attend kernels' non-temporal
+    16-byte loads (kvc_read_ceiling): bytes / time, the achievable read rate
+    next to the 8 TB/s peak."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    wgs = cus * 8
+    buf = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+    buf.fill_(3)
+    sink = torch.empty(kvc.load().kvc_read_ceiling_sink_bytes(wgs) // 4, dtype=torch.int32,
+                       device=dev)
+    for _ in range(2):
+        kvc.kvc_read_ceiling(buf, wgs, sink)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        kvc.kvc_read_ceiling(buf, wgs, sink)
+    e.record()
+    e.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del buf, sink
+    torch.cuda.empty_cache()
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(wl, inputs, budget_s: float):
-    """The oracle (plain C, one thread) on the same workload: whole steps,
-    repeated until the time budget is used (at least once)."""
+    """The oracle on the same workload, whole steps repeated until each half
+    of the time budget is used (at least once): on one thread (step) and on
+    every host core (step_threaded: the same row calls over a thread pool)."""
     import oracle
     from autoregressive_kv_cache_amd.workloads import host_arrays
     h = host_arrays(inputs)
     orc = oracle.default()
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        orc.step(h["query"], h["new_key"], h["new_value"], h["key_cache"], h["value_cache"],
-                 h["lengths"], h["append_mask"], scale=wl.scale)
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": reps / dt, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} whole {wl.name} step(s) of the oracle (double precision, "
-                      f"single thread) on the same seeded inputs, {dt:.1f} s"}
+    args = (h["query"], h["new_key"], h["new_value"], h["key_cache"], h["value_cache"],
+            h["lengths"], h["append_mask"])
+
+    def rate(fn):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s / 2:
+                break
+        return reps, time.perf_counter() - t0
+
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = max(1, threads or 1)
+    r1, t1 = rate(lambda: orc.step(*args, scale=wl.scale))
+    rn, tn = rate(lambda: orc.step_threaded(*args, scale=wl.scale, threads=threads))
+    return {"value": rn / tn, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "single_thread_value": r1 / t1,
+            "sample": f"whole {wl.name} steps of the oracle (double precision) on the same "
+                      f"seeded inputs: {rn} in {tn:.1f} s on {threads} threads (rows over a "
+                      f"thread pool), {r1} in {t1:.1f} s on one thread"}
 
 
 def main():
@@ -342,6 +406,7 @@ def main():
                                       d["status"], workspace=ws, scale=wl.scale, events=events)
 
     ceiling = copy_ceiling_gbps(torch, dev)
+    read_ceiling = read_ceiling_gbps(torch, kvc, dev)
     for w in range(args.warmup):
         step(None, w)
     torch.cuda.synchronize()
@@ -356,6 +421,11 @@ def main():
         ev.destroy(e)
 
     step_bytes, attend_bytes, kv_bytes = algorithmic_bytes(wl, lengths, n)
+    inter_bytes = None
+    if args.mode in ("inplace", "oop", "paged") and plan["path"] == 1 and wl.dtype == "bf16":
+        P = torch.cuda.get_device_properties(dev).multi_processor_count * (
+            2 if plan["rows_per_tile"] <= 4 else 1) * 4
+        inter_bytes = intermediate_bytes(wl, lengths, n, P)
     if args.mode == "oop":
         extra_step, extra_attend = oop_extra_bytes(wl, lengths, n)
         step_bytes += extra_step
@@ -396,15 +466,18 @@ def main():
         "tokens_per_s": steps_per_s * wl.B * wl.Q,
         "step_algorithmic_bytes": step_bytes,
         "copy_ceiling_gbps": ceiling,
+        "read_ceiling_gbps": read_ceiling,
         "roofline": {"bound": "hbm",
                      "kernel": "backward (all four kernels)" if args.mode == "backward"
                      else DOMINANT_KERNEL, "achieved": k_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": k_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic, "bytes_per_launch": attend_bytes,
+                     "intermediate_bytes_per_launch": inter_bytes,
                      "avg_launch_ms": k_ms, "launches_sampled": len(kernel_ms),
                      "p10_launch_ms": pct(0.1), "median_launch_ms": pct(0.5),
                      "p90_launch_ms": pct(0.9),
-                     "frac_of_copy_ceiling": k_gbps / ceiling},
+                     "frac_of_copy_ceiling": k_gbps / ceiling,
+                     "frac_of_read_ceiling": k_gbps / read_ceiling},
     }
     if args.mode == "paged":
         result["config"]["block_size"] = args.block_size

@@ -105,7 +105,8 @@ typedef struct kvc_events {
   void *stop;
 } kvc_events;
 
-/* Kernel plan the library picks for a shape (host-only, no HIP call). */
+/* Kernel plan the library picks for a shape (host-only: it reads the
+ * current device's compute-unit count, and assumes 256 without a device). */
 typedef struct kvc_plan {
   int32_t path;          /* 0 generic, 1 vector decode, 2 MFMA chunk */
   int32_t rows;          /* packed query rows per KV head: (Hq/Hk) * Q */
@@ -283,6 +284,18 @@ int kvc_step_backward(const kvc_dims *dims, int dtype, int has_scale,
 
 /* Static description of a return or row-status code. */
 const char *kvc_status_string(int code);
+
+/* Measurement helper (no part of the step): stream-reads `bytes` of the
+ * device buffer `buffer` with the non-temporal 16-byte loads the attend
+ * kernels use for K/V rows, one contiguous slab per workgroup, and folds
+ * what each lane read into one word of `sink` (a device buffer of at least
+ * kvc_read_ceiling_sink_bytes(workgroups) bytes) so that no load is dead.
+ * `bytes` must be a multiple of workgroups * 32 KiB (else KVC_ERR_SHAPE).
+ * Enqueued on `stream`; time it with events around the call to get an
+ * achievable read bandwidth of the part. */
+size_t kvc_read_ceiling_sink_bytes(int workgroups);
+int kvc_read_ceiling(const void *buffer, size_t bytes, int workgroups,
+                     void *sink, size_t sink_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -148,6 +148,45 @@ class Oracle:
             raise ValueError(f"oracle rejected the append (code {rc})")
         return kc_out, vc_out, len_out, n, status
 
+    def step_threaded(self, query, new_key, new_value, key_cache, value_cache, lengths,
+                      append_mask, scale: float | None = None,
+                      threads: int | None = None) -> StepResult:
+        """step() with its rows spread over a thread pool: one append, then the
+        (b, hq, t) rows of kvc_oracle_attend_row (the calls kvc_oracle_step
+        makes, in any order) on `threads` threads; ctypes releases the GIL
+        during each call.  The arithmetic is that of step(), row for row."""
+        from concurrent.futures import ThreadPoolExecutor
+        args = [np.ascontiguousarray(a) for a in (query, new_key, new_value, key_cache,
+                                                   value_cache)]
+        query, new_key, new_value, key_cache, value_cache = args
+        lengths = np.ascontiguousarray(lengths, dtype=np.int64)
+        B, Hq, Hk, Q, M, D, Dv = self._dims(*args)
+        kc, vc, len_out, n, status = self.append(new_key, new_value, key_cache, value_cache,
+                                                 lengths, append_mask, Hq=Hq)
+        attn = np.empty((B, Hq, Q, M), dtype=np.float64)
+        ctx = np.empty((B, Hq, Q, Dv), dtype=np.float64)
+        dt = _dtype_code(query)
+        has, sc = (0, 0.0) if scale is None else (1, float(scale))
+        qp, kp, vp = _ptr(query), _ptr(kc), _ptr(vc)
+        a0, c0 = attn.ctypes.data, ctx.ctypes.data
+        rows = [(b, hq, t) for b in range(B) for hq in range(Hq) for t in range(Q)]
+
+        def run(chunk):
+            for b, hq, t in chunk:
+                row = (b * Hq + hq) * Q + t
+                rc = self.lib.kvc_oracle_attend_row(
+                    B, Hq, Hk, Q, M, D, Dv, dt, has, sc, qp, kp, vp, int(lengths[b]),
+                    int(n[b]), b, hq, t, a0 + row * M * 8, c0 + row * Dv * 8)
+                if rc != 0:
+                    raise ValueError(f"oracle rejected the row (code {rc})")
+
+        threads = max(1, threads or os.cpu_count() or 1)
+        parts = [rows[i::threads] for i in range(threads)]
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            for f in [ex.submit(run, part) for part in parts if part]:
+                f.result()
+        return StepResult(kc, vc, len_out, attn, ctx, status)
+
     def attend_row(self, query, key_updated, value_updated, old_len: int, n: int, b: int,
                    hq: int, t: int, scale: float | None = None):
         """One (b, hq, t) row over an updated cache: returns (attention[M], context[Dv])."""

@@ -32,10 +32,24 @@ def test_step_bytes_match_closed_forms():
         assert step == inplace
         assert step + extra_step == oop
         e = 2 if wl.dtype == "bf16" else 4
-        visible = sum(wl.Hq * (L + t + 1) for L, k in zip(lengths, n) for t in range(k)) * e
         kv_read = sum(wl.Hk * (L + k) * (wl.D + wl.Dv) * e for L, k in zip(lengths, n))
-        assert attend == kv_read + wl.B * wl.Hq * wl.Q * wl.D * e + visible + wl.B * (8 + wl.Q)
+        assert attend == kv_read + wl.B * wl.Hq * wl.Q * wl.D * e + wl.B * (8 + wl.Q)
         assert extra_attend == sum(wl.Hk * L * (wl.D + wl.Dv) * e for L in lengths)
+
+
+def test_intermediate_bytes_closed_forms():
+    """The stream kernel's writes for the combine: with one chunk per worker
+    every chunk is a segment; with one worker every KV head of an appending
+    row is one segment."""
+    wl = WORKLOADS["decode_gqa_bf16"].with_(B=3, M=300, len_range=(0, 299))
+    lengths, n = [5, 130, 64], [1, 1, 0]
+    R, C = wl.Hq // wl.Hk * wl.Q, 64
+    chunks = sum(wl.Hk * (-(-L // C) + 1) for L, k in zip(lengths, n) if k)
+    per_chunk, per_seg = R * C * 2 + R * 4, R * (wl.Dv * 4 + 8)
+    assert bench.intermediate_bytes(wl, lengths, n, P=10 ** 6) == chunks * (per_chunk + per_seg)
+    heads = sum(wl.Hk for k in n if k)
+    assert bench.intermediate_bytes(wl, lengths, n, P=1) == chunks * per_chunk + heads * per_seg
+    assert bench.intermediate_bytes(wl, lengths, [0, 0, 0], P=4) == 0
 
 
 def test_decode_bytes_are_kv_dominated():
@@ -44,7 +58,8 @@ def test_decode_bytes_are_kv_dominated():
     step, attend, kv = bench.algorithmic_bytes(wl, [int(x) for x in lengths], [int(x) for x in n])
     assert 0.95 < kv / step < 1.0
     assert attend < step
-    assert np.isclose(attend / step, 1.0, atol=0.03)
+    # the attend share is the K/V stream and q; the attention rows (3 %) are the combine's
+    assert 0.95 < attend / step < 0.98
 
 
 def test_backward_bytes_scale_with_the_element_size():

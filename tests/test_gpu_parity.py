@@ -11,7 +11,7 @@ import oracle
 from autoregressive_kv_cache_amd import kvc
 from autoregressive_kv_cache_amd.workloads import (WORKLOADS, Workload, draw_lengths_and_counts,
                                                    host_arrays, make_inputs, paged_layout)
-from gpu_helpers import (bits, check_floats, check_row_sums, check_step, run_gpu, say, to_f64)
+from gpu_helpers import bits, check_floats, check_step, run_gpu, say, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -97,33 +97,21 @@ def test_long_decode_share_full_check():
         full_check(wl, 0, mode, gen_device=DEV)
 
 
-def test_long_decode_full_size_sampled():
-    """Long-context decode at its full size (B=4, Hq=64, Hk=8, M=131072):
-    caches bit-exact against the oracle's append, sampled rows against the
-    oracle one by one, row sums and zero tails on every row."""
+def test_long_decode_full_size():
+    """Long-context GQA decode at its full size (B=4, Hq=64, Hk=8, M=131072,
+    D=Dv=128, bf16): every output element against the oracle (one oracle
+    step, ~7 s, serves both entry points), in place and out of place."""
     wl = WORKLOADS["long_decode_bf16"]
+    say(f"[case] {wl.name} full size, oracle step")
+    inp = {k: v.cpu() for k, v in make_inputs(wl, 0, "cpu").items()}
+    h = host_arrays(inp)
+    ref = oracle.default().step(h["query"], h["new_key"], h["new_value"], h["key_cache"],
+                                h["value_cache"], h["lengths"], h["append_mask"], scale=wl.scale)
     for mode in ("inplace", "oop"):
         say(f"[case] {wl.name} full size mode={mode}")
-        dinp = make_inputs(wl, 0, DEV)
-        h = host_arrays(dinp)
-        kc, vc, lens, n, status = oracle.default().append(
-            h["new_key"], h["new_value"], h["key_cache"], h["value_cache"], h["lengths"],
-            h["append_mask"], Hq=wl.Hq)
+        dinp = {k: v.to(DEV) for k, v in inp.items()}
         out = run_gpu(dinp, mode)
-        assert np.array_equal(host_arrays({"x": out["key_cache"]})["x"], kc)
-        assert np.array_equal(host_arrays({"x": out["value_cache"]})["x"], vc)
-        assert np.array_equal(out["lengths"].cpu().numpy(), lens)
-        assert np.array_equal(out["row_status"].cpu().numpy(), status)
-        att = to_f64(out["attention"])
-        ctx = to_f64(out["context"])
-        check_row_sums(att, h["lengths"], n, wl.dtype, wl.name)
-        rng = np.random.default_rng(1)
-        for b in range(wl.B):
-            for hq in list(rng.choice(wl.Hq, 3, replace=False)):
-                a_ref, c_ref = oracle.default().attend_row(h["query"], kc, vc, int(h["lengths"][b]),
-                                                           int(n[b]), b, int(hq), 0)
-                check_floats(att[b, hq, 0], a_ref, wl.dtype, f"row {b},{hq}", "attention")
-                check_floats(ctx[b, hq, 0], c_ref, wl.dtype, f"row {b},{hq}", "context")
+        check_step(out, ref, wl.dtype, f"{wl.name}/{mode}")
         del dinp, out
         torch.cuda.empty_cache()
 
@@ -711,8 +699,25 @@ def test_reattend_rejected_sequences():
 
 
 # -- backward of the step (kvc_step_backward, fp32) ---------------------------
-BWD_TOL = {"f32": 1e-4,   # |d| <= 1e-4 (1 + |ref|): fp32 sums of <= M terms against the double oracle
-           "bf16": 4e-3}  # plus one rounding to bf16 (relative <= 2^-9) of every gradient
+# |d| <= BWD_TOL (1 + |ref|).  fp32: the gradients are summed in fp64 and
+# rounded once to fp32 (relative 2^-24); the largest error seen over every
+# backward case is 1.1e-7 (1 + |ref|), so 1e-6 leaves a margin of ~9x.
+# bf16: one rounding to bf16 (relative <= 2^-9) of the gradient and of the
+# pass-through sum it is added to; the largest seen is 3.7e-3.
+BWD_TOL = {"f32": 1e-6,
+           "bf16": 4e-3}
+
+
+def check_grad(got: np.ndarray, want: np.ndarray, dtype: str, what: str):
+    """|got - want| <= BWD_TOL (1 + |want|) element-wise; the largest error,
+    absolute and relative to (1 + |want|), is printed beside the bar."""
+    assert np.all(np.isfinite(got)), f"{what}: not finite"
+    diff = np.abs(got - want)
+    scaled = diff / (1 + np.abs(want))
+    mx = float(diff.max()) if diff.size else 0.0
+    ms = float(scaled.max()) if diff.size else 0.0
+    say(f"  {what}: max |d| {mx:.3e}, max |d|/(1+|ref|) {ms:.3e}; bar {BWD_TOL[dtype]:g}")
+    assert ms <= BWD_TOL[dtype], f"{what}: off by {ms:.3e} (1 + |ref|) > {BWD_TOL[dtype]:g}"
 
 BWD_CASES = [
     WORKLOADS["decode_gqa_bf16"].with_(name="bwd_decode", dtype="f32", B=3, M=300,
@@ -768,11 +773,7 @@ def test_backward_against_oracle(wl, upstream, dtype):
         for name, want in (("g_query", ref.query), ("g_new_key", ref.new_key),
                            ("g_new_value", ref.new_value), ("g_key_cache", ref.key_cache),
                            ("g_value_cache", ref.value_cache)):
-            got = to_f64(outs[name])
-            assert np.all(np.isfinite(got)), f"{wl.name}/{seed}: {name} not finite"
-            err = np.abs(got - want) - BWD_TOL[dtype] * (1 + np.abs(want))
-            assert err.max() <= 0, \
-                f"{wl.name}/{dtype}/{upstream}/{seed}: {name} off by {err.max():.3e}"
+            check_grad(to_f64(outs[name]), want, dtype, f"{wl.name}/{dtype}/{upstream}/{seed} {name}")
 
 
 @pytest.mark.parametrize("which", ["query", "d_key_cache_out", "g_value_cache", "g_new_key"])
@@ -843,6 +844,4 @@ def test_backward_full_decode_bench_configuration():
     for name, want in (("g_query", ref.query), ("g_new_key", ref.new_key),
                        ("g_new_value", ref.new_value), ("g_key_cache", ref.key_cache),
                        ("g_value_cache", ref.value_cache)):
-        assert np.all(np.isfinite(got[name])), f"full decode backward: {name} not finite"
-        err = np.abs(got[name] - want) - BWD_TOL["bf16"] * (1 + np.abs(want))
-        assert err.max() <= 0, f"full decode backward: {name} off by {err.max():.3e}"
+        check_grad(got[name], want, "bf16", f"full decode backward {name}")
