@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/kvc.h"
 #include "kvc_chunk.h"
@@ -570,9 +571,72 @@ bool reatt_layout(const kvc_dims* d, int dtype, ReattLayout* L) {
   return true;
 }
 
+// ---- scratch for the no-allocation step ----
+// A file-scope device array that serves as the step's workspace for callers
+// that cannot allocate (kvc_step_inplace_noalloc).  Every GPU the library
+// runs on holds its own copy until the process ends.  Host code never uses
+// the array's name as an address: scratch_address() looks up each device's
+// copy once, with that device current, and keeps it.
+constexpr size_t kScratchBytes = size_t(96) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The device `stream` runs on (the current device for the null stream).
+int stream_device(hipStream_t stream, int* dev) {
+  if (stream) return hipStreamGetDevice(stream, dev) == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+  return hipGetDevice(dev) == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
+// Address of device `dev`'s copy of `scratch`, looked up on first use.
+int scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return KVC_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) return KVC_ERR_HIP;
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) return KVC_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (prev != dev) (void)hipSetDevice(prev);
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return KVC_ERR_HIP;
+    }
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return KVC_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t kvc_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int kvc_step_inplace_noalloc(const kvc_dims* dims, int dtype, int has_scale, double scale,
+                             const void* query, const void* new_key, const void* new_value,
+                             void* key_cache, void* value_cache, const int64_t* lengths,
+                             const uint8_t* append_mask, int64_t* lengths_out, void* attention,
+                             void* context, int32_t* row_status, void* stream,
+                             const kvc_events* events) {
+  Plan p;
+  int rc = make_plan(dims, dtype, &p);
+  if (rc != KVC_OK) return rc;
+  if (p.pub.workspace_bytes > kScratchBytes) return KVC_ERR_TOO_LARGE;
+  int dev = 0;
+  rc = stream_device(static_cast<hipStream_t>(stream), &dev);
+  if (rc != KVC_OK) return rc;
+  void* ws = nullptr;
+  rc = scratch_address(dev, &ws);
+  if (rc != KVC_OK) return rc;
+  return run_step(dims, dtype, has_scale, scale, query, new_key, new_value, key_cache,
+                  value_cache, key_cache, value_cache, false, lengths, append_mask, lengths_out,
+                  attention, context, row_status, ws, kScratchBytes, stream, events);
+}
 
 size_t kvc_attend_workspace_bytes(const kvc_dims* dims, int dtype) {
   ReattLayout L;
@@ -750,6 +814,8 @@ const char* kvc_status_string(int code) {
     case KVC_ERR_WORKSPACE: return "workspace too small";
     case KVC_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case KVC_ERR_HIP: return "a HIP launch failed";
+    case KVC_ERR_TOO_LARGE: return "the step needs more workspace than the no-allocation entry "
+                                   "point's static scratch holds";
     case KVC_ERR_UNSUPPORTED: return "the paged cache needs the stream decode path and blocks of "
                                      ">= 64 slots";
     case KVC_ROW_BAD_LENGTH: return "row rejected: length outside [0, M]";

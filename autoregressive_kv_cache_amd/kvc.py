@@ -29,13 +29,14 @@ KVC_F32, KVC_BF16 = 0, 1
 KVC_OK = 0
 ERRORS = {-1: "KVC_ERR_NULL", -2: "KVC_ERR_SHAPE", -3: "KVC_ERR_DTYPE", -4: "KVC_ERR_SCALE",
           -5: "KVC_ERR_WORKSPACE", -6: "KVC_ERR_ALIAS", -7: "KVC_ERR_HIP",
-          -8: "KVC_ERR_UNSUPPORTED"}
+          -8: "KVC_ERR_UNSUPPORTED", -9: "KVC_ERR_TOO_LARGE"}
 ROW_OK, ROW_BAD_LENGTH, ROW_OVERFLOW, ROW_NOT_PREFIX, ROW_BAD_QUERIES = 0, 1, 2, 3, 4
 EXPORTED = ("kvc_workspace_bytes", "kvc_plan_step", "kvc_step_out_of_place",
             "kvc_step_inplace", "kvc_step_paged", "kvc_attend_workspace_bytes",
             "kvc_attend_over_cache", "kvc_backward_workspace_bytes", "kvc_step_backward",
             "kvc_status_string",
-            "kvc_read_ceiling_sink_bytes", "kvc_read_ceiling")
+            "kvc_read_ceiling_sink_bytes", "kvc_read_ceiling", "kvc_noalloc_scratch_bytes",
+            "kvc_step_inplace_noalloc")
 
 
 class KvcDims(ctypes.Structure):
@@ -101,6 +102,11 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
                                       + [_sz, _vp])
     lib.kvc_status_string.restype = ctypes.c_char_p
     lib.kvc_status_string.argtypes = [_int]
+    lib.kvc_noalloc_scratch_bytes.restype = _sz
+    lib.kvc_noalloc_scratch_bytes.argtypes = []
+    lib.kvc_step_inplace_noalloc.restype = _int
+    lib.kvc_step_inplace_noalloc.argtypes = ([ctypes.POINTER(KvcDims), _int, _int, _dbl]
+                                             + [_vp] * 11 + [_vp, ctypes.POINTER(KvcEvents)])
     lib.kvc_read_ceiling_sink_bytes.restype = _sz
     lib.kvc_read_ceiling_sink_bytes.argtypes = [_int]
     lib.kvc_read_ceiling.restype = _int
@@ -215,6 +221,24 @@ def kvc_step_inplace(query, new_key, new_value, key_cache, value_cache, lengths,
         _stream(stream, key_cache.device), _events(events))
     if rc != KVC_OK:
         raise KvcError(rc, "kvc_step_inplace")
+
+
+def kvc_step_inplace_noalloc(query, new_key, new_value, key_cache, value_cache, lengths,
+                             append_mask, lengths_out, attention, context, row_status=None,
+                             scale=None, stream=None, events=None) -> None:
+    """kvc_step_inplace without a workspace: the library's static scratch
+    serves as one (for callers that cannot allocate; see include/kvc.h)."""
+    lib = load()
+    dims = dims_of(query, key_cache, value_cache)
+    dt = dtype_code(key_cache.dtype)
+    hs, sc = _scale_args(scale)
+    rc = lib.kvc_step_inplace_noalloc(
+        ctypes.byref(dims), dt, hs, sc, _ptr(query), _ptr(new_key), _ptr(new_value),
+        _ptr(key_cache), _ptr(value_cache), _ptr(lengths), _ptr(append_mask), _ptr(lengths_out),
+        _ptr(attention), _ptr(context), _ptr(row_status), _stream(stream, key_cache.device),
+        _events(events))
+    if rc != KVC_OK:
+        raise KvcError(rc, "kvc_step_inplace_noalloc")
 
 
 def kvc_step_paged(query, new_key, new_value, key_pool, value_pool, block_table, lengths,

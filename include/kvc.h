@@ -83,7 +83,8 @@ enum {
   KVC_ERR_WORKSPACE = -5,   /* workspace_bytes < kvc_workspace_bytes() */
   KVC_ERR_ALIAS = -6,       /* an output overlaps an input or another output */
   KVC_ERR_HIP = -7,         /* a kernel launch failed (HIP error) */
-  KVC_ERR_UNSUPPORTED = -8  /* a shape, block size or buffer alignment the entry point does not take */
+  KVC_ERR_UNSUPPORTED = -8, /* a shape, block size or buffer alignment the entry point does not take */
+  KVC_ERR_TOO_LARGE = -9    /* kvc_step_inplace_noalloc: the step needs more than its static scratch */
 };
 
 /* Per-row status written to row_status[b]. */
@@ -281,6 +282,29 @@ int kvc_step_backward(const kvc_dims *dims, int dtype, int has_scale,
                       void *g_new_key, void *g_new_value, void *g_key_cache,
                       void *g_value_cache, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as kvc_step_inplace, with the same arguments minus the workspace.
+ * Its workspace is a static device array inside the library, of
+ * kvc_noalloc_scratch_bytes() bytes (96 MiB) on every GPU the library runs
+ * on, held until the process ends.  A step whose kvc_workspace_bytes()
+ * exceeds it returns KVC_ERR_TOO_LARGE before anything is enqueued.  The
+ * call allocates nothing: on its first use on a device it looks up that
+ * device's copy of the array (hipGetSymbolAddress) and keeps the address.
+ * Every call on one GPU shares that array, and nothing in it needs to start
+ * at any value; calls that overlap on one GPU (two streams, or two host
+ * threads without ordering) race on it -- order them on one stream. */
+size_t kvc_noalloc_scratch_bytes(void);
+int kvc_step_inplace_noalloc(const kvc_dims *dims, int dtype, int has_scale,
+                             double scale, const void *query,
+                             const void *new_key, const void *new_value,
+                             void *key_cache, void *value_cache,
+                             const int64_t *lengths,
+                             const uint8_t *append_mask, int64_t *lengths_out,
+                             void *attention, void *context,
+                             int32_t *row_status, void *stream,
+                             const kvc_events *events);
 
 /* Static description of a return or row-status code. */
 const char *kvc_status_string(int code);

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, 1, 2, 3, 4]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, 1, 2, 3, 4]:
         s = kvc.kvc_status_string(code)
         assert s and s != "unknown code"
     assert kvc.kvc_status_string(12345) == "unknown code"
@@ -257,3 +257,18 @@ def test_binding_argument_counts_match_the_header(lib):
     for name, params in protos.items():
         count = 0 if params.strip() in ("", "void") else params.count(",") + 1
         assert len(getattr(lib, name).argtypes) == count, (name, count)
+
+
+def test_noalloc_refuses_steps_beyond_its_scratch(lib):
+    """A step whose workspace exceeds the static scratch is refused before
+    anything is enqueued (the pointers are never touched); a bad shape is a
+    shape error."""
+    big = kvc.KvcDims(64, 64, 8, 1, 131072, 128, 128)
+    assert kvc.kvc_workspace_bytes(big, kvc.KVC_BF16) > lib.kvc_noalloc_scratch_bytes()
+    fake = [16] * 11
+    rc = lib.kvc_step_inplace_noalloc(ctypes.byref(big), kvc.KVC_BF16, 0, 0.0, *fake, None, None)
+    assert rc == -9, rc
+    rc = lib.kvc_step_inplace_noalloc(ctypes.byref(dims(B=0)), kvc.KVC_BF16, 0, 0.0, *fake, None,
+                                      None)
+    assert rc == -2, rc
+    assert lib.kvc_noalloc_scratch_bytes() == 96 << 20
