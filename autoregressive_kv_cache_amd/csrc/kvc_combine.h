@@ -44,8 +44,8 @@ __device__ inline SegRange group_segments(const StepArgs& a, int64_t grp, int64_
   if (nc <= 0) return {0, 0};
   if (!a.seg_mode) return {grp * a.nchunk_max, nc};
   const int64_t x0 = first_chunk + kvh * nc, x1 = x0 + nc - 1;
-  // owner(x) = the worker w with floor(w*Nc/Pe) <= x < floor((w+1)*Nc/Pe)
-  const int64_t w0 = ((x0 + 1) * Pe - 1) / Nc, w1 = ((x1 + 1) * Pe - 1) / Nc;
+  const int32_t lead = effective_lead(Nc, Pe, a.lead);
+  const int64_t w0 = worker_owner(x0, Nc, Pe, lead), w1 = worker_owner(x1, Nc, Pe, lead);
   return {w0 + grp, w1 - w0 + 1};
 }
 

@@ -83,6 +83,7 @@ struct StepArgs {
   int64_t nchunk_max; // ceil(M / C)
   int64_t CS;         // slots per combine workgroup (a multiple of C)
   int64_t P;          // stream workers (waves of the attend grid, stream mode)
+  int32_t lead;       // stream shares: weight, in eighths, of the workers in the first half of the grid
   int32_t seg_mode;   // 0 dense, 1 stream, 2 stream with the bf16 stream kernel's workspace
   int32_t combine_copies_tail;  // out of place: combine copies slots the attend kernel skips
   double scale;       // resolved softmax scale
@@ -237,6 +238,37 @@ __device__ __forceinline__ int64_t stream_chunks(int64_t len, int64_t n, int64_t
 }
 __device__ __forceinline__ int64_t stream_chunk_of(int64_t j, int64_t len, int64_t C) {
   return j < len ? j / C : ceil_div(len, C);
+}
+
+// Stream-K shares.  Worker w (workgroup * waves + wave) owns the flattened
+// chunks [worker_start(w), worker_start(w + 1)) of the Nc chunks, for
+// w < Pe.  With lead == 8 the shares are even: floor(w * Nc / Pe).  With
+// another lead, the workers of the first half of the grid (the first
+// workgroup placed on each compute unit when the grid holds two per unit)
+// take lead / 8 times the share of the others: on a unit the earlier
+// workgroup wins most of the memory arbitration, so even shares leave the
+// later one finishing alone.  The weights apply only when every worker
+// still gets at least one chunk (Nc >= 2 Pe); else the shares are even.
+__device__ __forceinline__ int32_t effective_lead(int64_t Nc, int64_t Pe, int32_t lead) {
+  return (lead > 8 && Pe >= 2 && Nc >= 2 * Pe) ? lead : 8;
+}
+// S(w) = lead * min(w, H) + 8 * max(w - H, 0), H = Pe / 2; start = floor(S(w) Nc / S(Pe))
+__device__ __forceinline__ int64_t worker_start(int64_t w, int64_t Nc, int64_t Pe, int32_t lead) {
+  if (lead == 8) return w * Nc / Pe;
+  const int64_t H = Pe / 2;
+  const int64_t S = lead * (w < H ? w : H) + 8 * (w > H ? w - H : 0);
+  const int64_t T = lead * H + 8 * (Pe - H);
+  return S * Nc / T;
+}
+// The worker whose range holds chunk x (0 <= x < Nc): the largest w < Pe
+// with worker_start(w) <= x, i.e. with S(w) <= floor(((x + 1) T - 1) / Nc).
+__device__ __forceinline__ int64_t worker_owner(int64_t x, int64_t Nc, int64_t Pe, int32_t lead) {
+  if (lead == 8) return ((x + 1) * Pe - 1) / Nc;
+  const int64_t H = Pe / 2;
+  const int64_t T = lead * H + 8 * (Pe - H);
+  const int64_t K = ((x + 1) * T - 1) / Nc;
+  const int64_t w = K >= lead * H ? H + (K - lead * H) / 8 : K / lead;
+  return w < Pe - 1 ? w : Pe - 1;
 }
 
 // Row preparation by one thread (same checks, same order as wave_row_info).

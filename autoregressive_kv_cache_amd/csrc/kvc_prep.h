@@ -74,11 +74,12 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(StepArgs a) {
     a.ws_hdr[1] = Pe;
   }
   if (Nc == 0) return;
-  // first chunk of each worker: x = floor(w * Nc / Pe) -> (b, head, chunk);
+  const int32_t lead = effective_lead(Nc, Pe, a.lead);
+  // first chunk of each worker: x = worker_start(w) -> (b, head, chunk);
   // the search reads the row starts from LDS when they all fit there
   const bool in_lds = a.B <= kPrepLdsRows;
   for (int64_t wk = tid; wk < Pe; wk += kPrepThreads) {
-    const int64_t x = wk * Nc / Pe;
+    const int64_t x = worker_start(wk, Nc, Pe, lead);
     int64_t lo = 0, hi = a.B - 1;  // last row whose first chunk index <= x
     while (lo < hi) {
       const int64_t mid = (lo + hi + 1) / 2;

@@ -212,7 +212,8 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
   }
   const int64_t w = blockIdx.x * static_cast<int64_t>(kDecodeWaves) + wave;
   if (w >= Pw) return;
-  const int64_t x_begin = w * Nc / Pw, x_end = (w + 1) * Nc / Pw;
+  const int32_t lead = effective_lead(Nc, Pw, a.lead);
+  const int64_t x_begin = worker_start(w, Nc, Pw, lead), x_end = worker_start(w + 1, Nc, Pw, lead);
   if (x_begin >= x_end) return;
 
   ChunkPos pos;

@@ -119,13 +119,25 @@ def algorithmic_bytes(wl, lengths, n):
     return step, attend, kv
 
 
-def intermediate_bytes(wl, lengths, n, P: int, C: int = 64, seg_partials: bool = True):
+def worker_start(w: int, Nc: int, Pe: int, lead: int) -> int:
+    """First chunk of stream worker w, as the kernels split the chunk list:
+    even shares for lead 8, else the first half of the workers weigh
+    lead / 8 (applied only when Nc >= 2 Pe)."""
+    if lead <= 8 or Pe < 2 or Nc < 2 * Pe:
+        return w * Nc // Pe
+    H = Pe // 2
+    S = lead * min(w, H) + 8 * max(w - H, 0)
+    return S * Nc // (lead * H + 8 * (Pe - H))
+
+
+def intermediate_bytes(wl, lengths, n, P: int, C: int = 64, seg_partials: bool = True,
+                       lead: int = 8):
     """Bytes the stream attend kernel writes for the combine kernel (bf16
     decode path): per chunk of the flattened list, R rows of C exp values
     (2 B) and R references (4 B); per segment (a worker's run of one KV
     head), R rows of Dv fp32 context partials and (m, l) as two floats.
-    Workers own equal contiguous ranges of the chunk list, as the kernel
-    splits it."""
+    Workers own contiguous ranges of the chunk list, split as the kernel
+    splits it (worker_start)."""
     R = wl.Hq // wl.Hk * wl.Q
     heads = []  # flattened chunk list: one entry per chunk, its (b, head)
     for b, (L, k) in enumerate(zip(lengths, n)):
@@ -140,7 +152,7 @@ def intermediate_bytes(wl, lengths, n, P: int, C: int = 64, seg_partials: bool =
     Pe = min(P, Nc)
     segs = 0
     for w in range(Pe):
-        x0, x1 = w * Nc // Pe, (w + 1) * Nc // Pe
+        x0, x1 = worker_start(w, Nc, Pe, lead), worker_start(w + 1, Nc, Pe, lead)
         segs += len(set(heads[x0:x1]))
     per_chunk = R * C * 2 + R * 4
     per_seg = R * (wl.Dv * 4 + 8) if seg_partials else 0
@@ -423,9 +435,9 @@ def main():
     step_bytes, attend_bytes, kv_bytes = algorithmic_bytes(wl, lengths, n)
     inter_bytes = None
     if args.mode in ("inplace", "oop", "paged") and plan["path"] == 1 and wl.dtype == "bf16":
-        P = torch.cuda.get_device_properties(dev).multi_processor_count * (
-            2 if plan["rows_per_tile"] <= 4 else 1) * 4
-        inter_bytes = intermediate_bytes(wl, lengths, n, P)
+        two = plan["rows_per_tile"] <= 4  # two workgroups per unit, uneven shares
+        P = torch.cuda.get_device_properties(dev).multi_processor_count * (2 if two else 1) * 4
+        inter_bytes = intermediate_bytes(wl, lengths, n, P, lead=16 if two else 8)
     if args.mode == "oop":
         extra_step, extra_attend = oop_extra_bytes(wl, lengths, n)
         step_bytes += extra_step

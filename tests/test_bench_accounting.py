@@ -93,3 +93,33 @@ def test_committed_traffic_is_gated_by_the_source_digest():
     lengths, n = draw_lengths_and_counts(wl, 0)
     _, attend, _ = bench.algorithmic_bytes(wl, [int(x) for x in lengths], [int(x) for x in n])
     assert 1.0 <= nbytes / attend < 1.05
+
+
+def _owner(x, Nc, Pe, lead):
+    """The kernels' closed-form inverse of worker_start (worker_owner)."""
+    if lead <= 8 or Pe < 2 or Nc < 2 * Pe:
+        return ((x + 1) * Pe - 1) // Nc
+    H = Pe // 2
+    T = lead * H + 8 * (Pe - H)
+    K = ((x + 1) * T - 1) // Nc
+    w = H + (K - lead * H) // 8 if K >= lead * H else K // lead
+    return min(w, Pe - 1)
+
+
+def test_uneven_worker_shares_partition_the_chunks():
+    """The stream workers' ranges cover [0, Nc) once, each holds a chunk, the
+    first half takes about lead / 8 times the share of the second, and the
+    combine's owner formula names the worker whose range holds a chunk."""
+    for lead in (8, 16, 24):
+        for Nc, Pe in ((18431, 2048), (4096, 2048), (4095, 2048), (100003, 1024), (37, 6)):
+            starts = [bench.worker_start(w, Nc, Pe, lead) for w in range(Pe + 1)]
+            assert starts[0] == 0 and starts[-1] == Nc
+            assert all(b - a >= 1 for a, b in zip(starts, starts[1:]))
+            if lead > 8 and Nc >= 2 * Pe:
+                H = Pe // 2  # the first half's chunks: lead H / (lead H + 8 (Pe - H)) of all
+                assert starts[H] == lead * H * Nc // (lead * H + 8 * (Pe - H))
+            w = 0
+            for x in range(Nc):
+                while starts[w + 1] <= x:
+                    w += 1
+                assert _owner(x, Nc, Pe, lead) == w, (lead, Nc, Pe, x)
