@@ -332,8 +332,8 @@ template <typename T>
 void launch_combine(const StepArgs& a, hipStream_t stream) {
   const int64_t groups = a.B * a.Hk;
   const int64_t nrb = a.R > 0 ? (a.R + kvc::kCombineWaves - 1) / kvc::kCombineWaves : 1;
-  hipLaunchKernelGGL(kvc::combine_kernel<T>,
-                     dim3(static_cast<unsigned>(groups * ((a.M + a.CS - 1) / a.CS + 1) * nrb)),
+  const int64_t roles = a.read_only ? 1 : (a.M + a.CS - 1) / a.CS + 1;
+  hipLaunchKernelGGL(kvc::combine_kernel<T>, dim3(static_cast<unsigned>(groups * roles * nrb)),
                      dim3(kvc::kCombineThreads), 0, stream, a);
 }
 
@@ -371,8 +371,8 @@ void launch_stream(StepArgs& a, const DecodeEntry& e, hipStream_t stream, const 
   if (e.stream) {
     const int64_t groups = a.B * a.Hk;
     const int64_t nrb = a.R > 0 ? (a.R + kvc::kCombineWaves - 1) / kvc::kCombineWaves : 1;
-    hipLaunchKernelGGL(kvc::combine_stream_kernel,
-                       dim3(static_cast<unsigned>(groups * ((a.M + a.CS - 1) / a.CS + 1) * nrb)),
+    const int64_t roles = a.read_only ? 1 : (a.M + a.CS - 1) / a.CS + 1;
+    hipLaunchKernelGGL(kvc::combine_stream_kernel, dim3(static_cast<unsigned>(groups * roles * nrb)),
                        dim3(kvc::kCombineThreads), 0, stream, a);
   } else {
     launch_combine<T>(a, stream);
@@ -433,7 +433,9 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
   }
 
   if (!kc_in || !vc_in || !kc_out || !vc_out || !lengths || !lengths_out) return KVC_ERR_NULL;
-  if (d->Q > 0 && (!query || !new_key || !new_value || !mask || !attention || !context))
+  // (read-only re-attention writes no attention rows: none is passed)
+  if (d->Q > 0 && (!query || !new_key || !new_value || !mask || (!attention && !read_only) ||
+                   !context))
     return KVC_ERR_NULL;
   if (p.pub.workspace_bytes > 0 && !workspace) return KVC_ERR_NULL;
   if (workspace_bytes < p.pub.workspace_bytes) return KVC_ERR_WORKSPACE;
@@ -545,8 +547,10 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
 // Workspace of a re-attention: the equivalent step's own workspace, then its
 // inputs (old lengths, mask, query rows, the appended-row copies) and
 // outputs (lengths, status, attention, context).
+// The equivalent step's inputs and context (no attention rows: the step runs
+// read-only and writes none).
 struct ReattLayout {
-  size_t step, len0, lens_out, rstat, status, mask, qs, nk, nv, att, ctx, bytes;
+  size_t step, len0, lens_out, rstat, status, mask, qs, nk, nv, ctx, bytes;
 };
 
 bool reatt_layout(const kvc_dims* d, int dtype, ReattLayout* L) {
@@ -570,9 +574,9 @@ bool reatt_layout(const kvc_dims* d, int dtype, ReattLayout* L) {
   L->qs = take(B * Hq * Q * D * e);
   L->nk = take(B * Hk * Q * D * e);
   L->nv = take(B * Hk * Q * Dv * e);
-  L->att = take(B * Hq * Q * M * e);
   L->ctx = take(B * Hq * Q * Dv * e);
   L->bytes = off;
+  (void)M;
   return true;
 }
 
@@ -652,7 +656,8 @@ int kvc_attend_over_cache(const kvc_dims* dims, int dtype, int has_scale, double
                           const void* q, int64_t total_q, const int64_t* cu_seqlens_q,
                           const void* key_cache, const void* value_cache, int64_t num_blocks,
                           int64_t block_size, const int32_t* block_table, const int32_t* slot_ids,
-                          const int64_t* seqlens_k, const float* head_sink, void* out,
+                          const int64_t* seqlens_k, int64_t seqlens_k_count,
+                          const float* head_sink, void* out,
                           int32_t* row_status, void* workspace, size_t workspace_bytes,
                           void* stream, const kvc_events* events) {
   if (!dims) return KVC_ERR_NULL;
@@ -665,6 +670,7 @@ int kvc_attend_over_cache(const kvc_dims* dims, int dtype, int has_scale, double
   ReattLayout L;
   if (!reatt_layout(d, dtype, &L)) return KVC_ERR_SHAPE;
   if (total_q < 0 || num_blocks < 1) return KVC_ERR_SHAPE;
+  if (seqlens_k_count != d->B && seqlens_k_count != d->B + 1) return KVC_ERR_SHAPE;
   if (!cu_seqlens_q || !key_cache || !value_cache || !seqlens_k || !workspace) return KVC_ERR_NULL;
   if (total_q > 0 && (!q || !out)) return KVC_ERR_NULL;
   if (workspace_bytes < L.bytes) return KVC_ERR_WORKSPACE;
@@ -709,7 +715,8 @@ int kvc_attend_over_cache(const kvc_dims* dims, int dtype, int has_scale, double
   const Range r_q{q, Tq * Hq * D * e}, r_cu{cu_seqlens_q, (B + 1) * 8},
       r_kc{key_cache, rows * Hk * D * e}, r_vc{value_cache, rows * Hk * Dv * e},
       r_tab{block_table ? static_cast<const void*>(block_table) : slot_ids, tab},
-      r_lk{seqlens_k, B * 8}, r_sink{head_sink, head_sink ? Hq * 4 : 0},
+      r_lk{seqlens_k, static_cast<size_t>(seqlens_k_count) * 8},
+      r_sink{head_sink, head_sink ? Hq * 4 : 0},
       r_out{out, Tq * Hq * Dv * e}, r_st{row_status, row_status ? B * 4 : 0},
       r_ws{workspace, L.bytes};
   const Range ins[] = {r_q, r_cu, r_kc, r_vc, r_tab, r_lk, r_sink};
@@ -736,6 +743,7 @@ int kvc_attend_over_cache(const kvc_dims* dims, int dtype, int has_scale, double
   r.q = static_cast<const uint8_t*>(q);
   r.cu_q = cu_seqlens_q;
   r.seqlens_k = seqlens_k;
+  r.cum_k = seqlens_k_count == d->B + 1 ? 1 : 0;
   r.out = static_cast<uint8_t*>(out);
   r.row_status = row_status;
   r.len0 = reinterpret_cast<int64_t*>(ws + L.len0);
@@ -750,7 +758,7 @@ int kvc_attend_over_cache(const kvc_dims* dims, int dtype, int has_scale, double
                      dim3(kvc::kReattThreads), 0, s, a, r);
   rc = run_step(d, dtype, has_scale, scale, r.qs, r.nk, r.nv, key_cache, value_cache,
                 const_cast<void*>(key_cache), const_cast<void*>(value_cache), false, r.len0,
-                r.mask, reinterpret_cast<int64_t*>(ws + L.lens_out), ws + L.att, ws + L.ctx,
+                r.mask, reinterpret_cast<int64_t*>(ws + L.lens_out), nullptr, ws + L.ctx,
                 reinterpret_cast<int32_t*>(ws + L.status), workspace, L.step, stream, events,
                 pgp, true, head_sink);
   if (rc != KVC_OK) return rc;

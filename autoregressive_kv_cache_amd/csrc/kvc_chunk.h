@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_kernel(StepArgs a)
       for (int jt = 0; jt < C / 16; jt++) {
         const int jl = jt * 16 + li;
         const uint16_t pb = f32_to_bf16(sv[jt][i]);
-        if (row_ok[i] && jl < nact && s0 + jl <= len + t_of[i]) arow[jl] = pb;
+        if (row_ok[i] && jl < nact && s0 + jl <= len + t_of[i] && !a.read_only) arow[jl] = pb;
         ptile[(4 * lq + i) * PP + jl] = pb;
       }
       if (li == 0 && r < a.R) {
@@ -481,7 +481,8 @@ __global__ __launch_bounds__(kChunkThreads) void attend_chunk_f32_kernel(StepArg
 #pragma unroll
       for (int jt = 0; jt < C / 16; jt++) {
         const int jl = jt * 16 + li;
-        if (row_ok && jl < nact && s0 + jl <= len + t) arow[jl] = static_cast<float>(sv[jt]);
+        if (row_ok && jl < nact && s0 + jl <= len + t && !a.read_only)
+          arow[jl] = static_cast<float>(sv[jt]);
         ptile[(4 * i + lq) * PP + jl] = sv[jt];
       }
       if (li == 0 && r < a.R) {

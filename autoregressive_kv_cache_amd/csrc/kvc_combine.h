@@ -156,9 +156,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int64_t ncw = ceil_div(a.M, a.CS);
   const int64_t nrb = a.R > 0 ? ceil_div(a.R, kCombineWaves) : 1;
+  // read-only (re-attention): only the context is wanted -- the grid holds
+  // the context role of each group alone, and no attention row is written
   const int64_t rb = blockIdx.x % nrb;
-  const int64_t k = (blockIdx.x / nrb) % (ncw + 1);
-  const int64_t grp = blockIdx.x / nrb / (ncw + 1);
+  const int64_t k = a.read_only ? ncw : (blockIdx.x / nrb) % (ncw + 1);
+  const int64_t grp = a.read_only ? blockIdx.x / nrb : blockIdx.x / nrb / (ncw + 1);
   const bool ctx_role = k == ncw;
   const int64_t b = grp / a.Hk, kvh = grp % a.Hk;
   // the row record and the stream header in one round of loads
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(StepArgs a) {
     return a.seg_mode && j >= len ? len_chunks : j >> a.C_log2;
   };
 
-  if (k == 0 && kvh == 0 && rb == 0 && tid == 0) {
+  if ((a.read_only ? ctx_role : k == 0) && kvh == 0 && rb == 0 && tid == 0) {
     a.lengths_out[b] = len + n;
     if (a.row_status) a.row_status[b] = status;
   }

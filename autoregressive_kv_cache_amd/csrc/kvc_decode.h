@@ -661,7 +661,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<ROWS>()))) void attend_
       for (int gi = lane; gi < ROWS * C / AVEC; gi += kWave) {
         const int r = gi / (C / AVEC), s0 = (gi % (C / AVEC)) * AVEC;
         const int t = Q1 ? 0 : r % Q;
-        if (r < R && t < pos.n && s0 < n_all) {
+        if (r < R && t < pos.n && s0 < n_all && !a.read_only) {
           T* dst = abase + static_cast<int64_t>(r) * M + s0;
           if (vec16 && s0 + AVEC <= n_all) {
             *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(atile + r * C + s0);

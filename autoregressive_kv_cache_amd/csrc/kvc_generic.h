@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kGenericThreads) void attend_generic_kernel(StepArg
       const Acc p = (m == neg_inf || sc[r][i] == neg_inf) ? Acc(0) : acc_exp(sc[r][i] - m);
       sc[r][i] = p;
       l += p;
-      if (t < n) E::store(arow + i, p);
+      if (t < n && !a.read_only) E::store(arow + i, p);
     }
     l = wave_sum(l);
     if (lane == 0) {

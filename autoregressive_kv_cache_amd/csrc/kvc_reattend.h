@@ -23,7 +23,8 @@ struct ReattArgs {
   int64_t Tq;
   const uint8_t* q;          // [Tq][Hq][D]
   const int64_t* cu_q;       // [B + 1]
-  const int64_t* seqlens_k;  // [B]
+  const int64_t* seqlens_k;  // [B] lengths, or [B + 1] cumulative offsets (cum_k)
+  int32_t cum_k;
   uint8_t* out;              // [Tq][Hq][Dv]
   int32_t* row_status;       // [B] or null
   // the equivalent step's inputs and context, in the workspace
@@ -61,11 +62,18 @@ __device__ inline void copy_rows(int64_t rows, int64_t rb, Src src, Dst dst, boo
   }
 }
 
+// Sequence b's total cached length L_b: seqlens_k[b], or seqlens_k[b + 1] -
+// seqlens_k[b] in the cumulative form ("ClikaRT::ops::attention_over_cache",
+// function description: per-seq [B] or cumulative [B+1]).
+__device__ inline int64_t reatt_len(const ReattArgs& r, int64_t b) {
+  return r.cum_k ? r.seqlens_k[b + 1] - r.seqlens_k[b] : r.seqlens_k[b];
+}
+
 // Row checks of sequence b: a cached length outside [0, M] (bad length), or
 // a query range that is not inside [0, Tq], holds more than Q tokens or more
 // tokens than are cached (bad queries).
 __device__ inline int32_t reatt_status(const StepArgs& a, const ReattArgs& r, int64_t b) {
-  const int64_t L = r.seqlens_k[b], c0 = r.cu_q[b], c1 = r.cu_q[b + 1], S = c1 - c0;
+  const int64_t L = reatt_len(r, b), c0 = r.cu_q[b], c1 = r.cu_q[b + 1], S = c1 - c0;
   if (L < 0 || L > a.M) return kRowBadLength;
   if (c0 < 0 || c1 > r.Tq || S < 0 || S > a.Q || S > L) return kRowBadQueries;
   return kRowOk;
@@ -80,7 +88,7 @@ __global__ __launch_bounds__(kReattThreads) void reattend_prep_kernel(StepArgs a
   const int tid = threadIdx.x;
   const int32_t st = reatt_status(a, r, b);
   const bool ok = st == kRowOk;
-  const int64_t L = r.seqlens_k[b], c0 = r.cu_q[b], S = ok ? r.cu_q[b + 1] - c0 : 0;
+  const int64_t L = reatt_len(r, b), c0 = r.cu_q[b], S = ok ? r.cu_q[b + 1] - c0 : 0;
   if (tid == 0) {
     r.len0[b] = ok ? L - S : 0;
     r.rstat[b] = st;

@@ -337,6 +337,11 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
   int64_t xs0 = x_begin;
   int ns = 0;
   auto flush_stash = [&]() {
+    if (a.read_only) {  // re-attention: the exp values serve only the attention rows
+      xs0 += ns;
+      ns = 0;
+      return;
+    }
     wave_lds_sync();
     // exp values: ns chunks of R rows of C bf16, contiguous in the workspace
     const int pieces = ns * R * (C / 8);

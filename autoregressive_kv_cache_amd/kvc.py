@@ -93,8 +93,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kvc_attend_workspace_bytes.argtypes = [ctypes.POINTER(KvcDims), _int]
     lib.kvc_attend_over_cache.restype = _int
     lib.kvc_attend_over_cache.argtypes = ([ctypes.POINTER(KvcDims), _int, _int, _dbl, _vp, _i64,
-                                           _vp, _vp, _vp, _i64, _i64] + [_vp] * 7
-                                          + [_sz, _vp, ctypes.POINTER(KvcEvents)])
+                                           _vp, _vp, _vp, _i64, _i64] + [_vp] * 3 + [_i64]
+                                          + [_vp] * 4 + [_sz, _vp, ctypes.POINTER(KvcEvents)])
     lib.kvc_backward_workspace_bytes.restype = _sz
     lib.kvc_backward_workspace_bytes.argtypes = [ctypes.POINTER(KvcDims), _int]
     lib.kvc_step_backward.restype = _int
@@ -276,11 +276,12 @@ def kvc_attend_over_cache(q, cu_seqlens_q, key_cache, value_cache, seqlens_k, ou
     """Enqueue the read-only re-attention on ``stream``.  ``key_cache`` is a
     block pool ``[num_blocks, Hk, block_size, D]`` when ``block_table`` is
     given, else a continuous cache ``[rows, Hk, M, D]`` read through
-    ``slot_ids`` (or row b); ``Q`` is the most query tokens of a sequence."""
+    ``slot_ids`` (or row b); ``Q`` is the most query tokens of a sequence.
+    ``seqlens_k`` holds the B cached lengths, or B + 1 cumulative offsets."""
     lib = load()
     Tq, Hq, D = q.shape
     num_blocks, Hk, bs, _ = key_cache.shape
-    B = seqlens_k.shape[0]
+    B = cu_seqlens_q.shape[0] - 1
     if M is None:
         M = block_table.shape[1] * bs if block_table is not None else bs
     dims = KvcDims(B, Hq, Hk, int(Q), int(M), D, value_cache.shape[3])
@@ -292,7 +293,8 @@ def kvc_attend_over_cache(q, cu_seqlens_q, key_cache, value_cache, seqlens_k, ou
     rc = lib.kvc_attend_over_cache(
         ctypes.byref(dims), dt, hs, sc, _ptr(q), int(Tq), _ptr(cu_seqlens_q), _ptr(key_cache),
         _ptr(value_cache), int(num_blocks), int(bs), _ptr(block_table), _ptr(slot_ids),
-        _ptr(seqlens_k), _ptr(head_sink), _ptr(out), _ptr(row_status), _ptr(workspace),
+        _ptr(seqlens_k), int(seqlens_k.numel()), _ptr(head_sink), _ptr(out), _ptr(row_status),
+        _ptr(workspace),
         workspace.numel(), _stream(stream, key_cache.device), _events(events))
     if rc != KVC_OK:
         raise KvcError(rc, "kvc_attend_over_cache")

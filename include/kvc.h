@@ -202,7 +202,11 @@ int kvc_step_paged(const kvc_dims *dims, int dtype, int has_scale,
  *   q            [total_q, Hq, D]   packed varlen queries; sequence b owns
  *                                   rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
  *   cu_seqlens_q [B + 1] int64      (S_b = cu_seqlens_q[b+1] - cu_seqlens_q[b])
- *   seqlens_k    [B] int64          each sequence's total cached length L_b
+ *   seqlens_k    int64, seqlens_k_count entries: each sequence's total
+ *                cached length L_b, either per sequence ([B]: L_b =
+ *                seqlens_k[b]) or cumulative ([B + 1]: L_b = seqlens_k[b+1]
+ *                - seqlens_k[b]) -- the page's two forms of cu_seqlens_k;
+ *                any other count is KVC_ERR_SHAPE
  *   head_sink    [Hq] float32       optional per-head sink logit
  *   out          [total_q, Hq, Dv]  written for every query row
  *
@@ -236,7 +240,7 @@ int kvc_attend_over_cache(const kvc_dims *dims, int dtype, int has_scale,
                           const void *value_cache, int64_t num_blocks,
                           int64_t block_size, const int32_t *block_table,
                           const int32_t *slot_ids, const int64_t *seqlens_k,
-                          const float *head_sink, void *out,
+                          int64_t seqlens_k_count, const float *head_sink, void *out,
                           int32_t *row_status, void *workspace,
                           size_t workspace_bytes, void *stream,
                           const kvc_events *events);

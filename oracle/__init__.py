@@ -270,8 +270,11 @@ def _oracle_reattend(oracle: "Oracle", q, cu_seqlens_q, key, value, seqlens_k, Q
                      sink=None, scale=None):
     """Read-only re-attention over the logical caches key [B, Hk, M, D] /
     value [B, Hk, M, Dv] (sequence b's cache; paged or row-mapped caches are
-    gathered into this form first).  Returns (out [Tq, Hq, Dv] float64,
-    status [B] int32)."""
+    gathered into this form first).  seqlens_k holds each sequence's total
+    cached length, per sequence ([B]) or cumulative ([B + 1], the length
+    being the difference of neighbours): "ClikaRT::ops::attention_over_cache",
+    function description, on cu_seqlens_k.  Returns (out [Tq, Hq, Dv]
+    float64, status [B] int32)."""
     q = np.ascontiguousarray(q)
     key = np.ascontiguousarray(key)
     value = np.ascontiguousarray(value)
@@ -280,6 +283,10 @@ def _oracle_reattend(oracle: "Oracle", q, cu_seqlens_q, key, value, seqlens_k, Q
     dt = _dtype_code(q)
     Tq, Hq, D = q.shape
     B, Hk, M, _ = key.shape
+    if lk.shape == (B + 1,):
+        lk = np.ascontiguousarray(lk[1:] - lk[:-1])
+    elif lk.shape != (B,):
+        raise ValueError(f"seqlens_k has {lk.shape[0]} entries; {B} or {B + 1} expected")
     Dv = value.shape[3]
     sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float64)
     out = np.empty((Tq, Hq, Dv), dtype=np.float64)

@@ -209,7 +209,7 @@ def test_host_checks_attend_over_cache(lib):
     """kvc_attend_over_cache: layout, scope, workspace and aliasing are checked
     on the host before anything is enqueued (every call here fails one)."""
     def run(d, Tq=4, num_blocks=8, block_size=None, table=False, slots=False, ptrs=None,
-            ws=1 << 34, sink=True):
+            ws=1 << 34, sink=True, kcount=None):
         e = 2
         B, Hq, Hk, Q, M, D, Dv = d.B, d.Hq, d.Hk, d.Q, d.M, d.D, d.Dv
         bs = M if block_size is None else block_size
@@ -224,7 +224,9 @@ def test_host_checks_attend_over_cache(lib):
         qp, cu, kc, vc, tb, sl, lk, sk, out, st = ptrs
         return lib.kvc_attend_over_cache(ctypes.byref(d), kvc.KVC_BF16, 0, 0.0, qp, Tq, cu, kc, vc,
                                          num_blocks, bs, tb if table else None,
-                                         sl if slots else None, lk, sk if sink else None, out, st,
+                                         sl if slots else None, lk,
+                                         d.B if kcount is None else kcount,
+                                         sk if sink else None, out, st,
                                          FAKE * 4, ws, None, None), ptrs
 
     d = dims(B=4, Hq=8, Hk=2, Q=1, M=1024, D=128, Dv=128)
@@ -237,6 +239,9 @@ def test_host_checks_attend_over_cache(lib):
     assert run(d, table=True, block_size=32)[0] == -8               # smaller than a chunk
     assert run(dims(B=4, Hq=8, Hk=2, Q=4, M=1024, D=96, Dv=96), slots=True)[0] == -8  # generic
     assert run(d, ws=16)[0] == -5
+    assert run(d, ws=16, kcount=d.B + 1)[0] == -5                   # cumulative form accepted
+    for kc in (0, d.B - 1, d.B + 2):                                # [B] or [B + 1] only
+        assert run(d, kcount=kc)[0] == -2, kc
     _, ptrs = run(d, ws=16)
     bad = list(ptrs)
     bad[1] = None

@@ -596,7 +596,7 @@ def run_reatt(q, cu, kc, vc, L, Q, M=None, table=None, slots=None, sink=None, sc
         q=q, cu=cu, kc=kc, vc=vc, L=L, table=table, slots=slots, sink=sink).items()}
     out = torch.full((q.shape[0], q.shape[1], vc.shape[3]), float("nan"), dtype=kc.dtype,
                      device=DEV)
-    status = torch.full((L.shape[0],), -9, dtype=torch.int32, device=DEV)
+    status = torch.full((cu.shape[0] - 1,), -9, dtype=torch.int32, device=DEV)
     before = (bits_t(d["kc"]).clone(), bits_t(d["vc"]).clone())
     kvc.kvc_attend_over_cache(d["q"], d["cu"], d["kc"], d["vc"], d["L"], out, Q, M=M,
                               block_table=d["table"], slot_ids=d["slots"], head_sink=d["sink"],
@@ -614,16 +614,22 @@ def reatt_ref(q, cu, kc_logical, vc_logical, L, Q, sink=None, scale=None):
                                      scale=scale)
 
 
+def cumulative(L: torch.Tensor, start: int = 1000) -> torch.Tensor:
+    """The [B + 1] cumulative form of per-sequence lengths (any start)."""
+    return torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(L, 0)]) + start
+
+
 def test_reattend_full_size_decode_shape():
     """Re-attention at the full decode size (32 sequences, 32 query heads
     over 8 KV heads, 8192 cached slots, up to one query each): the packed
-    output against the oracle."""
-    say("[case] reattend full decode size")
+    output against the oracle, with the cached lengths in both forms."""
     q, cu, kc, vc, L, S = reatt_case("bf16", 32, 32, 8, 1, 8192, 128, 128, 3)
-    out, st = run_reatt(q, cu, kc, vc, L, 1)
     ref, rst = reatt_ref(q, cu, kc, vc, L, 1)
-    assert list(st.numpy()) == list(rst)
-    check_floats(to_f64(out), ref, "bf16", "reattend full size", "context")
+    for form, Lk in (("lengths", L), ("cumulative", cumulative(L))):
+        say(f"[case] reattend full decode size, {form}")
+        out, st = run_reatt(q, cu, kc, vc, Lk, 1)
+        assert list(st.numpy()) == list(rst)
+        check_floats(to_f64(out), ref, "bf16", f"reattend full size ({form})", "context")
     del q, kc, vc
     torch.cuda.empty_cache()
 
@@ -636,15 +642,18 @@ REATT_CASES = [
 ]
 
 
+@pytest.mark.parametrize("kform", ["lengths", "cumulative"])
 @pytest.mark.parametrize("case", REATT_CASES, ids=lambda c: "-".join(map(str, c)))
 @pytest.mark.parametrize("layout", ["rows", "slot_ids", "paged"])
-def test_reattend_against_oracle(case, layout):
+def test_reattend_against_oracle(case, layout, kform):
     dtype, B, Hq, Hk, Qmax, M, D, Dv = case
     for seed in (0, 1):
-        say(f"[case] reattend {case} {layout} seed={seed}")
+        say(f"[case] reattend {case} {layout} {kform} seed={seed}")
         rows = B + 3 if layout == "slot_ids" else B
         q, cu, kc, vc, L, S = reatt_case(dtype, B, Hq, Hk, Qmax, M, D, Dv, seed, rows=rows,
                                          std=4.0 if dtype == "f32" else 1.0)
+        if kform == "cumulative":  # the oracle takes the same form
+            L = cumulative(L, start=seed * 77)
         sink = torch.from_numpy(np.random.default_rng(seed + 9).standard_normal(Hq) * 3
                                 ).float() if seed == 1 else None
         scale = 0.25 if dtype == "f32" else None
@@ -689,13 +698,18 @@ def test_reattend_rejected_sequences():
     cu = torch.tensor([0, 1, 3, 4, 7], dtype=torch.int64)  # S = 1, 2, 1, 3 (> Q = 2)
     q = torch.randn(7, 8, 128).to(torch.bfloat16)
     L = torch.tensor([300, 1, 50, 100], dtype=torch.int64)   # L > M; S > L
-    out, st = run_reatt(q, cu, kc, vc, L, 2)
-    ref, rst = reatt_ref(q, cu, kc, vc, L, 2)
-    assert list(st.numpy()) == [kvc.ROW_BAD_LENGTH, kvc.ROW_BAD_QUERIES, kvc.ROW_OK,
-                                kvc.ROW_BAD_QUERIES] == list(rst)
-    got = to_f64(out)
-    assert not got[[0, 1, 2, 4, 5, 6]].any()
-    check_floats(got, ref, "bf16", "reattend rejected", "context")
+    for Lk in (L, cumulative(L)):
+        out, st = run_reatt(q, cu, kc, vc, Lk, 2)
+        ref, rst = reatt_ref(q, cu, kc, vc, Lk, 2)
+        assert list(st.numpy()) == [kvc.ROW_BAD_LENGTH, kvc.ROW_BAD_QUERIES, kvc.ROW_OK,
+                                    kvc.ROW_BAD_QUERIES] == list(rst)
+        got = to_f64(out)
+        assert not got[[0, 1, 2, 4, 5, 6]].any()
+        check_floats(got, ref, "bf16", "reattend rejected", "context")
+    # offsets that go down: a negative length is a bad length
+    down = torch.tensor([0, 5, 3, 53, 153], dtype=torch.int64)
+    _, st = run_reatt(q, cu, kc, vc, down, 2)
+    assert int(st[1]) == kvc.ROW_BAD_LENGTH
 
 
 # -- backward of the step (kvc_step_backward, fp32) ---------------------------

@@ -106,3 +106,24 @@ def test_rejected_rows(orc):
     assert not out[:4].any() and out[4].any()
     _, st = orc.reattend(q, cu, k, v, np.array([1, 3, 1]), 2)  # S = 3 > Q = 2
     assert st[1] == oracle.ROW_BAD_QUERIES
+
+
+def test_cumulative_lengths_form(orc):
+    """cu_seqlens_k in its cumulative form ([B + 1] offsets, any start):
+    sequence b's length is the difference of neighbours, so the outputs and
+    codes are those of the per-sequence form; offsets that go down give a
+    negative length, which is a bad length; any other count is refused."""
+    rng = np.random.default_rng(7)
+    B, Hq, Hk, M, D, Dv, Q = 4, 4, 2, 10, 8, 8, 2
+    S, L = [1, 2, 0, 2], [3, 10, 4, 2]
+    q, cu, k, v, lk = draw(rng, B, Hq, Hk, M, D, Dv, S, L)
+    want, wst = orc.reattend(q, cu, k, v, lk, Q)
+    cum = 17 + np.concatenate([[0], np.cumsum(lk)]).astype(np.int64)
+    got, gst = orc.reattend(q, cu, k, v, cum, Q)
+    assert np.array_equal(got, want) and np.array_equal(gst, wst)
+    down = cum.copy()
+    down[2] = down[1] - 1  # sequence 1 gets length -1, sequence 2 a longer one
+    _, st = orc.reattend(q, cu, k, v, down, Q)
+    assert st[1] == 1 and st[0] == wst[0] and st[3] == wst[3]
+    with pytest.raises(ValueError):
+        orc.reattend(q, cu, k, v, cum[:-2], Q)
