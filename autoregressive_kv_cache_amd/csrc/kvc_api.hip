@@ -64,30 +64,43 @@ void launch_decode(const StepArgs& a, hipStream_t s) {
 }
 
 // bf16 caches: the stream kernel of kvc_stream.h.
-template <int D, int DV, int ROWS, bool Q1>
-void launch_stream_q(const StepArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.P / kvc::kDecodeWaves)), block(kvc::kDecodeThreads);
+template <int D, int DV, int ROWS, bool Q1, bool G>
+void launch_stream_g(const StepArgs& a, hipStream_t s) {
+  // rg_waves waves per stream worker
+  const dim3 grid(static_cast<unsigned>(a.P * a.rg_waves / kvc::kDecodeWaves)),
+      block(kvc::kDecodeThreads);
   const int64_t* ri = a.ws_rowinfo;
   const int32_t* wst = a.ws_wstart;
   const bool fused = a.B <= kvc::kDecodeFusedRows;
   if (a.paged && fused)
-    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, false, true, true>), grid,
+    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, false, true, true, G>), grid,
                        block, 0, s, a, ri, wst);
   else if (a.paged)
-    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, false, false, true>), grid,
+    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, false, false, true, G>), grid,
                        block, 0, s, a, ri, wst);
   else if (a.out_of_place && fused)
-    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, true, true, false>), grid,
+    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, true, true, false, G>), grid,
                        block, 0, s, a, ri, wst);
   else if (a.out_of_place)
-    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, true, false, false>), grid,
+    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, true, false, false, G>), grid,
                        block, 0, s, a, ri, wst);
   else if (fused)
-    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, false, true, false>), grid,
+    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, false, true, false, G>), grid,
                        block, 0, s, a, ri, wst);
   else
-    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, false, false, false>), grid,
+    hipLaunchKernelGGL((kvc::attend_stream_kernel<D, DV, ROWS, Q1, false, false, false, G>), grid,
                        block, 0, s, a, ri, wst);
+}
+
+template <int D, int DV, int ROWS, bool Q1>
+void launch_stream_q(const StepArgs& a, hipStream_t s) {
+  if constexpr (ROWS == 8) {  // row groups: past 8 packed rows only
+    if (a.rg_waves > 1) {
+      launch_stream_g<D, DV, ROWS, Q1, true>(a, s);
+      return;
+    }
+  }
+  launch_stream_g<D, DV, ROWS, Q1, false>(a, s);
 }
 
 template <typename T, int D, int DV, int ROWS>
@@ -174,18 +187,31 @@ const ChunkEntry kChunkTable[] = {
     {KVC_F32, 128, 128, &launch_chunk_f32<128, 128>},
 };
 
+// The matrix-core chunk path: only where the packed rows of a KV head fill
+// at least one 16-row MFMA tile ("a real dense contraction").
+constexpr int64_t kChunkMinRows = 16;
 const ChunkEntry* find_chunk(const kvc_dims* d, int dtype, int64_t R) {
-  if (R <= 8) return nullptr;
+  if (R < kChunkMinRows) return nullptr;
   for (const ChunkEntry& e : kChunkTable)
     if (e.dtype == dtype && e.D == d->D && e.Dv == d->Dv) return &e;
   return nullptr;
 }
 
-const DecodeEntry* find_decode(const kvc_dims* d, int dtype, int64_t R) {
-  if (R > 8) return nullptr;
+// The vector decode path: a wave holds 4 or 8 packed rows.  Past 8 (up to
+// 15: the chunk path starts at 16) the bf16 stream kernel splits the rows
+// into two groups of up to 8, two waves of one worker (*rg_waves = 2).
+constexpr int64_t kStreamMaxRows = kChunkMinRows - 1;
+const DecodeEntry* find_decode(const kvc_dims* d, int dtype, int64_t R, int* rg_waves) {
+  *rg_waves = 1;
   const int rows = R <= 4 ? 4 : 8;
-  for (const DecodeEntry& e : kDecodeTable)
-    if (e.dtype == dtype && e.D == d->D && e.Dv == d->Dv && e.rows == rows) return &e;
+  for (const DecodeEntry& e : kDecodeTable) {
+    if (e.dtype != dtype || e.D != d->D || e.Dv != d->Dv || e.rows != rows) continue;
+    if (R <= 8) return &e;
+    if (e.stream && R <= kStreamMaxRows) {
+      *rg_waves = 2;
+      return &e;
+    }
+  }
   return nullptr;
 }
 
@@ -247,7 +273,8 @@ struct Plan {
   const DecodeEntry* decode;  // vector decode path, or null
   const ChunkEntry* chunk;    // matrix-core chunk path, or null
   Layout generic, stream, dense;
-  int64_t P;
+  int64_t P;     // stream workers
+  int rg_waves;  // waves per stream worker
 };
 
 int make_plan(const kvc_dims* d, int dtype, Plan* p) {
@@ -256,9 +283,11 @@ int make_plan(const kvc_dims* d, int dtype, Plan* p) {
   std::memset(p, 0, sizeof *p);
   const int64_t R = (d->Hq / d->Hk) * d->Q;
   p->pub.rows = static_cast<int32_t>(R);
-  p->decode = find_decode(d, dtype, R);
+  p->decode = find_decode(d, dtype, R, &p->rg_waves);
   p->chunk = p->decode ? nullptr : find_chunk(d, dtype, R);
-  p->P = p->decode ? compute_units() * p->decode->wgs_per_cu * kvc::kDecodeWaves : 0;
+  p->P = p->decode
+             ? compute_units() * p->decode->wgs_per_cu * (kvc::kDecodeWaves / p->rg_waves)
+             : 0;
   const int64_t row_tiles = R == 0 ? 1 : (R + kvc::kGenericRowsPerTile - 1) / kvc::kGenericRowsPerTile;
   if (!make_layout(d, R, kvc::kGenericChunk, false, 0, &p->generic)) return KVC_ERR_SHAPE;
   int64_t wgs;
@@ -280,7 +309,8 @@ int make_plan(const kvc_dims* d, int dtype, Plan* p) {
     if (p->stream.bytes > bytes) bytes = p->stream.bytes;
     p->pub.path = 1;
     p->pub.rows_per_tile = p->decode->rows;
-    p->pub.row_tiles = 1;
+    p->pub.row_tiles = static_cast<int32_t>(R <= p->decode->rows ? 1 : (R + p->decode->rows - 1) /
+                                                                        p->decode->rows);
     p->pub.split = p->decode->chunk;
     p->pub.nsplit = p->stream.nchunk_max;
   } else if (p->chunk) {
@@ -490,6 +520,7 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
   a.rows_per_tile = p.pub.rows_per_tile;
   a.row_tiles = p.pub.row_tiles;
   a.P = p.P;
+  a.rg_waves = p.rg_waves > 0 ? p.rg_waves : 1;
   a.lead = p.decode ? p.decode->lead : 8;
   a.scale = sc;
   a.elem_bytes = static_cast<int64_t>(e);

@@ -128,6 +128,7 @@ struct StepArgs {
   // sinks[query head] (if given) as one more logit to each softmax
   int32_t read_only;
   const float* sinks;
+  int32_t rg_waves;   // stream decode: waves per worker (row groups rounded up to 1, 2 or 4)
 };
 
 // Block holding slot j of batch row b (paged cache).

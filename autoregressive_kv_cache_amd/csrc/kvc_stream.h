@@ -121,7 +121,7 @@ __device__ __forceinline__ void ws_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, f
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(off), 0, 0);
 }
 
-template <int D, int DV, int ROWS, bool Q1, bool OOP, bool FUSED, bool PAGED>
+template <int D, int DV, int ROWS, bool Q1, bool OOP, bool FUSED, bool PAGED, bool GROUPS>
 __global__ __launch_bounds__(kDecodeThreads)
 __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_stream_kernel(
     StepArgs a, const int64_t* __restrict__ rowinfo, const int32_t* __restrict__ wstart) {
@@ -163,6 +163,18 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
   const int R = static_cast<int>(a.R);
   const int Hk = static_cast<int>(a.Hk);
   const int64_t M = a.M;
+  // Row groups (more packed rows than a wave holds): a KV head's R packed
+  // rows are cut into groups of ROWS, one wave each; the waves of one
+  // stream worker (rg_waves of them, side by side in the workgroup, a power
+  // of two) walk the same chunk range.  Their K/V loads use the default
+  // cache policy, so that the unit's caches serve a chunk's rows to the
+  // later waves (non-temporal loads would send each group to memory: 1.8x
+  // the time at 8 rows in two groups of 4).  Waves past the last group have
+  // no rows.
+  // (GROUPS false: one group, rows [0, R), R <= ROWS)
+  const int RGW = GROUPS ? a.rg_waves : 1;
+  const int r0 = GROUPS ? (wave % RGW) * ROWS : 0;  // the group's first packed row
+  const int NR = GROUPS ? (R - r0 < ROWS ? R - r0 : ROWS) : R;  // rows of the group (<= 0: none)
 
   // ---- row information (as attend_decode_kernel) ----
   auto row_len = [&](int b) { return FUSED ? rt_len[b] : static_cast<int>(rowinfo[b * 4 + 0]); };
@@ -210,8 +222,8 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
     Nc = a.ws_hdr[0];
     Pw = a.ws_hdr[1];
   }
-  const int64_t w = blockIdx.x * static_cast<int64_t>(kDecodeWaves) + wave;
-  if (w >= Pw) return;
+  const int64_t w = blockIdx.x * static_cast<int64_t>(kDecodeWaves / RGW) + wave / RGW;
+  if (w >= Pw || (GROUPS && NR <= 0)) return;
   const int32_t lead = effective_lead(Nc, Pw, a.lead);
   const int64_t x_begin = worker_start(w, Nc, Pw, lead), x_end = worker_start(w + 1, Nc, Pw, lead);
   if (x_begin >= x_end) return;
@@ -305,12 +317,19 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
     }
     return r;
   };
+  // V load u of a chunk (as load_one, kvc_decode.h; cache policy as for K)
+  auto load_v = [&](const RowSrc& s, int u, uint32_t lane_off) {
+    const uint32_t base = static_cast<uint32_t>(u / 4) * 4096u;
+    const uint32_t imm = static_cast<uint32_t>(u % 4) * 1024u;
+    const uint32_t left = s.bytes > base ? s.bytes - base : 0u;
+    return buf_ld16<GROUPS ? 0 : kNonTemporal>(make_rsrc(s.rows + base, left), lane_off + imm);
+  };
   // K load (k, h): slot 8k + (lane & 7), bytes [h*128 + (lane>>3)*16, +16);
   // the descriptor starts at the 8-slot group so the lane offset stays small
   auto load_k = [&](const RowSrc& s, int k, int h) {
     const uint32_t base = static_cast<uint32_t>(k) * 8u * KROW;
     const uint32_t left = s.bytes > base ? s.bytes - base : 0u;
-    return buf_ld16<kNonTemporal>(make_rsrc(s.rows + base, left), k_off + h * 128u);
+    return buf_ld16<GROUPS ? 0 : kNonTemporal>(make_rsrc(s.rows + base, left), k_off + h * 128u);
   };
   auto store_k = [&](uint8_t* out, uint32_t bytes, int k, int h, const uint4& v) {
     const uint32_t base = static_cast<uint32_t>(k) * 8u * KROW;
@@ -322,9 +341,9 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
   auto load_q = [&](uint4 (&qv)[ROWS][NH], const ChunkPos& p) {
 #pragma unroll
     for (int r = 0; r < ROWS; r++) {
-      const int t = Q1 ? 0 : r % Q;
-      const int g = Q1 ? r : r / Q;
-      const bool valid = r < R && t < p.n;
+      const int t = Q1 ? 0 : (r0 + r) % Q;
+      const int g = Q1 ? r0 + r : (r0 + r) / Q;
+      const bool valid = r < NR && t < p.n;
       const int64_t row = valid ? (static_cast<int64_t>(p.b) * a.Hq + p.kvh * a.G + g) * Q + t : 0;
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(qbase + row * KROW, valid ? KROW : 0u);
 #pragma unroll
@@ -343,18 +362,35 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
       return;
     }
     wave_lds_sync();
-    // exp values: ns chunks of R rows of C bf16, contiguous in the workspace
-    const int pieces = ns * R * (C / 8);
-    const __amdgpu_buffer_rsrc_t dx =
-        make_rsrc(a.ws_pexp + xs0 * R * C, static_cast<uint32_t>(pieces) * 16u);
-    for (int p = lane; p < pieces; p += kWave) {
-      const int i = p / (R * (C / 8)), rr = (p / (C / 8)) % R, s8 = p % (C / 8);
-      ws_st16(dx, static_cast<uint32_t>(p) * 16u,
-              *reinterpret_cast<const uint4*>(&xs[i][rr * C + s8 * 8]));
+    // exp values: ns chunks of R rows of C bf16 in the workspace; with row
+    // groups, this group's NR rows of each (one contiguous run per chunk)
+    if constexpr (GROUPS) {
+      const int pieces = ns * NR * (C / 8);
+      const __amdgpu_buffer_rsrc_t dx =
+          make_rsrc(a.ws_pexp + xs0 * R * C, static_cast<uint32_t>(ns * R * C) * 2u);
+      for (int p = lane; p < pieces; p += kWave) {
+        const int i = p / (NR * (C / 8)), rr = (p / (C / 8)) % NR, s8 = p % (C / 8);
+        ws_st16(dx, static_cast<uint32_t>(((i * R + r0 + rr) * (C / 8) + s8) * 16),
+                *reinterpret_cast<const uint4*>(&xs[i][rr * C + s8 * 8]));
+      }
+      const __amdgpu_buffer_rsrc_t dr =
+          make_rsrc(a.ws_cref + xs0 * R, static_cast<uint32_t>(ns * R) * 4u);
+      for (int p = lane; p < ns * NR; p += kWave)
+        ws_st4(dr, static_cast<uint32_t>((p / NR) * R + r0 + p % NR) * 4u, xr[p / NR][p % NR]);
+    } else {
+      const int pieces = ns * R * (C / 8);
+      const __amdgpu_buffer_rsrc_t dx =
+          make_rsrc(a.ws_pexp + xs0 * R * C, static_cast<uint32_t>(pieces) * 16u);
+      for (int p = lane; p < pieces; p += kWave) {
+        const int i = p / (R * (C / 8)), rr = (p / (C / 8)) % R, s8 = p % (C / 8);
+        ws_st16(dx, static_cast<uint32_t>(p) * 16u,
+                *reinterpret_cast<const uint4*>(&xs[i][rr * C + s8 * 8]));
+      }
+      const __amdgpu_buffer_rsrc_t dr =
+          make_rsrc(a.ws_cref + xs0 * R, static_cast<uint32_t>(ns * R) * 4u);
+      for (int p = lane; p < ns * R; p += kWave)
+        ws_st4(dr, static_cast<uint32_t>(p) * 4u, xr[p / R][p % R]);
     }
-    const __amdgpu_buffer_rsrc_t dr =
-        make_rsrc(a.ws_cref + xs0 * R, static_cast<uint32_t>(ns * R) * 4u);
-    for (int p = lane; p < ns * R; p += kWave) ws_st4(dr, static_cast<uint32_t>(p) * 4u, xr[p / R][p % R]);
     xs0 += ns;
     ns = 0;
   };
@@ -379,7 +415,7 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
 #pragma unroll
       for (int h = 0; h < NH; h++) kb[k * NH + h] = load_k(sk, k, h);
 #pragma unroll
-    for (int u = 0; u < UV; u++) vb[u] = load_one(sv, u, v_off);
+    for (int u = 0; u < UV; u++) vb[u] = load_v(sv, u, v_off);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -480,8 +516,8 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
     bool big = false;
 #pragma unroll
     for (int r = 0; r < ROWS; r++) {
-      const int t = Q1 ? 0 : r % Q;
-      const bool vis = r < R && t < pos.n && jl < n_all && j0 + jl <= pos.len + t;
+      const int t = Q1 ? 0 : (r0 + r) % Q;
+      const bool vis = r < NR && t < pos.n && jl < n_all && j0 + jl <= pos.len + t;
       sc[r] = vis ? sc[r] * scale_l2 : -INFINITY;
       big = big || sc[r] > mref[r] + kLazyMargin;
     }
@@ -533,8 +569,8 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
         lo[e] = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
         hi[e] = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
       }
-      vb[2 * m] = load_one(nv, 2 * m, v_off);
-      vb[2 * m + 1] = load_one(nv, 2 * m + 1, v_off);
+      vb[2 * m] = load_v(nv, 2 * m, v_off);
+      vb[2 * m + 1] = load_v(nv, 2 * m + 1, v_off);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int e = 0; e < 4; e++) {
@@ -571,9 +607,10 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
         __builtin_amdgcn_sched_barrier(0);
       }
       const int64_t seg = w + grp;
-      // rows >= R fall outside the descriptors and are not stored
+      // this group's rows r0 .. r0 + NR - 1; rows >= NR fall outside the
+      // descriptors and are not stored
       const __amdgpu_buffer_rsrc_t so_rs =
-          make_rsrc(a.ws_seg_o + seg * R * DV, static_cast<uint32_t>(R * DV) * 4u);
+          make_rsrc(a.ws_seg_o + (seg * R + r0) * DV, static_cast<uint32_t>(NR * DV) * 4u);
       if (rs == 0) {
 #pragma unroll
         for (int r = 0; r < ROWS; r++) {
@@ -587,7 +624,7 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
       }
       {
         const __amdgpu_buffer_rsrc_t sm_rs =
-            make_rsrc(a.ws_seg2 + seg * R * 2, static_cast<uint32_t>(R * 2) * 4u);
+            make_rsrc(a.ws_seg2 + (seg * R + r0) * 2, static_cast<uint32_t>(NR * 2) * 4u);
         float mv = mref[0], lv = l_seg[0];
 #pragma unroll
         for (int r = 1; r < ROWS; r++) {

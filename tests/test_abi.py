@@ -60,24 +60,35 @@ def test_workspace_and_plan(lib):
 
 
 def test_plan_dispatch_rule(lib):
-    """Host-only path choice: <= 8 packed rows with a tabled head size -> the
-    vector decode kernel (1); > 8 packed rows with D = Dv in {64, 128, 256}
-    (bf16) or {64, 128} (fp32) -> the matrix-core chunk kernel (2); the rest
-    -> the generic kernel (0).  The workspace covers every path of the shape."""
+    """Host-only path choice.  The matrix-core chunk kernel (2) only where a
+    KV head's packed rows R = (Hq/Hk) Q fill a 16-row tile (R >= 16, D = Dv
+    in {64, 128, 256} bf16 or {64, 128} fp32).  Below that the vector decode
+    kernels (1): 4 rows a wave up to R = 4, 8 up to 8, and for bf16 with
+    D = Dv in {64, 128} two waves of up to 8 rows each up to R = 15
+    (rows_per_tile 8, row_tiles 2).  The rest -> the generic kernel (0).
+    The workspace covers every path of the shape."""
     cases = [
-        (dims(B=32, Hq=32, Hk=8, Q=1, M=8192, D=128, Dv=128), kvc.KVC_BF16, 1),
-        (dims(B=4, Hq=64, Hk=8, Q=1, M=131072, D=128, Dv=128), kvc.KVC_BF16, 1),
-        (dims(B=8, Hq=16, Hk=16, Q=4, M=1024, D=64, Dv=32), kvc.KVC_F32, 1),
-        (dims(B=2, Hq=8, Hk=2, Q=40, M=4096, D=64, Dv=64), kvc.KVC_BF16, 2),
-        (dims(B=2, Hq=8, Hk=2, Q=40, M=4096, D=64, Dv=64), kvc.KVC_F32, 2),
-        (dims(B=2, Hq=8, Hk=2, Q=40, M=4096, D=256, Dv=256), kvc.KVC_F32, 0),
-        (dims(B=2, Hq=4, Hk=1, Q=3, M=100, D=128, Dv=128), kvc.KVC_BF16, 2),   # R = 12
-        (dims(B=2, Hq=4, Hk=1, Q=3, M=100, D=96, Dv=96), kvc.KVC_BF16, 0),     # no table entry
-        (dims(B=2, Hq=4, Hk=2, Q=3, M=16, D=8, Dv=8), kvc.KVC_F32, 0),
+        (dims(B=32, Hq=32, Hk=8, Q=1, M=8192, D=128, Dv=128), kvc.KVC_BF16, 1, 4, 1),
+        (dims(B=4, Hq=64, Hk=8, Q=1, M=131072, D=128, Dv=128), kvc.KVC_BF16, 1, 8, 1),
+        (dims(B=8, Hq=16, Hk=16, Q=4, M=1024, D=64, Dv=32), kvc.KVC_F32, 1, 4, 1),
+        (dims(B=2, Hq=8, Hk=2, Q=40, M=4096, D=64, Dv=64), kvc.KVC_BF16, 2, None, None),
+        (dims(B=2, Hq=8, Hk=2, Q=40, M=4096, D=64, Dv=64), kvc.KVC_F32, 2, None, None),
+        (dims(B=2, Hq=8, Hk=2, Q=40, M=4096, D=256, Dv=256), kvc.KVC_F32, 0, None, None),
+        (dims(B=2, Hq=4, Hk=1, Q=3, M=100, D=128, Dv=128), kvc.KVC_BF16, 1, 8, 2),   # R = 12
+        (dims(B=2, Hq=12, Hk=1, Q=1, M=100, D=64, Dv=64), kvc.KVC_BF16, 1, 8, 2),    # R = 12
+        (dims(B=2, Hq=5, Hk=1, Q=3, M=100, D=128, Dv=128), kvc.KVC_BF16, 1, 8, 2),   # R = 15
+        (dims(B=2, Hq=9, Hk=1, Q=1, M=100, D=64, Dv=64), kvc.KVC_BF16, 1, 8, 2),     # R = 9
+        (dims(B=2, Hq=4, Hk=1, Q=4, M=100, D=128, Dv=128), kvc.KVC_BF16, 2, None, None),  # R = 16
+        (dims(B=2, Hq=4, Hk=1, Q=3, M=100, D=128, Dv=128), kvc.KVC_F32, 0, None, None),   # R = 12
+        (dims(B=2, Hq=4, Hk=1, Q=3, M=100, D=256, Dv=256), kvc.KVC_BF16, 0, None, None),  # R = 12
+        (dims(B=2, Hq=4, Hk=1, Q=3, M=100, D=96, Dv=96), kvc.KVC_BF16, 0, None, None),    # no entry
+        (dims(B=2, Hq=4, Hk=2, Q=3, M=16, D=8, Dv=8), kvc.KVC_F32, 0, None, None),
     ]
-    for d, dt, path in cases:
+    for d, dt, path, rows, tiles in cases:
         plan = kvc.kvc_plan_step(d, dt)
         assert plan["path"] == path, (d.Q, d.Hq, d.Hk, d.D, dt)
+        if path == 1:
+            assert (plan["rows_per_tile"], plan["row_tiles"]) == (rows, tiles), plan
         assert plan["nsplit"] * plan["split"] >= d.M
         assert plan["workspace_bytes"] == kvc.kvc_workspace_bytes(d, dt) > 0
 

@@ -70,6 +70,14 @@ def test_tiny_more_seeds(seed):
     # nothing, caches filled to capacity
     Workload(name="decode_q2_edges", B=8, Hq=4, Hk=2, Q=2, M=200, D=64, Dv=64, dtype="bf16",
              len_range=(0, 198), n_rule="uniform", force_len0_row=0, force_n0_row=1),
+    # 9 to 15 packed rows: the stream kernel's two 8-row groups (two waves
+    # per worker); ragged row counts, two tokens, rows that append nothing
+    Workload(name="decode_r12", B=5, Hq=12, Hk=1, Q=1, M=777, D=128, Dv=128, dtype="bf16",
+             len_range=(0, 776), n_rule="all"),
+    Workload(name="decode_r9_d64", B=6, Hq=18, Hk=2, Q=1, M=640, D=64, Dv=64, dtype="bf16",
+             len_range=(1, 639), n_rule="all"),
+    Workload(name="decode_r15_q3", B=4, Hq=10, Hk=2, Q=3, M=300, D=128, Dv=128, dtype="bf16",
+             len_range=(0, 297), n_rule="uniform", force_len0_row=0, force_n0_row=1),
     # more batch rows than the attend kernel prepares by itself (the
     # preparation kernel runs first)
     Workload(name="decode_b1030", B=1030, Hq=2, Hk=1, Q=1, M=96, D=64, Dv=64, dtype="bf16",
@@ -256,7 +264,7 @@ def chunk_wl(**kw) -> Workload:
 CHUNK_CASES = [
     chunk_wl(name="rows20_ragged"),                                   # R = 20, not a multiple of 16
     chunk_wl(name="rows16_d128", Hq=2, Q=8, D=128, Dv=128, M=300, len_range=(0, 290)),
-    chunk_wl(name="rows12_d256", Hq=1, Q=12, D=256, Dv=256, M=130, len_range=(0, 118)),
+    chunk_wl(name="rows16_d256", Hq=1, Q=16, D=256, Dv=256, M=130, len_range=(0, 114)),
     chunk_wl(name="fill_to_capacity", Hq=1, Q=16, M=128, len_range=(112, 112), n_rule="all"),
     chunk_wl(name="prefill_len0", Hq=8, Hk=2, Q=40, M=96, len_range=(0, 0), n_rule="all"),
     chunk_wl(name="many_heads", B=3, Hq=16, Hk=2, Q=3, M=257, len_range=(0, 250)),
