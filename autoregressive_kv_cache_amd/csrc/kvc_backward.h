@@ -48,7 +48,8 @@ constexpr int kBwdMaxRowGroups = 16;
 struct BwdArgs {
   int64_t B, Hq, Hk, Q, M, D, Dv;
   int32_t G, R;
-  int64_t nchunk;  // ceil(M / kBwdSlots)
+  int64_t nchunk;  // partials per head: ceil(M / part_slots)
+  int32_t part_slots;  // slots per partial (kBwdSlots here, kBwdVecSlots in kvc_backward_vec.h)
   int32_t row_groups;  // bwd_stats: workgroups per chunk, each over every row_groups-th row tile
   float scale;
   // tensors of the element type T the kernels are built for (float or bf16)
@@ -535,7 +536,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(BwdArgs a) {
   int64_t len, n;
   bwd_row_info(a, b, &len, &n);
   const int64_t kvh = hq / a.G, g = hq % a.G, r = g * a.Q + t, grp = b * a.Hk + kvh;
-  const int64_t nc = t < n ? (len + t) / kBwdSlots + 1 : 0;
+  const int64_t nc = t < n ? (len + t) / a.part_slots + 1 : 0;
   double m = -INFINITY, l = 0, pd = 0;
   for (int64_t c = lane; c < nc; c += kWave) {
     const double* p = a.ws_part + ((grp * a.nchunk + c) * a.R + r) * 4;
@@ -811,7 +812,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a) {
   int64_t len, n;
   bwd_row_info(a, b, &len, &n);
   const int64_t kvh = hq / a.G, g = hq % a.G, r = g * a.Q + t, grp = b * a.Hk + kvh;
-  const int64_t nc = t < n ? (len + t) / kBwdSlots + 1 : 0;  // chunks holding slots <= len + t
+  const int64_t nc = t < n ? (len + t) / a.part_slots + 1 : 0;  // partials over slots <= len + t
   const int64_t cs = static_cast<int64_t>(a.R) * D;          // one chunk's stride
   const double* p = a.ws_dq + (grp * a.nchunk * a.R + r) * D + d;
   double s0 = 0, s1 = 0, s2 = 0, s3 = 0;

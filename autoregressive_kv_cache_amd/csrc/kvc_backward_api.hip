@@ -8,6 +8,7 @@
 
 #include "../../include/kvc.h"
 #include "kvc_backward.h"
+#include "kvc_backward_vec.h"
 #include "kvc_host.h"
 
 namespace {
@@ -55,6 +56,23 @@ const BwdEntry kBwdTable[] = {
     KVC_BWD(kvc::bf16, KVC_BF16, 128, 128), KVC_BWD(kvc::bf16, KVC_BF16, 64, 32),
 };
 #undef KVC_BWD
+// The vector-unit kernels of kvc_backward_vec.h: bf16, D = Dv in {64, 128},
+// at most kBwdVecRows packed rows per KV head.
+template <int D>
+void launch_bwd_vec(const kvc::BwdArgs& a, hipStream_t s, bool stats) {
+  const unsigned blocks = static_cast<unsigned>(
+      (a.B * a.Hk * a.nchunk + kvc::kBwdThreads / kvc::kWave - 1) / (kvc::kBwdThreads / kvc::kWave));
+  if (stats)
+    hipLaunchKernelGGL((kvc::bwd_vstats_kernel<D>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((kvc::bwd_vgrad_kernel<D>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
+}
+bool bwd_vec_ok(const kvc_dims* d, int dtype) {
+  const int64_t R = (d->Hq / d->Hk) * d->Q;
+  return dtype == KVC_BF16 && d->D == d->Dv && (d->D == 64 || d->D == 128) &&
+         R <= kvc::kBwdVecRows;
+}
+
 const BwdEntry* find_bwd(const kvc_dims* d, int dtype) {
   for (const BwdEntry& e : kBwdTable)
     if (e.dtype == dtype && e.D == d->D && e.Dv == d->Dv) return &e;
@@ -132,7 +150,9 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
   a.B = d->B; a.Hq = d->Hq; a.Hk = d->Hk; a.Q = d->Q; a.M = d->M; a.D = d->D; a.Dv = d->Dv;
   a.G = static_cast<int32_t>(d->Hq / d->Hk);
   a.R = static_cast<int32_t>(a.G * d->Q);
-  a.nchunk = (d->M + kvc::kBwdSlots - 1) / kvc::kBwdSlots;
+  const bool vec = bwd_vec_ok(d, dtype);
+  a.part_slots = vec ? kvc::kBwdVecSlots : kvc::kBwdSlots;
+  a.nchunk = (d->M + a.part_slots - 1) / a.part_slots;
   {
     const int64_t tiles = (a.R + kvc::kBwdRowTile - 1) / kvc::kBwdRowTile;
     a.row_groups = static_cast<int32_t>(tiles < 1 ? 1 : tiles < kvc::kBwdMaxRowGroups ? tiles : kvc::kBwdMaxRowGroups);
@@ -171,6 +191,16 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t rows = d->B * d->Hq * d->Q;
   const unsigned row_blocks = static_cast<unsigned>((rows + 3) / 4);
+  if (vec) {  // statistics, rows, slot gradients with the dq partials, dq
+    const bool d128 = d->D == 128;
+    if (rows > 0) {
+      d128 ? launch_bwd_vec<128>(a, s, true) : launch_bwd_vec<64>(a, s, true);
+      hipLaunchKernelGGL(kvc::bwd_rows_kernel, dim3(row_blocks), dim3(kvc::kBwdThreads), 0, s, a);
+    }
+    d128 ? launch_bwd_vec<128>(a, s, false) : launch_bwd_vec<64>(a, s, false);
+    if (rows > 0) e->dq(a, s);
+    return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+  }
   if (rows > 0) {
     e->stats(a, s);
     hipLaunchKernelGGL(kvc::bwd_rows_kernel, dim3(row_blocks), dim3(kvc::kBwdThreads), 0, s, a);

@@ -1,0 +1,461 @@
+// kvc_backward_vec.h -- vector-unit backward of the step for decode-shaped
+// heads: bf16 tensors, D = Dv in {64, 128}, at most 4 packed rows per KV
+// head.  Same gradients as kvc_backward.h (see there for the formulas, from
+// "Autoregressive KV-cache append and causal attention", the workspace
+// note); what changes is the arithmetic's shape.  With 4 rows a head's
+// products are matrix-vector products: the 16-row fp64 matrix-core tiles of
+// kvc_backward.h would be three quarters padding, so here every product is
+// a per-slot dot product on the vector units, in fp32 (bf16 inputs widen
+// exactly; the row statistics are merged in fp64 by bwd_rows_kernel).
+//
+// Layout (as attend_stream_kernel, kvc_stream.h): for a 64-slot chunk, lane
+// l holds dims [h*64 + (l>>3)*8, +8) of slot 8k + (l&7) in piece (k, h), so
+// each 16-byte load covers whole 128-byte lines; the 8 partial dot products
+// of a slot are finished by a reduce-scatter over lane bits 5, 4 and 3,
+// after which lane l holds slot l's value for every packed row.
+//
+// Kernels (one wave per (batch row, KV head, run of kBwdVecSlots slots)):
+//   bwd_vstats: scores s = scale q.K'_j and dP_j = dA_j + dO.V'_j of the
+//     run's visible slots, and per packed row the run's max m, sum of
+//     e^(s-m) and sum of e^(s-m) dP (the partials bwd_rows_kernel merges);
+//   bwd_vgrad: s and dP again, P = e^(s-m)/l and dS = P (dP - sum P dP),
+//     then per slot dK'_j = scale sum_r dS_jr q_r and dV'_j = sum_r P_jr dO_r
+//     added to the returned cache's gradient and stored (kept slots to the
+//     cache gradient, appended ones to the new rows' gradient, the rest
+//     passed through), and the run's share of dq_r = scale sum_j dS_jr K'_j
+//     (summed over the runs by bwd_dq_kernel).
+// Every slot of the cache belongs to one run of bwd_vgrad, so the pass-
+// through of the returned cache's gradient needs no other kernel.
+#pragma once
+
+#include "kvc_backward.h"
+#include "kvc_stream.h"
+
+namespace kvc {
+
+constexpr int kBwdVecChunks = 8;                    // 64-slot chunks per wave
+constexpr int kBwdVecSlots = 64 * kBwdVecChunks;    // slots per run (one wave)
+constexpr int kBwdVecRows = 4;                      // packed rows a wave holds
+
+// Dot products of 8-slot groups k = 0..7 (pieces kb[k * NH + h]) with the
+// ROWS row slices qv[r][h], finished so that lane l returns slot l's values.
+template <int ROWS, int NH>
+__device__ __forceinline__ void lk8_dots(const uint4 (&kb)[8 * NH], const uint4 (&qv)[ROWS][NH],
+                                         float (&out)[ROWS]) {
+  using Mth = DecodeMath<bf16>;
+  const int lane = threadIdx.x % kWave;
+  auto partials = [&](int k, float (&p)[ROWS]) {
+#pragma unroll
+    for (int r = 0; r < ROWS; r++) {
+      float acc = Mth::dot(qv[r][0], kb[k * NH]);
+      if constexpr (NH == 2) {
+        acc = Mth::dot2(qv[r][1].x, kb[k * NH + 1].x, acc);
+        acc = Mth::dot2(qv[r][1].y, kb[k * NH + 1].y, acc);
+        acc = Mth::dot2(qv[r][1].z, kb[k * NH + 1].z, acc);
+        acc = Mth::dot2(qv[r][1].w, kb[k * NH + 1].w, acc);
+      }
+      p[r] = acc;
+    }
+  };
+  float s5[4][ROWS], s4[2][ROWS];
+  constexpr int kOrder[4] = {0, 2, 1, 3};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int kl = kOrder[i];
+    float pa[ROWS], pb[ROWS];
+    partials(kl, pa);
+    partials(kl + 4, pb);
+#pragma unroll
+    for (int r = 0; r < ROWS; r++) s5[kl][r] = sum_swap32(pa[r], pb[r]);
+    if (i == 1 || i == 3) {
+      const int k2 = i == 1 ? 0 : 1;
+#pragma unroll
+      for (int r = 0; r < ROWS; r++) s4[k2][r] = sum_swap16(s5[k2][r], s5[k2 + 2][r]);
+    }
+  }
+  const bool upper = (lane & 8) != 0;
+#pragma unroll
+  for (int r = 0; r < ROWS; r++) {
+    const float send = upper ? s4[0][r] : s4[1][r], keep = upper ? s4[1][r] : s4[0][r];
+    out[r] = keep + dpp<dpp_row_ror(8)>(send);
+  }
+}
+
+// What the two kernels share for one wave: its head, its run, the rows'
+// q and dO slices, the LK8 loads of K' / V' / the returned cache's gradient.
+template <int D>
+struct BwdVecWave {
+  static constexpr int NH = D / 64, ROWS = kBwdVecRows;
+  const BwdArgs& a;
+  int lane;
+  int64_t grp, b, kvh, j0, len, n;
+  int Q;
+
+  __device__ BwdVecWave(const BwdArgs& args, int64_t wave_id, int64_t nrun)
+      : a(args), lane(static_cast<int>(threadIdx.x % kWave)) {
+    grp = wave_id / nrun;
+    j0 = (wave_id % nrun) * kBwdVecSlots;
+    b = grp / a.Hk;
+    kvh = grp % a.Hk;
+    Q = static_cast<int>(a.Q);
+  }
+  // step query / context row of packed row r (r = g * Q + t)
+  __device__ int64_t row_of(int r) const {
+    return (b * a.Hq + kvh * a.G + r / Q) * a.Q + r % Q;
+  }
+  __device__ bool row_valid(int r) const { return r < a.R && r % Q < n; }
+  // slices [h*64 + (lane>>3)*8, +8) of rows r of src ([rows][D]), zeros
+  // for rows that are not valid or a null src
+  __device__ void load_rows(const void* src, uint4 (&v)[ROWS][NH]) const {
+#pragma unroll
+    for (int r = 0; r < ROWS; r++)
+#pragma unroll
+      for (int h = 0; h < NH; h++) {
+        const bool ok = src && row_valid(r);
+        v[r][h] = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) +
+                                                       row_of(r) * D + h * 64 + (lane >> 3) * 8)
+                     : make_uint4(0u, 0u, 0u, 0u);
+      }
+  }
+  // LK8 pieces of chunk slots [jb, jb + 64) of K' (cache, or the appended
+  // rows for slots in [len, len + n)); zeros past len + n
+  __device__ void load_kv(const void* cache, const void* fresh, int64_t jb,
+                          uint4 (&v)[8 * NH]) const {
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int64_t j = jb + 8 * k + (lane & 7);
+      const uint16_t* src = nullptr;
+      if (j < len)
+        src = static_cast<const uint16_t*>(cache) + (grp * a.M + j) * D;
+      else if (j < len + n)
+        src = static_cast<const uint16_t*>(fresh) + (grp * a.Q + (j - len)) * D;
+#pragma unroll
+      for (int h = 0; h < NH; h++)
+        v[k * NH + h] = src ? *reinterpret_cast<const uint4*>(src + h * 64 + (lane >> 3) * 8)
+                            : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  // lane l's slot of the chunk at jb and its visibility for packed row r
+  __device__ bool visible(int64_t jb, int r) const {
+    const int64_t j = jb + lane;
+    return row_valid(r) && j <= len + r % Q;
+  }
+};
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Scores (natural units, -inf where not visible) and dP of the chunk at jb
+// for lane l's slot.
+template <int D>
+__device__ __forceinline__ void bwd_vec_chunk(const BwdVecWave<D>& W, int64_t jb,
+                                              const uint4 (&qv)[kBwdVecRows][D / 64],
+                                              const uint4 (&dov)[kBwdVecRows][D / 64],
+                                              uint4 (&kb)[8 * (D / 64)],
+                                              float (&s)[kBwdVecRows], float (&dp)[kBwdVecRows]) {
+  constexpr int NH = D / 64, ROWS = kBwdVecRows;
+  const BwdArgs& a = W.a;
+  {
+    uint4 vb[8 * NH];
+    W.load_kv(a.vc, a.new_value, jb, vb);
+    lk8_dots<ROWS, NH>(vb, dov, dp);
+  }
+  // the V' pieces are dead before the K' ones load (both at once would not
+  // fit the registers of two waves per SIMD)
+  __builtin_amdgcn_sched_barrier(0);
+  W.load_kv(a.kc, a.new_key, jb, kb);
+  lk8_dots<ROWS, NH>(kb, qv, s);
+  const int64_t j = jb + W.lane;
+#pragma unroll
+  for (int r = 0; r < ROWS; r++) {
+    const bool vis = W.visible(jb, r);
+    float da = 0.0f;
+    if (vis && a.d_att) da = bf16_to_f32(static_cast<const uint16_t*>(a.d_att)[W.row_of(r) * a.M + j]);
+    s[r] = vis ? s[r] * a.scale : -INFINITY;
+    dp[r] = vis ? dp[r] + da : 0.0f;
+  }
+}
+
+// A run with no visible slot (all of its slots at or past len + n): the
+// gradients of its slots are the returned cache's, passed through (zeros
+// for a null one); a plain copy, eight 16-byte pieces in flight per lane.
+template <int D>
+__device__ void bwd_vec_pass_run(const BwdVecWave<D>& W) {
+  const BwdArgs& a = W.a;
+  const int64_t j1 = W.j0 + kBwdVecSlots < a.M ? W.j0 + kBwdVecSlots : a.M;
+  const int64_t pieces = (j1 - W.j0) * D / 8, base = (W.grp * a.M + W.j0) * D;
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const uint4* src = static_cast<const uint4*>(t == 0 ? a.d_kc_out : a.d_vc_out);
+    uint4* dst = static_cast<uint4*>(t == 0 ? a.g_kc : a.g_vc);
+    src = src ? src + base / 8 : nullptr;
+    dst += base / 8;
+    for (int64_t p0 = 0; p0 < pieces; p0 += 8 * kWave) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int64_t p = p0 + u * kWave + W.lane;
+        v[u] = (src && p < pieces) ? src[p] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int64_t p = p0 + u * kWave + W.lane;
+        if (p < pieces) dst[p] = v[u];
+      }
+    }
+  }
+}
+
+// The appended rows past n get zero gradients (done by each head's first run).
+template <int D>
+__device__ void bwd_vec_zero_new_rows(const BwdVecWave<D>& W) {
+  const BwdArgs& a = W.a;
+  for (int64_t i = W.n * D + W.lane * 8; i < a.Q * D; i += kWave * 8) {
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.g_new_key) + W.grp * a.Q * D + i) =
+        make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.g_new_value) + W.grp * a.Q * D + i) =
+        make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void
+bwd_vstats_kernel(BwdArgs a) {
+  constexpr int NH = D / 64, ROWS = kBwdVecRows;
+  const int64_t wave_id = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
+  if (wave_id >= a.B * a.Hk * a.nchunk) return;
+  BwdVecWave<D> W(a, wave_id, a.nchunk);
+  bwd_row_info(a, W.b, &W.len, &W.n);
+  if (W.n == 0 || W.j0 >= W.len + W.n) return;  // no visible slot: bwd_rows reads nothing here
+  uint4 qv[ROWS][NH], dov[ROWS][NH];
+  W.load_rows(a.query, qv);
+  W.load_rows(a.d_ctx, dov);
+  float m[ROWS], l[ROWS], pd[ROWS];  // this lane's running max, sum e^(s-m), sum e^(s-m) dP
+#pragma unroll
+  for (int r = 0; r < ROWS; r++) {
+    m[r] = -INFINITY;
+    l[r] = 0.0f;
+    pd[r] = 0.0f;
+  }
+#pragma unroll 1
+  for (int c = 0; c < kBwdVecChunks; c++) {
+    const int64_t jb = W.j0 + static_cast<int64_t>(c) * 64;
+    if (jb >= W.len + W.n) break;
+    uint4 kb[8 * NH];
+    float s[ROWS], dp[ROWS];
+    bwd_vec_chunk<D>(W, jb, qv, dov, kb, s, dp);
+#pragma unroll
+    for (int r = 0; r < ROWS; r++) {
+      if (s[r] == -INFINITY) continue;
+      const float mn = s[r] > m[r] ? s[r] : m[r];
+      const float fo = m[r] == -INFINITY ? 0.0f : expf(m[r] - mn), e = expf(s[r] - mn);
+      l[r] = l[r] * fo + e;
+      pd[r] = pd[r] * fo + e * dp[r];
+      m[r] = mn;
+    }
+  }
+  // merge the lanes in fp64 and store the run's partials
+#pragma unroll
+  for (int r = 0; r < ROWS; r++) {
+    if (r >= a.R) continue;
+    double md = m[r], ld = l[r], pdd = pd[r];
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      const double mo = __shfl_xor(md, o), lo = __shfl_xor(ld, o), po = __shfl_xor(pdd, o);
+      const double mn = mo > md ? mo : md;
+      if (mn != -INFINITY) {
+        const double fa = md == -INFINITY ? 0.0 : exp(md - mn);
+        const double fb = mo == -INFINITY ? 0.0 : exp(mo - mn);
+        ld = ld * fa + lo * fb;
+        pdd = pdd * fa + po * fb;
+      }
+      md = mn;
+    }
+    if (W.lane == 0) {
+      double* p = a.ws_part + ((W.grp * a.nchunk + wave_id % a.nchunk) * a.R + r) * 4;
+      p[0] = md;
+      p[1] = ld;
+      p[2] = pdd;
+      p[3] = 0.0;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void
+bwd_vgrad_kernel(BwdArgs a) {
+  constexpr int NH = D / 64, ROWS = kBwdVecRows, NQ = ROWS * NH * 8;
+  // each lane's share of dq (its dims of every row, summed over its slots)
+  // lives in LDS, lane-private: no registers held across the chunks
+  __shared__ float dq_all[kBwdThreads / kWave][NQ][kWave];
+  const int64_t wave_id = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
+  if (wave_id >= a.B * a.Hk * a.nchunk) return;
+  BwdVecWave<D> W(a, wave_id, a.nchunk);
+  bwd_row_info(a, W.b, &W.len, &W.n);
+  const int lane = W.lane;
+  float(*dql)[kWave] = dq_all[threadIdx.x / kWave];
+  const int64_t run = wave_id % a.nchunk;
+  if (run == 0) bwd_vec_zero_new_rows<D>(W);
+  if (W.n == 0 || W.j0 >= W.len + W.n) {  // no visible slot: a plain copy
+    bwd_vec_pass_run<D>(W);
+    return;
+  }
+  uint4 qv[ROWS][NH], dov[ROWS][NH];
+  W.load_rows(a.query, qv);
+  W.load_rows(a.d_ctx, dov);
+  float rm[ROWS], rinv[ROWS], rc[ROWS];  // row max, 1 / sum, sum P dP (bwd_rows_kernel)
+#pragma unroll
+  for (int r = 0; r < ROWS; r++) {
+    rm[r] = 0.0f;
+    rinv[r] = 0.0f;
+    rc[r] = 0.0f;
+    if (W.row_valid(r)) {
+      const double* st = a.ws_row + W.row_of(r) * 4;
+      rm[r] = static_cast<float>(st[0]);
+      rinv[r] = st[1] > 0.0 ? static_cast<float>(1.0 / st[1]) : 0.0f;
+      rc[r] = static_cast<float>(st[2]);
+    }
+    // one value per wave: kept in scalar registers
+    rm[r] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(rm[r])));
+    rinv[r] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(rinv[r])));
+    rc[r] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(rc[r])));
+  }
+#pragma unroll
+  for (int i = 0; i < NQ; i++) dql[i][lane] = 0.0f;
+
+#pragma unroll 1
+  for (int c = 0; c < kBwdVecChunks; c++) {
+    const int64_t jb = W.j0 + static_cast<int64_t>(c) * 64;
+    if (jb >= a.M) break;
+    float P[ROWS], dS[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; r++) P[r] = dS[r] = 0.0f;
+    if (jb < W.len + W.n) {
+      uint4 kb[8 * NH];
+      float s[ROWS], dp[ROWS];
+      bwd_vec_chunk<D>(W, jb, qv, dov, kb, s, dp);
+#pragma unroll
+      for (int r = 0; r < ROWS; r++) {
+        P[r] = s[r] == -INFINITY ? 0.0f : expf(s[r] - rm[r]) * rinv[r];
+        dS[r] = P[r] * (dp[r] - rc[r]);
+      }
+      // dq share: dS of slot 8k + (l & 7) times that slot's K' dims, one
+      // row at a time into the lane's LDS accumulators
+#pragma unroll
+      for (int r = 0; r < ROWS; r++) {
+        float acc[NH][8];
+#pragma unroll
+        for (int h = 0; h < NH; h++)
+#pragma unroll
+          for (int e = 0; e < 8; e++) acc[h][e] = dql[(r * NH + h) * 8 + e][lane];
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          const float ds = __shfl(dS[r], 8 * k + (lane & 7));
+#pragma unroll
+          for (int h = 0; h < NH; h++) {
+            const uint32_t w4[4] = {kb[k * NH + h].x, kb[k * NH + h].y, kb[k * NH + h].z,
+                                    kb[k * NH + h].w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              acc[h][2 * e] += ds * bf_lo(w4[e]);
+              acc[h][2 * e + 1] += ds * bf_hi(w4[e]);
+            }
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < NH; h++)
+#pragma unroll
+          for (int e = 0; e < 8; e++) dql[(r * NH + h) * 8 + e][lane] = acc[h][e];
+      }
+    }
+    // slot gradients, LK8 pieces: dK'_j = scale sum_r dS_jr q_r, dV'_j = sum_r P_jr dO_r,
+    // plus the returned cache's gradient; keys, then values (one tensor's
+    // pass-through loads in flight at a time)
+#pragma unroll
+    for (int t = 0; t < 2; t++) {  // t = 0: keys, t = 1: values
+      const void* pass = t == 0 ? a.d_kc_out : a.d_vc_out;
+      void* gcache = t == 0 ? a.g_kc : a.g_vc;
+      void* gnew = t == 0 ? a.g_new_key : a.g_new_value;
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const int64_t j = jb + 8 * k + (lane & 7);
+        float wk[ROWS];
+#pragma unroll
+        for (int r = 0; r < ROWS; r++)
+          wk[r] = t == 0 ? __shfl(dS[r], 8 * k + (lane & 7)) * a.scale
+                         : __shfl(P[r], 8 * k + (lane & 7));
+        if (j >= a.M) continue;
+#pragma unroll
+        for (int h = 0; h < NH; h++) {
+          const int64_t col = h * 64 + (lane >> 3) * 8;
+          float v[8];
+          if (pass) {
+            const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(pass) +
+                                                            (W.grp * a.M + j) * D + col);
+            const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              v[2 * e] = bf_lo(xw[e]);
+              v[2 * e + 1] = bf_hi(xw[e]);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++) v[e] = 0.0f;
+          }
+#pragma unroll
+          for (int r = 0; r < ROWS; r++) {
+            const uint4 src = t == 0 ? qv[r][h] : dov[r][h];
+            const uint32_t sw[4] = {src.x, src.y, src.z, src.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              v[2 * e] += wk[r] * bf_lo(sw[e]);
+              v[2 * e + 1] += wk[r] * bf_hi(sw[e]);
+            }
+          }
+          uint32_t y[4];
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            y[e] = static_cast<uint32_t>(f32_to_bf16(v[2 * e])) |
+                   (static_cast<uint32_t>(f32_to_bf16(v[2 * e + 1])) << 16);
+          const uint4 out{y[0], y[1], y[2], y[3]};
+          uint4* at = reinterpret_cast<uint4*>(static_cast<uint16_t*>(gcache) +
+                                               (W.grp * a.M + j) * D + col);
+          if (j >= W.len && j < W.len + W.n) {  // appended: its gradient goes to the new row
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(gnew) +
+                                      (W.grp * a.Q + (j - W.len)) * D + col) = out;
+            *at = make_uint4(0u, 0u, 0u, 0u);
+          } else {
+            *at = out;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // dq share: the 8 lanes that hold the same dims sum their slots; rows of
+  // this run that bwd_dq_kernel reads (run <= (len + t) / kBwdVecSlots) get
+  // a partial, zero where the run saw no visible slot of the row
+#pragma unroll
+  for (int r = 0; r < ROWS; r++) {
+    if (r >= a.R) continue;
+    float dq[NH][8];
+#pragma unroll
+    for (int h = 0; h < NH; h++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        float x = dql[(r * NH + h) * 8 + e][lane];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        dq[h][e] = x;
+      }
+    if ((lane & 7) == 0) {
+      double* p = a.ws_dq + ((W.grp * a.nchunk + run) * a.R + r) * D + (lane >> 3) * 8;
+#pragma unroll
+      for (int h = 0; h < NH; h++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) p[h * 64 + e] = static_cast<double>(dq[h][e]) * a.scale;
+    }
+  }
+}
+
+}  // namespace kvc

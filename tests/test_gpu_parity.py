@@ -749,6 +749,15 @@ BWD_CASES = [
     # R = 320 packed rows: ten 32-row tiles per chunk, and statistics row
     # groups that take a second tile
     chunk_wl(name="bwd_rows320", dtype="f32", B=2, Hq=16, Hk=2, Q=40, M=160, len_range=(0, 100)),
+    # at most 4 packed rows, D = Dv in {64, 128}: the vector-unit kernels
+    # for bf16 (runs of 512 slots; capacities that end inside a run and a
+    # 64-slot chunk), the fp64 matrix-core ones for fp32
+    Workload(name="bwd_vec_q2", B=3, Hq=4, Hk=2, Q=2, M=1100, D=64, Dv=64, dtype="f32",
+             len_range=(0, 1090), n_rule="uniform"),
+    Workload(name="bwd_vec_r1", B=2, Hq=4, Hk=4, Q=1, M=700, D=128, Dv=128, dtype="f32",
+             len_range=(0, 699), n_rule="all"),
+    Workload(name="bwd_vec_r3", B=2, Hq=3, Hk=1, Q=1, M=1536, D=64, Dv=64, dtype="f32",
+             len_range=(500, 1535), n_rule="all"),
     # the two backward workloads of bench.py at their full sizes
     WORKLOADS["chunk_gqa_f32"].with_(name="bwd_chunk_gqa_full"),
     WORKLOADS["mha_stress_f32"].with_(name="bwd_stress_full"),
