@@ -72,6 +72,7 @@ struct BwdArgs {
   double* ws_row;          // [B][Hq][Q][4]: m, l, sum_k P_k dP_k / l
   double* ws_part;         // [B*Hk][nchunk][R][4]: m_c, l_c, sum over the chunk of e^(s-m_c) dP
   double* ws_dq;           // [B*Hk][nchunk][R][D]
+  float* ws_sdp;           // vector path: [B*Hk][R][M][2] score and dP of each visible slot
 };
 
 // Row information of batch row b: its length and prefix count n (0 for a

@@ -58,14 +58,17 @@ const BwdEntry kBwdTable[] = {
 #undef KVC_BWD
 // The vector-unit kernels of kvc_backward_vec.h: bf16, D = Dv in {64, 128},
 // at most kBwdVecRows packed rows per KV head.
+// which: 0 statistics, 1 dq, 2 slot gradients
 template <int D>
-void launch_bwd_vec(const kvc::BwdArgs& a, hipStream_t s, bool stats) {
+void launch_bwd_vec(const kvc::BwdArgs& a, hipStream_t s, int which) {
   const unsigned blocks = static_cast<unsigned>(
       (a.B * a.Hk * a.nchunk + kvc::kBwdThreads / kvc::kWave - 1) / (kvc::kBwdThreads / kvc::kWave));
-  if (stats)
+  if (which == 0)
     hipLaunchKernelGGL((kvc::bwd_vstats_kernel<D>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
+  else if (which == 1)
+    hipLaunchKernelGGL((kvc::bwd_vdq_kernel<D>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((kvc::bwd_vgrad_kernel<D>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
+    hipLaunchKernelGGL((kvc::bwd_vslot_kernel<D>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
 }
 bool bwd_vec_ok(const kvc_dims* d, int dtype) {
   const int64_t R = (d->Hq / d->Hk) * d->Q;
@@ -79,12 +82,14 @@ const BwdEntry* find_bwd(const kvc_dims* d, int dtype) {
   return nullptr;
 }
 
-size_t bwd_workspace(const kvc_dims* d) {
-  const size_t B = d->B, Hq = d->Hq, Hk = d->Hk, Q = d->Q, D = d->D;
+bool bwd_vec_ok(const kvc_dims* d, int dtype);
+size_t bwd_workspace(const kvc_dims* d, int dtype) {
+  const size_t B = d->B, Hq = d->Hq, Hk = d->Hk, Q = d->Q, D = d->D, M = d->M;
   const size_t R = (d->Hq / d->Hk) * d->Q;
   const size_t nchunk = (d->M + kvc::kBwdSlots - 1) / kvc::kBwdSlots;
+  const size_t sdp = bwd_vec_ok(d, dtype) ? align_up(B * Hk * R * M * 2 * 4, 256) : 0;
   return align_up(B * Hq * Q * 4 * 8, 256) + align_up(B * Hk * nchunk * R * 4 * 8, 256) +
-         align_up(B * Hk * nchunk * R * D * 8, 256);
+         align_up(B * Hk * nchunk * R * D * 8, 256) + sdp;
 }
 
 }  // namespace
@@ -93,7 +98,7 @@ extern "C" {
 
 size_t kvc_backward_workspace_bytes(const kvc_dims* dims, int dtype) {
   if (!dims || check_dims(dims, dtype) != KVC_OK) return 0;
-  return bwd_workspace(dims);
+  return bwd_workspace(dims, dtype);
 }
 
 int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double scale,
@@ -126,7 +131,7 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
                       !al16(d_context) || !al16(g_new_key) || !al16(g_new_value))))
       return KVC_ERR_UNSUPPORTED;
   }
-  if (workspace_bytes < bwd_workspace(d)) return KVC_ERR_WORKSPACE;
+  if (workspace_bytes < bwd_workspace(d, dtype)) return KVC_ERR_WORKSPACE;
   const size_t B = d->B, Hq = d->Hq, Hk = d->Hk, Q = d->Q, M = d->M, D = d->D, Dv = d->Dv;
   const size_t e4 = dtype == KVC_BF16 ? 2 : 4;  // element bytes
   const Range ins[] = {{query, B * Hq * Q * D * e4}, {new_key, B * Hk * Q * D * e4},
@@ -137,7 +142,7 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
                        {d_value_cache_out, B * Hk * M * Dv * e4}};
   const Range outs[] = {{g_query, B * Hq * Q * D * e4}, {g_new_key, B * Hk * Q * D * e4},
                         {g_new_value, B * Hk * Q * Dv * e4}, {g_key_cache, B * Hk * M * D * e4},
-                        {g_value_cache, B * Hk * M * Dv * e4}, {workspace, bwd_workspace(d)}};
+                        {g_value_cache, B * Hk * M * Dv * e4}, {workspace, bwd_workspace(d, dtype)}};
   for (int i = 0; i < 6; i++) {
     for (const Range& in : ins)
       if (overlap(outs[i], in)) return KVC_ERR_ALIAS;
@@ -188,16 +193,25 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
   a.ws_part = reinterpret_cast<double*>(ws + align_up(B * Hq * Q * 4 * 8, 256));
   a.ws_dq = reinterpret_cast<double*>(ws + align_up(B * Hq * Q * 4 * 8, 256) +
                                       align_up(B * Hk * nchunk * R * 4 * 8, 256));
+  {  // after the partial arrays at their largest (64-slot chunks)
+    const size_t n64 = (d->M + kvc::kBwdSlots - 1) / kvc::kBwdSlots;
+    a.ws_sdp = reinterpret_cast<float*>(ws + align_up(B * Hq * Q * 4 * 8, 256) +
+                                        align_up(B * Hk * n64 * R * 4 * 8, 256) +
+                                        align_up(B * Hk * n64 * R * D * 8, 256));
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t rows = d->B * d->Hq * d->Q;
   const unsigned row_blocks = static_cast<unsigned>((rows + 3) / 4);
-  if (vec) {  // statistics, rows, slot gradients with the dq partials, dq
-    const bool d128 = d->D == 128;
+  if (vec) {  // statistics, rows, dq partials, slot gradients, dq
+    auto run = [&](int which) {
+      d->D == 128 ? launch_bwd_vec<128>(a, s, which) : launch_bwd_vec<64>(a, s, which);
+    };
     if (rows > 0) {
-      d128 ? launch_bwd_vec<128>(a, s, true) : launch_bwd_vec<64>(a, s, true);
+      run(0);
       hipLaunchKernelGGL(kvc::bwd_rows_kernel, dim3(row_blocks), dim3(kvc::kBwdThreads), 0, s, a);
+      run(1);
     }
-    d128 ? launch_bwd_vec<128>(a, s, false) : launch_bwd_vec<64>(a, s, false);
+    run(2);
     if (rows > 0) e->dq(a, s);
     return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
   }

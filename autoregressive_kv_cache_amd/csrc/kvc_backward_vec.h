@@ -18,13 +18,16 @@
 //   bwd_vstats: scores s = scale q.K'_j and dP_j = dA_j + dO.V'_j of the
 //     run's visible slots, and per packed row the run's max m, sum of
 //     e^(s-m) and sum of e^(s-m) dP (the partials bwd_rows_kernel merges);
-//   bwd_vgrad: s and dP again, P = e^(s-m)/l and dS = P (dP - sum P dP),
-//     then per slot dK'_j = scale sum_r dS_jr q_r and dV'_j = sum_r P_jr dO_r
-//     added to the returned cache's gradient and stored (kept slots to the
-//     cache gradient, appended ones to the new rows' gradient, the rest
-//     passed through), and the run's share of dq_r = scale sum_j dS_jr K'_j
-//     (summed over the runs by bwd_dq_kernel).
-// Every slot of the cache belongs to one run of bwd_vgrad, so the pass-
+//     it also stores (s, dP) of every visible slot (fp32, 32 bytes a slot
+//     at 4 rows, against 512 bytes of K' and V'), so no later kernel reads V';
+//   bwd_vdq: P = e^(s-m)/l and dS = P (dP - sum P dP) from those, and the
+//     run's share of dq_r = scale sum_j dS_jr K'_j (summed over the runs by
+//     bwd_dq_kernel) -- the one later read of K';
+//   bwd_vslot: per slot dK'_j = scale sum_r dS_jr q_r and dV'_j = sum_r
+//     P_jr dO_r added to the returned cache's gradient and stored (kept
+//     slots to the cache gradient, appended ones to the new rows' gradient,
+//     the rest passed through) -- a streaming pass over that gradient.
+// Every slot of the cache belongs to one run of bwd_vslot, so the pass-
 // through of the returned cache's gradient needs no other kernel.
 #pragma once
 
@@ -244,6 +247,14 @@ bwd_vstats_kernel(BwdArgs a) {
     uint4 kb[8 * NH];
     float s[ROWS], dp[ROWS];
     bwd_vec_chunk<D>(W, jb, qv, dov, kb, s, dp);
+    {  // for the other kernels: (s, dP) of the slot, -inf where not visible
+      const int64_t j = jb + W.lane;
+#pragma unroll
+      for (int r = 0; r < ROWS; r++)
+        if (r < a.R && j < W.len + W.n)
+          *reinterpret_cast<float2*>(a.ws_sdp + ((W.grp * a.R + r) * a.M + j) * 2) =
+              make_float2(s[r], dp[r]);
+    }
 #pragma unroll
     for (int r = 0; r < ROWS; r++) {
       if (s[r] == -INFINITY) continue;
@@ -280,31 +291,38 @@ bwd_vstats_kernel(BwdArgs a) {
   }
 }
 
+// P and dS of packed row r at lane l's slot of the chunk at jb, from the
+// scores and dP bwd_vstats_kernel stored and the merged row statistics.
 template <int D>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void
-bwd_vgrad_kernel(BwdArgs a) {
-  constexpr int NH = D / 64, ROWS = kBwdVecRows, NQ = ROWS * NH * 8;
-  // each lane's share of dq (its dims of every row, summed over its slots)
-  // lives in LDS, lane-private: no registers held across the chunks
-  __shared__ float dq_all[kBwdThreads / kWave][NQ][kWave];
-  const int64_t wave_id = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
-  if (wave_id >= a.B * a.Hk * a.nchunk) return;
-  BwdVecWave<D> W(a, wave_id, a.nchunk);
-  bwd_row_info(a, W.b, &W.len, &W.n);
-  const int lane = W.lane;
-  float(*dql)[kWave] = dq_all[threadIdx.x / kWave];
-  const int64_t run = wave_id % a.nchunk;
-  if (run == 0) bwd_vec_zero_new_rows<D>(W);
-  if (W.n == 0 || W.j0 >= W.len + W.n) {  // no visible slot: a plain copy
-    bwd_vec_pass_run<D>(W);
-    return;
-  }
-  uint4 qv[ROWS][NH], dov[ROWS][NH];
-  W.load_rows(a.query, qv);
-  W.load_rows(a.d_ctx, dov);
-  float rm[ROWS], rinv[ROWS], rc[ROWS];  // row max, 1 / sum, sum P dP (bwd_rows_kernel)
+__device__ __forceinline__ void bwd_vec_pds(const BwdVecWave<D>& W, int64_t jb,
+                                            const float (&rm)[kBwdVecRows],
+                                            const float (&rinv)[kBwdVecRows],
+                                            const float (&rc)[kBwdVecRows],
+                                            float (&P)[kBwdVecRows], float (&dS)[kBwdVecRows]) {
+  const BwdArgs& a = W.a;
+  const int64_t j = jb + W.lane;
+  float2 sd[kBwdVecRows];
 #pragma unroll
-  for (int r = 0; r < ROWS; r++) {
+  for (int r = 0; r < kBwdVecRows; r++)
+    sd[r] = (r < a.R && j < W.len + W.n)
+                ? *reinterpret_cast<const float2*>(a.ws_sdp + ((W.grp * a.R + r) * a.M + j) * 2)
+                : make_float2(-INFINITY, 0.0f);
+#pragma unroll
+  for (int r = 0; r < kBwdVecRows; r++) {
+    P[r] = sd[r].x == -INFINITY ? 0.0f : expf(sd[r].x - rm[r]) * rinv[r];
+    dS[r] = P[r] * (sd[r].y - rc[r]);
+  }
+}
+
+// The merged statistics of the wave's rows (bwd_rows_kernel): max, 1 / sum
+// and sum P dP, one value per wave each (scalar registers).
+template <int D>
+__device__ __forceinline__ void bwd_vec_row_stats(const BwdVecWave<D>& W, float (&rm)[kBwdVecRows],
+                                                  float (&rinv)[kBwdVecRows],
+                                                  float (&rc)[kBwdVecRows]) {
+  const BwdArgs& a = W.a;
+#pragma unroll
+  for (int r = 0; r < kBwdVecRows; r++) {
     rm[r] = 0.0f;
     rinv[r] = 0.0f;
     rc[r] = 0.0f;
@@ -314,97 +332,166 @@ bwd_vgrad_kernel(BwdArgs a) {
       rinv[r] = st[1] > 0.0 ? static_cast<float>(1.0 / st[1]) : 0.0f;
       rc[r] = static_cast<float>(st[2]);
     }
-    // one value per wave: kept in scalar registers
     rm[r] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(rm[r])));
     rinv[r] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(rinv[r])));
     rc[r] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(rc[r])));
   }
-#pragma unroll
-  for (int i = 0; i < NQ; i++) dql[i][lane] = 0.0f;
+}
 
+// dq: per visible run, dq_r = scale sum_j dS_jr K'_j over the run's slots
+// (K' in the LK8 layout: lane l sums its 8 slots of each chunk for its dims,
+// then the 8 lanes that hold the same dims add up).
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void
+bwd_vdq_kernel(BwdArgs a) {
+  constexpr int NH = D / 64, ROWS = kBwdVecRows;
+  const int64_t wave_id = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
+  if (wave_id >= a.B * a.Hk * a.nchunk) return;
+  BwdVecWave<D> W(a, wave_id, a.nchunk);
+  bwd_row_info(a, W.b, &W.len, &W.n);
+  if (W.n == 0 || W.j0 >= W.len + W.n) return;  // bwd_dq reads no partial of this run
+  const int lane = W.lane;
+  float rm[ROWS], rinv[ROWS], rc[ROWS];
+  bwd_vec_row_stats<D>(W, rm, rinv, rc);
+  float dq[ROWS][NH][8];
+#pragma unroll
+  for (int r = 0; r < ROWS; r++)
+#pragma unroll
+    for (int h = 0; h < NH; h++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) dq[r][h][e] = 0.0f;
+#pragma unroll 1
+  for (int c = 0; c < kBwdVecChunks; c++) {
+    const int64_t jb = W.j0 + static_cast<int64_t>(c) * 64;
+    if (jb >= W.len + W.n) break;
+    uint4 kb[8 * NH];
+    W.load_kv(a.kc, a.new_key, jb, kb);
+    float P[ROWS], dS[ROWS];
+    bwd_vec_pds<D>(W, jb, rm, rinv, rc, P, dS);
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+#pragma unroll
+      for (int r = 0; r < ROWS; r++) {
+        const float ds = __shfl(dS[r], 8 * k + (lane & 7));
+#pragma unroll
+        for (int h = 0; h < NH; h++) {
+          const uint32_t w4[4] = {kb[k * NH + h].x, kb[k * NH + h].y, kb[k * NH + h].z,
+                                  kb[k * NH + h].w};
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            dq[r][h][2 * e] += ds * bf_lo(w4[e]);
+            dq[r][h][2 * e + 1] += ds * bf_hi(w4[e]);
+          }
+        }
+      }
+    }
+  }
+  const int64_t run = wave_id % a.nchunk;
+#pragma unroll
+  for (int r = 0; r < ROWS; r++) {
+    if (r >= a.R) continue;
+#pragma unroll
+    for (int h = 0; h < NH; h++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        float x = dq[r][h][e];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        dq[r][h][e] = x;
+      }
+    if ((lane & 7) == 0) {
+      double* p = a.ws_dq + ((W.grp * a.nchunk + run) * a.R + r) * D + (lane >> 3) * 8;
+#pragma unroll
+      for (int h = 0; h < NH; h++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) p[h * 64 + e] = static_cast<double>(dq[r][h][e]) * a.scale;
+    }
+  }
+}
+
+// Slot gradients: per run, dK'_j = scale sum_r dS_jr q_r and dV'_j = sum_r
+// P_jr dO_r added to the returned cache's gradient and stored (kept slots
+// to the cache gradient, appended ones to the new rows' gradient); runs with
+// no visible slot are a plain copy.  No K' / V' read: P and dS come from the
+// stored scores and dP.  Layout: D / 8 lanes per slot, lane l holding dims
+// [(l % (D/8)) * 8, +8) of slot (l / (D/8)) + u * (64 / (D/8)) in step u,
+// so each lane keeps only its 8 dims of every row's q and dO.
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void
+bwd_vslot_kernel(BwdArgs a) {
+  constexpr int ROWS = kBwdVecRows;
+  constexpr int LPS = D / 8, SPI = kWave / LPS, NI = 64 / SPI;  // lanes per slot, slots per step
+  constexpr int kSlotBatch = 8;  // steps whose loads are issued together
+  const int64_t wave_id = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
+  if (wave_id >= a.B * a.Hk * a.nchunk) return;
+  BwdVecWave<D> W(a, wave_id, a.nchunk);
+  bwd_row_info(a, W.b, &W.len, &W.n);
+  const int lane = W.lane;
+  if (W.j0 == 0) bwd_vec_zero_new_rows<D>(W);
+  if (W.n == 0 || W.j0 >= W.len + W.n) {
+    bwd_vec_pass_run<D>(W);
+    return;
+  }
+  const int col = (lane % LPS) * 8, sl = lane / LPS;
+  uint4 qr[ROWS], dor[ROWS];  // this lane's 8 dims of each row's q and dO
+#pragma unroll
+  for (int r = 0; r < ROWS; r++) {
+    const bool ok = W.row_valid(r);
+    qr[r] = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.query) +
+                                                 W.row_of(r) * D + col)
+               : make_uint4(0u, 0u, 0u, 0u);
+    dor[r] = ok && a.d_ctx ? *reinterpret_cast<const uint4*>(
+                                 static_cast<const uint16_t*>(a.d_ctx) + W.row_of(r) * D + col)
+                           : make_uint4(0u, 0u, 0u, 0u);
+  }
+  float rm[ROWS], rinv[ROWS], rc[ROWS];
+  bwd_vec_row_stats<D>(W, rm, rinv, rc);
 #pragma unroll 1
   for (int c = 0; c < kBwdVecChunks; c++) {
     const int64_t jb = W.j0 + static_cast<int64_t>(c) * 64;
     if (jb >= a.M) break;
     float P[ROWS], dS[ROWS];
-#pragma unroll
-    for (int r = 0; r < ROWS; r++) P[r] = dS[r] = 0.0f;
-    if (jb < W.len + W.n) {
-      uint4 kb[8 * NH];
-      float s[ROWS], dp[ROWS];
-      bwd_vec_chunk<D>(W, jb, qv, dov, kb, s, dp);
-#pragma unroll
-      for (int r = 0; r < ROWS; r++) {
-        P[r] = s[r] == -INFINITY ? 0.0f : expf(s[r] - rm[r]) * rinv[r];
-        dS[r] = P[r] * (dp[r] - rc[r]);
-      }
-      // dq share: dS of slot 8k + (l & 7) times that slot's K' dims, one
-      // row at a time into the lane's LDS accumulators
-#pragma unroll
-      for (int r = 0; r < ROWS; r++) {
-        float acc[NH][8];
-#pragma unroll
-        for (int h = 0; h < NH; h++)
-#pragma unroll
-          for (int e = 0; e < 8; e++) acc[h][e] = dql[(r * NH + h) * 8 + e][lane];
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-          const float ds = __shfl(dS[r], 8 * k + (lane & 7));
-#pragma unroll
-          for (int h = 0; h < NH; h++) {
-            const uint32_t w4[4] = {kb[k * NH + h].x, kb[k * NH + h].y, kb[k * NH + h].z,
-                                    kb[k * NH + h].w};
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-              acc[h][2 * e] += ds * bf_lo(w4[e]);
-              acc[h][2 * e + 1] += ds * bf_hi(w4[e]);
-            }
-          }
-        }
-#pragma unroll
-        for (int h = 0; h < NH; h++)
-#pragma unroll
-          for (int e = 0; e < 8; e++) dql[(r * NH + h) * 8 + e][lane] = acc[h][e];
-      }
-    }
-    // slot gradients, LK8 pieces: dK'_j = scale sum_r dS_jr q_r, dV'_j = sum_r P_jr dO_r,
-    // plus the returned cache's gradient; keys, then values (one tensor's
-    // pass-through loads in flight at a time)
+    bwd_vec_pds<D>(W, jb, rm, rinv, rc, P, dS);
 #pragma unroll
     for (int t = 0; t < 2; t++) {  // t = 0: keys, t = 1: values
-      const void* pass = t == 0 ? a.d_kc_out : a.d_vc_out;
-      void* gcache = t == 0 ? a.g_kc : a.g_vc;
-      void* gnew = t == 0 ? a.g_new_key : a.g_new_value;
+      const uint16_t* pass = static_cast<const uint16_t*>(t == 0 ? a.d_kc_out : a.d_vc_out);
+      uint16_t* gcache = static_cast<uint16_t*>(t == 0 ? a.g_kc : a.g_vc);
+      uint16_t* gnew = static_cast<uint16_t*>(t == 0 ? a.g_new_key : a.g_new_value);
+      float wsrc[ROWS];
+      uint4 src[ROWS];
 #pragma unroll
-      for (int k = 0; k < 8; k++) {
-        const int64_t j = jb + 8 * k + (lane & 7);
-        float wk[ROWS];
+      for (int r = 0; r < ROWS; r++) {
+        wsrc[r] = t == 0 ? dS[r] * a.scale : P[r];
+        src[r] = t == 0 ? qr[r] : dor[r];
+      }
+#pragma unroll 1
+      for (int ub = 0; ub < NI; ub += kSlotBatch) {
+        uint4 x[kSlotBatch];  // pass-through pieces, all in flight together
 #pragma unroll
-        for (int r = 0; r < ROWS; r++)
-          wk[r] = t == 0 ? __shfl(dS[r], 8 * k + (lane & 7)) * a.scale
-                         : __shfl(P[r], 8 * k + (lane & 7));
-        if (j >= a.M) continue;
+        for (int u = 0; u < kSlotBatch; u++) {
+          const int64_t j = jb + (ub + u) * SPI + sl;
+          x[u] = (pass && j < a.M)
+                     ? *reinterpret_cast<const uint4*>(pass + (W.grp * a.M + j) * D + col)
+                     : make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
-        for (int h = 0; h < NH; h++) {
-          const int64_t col = h * 64 + (lane >> 3) * 8;
+        for (int u = 0; u < kSlotBatch; u++) {
+          const int64_t j = jb + (ub + u) * SPI + sl;
+          float wk[ROWS];
+#pragma unroll
+          for (int r = 0; r < ROWS; r++) wk[r] = __shfl(wsrc[r], (ub + u) * SPI + sl);
+          if (j >= a.M) continue;
+          const uint32_t xw[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
           float v[8];
-          if (pass) {
-            const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(pass) +
-                                                            (W.grp * a.M + j) * D + col);
-            const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-              v[2 * e] = bf_lo(xw[e]);
-              v[2 * e + 1] = bf_hi(xw[e]);
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; e++) v[e] = 0.0f;
+          for (int e = 0; e < 4; e++) {
+            v[2 * e] = bf_lo(xw[e]);
+            v[2 * e + 1] = bf_hi(xw[e]);
           }
 #pragma unroll
           for (int r = 0; r < ROWS; r++) {
-            const uint4 src = t == 0 ? qv[r][h] : dov[r][h];
-            const uint32_t sw[4] = {src.x, src.y, src.z, src.w};
+            const uint32_t sw[4] = {src[r].x, src[r].y, src[r].z, src[r].w};
 #pragma unroll
             for (int e = 0; e < 4; e++) {
               v[2 * e] += wk[r] * bf_lo(sw[e]);
@@ -417,43 +504,15 @@ bwd_vgrad_kernel(BwdArgs a) {
             y[e] = static_cast<uint32_t>(f32_to_bf16(v[2 * e])) |
                    (static_cast<uint32_t>(f32_to_bf16(v[2 * e + 1])) << 16);
           const uint4 out{y[0], y[1], y[2], y[3]};
-          uint4* at = reinterpret_cast<uint4*>(static_cast<uint16_t*>(gcache) +
-                                               (W.grp * a.M + j) * D + col);
+          uint4* at = reinterpret_cast<uint4*>(gcache + (W.grp * a.M + j) * D + col);
           if (j >= W.len && j < W.len + W.n) {  // appended: its gradient goes to the new row
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(gnew) +
-                                      (W.grp * a.Q + (j - W.len)) * D + col) = out;
+            *reinterpret_cast<uint4*>(gnew + (W.grp * a.Q + (j - W.len)) * D + col) = out;
             *at = make_uint4(0u, 0u, 0u, 0u);
           } else {
             *at = out;
           }
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  // dq share: the 8 lanes that hold the same dims sum their slots; rows of
-  // this run that bwd_dq_kernel reads (run <= (len + t) / kBwdVecSlots) get
-  // a partial, zero where the run saw no visible slot of the row
-#pragma unroll
-  for (int r = 0; r < ROWS; r++) {
-    if (r >= a.R) continue;
-    float dq[NH][8];
-#pragma unroll
-    for (int h = 0; h < NH; h++)
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        float x = dql[(r * NH + h) * 8 + e][lane];
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
-        x += __shfl_xor(x, 4);
-        dq[h][e] = x;
-      }
-    if ((lane & 7) == 0) {
-      double* p = a.ws_dq + ((W.grp * a.nchunk + run) * a.R + r) * D + (lane >> 3) * 8;
-#pragma unroll
-      for (int h = 0; h < NH; h++)
-#pragma unroll
-        for (int e = 0; e < 8; e++) p[h * 64 + e] = static_cast<double>(dq[h][e]) * a.scale;
     }
   }
 }

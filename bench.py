@@ -482,7 +482,7 @@ def main():
         "copy_ceiling_gbps": ceiling,
         "read_ceiling_gbps": read_ceiling,
         "roofline": {"bound": "hbm",
-                     "kernel": "backward (all four kernels)" if args.mode == "backward"
+                     "kernel": "backward (every kernel of the step)" if args.mode == "backward"
                      else DOMINANT_KERNEL, "achieved": k_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": k_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic, "bytes_per_launch": attend_bytes,
