@@ -50,8 +50,10 @@ struct BwdArgs {
   int32_t G, R;
   int64_t nchunk;  // partials per head: ceil(M / part_slots)
   int32_t part_slots;  // slots per partial (kBwdSlots here, kBwdVecSlots in kvc_backward_vec.h)
+  int32_t gen_slots;  // kvc_backward_generic.h: slots per piece of a chunk
   int32_t row_groups;  // bwd_stats: workgroups per chunk, each over every row_groups-th row tile
   float scale;
+  double scale_d;  // the same scale in fp64 (kvc_backward_generic.h)
   // tensors of the element type T the kernels are built for (float or bf16)
   const void* query;       // [B][Hq][Q][D]
   const void* new_key;     // [B][Hk][Q][D]

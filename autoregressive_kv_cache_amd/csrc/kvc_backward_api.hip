@@ -8,6 +8,7 @@
 
 #include "../../include/kvc.h"
 #include "kvc_backward.h"
+#include "kvc_backward_generic.h"
 #include "kvc_backward_vec.h"
 #include "kvc_host.h"
 
@@ -70,6 +71,20 @@ void launch_bwd_vec(const kvc::BwdArgs& a, hipStream_t s, int which) {
   else
     hipLaunchKernelGGL((kvc::bwd_vslot_kernel<D>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
 }
+// The generic kernels of kvc_backward_generic.h: any head sizes with
+// D + Dv <= kBwdGenAccDoubles, any element-aligned buffers.
+template <typename T>
+void launch_bwd_generic(const kvc::BwdArgs& a, hipStream_t s, int which) {
+  const dim3 grid(static_cast<unsigned>(a.B * a.Hk * a.nchunk)), block(kvc::kBwdThreads);
+  if (which == 0)
+    hipLaunchKernelGGL((kvc::bwd_gstats_kernel<T>), grid, block, 0, s, a);
+  else if (which == 1)
+    hipLaunchKernelGGL((kvc::bwd_gchunk_kernel<T>), grid, block,
+                       static_cast<size_t>(a.gen_slots) * (a.D + a.Dv) * sizeof(double), s, a);
+  else
+    hipLaunchKernelGGL((kvc::bwd_gdq_kernel<T>), dim3(static_cast<unsigned>(a.B * a.Hq * a.Q)),
+                       block, 0, s, a);
+}
 bool bwd_vec_ok(const kvc_dims* d, int dtype) {
   const int64_t R = (d->Hq / d->Hk) * d->Q;
   return dtype == KVC_BF16 && d->D == d->Dv && (d->D == 64 || d->D == 128) &&
@@ -114,7 +129,7 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
   int rc = check_dims(d, dtype);
   if (rc != KVC_OK) return rc;
   const BwdEntry* e = find_bwd(d, dtype);
-  if (!e) return KVC_ERR_UNSUPPORTED;
+  if (!e && kvc::bwd_gen_slots(d->D, d->Dv) == 0) return KVC_ERR_UNSUPPORTED;
   double sc;
   rc = check_scale(has_scale, scale, d->D, &sc);
   if (rc != KVC_OK) return rc;
@@ -123,13 +138,22 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
   if (d->Q > 0 && (!query || !new_key || !new_value || !append_mask || !g_query || !g_new_key ||
                    !g_new_value))
     return KVC_ERR_NULL;
-  {  // the K'/V', q and dO rows and the slot gradients move in 16-byte pieces
-    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-    if (!al16(key_cache) || !al16(value_cache) || !al16(d_key_cache_out) ||
-        !al16(d_value_cache_out) || !al16(g_key_cache) || !al16(g_value_cache) ||
-        (d->Q > 0 && (!al16(query) || !al16(new_key) || !al16(new_value) ||
-                      !al16(d_context) || !al16(g_new_key) || !al16(g_new_value))))
-      return KVC_ERR_UNSUPPORTED;
+  // The tiled kernels move the K'/V', q and dO rows and the slot gradients
+  // in 16-byte pieces; shapes without a tile, or buffers that are not
+  // 16-byte aligned, take the generic kernels, which need each buffer
+  // aligned to its element only.
+  bool generic = !e;
+  {
+    const void* bufs[] = {key_cache, value_cache, d_key_cache_out, d_value_cache_out, g_key_cache,
+                          g_value_cache, query, new_key, new_value, d_context, g_new_key,
+                          g_new_value, d_attention, g_query};
+    const uintptr_t el = dtype == KVC_BF16 ? 2u : 4u;
+    for (const void* p : bufs) {
+      const uintptr_t u = reinterpret_cast<uintptr_t>(p);
+      if (u % el) return KVC_ERR_UNSUPPORTED;
+      if (p != d_attention && p != g_query && (u & 15u)) generic = true;
+    }
+    if (generic && kvc::bwd_gen_slots(d->D, d->Dv) == 0) return KVC_ERR_UNSUPPORTED;
   }
   if (workspace_bytes < bwd_workspace(d, dtype)) return KVC_ERR_WORKSPACE;
   const size_t B = d->B, Hq = d->Hq, Hk = d->Hk, Q = d->Q, M = d->M, D = d->D, Dv = d->Dv;
@@ -155,7 +179,7 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
   a.B = d->B; a.Hq = d->Hq; a.Hk = d->Hk; a.Q = d->Q; a.M = d->M; a.D = d->D; a.Dv = d->Dv;
   a.G = static_cast<int32_t>(d->Hq / d->Hk);
   a.R = static_cast<int32_t>(a.G * d->Q);
-  const bool vec = bwd_vec_ok(d, dtype);
+  const bool vec = !generic && bwd_vec_ok(d, dtype);
   a.part_slots = vec ? kvc::kBwdVecSlots : kvc::kBwdSlots;
   a.nchunk = (d->M + a.part_slots - 1) / a.part_slots;
   {
@@ -171,6 +195,8 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
       return KVC_ERR_SHAPE;
   }
   a.scale = static_cast<float>(sc);
+  a.scale_d = sc;
+  a.gen_slots = generic ? kvc::bwd_gen_slots(d->D, d->Dv) : 0;
   a.query = query;
   a.new_key = new_key;
   a.new_value = new_value;
@@ -202,6 +228,19 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t rows = d->B * d->Hq * d->Q;
   const unsigned row_blocks = static_cast<unsigned>((rows + 3) / 4);
+  if (generic) {  // statistics, rows, chunks (dq partials, slot gradients), dq
+    auto run = [&](int which) {
+      dtype == KVC_BF16 ? launch_bwd_generic<kvc::bf16>(a, s, which)
+                        : launch_bwd_generic<float>(a, s, which);
+    };
+    if (rows > 0) {
+      run(0);
+      hipLaunchKernelGGL(kvc::bwd_rows_kernel, dim3(row_blocks), dim3(kvc::kBwdThreads), 0, s, a);
+    }
+    run(1);
+    if (rows > 0) run(2);
+    return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+  }
   if (vec) {  // statistics, rows, dq partials, slot gradients, dq
     auto run = [&](int which) {
       d->D == 128 ? launch_bwd_vec<128>(a, s, which) : launch_bwd_vec<64>(a, s, which);

@@ -246,14 +246,18 @@ int kvc_attend_over_cache(const kvc_dims *dims, int dtype, int has_scale,
                           const kvc_events *events);
 
 /* Backward of the step (fp32 or bf16: every tensor argument of the dtype,
- * gradients in and out included; head sizes (D, Dv) in {(64, 64),
- * (128, 128), (64, 32)}; query, key_cache, value_cache, new_key,
+ * gradients in and out included; any head sizes with D + Dv <= 6144; every
+ * buffer aligned to its element; else KVC_ERR_UNSUPPORTED): the gradients
+ * of the step's inputs given those of its outputs.  Head sizes (64, 64),
+ * (128, 128) and (64, 32) with query, key_cache, value_cache, new_key,
  * new_value, d_context, d_key_cache_out, d_value_cache_out and the five
- * gradient outputs 16-byte aligned; else KVC_ERR_UNSUPPORTED): the
- * gradients of the step's inputs given those of its outputs.  The math
- * runs in fp32 and fp64 either way; each gradient is rounded once to the
- * dtype.  The page grades gradients as well as values ("Autoregressive
- * KV-cache append and causal attention", the workspace note).
+ * gradient outputs 16-byte aligned take tiled kernels (and bf16 heads of
+ * at most 4 packed rows with D = Dv in {64, 128} vector-unit ones); every
+ * other call takes generic kernels with scalar loads, in fp64 throughout.
+ * The math runs in fp32 and fp64 either way; each gradient is rounded once
+ * to the dtype.  The page grades gradients as well as values
+ * ("Autoregressive KV-cache append and causal attention", the workspace
+ * note).
  *
  * Inputs: the step's own inputs (query, new_key, new_value, lengths,
  * append_mask as given to the step; key_cache / value_cache either the

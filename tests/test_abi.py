@@ -216,6 +216,38 @@ def test_host_checks_paged(lib):
     assert run(d, ptrs=bad)[0] == -6
 
 
+def test_host_checks_backward(lib):
+    """kvc_step_backward: head sizes beyond the generic kernels' limit
+    (D + Dv > 6144), buffers not aligned to their element, and a short
+    workspace are refused on the host; any other head size is taken (the
+    calls here then fail the workspace check, before a launch)."""
+    def run(d, dtype=kvc.KVC_F32, shift=None, ws=16):
+        e = 2 if dtype == kvc.KVC_BF16 else 4
+        B, Hq, Hk, Q, M, D, Dv = d.B, d.Hq, d.Hk, d.Q, d.M, d.D, d.Dv
+        sizes = [B * Hq * Q * D * e, B * Hk * Q * D * e, B * Hk * Q * Dv * e,
+                 B * Hk * M * D * e, B * Hk * M * Dv * e, B * 8, B * Q,
+                 B * Hq * Q * M * e, B * Hq * Q * Dv * e, B * Hk * M * D * e,
+                 B * Hk * M * Dv * e, B * Hq * Q * D * e, B * Hk * Q * D * e,
+                 B * Hk * Q * Dv * e, B * Hk * M * D * e, B * Hk * M * Dv * e, ws]
+        ptrs, off = [], FAKE
+        for sz in sizes:
+            ptrs.append(off)
+            off += (sz + 4095) // 4096 * 4096 + 4096
+        if shift is not None:
+            ptrs[shift] += 1
+        return lib.kvc_step_backward(ctypes.byref(d), dtype, 0, 0.0, *ptrs, ws, None)
+
+    assert run(dims(D=4096, Dv=2049)) == -8          # D + Dv above 6144
+    assert run(dims(D=4096, Dv=2048)) == -5          # at the limit: taken
+    for D, Dv in [(8, 8), (96, 80), (256, 256), (1, 3)]:
+        assert run(dims(D=D, Dv=Dv)) == -5, (D, Dv)  # no tile: the generic kernels
+        assert run(dims(D=D, Dv=Dv), dtype=kvc.KVC_BF16) == -5, (D, Dv)
+    for i in (0, 3, 7, 9, 14):  # query, key cache, d_attention, d_key_cache_out, g_key_cache
+        assert run(dims(D=64, Dv=64), shift=i) == -8, i
+    assert run(dims(D=64, Dv=64), dtype=kvc.KVC_BF16, shift=3) == -8
+    assert lib.kvc_backward_workspace_bytes(ctypes.byref(dims(D=96, Dv=80)), kvc.KVC_F32) > 16
+
+
 def test_host_checks_attend_over_cache(lib):
     """kvc_attend_over_cache: layout, scope, workspace and aliasing are checked
     on the host before anything is enqueued (every call here fails one)."""

@@ -758,6 +758,17 @@ BWD_CASES = [
              len_range=(0, 699), n_rule="all"),
     Workload(name="bwd_vec_r3", B=2, Hq=3, Hk=1, Q=1, M=1536, D=64, Dv=64, dtype="f32",
              len_range=(500, 1535), n_rule="all"),
+    # head sizes without a tiled kernel: the generic kernels (slot pieces of
+    # 64, 32, 8 and 4 slots; ragged row tiles; D != Dv; the tiny step)
+    WORKLOADS["tiny_mixed_f32"].with_(name="bwd_gen_tiny"),
+    Workload(name="bwd_gen_d96_80", B=2, Hq=6, Hk=2, Q=3, M=300, D=96, Dv=80, dtype="f32",
+             len_range=(0, 290), n_rule="uniform"),
+    Workload(name="bwd_gen_d256", B=2, Hq=8, Hk=2, Q=1, M=200, D=256, Dv=256, dtype="f32",
+             len_range=(0, 199), n_rule="all"),
+    Workload(name="bwd_gen_rows40", B=2, Hq=8, Hk=2, Q=10, M=150, D=48, Dv=40, dtype="f32",
+             len_range=(0, 130), n_rule="uniform"),
+    Workload(name="bwd_gen_d1024", B=2, Hq=2, Hk=1, Q=2, M=70, D=1024, Dv=512, dtype="f32",
+             len_range=(0, 60), n_rule="all"),
     # the two backward workloads of bench.py at their full sizes
     WORKLOADS["chunk_gqa_f32"].with_(name="bwd_chunk_gqa_full"),
     WORKLOADS["mha_stress_f32"].with_(name="bwd_stress_full"),
@@ -773,9 +784,14 @@ def test_backward_against_oracle(wl, upstream, dtype):
     for seed in (0, 1):
         say(f"[case] backward {wl.name} {dtype} {upstream} seed={seed}")
         inp = make_inputs(wl, seed, "cpu")
-        if seed == 1:  # a rejected row and a row that appends nothing
+        if seed == 1:
+            # a rejected row, a row that appends nothing (with three rows or
+            # more), and a last row that appends at least one
             inp["lengths"][0] = wl.M + 5
-            inp["append_mask"][1] = False
+            if wl.B > 2:
+                inp["append_mask"][-2] = False
+            if not inp["append_mask"][-1, 0] and inp["lengths"][-1] < wl.M:
+                inp["append_mask"][-1, 0] = True
         dinp = {k: v.to(DEV) for k, v in inp.items()}
         g = torch.Generator().manual_seed(100 + seed)
         B, Hq, Q, D = inp["query"].shape
@@ -808,35 +824,47 @@ def test_backward_against_oracle(wl, upstream, dtype):
 
 
 @pytest.mark.parametrize("which", ["query", "d_key_cache_out", "g_value_cache", "g_new_key"])
-def test_backward_refuses_misaligned_gradient_buffers(which):
-    """The slot gradients move in 16-byte pieces: a gradient buffer, in or
-    out, that is not 16-byte aligned is refused (KVC_ERR_UNSUPPORTED) before
-    anything runs, and the outputs stay as they were."""
-    wl = BWD_CASES[0]
-    say(f"[case] backward misaligned {which}")
-    dinp = {k: v.to(DEV) for k, v in make_inputs(wl, 0, "cpu").items()}
-    B, Hq, Q, D = dinp["query"].shape
-    Hk, M = dinp["key_cache"].shape[1], dinp["key_cache"].shape[2]
-    ups = {"d_attention": None, "d_context": None,
-           "d_key_cache_out": torch.zeros(B, Hk, M, D, dtype=dinp["query"].dtype, device=DEV),
+@pytest.mark.parametrize("wl", [BWD_CASES[0], BWD_CASES[4]], ids=lambda w: w.name)
+def test_backward_misaligned_buffers_take_generic_path(which, wl):
+    """A buffer, in or out, that is not 16-byte aligned (2 bytes past a
+    boundary) sends the call to the generic kernels: every gradient still
+    matches the oracle."""
+    wl = wl.with_(dtype="bf16")
+    say(f"[case] backward misaligned {wl.name} {which}")
+    inp = make_inputs(wl, 0, "cpu")
+    dinp = {k: v.to(DEV) for k, v in inp.items()}
+    B, Hq, Q, D = inp["query"].shape
+    Hk, M, Dv = inp["key_cache"].shape[1], inp["key_cache"].shape[2], inp["value_cache"].shape[3]
+    g = torch.Generator().manual_seed(7)
+    ups = {"d_attention": torch.randn(B, Hq, Q, M, generator=g).to(torch.bfloat16),
+           "d_context": torch.randn(B, Hq, Q, Dv, generator=g).to(torch.bfloat16),
+           "d_key_cache_out": torch.randn(B, Hk, M, D, generator=g).to(torch.bfloat16),
            "d_value_cache_out": None}
+    dups = {k: None if v is None else v.to(DEV) for k, v in ups.items()}
     outs = {k: torch.full_like(dinp[src], float("nan")) for k, src in
             (("g_query", "query"), ("g_new_key", "new_key"), ("g_new_value", "new_value"),
              ("g_key_cache", "key_cache"), ("g_value_cache", "value_cache"))}
     if which == "query":
         dinp["query"] = misaligned(dinp["query"])
-    elif which in ups:
-        ups[which] = misaligned(ups[which])
+    elif which in dups:
+        dups[which] = misaligned(dups[which])
     else:
         outs[which] = misaligned(outs[which])
     mask = dinp["append_mask"].contiguous().view(torch.uint8)
-    with pytest.raises(kvc.KvcError) as e:
-        kvc.kvc_step_backward(dinp["query"], dinp["new_key"], dinp["new_value"],
-                              dinp["key_cache"], dinp["value_cache"], dinp["lengths"], mask,
-                              *ups.values(), **outs, scale=wl.scale)
-    assert e.value.code == -8
+    kvc.kvc_step_backward(dinp["query"], dinp["new_key"], dinp["new_value"],
+                          dinp["key_cache"], dinp["value_cache"], dinp["lengths"], mask,
+                          *dups.values(), **outs, scale=wl.scale)
     torch.cuda.synchronize()
-    assert all(torch.isnan(v).all() for v in outs.values())
+    h = host_arrays(inp)
+    ref = oracle.step_backward(*(to_f64(inp[k]) for k in ("query", "new_key", "new_value",
+                                                          "key_cache", "value_cache")),
+                               h["lengths"], h["append_mask"],
+                               **{k: None if v is None else to_f64(v) for k, v in ups.items()},
+                               scale=wl.scale)
+    for name, want in (("g_query", ref.query), ("g_new_key", ref.new_key),
+                       ("g_new_value", ref.new_value), ("g_key_cache", ref.key_cache),
+                       ("g_value_cache", ref.value_cache)):
+        check_grad(to_f64(outs[name]), want, "bf16", f"misaligned {which} {name}")
 
 
 def test_backward_full_decode_bench_configuration():
