@@ -457,9 +457,6 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
     if (!mul_ok(pg->num_blocks, d->Hk, kMaxElems, &x) || !mul_ok(x, bs, kMaxElems, &x) ||
         !mul_ok(x, d->D > d->Dv ? d->D : d->Dv, kMaxElems, &x))
       return KVC_ERR_SHAPE;
-    // the stream decode or matrix-core chunk path, every chunk inside one block
-    const int64_t chunk = p.decode ? p.decode->chunk : (p.chunk ? kvc::kChunkSlots : 0);
-    if (!chunk || (!single && bs < chunk)) return KVC_ERR_UNSUPPORTED;
   }
 
   if (!kc_in || !vc_in || !kc_out || !vc_out || !lengths || !lengths_out) return KVC_ERR_NULL;
@@ -530,15 +527,17 @@ int run_step(const kvc_dims* d, int dtype, int has_scale, double scale, const vo
   a.lengths = lengths; a.mask = mask; a.attention = attention; a.context = context;
   a.lengths_out = lengths_out; a.row_status = row_status;
 
-  // the vector and matrix paths need 16-byte aligned rows
-  const bool aligned = aligned16(query) && aligned16(new_key) && aligned16(new_value) &&
-                       aligned16(kc_in) && aligned16(vc_in) && aligned16(kc_out) &&
-                       aligned16(vc_out);
-  const bool vec_ok = p.decode && aligned;
+  // the vector and matrix paths need 16-byte aligned rows, and on a paged
+  // cache every one of their chunks inside one block; other calls take the
+  // generic kernel
+  bool aligned = aligned16(query) && aligned16(new_key) && aligned16(new_value) &&
+                 aligned16(kc_in) && aligned16(vc_in) && aligned16(kc_out) && aligned16(vc_out);
   if (pg) {
-    if (!aligned) return KVC_ERR_UNSUPPORTED;
+    const int64_t chunk = p.decode ? p.decode->chunk : (p.chunk ? kvc::kChunkSlots : 0);
+    if (pg->block_size != d->M && pg->block_size < chunk) aligned = false;
     set_paged(a, d, *pg);
   }
+  const bool vec_ok = p.decode && aligned;
   a.read_only = read_only ? 1 : 0;
   a.sinks = sinks;
   const bool chunk_ok = p.chunk && aligned;
@@ -728,15 +727,10 @@ int kvc_attend_over_cache(const kvc_dims* dims, int dtype, int has_scale, double
       return KVC_ERR_SHAPE;
     }
   }
-  if (pgp) {  // the checks the step makes on the mapped cache, before anything is enqueued
-    Plan p;
-    make_plan(d, dtype, &p);
+  if (pgp) {  // the check the step makes on the mapped cache, before anything is enqueued
     const int64_t bs = pg.block_size;
     const bool single = bs == d->M;
-    if (!single && ((bs & (bs - 1)) != 0 || d->M % bs != 0)) return KVC_ERR_SHAPE;
-    const int64_t chunk = p.decode ? p.decode->chunk : (p.chunk ? kvc::kChunkSlots : 0);
-    if (!chunk || (!single && bs < chunk) || !aligned16(key_cache) || !aligned16(value_cache))
-      return KVC_ERR_UNSUPPORTED;
+    if (bs < 1 || (!single && ((bs & (bs - 1)) != 0 || d->M % bs != 0))) return KVC_ERR_SHAPE;
   }
   const size_t e = dtype == KVC_F32 ? 4 : 2;
   const size_t B = d->B, Hq = d->Hq, Hk = d->Hk, Tq = total_q, D = d->D, Dv = d->Dv;
@@ -860,8 +854,8 @@ const char* kvc_status_string(int code) {
     case KVC_ERR_HIP: return "a HIP launch failed";
     case KVC_ERR_TOO_LARGE: return "the step needs more workspace than the no-allocation entry "
                                    "point's static scratch holds";
-    case KVC_ERR_UNSUPPORTED: return "the paged cache needs the stream decode path and blocks of "
-                                     ">= 64 slots";
+    case KVC_ERR_UNSUPPORTED: return "a shape, block size or buffer alignment the entry point "
+                                     "does not take";
     case KVC_ROW_BAD_LENGTH: return "row rejected: length outside [0, M]";
     case KVC_ROW_OVERFLOW: return "row rejected: length + n exceeds M";
     case KVC_ROW_NOT_PREFIX: return "row rejected: append mask is not a prefix";

@@ -1,7 +1,8 @@
 // kvc_generic.h -- attend kernel for any head sizes (D, Dv) and any packed
 // row count, in dense chunk mode (one workgroup per chunk and row tile).
 // It is the path for shapes the vector decode kernel does not cover (odd
-// head sizes, misaligned buffers, many packed rows); it leaves the same
+// head sizes, misaligned buffers, many packed rows) and for paged caches
+// whose blocks are smaller than the other paths' chunks; it leaves the same
 // chunk and segment results and shares the combine kernel.
 //
 // One workgroup handles one (batch row b, KV head h, row tile, chunk c):
@@ -139,9 +140,35 @@ __global__ __launch_bounds__(kGenericThreads) void attend_generic_kernel(StepArg
   const T* nk_head = nk + head * a.Q * a.D;
   const T* nv_head = nv + head * a.Q * a.Dv;
 
+  // slot j's key / value row of the updated caches: appended rows from the
+  // new rows, kept ones from the cache (dense, or the paged pool; nullptr
+  // for a table entry outside the pool, read as a zero row)
+  const int64_t kb = a.D * E::kBytes, vb = a.Dv * E::kBytes;
+  auto key_row = [&](int64_t j) -> const T* {
+    if (j >= len) return nk_head + (j - len) * a.D;
+    if (!a.paged) return k_head + j * a.D;
+    return reinterpret_cast<const T*>(slot_row(a, a.kc_in, b, kvh, j, kb));
+  };
+  auto value_row = [&](int64_t j) -> const T* {
+    if (j >= len) return nv_head + (j - len) * a.Dv;
+    if (!a.paged) return v_head + j * a.Dv;
+    return reinterpret_cast<const T*>(slot_row(a, a.vc_in, b, kvh, j, vb));
+  };
+
   // 1. cache writes
-  if (rt == 0 && !a.read_only) {
-    const int64_t kb = a.D * E::kBytes, vb = a.Dv * E::kBytes;
+  if (rt == 0 && !a.read_only && a.paged) {  // in place: the appended rows' blocks
+    const int64_t m0 = s0 > len ? s0 : len, m1 = s1 < len + n ? s1 : len + n;
+    for (int64_t j = m0; j < m1; j++) {
+      uint8_t* kd = const_cast<uint8_t*>(slot_row(a, a.kc_out, b, kvh, j, kb));
+      uint8_t* vd = const_cast<uint8_t*>(slot_row(a, a.vc_out, b, kvh, j, vb));
+      if (kd)
+        copy_bytes(kd, reinterpret_cast<const uint8_t*>(nk_head + (j - len) * a.D), kb, tid,
+                   kGenericThreads);
+      if (vd)
+        copy_bytes(vd, reinterpret_cast<const uint8_t*>(nv_head + (j - len) * a.Dv), vb, tid,
+                   kGenericThreads);
+    }
+  } else if (rt == 0 && !a.read_only) {
     write_cache_slots(static_cast<uint8_t*>(a.kc_out) + head * a.M * kb,
                       reinterpret_cast<const uint8_t*>(k_head),
                       reinterpret_cast<const uint8_t*>(nk_head), kb, s0, s1, len, n,
@@ -168,10 +195,11 @@ __global__ __launch_bounds__(kGenericThreads) void attend_generic_kernel(StepArg
     const int64_t g = rg / a.Q, t = rg % a.Q;
     Acc val = neg_inf;
     if (t < n && j <= len + t) {
-      const T* kp = j < len ? k_head + j * a.D : nk_head + (j - len) * a.D;
+      const T* kp = key_row(j);
       const T* qp = q + ((b * a.Hq + kvh * a.G + g) * a.Q + t) * a.D;
       Acc dot = 0;
-      for (int64_t d = 0; d < a.D; d++) dot += E::load(qp + d) * E::load(kp + d);
+      if (kp)
+        for (int64_t d = 0; d < a.D; d++) dot += E::load(qp + d) * E::load(kp + d);
       val = scale * dot;
     }
     sc[r][idx % nact] = val;
@@ -218,8 +246,8 @@ __global__ __launch_bounds__(kGenericThreads) void attend_generic_kernel(StepArg
     Acc o = 0;
     for (int i = 0; i < nact; i++) {
       const int64_t j = s0 + i;
-      const T* vp = j < len ? v_head + j * a.Dv : nv_head + (j - len) * a.Dv;
-      o += sc[r][i] * E::load(vp + dv);
+      const T* vp = value_row(j);
+      if (vp) o += sc[r][i] * E::load(vp + dv);
     }
     a.ws_seg_o[(seg * a.R + rg) * a.Dv + dv] = static_cast<float>(o);
   }

@@ -172,12 +172,13 @@ int kvc_step_inplace(const kvc_dims *dims, int dtype, int has_scale,
  * context, row_status, workspace) is as for kvc_step_inplace, and the
  * results equal kvc_step_inplace's on the dense cache the table describes.
  *
- * Scope: shapes the plan sends to the vector decode path (path 1) or the
- * matrix-core chunk path (path 2), 16-byte aligned buffers, and a
- * block_size that is a power of two of at least 64 slots, or M itself (one
- * block per row: a continuous cache whose rows the table picks); anything
- * else (the generic path's head sizes) returns KVC_ERR_UNSUPPORTED (or
- * KVC_ERR_SHAPE for a block_size that does not divide M).  Table entries are device data: an entry outside
+ * block_size: a power of two that divides M, or M itself (one block per
+ * row: a continuous cache whose rows the table picks); else KVC_ERR_SHAPE.
+ * Every shape of kvc_step_inplace is taken: the vector decode and
+ * matrix-core chunk paths read the pools when the buffers are 16-byte
+ * aligned and each of their chunks (64 slots) sits in one block; other
+ * calls (smaller blocks, misaligned pools, head sizes without those
+ * kernels) take the generic kernel.  Table entries are device data: an entry outside
  * [0, num_blocks) for a slot below lengths[b] + n_b is outside the contract
  * -- those slots read as zero rows and are never written, so no access
  * leaves the pools -- and the row's results are then unspecified.  Rows may
@@ -228,9 +229,8 @@ int kvc_step_paged(const kvc_dims *dims, int dtype, int has_scale,
  * range (KVC_ROW_BAD_QUERIES) gets zero output rows where its range is
  * addressable, and its code in row_status (optional).
  *
- * Scope: the paged and slot_ids layouts take the shapes of kvc_step_paged
- * (else KVC_ERR_UNSUPPORTED); the continuous layout read by row takes every
- * shape of kvc_step_inplace.
+ * Scope: every shape of kvc_step_inplace, in each layout (the paged one
+ * with kvc_step_paged's block sizes).
  * workspace: kvc_attend_workspace_bytes(dims, dtype) bytes.  Outputs and the
  * workspace must not overlap any input (KVC_ERR_ALIAS). */
 size_t kvc_attend_workspace_bytes(const kvc_dims *dims, int dtype);

@@ -175,8 +175,8 @@ def test_page_face_rejects_cpu_and_options():
 
 
 def test_host_checks_paged(lib):
-    """kvc_step_paged: block size, scope and aliasing are checked on the host
-    (every call here fails one of those checks; none reaches a launch)."""
+    """kvc_step_paged: block size, workspace and aliasing are checked on the
+    host (every call here fails one of those checks; none reaches a launch)."""
     def run(d, block_size=64, num_blocks=64, ptrs=None, ws=1 << 30, dtype=kvc.KVC_BF16):
         e = 2 if dtype == kvc.KVC_BF16 else 4
         B, Hq, Hk, Q, M, D, Dv = d.B, d.Hq, d.Hk, d.Q, d.M, d.D, d.Dv
@@ -197,11 +197,14 @@ def test_host_checks_paged(lib):
     d = dims(B=4, Hq=8, Hk=2, Q=1, M=1024, D=128, Dv=128)  # 4 packed rows: the decode path
     assert run(d, block_size=48)[0] == -2       # not a power of two
     assert run(d, block_size=2048)[0] == -2     # does not divide M
-    assert run(d, block_size=32)[0] == -8       # smaller than a decode chunk
     assert run(d, num_blocks=0)[0] == -2
-    assert run(dims(B=4, Hq=8, Hk=2, Q=4, M=1024, D=128, Dv=128),
-               block_size=32)[0] == -8                  # chunk path, blocks below 64 slots
-    assert run(dims(B=4, Hq=8, Hk=2, Q=1, M=1024, D=96, Dv=96))[0] == -8   # no decode kernel
+    # blocks smaller than a chunk, and shapes without a decode or chunk
+    # kernel, take the generic kernel (the calls then fail the workspace
+    # check, before a launch)
+    assert run(d, block_size=32, ws=16)[0] == -5
+    assert run(d, block_size=1, ws=16)[0] == -5
+    assert run(dims(B=4, Hq=8, Hk=2, Q=4, M=1024, D=128, Dv=128), block_size=32, ws=16)[0] == -5
+    assert run(dims(B=4, Hq=8, Hk=2, Q=1, M=1024, D=96, Dv=96), ws=16)[0] == -5
     _, ptrs = run(d, ws=16)
     assert run(d, ws=16)[0] == -5
     bad = list(ptrs)
@@ -249,8 +252,8 @@ def test_host_checks_backward(lib):
 
 
 def test_host_checks_attend_over_cache(lib):
-    """kvc_attend_over_cache: layout, scope, workspace and aliasing are checked
-    on the host before anything is enqueued (every call here fails one)."""
+    """kvc_attend_over_cache: layout, workspace and aliasing are checked on
+    the host before anything is enqueued (every call here fails one)."""
     def run(d, Tq=4, num_blocks=8, block_size=None, table=False, slots=False, ptrs=None,
             ws=1 << 34, sink=True, kcount=None):
         e = 2
@@ -279,8 +282,11 @@ def test_host_checks_attend_over_cache(lib):
     assert run(d, num_blocks=3)[0] == -2                            # row b needs B rows
     assert run(d, Tq=-1)[0] == -2
     assert run(d, table=True, block_size=48)[0] == -2
-    assert run(d, table=True, block_size=32)[0] == -8               # smaller than a chunk
-    assert run(dims(B=4, Hq=8, Hk=2, Q=4, M=1024, D=96, Dv=96), slots=True)[0] == -8  # generic
+    # blocks smaller than a chunk, and shapes of the generic kernel, are taken
+    # (the calls then fail the workspace check, before a launch)
+    assert run(d, table=True, block_size=32, ws=16)[0] == -5
+    assert run(d, table=True, block_size=1, ws=16)[0] == -5
+    assert run(dims(B=4, Hq=8, Hk=2, Q=4, M=1024, D=96, Dv=96), slots=True, ws=16)[0] == -5
     assert run(d, ws=16)[0] == -5
     assert run(d, ws=16, kcount=d.B + 1)[0] == -5                   # cumulative form accepted
     for kc in (0, d.B - 1, d.B + 2):                                # [B] or [B + 1] only

@@ -404,6 +404,15 @@ PAGED_CASES = [
               len_range=(0, 500)), 128),
     (chunk_wl(name="paged_chunk_f32", dtype="f32", B=2, Hq=8, Hk=2, Q=20, M=256,
               len_range=(0, 230), std=8.0, scale=4.0), 64),
+    # the generic kernel: blocks smaller than the decode or chunk paths'
+    # chunks, and head sizes without a decode or chunk kernel
+    (WORKLOADS["decode_gqa_bf16"].with_(name="paged_gen_b16", B=3, M=512,
+                                        len_range=(0, 511)), 16),
+    (chunk_wl(name="paged_gen_chunk_b32", B=2, Hq=8, Hk=2, Q=40, M=256, len_range=(0, 200)), 32),
+    (WORKLOADS["tiny_mixed_f32"].with_(name="paged_gen_tiny"), 4),
+    (WORKLOADS["tiny_mixed_f32"].with_(name="paged_gen_tiny_b1"), 1),
+    (chunk_wl(name="paged_gen_d96", B=3, Hq=6, Hk=2, Q=3, M=384, D=96, Dv=80,
+              len_range=(0, 380), n_rule="uniform"), 128),
 ]
 
 
@@ -417,6 +426,32 @@ def test_paged_against_oracle(wl, bs):
         ref = paged_ref(inp, kp, vp, table, scale=wl.scale)
         out = run_paged(inp, kp, vp, table, scale=wl.scale)
         check_step(out, ref, wl.dtype, f"paged {wl.name}/{seed}")
+
+
+def test_paged_misaligned_pools_take_generic_path():
+    """Pools that start 2 bytes past a 16-byte boundary: the generic kernel,
+    results as the oracle's."""
+    wl = WORKLOADS["decode_gqa_bf16"].with_(name="paged_misaligned", B=3, M=512,
+                                            len_range=(0, 511))
+    say(f"[case] paged misaligned pools")
+    inp = make_inputs(wl, 0, "cpu")
+    kp, vp, table = paged_layout(inp["key_cache"], inp["value_cache"], 64, 0)
+    ref = paged_ref(inp, kp, vp, table)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    kpd, vpd = misaligned(kp.to(DEV)), misaligned(vp.to(DEV))
+    tab = table.to(DEV)
+    B, Hq, Q, _ = d["query"].shape
+    att = torch.full((B, Hq, Q, wl.M), 3.0, dtype=kp.dtype, device=DEV)
+    ctx = torch.full((B, Hq, Q, wl.Dv), 3.0, dtype=kp.dtype, device=DEV)
+    lens_out = torch.empty_like(d["lengths"])
+    status = torch.empty(B, dtype=torch.int32, device=DEV)
+    mask = d["append_mask"].contiguous().view(torch.uint8)
+    kvc.kvc_step_paged(d["query"], d["new_key"], d["new_value"], kpd, vpd, tab, d["lengths"],
+                       mask, lens_out, att, ctx, status)
+    torch.cuda.synchronize()
+    out = {"key_cache": kpd.cpu(), "value_cache": vpd.cpu(), "lengths": lens_out.cpu(),
+           "attention": att.cpu(), "context": ctx.cpu(), "row_status": status.cpu()}
+    check_step(out, ref, wl.dtype, "paged misaligned pools")
 
 
 def test_paged_full_size_bench_configuration():
@@ -507,16 +542,16 @@ def test_paged_bad_entries_stay_inside_the_pool():
     assert torch.equal(bits_t(out2["value_cache"]), bits_t(out["value_cache"]))
 
 
-def test_paged_unsupported_shapes_are_refused():
-    """Blocks smaller than a decode chunk, and shapes outside the decode path,
-    come back as KVC_ERR_UNSUPPORTED before anything runs."""
-    wl = WORKLOADS["decode_gqa_bf16"].with_(name="paged_refuse", B=2, M=256, len_range=(0, 200))
+def test_paged_bad_block_size_is_refused():
+    """A block size that is not a power of two (and not M) comes back as
+    KVC_ERR_SHAPE before anything runs: the pools stay as they were."""
+    wl = WORKLOADS["decode_gqa_bf16"].with_(name="paged_refuse", B=2, M=192, len_range=(0, 150))
     inp = make_inputs(wl, 1, "cpu")
-    kp, vp, table = paged_layout(inp["key_cache"], inp["value_cache"], 32, 1)
+    kp, vp, table = paged_layout(inp["key_cache"], inp["value_cache"], 48, 1)
     rest = {k: v for k, v in inp.items() if k not in ("key_cache", "value_cache")}
     with pytest.raises(kvc.KvcError) as e:
         run_paged(rest, kp, vp, table)
-    assert e.value.code == -8
+    assert e.value.code == -2
 
 
 # -- capture in a HIP graph (serving loops replay a captured step) ----------
@@ -647,12 +682,14 @@ REATT_CASES = [
     ("bf16", 6, 16, 4, 2, 700, 128, 128),
     ("bf16", 5, 8, 2, 1, 1024, 64, 64),
     ("f32", 4, 8, 8, 4, 300, 64, 32),
+    # head sizes without a decode kernel: the generic kernel
+    ("bf16", 4, 6, 2, 3, 200, 96, 80),
 ]
 
 
 @pytest.mark.parametrize("kform", ["lengths", "cumulative"])
 @pytest.mark.parametrize("case", REATT_CASES, ids=lambda c: "-".join(map(str, c)))
-@pytest.mark.parametrize("layout", ["rows", "slot_ids", "paged"])
+@pytest.mark.parametrize("layout", ["rows", "slot_ids", "paged", "paged16"])
 def test_reattend_against_oracle(case, layout, kform):
     dtype, B, Hq, Hk, Qmax, M, D, Dv = case
     for seed in (0, 1):
@@ -678,7 +715,8 @@ def test_reattend_against_oracle(case, layout, kform):
             kpad = torch.zeros(B, Hk, Mp, D, dtype=kc.dtype)
             vpad = torch.zeros(B, Hk, Mp, Dv, dtype=vc.dtype)
             kpad[:, :, :M], vpad[:, :, :M] = kc, vc
-            kp, vp, table = paged_layout(kpad, vpad, 64, seed)
+            # 64-slot blocks, or 16-slot ones (below a chunk: the generic kernel)
+            kp, vp, table = paged_layout(kpad, vpad, 16 if layout == "paged16" else 64, seed)
             out, st = run_reatt(q, cu, kp, vp, L, Qmax, M=Mp, table=table, sink=sink,
                                 scale=scale)
             ref, rst = reatt_ref(q, cu, kpad, vpad, L, Qmax, sink, scale)
