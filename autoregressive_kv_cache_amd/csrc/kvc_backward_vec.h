@@ -8,11 +8,13 @@
 // a per-slot dot product on the vector units, in fp32 (bf16 inputs widen
 // exactly; the row statistics are merged in fp64 by bwd_rows_kernel).
 //
-// Layout (as attend_stream_kernel, kvc_stream.h): for a 64-slot chunk, lane
-// l holds dims [h*64 + (l>>3)*8, +8) of slot 8k + (l&7) in piece (k, h), so
-// each 16-byte load covers whole 128-byte lines; the 8 partial dot products
-// of a slot are finished by a reduce-scatter over lane bits 5, 4 and 3,
-// after which lane l holds slot l's value for every packed row.
+// Layout of bwd_vstats and bwd_vdq (as attend_stream_kernel, kvc_stream.h):
+// for a 64-slot chunk, lane l holds dims [h*64 + (l>>3)*8, +8) of slot
+// 8k + (l&7) in piece (k, h), so each 16-byte load covers whole 128-byte
+// lines; the 8 partial dot products of a slot are finished by a
+// reduce-scatter over lane bits 5, 4 and 3, after which lane l holds slot
+// l's value for every packed row.  bwd_vslot computes no dot product and
+// gives each lane 8 dims of one slot instead (see there).
 //
 // Kernels (one wave per (batch row, KV head, run of kBwdVecSlots slots)):
 //   bwd_vstats: scores s = scale q.K'_j and dP_j = dA_j + dO.V'_j of the

@@ -1,12 +1,16 @@
 // kvc_stream.h -- stream-mode attend kernel for bf16 decode-shaped steps
-// (at most 8 packed query rows per KV head, D = Dv in {64, 128}).
+// (at most 15 packed query rows per KV head, D = Dv in {64, 128}).
 //
 // Work split (as attend_decode_kernel, kvc_decode.h): the visible slots of
 // every (batch row, KV head) are cut into chunks of 64 slots -- the cached
 // slots, then one chunk with the appended rows read from new_key/new_value
-// (stream_chunks) -- and the flattened chunk list is cut into equal
-// contiguous ranges, one per wave.  A wave keeps running statistics across
-// the chunks of one KV head (a segment).
+// (stream_chunks) -- and the flattened chunk list is cut into contiguous
+// ranges, one per stream worker (worker_start: with two workgroups per
+// compute unit, the workers of the first half of the grid take `lead`/8
+// times the share of the others).  A worker is one wave holding up to
+// ROWS packed rows, or, past 8 rows (GROUPS), two waves side by side that
+// read the same chunks and hold 8 rows each.  A worker keeps running
+// statistics across the chunks of one KV head (a segment).
 //
 // What it leaves for the combine kernel (kvc_combine_stream.h), in the
 // workspace, indexed by the flattened chunk x or the segment id:

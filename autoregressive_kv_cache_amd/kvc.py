@@ -182,23 +182,67 @@ def workspace_for(dims: KvcDims, dtype: int, device) -> torch.Tensor:
     return torch.empty(max(1, kvc_workspace_bytes(dims, dtype)), dtype=torch.uint8, device=device)
 
 
+def _oop_args(query, new_key, new_value, key_cache, value_cache, lengths, append_mask,
+              key_cache_out, value_cache_out, lengths_out, attention, context, row_status,
+              workspace, scale, stream) -> tuple:
+    """kvc_step_out_of_place's arguments but the events pointer, and the
+    workspace they name."""
+    dims = dims_of(query, key_cache, value_cache)
+    dt = dtype_code(key_cache.dtype)
+    if workspace is None:
+        workspace = workspace_for(dims, dt, key_cache.device)
+    hs, sc = _scale_args(scale)
+    return [ctypes.byref(dims), dt, hs, sc, _ptr(query), _ptr(new_key), _ptr(new_value),
+            _ptr(key_cache), _ptr(value_cache), _ptr(lengths), _ptr(append_mask),
+            _ptr(key_cache_out), _ptr(value_cache_out), _ptr(lengths_out), _ptr(attention),
+            _ptr(context), _ptr(row_status), _ptr(workspace), workspace.numel(),
+            _stream(stream, key_cache.device)], workspace
+
+
+def _inplace_args(query, new_key, new_value, key_cache, value_cache, lengths, append_mask,
+                  lengths_out, attention, context, row_status, workspace, scale, stream) -> tuple:
+    """kvc_step_inplace's arguments but the events pointer, and the workspace
+    they name."""
+    dims = dims_of(query, key_cache, value_cache)
+    dt = dtype_code(key_cache.dtype)
+    if workspace is None:
+        workspace = workspace_for(dims, dt, key_cache.device)
+    hs, sc = _scale_args(scale)
+    return [ctypes.byref(dims), dt, hs, sc, _ptr(query), _ptr(new_key), _ptr(new_value),
+            _ptr(key_cache), _ptr(value_cache), _ptr(lengths), _ptr(append_mask),
+            _ptr(lengths_out), _ptr(attention), _ptr(context), _ptr(row_status), _ptr(workspace),
+            workspace.numel(), _stream(stream, key_cache.device)], workspace
+
+
+def _paged_args(query, new_key, new_value, key_pool, value_pool, block_table, lengths,
+                append_mask, lengths_out, attention, context, row_status, workspace, scale,
+                stream) -> tuple:
+    """kvc_step_paged's arguments but the events pointer, and the workspace
+    they name."""
+    B, Hq, Q, D = query.shape
+    num_blocks, Hk, block_size, _ = key_pool.shape
+    dims = KvcDims(B, Hq, Hk, Q, block_table.shape[1] * block_size, D, value_pool.shape[3])
+    dt = dtype_code(key_pool.dtype)
+    if workspace is None:
+        workspace = workspace_for(dims, dt, key_pool.device)
+    hs, sc = _scale_args(scale)
+    return [ctypes.byref(dims), dt, hs, sc, _ptr(query), _ptr(new_key), _ptr(new_value),
+            _ptr(key_pool), _ptr(value_pool), int(num_blocks), int(block_size),
+            _ptr(block_table), _ptr(lengths), _ptr(append_mask), _ptr(lengths_out),
+            _ptr(attention), _ptr(context), _ptr(row_status), _ptr(workspace),
+            workspace.numel(), _stream(stream, key_pool.device)], workspace
+
+
 def kvc_step_out_of_place(query, new_key, new_value, key_cache, value_cache, lengths, append_mask,
                           key_cache_out, value_cache_out, lengths_out, attention, context,
                           row_status=None, workspace=None, scale=None, stream=None,
                           events=None) -> None:
     """Enqueue the out-of-place step on ``stream`` (default: torch's current
     stream).  All tensors are device tensors in the layouts of ``kvc.h``."""
-    lib = load()
-    dims = dims_of(query, key_cache, value_cache)
-    dt = dtype_code(key_cache.dtype)
-    if workspace is None:
-        workspace = workspace_for(dims, dt, key_cache.device)
-    hs, sc = _scale_args(scale)
-    rc = lib.kvc_step_out_of_place(
-        ctypes.byref(dims), dt, hs, sc, _ptr(query), _ptr(new_key), _ptr(new_value),
-        _ptr(key_cache), _ptr(value_cache), _ptr(lengths), _ptr(append_mask), _ptr(key_cache_out),
-        _ptr(value_cache_out), _ptr(lengths_out), _ptr(attention), _ptr(context), _ptr(row_status),
-        _ptr(workspace), workspace.numel(), _stream(stream, key_cache.device), _events(events))
+    args, _ = _oop_args(query, new_key, new_value, key_cache, value_cache, lengths, append_mask,
+                        key_cache_out, value_cache_out, lengths_out, attention, context,
+                        row_status, workspace, scale, stream)
+    rc = load().kvc_step_out_of_place(*args, _events(events))
     if rc != KVC_OK:
         raise KvcError(rc, "kvc_step_out_of_place")
 
@@ -208,19 +252,80 @@ def kvc_step_inplace(query, new_key, new_value, key_cache, value_cache, lengths,
                      stream=None, events=None) -> None:
     """Enqueue the in-place step on ``stream``; ``lengths_out`` may be
     ``lengths`` itself."""
-    lib = load()
-    dims = dims_of(query, key_cache, value_cache)
-    dt = dtype_code(key_cache.dtype)
-    if workspace is None:
-        workspace = workspace_for(dims, dt, key_cache.device)
-    hs, sc = _scale_args(scale)
-    rc = lib.kvc_step_inplace(
-        ctypes.byref(dims), dt, hs, sc, _ptr(query), _ptr(new_key), _ptr(new_value),
-        _ptr(key_cache), _ptr(value_cache), _ptr(lengths), _ptr(append_mask), _ptr(lengths_out),
-        _ptr(attention), _ptr(context), _ptr(row_status), _ptr(workspace), workspace.numel(),
-        _stream(stream, key_cache.device), _events(events))
+    args, _ = _inplace_args(query, new_key, new_value, key_cache, value_cache, lengths,
+                            append_mask, lengths_out, attention, context, row_status, workspace,
+                            scale, stream)
+    rc = load().kvc_step_inplace(*args, _events(events))
     if rc != KVC_OK:
         raise KvcError(rc, "kvc_step_inplace")
+
+
+def kvc_step_paged(query, new_key, new_value, key_pool, value_pool, block_table, lengths,
+                   append_mask, lengths_out, attention, context, row_status=None,
+                   workspace=None, scale=None, stream=None, events=None) -> None:
+    """Enqueue the in-place step over a paged cache on ``stream``: pools
+    ``[num_blocks, Hk, block_size, D|Dv]``, ``block_table`` int32
+    ``[B, max_blocks]``; each row's capacity is ``max_blocks * block_size``."""
+    args, _ = _paged_args(query, new_key, new_value, key_pool, value_pool, block_table, lengths,
+                          append_mask, lengths_out, attention, context, row_status, workspace,
+                          scale, stream)
+    rc = load().kvc_step_paged(*args, _events(events))
+    if rc != KVC_OK:
+        raise KvcError(rc, "kvc_step_paged")
+
+
+class BoundCall:
+    """One step entry point with its arguments marshalled once, for loops
+    that repeat the same call on the same buffers (a serving loop, the
+    bench): each call is then one foreign call.  It keeps the tensors it was
+    bound to (and the workspace it made, if any) alive; ``events`` may
+    change from call to call."""
+
+    def __init__(self, name: str, args: list, keep: tuple):
+        self._fn = getattr(load(), name)
+        self._name = name
+        self._keep = keep
+        conv = []
+        for t, a in zip(self._fn.argtypes, args):
+            simple = isinstance(t, type) and issubclass(t, ctypes._SimpleCData)
+            conv.append(t(a) if simple and a is not None else a)
+        self._args = tuple(conv)
+
+    def __call__(self, events=None) -> None:
+        rc = self._fn(*self._args, _events(events))
+        if rc != KVC_OK:
+            raise KvcError(rc, self._name)
+
+
+def bind_step_out_of_place(query, new_key, new_value, key_cache, value_cache, lengths,
+                           append_mask, key_cache_out, value_cache_out, lengths_out, attention,
+                           context, row_status=None, workspace=None, scale=None,
+                           stream=None) -> BoundCall:
+    """kvc_step_out_of_place bound to these buffers (see BoundCall)."""
+    t = (query, new_key, new_value, key_cache, value_cache, lengths, append_mask, key_cache_out,
+         value_cache_out, lengths_out, attention, context, row_status)
+    args, ws = _oop_args(*t, workspace, scale, stream)
+    return BoundCall("kvc_step_out_of_place", args, t + (ws,))
+
+
+def bind_step_inplace(query, new_key, new_value, key_cache, value_cache, lengths, append_mask,
+                      lengths_out, attention, context, row_status=None, workspace=None,
+                      scale=None, stream=None) -> BoundCall:
+    """kvc_step_inplace bound to these buffers (see BoundCall)."""
+    t = (query, new_key, new_value, key_cache, value_cache, lengths, append_mask, lengths_out,
+         attention, context, row_status)
+    args, ws = _inplace_args(*t, workspace, scale, stream)
+    return BoundCall("kvc_step_inplace", args, t + (ws,))
+
+
+def bind_step_paged(query, new_key, new_value, key_pool, value_pool, block_table, lengths,
+                    append_mask, lengths_out, attention, context, row_status=None,
+                    workspace=None, scale=None, stream=None) -> BoundCall:
+    """kvc_step_paged bound to these buffers (see BoundCall)."""
+    t = (query, new_key, new_value, key_pool, value_pool, block_table, lengths, append_mask,
+         lengths_out, attention, context, row_status)
+    args, ws = _paged_args(*t, workspace, scale, stream)
+    return BoundCall("kvc_step_paged", args, t + (ws,))
 
 
 def kvc_step_inplace_noalloc(query, new_key, new_value, key_cache, value_cache, lengths,
@@ -239,30 +344,6 @@ def kvc_step_inplace_noalloc(query, new_key, new_value, key_cache, value_cache, 
         _events(events))
     if rc != KVC_OK:
         raise KvcError(rc, "kvc_step_inplace_noalloc")
-
-
-def kvc_step_paged(query, new_key, new_value, key_pool, value_pool, block_table, lengths,
-                   append_mask, lengths_out, attention, context, row_status=None,
-                   workspace=None, scale=None, stream=None, events=None) -> None:
-    """Enqueue the in-place step over a paged cache on ``stream``: pools
-    ``[num_blocks, Hk, block_size, D|Dv]``, ``block_table`` int32
-    ``[B, max_blocks]``; each row's capacity is ``max_blocks * block_size``."""
-    lib = load()
-    B, Hq, Q, D = query.shape
-    num_blocks, Hk, block_size, _ = key_pool.shape
-    dims = KvcDims(B, Hq, Hk, Q, block_table.shape[1] * block_size, D, value_pool.shape[3])
-    dt = dtype_code(key_pool.dtype)
-    if workspace is None:
-        workspace = workspace_for(dims, dt, key_pool.device)
-    hs, sc = _scale_args(scale)
-    rc = lib.kvc_step_paged(
-        ctypes.byref(dims), dt, hs, sc, _ptr(query), _ptr(new_key), _ptr(new_value),
-        _ptr(key_pool), _ptr(value_pool), int(num_blocks), int(block_size), _ptr(block_table),
-        _ptr(lengths), _ptr(append_mask), _ptr(lengths_out), _ptr(attention), _ptr(context),
-        _ptr(row_status), _ptr(workspace), workspace.numel(), _stream(stream, key_pool.device),
-        _events(events))
-    if rc != KVC_OK:
-        raise KvcError(rc, "kvc_step_paged")
 
 
 def kvc_attend_workspace_bytes(dims: KvcDims, dtype: int) -> int:

@@ -301,6 +301,43 @@ def test_host_checks_attend_over_cache(lib):
         assert run(d, ptrs=bad)[0] == -6, (out_i, in_i)
 
 
+def test_bound_calls_marshal_like_the_plain_calls(lib):
+    """A bound step (arguments marshalled once) reaches the same host checks
+    as the plain call: with a 16-byte workspace both fail the workspace check
+    (KVC_ERR_WORKSPACE) before anything is enqueued, on every call."""
+    import torch
+    B, Hq, Hk, Q, M, D = 2, 4, 2, 1, 64, 16
+    t = {"query": torch.zeros(B, Hq, Q, D), "new_key": torch.zeros(B, Hk, Q, D),
+         "new_value": torch.zeros(B, Hk, Q, D), "key_cache": torch.zeros(B, Hk, M, D),
+         "value_cache": torch.zeros(B, Hk, M, D), "lengths": torch.zeros(B, dtype=torch.int64),
+         "append_mask": torch.ones(B, Q, dtype=torch.uint8)}
+    outs = {"lengths_out": torch.zeros(B, dtype=torch.int64),
+            "attention": torch.zeros(B, Hq, Q, M), "context": torch.zeros(B, Hq, Q, D)}
+    ws = torch.empty(16, dtype=torch.uint8)
+    bound = kvc.bind_step_inplace(*t.values(), *outs.values(), workspace=ws, stream=0)
+    for _ in range(2):
+        with pytest.raises(kvc.KvcError) as e:
+            bound()
+        assert e.value.code == -5
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kvc_step_inplace(*t.values(), *outs.values(), workspace=ws, stream=0)
+    assert e.value.code == -5
+    kc_out, vc_out = torch.zeros(B, Hk, M, D), torch.zeros(B, Hk, M, D)
+    bound = kvc.bind_step_out_of_place(*t.values(), kc_out, vc_out, *outs.values(), workspace=ws,
+                                       stream=0)
+    with pytest.raises(kvc.KvcError) as e:
+        bound()
+    assert e.value.code == -5
+    pool = torch.zeros(4, Hk, 32, D)
+    table = torch.zeros(B, 2, dtype=torch.int32)
+    bound = kvc.bind_step_paged(t["query"], t["new_key"], t["new_value"], pool, pool.clone(),
+                                table, t["lengths"], t["append_mask"], *outs.values(),
+                                workspace=ws, stream=0)
+    with pytest.raises(kvc.KvcError) as e:
+        bound()
+    assert e.value.code == -5
+
+
 def test_binding_argument_counts_match_the_header(lib):
     """Every ctypes declaration of the binding has as many arguments as the
     C prototype in include/kvc.h (a short list would let ctypes pass the
