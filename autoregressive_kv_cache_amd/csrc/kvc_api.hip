@@ -153,7 +153,7 @@ int64_t compute_units() {
   return n;
 }
 // Slots per combine workgroup (a multiple of every chunk size).
-constexpr int64_t kCombineSlots = 2048;
+constexpr int64_t kCombineSlots = 4096;
 
 // Matrix-core chunk path: more than 8 packed rows per KV head.
 struct ChunkEntry {

@@ -137,7 +137,7 @@ struct Vec8<float> {
   }
 };
 
-constexpr int kCombineVecPerLane = 4;  // 8-element vectors per lane and pass
+constexpr int kCombineVecPerLane = 8;  // 8-element vectors per lane and pass
 
 // Workgroup = kCombineWaves waves; wave w owns packed row rb * kCombineWaves + w
 // of its group.  Workgroups k < ceil(M / CS) rescale the slot range
