@@ -18,6 +18,7 @@
 #include "kvc_prep.h"
 #include "kvc_reattend.h"
 #include "kvc_combine_stream.h"
+#include "kvc_small.h"
 #include "kvc_stream.h"
 
 namespace {
@@ -111,6 +112,16 @@ void launch_decode_bf16(const StepArgs& a, hipStream_t s) {
     launch_stream_q<D, DV, ROWS, false>(a, s);
 }
 
+// Small heads (rows of at most 64 bytes): the one-slot-per-lane kernel of
+// kvc_small.h, one launch for every variant (the row table, the paged
+// source and the out-of-place copy are chosen at run time).
+template <typename T, int D, int DV, int ROWS>
+void launch_small(const StepArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.P / kvc::kDecodeWaves)), block(kvc::kDecodeThreads);
+  hipLaunchKernelGGL((kvc::attend_small_kernel<T, D, DV, ROWS>), grid, block, 0, s, a,
+                     a.ws_rowinfo, a.ws_wstart);
+}
+
 struct DecodeEntry {
   int dtype, D, Dv, rows, chunk, wgs_per_cu;
   void (*launch)(const StepArgs&, hipStream_t);
@@ -124,6 +135,8 @@ struct DecodeEntry {
 // the two kernels of a bf16 entry share chunk size and occupancy; with two
 // workgroups per unit the first one placed takes twice the share (measured:
 // 2.3 us less per decode step at B=32, Hq=32, Hk=8, M=8192)
+#define KVC_SMALL(T, CODE, D, DV, ROWS) \
+  {CODE, D, DV, ROWS, kvc::kSmallChunk, 2, &launch_small<T, D, DV, ROWS>, false, 8}
 #define KVC_STREAM(D, DV, ROWS) \
   {KVC_BF16, D, DV, ROWS, kvc::kStreamChunk, kvc::stream_waves_per_simd<ROWS>(), \
    &launch_decode_bf16<kvc::bf16, D, DV, ROWS>, true, \
@@ -133,7 +146,12 @@ const DecodeEntry kDecodeTable[] = {
     KVC_DECODE(kvc::bf16, KVC_BF16, 256, 256, 4), KVC_DECODE(kvc::bf16, KVC_BF16, 256, 256, 8),
     KVC_DECODE(float, KVC_F32, 128, 128, 4),      KVC_DECODE(float, KVC_F32, 64, 64, 4),
     KVC_DECODE(float, KVC_F32, 64, 32, 4),
+    KVC_SMALL(float, KVC_F32, 8, 8, 4),           KVC_SMALL(float, KVC_F32, 8, 8, 8),
+    KVC_SMALL(float, KVC_F32, 16, 16, 4),         KVC_SMALL(float, KVC_F32, 16, 16, 8),
+    KVC_SMALL(kvc::bf16, KVC_BF16, 16, 16, 4),    KVC_SMALL(kvc::bf16, KVC_BF16, 16, 16, 8),
+    KVC_SMALL(kvc::bf16, KVC_BF16, 32, 32, 4),    KVC_SMALL(kvc::bf16, KVC_BF16, 32, 32, 8),
 };
+#undef KVC_SMALL
 #undef KVC_DECODE
 #undef KVC_STREAM
 

@@ -65,7 +65,9 @@ def test_plan_dispatch_rule(lib):
     in {64, 128, 256} bf16 or {64, 128} fp32).  Below that the vector decode
     kernels (1): 4 rows a wave up to R = 4, 8 up to 8, and for bf16 with
     D = Dv in {64, 128} two waves of up to 8 rows each up to R = 15
-    (rows_per_tile 8, row_tiles 2).  The rest -> the generic kernel (0).
+    (rows_per_tile 8, row_tiles 2); small heads (fp32 D = Dv in {8, 16},
+    bf16 {16, 32}) up to R = 8 on the one-slot-per-lane kernel.  The rest
+    -> the generic kernel (0).
     The workspace covers every path of the shape."""
     cases = [
         (dims(B=32, Hq=32, Hk=8, Q=1, M=8192, D=128, Dv=128), kvc.KVC_BF16, 1, 4, 1),
@@ -82,7 +84,13 @@ def test_plan_dispatch_rule(lib):
         (dims(B=2, Hq=4, Hk=1, Q=3, M=100, D=128, Dv=128), kvc.KVC_F32, 0, None, None),   # R = 12
         (dims(B=2, Hq=4, Hk=1, Q=3, M=100, D=256, Dv=256), kvc.KVC_BF16, 0, None, None),  # R = 12
         (dims(B=2, Hq=4, Hk=1, Q=3, M=100, D=96, Dv=96), kvc.KVC_BF16, 0, None, None),    # no entry
-        (dims(B=2, Hq=4, Hk=2, Q=3, M=16, D=8, Dv=8), kvc.KVC_F32, 0, None, None),
+        # small heads (rows of at most 64 bytes): the one-slot-per-lane decode kernel
+        (dims(B=2, Hq=4, Hk=2, Q=3, M=16, D=8, Dv=8), kvc.KVC_F32, 1, 8, 1),
+        (dims(B=2, Hq=4, Hk=2, Q=1, M=16, D=8, Dv=8), kvc.KVC_F32, 1, 4, 1),
+        (dims(B=2, Hq=8, Hk=2, Q=2, M=99, D=16, Dv=16), kvc.KVC_F32, 1, 8, 1),
+        (dims(B=2, Hq=8, Hk=2, Q=1, M=99, D=32, Dv=32), kvc.KVC_BF16, 1, 4, 1),
+        (dims(B=2, Hq=8, Hk=2, Q=1, M=99, D=8, Dv=16), kvc.KVC_F32, 0, None, None),
+        (dims(B=2, Hq=4, Hk=1, Q=3, M=99, D=8, Dv=8), kvc.KVC_F32, 0, None, None),   # R = 12
     ]
     for d, dt, path, rows, tiles in cases:
         plan = kvc.kvc_plan_step(d, dt)

@@ -82,6 +82,20 @@ def test_tiny_more_seeds(seed):
     # preparation kernel runs first)
     Workload(name="decode_b1030", B=1030, Hq=2, Hk=1, Q=1, M=96, D=64, Dv=64, dtype="bf16",
              len_range=(0, 95), n_rule="all"),
+    # small heads (rows of at most 64 bytes): the one-slot-per-lane decode
+    # kernel, fp32 and bf16, 1 to 8 packed rows, several chunks and ragged
+    # tails, empty caches and rows that append nothing, and the preparation
+    # kernel above 1024 rows
+    Workload(name="small_f32_d8_r6", B=5, Hq=4, Hk=2, Q=3, M=300, D=8, Dv=8, dtype="f32",
+             len_range=(0, 297), n_rule="uniform", force_len0_row=0, force_n0_row=1),
+    Workload(name="small_f32_d16_r4", B=4, Hq=8, Hk=2, Q=1, M=700, D=16, Dv=16, dtype="f32",
+             len_range=(0, 699), n_rule="all", std=4.0),
+    Workload(name="small_bf16_d32_r8", B=4, Hq=8, Hk=2, Q=2, M=500, D=32, Dv=32, dtype="bf16",
+             len_range=(0, 498), n_rule="uniform"),
+    Workload(name="small_bf16_d16_r1", B=3, Hq=4, Hk=4, Q=1, M=200, D=16, Dv=16, dtype="bf16",
+             len_range=(0, 199), n_rule="all"),
+    Workload(name="small_b1030", B=1030, Hq=2, Hk=1, Q=1, M=96, D=8, Dv=8, dtype="f32",
+             len_range=(0, 95), n_rule="all"),
 ], ids=lambda w: w.name)
 def test_reduced_decode_shapes(wl, mode):
     full_check(wl, 0, mode)
@@ -242,11 +256,11 @@ def test_page_face_dict_and_inplace_twin():
 
 
 def test_plan_paths():
-    """The decode-shaped workloads take the vector stream path, the chunk
-    workloads (160 packed rows) the matrix-core chunk path, the rest the
-    generic one."""
+    """The decode-shaped workloads (the tiny step's head size 8 included)
+    take the vector decode path, the chunk workloads (160 packed rows) the
+    matrix-core chunk path."""
     expect = {"decode_gqa_bf16": 1, "long_decode_bf16": 1, "mha_stress_f32": 1,
-              "chunk_gqa_bf16": 2, "chunk_gqa_f32": 2, "tiny_mixed_f32": 0}
+              "chunk_gqa_bf16": 2, "chunk_gqa_f32": 2, "tiny_mixed_f32": 1}
     for name, path in expect.items():
         w = WORKLOADS[name]
         d = kvc.KvcDims(w.B, w.Hq, w.Hk, w.Q, w.M, w.D, w.Dv)
@@ -409,6 +423,8 @@ PAGED_CASES = [
     (WORKLOADS["decode_gqa_bf16"].with_(name="paged_gen_b16", B=3, M=512,
                                         len_range=(0, 511)), 16),
     (chunk_wl(name="paged_gen_chunk_b32", B=2, Hq=8, Hk=2, Q=40, M=256, len_range=(0, 200)), 32),
+    (Workload(name="paged_small_d8", B=3, Hq=4, Hk=2, Q=3, M=512, D=8, Dv=8, dtype="f32",
+              len_range=(0, 500), n_rule="uniform"), 64),
     (WORKLOADS["tiny_mixed_f32"].with_(name="paged_gen_tiny"), 4),
     (WORKLOADS["tiny_mixed_f32"].with_(name="paged_gen_tiny_b1"), 1),
     (chunk_wl(name="paged_gen_d96", B=3, Hq=6, Hk=2, Q=3, M=384, D=96, Dv=80,
