@@ -306,6 +306,15 @@ int make_plan(const kvc_dims* d, int dtype, Plan* p) {
   p->P = p->decode
              ? compute_units() * p->decode->wgs_per_cu * (kvc::kDecodeWaves / p->rg_waves)
              : 0;
+  if (p->decode) {
+    // no more workers than the step can have chunks (every (b, KV head):
+    // its cached slots in chunks, plus one chunk of appended rows), rounded
+    // to whole workgroups: small steps launch a few workgroups, not a full
+    // grid of idle ones.  Busy workers are min(P, chunks) either way.
+    const int64_t most = d->B * d->Hk * ((d->M + p->decode->chunk - 1) / p->decode->chunk + 1);
+    const int64_t cap = (most + kvc::kDecodeWaves - 1) / kvc::kDecodeWaves * kvc::kDecodeWaves;
+    if (p->P > cap) p->P = cap;
+  }
   const int64_t row_tiles = R == 0 ? 1 : (R + kvc::kGenericRowsPerTile - 1) / kvc::kGenericRowsPerTile;
   if (!make_layout(d, R, kvc::kGenericChunk, false, 0, &p->generic)) return KVC_ERR_SHAPE;
   int64_t wgs;

@@ -19,10 +19,81 @@
 #pragma once
 
 #include "kvc_decode.h"
+#include "kvc_stream.h"
 
 namespace kvc {
 
 constexpr int kSmallChunk = kWave;  // one slot per lane
+
+// Max or sum over all 64 lanes, every lane getting the result: row
+// rotations (DPP) inside each 16-lane row, then the permlane16 / permlane32
+// swaps across rows (wave_reduce of kvc_stream.h for fp32; the same steps
+// on both halves of an fp64 value here).
+// The permlane swaps with both operands v: one result holds this lane's
+// value, the other its partner's (lane bit 4 or 5 flipped); both halves of
+// an fp64 value travel the same way, so (a, b) are whole values.
+template <bool ACROSS32>
+__device__ __forceinline__ void swap_pair(double v, double* a, double* b) {
+  const int2 w = __builtin_bit_cast(int2, v);
+  const uint32_t x = static_cast<uint32_t>(w.x), y = static_cast<uint32_t>(w.y);
+  const auto lo = ACROSS32 ? __builtin_amdgcn_permlane32_swap(x, x, false, false)
+                           : __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const auto hi = ACROSS32 ? __builtin_amdgcn_permlane32_swap(y, y, false, false)
+                           : __builtin_amdgcn_permlane16_swap(y, y, false, false);
+  *a = __builtin_bit_cast(double, make_int2(static_cast<int>(lo[0]), static_cast<int>(hi[0])));
+  *b = __builtin_bit_cast(double, make_int2(static_cast<int>(lo[1]), static_cast<int>(hi[1])));
+}
+template <bool MAX>
+__device__ __forceinline__ double small_reduce(double v) {
+  auto op = [](double x, double y) { return MAX ? (x > y ? x : y) : x + y; };
+  v = op(v, dpp<dpp_row_ror(8)>(v));
+  v = op(v, dpp<dpp_row_ror(4)>(v));
+  v = op(v, dpp<dpp_row_ror(2)>(v));
+  v = op(v, dpp<dpp_row_ror(1)>(v));
+  double a, b;
+  swap_pair<false>(v, &a, &b);
+  v = op(a, b);
+  swap_pair<true>(v, &a, &b);
+  return op(a, b);
+}
+template <bool MAX>
+__device__ __forceinline__ float small_reduce(float v) {
+  return wave_reduce<MAX>(v);
+}
+
+// Sum of N per-lane values over the wave, scattered: each exchange step
+// halves the values a lane holds (lanes with the step's lane bit set keep
+// the upper half and add their partner's copy of it), over lane bits 5
+// (permlane32 swap), 4 (permlane16 swap) and 3..0 (lane shuffles).  After
+// the six steps lane l holds values [l * N / 64, +N / 64) when N >= 64, or
+// value l / (64 / N) (summed over the lanes that share it) when N < 64.
+template <int N, int BIT>
+__device__ __forceinline__ void sum_scatter_step(float (&v)[N], int lane) {
+  constexpr int n = (N >> (5 - BIT)) > 0 ? (N >> (5 - BIT)) : 1;  // values held before the step
+  if constexpr (n > 1) {
+    constexpr int h = n / 2;
+    const bool up = (lane >> BIT) & 1;
+#pragma unroll
+    for (int i = 0; i < h; i++) {
+      if constexpr (BIT == 5) {
+        v[i] = sum_swap32(v[i], v[h + i]);
+      } else if constexpr (BIT == 4) {
+        v[i] = sum_swap16(v[i], v[h + i]);
+      } else {
+        const float give = up ? v[i] : v[h + i];
+        v[i] = (up ? v[h + i] : v[i]) + __shfl_xor(give, 1 << BIT);
+      }
+    }
+  } else {
+    v[0] += __shfl_xor(v[0], 1 << BIT);
+  }
+  if constexpr (BIT > 0) sum_scatter_step<N, BIT - 1>(v, lane);
+}
+template <int N>
+__device__ __forceinline__ void sum_scatter(float (&v)[N], int lane) {
+  static_assert(N >= 1 && (N & (N - 1)) == 0 && N <= 256, "power of two");
+  sum_scatter_step<N, 5>(v, lane);
+}
 
 template <typename T, int D, int DV, int ROWS>
 __global__ __launch_bounds__(kDecodeThreads) void attend_small_kernel(
@@ -209,9 +280,9 @@ __global__ __launch_bounds__(kDecodeThreads) void attend_small_kernel(
     for (int r = 0; r < ROWS; r++) {
       const int t = r % Q, g = r / Q;
       const bool row_ok = r < R && t < pos.n;
-      const Acc m_c = wave_max(s[r]);
+      const Acc m_c = small_reduce<true>(s[r]);
       const Acc p = s[r] == neg_inf ? Acc(0) : acc_exp(s[r] - m_c);
-      const Acc l_c = wave_sum(p);
+      const Acc l_c = small_reduce<false>(p);
       const Acc m_new = m_c > seg_m[r] ? m_c : seg_m[r];
       const Acc alpha = seg_m[r] == neg_inf ? Acc(0) : acc_exp(seg_m[r] - m_new);
       const Acc beta = m_c == neg_inf ? Acc(0) : acc_exp(m_c - m_new);
@@ -280,14 +351,28 @@ __global__ __launch_bounds__(kDecodeThreads) void attend_small_kernel(
     // ---- flush the segment when the KV head changes or at the end ----
     if (group_ends || x + 1 == x_end) {
       const int64_t seg = w + grp;
+      // the rows' contexts summed over the wave's slots, scattered over the
+      // lanes (value r * DV + i is row r, dim i)
+      constexpr int NO = ROWS * DV;
+      float flat[NO];
 #pragma unroll
-      for (int r = 0; r < ROWS; r++) {
+      for (int r = 0; r < ROWS; r++)
 #pragma unroll
         for (int i = 0; i < DV; i++) {
-          const float tot = wave_sum(o_acc[r][i]);
-          if (r < R && lane == (r * DV + i) % kWave) a.ws_seg_o[(seg * R + r) * DV + i] = tot;
+          flat[r * DV + i] = o_acc[r][i];
           o_acc[r][i] = 0.0f;
         }
+      sum_scatter<NO>(flat, lane);
+      constexpr int PER = NO >= kWave ? NO / kWave : 1;  // values a lane holds
+      constexpr int SHARE = NO >= kWave ? 1 : kWave / NO;  // lanes per value
+#pragma unroll
+      for (int k = 0; k < PER; k++) {
+        const int idx = NO >= kWave ? lane * PER + k : lane / SHARE;
+        const int r = idx / DV, i = idx % DV;
+        if (r < R && lane % SHARE == 0) a.ws_seg_o[(seg * R + r) * DV + i] = flat[k];
+      }
+#pragma unroll
+      for (int r = 0; r < ROWS; r++) {
         if (r < R && lane == 0) {
           double* ml = a.ws_seg_ml + (seg * R + r) * 2;
           ml[0] = static_cast<double>(seg_m[r]);
