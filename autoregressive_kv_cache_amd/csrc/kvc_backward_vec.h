@@ -38,6 +38,8 @@
 
 namespace kvc {
 
+typedef unsigned int bwd_u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kBwdVecChunks = 8;                    // 64-slot chunks per wave
 constexpr int kBwdVecSlots = 64 * kBwdVecChunks;    // slots per run (one wave)
 constexpr int kBwdVecRows = 4;                      // packed rows a wave holds
@@ -135,9 +137,14 @@ struct BwdVecWave {
       else if (j < len + n)
         src = static_cast<const uint16_t*>(fresh) + (grp * a.Q + (j - len)) * D;
 #pragma unroll
-      for (int h = 0; h < NH; h++)
-        v[k * NH + h] = src ? *reinterpret_cast<const uint4*>(src + h * 64 + (lane >> 3) * 8)
-                            : make_uint4(0u, 0u, 0u, 0u);
+      for (int h = 0; h < NH; h++) {
+        // read once per kernel: non-temporal, so they do not displace
+        // what is read again
+        const bwd_u32x4 w = src ? __builtin_nontemporal_load(reinterpret_cast<const bwd_u32x4*>(
+                                      src + h * 64 + (lane >> 3) * 8))
+                                : bwd_u32x4{0u, 0u, 0u, 0u};
+        v[k * NH + h] = make_uint4(w.x, w.y, w.z, w.w);
+      }
     }
   }
   // lane l's slot of the chunk at jb and its visibility for packed row r
