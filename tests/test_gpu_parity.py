@@ -700,6 +700,8 @@ REATT_CASES = [
     ("f32", 4, 8, 8, 4, 300, 64, 32),
     # head sizes without a decode kernel: the generic kernel
     ("bf16", 4, 6, 2, 3, 200, 96, 80),
+    # a small head: the one-slot-per-lane decode kernel, read only
+    ("bf16", 4, 8, 2, 2, 300, 32, 32),
 ]
 
 
