@@ -114,16 +114,32 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-// Stores through a scalar descriptor (default cache policy): the address is
-// the descriptor's base plus a 32-bit lane offset, so no 64-bit per-lane
-// address has to stay live across the kernel's loop.
+// Workspace stores through a scalar descriptor: the address is the
+// descriptor's base plus a 32-bit lane offset, so no 64-bit per-lane address
+// has to stay live across the kernel's loop.  POLICY is the store's cache
+// operand: 0 (the default: the line stays in the XCD's L2 until it is
+// evicted or the kernel ends) or kDeviceScope (the sc1 bit: device-scope
+// coherence, so the store is written through the L2 as it happens).
+constexpr int kDeviceScope = 16;
+template <int V>
+struct StorePolicy {
+  static constexpr int value = V;
+};
+template <int POLICY>
 __device__ __forceinline__ void ws_st16(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4& v) {
   const u32x4 w = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(w, r, static_cast<int>(off), 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, static_cast<int>(off), 0, POLICY);
 }
+template <int POLICY>
 __device__ __forceinline__ void ws_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(off), 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(off), 0, POLICY);
 }
+// Above this many bytes of exp values per launch the workspace stores are
+// written through (kDeviceScope).  Measured: at 13.6 MB (B = 32, 8192 slots,
+// 4 rows per KV head) keeping the lines in L2 is 1.5 us faster per step; at
+// 22 MB and more (twice the batch, twice the capacity, 8 rows, 131072
+// slots) writing through is 2-4 % faster, 12 us per step at 131072 slots.
+constexpr int64_t kStashWriteThroughBytes = int64_t{16} << 20;
 
 template <int D, int DV, int ROWS, bool Q1, bool OOP, bool FUSED, bool PAGED, bool GROUPS>
 __global__ __launch_bounds__(kDecodeThreads)
@@ -228,6 +244,7 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
   }
   const int64_t w = blockIdx.x * static_cast<int64_t>(kDecodeWaves / RGW) + wave / RGW;
   if (w >= Pw || (GROUPS && NR <= 0)) return;
+  const bool write_through = Nc * R * C * 2 > kStashWriteThroughBytes;
   const int32_t lead = effective_lead(Nc, Pw, a.lead);
   const int64_t x_begin = worker_start(w, Nc, Pw, lead), x_end = worker_start(w + 1, Nc, Pw, lead);
   if (x_begin >= x_end) return;
@@ -366,35 +383,39 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
       return;
     }
     wave_lds_sync();
-    // exp values: ns chunks of R rows of C bf16 in the workspace; with row
-    // groups, this group's NR rows of each (one contiguous run per chunk)
-    if constexpr (GROUPS) {
-      const int pieces = ns * NR * (C / 8);
-      const __amdgpu_buffer_rsrc_t dx =
-          make_rsrc(a.ws_pexp + xs0 * R * C, static_cast<uint32_t>(ns * R * C) * 2u);
-      for (int p = lane; p < pieces; p += kWave) {
-        const int i = p / (NR * (C / 8)), rr = (p / (C / 8)) % NR, s8 = p % (C / 8);
-        ws_st16(dx, static_cast<uint32_t>(((i * R + r0 + rr) * (C / 8) + s8) * 16),
-                *reinterpret_cast<const uint4*>(&xs[i][rr * C + s8 * 8]));
+    auto put = [&](auto pol) {
+      constexpr int POL = decltype(pol)::value;
+      // exp values: ns chunks of R rows of C bf16 in the workspace; with row
+      // groups, this group's NR rows of each (one contiguous run per chunk)
+      if constexpr (GROUPS) {
+        const int pieces = ns * NR * (C / 8);
+        const __amdgpu_buffer_rsrc_t dx =
+            make_rsrc(a.ws_pexp + xs0 * R * C, static_cast<uint32_t>(ns * R * C) * 2u);
+        for (int p = lane; p < pieces; p += kWave) {
+          const int i = p / (NR * (C / 8)), rr = (p / (C / 8)) % NR, s8 = p % (C / 8);
+          ws_st16<POL>(dx, static_cast<uint32_t>(((i * R + r0 + rr) * (C / 8) + s8) * 16),
+                  *reinterpret_cast<const uint4*>(&xs[i][rr * C + s8 * 8]));
+        }
+        const __amdgpu_buffer_rsrc_t dr =
+            make_rsrc(a.ws_cref + xs0 * R, static_cast<uint32_t>(ns * R) * 4u);
+        for (int p = lane; p < ns * NR; p += kWave)
+          ws_st4<POL>(dr, static_cast<uint32_t>((p / NR) * R + r0 + p % NR) * 4u, xr[p / NR][p % NR]);
+      } else {
+        const int pieces = ns * R * (C / 8);
+        const __amdgpu_buffer_rsrc_t dx =
+            make_rsrc(a.ws_pexp + xs0 * R * C, static_cast<uint32_t>(pieces) * 16u);
+        for (int p = lane; p < pieces; p += kWave) {
+          const int i = p / (R * (C / 8)), rr = (p / (C / 8)) % R, s8 = p % (C / 8);
+          ws_st16<POL>(dx, static_cast<uint32_t>(p) * 16u,
+                  *reinterpret_cast<const uint4*>(&xs[i][rr * C + s8 * 8]));
+        }
+        const __amdgpu_buffer_rsrc_t dr =
+            make_rsrc(a.ws_cref + xs0 * R, static_cast<uint32_t>(ns * R) * 4u);
+        for (int p = lane; p < ns * R; p += kWave)
+          ws_st4<POL>(dr, static_cast<uint32_t>(p) * 4u, xr[p / R][p % R]);
       }
-      const __amdgpu_buffer_rsrc_t dr =
-          make_rsrc(a.ws_cref + xs0 * R, static_cast<uint32_t>(ns * R) * 4u);
-      for (int p = lane; p < ns * NR; p += kWave)
-        ws_st4(dr, static_cast<uint32_t>((p / NR) * R + r0 + p % NR) * 4u, xr[p / NR][p % NR]);
-    } else {
-      const int pieces = ns * R * (C / 8);
-      const __amdgpu_buffer_rsrc_t dx =
-          make_rsrc(a.ws_pexp + xs0 * R * C, static_cast<uint32_t>(pieces) * 16u);
-      for (int p = lane; p < pieces; p += kWave) {
-        const int i = p / (R * (C / 8)), rr = (p / (C / 8)) % R, s8 = p % (C / 8);
-        ws_st16(dx, static_cast<uint32_t>(p) * 16u,
-                *reinterpret_cast<const uint4*>(&xs[i][rr * C + s8 * 8]));
-      }
-      const __amdgpu_buffer_rsrc_t dr =
-          make_rsrc(a.ws_cref + xs0 * R, static_cast<uint32_t>(ns * R) * 4u);
-      for (int p = lane; p < ns * R; p += kWave)
-        ws_st4(dr, static_cast<uint32_t>(p) * 4u, xr[p / R][p % R]);
-    }
+    };
+    if (write_through) put(StorePolicy<kDeviceScope>{}); else put(StorePolicy<0>{});
     xs0 += ns;
     ns = 0;
   };
@@ -615,28 +636,31 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
       // descriptors and are not stored
       const __amdgpu_buffer_rsrc_t so_rs =
           make_rsrc(a.ws_seg_o + (seg * R + r0) * DV, static_cast<uint32_t>(NR * DV) * 4u);
-      if (rs == 0) {
+      const __amdgpu_buffer_rsrc_t sm_rs =
+          make_rsrc(a.ws_seg2 + (seg * R + r0) * 2, static_cast<uint32_t>(NR * 2) * 4u);
+      float mv = mref[0], lv = l_seg[0];
 #pragma unroll
-        for (int r = 0; r < ROWS; r++) {
-          const uint32_t off = static_cast<uint32_t>(r * DV + lane * 8) * 4u;
-          ws_st16(so_rs, off, make_uint4(__float_as_uint(o_acc[r][0]), __float_as_uint(o_acc[r][1]),
-                                         __float_as_uint(o_acc[r][2]), __float_as_uint(o_acc[r][3])));
-          ws_st16(so_rs, off + 16u,
-                  make_uint4(__float_as_uint(o_acc[r][4]), __float_as_uint(o_acc[r][5]),
-                             __float_as_uint(o_acc[r][6]), __float_as_uint(o_acc[r][7])));
-        }
+      for (int r = 1; r < ROWS; r++) {
+        mv = (lane >> 1) == r ? mref[r] : mv;
+        lv = (lane >> 1) == r ? l_seg[r] : lv;
       }
-      {
-        const __amdgpu_buffer_rsrc_t sm_rs =
-            make_rsrc(a.ws_seg2 + (seg * R + r0) * 2, static_cast<uint32_t>(NR * 2) * 4u);
-        float mv = mref[0], lv = l_seg[0];
+      auto put = [&](auto pol) {
+        constexpr int POL = decltype(pol)::value;
+        if (rs == 0) {
 #pragma unroll
-        for (int r = 1; r < ROWS; r++) {
-          mv = (lane >> 1) == r ? mref[r] : mv;
-          lv = (lane >> 1) == r ? l_seg[r] : lv;
+          for (int r = 0; r < ROWS; r++) {
+            const uint32_t off = static_cast<uint32_t>(r * DV + lane * 8) * 4u;
+            ws_st16<POL>(so_rs, off,
+                         make_uint4(__float_as_uint(o_acc[r][0]), __float_as_uint(o_acc[r][1]),
+                                    __float_as_uint(o_acc[r][2]), __float_as_uint(o_acc[r][3])));
+            ws_st16<POL>(so_rs, off + 16u,
+                         make_uint4(__float_as_uint(o_acc[r][4]), __float_as_uint(o_acc[r][5]),
+                                    __float_as_uint(o_acc[r][6]), __float_as_uint(o_acc[r][7])));
+          }
         }
-        if (lane < 2 * ROWS) ws_st4(sm_rs, static_cast<uint32_t>(lane) * 4u, lane & 1 ? lv : mv);
-      }
+        if (lane < 2 * ROWS) ws_st4<POL>(sm_rs, static_cast<uint32_t>(lane) * 4u, lane & 1 ? lv : mv);
+      };
+      if (write_through) put(StorePolicy<kDeviceScope>{}); else put(StorePolicy<0>{});
 #pragma unroll
       for (int r = 0; r < ROWS; r++) {
         mref[r] = kRefFloor;
