@@ -134,11 +134,14 @@ template <int POLICY>
 __device__ __forceinline__ void ws_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(off), 0, POLICY);
 }
-// Above this many bytes of exp values per launch the workspace stores are
-// written through (kDeviceScope).  Measured: at 13.6 MB (B = 32, 8192 slots,
-// 4 rows per KV head) keeping the lines in L2 is 1.5 us faster per step; at
-// 22 MB and more (twice the batch, twice the capacity, 8 rows, 131072
-// slots) writing through is 2-4 % faster, 12 us per step at 131072 slots.
+// The workspace stores are written through (kDeviceScope) when a KV head
+// packs 8 rows or more, or when the launch's exp values pass this many
+// bytes; otherwise they keep the default policy.  Measured per step: with 4
+// rows per KV head at 13.6 MB (B = 32, 8192 slots) the default is 2.5 us
+// faster, and so it is for the paged step and re-attention there; from
+// 22 MB on (twice the batch, twice the capacity, 131072 slots) writing
+// through is 2-4 % faster; with 8 rows (16384 or 131072 slots) and 12 rows
+// it is up to 4 % faster, and never slower.
 constexpr int64_t kStashWriteThroughBytes = int64_t{16} << 20;
 
 template <int D, int DV, int ROWS, bool Q1, bool OOP, bool FUSED, bool PAGED, bool GROUPS>
@@ -244,7 +247,7 @@ __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<ROWS>()))) void attend_
   }
   const int64_t w = blockIdx.x * static_cast<int64_t>(kDecodeWaves / RGW) + wave / RGW;
   if (w >= Pw || (GROUPS && NR <= 0)) return;
-  const bool write_through = Nc * R * C * 2 > kStashWriteThroughBytes;
+  const bool write_through = R >= 8 || Nc * R * C * 2 > kStashWriteThroughBytes;
   const int32_t lead = effective_lead(Nc, Pw, a.lead);
   const int64_t x_begin = worker_start(w, Nc, Pw, lead), x_end = worker_start(w + 1, Nc, Pw, lead);
   if (x_begin >= x_end) return;
