@@ -60,10 +60,15 @@ const BwdEntry kBwdTable[] = {
 // The vector-unit kernels of kvc_backward_vec.h: bf16, D = Dv in {64, 128},
 // at most kBwdVecRows packed rows per KV head.
 // which: 0 statistics, 1 dq, 2 slot gradients
+// (the slot pass runs over kBwdSlotPassSlots-slot runs: at most the 64-slot
+// chunk count the host checks bound for every grid)
 template <int D>
 void launch_bwd_vec(const kvc::BwdArgs& a, hipStream_t s, int which) {
-  const unsigned blocks = static_cast<unsigned>(
-      (a.B * a.Hk * a.nchunk + kvc::kBwdThreads / kvc::kWave - 1) / (kvc::kBwdThreads / kvc::kWave));
+  constexpr int64_t kWavesPerBlock = kvc::kBwdThreads / kvc::kWave;
+  const int64_t runs =
+      which == 2 ? (a.M + kvc::kBwdSlotPassSlots - 1) / kvc::kBwdSlotPassSlots : a.nchunk;
+  const unsigned blocks =
+      static_cast<unsigned>((a.B * a.Hk * runs + kWavesPerBlock - 1) / kWavesPerBlock);
   if (which == 0)
     hipLaunchKernelGGL((kvc::bwd_vstats_kernel<D>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
   else if (which == 1)

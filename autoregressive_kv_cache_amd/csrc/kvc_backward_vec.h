@@ -16,7 +16,8 @@
 // l's value for every packed row.  bwd_vslot computes no dot product and
 // gives each lane 8 dims of one slot instead (see there).
 //
-// Kernels (one wave per (batch row, KV head, run of kBwdVecSlots slots)):
+// Kernels (one wave per (batch row, KV head, run of kBwdVecSlots slots);
+// bwd_vslot takes runs of kBwdSlotPassSlots):
 //   bwd_vstats: scores s = scale q.K'_j and dP_j = dA_j + dO.V'_j of the
 //     run's visible slots, and per packed row the run's max m, sum of
 //     e^(s-m) and sum of e^(s-m) dP (the partials bwd_rows_kernel merges);
@@ -43,6 +44,15 @@ typedef unsigned int bwd_u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBwdVecChunks = 8;                    // 64-slot chunks per wave
 constexpr int kBwdVecSlots = 64 * kBwdVecChunks;    // slots per run (one wave)
 constexpr int kBwdVecRows = 4;                      // packed rows a wave holds
+// The slot pass in one-chunk runs: it has a wave for every run of the cache
+// (pass-through runs included), and more, shorter waves spread its end over
+// the chip.  Measured at B = 32, Hk = 8, 8192 slots: the pass took 517 us
+// with 512-slot runs, 447 with 256 and 424 with 128, and the whole backward
+// call 760 us with 128-slot runs against 730 with 64.  The statistics and
+// dq passes, which load every packed row's q and dO per wave, were slower
+// with shorter runs (208 -> 232 -> 273 us) and keep 512.
+constexpr int kBwdSlotPassChunks = 1;
+constexpr int kBwdSlotPassSlots = 64 * kBwdSlotPassChunks;
 
 // Dot products of 8-slot groups k = 0..7 (pieces kb[k * NH + h]) with the
 // ROWS row slices qv[r][h], finished so that lane l returns slot l's values.
@@ -95,13 +105,15 @@ struct BwdVecWave {
   static constexpr int NH = D / 64, ROWS = kBwdVecRows;
   const BwdArgs& a;
   int lane;
-  int64_t grp, b, kvh, j0, len, n;
+  int64_t grp, b, kvh, j0, len, n, run_slots;
   int Q;
 
-  __device__ BwdVecWave(const BwdArgs& args, int64_t wave_id, int64_t nrun)
+  __device__ BwdVecWave(const BwdArgs& args, int64_t wave_id, int64_t nrun,
+                        int64_t slots_per_run = kBwdVecSlots)
       : a(args), lane(static_cast<int>(threadIdx.x % kWave)) {
+    run_slots = slots_per_run;
     grp = wave_id / nrun;
-    j0 = (wave_id % nrun) * kBwdVecSlots;
+    j0 = (wave_id % nrun) * slots_per_run;
     b = grp / a.Hk;
     kvh = grp % a.Hk;
     Q = static_cast<int>(a.Q);
@@ -194,7 +206,7 @@ __device__ __forceinline__ void bwd_vec_chunk(const BwdVecWave<D>& W, int64_t jb
 template <int D>
 __device__ void bwd_vec_pass_run(const BwdVecWave<D>& W) {
   const BwdArgs& a = W.a;
-  const int64_t j1 = W.j0 + kBwdVecSlots < a.M ? W.j0 + kBwdVecSlots : a.M;
+  const int64_t j1 = W.j0 + W.run_slots < a.M ? W.j0 + W.run_slots : a.M;
   const int64_t pieces = (j1 - W.j0) * D / 8, base = (W.grp * a.M + W.j0) * D;
 #pragma unroll
   for (int t = 0; t < 2; t++) {
@@ -433,8 +445,9 @@ bwd_vslot_kernel(BwdArgs a) {
   constexpr int LPS = D / 8, SPI = kWave / LPS, NI = 64 / SPI;  // lanes per slot, slots per step
   constexpr int kSlotBatch = 8;  // steps whose loads are issued together
   const int64_t wave_id = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
-  if (wave_id >= a.B * a.Hk * a.nchunk) return;
-  BwdVecWave<D> W(a, wave_id, a.nchunk);
+  const int64_t nrun = (a.M + kBwdSlotPassSlots - 1) / kBwdSlotPassSlots;
+  if (wave_id >= a.B * a.Hk * nrun) return;
+  BwdVecWave<D> W(a, wave_id, nrun, kBwdSlotPassSlots);
   bwd_row_info(a, W.b, &W.len, &W.n);
   const int lane = W.lane;
   if (W.j0 == 0) bwd_vec_zero_new_rows<D>(W);
@@ -457,7 +470,7 @@ bwd_vslot_kernel(BwdArgs a) {
   float rm[ROWS], rinv[ROWS], rc[ROWS];
   bwd_vec_row_stats<D>(W, rm, rinv, rc);
 #pragma unroll 1
-  for (int c = 0; c < kBwdVecChunks; c++) {
+  for (int c = 0; c < kBwdSlotPassChunks; c++) {
     const int64_t jb = W.j0 + static_cast<int64_t>(c) * 64;
     if (jb >= a.M) break;
     float P[ROWS], dS[ROWS];
