@@ -179,7 +179,7 @@ int64_t compute_units() {
 constexpr int64_t kCombineSlots = 4096;
 constexpr int64_t kCombineSlotsCopy = 512;
 
-// Matrix-core chunk path: more than 8 packed rows per KV head.
+// Matrix-core chunk path: kChunkMinRows (16) packed rows per KV head or more.
 struct ChunkEntry {
   int dtype;
   int64_t D, Dv;

@@ -137,12 +137,13 @@ __device__ __forceinline__ void ws_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, f
 // The workspace stores are written through (kDeviceScope) when a KV head
 // packs 8 rows or more, or when the launch's exp values pass this many
 // bytes; otherwise they keep the default policy.  Measured per step: with 4
-// rows per KV head at 13.6 MB (B = 32, 8192 slots) the default is 2.5 us
-// faster, and so it is for the paged step and re-attention there; from
-// 22 MB on (twice the batch, twice the capacity, 131072 slots) writing
-// through is 2-4 % faster; with 8 rows (16384 or 131072 slots) and 12 rows
-// it is up to 4 % faster, and never slower.
-constexpr int64_t kStashWriteThroughBytes = int64_t{16} << 20;
+// rows per KV head and 8.2 MiB of exp values (B = 32, 8192 slots) the
+// default is 2.5 us faster, and so it is for the paged step and
+// re-attention there; from 16.3 MiB on (twice the batch; twice the
+// capacity: 18 MiB; 131072 slots: 24 MiB) writing through is 2-4 % faster;
+// with 8 rows (16384 or 131072 slots) and 12 rows it is up to 4 % faster,
+// and never slower.  The bound sits between the measured sizes.
+constexpr int64_t kStashWriteThroughBytes = int64_t{12} << 20;
 
 template <int D, int DV, int ROWS, bool Q1, bool OOP, bool FUSED, bool PAGED, bool GROUPS>
 __global__ __launch_bounds__(kDecodeThreads)

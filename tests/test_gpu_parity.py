@@ -110,6 +110,20 @@ def test_decode_gqa_full_size_inplace_and_oop():
         full_check(wl, 0, mode, gen_device=DEV)
 
 
+def test_decode_write_through_full_check():
+    """The decode step at twice the batch (B=64, 4 packed rows per KV head):
+    its exp values pass 12 MiB per launch (16.3 MiB at seed 0), so the stream
+    kernel writes its workspace through the L2 where the B=32 step (8.2 MiB)
+    keeps the default policy.
+    Every output against the oracle, in place and out of place."""
+    wl = WORKLOADS["decode_gqa_bf16"].with_(name="decode_gqa_bf16_b64", B=64)
+    lengths, n = draw_lengths_and_counts(wl, 0)
+    chunks = sum(wl.Hk * (-(-int(l) // 64) + (1 if k > 0 else 0)) for l, k in zip(lengths, n))
+    assert chunks * 4 * 64 * 2 > 12 << 20  # 4 rows of 64 bf16 exp values per chunk
+    for mode in ("inplace", "oop"):
+        full_check(wl, 0, mode, gen_device=DEV)
+
+
 def test_long_decode_share_full_check():
     """One GPU's share of the slot-sharded long decode (M = 16384 of 131072,
     64 query heads over 8 KV heads): every output against the oracle, in
