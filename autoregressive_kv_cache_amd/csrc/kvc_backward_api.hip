@@ -58,11 +58,12 @@ const BwdEntry kBwdTable[] = {
 };
 #undef KVC_BWD
 // The vector-unit kernels of kvc_backward_vec.h: bf16, D = Dv in {64, 128},
-// at most kBwdVecRows packed rows per KV head.
+// at most kBwdVecRows packed rows per KV head (waves of 4 rows up to 4, of 8
+// above).
 // which: 0 statistics, 1 dq, 2 slot gradients
 // (the slot pass runs over kBwdSlotPassSlots-slot runs: at most the 64-slot
 // chunk count the host checks bound for every grid)
-template <int D>
+template <int D, int ROWS>
 void launch_bwd_vec(const kvc::BwdArgs& a, hipStream_t s, int which) {
   constexpr int64_t kWavesPerBlock = kvc::kBwdThreads / kvc::kWave;
   const int64_t runs =
@@ -70,11 +71,11 @@ void launch_bwd_vec(const kvc::BwdArgs& a, hipStream_t s, int which) {
   const unsigned blocks =
       static_cast<unsigned>((a.B * a.Hk * runs + kWavesPerBlock - 1) / kWavesPerBlock);
   if (which == 0)
-    hipLaunchKernelGGL((kvc::bwd_vstats_kernel<D>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
+    hipLaunchKernelGGL((kvc::bwd_vstats_kernel<D, ROWS>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
   else if (which == 1)
-    hipLaunchKernelGGL((kvc::bwd_vdq_kernel<D>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
+    hipLaunchKernelGGL((kvc::bwd_vdq_kernel<D, ROWS>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((kvc::bwd_vslot_kernel<D>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
+    hipLaunchKernelGGL((kvc::bwd_vslot_kernel<D, ROWS>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
 }
 // The generic kernels of kvc_backward_generic.h: any head sizes with
 // D + Dv <= kBwdGenAccDoubles, any element-aligned buffers.
@@ -248,7 +249,10 @@ int kvc_step_backward(const kvc_dims* dims, int dtype, int has_scale, double sca
   }
   if (vec) {  // statistics, rows, dq partials, slot gradients, dq
     auto run = [&](int which) {
-      d->D == 128 ? launch_bwd_vec<128>(a, s, which) : launch_bwd_vec<64>(a, s, which);
+      if (a.R <= 4)
+        d->D == 128 ? launch_bwd_vec<128, 4>(a, s, which) : launch_bwd_vec<64, 4>(a, s, which);
+      else
+        d->D == 128 ? launch_bwd_vec<128, 8>(a, s, which) : launch_bwd_vec<64, 8>(a, s, which);
     };
     if (rows > 0) {
       run(0);

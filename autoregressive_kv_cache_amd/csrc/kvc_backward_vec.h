@@ -1,11 +1,12 @@
 // kvc_backward_vec.h -- vector-unit backward of the step for decode-shaped
-// heads: bf16 tensors, D = Dv in {64, 128}, at most 4 packed rows per KV
-// head.  Same gradients as kvc_backward.h (see there for the formulas, from
-// "Autoregressive KV-cache append and causal attention", the workspace
-// note); what changes is the arithmetic's shape.  With 4 rows a head's
-// products are matrix-vector products: the 16-row fp64 matrix-core tiles of
-// kvc_backward.h would be three quarters padding, so here every product is
-// a per-slot dot product on the vector units, in fp32 (bf16 inputs widen
+// heads: bf16 tensors, D = Dv in {64, 128}, at most 8 packed rows per KV
+// head (waves of 4 rows for up to 4, of 8 above).  Same gradients as
+// kvc_backward.h (see there for the formulas, from "Autoregressive KV-cache
+// append and causal attention", the workspace note); what changes is the
+// arithmetic's shape.  With so few rows a head's products are
+// matrix-vector products: the 16-row fp64 matrix-core tiles of
+// kvc_backward.h would be half padding or more, so here every product is a
+// per-slot dot product on the vector units, in fp32 (bf16 inputs widen
 // exactly; the row statistics are merged in fp64 by bwd_rows_kernel).
 //
 // Layout of bwd_vstats and bwd_vdq (as attend_stream_kernel, kvc_stream.h):
@@ -43,7 +44,7 @@ typedef unsigned int bwd_u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBwdVecChunks = 8;                    // 64-slot chunks per wave
 constexpr int kBwdVecSlots = 64 * kBwdVecChunks;    // slots per run (one wave)
-constexpr int kBwdVecRows = 4;                      // packed rows a wave holds
+constexpr int kBwdVecRows = 8;                      // packed rows a wave holds, at most
 // The slot pass in one-chunk runs: it has a wave for every run of the cache
 // (pass-through runs included), and more, shorter waves spread its end over
 // the chip.  Measured at B = 32, Hk = 8, 8192 slots: the pass took 517 us
@@ -100,9 +101,9 @@ __device__ __forceinline__ void lk8_dots(const uint4 (&kb)[8 * NH], const uint4 
 
 // What the two kernels share for one wave: its head, its run, the rows'
 // q and dO slices, the LK8 loads of K' / V' / the returned cache's gradient.
-template <int D>
+template <int D, int ROWS>
 struct BwdVecWave {
-  static constexpr int NH = D / 64, ROWS = kBwdVecRows;
+  static constexpr int NH = D / 64;
   const BwdArgs& a;
   int lane;
   int64_t grp, b, kvh, j0, len, n, run_slots;
@@ -171,13 +172,13 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 
 // Scores (natural units, -inf where not visible) and dP of the chunk at jb
 // for lane l's slot.
-template <int D>
-__device__ __forceinline__ void bwd_vec_chunk(const BwdVecWave<D>& W, int64_t jb,
-                                              const uint4 (&qv)[kBwdVecRows][D / 64],
-                                              const uint4 (&dov)[kBwdVecRows][D / 64],
+template <int D, int ROWS>
+__device__ __forceinline__ void bwd_vec_chunk(const BwdVecWave<D, ROWS>& W, int64_t jb,
+                                              const uint4 (&qv)[ROWS][D / 64],
+                                              const uint4 (&dov)[ROWS][D / 64],
                                               uint4 (&kb)[8 * (D / 64)],
-                                              float (&s)[kBwdVecRows], float (&dp)[kBwdVecRows]) {
-  constexpr int NH = D / 64, ROWS = kBwdVecRows;
+                                              float (&s)[ROWS], float (&dp)[ROWS]) {
+  constexpr int NH = D / 64;
   const BwdArgs& a = W.a;
   {
     uint4 vb[8 * NH];
@@ -203,8 +204,8 @@ __device__ __forceinline__ void bwd_vec_chunk(const BwdVecWave<D>& W, int64_t jb
 // A run with no visible slot (all of its slots at or past len + n): the
 // gradients of its slots are the returned cache's, passed through (zeros
 // for a null one); a plain copy, eight 16-byte pieces in flight per lane.
-template <int D>
-__device__ void bwd_vec_pass_run(const BwdVecWave<D>& W) {
+template <int D, int ROWS>
+__device__ void bwd_vec_pass_run(const BwdVecWave<D, ROWS>& W) {
   const BwdArgs& a = W.a;
   const int64_t j1 = W.j0 + W.run_slots < a.M ? W.j0 + W.run_slots : a.M;
   const int64_t pieces = (j1 - W.j0) * D / 8, base = (W.grp * a.M + W.j0) * D;
@@ -231,8 +232,8 @@ __device__ void bwd_vec_pass_run(const BwdVecWave<D>& W) {
 }
 
 // The appended rows past n get zero gradients (done by each head's first run).
-template <int D>
-__device__ void bwd_vec_zero_new_rows(const BwdVecWave<D>& W) {
+template <int D, int ROWS>
+__device__ void bwd_vec_zero_new_rows(const BwdVecWave<D, ROWS>& W) {
   const BwdArgs& a = W.a;
   for (int64_t i = W.n * D + W.lane * 8; i < a.Q * D; i += kWave * 8) {
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.g_new_key) + W.grp * a.Q * D + i) =
@@ -242,13 +243,13 @@ __device__ void bwd_vec_zero_new_rows(const BwdVecWave<D>& W) {
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void
+template <int D, int ROWS>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(ROWS <= 4 ? 2 : 1))) void
 bwd_vstats_kernel(BwdArgs a) {
-  constexpr int NH = D / 64, ROWS = kBwdVecRows;
+  constexpr int NH = D / 64;
   const int64_t wave_id = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
   if (wave_id >= a.B * a.Hk * a.nchunk) return;
-  BwdVecWave<D> W(a, wave_id, a.nchunk);
+  BwdVecWave<D, ROWS> W(a, wave_id, a.nchunk);
   bwd_row_info(a, W.b, &W.len, &W.n);
   if (W.n == 0 || W.j0 >= W.len + W.n) return;  // no visible slot: bwd_rows reads nothing here
   uint4 qv[ROWS][NH], dov[ROWS][NH];
@@ -267,7 +268,7 @@ bwd_vstats_kernel(BwdArgs a) {
     if (jb >= W.len + W.n) break;
     uint4 kb[8 * NH];
     float s[ROWS], dp[ROWS];
-    bwd_vec_chunk<D>(W, jb, qv, dov, kb, s, dp);
+    bwd_vec_chunk<D, ROWS>(W, jb, qv, dov, kb, s, dp);
     {  // for the other kernels: (s, dP) of the slot, -inf where not visible
       const int64_t j = jb + W.lane;
 #pragma unroll
@@ -314,22 +315,22 @@ bwd_vstats_kernel(BwdArgs a) {
 
 // P and dS of packed row r at lane l's slot of the chunk at jb, from the
 // scores and dP bwd_vstats_kernel stored and the merged row statistics.
-template <int D>
-__device__ __forceinline__ void bwd_vec_pds(const BwdVecWave<D>& W, int64_t jb,
-                                            const float (&rm)[kBwdVecRows],
-                                            const float (&rinv)[kBwdVecRows],
-                                            const float (&rc)[kBwdVecRows],
-                                            float (&P)[kBwdVecRows], float (&dS)[kBwdVecRows]) {
+template <int D, int ROWS>
+__device__ __forceinline__ void bwd_vec_pds(const BwdVecWave<D, ROWS>& W, int64_t jb,
+                                            const float (&rm)[ROWS],
+                                            const float (&rinv)[ROWS],
+                                            const float (&rc)[ROWS],
+                                            float (&P)[ROWS], float (&dS)[ROWS]) {
   const BwdArgs& a = W.a;
   const int64_t j = jb + W.lane;
-  float2 sd[kBwdVecRows];
+  float2 sd[ROWS];
 #pragma unroll
-  for (int r = 0; r < kBwdVecRows; r++)
+  for (int r = 0; r < ROWS; r++)
     sd[r] = (r < a.R && j < W.len + W.n)
                 ? *reinterpret_cast<const float2*>(a.ws_sdp + ((W.grp * a.R + r) * a.M + j) * 2)
                 : make_float2(-INFINITY, 0.0f);
 #pragma unroll
-  for (int r = 0; r < kBwdVecRows; r++) {
+  for (int r = 0; r < ROWS; r++) {
     P[r] = sd[r].x == -INFINITY ? 0.0f : expf(sd[r].x - rm[r]) * rinv[r];
     dS[r] = P[r] * (sd[r].y - rc[r]);
   }
@@ -337,13 +338,13 @@ __device__ __forceinline__ void bwd_vec_pds(const BwdVecWave<D>& W, int64_t jb,
 
 // The merged statistics of the wave's rows (bwd_rows_kernel): max, 1 / sum
 // and sum P dP, one value per wave each (scalar registers).
-template <int D>
-__device__ __forceinline__ void bwd_vec_row_stats(const BwdVecWave<D>& W, float (&rm)[kBwdVecRows],
-                                                  float (&rinv)[kBwdVecRows],
-                                                  float (&rc)[kBwdVecRows]) {
+template <int D, int ROWS>
+__device__ __forceinline__ void bwd_vec_row_stats(const BwdVecWave<D, ROWS>& W, float (&rm)[ROWS],
+                                                  float (&rinv)[ROWS],
+                                                  float (&rc)[ROWS]) {
   const BwdArgs& a = W.a;
 #pragma unroll
-  for (int r = 0; r < kBwdVecRows; r++) {
+  for (int r = 0; r < ROWS; r++) {
     rm[r] = 0.0f;
     rinv[r] = 0.0f;
     rc[r] = 0.0f;
@@ -362,18 +363,18 @@ __device__ __forceinline__ void bwd_vec_row_stats(const BwdVecWave<D>& W, float 
 // dq: per visible run, dq_r = scale sum_j dS_jr K'_j over the run's slots
 // (K' in the LK8 layout: lane l sums its 8 slots of each chunk for its dims,
 // then the 8 lanes that hold the same dims add up).
-template <int D>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void
+template <int D, int ROWS>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(ROWS <= 4 ? 2 : 1))) void
 bwd_vdq_kernel(BwdArgs a) {
-  constexpr int NH = D / 64, ROWS = kBwdVecRows;
+  constexpr int NH = D / 64;
   const int64_t wave_id = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
   if (wave_id >= a.B * a.Hk * a.nchunk) return;
-  BwdVecWave<D> W(a, wave_id, a.nchunk);
+  BwdVecWave<D, ROWS> W(a, wave_id, a.nchunk);
   bwd_row_info(a, W.b, &W.len, &W.n);
   if (W.n == 0 || W.j0 >= W.len + W.n) return;  // bwd_dq reads no partial of this run
   const int lane = W.lane;
   float rm[ROWS], rinv[ROWS], rc[ROWS];
-  bwd_vec_row_stats<D>(W, rm, rinv, rc);
+  bwd_vec_row_stats<D, ROWS>(W, rm, rinv, rc);
   float dq[ROWS][NH][8];
 #pragma unroll
   for (int r = 0; r < ROWS; r++)
@@ -388,7 +389,7 @@ bwd_vdq_kernel(BwdArgs a) {
     uint4 kb[8 * NH];
     W.load_kv(a.kc, a.new_key, jb, kb);
     float P[ROWS], dS[ROWS];
-    bwd_vec_pds<D>(W, jb, rm, rinv, rc, P, dS);
+    bwd_vec_pds<D, ROWS>(W, jb, rm, rinv, rc, P, dS);
 #pragma unroll
     for (int k = 0; k < 8; k++) {
 #pragma unroll
@@ -438,21 +439,20 @@ bwd_vdq_kernel(BwdArgs a) {
 // stored scores and dP.  Layout: D / 8 lanes per slot, lane l holding dims
 // [(l % (D/8)) * 8, +8) of slot (l / (D/8)) + u * (64 / (D/8)) in step u,
 // so each lane keeps only its 8 dims of every row's q and dO.
-template <int D>
+template <int D, int ROWS>
 __global__ __launch_bounds__(kBwdThreads) void
 bwd_vslot_kernel(BwdArgs a) {
-  constexpr int ROWS = kBwdVecRows;
   constexpr int LPS = D / 8, SPI = kWave / LPS, NI = 64 / SPI;  // lanes per slot, slots per step
   constexpr int kSlotBatch = 8;  // steps whose loads are issued together
   const int64_t wave_id = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
   const int64_t nrun = (a.M + kBwdSlotPassSlots - 1) / kBwdSlotPassSlots;
   if (wave_id >= a.B * a.Hk * nrun) return;
-  BwdVecWave<D> W(a, wave_id, nrun, kBwdSlotPassSlots);
+  BwdVecWave<D, ROWS> W(a, wave_id, nrun, kBwdSlotPassSlots);
   bwd_row_info(a, W.b, &W.len, &W.n);
   const int lane = W.lane;
-  if (W.j0 == 0) bwd_vec_zero_new_rows<D>(W);
+  if (W.j0 == 0) bwd_vec_zero_new_rows<D, ROWS>(W);
   if (W.n == 0 || W.j0 >= W.len + W.n) {
-    bwd_vec_pass_run<D>(W);
+    bwd_vec_pass_run<D, ROWS>(W);
     return;
   }
   const int col = (lane % LPS) * 8, sl = lane / LPS;
@@ -468,13 +468,13 @@ bwd_vslot_kernel(BwdArgs a) {
                            : make_uint4(0u, 0u, 0u, 0u);
   }
   float rm[ROWS], rinv[ROWS], rc[ROWS];
-  bwd_vec_row_stats<D>(W, rm, rinv, rc);
+  bwd_vec_row_stats<D, ROWS>(W, rm, rinv, rc);
 #pragma unroll 1
   for (int c = 0; c < kBwdSlotPassChunks; c++) {
     const int64_t jb = W.j0 + static_cast<int64_t>(c) * 64;
     if (jb >= a.M) break;
     float P[ROWS], dS[ROWS];
-    bwd_vec_pds<D>(W, jb, rm, rinv, rc, P, dS);
+    bwd_vec_pds<D, ROWS>(W, jb, rm, rinv, rc, P, dS);
 #pragma unroll
     for (int t = 0; t < 2; t++) {  // t = 0: keys, t = 1: values
       const uint16_t* pass = static_cast<const uint16_t*>(t == 0 ? a.d_kc_out : a.d_vc_out);

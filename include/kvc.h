@@ -252,7 +252,7 @@ int kvc_attend_over_cache(const kvc_dims *dims, int dtype, int has_scale,
  * (128, 128) and (64, 32) with query, key_cache, value_cache, new_key,
  * new_value, d_context, d_key_cache_out, d_value_cache_out and the five
  * gradient outputs 16-byte aligned take tiled kernels (and bf16 heads of
- * at most 4 packed rows with D = Dv in {64, 128} vector-unit ones); every
+ * at most 8 packed rows with D = Dv in {64, 128} vector-unit ones); every
  * other call takes generic kernels with scalar loads, in fp64 throughout.
  * The math runs in fp32 and fp64 either way; each gradient is rounded once
  * to the dtype.  The page grades gradients as well as values

@@ -828,6 +828,12 @@ BWD_CASES = [
              len_range=(0, 699), n_rule="all"),
     Workload(name="bwd_vec_r3", B=2, Hq=3, Hk=1, Q=1, M=1536, D=64, Dv=64, dtype="f32",
              len_range=(500, 1535), n_rule="all"),
+    # 5 to 8 packed rows: the 8-row vector waves in bf16 (the long decode's
+    # 8 query heads per KV head; two tokens of three heads)
+    Workload(name="bwd_vec_r8", B=3, Hq=16, Hk=2, Q=1, M=1100, D=128, Dv=128, dtype="f32",
+             len_range=(0, 1090), n_rule="all"),
+    Workload(name="bwd_vec_r6_q2", B=3, Hq=6, Hk=2, Q=2, M=700, D=64, Dv=64, dtype="f32",
+             len_range=(0, 690), n_rule="uniform"),
     # head sizes without a tiled kernel: the generic kernels (slot pieces of
     # 64, 32, 8 and 4 slots; ragged row tiles; D != Dv; the tiny step)
     WORKLOADS["tiny_mixed_f32"].with_(name="bwd_gen_tiny"),
@@ -937,12 +943,15 @@ def test_backward_misaligned_buffers_take_generic_path(which, wl):
         check_grad(to_f64(outs[name]), want, "bf16", f"misaligned {which} {name}")
 
 
-def test_backward_full_decode_bench_configuration():
-    """The backward at the full decode size bench.py --mode backward times
-    (bf16, 32 sequences, 32 query heads over 8 KV heads, 8192 slots, upstream
-    gradients for all four outputs): every gradient element against the
-    oracle (about half a minute of oracle time)."""
-    wl = WORKLOADS["decode_gqa_bf16"]
+@pytest.mark.parametrize("name", ["decode_gqa_bf16", "long_decode_share8_bf16"])
+def test_backward_full_decode_bench_configuration(name):
+    """The backward at full size with upstream gradients for all four
+    outputs, every gradient element against the oracle: the decode workload
+    bench.py --mode backward times (bf16, 32 sequences, 32 query heads over
+    8 KV heads, 8192 slots: 4 packed rows; about half a minute of oracle
+    time), and one GPU's share of the long decode (4 sequences, 64 query
+    heads over 8 KV heads, 16384 slots: the 8-row vector waves)."""
+    wl = WORKLOADS[name]
     say(f"[case] backward {wl.name} full size")
     inp = make_inputs(wl, 0, "cpu")
     dinp = {k: v.to(DEV) for k, v in inp.items()}
@@ -970,7 +979,7 @@ def test_backward_full_decode_bench_configuration():
                                                           "key_cache", "value_cache")),
                                h["lengths"], h["append_mask"],
                                **{k: to_f64(v) for k, v in ups.items()}, scale=wl.scale)
-    for name, want in (("g_query", ref.query), ("g_new_key", ref.new_key),
-                       ("g_new_value", ref.new_value), ("g_key_cache", ref.key_cache),
-                       ("g_value_cache", ref.value_cache)):
-        check_grad(got[name], want, "bf16", f"full decode backward {name}")
+    for out_name, want in (("g_query", ref.query), ("g_new_key", ref.new_key),
+                           ("g_new_value", ref.new_value), ("g_key_cache", ref.key_cache),
+                           ("g_value_cache", ref.value_cache)):
+        check_grad(got[out_name], want, "bf16", f"full {wl.name} backward {out_name}")
