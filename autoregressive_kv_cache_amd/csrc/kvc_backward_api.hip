@@ -66,12 +66,16 @@ const BwdEntry kBwdTable[] = {
 template <int D, int ROWS>
 void launch_bwd_vec(const kvc::BwdArgs& a, hipStream_t s, int which) {
   constexpr int64_t kWavesPerBlock = kvc::kBwdThreads / kvc::kWave;
+  // the statistics pass holds 4 rows a wave: 8-row heads take two waves a run
+  constexpr int RG = ROWS / 4;
   const int64_t runs =
-      which == 2 ? (a.M + kvc::kBwdSlotPassSlots - 1) / kvc::kBwdSlotPassSlots : a.nchunk;
+      which == 2 ? (a.M + kvc::kBwdSlotPassSlots - 1) / kvc::kBwdSlotPassSlots
+                 : a.nchunk * (which == 0 ? RG : 1);
   const unsigned blocks =
       static_cast<unsigned>((a.B * a.Hk * runs + kWavesPerBlock - 1) / kWavesPerBlock);
   if (which == 0)
-    hipLaunchKernelGGL((kvc::bwd_vstats_kernel<D, ROWS>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
+    hipLaunchKernelGGL((kvc::bwd_vstats_kernel<D, 4, RG>), dim3(blocks), dim3(kvc::kBwdThreads), 0,
+                       s, a);
   else if (which == 1)
     hipLaunchKernelGGL((kvc::bwd_vdq_kernel<D, ROWS>), dim3(blocks), dim3(kvc::kBwdThreads), 0, s, a);
   else

@@ -108,6 +108,7 @@ struct BwdVecWave {
   int lane;
   int64_t grp, b, kvh, j0, len, n, run_slots;
   int Q;
+  int r0 = 0;  // the first packed row of the wave's rows (row groups)
 
   __device__ BwdVecWave(const BwdArgs& args, int64_t wave_id, int64_t nrun,
                         int64_t slots_per_run = kBwdVecSlots)
@@ -119,11 +120,12 @@ struct BwdVecWave {
     kvh = grp % a.Hk;
     Q = static_cast<int>(a.Q);
   }
-  // step query / context row of packed row r (r = g * Q + t)
+  // step query / context row of the wave's row r (packed row r0 + r = g * Q + t)
   __device__ int64_t row_of(int r) const {
-    return (b * a.Hq + kvh * a.G + r / Q) * a.Q + r % Q;
+    const int rr = r0 + r;
+    return (b * a.Hq + kvh * a.G + rr / Q) * a.Q + rr % Q;
   }
-  __device__ bool row_valid(int r) const { return r < a.R && r % Q < n; }
+  __device__ bool row_valid(int r) const { return r0 + r < a.R && (r0 + r) % Q < n; }
   // slices [h*64 + (lane>>3)*8, +8) of rows r of src ([rows][D]), zeros
   // for rows that are not valid or a null src
   __device__ void load_rows(const void* src, uint4 (&v)[ROWS][NH]) const {
@@ -138,7 +140,11 @@ struct BwdVecWave {
       }
   }
   // LK8 pieces of chunk slots [jb, jb + 64) of K' (cache, or the appended
-  // rows for slots in [len, len + n)); zeros past len + n
+  // rows for slots in [len, len + n)); zeros past len + n.  Read once per
+  // kernel: non-temporal, so they do not displace what is read again --
+  // except for row groups (TEMPORAL), whose second wave finds the rows the
+  // first one read in L2.
+  template <bool TEMPORAL = false>
   __device__ void load_kv(const void* cache, const void* fresh, int64_t jb,
                           uint4 (&v)[8 * NH]) const {
 #pragma unroll
@@ -151,11 +157,9 @@ struct BwdVecWave {
         src = static_cast<const uint16_t*>(fresh) + (grp * a.Q + (j - len)) * D;
 #pragma unroll
       for (int h = 0; h < NH; h++) {
-        // read once per kernel: non-temporal, so they do not displace
-        // what is read again
-        const bwd_u32x4 w = src ? __builtin_nontemporal_load(reinterpret_cast<const bwd_u32x4*>(
-                                      src + h * 64 + (lane >> 3) * 8))
-                                : bwd_u32x4{0u, 0u, 0u, 0u};
+        const bwd_u32x4* p = reinterpret_cast<const bwd_u32x4*>(src + h * 64 + (lane >> 3) * 8);
+        bwd_u32x4 w{0u, 0u, 0u, 0u};
+        if (src) w = TEMPORAL ? *p : __builtin_nontemporal_load(p);
         v[k * NH + h] = make_uint4(w.x, w.y, w.z, w.w);
       }
     }
@@ -163,7 +167,7 @@ struct BwdVecWave {
   // lane l's slot of the chunk at jb and its visibility for packed row r
   __device__ bool visible(int64_t jb, int r) const {
     const int64_t j = jb + lane;
-    return row_valid(r) && j <= len + r % Q;
+    return row_valid(r) && j <= len + (r0 + r) % Q;
   }
 };
 
@@ -172,7 +176,7 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 
 // Scores (natural units, -inf where not visible) and dP of the chunk at jb
 // for lane l's slot.
-template <int D, int ROWS>
+template <int D, int ROWS, bool TEMPORAL>
 __device__ __forceinline__ void bwd_vec_chunk(const BwdVecWave<D, ROWS>& W, int64_t jb,
                                               const uint4 (&qv)[ROWS][D / 64],
                                               const uint4 (&dov)[ROWS][D / 64],
@@ -182,13 +186,13 @@ __device__ __forceinline__ void bwd_vec_chunk(const BwdVecWave<D, ROWS>& W, int6
   const BwdArgs& a = W.a;
   {
     uint4 vb[8 * NH];
-    W.load_kv(a.vc, a.new_value, jb, vb);
+    W.template load_kv<TEMPORAL>(a.vc, a.new_value, jb, vb);
     lk8_dots<ROWS, NH>(vb, dov, dp);
   }
   // the V' pieces are dead before the K' ones load (both at once would not
   // fit the registers of two waves per SIMD)
   __builtin_amdgcn_sched_barrier(0);
-  W.load_kv(a.kc, a.new_key, jb, kb);
+  W.template load_kv<TEMPORAL>(a.kc, a.new_key, jb, kb);
   lk8_dots<ROWS, NH>(kb, qv, s);
   const int64_t j = jb + W.lane;
 #pragma unroll
@@ -243,13 +247,20 @@ __device__ void bwd_vec_zero_new_rows(const BwdVecWave<D, ROWS>& W) {
   }
 }
 
-template <int D, int ROWS>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(ROWS <= 4 ? 2 : 1))) void
+// ROWS rows a wave; RG row groups: with RG = 2 two adjacent waves take rows
+// [0, ROWS) and [ROWS, 2 ROWS) of the same run, and the second finds the K'
+// and V' rows the first loaded in L2 (one wave of 8 rows would need a
+// register file of its own per SIMD for the rows' q and dO slices).
+template <int D, int ROWS, int RG>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 bwd_vstats_kernel(BwdArgs a) {
   constexpr int NH = D / 64;
-  const int64_t wave_id = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
+  const int64_t wave_all = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
+  const int64_t wave_id = wave_all / RG;
   if (wave_id >= a.B * a.Hk * a.nchunk) return;
   BwdVecWave<D, ROWS> W(a, wave_id, a.nchunk);
+  W.r0 = static_cast<int>(wave_all % RG) * ROWS;
+  if (W.r0 >= a.R) return;
   bwd_row_info(a, W.b, &W.len, &W.n);
   if (W.n == 0 || W.j0 >= W.len + W.n) return;  // no visible slot: bwd_rows reads nothing here
   uint4 qv[ROWS][NH], dov[ROWS][NH];
@@ -268,13 +279,13 @@ bwd_vstats_kernel(BwdArgs a) {
     if (jb >= W.len + W.n) break;
     uint4 kb[8 * NH];
     float s[ROWS], dp[ROWS];
-    bwd_vec_chunk<D, ROWS>(W, jb, qv, dov, kb, s, dp);
+    bwd_vec_chunk<D, ROWS, (RG > 1)>(W, jb, qv, dov, kb, s, dp);
     {  // for the other kernels: (s, dP) of the slot, -inf where not visible
       const int64_t j = jb + W.lane;
 #pragma unroll
       for (int r = 0; r < ROWS; r++)
-        if (r < a.R && j < W.len + W.n)
-          *reinterpret_cast<float2*>(a.ws_sdp + ((W.grp * a.R + r) * a.M + j) * 2) =
+        if (W.r0 + r < a.R && j < W.len + W.n)
+          *reinterpret_cast<float2*>(a.ws_sdp + ((W.grp * a.R + W.r0 + r) * a.M + j) * 2) =
               make_float2(s[r], dp[r]);
     }
 #pragma unroll
@@ -290,7 +301,7 @@ bwd_vstats_kernel(BwdArgs a) {
   // merge the lanes in fp64 and store the run's partials
 #pragma unroll
   for (int r = 0; r < ROWS; r++) {
-    if (r >= a.R) continue;
+    if (W.r0 + r >= a.R) continue;
     double md = m[r], ld = l[r], pdd = pd[r];
     for (int o = kWave / 2; o > 0; o >>= 1) {
       const double mo = __shfl_xor(md, o), lo = __shfl_xor(ld, o), po = __shfl_xor(pdd, o);
@@ -304,7 +315,7 @@ bwd_vstats_kernel(BwdArgs a) {
       md = mn;
     }
     if (W.lane == 0) {
-      double* p = a.ws_part + ((W.grp * a.nchunk + wave_id % a.nchunk) * a.R + r) * 4;
+      double* p = a.ws_part + ((W.grp * a.nchunk + wave_id % a.nchunk) * a.R + W.r0 + r) * 4;
       p[0] = md;
       p[1] = ld;
       p[2] = pdd;
