@@ -132,9 +132,11 @@ struct DecodeEntry {
 #define KVC_DECODE(T, CODE, D, DV, ROWS) \
   {CODE, D, DV, ROWS, kvc::decode_chunk<T, D, DV, ROWS>(), kvc::decode_waves_per_simd<ROWS>(), \
    &launch_decode<T, D, DV, ROWS>, false, 8}
-// the two kernels of a bf16 entry share chunk size and occupancy; with two
-// workgroups per unit the first one placed takes twice the share (measured:
-// 2.3 us less per decode step at B=32, Hq=32, Hk=8, M=8192)
+// the two kernels of a bf16 entry share chunk size and occupancy.  Were a
+// unit to hold two stream workgroups, the first one placed would take twice
+// the share (its waves win the SIMDs' issue arbitration; measured 2.3 us
+// less per decode step at B=32, Hq=32, Hk=8, M=8192 than even shares); the
+// stream entries now hold one workgroup per unit, and even shares.
 #define KVC_SMALL(T, CODE, D, DV, ROWS) \
   {CODE, D, DV, ROWS, kvc::kSmallChunk, 2, &launch_small<T, D, DV, ROWS>, false, 8}
 #define KVC_STREAM(D, DV, ROWS) \
@@ -346,6 +348,8 @@ int make_plan(const kvc_dims* d, int dtype, Plan* p) {
                                                                         p->decode->rows);
     p->pub.split = p->decode->chunk;
     p->pub.nsplit = p->stream.nchunk_max;
+    p->pub.workers = p->P;
+    p->pub.lead = p->decode->lead;
   } else if (p->chunk) {
     if (!make_layout(d, R, kvc::kChunkSlots, false, 0, &p->dense)) return KVC_ERR_SHAPE;
     int64_t cwgs;

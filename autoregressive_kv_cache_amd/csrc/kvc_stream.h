@@ -5,9 +5,9 @@
 // every (batch row, KV head) are cut into chunks of 64 slots -- the cached
 // slots, then one chunk with the appended rows read from new_key/new_value
 // (stream_chunks) -- and the flattened chunk list is cut into contiguous
-// ranges, one per stream worker (worker_start: with two workgroups per
-// compute unit, the workers of the first half of the grid take `lead`/8
-// times the share of the others).  A worker is one wave holding up to
+// ranges, one per stream worker (worker_start: even shares, or, were a unit
+// to hold two workgroups, `lead`/8 times the share for the first half of
+// the grid).  A worker is one wave holding up to
 // ROWS packed rows, or, past 8 rows (GROUPS), two waves side by side that
 // read the same chunks and hold 8 rows each.  A worker keeps running
 // statistics across the chunks of one KV head (a segment).
@@ -61,14 +61,25 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRefFloor = -1.0e30f;
 constexpr int kStreamChunk = 64;
 
+// One worker wave per SIMD (one workgroup of 4 waves per compute unit), for
+// 4 rows as for 8.  Measured at B = 32, Hq = 32, Hk = 8, 8192 slots (4
+// rows): two 4-row waves per SIMD (two workgroups per unit, the first one
+// placed taking twice the share) 109.7 us per step against 107.4 with one;
+// at twice the batch 207.3 against 200.5.  With one wave per SIMD no wave
+// has an older neighbour that wins the issue arbitration, and a chunk of K
+// and V in flight per wave (128 KB per unit) keeps the stream going.
 template <int ROWS>
 constexpr int stream_waves_per_simd() {
-  return ROWS > 4 ? 1 : 2;
+  return 1;
 }
-// Chunks a wave keeps in LDS before it writes them out.
+// Chunks a wave keeps in LDS before it writes them out (the LDS of a unit
+// holds one workgroup's stashes: 4 x 48 chunks of 4 rows, or 4 x 24 of 8).
+// A wave whose range fits its stash writes it once, when the range ends;
+// with 4 rows 48 chunks were 4 us per step faster than 24 at twice the
+// decode batch (37 chunks a worker) and level at the decode batch.
 template <int ROWS>
 constexpr int stream_stash_chunks() {
-  return ROWS > 4 ? 24 : 12;
+  return ROWS > 4 ? 24 : 48;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

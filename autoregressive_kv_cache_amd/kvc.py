@@ -51,7 +51,8 @@ class KvcPlan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("rows", ctypes.c_int32),
                 ("rows_per_tile", ctypes.c_int32), ("row_tiles", ctypes.c_int32),
                 ("split", ctypes.c_int64), ("nsplit", ctypes.c_int64),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("workers", ctypes.c_int64),
+                ("lead", ctypes.c_int64)]
 
 
 class KvcError(RuntimeError):

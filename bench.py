@@ -447,11 +447,9 @@ def main():
     step_bytes, attend_bytes, kv_bytes = algorithmic_bytes(wl, lengths, n)
     inter_bytes = None
     if args.mode in ("inplace", "oop", "paged") and plan["path"] == 1 and wl.dtype == "bf16":
-        # two workgroups of 4 waves per unit (uneven shares); the waves of a
-        # worker hold its row groups (1, 2 or 4 waves)
-        rgw = 1 if plan["row_tiles"] <= 1 else (2 if plan["row_tiles"] <= 2 else 4)
-        P = torch.cuda.get_device_properties(dev).multi_processor_count * 2 * (4 // rgw)
-        inter_bytes = intermediate_bytes(wl, lengths, n, P, lead=16)
+        # the workers and their shares as the library's plan states them
+        inter_bytes = intermediate_bytes(wl, lengths, n, int(plan["workers"]),
+                                         lead=int(plan["lead"]))
     if args.mode == "oop":
         extra_step, extra_attend = oop_extra_bytes(wl, lengths, n)
         step_bytes += extra_step

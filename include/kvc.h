@@ -116,6 +116,9 @@ typedef struct kvc_plan {
   int64_t split;         /* cache slots per split-K workgroup */
   int64_t nsplit;        /* ceil(M / split) */
   size_t workspace_bytes;
+  int64_t workers;       /* path 1: decode workers the chunk list is split over */
+  int64_t lead;          /* path 1: share weight of the first half of the workers,
+                            in eighths (8: even shares) */
 } kvc_plan;
 
 /* Bytes of device workspace a step with these sizes needs (0 on bad

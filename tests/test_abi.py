@@ -99,6 +99,25 @@ def test_plan_dispatch_rule(lib):
             assert (plan["rows_per_tile"], plan["row_tiles"]) == (rows, tiles), plan
         assert plan["nsplit"] * plan["split"] >= d.M
         assert plan["workspace_bytes"] == kvc.kvc_workspace_bytes(d, dt) > 0
+        if path != 1:
+            assert plan["workers"] == 0 and plan["lead"] == 0
+
+
+def test_plan_stream_workers():
+    """The bf16 stream decode: one workgroup of 4 worker waves per compute
+    unit (256 assumed without a device), even shares, two waves per worker
+    past 8 rows, and never more workers than the step can have chunks."""
+    cases = [
+        (dims(B=32, Hq=32, Hk=8, Q=1, M=8192, D=128, Dv=128), 1024),   # 4 rows
+        (dims(B=4, Hq=64, Hk=8, Q=1, M=131072, D=128, Dv=128), 1024),  # 8 rows
+        (dims(B=4, Hq=96, Hk=8, Q=1, M=8192, D=128, Dv=128), 512),     # 12 rows: row groups
+        (dims(B=1, Hq=4, Hk=1, Q=1, M=64, D=64, Dv=64), 4),            # 2 chunks: one workgroup
+    ]
+    for d, workers in cases:
+        plan = kvc.kvc_plan_step(d, kvc.KVC_BF16)
+        assert plan["path"] == 1, plan
+        assert plan["workers"] == workers, (plan, workers)
+        assert plan["lead"] == 8, plan
 
 
 FAKE = 1 << 40  # never dereferenced: each call below fails a host check first
