@@ -450,11 +450,15 @@ bwd_vdq_kernel(BwdArgs a) {
 // stored scores and dP.  Layout: D / 8 lanes per slot, lane l holding dims
 // [(l % (D/8)) * 8, +8) of slot (l / (D/8)) + u * (64 / (D/8)) in step u,
 // so each lane keeps only its 8 dims of every row's q and dO.
+// Three waves per SIMD: the 4-row form fits them as it is; the 8-row form
+// is held to them with 4 loads per batch (a few spilled bytes), which took
+// the long decode's backward (131072 slots, 8 rows) from 1827 to 1776 us
+// against two waves per SIMD with 8 loads per batch.
 template <int D, int ROWS>
-__global__ __launch_bounds__(kBwdThreads) void
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))) void
 bwd_vslot_kernel(BwdArgs a) {
   constexpr int LPS = D / 8, SPI = kWave / LPS, NI = 64 / SPI;  // lanes per slot, slots per step
-  constexpr int kSlotBatch = 8;  // steps whose loads are issued together
+  constexpr int kSlotBatch = ROWS > 4 ? 4 : 8;  // steps whose loads are issued together
   const int64_t wave_id = blockIdx.x * (kBwdThreads / kWave) + threadIdx.x / kWave;
   const int64_t nrun = (a.M + kBwdSlotPassSlots - 1) / kBwdSlotPassSlots;
   if (wave_id >= a.B * a.Hk * nrun) return;
