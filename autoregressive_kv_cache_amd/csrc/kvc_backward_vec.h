@@ -42,7 +42,13 @@ namespace kvc {
 
 typedef unsigned int bwd_u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBwdVecChunks = 8;                    // 64-slot chunks per wave
+// 64-slot chunks per wave of the statistics and dq passes.  The run length
+// sets how many waves have visible slots against the 2048 the chip runs at
+// once, and so whether a last, nearly empty round of waves remains.
+// Measured (us per backward call; B=32 decode / one GPU's eighth of the long
+// decode / the long decode): 8 chunks 735 / 318 / 1771, 9 chunks
+// 725 / 328 / 1650, 10 chunks 738 / 341 / 1662.
+constexpr int kBwdVecChunks = 9;
 constexpr int kBwdVecSlots = 64 * kBwdVecChunks;    // slots per run (one wave)
 constexpr int kBwdVecRows = 8;                      // packed rows a wave holds, at most
 // The slot pass in one-chunk runs: it has a wave for every run of the cache
@@ -51,7 +57,8 @@ constexpr int kBwdVecRows = 8;                      // packed rows a wave holds,
 // with 512-slot runs, 447 with 256 and 424 with 128, and the whole backward
 // call 760 us with 128-slot runs against 730 with 64.  The statistics and
 // dq passes, which load every packed row's q and dO per wave, were slower
-// with shorter runs (208 -> 232 -> 273 us) and keep 512.
+// with shorter runs (208 -> 232 -> 273 us at 512 -> 256 -> 128) and keep
+// longer ones (kBwdVecChunks).
 constexpr int kBwdSlotPassChunks = 1;
 constexpr int kBwdSlotPassSlots = 64 * kBwdSlotPassChunks;
 

@@ -820,7 +820,7 @@ BWD_CASES = [
     # groups that take a second tile
     chunk_wl(name="bwd_rows320", dtype="f32", B=2, Hq=16, Hk=2, Q=40, M=160, len_range=(0, 100)),
     # at most 4 packed rows, D = Dv in {64, 128}: the vector-unit kernels
-    # for bf16 (runs of 512 slots; capacities that end inside a run and a
+    # for bf16 (runs of 576 slots; capacities that end inside a run and a
     # 64-slot chunk), the fp64 matrix-core ones for fp32
     Workload(name="bwd_vec_q2", B=3, Hq=4, Hk=2, Q=2, M=1100, D=64, Dv=64, dtype="f32",
              len_range=(0, 1090), n_rule="uniform"),
